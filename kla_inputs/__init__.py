@@ -1,0 +1,198 @@
+"""Seeded synthetic inputs for the KLA forward scan and the precision-only scan.
+
+This module is shared by the tests, the oracle runs and the benchmark. It holds
+the input *recipes* only (distributions, shapes, bf16 rounding of the values
+that both sides consume); it contains none of the filter's arithmetic.
+
+Workloads (names used throughout the repository):
+
+  tiny_f32      B=1,  H=1,  T=256,   d_k=d_v=16,  fp32
+  lm45m_bf16    B=8,  H=8,  T=2048,  d_k=d_v=64,  bf16 inputs
+  lm180m_bf16   B=16, H=12, T=2048,  d_k=d_v=64,  bf16, 5% of tokens with val_prec x100
+  long_bf16     B=2,  H=16, T=16384, d_k=d_v=128, bf16, long-memory decay
+  chains_f32    65536 chains x T=65536 (as B=1, H=1024, D=64), fp32, precision path only
+
+Distributions (all draws float64, then cast):
+  q, k        ~ N(0, 1/d_k)                       (variance 1/d_k)
+  v           ~ N(0, 1)
+  log_decay   = -softplus(N(mu_decay, 1))          mu_decay = 0, or -2 for long_bf16
+  proc_noise  = softplus(N(0, 1)) + 1e-3
+  val_prec    = softplus(N(0, 1)) + 1e-3           (x100 on masked tokens, lm180m_bf16)
+  lambda0 = 1, M0 = 0
+
+Seeding: seed = 1000 + workload index; one PCG64 stream per tensor from
+``SeedSequence(seed).spawn(7)`` in the order q, k, v, log_decay, proc_noise,
+val_prec, mask.  bf16 workloads round every input once, round-to-nearest-even,
+and both the GPU path and the oracle consume exactly those rounded values.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+import numpy as np
+
+__all__ = [
+    "Workload", "WORKLOADS", "workload", "round_bf16", "bf16_bits",
+    "make_forward_inputs", "make_precision_inputs", "make_precision_inputs_torch",
+    "softplus",
+]
+
+
+@dataclass(frozen=True)
+class Workload:
+    index: int
+    name: str
+    kind: str            # "forward" or "precision"
+    B: int
+    H: int
+    T: int
+    dk: int
+    dv: int
+    dtype: str           # "f32" or "bf16"
+    decay_mean: float = 0.0
+    spike_frac: float = 0.0
+    spike_scale: float = 1.0
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.index
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.H * self.T
+
+
+WORKLOADS = (
+    Workload(0, "tiny_f32", "forward", 1, 1, 256, 16, 16, "f32"),
+    Workload(1, "lm45m_bf16", "forward", 8, 8, 2048, 64, 64, "bf16"),
+    Workload(2, "lm180m_bf16", "forward", 16, 12, 2048, 64, 64, "bf16",
+             spike_frac=0.05, spike_scale=100.0),
+    Workload(3, "long_bf16", "forward", 2, 16, 16384, 128, 128, "bf16", decay_mean=-2.0),
+    Workload(4, "chains_f32", "precision", 1, 1024, 65536, 64, 64, "f32"),
+)
+
+
+def workload(key) -> Workload:
+    """Look a workload up by index or by name."""
+    for w in WORKLOADS:
+        if key == w.index or key == w.name:
+            return w
+    raise KeyError(key)
+
+
+def softplus(x: np.ndarray) -> np.ndarray:
+    """log(1 + e^x), evaluated without overflow."""
+    return np.logaddexp(0.0, x)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of float32 values, round-to-nearest-even.
+
+    Inputs must be finite.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
+    bits = bf16_bits(x).astype(np.uint32) << 16
+    return bits.view(np.float32)
+
+
+def _streams(seed: int, n: int = 7):
+    return [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(n)]
+
+
+def make_forward_inputs(w: Workload | int | str, *, B=None, H=None, T=None, dk=None, dv=None,
+                        seed=None, dtype=None) -> dict:
+    """Seeded inputs of a forward workload, optionally at another shape.
+
+    Returns a dict of float32 numpy arrays (bf16-rounded when the dtype is
+    bf16): q, k, log_decay, proc_noise, val_prec [B,H,T,dk]; v [B,H,T,dv];
+    lambda0 [B,H,dk]; M0 [B,H,dk,dv]; plus "dtype" and "seed".
+    """
+    if not isinstance(w, Workload):
+        w = workload(w)
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    T = w.T if T is None else T
+    dk = w.dk if dk is None else dk
+    dv = w.dv if dv is None else dv
+    seed = w.seed if seed is None else seed
+    dtype = w.dtype if dtype is None else dtype
+    rq, rk, rv, rd, rp, rl, rm = _streams(seed)
+    sk = (B, H, T, dk)
+    q = rq.standard_normal(sk) / np.sqrt(dk)
+    k = rk.standard_normal(sk) / np.sqrt(dk)
+    v = rv.standard_normal((B, H, T, dv))
+    log_decay = -softplus(rd.standard_normal(sk) + w.decay_mean)
+    proc_noise = softplus(rp.standard_normal(sk)) + 1e-3
+    val_prec = softplus(rl.standard_normal(sk)) + 1e-3
+    if w.spike_frac > 0.0:
+        mask = rm.random((B, H, T)) < w.spike_frac
+        val_prec = np.where(mask[..., None], val_prec * w.spike_scale, val_prec)
+    out = {}
+    for name, arr in (("q", q), ("k", k), ("v", v), ("log_decay", log_decay),
+                      ("proc_noise", proc_noise), ("val_prec", val_prec)):
+        a32 = arr.astype(np.float32)
+        out[name] = round_bf16(a32) if dtype == "bf16" else a32
+    out["lambda0"] = np.ones((B, H, dk), np.float32)
+    out["M0"] = np.zeros((B, H, dk, dv), np.float32)
+    out["dtype"] = dtype
+    out["seed"] = seed
+    return out
+
+
+def make_precision_inputs(*, B: int, H: int, T: int, D: int, seed: int = 1004) -> dict:
+    """Host-side seeded inputs of the precision-only scan (chains_f32 recipe).
+
+    log_decay = -softplus(N(0,1)); proc_noise = softplus(N(0,1));
+    obs_prec = k^2 * Lambda^v with k ~ N(0,1), Lambda^v = softplus(N(0,1)),
+    formed in float32 as the recipe's input; lambda0 = 1.  All float32.
+    """
+    rk, rl, rd, rp = _streams(seed, 4)
+    shape = (B, H, T, D)
+    log_decay = (-softplus(rd.standard_normal(shape))).astype(np.float32)
+    proc_noise = softplus(rp.standard_normal(shape)).astype(np.float32)
+    kk = rk.standard_normal(shape).astype(np.float32)
+    lv = softplus(rl.standard_normal(shape)).astype(np.float32)
+    obs_prec = (kk * kk * lv).astype(np.float32)
+    return {"log_decay": log_decay, "proc_noise": proc_noise, "obs_prec": obs_prec,
+            "lambda0": np.ones((B, H, D), np.float32), "seed": seed}
+
+
+def make_precision_inputs_torch(*, B: int, H: int, T: int, D: int, seed: int = 1004,
+                                device="cuda", chunk_rows: int = 1 << 26):
+    """Device-side seeded inputs of the precision-only scan, for sizes the host cannot
+    generate quickly (the full chains_f32 workload is 4.3 G elements per tensor).
+
+    Same recipe as :func:`make_precision_inputs` but drawn with torch's generator on
+    ``device``; the values differ from the host version.  Tensors are float32 and
+    contiguous [B,H,T,D]; generation runs in slabs to bound temporaries.
+    """
+    import torch
+    gens = []
+    for i in range(4):
+        g = torch.Generator(device=device)
+        g.manual_seed(seed * 16 + i)
+        gens.append(g)
+    shape = (B, H, T, D)
+    n = B * H * T * D
+    ld = torch.empty(shape, dtype=torch.float32, device=device)
+    pn = torch.empty(shape, dtype=torch.float32, device=device)
+    op = torch.empty(shape, dtype=torch.float32, device=device)
+    fl, fp, fo = ld.view(-1), pn.view(-1), op.view(-1)
+    sp = torch.nn.functional.softplus
+    for s in range(0, n, chunk_rows):
+        e = min(n, s + chunk_rows)
+        m = e - s
+        fl[s:e] = -sp(torch.randn(m, generator=gens[0], device=device))
+        fp[s:e] = sp(torch.randn(m, generator=gens[1], device=device))
+        kk = torch.randn(m, generator=gens[2], device=device)
+        lv = sp(torch.randn(m, generator=gens[3], device=device))
+        fo[s:e] = kk * kk * lv
+        del kk, lv
+    lam0 = torch.ones((B, H, D), dtype=torch.float32, device=device)
+    return {"log_decay": ld, "proc_noise": pn, "obs_prec": op, "lambda0": lam0, "seed": seed}

@@ -1,0 +1,17 @@
+"""Float64 CPU oracle of the Kalman Linear Attention (KLA) forward scan.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the CPU
+baseline leg of the benchmark may import this package.  The product path (the
+HIP library and its Python binding) never imports it, and it imports nothing
+from the product path.
+"""
+from .kla_f64 import (  # noqa: F401
+    kla_forward_f64,
+    precision_scan_f64,
+    precision_path_from_coeffs,
+    predict_precision,
+    update_precision,
+    forget_gate,
+    write_gate,
+    readout,
+)

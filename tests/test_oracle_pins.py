@@ -1,0 +1,49 @@
+"""The float64 oracle against independent pins, and planted mistakes against the pins.
+
+CPU only.  See tests/oracle_pins.py for what each pin states.
+"""
+import numpy as np
+import pytest
+
+import oracle.kla_f64 as O
+import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+# Plausible mistakes, each planted in one step function of the oracle.  Every one
+# must make at least one pin fail; otherwise the pins would not notice it.
+MUTANTS = {
+    "predict_drops_process_noise": ("predict_precision", lambda lam, a, pbar: lam / (a * a)),
+    "predict_uses_a_not_a2": ("predict_precision", lambda lam, a, pbar: lam / (a + pbar * lam)),
+    "predict_noise_wrong_side": ("predict_precision", lambda lam, a, pbar: lam / (a * a) + pbar),
+    "update_drops_evidence": ("update_precision", lambda lam_pred, c: lam_pred),
+    "update_subtracts_evidence": ("update_precision", lambda lam_pred, c: lam_pred - c),
+    "forget_drops_decay": ("forget_gate", lambda a, lam_pred, lam: lam_pred / lam),
+    "forget_inverted": ("forget_gate", lambda a, lam_pred, lam: a * lam / lam_pred),
+    "forget_squared_decay": ("forget_gate", lambda a, lam_pred, lam: a * a * lam_pred / lam),
+    "write_drops_value_precision": ("write_gate", lambda k, vp, lam: k / lam),
+    "write_sign_flipped": ("write_gate", lambda k, vp, lam: -k * vp / lam),
+    "write_uses_k_squared": ("write_gate", lambda k, vp, lam: k * k * vp / lam),
+    "readout_transposed_state": ("readout",
+                                 lambda q, M: np.einsum("...i,...ji->...j", q, M[..., : q.shape[-1], : q.shape[-1]])),
+    "readout_sums_without_q": ("readout", lambda q, M: M.sum(axis=-2)),
+    "readout_abs_q": ("readout", lambda q, M: np.einsum("...i,...ij->...j", np.abs(q), M)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failed = []
+    for pin in P.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except Exception:  # AssertionError or a shape/ValueError from the mutant
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {name}"
