@@ -1,0 +1,231 @@
+"""Python binding of libkla.so, the KLA forward scan for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/kla.h.  PyTorch supplies device
+memory and the current stream.  Importing this package loads the library and
+raises if it has not been built (``python -m bius_scan_sequence_amd.build``);
+there is no fallback implementation.
+
+Low-level functions carry the C names (``kla_forward``, ``kla_precision_scan``,
+``kla_workspace_init``, ...) and take raw pointers; ``forward`` and
+``precision_scan`` are the tensor-level helpers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "LIB_PATH", "lib", "KLA_F32", "KLA_BF16", "KlaError",
+    "kla_forward_workspace_bytes", "kla_forward", "kla_precision_scan_workspace_bytes",
+    "kla_precision_scan", "kla_workspace_init", "kla_workspace_error", "kla_status_string",
+    "forward", "precision_scan", "Workspace",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkla.so")
+KLA_F32, KLA_BF16 = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m bius_scan_sequence_amd.build`")
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _fp, _sz, _i = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+lib.kla_forward_workspace_bytes.restype = _sz
+lib.kla_forward_workspace_bytes.argtypes = [_i] * 5
+lib.kla_forward.restype = _i
+lib.kla_forward.argtypes = [_vp] * 6 + [_fp] * 2 + [_vp] + [_fp] * 3 + [_i] * 6 + [_vp, _sz, _vp]
+lib.kla_precision_scan_workspace_bytes.restype = _sz
+lib.kla_precision_scan_workspace_bytes.argtypes = [_i] * 4
+lib.kla_precision_scan.restype = _i
+lib.kla_precision_scan.argtypes = [_fp] * 6 + [_i] * 4 + [_vp, _sz, _vp]
+lib.kla_workspace_init.restype = _i
+lib.kla_workspace_init.argtypes = [_vp, _sz, _vp]
+lib.kla_workspace_error.restype = _i
+lib.kla_workspace_error.argtypes = [_vp, ctypes.POINTER(ctypes.c_int)]
+lib.kla_status_string.restype = ctypes.c_char_p
+lib.kla_status_string.argtypes = [_i]
+
+
+class KlaError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(f"KLA status {code}: {kla_status_string(code)}")
+        self.code = code
+
+
+# ----------------------------------------------------------------------------- raw C ABI
+def kla_forward_workspace_bytes(B, H, T, dk, dv) -> int:
+    return int(lib.kla_forward_workspace_bytes(B, H, T, dk, dv))
+
+
+def kla_forward(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0, y, lambda_T, M_T,
+                lambda_path, B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream) -> int:
+    return int(lib.kla_forward(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0, y, lambda_T,
+                               M_T, lambda_path, B, H, T, dk, dv, dtype, workspace, workspace_bytes,
+                               stream))
+
+
+def kla_precision_scan_workspace_bytes(B, H, T, D) -> int:
+    return int(lib.kla_precision_scan_workspace_bytes(B, H, T, D))
+
+
+def kla_precision_scan(log_decay, proc_noise, obs_prec, lambda0, lambda_path, lambda_T, B, H, T, D,
+                       workspace, workspace_bytes, stream) -> int:
+    return int(lib.kla_precision_scan(log_decay, proc_noise, obs_prec, lambda0, lambda_path, lambda_T,
+                                      B, H, T, D, workspace, workspace_bytes, stream))
+
+
+def kla_workspace_init(workspace, workspace_bytes, stream) -> int:
+    return int(lib.kla_workspace_init(workspace, workspace_bytes, stream))
+
+
+def kla_workspace_error(workspace) -> int:
+    out = ctypes.c_int(0)
+    rc = int(lib.kla_workspace_error(workspace, ctypes.byref(out)))
+    if rc:
+        raise KlaError(rc)
+    return out.value
+
+
+def kla_status_string(status: int) -> str:
+    return lib.kla_status_string(status).decode()
+
+
+# ----------------------------------------------------------------------------- tensors
+def _torch():
+    import torch
+    return torch
+
+
+class Workspace:
+    """A zero-initialised device workspace that grows on demand.
+
+    One workspace serves calls ordered on one stream.  Growing it allocates a
+    new buffer and initialises it with kla_workspace_init on the given stream.
+    """
+
+    def __init__(self, device=None):
+        torch = _torch()
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.buf = None
+
+    def get(self, nbytes: int, stream_handle: int):
+        torch = _torch()
+        nbytes = max(256, (int(nbytes) + 255) // 256 * 256)
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            rc = kla_workspace_init(self.buf.data_ptr(), self.buf.numel(), stream_handle)
+            if rc:
+                raise KlaError(rc)
+        return self.buf
+
+    def error(self) -> int:
+        return 0 if self.buf is None else kla_workspace_error(self.buf.data_ptr())
+
+
+_ws_lock = threading.Lock()
+_ws_cache: dict = {}
+
+
+def _default_workspace(device, stream_handle) -> Workspace:
+    key = (str(device), int(stream_handle))
+    with _ws_lock:
+        ws = _ws_cache.get(key)
+        if ws is None:
+            ws = _ws_cache[key] = Workspace(device)
+        return ws
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check(t, name, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def forward(q, k, v, log_decay, proc_noise, val_prec, lambda0=None, M0=None,
+            return_lambda_path=False, workspace: Workspace | None = None, out=None):
+    """KLA forward pass on the current stream.
+
+    q, k, log_decay, proc_noise, val_prec: [B,H,T,dk]; v: [B,H,T,dv]; all
+    bfloat16 or all float32, contiguous, on one GPU.  lambda0 [B,H,dk] and
+    M0 [B,H,dk,dv] are float32 (None: 1 and 0).  Returns
+    (y [B,H,T,dv] input dtype, lambda_T [B,H,dk] f32, M_T [B,H,dk,dv] f32) and
+    the f32 precision path [B,H,T,dk] when return_lambda_path.  ``out`` may
+    hold preallocated (y, lambda_T, M_T) tensors.
+    """
+    torch = _torch()
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    dtype, dev = k.dtype, k.device
+    if dtype == torch.bfloat16:
+        code = KLA_BF16
+    elif dtype == torch.float32:
+        code = KLA_F32
+    else:
+        raise ValueError(f"unsupported dtype {dtype}")
+    for name, t, shp in (("q", q, (B, H, T, dk)), ("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)),
+                         ("log_decay", log_decay, (B, H, T, dk)), ("proc_noise", proc_noise, (B, H, T, dk)),
+                         ("val_prec", val_prec, (B, H, T, dk))):
+        _check(t, name, shp, dtype, dev)
+    if lambda0 is not None:
+        _check(lambda0, "lambda0", (B, H, dk), torch.float32, dev)
+    if M0 is not None:
+        _check(M0, "M0", (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        y = torch.empty((B, H, T, dv), dtype=dtype, device=dev)
+        lam_T = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+        M_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        y, lam_T, M_T = out
+    lpath = torch.empty((B, H, T, dk), dtype=torch.float32, device=dev) if return_lambda_path else None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    need = kla_forward_workspace_bytes(B, H, T, dk, dv)
+    if need == 0:
+        raise KlaError(2)
+    ws = (workspace or _default_workspace(dev, stream)).get(need, stream)
+    rc = kla_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(proc_noise), _ptr(val_prec),
+                     _ptr(lambda0), _ptr(M0), _ptr(y), _ptr(lam_T), _ptr(M_T), _ptr(lpath),
+                     B, H, T, dk, dv, code, ws.data_ptr(), ws.numel(), stream)
+    if rc:
+        raise KlaError(rc)
+    return (y, lam_T, M_T, lpath) if return_lambda_path else (y, lam_T, M_T)
+
+
+def precision_scan(log_decay, proc_noise, obs_prec, lambda0=None, workspace: Workspace | None = None,
+                   out=None):
+    """Precision path of B*H*D independent chains (float32 [B,H,T,D] inputs).
+
+    Returns (lambda_path [B,H,T,D], lambda_T [B,H,D]); ``out`` may hold
+    preallocated tensors for both.
+    """
+    torch = _torch()
+    B, H, T, D = log_decay.shape
+    dev = log_decay.device
+    for name, t in (("log_decay", log_decay), ("proc_noise", proc_noise), ("obs_prec", obs_prec)):
+        _check(t, name, (B, H, T, D), torch.float32, dev)
+    if lambda0 is not None:
+        _check(lambda0, "lambda0", (B, H, D), torch.float32, dev)
+    if out is None:
+        lpath = torch.empty((B, H, T, D), dtype=torch.float32, device=dev)
+        lam_T = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    else:
+        lpath, lam_T = out
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    need = kla_precision_scan_workspace_bytes(B, H, T, D)
+    if need == 0:
+        raise KlaError(1)
+    ws = (workspace or _default_workspace(dev, stream)).get(need, stream)
+    rc = kla_precision_scan(_ptr(log_decay), _ptr(proc_noise), _ptr(obs_prec), _ptr(lambda0), _ptr(lpath),
+                            _ptr(lam_T), B, H, T, D, ws.data_ptr(), ws.numel(), stream)
+    if rc:
+        raise KlaError(rc)
+    return lpath, lam_T

@@ -1,0 +1,227 @@
+// C ABI of the KLA library: argument validation, workspace layout, launches.
+// The public contract (argument meaning, layout, ownership, errors) is in
+// include/kla.h.
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/kla.h"
+#include "kla_internal.h"
+
+namespace kla {
+namespace {
+
+thread_local char g_hip_error[256] = "";
+
+int hip_fail(hipError_t e, const char* where) {
+  snprintf(g_hip_error, sizeof(g_hip_error), "HIP error in %s: %s", where, hipGetErrorString(e));
+  return KLA_ERR_HIP;
+}
+
+bool supported_width(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+constexpr size_t kHeader = 256;
+
+struct FwdLayout {
+  size_t pflag, mflag, pagg, pinc, mF, magg, minc, total;
+};
+
+bool fwd_shape_ok(int B, int H, int T, int dk, int dv) {
+  if (B < 1 || H < 1 || T < 0) return false;
+  if (!supported_width(dk) || !supported_width(dv)) return false;
+  const long long wide = dk > dv ? dk : dv;
+  return (long long)B * H * (long long)T * wide < (1LL << 31) && (long long)B * H < (1LL << 24);
+}
+
+FwdLayout fwd_layout(int B, int H, int T, int dk, int dv, int nseg) {
+  const size_t slots = (size_t)B * H * nseg;
+  FwdLayout l;
+  size_t o = kHeader;
+  l.pflag = o; o += round256(slots * 4);
+  l.mflag = o; o += round256(slots * 4);
+  l.pagg = o; o += round256(slots * dk * 16);
+  l.pinc = o; o += round256(slots * dk * 4);
+  l.mF = o; o += round256(slots * dk * 4);
+  l.magg = o; o += round256(slots * (size_t)dk * dv * 4);
+  l.minc = o; o += round256(slots * (size_t)dk * dv * 4);
+  l.total = o;
+  return l;
+}
+
+int fwd_nseg(int T, int dk, int dv, bool bf16) {
+  const int L = fwd_segment_len(dk, dv, bf16);
+  return (T + L - 1) / L;
+}
+
+struct PscanPlan {
+  int ncblocks, nseg, seglen;
+  size_t flag, agg, inc, total;
+};
+
+bool pscan_shape_ok(int B, int H, int T, int D) {
+  if (B < 1 || H < 1 || D < 1 || T < 0) return false;
+  const long long chains = (long long)B * H * D;
+  return chains < (1LL << 31) && chains * (long long)T < (1LL << 62);
+}
+
+PscanPlan pscan_plan(int B, int H, int T, int D) {
+  PscanPlan pl;
+  const long long chains = (long long)B * H * D;
+  pl.ncblocks = (int)((chains + 255) / 256);
+  // One walk per chain when the chains alone fill the GPU (a workgroup per
+  // compute unit); otherwise split T so that about 1024 workgroups run, with
+  // segments of at least 512 tokens.
+  int nseg = 1;
+  if (pl.ncblocks < 256 && T >= 1024) {
+    nseg = (1024 + pl.ncblocks - 1) / pl.ncblocks;
+    const int cap = T / 512;
+    if (nseg > cap) nseg = cap;
+    if (nseg < 1) nseg = 1;
+  }
+  int seglen = T > 0 ? (T + nseg - 1) / nseg : 16;
+  seglen = (seglen + 15) / 16 * 16;
+  pl.seglen = seglen;
+  pl.nseg = T > 0 ? (T + seglen - 1) / seglen : 1;
+  const size_t slots = (size_t)pl.ncblocks * pl.nseg;
+  size_t o = kHeader;
+  pl.flag = o; o += round256(slots * 4);
+  if (pl.nseg > 1) {
+    pl.agg = o; o += round256(slots * 256 * 16);
+    pl.inc = o; o += round256(slots * 256 * 4);
+  } else {
+    pl.agg = pl.inc = o;
+  }
+  pl.total = o;
+  return pl;
+}
+
+}  // namespace
+}  // namespace kla
+
+using namespace kla;
+
+extern "C" size_t kla_forward_workspace_bytes(int B, int H, int T, int dk, int dv) {
+  if (!fwd_shape_ok(B, H, T, dk, dv)) return 0;
+  // The layout does not depend on the dtype except through the segment
+  // length; size for the shorter segment (more segments) to cover both.
+  const int nseg = T > 0 ? fwd_nseg(T, dk, dv, false) : 1;
+  const int nseg_b = T > 0 ? fwd_nseg(T, dk, dv, true) : 1;
+  return fwd_layout(B, H, T, dk, dv, nseg > nseg_b ? nseg : nseg_b).total;
+}
+
+extern "C" int kla_forward(const void* q, const void* k, const void* v, const void* log_decay,
+                           const void* proc_noise, const void* val_prec, const float* lambda0,
+                           const float* M0, void* y, float* lambda_T, float* M_T, float* lambda_path,
+                           int B, int H, int T, int dk, int dv, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (B < 1 || H < 1 || T < 0) return KLA_ERR_INVALID_ARG;
+  if (!lambda_T || !M_T) return KLA_ERR_INVALID_ARG;
+  // With T = 0 the per-token arrays are empty and never touched (may be null).
+  if (T > 0 && (!q || !k || !v || !log_decay || !proc_noise || !val_prec || !y))
+    return KLA_ERR_INVALID_ARG;
+  if (dtype != KLA_F32 && dtype != KLA_BF16) return KLA_ERR_UNSUPPORTED;
+  if (!supported_width(dk) || !supported_width(dv)) return KLA_ERR_UNSUPPORTED;
+  if (!fwd_shape_ok(B, H, T, dk, dv)) return KLA_ERR_INVALID_ARG;
+  const size_t esz = dtype == KLA_BF16 ? 2 : 4;
+  const void* ins[6] = {q, k, v, log_decay, proc_noise, val_prec};
+  for (const void* p : ins)
+    if (!aligned(p, 16)) return KLA_ERR_INVALID_ARG;
+  if (!aligned(y, esz) || !aligned(lambda_T, 4) || !aligned(M_T, 4)) return KLA_ERR_INVALID_ARG;
+  if ((lambda0 && !aligned(lambda0, 4)) || (M0 && !aligned(M0, 4)) ||
+      (lambda_path && !aligned(lambda_path, 4)))
+    return KLA_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256)) return KLA_ERR_WORKSPACE;
+  const size_t need = kla_forward_workspace_bytes(B, H, T, dk, dv);
+  if (workspace_bytes < need) return KLA_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const long long nheads = (long long)B * H;
+  if (T == 0) {
+    hipError_t e = launch_state_copy(lambda0, M0, lambda_T, M_T, nheads * dk, nheads * dk * dv, st);
+    return e == hipSuccess ? KLA_OK : hip_fail(e, "kla_forward (T = 0 state copy)");
+  }
+  const bool bf16 = dtype == KLA_BF16;
+  const int nseg = fwd_nseg(T, dk, dv, bf16);
+  const FwdLayout l = fwd_layout(B, H, T, dk, dv, nseg);
+  char* ws = static_cast<char*>(workspace);
+  FwdParams p;
+  p.q = q; p.k = k; p.v = v; p.ld = log_decay; p.pn = proc_noise; p.vp = val_prec;
+  p.lam0 = lambda0; p.M0 = M0; p.y = y; p.lamT = lambda_T; p.MT = M_T; p.lpath = lambda_path;
+  p.nheads = (int)nheads; p.T = T; p.nseg = nseg;
+  p.ctrl = reinterpret_cast<unsigned*>(ws);
+  p.pflag = reinterpret_cast<unsigned*>(ws + l.pflag);
+  p.mflag = reinterpret_cast<unsigned*>(ws + l.mflag);
+  p.pagg = reinterpret_cast<float*>(ws + l.pagg);
+  p.pinc = reinterpret_cast<float*>(ws + l.pinc);
+  p.mF = reinterpret_cast<float*>(ws + l.mF);
+  p.magg = reinterpret_cast<float*>(ws + l.magg);
+  p.minc = reinterpret_cast<float*>(ws + l.minc);
+  hipError_t e = launch_forward(p, dk, dv, bf16, st);
+  return e == hipSuccess ? KLA_OK : hip_fail(e, "kla_forward");
+}
+
+extern "C" size_t kla_precision_scan_workspace_bytes(int B, int H, int T, int D) {
+  if (!pscan_shape_ok(B, H, T, D)) return 0;
+  return pscan_plan(B, H, T, D).total;
+}
+
+extern "C" int kla_precision_scan(const float* log_decay, const float* proc_noise, const float* obs_prec,
+                                  const float* lambda0, float* lambda_path, float* lambda_T, int B, int H,
+                                  int T, int D, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!pscan_shape_ok(B, H, T, D)) return KLA_ERR_INVALID_ARG;
+  if (T > 0 && (!log_decay || !proc_noise || !obs_prec || !lambda_path)) return KLA_ERR_INVALID_ARG;
+  const void* ptrs[6] = {log_decay, proc_noise, obs_prec, lambda_path, lambda0, lambda_T};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 4)) return KLA_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256)) return KLA_ERR_WORKSPACE;
+  const PscanPlan pl = pscan_plan(B, H, T, D);
+  if (workspace_bytes < pl.total) return KLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const long long chains = (long long)B * H * D;
+  if (T == 0) {
+    if (!lambda_T) return KLA_OK;
+    hipError_t e = launch_state_copy(lambda0, nullptr, lambda_T, nullptr, chains, 0, st);
+    return e == hipSuccess ? KLA_OK : hip_fail(e, "kla_precision_scan (T = 0 state copy)");
+  }
+  char* ws = static_cast<char*>(workspace);
+  PscanParams p;
+  p.ld = log_decay; p.pn = proc_noise; p.c = obs_prec; p.lam0 = lambda0;
+  p.lpath = lambda_path; p.lamT = lambda_T;
+  p.nchains = chains; p.D = D; p.T = T;
+  p.nseg = pl.nseg; p.seglen = pl.seglen; p.ncblocks = pl.ncblocks;
+  p.ctrl = reinterpret_cast<unsigned*>(ws);
+  p.flag = reinterpret_cast<unsigned*>(ws + pl.flag);
+  p.agg = reinterpret_cast<float*>(ws + pl.agg);
+  p.inc = reinterpret_cast<float*>(ws + pl.inc);
+  hipError_t e = launch_pscan(p, st);
+  return e == hipSuccess ? KLA_OK : hip_fail(e, "kla_precision_scan");
+}
+
+extern "C" int kla_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || !aligned(workspace, 256)) return KLA_ERR_WORKSPACE;
+  if (workspace_bytes < kHeader || workspace_bytes % 4) return KLA_ERR_INVALID_ARG;
+  hipError_t e = launch_fill_zero(workspace, workspace_bytes / 4, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KLA_OK : hip_fail(e, "kla_workspace_init");
+}
+
+extern "C" int kla_workspace_error(const void* workspace, int* error_out) {
+  if (!workspace || !error_out || !aligned(workspace, 256)) return KLA_ERR_INVALID_ARG;
+  unsigned w = 0;
+  hipError_t e = hipMemcpy(&w, static_cast<const char*>(workspace) + 4 * kError, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "kla_workspace_error");
+  *error_out = (int)w;
+  return KLA_OK;
+}
+
+extern "C" const char* kla_status_string(int status) {
+  switch (status) {
+    case KLA_OK: return "success";
+    case KLA_ERR_INVALID_ARG: return "invalid argument (null pointer, size or alignment)";
+    case KLA_ERR_UNSUPPORTED: return "unsupported d_k/d_v or dtype (widths 16, 32, 64, 128; dtype f32 or bf16)";
+    case KLA_ERR_WORKSPACE: return "workspace missing, not 256-byte aligned, or smaller than required";
+    case KLA_ERR_HIP: return g_hip_error[0] ? g_hip_error : "HIP error";
+    default: return "unknown status";
+  }
+}

@@ -1,0 +1,45 @@
+// Small helper kernels: workspace zero-fill and the T = 0 state copy.
+#include "kla_internal.h"
+
+namespace kla {
+
+__global__ void kla_fill_zero_kernel(unsigned* p, size_t words) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// T = 0: the scan is the identity, so the state out equals the state in
+// (lambda0 = 1 and M0 = 0 when not given).
+__global__ void kla_state_copy_kernel(const float* lam0, const float* M0, float* lamT, float* MT,
+                                      long long nl, long long nm) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < nl + nm;
+       i += (long long)gridDim.x * blockDim.x) {
+    if (i < nl)
+      lamT[i] = lam0 ? lam0[i] : 1.f;
+    else
+      MT[i - nl] = M0 ? M0[i - nl] : 0.f;
+  }
+}
+
+static unsigned grid_for(long long n) {
+  long long g = (n + 255) / 256;
+  if (g < 1) g = 1;
+  if (g > 4096) g = 4096;
+  return (unsigned)g;
+}
+
+hipError_t launch_fill_zero(void* ptr, size_t words, hipStream_t stream) {
+  hipLaunchKernelGGL(kla_fill_zero_kernel, dim3(grid_for((long long)words)), dim3(256), 0, stream,
+                     static_cast<unsigned*>(ptr), words);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_copy(const float* lam0, const float* M0, float* lamT, float* MT, long long nl,
+                             long long nm, hipStream_t stream) {
+  hipLaunchKernelGGL(kla_state_copy_kernel, dim3(grid_for(nl + nm)), dim3(256), 0, stream, lam0, M0, lamT,
+                     MT, nl, nm);
+  return hipGetLastError();
+}
+
+}  // namespace kla

@@ -1,0 +1,132 @@
+/*
+ * kla.h — C ABI of the Kalman Linear Attention (KLA) forward scan for AMD
+ * MI355X (gfx950).
+ *
+ * Method (gist.science summaries of arXiv 2602.10743, "Kalman Linear
+ * Attention"; [KLA-nl] = "Technische Samenvatting: Kalman Linear Attention
+ * (KLA)"): sequence mixing as exact Bayesian filtering in a diagonal
+ * linear-Gaussian state-space model.  Per head (b,h), key channel i and value
+ * channel j, one scalar filter:
+ *
+ *   prior   x_t = a_t x_{t-1} + w_t, w_t ~ N(0, pbar_t), a_t = exp(log_decay_t)
+ *           ([KLA-nl] §1, "Dynamics Prior": exactly discretised OU process)
+ *   evidence v_{t,j} = k_{t,i} x_{t,ij} + e, e of precision Lambda^v_{t,i}
+ *           ([KLA-nl] §1, "Observatiemodel")
+ *   output  y_{t,j} = sum_i q_{t,i} mu_{t,ij} (posterior mean; §1 "Readout")
+ *
+ * The posterior precision follows the Möbius map of [KLA-nl] §2
+ * ("Parallelisatie via Möbius-transformaties", precision equation)
+ *   lambda_t = ((1 + c pbar) lambda_{t-1} + c a^2) / (pbar lambda_{t-1} + a^2),
+ *   c = k^2 Lambda^v,
+ * evaluated as a scan of 2x2 projective matrices; the posterior mean follows
+ * the affine recursion mu_t = f_t mu_{t-1} + g_t v_t with the precision-ratio
+ * gates f = a lambda^-_t / lambda_t and g = k Lambda^v / lambda_t ([KLA-nl] §3,
+ * "Niet-lineaire Gating vanuit Onzekerheid").
+ *
+ * Conventions for every entry point:
+ *   - All tensors are dense, row-major, on the device, not aliased, and owned
+ *     by the caller.  The library never allocates or frees device memory and
+ *     never synchronises; work is enqueued on `stream` (a hipStream_t; NULL
+ *     means the default stream) and the call returns without waiting.
+ *   - Argument validation happens on the host before any HIP call; a
+ *     non-zero return means nothing was enqueued.  KLA_ERR_HIP means a launch
+ *     failed; kla_status_string() then returns the HIP error text.
+ *   - Device data is not checked: lambda0 must be positive and every input
+ *     finite, otherwise outputs are unspecified (typically NaN).
+ *   - A workspace is device memory of at least the size the matching
+ *     *_workspace_bytes() function returns, 256-byte aligned, zero-filled once
+ *     by kla_workspace_init() before its first use and not touched by the
+ *     caller afterwards.  Calls that share one workspace must be ordered on one
+ *     stream; concurrent calls on one workspace race.
+ */
+#ifndef KLA_H_
+#define KLA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KLA_F32 = 0, KLA_BF16 = 1 } kla_dtype;
+
+typedef enum {
+  KLA_OK = 0,
+  KLA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, bad alignment        */
+  KLA_ERR_UNSUPPORTED = 2,  /* d_k / d_v / dtype outside the supported set  */
+  KLA_ERR_WORKSPACE = 3,    /* workspace missing, misaligned or too small   */
+  KLA_ERR_HIP = 4           /* a HIP call failed (text via status string)   */
+} kla_status;
+
+/* Bytes of workspace kla_forward needs for this shape; 0 if the shape is
+ * invalid or unsupported. */
+size_t kla_forward_workspace_bytes(int B, int H, int T, int dk, int dv);
+
+/*
+ * KLA forward pass over T tokens of B*H independent heads.
+ *
+ * Inputs (dtype = KLA_BF16: bfloat16 values; KLA_F32: float32):
+ *   q, k, log_decay, proc_noise, val_prec   [B,H,T,dk]
+ *   v                                       [B,H,T,dv]
+ *   log_decay is log a_t (a_t = exp(log_decay) <= 1 expected), proc_noise is
+ *   the process-noise variance pbar_t >= 0, val_prec is Lambda^v_t >= 0.
+ * State in (float32, nullable):
+ *   lambda0 [B,H,dk]      posterior precision before token 1 (NULL: all 1)
+ *   M0      [B,H,dk,dv]   posterior mean before token 1     (NULL: all 0)
+ * Outputs:
+ *   y          [B,H,T,dv]  dtype; readout of the posterior mean after token t
+ *   lambda_T   [B,H,dk]    float32 precision after the last token
+ *   M_T        [B,H,dk,dv] float32 posterior mean after the last token
+ *   lambda_path [B,H,T,dk] float32 precision after every token (NULL: skipped)
+ * (lambda_T, M_T) fed back as (lambda0, M0) continue the scan exactly: two
+ * calls over T1 and T2 tokens equal one call over T1 + T2 up to rounding.
+ * T = 0 copies the state in to the state out; the per-token arrays are then
+ * not accessed and may be NULL.
+ *
+ * Supported: dk, dv in {16, 32, 64, 128}; B, H >= 1; T >= 0;
+ * B*H*T*max(dk,dv) < 2^31.  Arithmetic: float32 gates and scan; the bf16 path
+ * feeds the chunk contractions to bf16 matrix cores with float32 accumulation.
+ */
+int kla_forward(const void* q, const void* k, const void* v,
+                const void* log_decay, const void* proc_noise, const void* val_prec,
+                const float* lambda0, const float* M0,
+                void* y, float* lambda_T, float* M_T, float* lambda_path,
+                int B, int H, int T, int dk, int dv, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace kla_precision_scan needs; 0 if the shape is invalid. */
+size_t kla_precision_scan_workspace_bytes(int B, int H, int T, int D);
+
+/*
+ * Precision path only: B*H*D independent Möbius chains of length T
+ * ([KLA-nl] §2, precision equation), float32 throughout.
+ *   log_decay, proc_noise, obs_prec [B,H,T,D]   obs_prec = c_t = k_t^2 Lambda^v_t
+ *   lambda0     [B,H,D]   nullable (NULL: all 1)
+ *   lambda_path [B,H,T,D] precision after every token (required)
+ *   lambda_T    [B,H,D]   precision after the last token (nullable)
+ * Supported: D >= 1, B*H*T*D < 2^62, B*H*D < 2^31.  With T = 0 only lambda0
+ * and lambda_T are accessed (the other arrays may be NULL).
+ */
+int kla_precision_scan(const float* log_decay, const float* proc_noise, const float* obs_prec,
+                       const float* lambda0, float* lambda_path, float* lambda_T,
+                       int B, int H, int T, int D,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Zero-fills a workspace on `stream` (a fill kernel, no memset node), once
+ * before its first use.  bytes must be a multiple of 4. */
+int kla_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Reads (synchronously, with hipMemcpy) the device-side error word of a
+ * workspace: 0 = no error; 1 = a workgroup gave up waiting for a predecessor
+ * (the outputs of that call are then unspecified).  For tests and debugging. */
+int kla_workspace_error(const void* workspace, int* error_out);
+
+/* Static text for a status code; for KLA_ERR_HIP, the last HIP error text
+ * recorded on the calling thread. */
+const char* kla_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KLA_H_ */

@@ -32,7 +32,8 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "workload", "round_bf16", "bf16_bits",
-    "make_forward_inputs", "make_precision_inputs", "make_precision_inputs_torch",
+    "make_forward_inputs", "make_forward_inputs_torch", "make_precision_inputs",
+    "make_precision_inputs_torch",
     "softplus",
 ]
 
@@ -196,3 +197,49 @@ def make_precision_inputs_torch(*, B: int, H: int, T: int, D: int, seed: int = 1
         del kk, lv
     lam0 = torch.ones((B, H, D), dtype=torch.float32, device=device)
     return {"log_decay": ld, "proc_noise": pn, "obs_prec": op, "lambda0": lam0, "seed": seed}
+
+
+def make_forward_inputs_torch(w: Workload | int | str, *, seed=None, device="cuda", dtype=None):
+    """Device-side seeded inputs of a forward workload at its full shape, for
+    shapes the host generates slowly (long_bf16 draws 400 M values).
+
+    Same recipe as :func:`make_forward_inputs`, drawn with torch's generator on
+    ``device`` (values differ from the host version).  Returns torch tensors in
+    the workload dtype (bf16: rounded to nearest even by the cast), plus
+    float32 lambda0 = 1 and M0 = 0.
+    """
+    import torch
+    if not isinstance(w, Workload):
+        w = workload(w)
+    seed = w.seed if seed is None else seed
+    dtype = w.dtype if dtype is None else dtype
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    gens = []
+    for i in range(7):
+        g = torch.Generator(device=device)
+        g.manual_seed(seed * 16 + i)
+        gens.append(g)
+    sp = torch.nn.functional.softplus
+    sk, sv = (B, H, T, dk), (B, H, T, dv)
+
+    def rn(shape, g):
+        return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+
+    out = {
+        "q": (rn(sk, gens[0]) / dk ** 0.5).to(tdt),
+        "k": (rn(sk, gens[1]) / dk ** 0.5).to(tdt),
+        "v": rn(sv, gens[2]).to(tdt),
+        "log_decay": (-sp(rn(sk, gens[3]) + w.decay_mean)).to(tdt),
+        "proc_noise": (sp(rn(sk, gens[4])) + 1e-3).to(tdt),
+    }
+    vp = sp(rn(sk, gens[5])) + 1e-3
+    if w.spike_frac > 0.0:
+        mask = torch.rand((B, H, T), generator=gens[6], device=device) < w.spike_frac
+        vp = torch.where(mask[..., None], vp * w.spike_scale, vp)
+    out["val_prec"] = vp.to(tdt)
+    out["lambda0"] = torch.ones((B, H, dk), dtype=torch.float32, device=device)
+    out["M0"] = torch.zeros((B, H, dk, dv), dtype=torch.float32, device=device)
+    out["dtype"] = dtype
+    out["seed"] = seed
+    return out

@@ -1,0 +1,106 @@
+"""The C ABI library loads, exports every symbol include/kla.h declares, and
+rejects bad arguments on the host before any HIP call (CPU only)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kla.h")
+
+KLA_OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
+KLA_OK_T0 = KLA_OK  # T = 0 without lambda_T: nothing to do, no HIP call
+
+
+@pytest.fixture(scope="module")
+def K():
+    import bius_scan_sequence_amd as K
+    return K
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("kla_forward", "kla_forward_workspace_bytes", "kla_precision_scan",
+              "kla_precision_scan_workspace_bytes", "kla_workspace_init", "kla_workspace_error",
+              "kla_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(K):
+    out = subprocess.run(["nm", "-D", "--defined-only", K.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(K.lib, n)
+
+
+def test_status_strings(K):
+    for code in (0, 1, 2, 3, 4, 99):
+        assert isinstance(K.kla_status_string(code), str) and K.kla_status_string(code)
+
+
+def test_workspace_sizes(K):
+    assert K.kla_forward_workspace_bytes(8, 8, 2048, 64, 64) > 256
+    assert K.kla_forward_workspace_bytes(1, 1, 0, 16, 16) >= 256
+    assert K.kla_forward_workspace_bytes(1, 1, 256, 48, 16) == 0     # unsupported width
+    assert K.kla_forward_workspace_bytes(0, 1, 256, 16, 16) == 0     # empty batch
+    assert K.kla_precision_scan_workspace_bytes(1, 1024, 65536, 64) >= 256
+    assert K.kla_precision_scan_workspace_bytes(1, 1, 65536, 64) > 256  # few chains: T split
+    assert K.kla_precision_scan_workspace_bytes(1, 1, 10, 0) == 0
+
+
+A = 0x10000  # an aligned fake device address; validation never dereferences it
+
+
+def fwd(K, **over):
+    args = dict(q=A, k=A, v=A, log_decay=A, proc_noise=A, val_prec=A, lambda0=None, M0=None,
+                y=A, lambda_T=A, M_T=A, lambda_path=None, B=1, H=1, T=64, dk=16, dv=16, dtype=1,
+                workspace=A, workspace_bytes=1 << 30, stream=None)
+    args.update(over)
+    return K.kla_forward(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), INVALID), (dict(v=None), INVALID), (dict(y=None), INVALID),
+    (dict(lambda_T=None), INVALID), (dict(M_T=None), INVALID),
+    (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(T=-5), INVALID),
+    (dict(dk=48), UNSUPPORTED), (dict(dv=8), UNSUPPORTED), (dict(dk=256), UNSUPPORTED),
+    (dict(dtype=7), UNSUPPORTED),
+    (dict(q=A + 2), INVALID), (dict(log_decay=A + 8), INVALID),
+    (dict(lambda0=A + 2), INVALID),
+    (dict(workspace=None), WORKSPACE), (dict(workspace=A + 64), WORKSPACE),
+    (dict(workspace_bytes=16), WORKSPACE),
+    (dict(B=1 << 16, H=1 << 16, T=1024), INVALID),
+])
+def test_forward_rejects(K, over, code):
+    assert fwd(K, **over) == code
+
+
+def pscan(K, **over):
+    args = dict(log_decay=A, proc_noise=A, obs_prec=A, lambda0=None, lambda_path=A, lambda_T=None,
+                B=1, H=4, T=128, D=64, workspace=A, workspace_bytes=1 << 30, stream=None)
+    args.update(over)
+    return K.kla_precision_scan(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(log_decay=None), INVALID), (dict(lambda_path=None), INVALID),
+    (dict(T=0, lambda_path=None, log_decay=None), KLA_OK_T0),
+    (dict(D=0), INVALID), (dict(T=-1), INVALID), (dict(obs_prec=A + 1), INVALID),
+    (dict(workspace=None), WORKSPACE), (dict(workspace_bytes=8), WORKSPACE),
+])
+def test_precision_scan_rejects(K, over, code):
+    assert pscan(K, **over) == code
+
+
+def test_workspace_init_rejects(K):
+    assert K.kla_workspace_init(None, 1024, None) == WORKSPACE
+    assert K.kla_workspace_init(A + 4, 1024, None) == WORKSPACE
+    assert K.kla_workspace_init(A, 1022, None) == INVALID

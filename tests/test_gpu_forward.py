@@ -1,0 +1,200 @@
+"""GPU parity of kla_forward against the float64 oracle (needs an MI355X).
+
+Every case prints its name, seed and shape before touching the GPU.  Inputs are
+the seeded workload recipes (kla_inputs); the oracle consumes exactly the
+values handed to the GPU (bf16-rounded for bf16 workloads).  Tolerances are
+those of tests/kla_testutil.py.
+"""
+import numpy as np
+import pytest
+
+import kla_inputs as KI
+from kla_testutil import (check_bf16, check_f32, check_forward, gpu_forward, oracle_forward, say,
+                          to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import torch
+    import bius_scan_sequence_amd as K
+    assert torch.cuda.is_available()
+    yield K
+    torch.cuda.synchronize()
+
+
+def run_case(name, x, with_path=True):
+    say(f"[case] {name}: seed={x['seed']} shape q={x['q'].shape} v={x['v'].shape} dtype={x['dtype']}")
+    xd = to_dev(x)
+    got = gpu_forward(xd, return_lambda_path=with_path)
+    ref = oracle_forward(x, return_lambda_path=with_path)
+    stats = check_forward(x, got, ref, x["dtype"])
+    say(f"[ok] {name}: " + ", ".join(f"{k}={v:.2e}" for k, v in stats.items()))
+    return got, ref
+
+
+# ----------------------------------------------------------------------------- workloads
+def test_tiny_f32_full():
+    run_case("tiny_f32", KI.make_forward_inputs("tiny_f32"))
+
+
+def test_lm45m_bf16_full():
+    run_case("lm45m_bf16", KI.make_forward_inputs("lm45m_bf16"))
+
+
+def test_lm180m_bf16_full():
+    run_case("lm180m_bf16", KI.make_forward_inputs("lm180m_bf16"), with_path=False)
+
+
+def test_long_bf16_full_size_sampled_heads():
+    """long_bf16 at its full shape (B=2, H=16, T=16384, d=128), generated on the
+    device; the oracle checks two sampled heads over all 16384 tokens."""
+    import torch
+    import bius_scan_sequence_amd as K
+    w = KI.workload("long_bf16")
+    say(f"[case] long_bf16 full size: seed={w.seed} B={w.B} H={w.H} T={w.T} d={w.dk}")
+    xd = KI.make_forward_inputs_torch(w)
+    y, lT, MT = K.forward(xd["q"], xd["k"], xd["v"], xd["log_decay"], xd["proc_noise"], xd["val_prec"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed)
+    for flat in rng.choice(w.B * w.H, size=2, replace=False):
+        b, h = divmod(int(flat), w.H)
+        x = {n: xd[n][b:b + 1, h:h + 1].float().cpu().numpy() for n in
+             ("q", "k", "v", "log_decay", "proc_noise", "val_prec")}
+        x["dtype"] = "bf16"
+        ref = oracle_forward(x)
+        got = (y[b:b + 1, h:h + 1].float().cpu().numpy(), lT[b:b + 1, h:h + 1].cpu().numpy(),
+               MT[b:b + 1, h:h + 1].cpu().numpy())
+        stats = check_forward(x, got, ref, "bf16")
+        say(f"[ok] long_bf16 head ({b},{h}): " + ", ".join(f"{k}={v:.2e}" for k, v in stats.items()))
+    del xd, y, lT, MT
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------- shapes
+SHAPES = [
+    # (B, H, T, dk, dv, dtype)
+    (1, 1, 1, 16, 16, "f32"),
+    (1, 2, 17, 16, 32, "f32"),
+    (2, 1, 65, 32, 64, "f32"),
+    (1, 3, 200, 64, 32, "f32"),
+    (1, 1, 130, 128, 128, "f32"),
+    (1, 1, 96, 64, 128, "f32"),
+    (1, 1, 1, 64, 64, "bf16"),
+    (2, 2, 63, 16, 16, "bf16"),
+    (1, 2, 64, 32, 128, "bf16"),
+    (1, 1, 129, 128, 64, "bf16"),
+    (2, 3, 300, 64, 64, "bf16"),
+    (1, 1, 1000, 128, 128, "bf16"),
+    (1, 2, 777, 16, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_shapes_ragged(shape):
+    B, H, T, dk, dv, dt = shape
+    w = KI.workload("lm180m_bf16" if dt == "bf16" else "tiny_f32")
+    x = KI.make_forward_inputs(w, B=B, H=H, T=T, dk=dk, dv=dv, seed=7000 + T + dk, dtype=dt)
+    run_case(f"shape {shape}", x)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_nondefault_initial_state(dt):
+    x = KI.make_forward_inputs("tiny_f32", B=2, H=2, T=150, dk=32, dv=16, seed=71, dtype=dt)
+    rng = np.random.default_rng(5)
+    x["lambda0"] = (0.2 + 3 * rng.random((2, 2, 32))).astype(np.float32)
+    x["M0"] = rng.standard_normal((2, 2, 32, 16)).astype(np.float32)
+    run_case(f"initial state {dt}", x)
+
+
+def test_t_zero_copies_state():
+    import torch
+    import bius_scan_sequence_amd as K
+    say("[case] T=0 state copy")
+    x = KI.make_forward_inputs("lm45m_bf16", B=1, H=2, T=0, dk=64, dv=32)
+    xd = to_dev(x)
+    lam0 = torch.rand((1, 2, 64), device="cuda") + 0.5
+    M0 = torch.randn((1, 2, 64, 32), device="cuda")
+    y, lT, MT = K.forward(xd["q"], xd["k"], xd["v"], xd["log_decay"], xd["proc_noise"], xd["val_prec"],
+                          lam0, M0)
+    torch.cuda.synchronize()
+    assert y.shape == (1, 2, 0, 32)
+    assert torch.equal(lT, lam0) and torch.equal(MT, M0)
+    y, lT, MT = K.forward(xd["q"], xd["k"], xd["v"], xd["log_decay"], xd["proc_noise"], xd["val_prec"])
+    torch.cuda.synchronize()
+    assert torch.all(lT == 1) and torch.all(MT == 0)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_state_carry_resumes(dt):
+    """Two calls with the state passed on equal one call over all tokens."""
+    import torch
+    import bius_scan_sequence_amd as K
+    say(f"[case] state carry {dt}")
+    x = KI.make_forward_inputs("lm45m_bf16", B=2, H=2, T=700, dk=64, dv=64, seed=99, dtype=dt)
+    xd = to_dev(x)
+    names = ("q", "k", "v", "log_decay", "proc_noise", "val_prec")
+    y, lT, MT = K.forward(*(xd[n] for n in names))
+    T1 = 333
+    y1, l1, M1 = K.forward(*(xd[n][:, :, :T1].contiguous() for n in names))
+    y2, l2, M2 = K.forward(*(xd[n][:, :, T1:].contiguous() for n in names), l1, M1)
+    torch.cuda.synchronize()
+    ref = oracle_forward(x)
+    got = (torch.cat([y1, y2], 2).float().cpu().numpy(), l2.cpu().numpy(), M2.cpu().numpy())
+    check_forward(x, got, ref, dt)
+    if dt == "f32":
+        check_f32("carry vs single y", got[0], y.cpu().numpy(), per_head_floor=True)
+    else:
+        check_bf16("carry vs single y", got[0], y.float().cpu().numpy())
+    say(f"[ok] state carry {dt}")
+
+
+def test_deterministic_bitwise():
+    """Repeated calls give identical bits (carries are folded in a fixed order
+    whatever predecessor a look-back stops at)."""
+    import torch
+    import bius_scan_sequence_amd as K
+    say("[case] determinism lm45m_bf16")
+    x = KI.make_forward_inputs("lm45m_bf16")
+    xd = to_dev(x)
+    names = ("q", "k", "v", "log_decay", "proc_noise", "val_prec")
+    first = K.forward(*(xd[n] for n in names))
+    for _ in range(5):
+        again = K.forward(*(xd[n] for n in names))
+        torch.cuda.synchronize()
+        for a, b in zip(first, again):
+            assert torch.equal(a, b)
+    ws = K._default_workspace(xd["q"].device, torch.cuda.current_stream().cuda_stream)
+    assert ws.error() == 0
+    say("[ok] determinism")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_extreme_decay_exact_path(dt):
+    """Chunks whose in-chunk decay underflows 2^-64 on some channel take the
+    exact scalar path for their intra-chunk scores."""
+    x = KI.make_forward_inputs("tiny_f32", B=1, H=2, T=160, dk=32, dv=16, seed=123, dtype=dt)
+    ld = x["log_decay"].copy()
+    ld[0, 0, 20:40, 3] = -9.0      # e^-9 per token: far below 2^-64 within a chunk
+    ld[0, 1, 100:112, :] = -12.0
+    ld[0, 1, 70, 5] = -60.0        # one token wipes a channel's memory
+    x["log_decay"] = KI.round_bf16(ld) if dt == "bf16" else ld.astype(np.float32)
+    run_case(f"extreme decay {dt}", x)
+
+
+def test_precision_only_inputs_shared_over_value_channels():
+    """The precision path of kla_forward does not depend on q, v or M0."""
+    import torch
+    import bius_scan_sequence_amd as K
+    say("[case] precision independent of q/v")
+    x = KI.make_forward_inputs("lm45m_bf16", B=1, H=2, T=300)
+    xd = to_dev(x)
+    _, l1, _, p1 = K.forward(xd["q"], xd["k"], xd["v"], xd["log_decay"], xd["proc_noise"], xd["val_prec"],
+                             return_lambda_path=True)
+    _, l2, _, p2 = K.forward(-xd["q"], xd["k"], 2 * xd["v"], xd["log_decay"], xd["proc_noise"],
+                             xd["val_prec"], None, torch.ones((1, 2, 64, 64), device="cuda"),
+                             return_lambda_path=True)
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p2) and torch.equal(l1, l2)
+    say("[ok] precision independent of q/v")
