@@ -25,7 +25,7 @@ size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 constexpr size_t kHeader = 256;
 
 struct FwdLayout {
-  size_t pflag, mflag, pagg, pinc, mF, magg, minc, total;
+  size_t hdone, pflag, mflag, pagg, pinc, mF, magg, minc, total;
 };
 
 bool fwd_shape_ok(int B, int H, int T, int dk, int dv) {
@@ -39,6 +39,7 @@ FwdLayout fwd_layout(int B, int H, int T, int dk, int dv, int nseg) {
   const size_t slots = (size_t)B * H * nseg;
   FwdLayout l;
   size_t o = kHeader;
+  l.hdone = o; o += round256((size_t)B * H * 4);
   l.pflag = o; o += round256(slots * 4);
   l.mflag = o; o += round256(slots * 4);
   l.pagg = o; o += round256(slots * dk * 16);
@@ -57,7 +58,7 @@ int fwd_nseg(int T, int dk, int dv, bool bf16) {
 
 struct PscanPlan {
   int ncblocks, nseg, seglen;
-  size_t flag, agg, inc, total;
+  size_t bdone, flag, agg, inc, total;
 };
 
 bool pscan_shape_ok(int B, int H, int T, int D) {
@@ -86,6 +87,7 @@ PscanPlan pscan_plan(int B, int H, int T, int D) {
   pl.nseg = T > 0 ? (T + seglen - 1) / seglen : 1;
   const size_t slots = (size_t)pl.ncblocks * pl.nseg;
   size_t o = kHeader;
+  pl.bdone = o; o += round256((size_t)pl.ncblocks * 4);
   pl.flag = o; o += round256(slots * 4);
   if (pl.nseg > 1) {
     pl.agg = o; o += round256(slots * 256 * 16);
@@ -151,6 +153,7 @@ extern "C" int kla_forward(const void* q, const void* k, const void* v, const vo
   p.lam0 = lambda0; p.M0 = M0; p.y = y; p.lamT = lambda_T; p.MT = M_T; p.lpath = lambda_path;
   p.nheads = (int)nheads; p.T = T; p.nseg = nseg;
   p.ctrl = reinterpret_cast<unsigned*>(ws);
+  p.hdone = reinterpret_cast<unsigned*>(ws + l.hdone);
   p.pflag = reinterpret_cast<unsigned*>(ws + l.pflag);
   p.mflag = reinterpret_cast<unsigned*>(ws + l.mflag);
   p.pagg = reinterpret_cast<float*>(ws + l.pagg);
@@ -192,6 +195,7 @@ extern "C" int kla_precision_scan(const float* log_decay, const float* proc_nois
   p.nchains = chains; p.D = D; p.T = T;
   p.nseg = pl.nseg; p.seglen = pl.seglen; p.ncblocks = pl.ncblocks;
   p.ctrl = reinterpret_cast<unsigned*>(ws);
+  p.bdone = reinterpret_cast<unsigned*>(ws + pl.bdone);
   p.flag = reinterpret_cast<unsigned*>(ws + pl.flag);
   p.agg = reinterpret_cast<float*>(ws + pl.agg);
   p.inc = reinterpret_cast<float*>(ws + pl.inc);

@@ -24,12 +24,16 @@ constexpr int kSpinLimit = 1 << 25;
 __device__ __forceinline__ float to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 
-// float32 -> bfloat16, round to nearest even (finite inputs; NaN stays NaN).
+// float32 -> bfloat16, round to nearest even, by the hardware conversion
+// (v_cvt_pk_bf16_f32 converts two values per instruction).
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v2s bf16x2(float a, float b) {
+  return __builtin_bit_cast(v2s, __builtin_convertvector(v2f{a, b}, v2bf));
+}
 __device__ __forceinline__ uint16_t bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return (uint16_t)__builtin_bit_cast(short, static_cast<__bf16>(x));
 }
 
 template <typename In> __device__ __forceinline__ In from_f32(float x);
@@ -68,26 +72,22 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-struct SFrag {  // split fp32 block: hi and lo bf16 parts
-  v4s hi, lo;
-};
-
-__device__ __forceinline__ SFrag split4(v4f x) {
-  SFrag f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint16_t h = bf16_rne(x[e]);
-    f.hi[e] = (short)h;
-    f.lo[e] = (short)bf16_rne(x[e] - to_f32(h));
-  }
-  return f;
+// hi = bf16(x) (nearest even), lo = bf16(x - hi): about 16 mantissa bits together.
+__device__ __forceinline__ void split4(v4f x, v4s& hi, v4s& lo) {
+  const v2s h01 = bf16x2(x[0], x[1]), h23 = bf16x2(x[2], x[3]);
+  const v2s l01 = bf16x2(x[0] - to_f32((uint16_t)h01[0]), x[1] - to_f32((uint16_t)h01[1]));
+  const v2s l23 = bf16x2(x[2] - to_f32((uint16_t)h23[0]), x[3] - to_f32((uint16_t)h23[1]));
+  hi = v4s{h01[0], h01[1], h23[0], h23[1]};
+  lo = v4s{l01[0], l01[1], l23[0], l23[1]};
 }
+__device__ __forceinline__ v8s cat(v4s a, v4s b) { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
+// first / second half of a split block: the hi part / the lo part
+__device__ __forceinline__ v4s part_hi(v8s a) { return __builtin_shufflevector(a, a, 0, 1, 2, 3); }
+__device__ __forceinline__ v4s part_lo(v8s a) { return __builtin_shufflevector(a, a, 4, 5, 6, 7); }
 
-__device__ __forceinline__ v4f mma_x32(v4f acc, v4s a0, v4s a1, v4s b0, v4s b1) {
-  const v8s a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-  const v8s b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b),
-                                                 acc, 0, 0, 0);
+__device__ __forceinline__ v4f mma_x32(v4f acc, v8s a, v8s b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), acc,
+                                                 0, 0, 0);
 }
 __device__ __forceinline__ v4f mma_f32(v4f acc, v4f a, v4f b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
@@ -98,40 +98,52 @@ __device__ __forceinline__ v4f mma_f32(v4f acc, v4f a, v4f b) {
 }
 
 // Operand policy per input dtype.
-//   Op  : a gated fp32 operand block (split for bf16 inputs, plain for fp32)
-//   VOp : an operand block read from the inputs (exact in its own dtype)
+//   Op   one K=16 block of a gated fp32 operand.  bf16 inputs: the block's hi
+//        and lo parts as one 8-element vector [hi0..3 | lo0..3] (so an A-side
+//        block feeds v_mfma_f32_16x16x32_bf16 as it is loaded); fp32 inputs:
+//        the four fp32 values.
+//   VOp  one block read from the inputs, exact in its own dtype.
+// Stored operands keep this layout in LDS: 16 bytes per block (bf16) or
+// 16 bytes per 4 values (fp32), so one aligned 16-byte load fetches a block.
 template <bool BF16> struct Mma;
 
 template <> struct Mma<true> {
-  using Op = SFrag;
+  using Op = v8s;
   using VOp = v4s;
-  static __device__ __forceinline__ Op op(v4f x) { return split4(x); }
+  static __device__ __forceinline__ Op op(v4f x) {
+    v4s h, l;
+    split4(x, h, l);
+    return cat(h, l);
+  }
+  static __device__ __forceinline__ Op get(const unsigned char* p) { return *reinterpret_cast<const v8s*>(p); }
+  static __device__ __forceinline__ void put(unsigned char* p, v4f x) { *reinterpret_cast<v8s*>(p) = op(x); }
   static __device__ __forceinline__ VOp vop(const uint16_t* p, int stride) {
     return v4s{(short)p[0], (short)p[stride], (short)p[2 * stride], (short)p[3 * stride]};
   }
-  // acc += sum_b A[b] . B[b], both operands split.
+  // acc += sum_b A[b] . B[b]; each product takes hi*hi + lo*hi + hi*lo.
   template <int NB>
   static __device__ __forceinline__ v4f dot(v4f acc, const Op (&A)[NB], const Op (&B)[NB]) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc = mma_x32(acc, A[b].hi, A[b].lo, B[b].hi, B[b].hi);
+    for (int b = 0; b < NB; ++b) acc = mma_x32(acc, A[b], cat(part_hi(B[b]), part_hi(B[b])));
 #pragma unroll
-    for (int b = 0; b + 1 < NB; b += 2) acc = mma_x32(acc, A[b].hi, A[b + 1].hi, B[b].lo, B[b + 1].lo);
+    for (int b = 0; b + 1 < NB; b += 2)
+      acc = mma_x32(acc, cat(part_hi(A[b]), part_hi(A[b + 1])), cat(part_lo(B[b]), part_lo(B[b + 1])));
     if (NB % 2) {  // odd leftover: x32 with a zero second half
       const v4s z = v4s{0, 0, 0, 0};
-      acc = mma_x32(acc, A[NB - 1].hi, z, B[NB - 1].lo, z);
+      acc = mma_x32(acc, cat(part_hi(A[NB - 1]), z), cat(part_lo(B[NB - 1]), z));
     }
     return acc;
   }
   // acc += A . V, A split, V exact.
-  static __device__ __forceinline__ v4f dotv(v4f acc, const Op& A, VOp V) {
-    return mma_x32(acc, A.hi, A.lo, V, V);
-  }
+  static __device__ __forceinline__ v4f dotv(v4f acc, const Op& A, VOp V) { return mma_x32(acc, A, cat(V, V)); }
 };
 
 template <> struct Mma<false> {
   using Op = v4f;
   using VOp = v4f;
   static __device__ __forceinline__ Op op(v4f x) { return x; }
+  static __device__ __forceinline__ Op get(const unsigned char* p) { return *reinterpret_cast<const v4f*>(p); }
+  static __device__ __forceinline__ void put(unsigned char* p, v4f x) { *reinterpret_cast<v4f*>(p) = x; }
   static __device__ __forceinline__ VOp vop(const float* p, int stride) {
     return v4f{p[0], p[stride], p[2 * stride], p[3 * stride]};
   }
@@ -162,21 +174,25 @@ __device__ __forceinline__ Mob mob_identity() { return Mob{1.f, 0.f, 0.f, 1.f}; 
 // Rescale by a power of two so the largest entry lies in [0.5, 1): exact, and
 // a projective matrix is unchanged by any positive scale.
 __device__ __forceinline__ Mob mob_normalize(Mob m) {
-  float mx = fmaxf(fmaxf(m.m00, m.m01), fmaxf(m.m10, m.m11));
+  float mx = __builtin_fmaxf(__builtin_fmaxf(m.m00, m.m01), __builtin_fmaxf(m.m10, m.m11));
   int e = __builtin_amdgcn_frexp_expf(mx);
   return Mob{__builtin_amdgcn_ldexpf(m.m00, -e), __builtin_amdgcn_ldexpf(m.m01, -e),
              __builtin_amdgcn_ldexpf(m.m10, -e), __builtin_amdgcn_ldexpf(m.m11, -e)};
 }
 
-// step(a2, pb, c) . P, normalised.
-__device__ __forceinline__ Mob mob_step(Mob P, float a2, float pb, float c) {
-  const float al = fmaf(c, pb, 1.f), be = c * a2;
+// step(a2, pb, c) . P as two row operations (predict, then update); not
+// normalised: callers normalise every second step, which keeps every entry
+// far inside the fp32 range for any finite coefficients of realistic size.
+__device__ __forceinline__ Mob mob_step_raw(Mob P, float a2, float pb, float c) {
   Mob n;
-  n.m00 = fmaf(al, P.m00, be * P.m10);
-  n.m01 = fmaf(al, P.m01, be * P.m11);
-  n.m10 = fmaf(pb, P.m00, a2 * P.m10);
+  n.m10 = fmaf(pb, P.m00, a2 * P.m10);  // predict: row1 <- pb*row0 + a2*row1
   n.m11 = fmaf(pb, P.m01, a2 * P.m11);
-  return mob_normalize(n);
+  n.m00 = fmaf(c, n.m10, P.m00);        // update:  row0 <- row0 + c*row1
+  n.m01 = fmaf(c, n.m11, P.m01);
+  return n;
+}
+__device__ __forceinline__ Mob mob_step(Mob P, float a2, float pb, float c) {
+  return mob_normalize(mob_step_raw(P, a2, pb, c));
 }
 
 // A . B (B applied first), normalised.
@@ -203,73 +219,88 @@ __device__ __forceinline__ float lam_step(float lam, float a2, float pb, float c
 }
 
 // ----------------------------------------------------------------------------
-// Inter-workgroup publication (decoupled look-back).  Payload stores are
-// ordinary stores followed by an agent-scope release fence in every writing
-// thread; the flag is stored with release semantics by one thread after a
-// workgroup barrier.  Readers poll with acquire loads, then every reading
-// thread issues an agent-scope acquire fence before touching the payload.
+// Inter-workgroup publication (decoupled look-back).
+// Payloads and flags are written and read with agent-coherent accesses
+// (the sc1 cache policy that agent-scope atomics use), so no cache-wide write
+// back or invalidate is needed:
+//   publish: every writing thread stores its part of the payload coherently
+//            and waits for its stores to complete; a workgroup barrier; one
+//            thread stores the flag coherently.
+//   consume: one thread polls the flag with coherent loads (sleeping between
+//            polls); a workgroup barrier; the threads load the payload
+//            coherently.
+// A payload store that has completed is visible to every coherent load on
+// the device, and the flag is stored only after all payload stores of the
+// workgroup completed, so a reader that sees the flag sees the payload.
 // ----------------------------------------------------------------------------
-__device__ __forceinline__ unsigned ld_acquire(const unsigned* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+constexpr int kCoherent = 16;  // buffer cache-policy operand: sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ void st_release(unsigned* p, unsigned v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, v4f x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, x), r, (int)off, 0, kCoherent);
 }
-__device__ __forceinline__ void fence_release() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+__device__ __forceinline__ v4f ld_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoherent));
 }
-__device__ __forceinline__ void fence_acquire() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+__device__ __forceinline__ void st_coherent(float* p, float x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned ld_relaxed(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this thread's outstanding memory operations have completed.
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 
 // Walk back from segment `s - 1` to the nearest predecessor that has published
 // its inclusive carry (flag == finc); predecessors that have published only
 // their own aggregate (flag == fagg) are stepped over.  Segment 0 always
-// publishes an inclusive carry, so the walk ends.  Returns the index found.
-// Called by one thread.
-__device__ inline int lookback_find(const unsigned* flags, int s, unsigned fagg, unsigned finc,
+// publishes an inclusive carry, so the walk ends.  `stride` is the distance
+// between the flags of consecutive segments.  Called by one thread; on giving
+// up after kSpinLimit polls it records an error and returns.
+__device__ inline int lookback_find(const unsigned* flags, int stride, int s, unsigned fagg, unsigned finc,
                                     unsigned* ctrl) {
   int r = s - 1;
   int spins = 0;
-  while (r > 0) {
-    unsigned f = ld_acquire(flags + r);
-    if (f == finc) return r;
-    if (f == fagg) {
+  while (true) {
+    const unsigned f = ld_relaxed(flags + (size_t)r * stride);
+    if (f == finc) break;
+    if (f == fagg && r > 0) {
       --r;
       continue;
     }
     if (++spins > kSpinLimit) {
-      __hip_atomic_store(ctrl + kError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return r;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-  // r == 0: wait for segment 0's inclusive carry.
-  while (ld_acquire(flags) != finc) {
-    if (++spins > kSpinLimit) {
-      __hip_atomic_store(ctrl + kError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      st_relaxed(ctrl + kError, 1u);
       break;
     }
     __builtin_amdgcn_s_sleep(1);
   }
-  return 0;
+  return r;
 }
 
-// Workgroup order: a ticket taken at start, so every workgroup a segment waits
-// on has started before it (no wait on a workgroup that cannot be scheduled).
-__device__ __forceinline__ unsigned take_ticket(unsigned* ctrl) {
-  return __hip_atomic_fetch_add(ctrl + kTicket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Last workgroup out resets the ticket and exit counters and advances the
-// epoch, so flags of this call never match the next call's.
-__device__ __forceinline__ void finish_call(unsigned* ctrl, unsigned epoch, unsigned nblocks) {
-  unsigned old = __hip_atomic_fetch_add(ctrl + kDone, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  if (old == nblocks - 1) {
-    __hip_atomic_store(ctrl + kDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(ctrl + kTicket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(ctrl + kEpoch, epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  }
+// Call epochs.  Every workgroup reads the workspace epoch e before touching
+// flags, so flags of this call (values 2e+2, 2e+3) never match those left by
+// earlier calls, whatever their shapes.  Workgroups are grouped (the segments
+// of one head, or of one chain block); each counts itself done in its group
+// after its last flag access, the last of a group counts the group done, and
+// the last group resets the counters and advances the epoch for the next call.
+enum CtrlEpoch { kEpoch = 0, kGroupsDone = 1 };
+__device__ __forceinline__ void epoch_done(unsigned* ctrl, unsigned* group_done, unsigned group_size,
+                                           unsigned ngroups, unsigned e) {
+  if (__hip_atomic_fetch_add(group_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != group_size - 1) return;
+  st_relaxed(group_done, 0u);
+  if (__hip_atomic_fetch_add(ctrl + kGroupsDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ngroups - 1)
+    return;
+  st_relaxed(ctrl + kGroupsDone, 0u);
+  st_relaxed(ctrl + kEpoch, e + 1u);
 }
 
 }  // namespace kla

@@ -50,11 +50,16 @@ struct FwdCfg {
   static constexpr int NRT = DK / 16;                                   // state row tiles
   static constexpr int NCT = DV / 16;                                   // state col tiles
   static constexpr int CPW = (NCT + 3) / 4;                             // col tiles per wave
-  static constexpr int QLD = DK + 4;                                    // padded Qs/Ks row (floats)
-  static constexpr int KDT_LD = L + 4;                                  // padded Kd^T row (floats)
+  // Stored operands: 16 bytes per 4 consecutive values (bf16: [hi x4 | lo x4];
+  // fp32: the 4 values), rows padded by 16 bytes against bank conflicts.
+  static constexpr int QROW = DK * 4 + 16;                              // Qs / Ks row (bytes)
+  static constexpr int KROW = L * 4 + 16;                               // Kd^T row (bytes)
   static constexpr int RAW_BYTES = 5 * L * DK * (int)sizeof(In);        // q, k, ld, pn, vp
-  static constexpr int OPS_BYTES = (2 * L * QLD + DK * KDT_LD) * 4;     // Qs, Ks, Kd^T (fp32)
+  static constexpr int OPS_BYTES = 2 * L * QROW + DK * KROW;            // Qs, Ks, Kd^T
   static constexpr int UNION_BYTES = RAW_BYTES > OPS_BYTES ? RAW_BYTES : OPS_BYTES;
+  static constexpr int A_BYTES = NCH * 64 * 16;                         // per chunk: scores, A-operand order
+  static constexpr int PAGG_BYTES = NG * DK * 16;
+  static constexpr int AP_BYTES = A_BYTES > PAGG_BYTES ? A_BYTES : PAGG_BYTES;
   static_assert(TG % 16 == 0, "walker groups must own whole chunks");
 };
 
@@ -62,31 +67,29 @@ template <int DK, int DV, bool BF16>
 struct FwdSmem {
   using C = FwdCfg<DK, DV, BF16>;
   using In = typename C::In;
-  // Staged raw inputs q, k, ld, pn, vp ([L][DK] each) until the gate walk is
-  // done; afterwards the fp32 operands Qs [L][QLD], Ks [L][QLD], Kd^T [DK][KDT_LD].
+  // Raw inputs q, k, ld, pn, vp ([L][DK] each) until the gate walk is done;
+  // afterwards the stored operands Qs [L][QROW], Ks [L][QROW], Kd^T [DK][KROW].
   alignas(16) unsigned char u[C::UNION_BYTES];
-  alignas(16) In v[C::L * DV];     // raw v
-  float scr_f[16 * DK];            // slow path: f, g of one chunk
-  float scr_g[16 * DK];
-  float cpe[C::NCH * DK];          // per chunk: prod of f over the chunk
-  float lamc[C::NCH * DK];         // per chunk: precision entering the chunk
-  float pagg[C::NG * DK * 4];      // walker-group aggregates (2x2 per channel)
-  float lam_in[DK];                // precision entering the segment
-  float fseg[DK];                  // prod of f over the segment
-  float S[16 * 16];                // slow-path intra-chunk scores S[t][u]
+  alignas(16) In v[C::L * DV];             // raw v; staged y at the end
+  // Walker-group 2x2 aggregates until the gate walk starts; then the causal
+  // intra-chunk scores of every chunk in A-operand order.
+  alignas(16) unsigned char ap[C::AP_BYTES];
+  alignas(16) float cpe[C::NCH * DK];      // per chunk: prod of f over the chunk
+  float lamc[C::NCH * DK];                 // per chunk: precision entering the chunk
+  alignas(16) float lam_in[DK];            // precision entering the segment
+  alignas(16) float fseg[DK];              // prod of f over the segment
+  float red[2 * 256];                      // exact path: per-wave partial sums
   int unsafe[C::NCH];
   int ctl[4];
 
   __device__ In* raw(int which) { return reinterpret_cast<In*>(u) + which * C::L * DK; }
-  __device__ float* Qs() { return reinterpret_cast<float*>(u); }
-  __device__ float* Ks() { return reinterpret_cast<float*>(u) + C::L * C::QLD; }
-  __device__ float* KdT() { return reinterpret_cast<float*>(u) + 2 * C::L * C::QLD; }
+  __device__ float* pagg() { return reinterpret_cast<float*>(ap); }
 };
 
-// Copy one [rows x width] tile (contiguous in global memory) into LDS, zero
-// rows past `nvalid` (zeros are an identity filter step: a = 1, pbar = 0, c = 0,
-// and contribute nothing to y).  16-byte units; width*sizeof(In) is a
-// multiple of 32 bytes for every supported width.
+// Copy one [rows x width] tile between global memory and LDS (16-byte units;
+// width*sizeof(In) is a multiple of 32 bytes for every supported width).
+// Loads zero rows past `nvalid`: zeros are an identity filter step (a = 1,
+// pbar = 0, c = 0) and contribute nothing to y.
 template <typename In, int ROWS, int WIDTH>
 __device__ __forceinline__ void stage_tile(In* dst, const In* src, int nvalid, int tid) {
   constexpr int UNITS = ROWS * WIDTH * (int)sizeof(In) / 16;
@@ -106,8 +109,36 @@ __device__ __forceinline__ void stage_tile(In* dst, const In* src, int nvalid, i
     if (u < UNITS) d4[u] = buf[it];
   }
 }
+template <typename In, int ROWS, int WIDTH>
+__device__ __forceinline__ void unstage_tile(In* dst, const In* src, int nvalid, int tid) {
+  constexpr int PER_UNIT = 16 / (int)sizeof(In);
+  const int valid_units = nvalid * WIDTH / PER_UNIT;
+  const uint4* s4 = reinterpret_cast<const uint4*>(src);
+  uint4* d4 = reinterpret_cast<uint4*>(dst);
+  for (int u = tid; u < valid_units; u += 256) d4[u] = s4[u];
+}
 
 __device__ __forceinline__ v4f ld4(const float* p) { return *reinterpret_cast<const v4f*>(p); }
+
+// Sum over the 64 lanes of a wave, in a fixed order.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// One stored value of a 4-value block: bf16 hi at byte 2*j, lo at 8 + 2*j;
+// fp32 at byte 4*j.
+template <bool BF16>
+__device__ __forceinline__ void put1(unsigned char* block, int j, float x) {
+  if constexpr (BF16) {
+    const uint16_t h = bf16_rne(x);
+    reinterpret_cast<uint16_t*>(block)[j] = h;
+    reinterpret_cast<uint16_t*>(block)[4 + j] = bf16_rne(x - to_f32(h));
+  } else {
+    reinterpret_cast<float*>(block)[j] = x;
+  }
+}
 
 template <int DK, int DV, bool BF16>
 __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
@@ -116,31 +147,22 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
   using M = Mma<BF16>;
   using Op = typename M::Op;
   constexpr int L = C::L, NCH = C::NCH, NG = C::NG, TG = C::TG, CPG = C::CPG;
-  constexpr int NRT = C::NRT, NCT = C::NCT, CPW = C::CPW, QLD = C::QLD, KDT_LD = C::KDT_LD;
+  constexpr int NRT = C::NRT, NCT = C::NCT, CPW = C::CPW, QROW = C::QROW, KROW = C::KROW;
   __shared__ FwdSmem<DK, DV, BF16> s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lc = lane & 15;  // lane group (k block) / lane column
-  const unsigned nblocks = gridDim.x;
-
-  // ---------------------------------------------------------------- ticket
-  if (tid == 0) {
-    unsigned e = __hip_atomic_load(p.ctrl + kEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned tk = take_ticket(p.ctrl) % nblocks;
-    s.ctl[0] = (int)tk;
-    s.ctl[1] = (int)e;
-  }
-  if (tid < NCH) s.unsafe[tid] = 0;
-  __syncthreads();
-  const int ticket = s.ctl[0];
-  const unsigned epoch = (unsigned)s.ctl[1];
-  const unsigned FAGG = 2u * epoch + 2u, FINC = 2u * epoch + 3u;
   const int nheads = p.nheads, T = p.T, nseg = p.nseg;
-  const int seg = ticket / nheads, head = ticket % nheads;
+  // Segment-major order: every segment a workgroup waits on has a lower index.
+  const int seg = blockIdx.x / nheads, head = blockIdx.x % nheads;
   const int t0 = seg * L;
   const int nvalid = min(L, T - t0);
   const bool last = (seg == nseg - 1);
   const size_t hs = (size_t)head * nseg + seg;  // (head, segment) slot
+  const size_t hb = (size_t)head * nseg;
+
+  if (tid == 0) s.ctl[1] = nseg > 1 ? (int)ld_relaxed(p.ctrl + kEpoch) : 0;
+  if (tid < NCH) s.unsafe[tid] = 0;
 
   In* const rq = s.raw(0);
   In* const rk = s.raw(1);
@@ -159,72 +181,72 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
     stage_tile<In, L, DV>(s.v, static_cast<const In*>(p.v) + offv, nvalid, tid);
   }
   __syncthreads();
+  const unsigned epoch = (unsigned)s.ctl[1];
+  const unsigned FAGG = 2u * epoch + 2u, FINC = 2u * epoch + 3u;
 
   // ---------------------------------------------------------------- 1. group aggregates
   const int wi = tid % DK, wr = tid / DK;
   const bool walker = wr < NG;
   if (walker) {
     Mob P = mob_identity();
-    for (int t = wr * TG; t < (wr + 1) * TG; ++t) {
-      const int x = t * DK + wi;
-      const float kk = to_f32(rk[x]), a = __expf(to_f32(rld[x]));
-      const float c = kk * kk * to_f32(rvp[x]);
-      P = mob_step(P, a * a, to_f32(rpn[x]), c);
+#pragma unroll
+    for (int e = 0; e < TG; e += 2) {
+      const int x0 = (wr * TG + e) * DK + wi, x1 = x0 + DK;
+      const float k0 = to_f32(rk[x0]), a0 = __expf(to_f32(rld[x0]));
+      const float k1 = to_f32(rk[x1]), a1 = __expf(to_f32(rld[x1]));
+      P = mob_step_raw(P, a0 * a0, to_f32(rpn[x0]), k0 * k0 * to_f32(rvp[x0]));
+      P = mob_normalize(mob_step_raw(P, a1 * a1, to_f32(rpn[x1]), k1 * k1 * to_f32(rvp[x1])));
     }
-    float* d = s.pagg + (wr * DK + wi) * 4;
-    d[0] = P.m00; d[1] = P.m01; d[2] = P.m10; d[3] = P.m11;
+    *reinterpret_cast<v4f*>(s.pagg() + (wr * DK + wi) * 4) = v4f{P.m00, P.m01, P.m10, P.m11};
   }
   __syncthreads();
 
   // ---------------------------------------------------------------- 2. precision carry
   Mob Pseg = mob_identity();
   if (tid < DK) {
+#pragma unroll
     for (int r = 0; r < NG; ++r) {
-      const float* d = s.pagg + (r * DK + tid) * 4;
+      const v4f d = ld4(s.pagg() + (r * DK + tid) * 4);
       Pseg = mob_mul(Mob{d[0], d[1], d[2], d[3]}, Pseg);
     }
   }
   float lam_in = 1.f;
   if (seg == 0) {
-    if (tid < DK) lam_in = p.lam0 ? p.lam0[(size_t)head * DK + tid] : 1.f;
+    if (tid < DK) {
+      lam_in = p.lam0 ? p.lam0[(size_t)head * DK + tid] : 1.f;
+      if (!last) st_coherent(p.pinc + hs * DK + tid, mob_apply(Pseg, lam_in));
+    }
     if (!last) {
-      if (tid < DK) {
-        p.pinc[hs * DK + tid] = mob_apply(Pseg, lam_in);
-        fence_release();
-      }
+      wait_stores();
       __syncthreads();
-      if (tid == 0) st_release(p.pflag + hs, FINC);
+      if (tid == 0) st_relaxed(p.pflag + hs, FINC);
     }
   } else {
     if (!last) {  // publish the aggregate first so successors need not wait on us
       if (tid < DK) {
-        float4* d = reinterpret_cast<float4*>(p.pagg) + hs * DK + tid;
-        *d = make_float4(Pseg.m00, Pseg.m01, Pseg.m10, Pseg.m11);
-        fence_release();
+        const auto r = coherent_rsrc(p.pagg + hs * DK * 4, DK * 16);
+        st_coherent(r, tid * 16, v4f{Pseg.m00, Pseg.m01, Pseg.m10, Pseg.m11});
       }
+      wait_stores();
       __syncthreads();
-      if (tid == 0) st_release(p.pflag + hs, FAGG);
+      if (tid == 0) st_relaxed(p.pflag + hs, FAGG);
     }
-    if (tid == 0) s.ctl[2] = lookback_find(p.pflag + (size_t)head * nseg, seg, FAGG, FINC, p.ctrl);
+    if (tid == 0) s.ctl[2] = lookback_find(p.pflag + hb, 1, seg, FAGG, FINC, p.ctrl);
     __syncthreads();
     const int r0 = s.ctl[2];
     if (tid < DK) {
-      fence_acquire();
-      const size_t hb = (size_t)head * nseg;
-      float lam = p.pinc[(hb + r0) * DK + tid];
+      float lam = ld_coherent(p.pinc + (hb + r0) * DK + tid);
       for (int u = r0 + 1; u < seg; ++u) {
-        const float4 m = reinterpret_cast<const float4*>(p.pagg)[(hb + u) * DK + tid];
-        lam = mob_apply(Mob{m.x, m.y, m.z, m.w}, lam);
+        const v4f m = ld_coherent(coherent_rsrc(p.pagg + (hb + u) * DK * 4, DK * 16), tid * 16);
+        lam = mob_apply(Mob{m[0], m[1], m[2], m[3]}, lam);
       }
       lam_in = lam;
-      if (!last) {
-        p.pinc[hs * DK + tid] = mob_apply(Pseg, lam_in);
-        fence_release();
-      }
+      if (!last) st_coherent(p.pinc + hs * DK + tid, mob_apply(Pseg, lam_in));
     }
     if (!last) {
+      wait_stores();
       __syncthreads();
-      if (tid == 0) st_release(p.pflag + hs, FINC);
+      if (tid == 0) st_relaxed(p.pflag + hs, FINC);
     }
   }
   if (tid < DK) s.lam_in[tid] = lam_in;
@@ -232,13 +254,16 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
 
   // ---------------------------------------------------------------- 3. gate walk
   // Results stay in registers until every walker has finished reading the raw
-  // inputs, then overwrite them as fp32 operands.
+  // inputs, then overwrite them as stored operands.
   float wq[TG], wk[TG], wd[TG];
   if (walker) {
     float lam = s.lam_in[wi];
-    for (int r = 0; r < wr; ++r) {
-      const float* d = s.pagg + (r * DK + wi) * 4;
-      lam = mob_apply(Mob{d[0], d[1], d[2], d[3]}, lam);
+#pragma unroll
+    for (int r = 0; r < NG - 1; ++r) {
+      if (r < wr) {
+        const v4f d = ld4(s.pagg() + (r * DK + wi) * 4);
+        lam = mob_apply(Mob{d[0], d[1], d[2], d[3]}, lam);
+      }
     }
 #pragma unroll
     for (int cl = 0; cl < CPG; ++cl) {
@@ -250,13 +275,14 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
       for (int e = 0; e < 16; ++e) {
         const int t = cc * 16 + e;
         const int x = t * DK + wi;
-        const float kk = to_f32(rk[x]), vpv = to_f32(rvp[x]);
+        const float kk = to_f32(rk[x]);
+        const float kv = kk * to_f32(rvp[x]);
         const float a = __expf(to_f32(rld[x]));
         float lam_pred;
-        const float lam_new = lam_step(lam, a * a, to_f32(rpn[x]), kk * kk * vpv, lam_pred);
+        const float lam_new = lam_step(lam, a * a, to_f32(rpn[x]), kk * kv, lam_pred);
         const float inv = fast_rcp(lam_new);
         const float f = a * lam_pred * inv;
-        const float g = kk * vpv * inv;
+        const float g = kv * inv;
         cp *= f;
         wq[cl * 16 + e] = to_f32(rq[x]) * cp;
         wk[cl * 16 + e] = g * fast_rcp(cp);
@@ -277,26 +303,102 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
     if (last && wr == NG - 1) p.lamT[(size_t)head * DK + wi] = lam;
   }
   __syncthreads();
-  float* const Qs = s.Qs();
-  float* const Ks = s.Ks();
-  float* const KdT = s.KdT();
+  unsigned char* const Qs = s.u;
+  unsigned char* const Ks = s.u + L * QROW;
+  unsigned char* const KdT = s.u + 2 * L * QROW;
   if (walker) {
+    const int cb = (wi >> 2) * 16, cj = wi & 3;  // block and slot of channel wi in a row
 #pragma unroll
     for (int e = 0; e < TG; ++e) {
       const int t = wr * TG + e;
-      Qs[t * QLD + wi] = wq[e];
-      Ks[t * QLD + wi] = wk[e];
-      KdT[wi * KDT_LD + t] = wd[e];
+      put1<BF16>(Qs + t * QROW + cb, cj, wq[e]);
+      put1<BF16>(Ks + t * QROW + cb, cj, wk[e]);
     }
+#pragma unroll
+    for (int e = 0; e < TG; e += 4)  // Kd^T row wi: four tokens per block
+      M::put(KdT + wi * KROW + (wr * TG + e) * 4, v4f{wd[e], wd[e + 1], wd[e + 2], wd[e + 3]});
   }
   if (tid < DK) {
     float F = 1.f;
+#pragma unroll
     for (int cc = 0; cc < NCH; ++cc) F *= s.cpe[cc * DK + tid];
     s.fseg[tid] = F;
   }
   __syncthreads();
 
-  // ---------------------------------------------------------------- 4. chunk loop
+  // ---------------------------------------------------------------- 4a. intra-chunk scores
+  // A[t][u] = sum_i Qs[t][i] Ks[u][i] for u <= t (0 above the diagonal),
+  // stored in A-operand order: lane l, element e -> A[t = l%16][u = 4*(l/16) + e].
+  // A chunk flagged unsafe gets exact scores instead: each channel lane
+  // re-derives f, g of its channel (same instructions as the walk, raw inputs
+  // from global memory) and the channels are summed with wave reductions, in
+  // a fixed order.
+  unsigned char* const A = s.ap;
+  for (int cc = 0; cc < NCH; ++cc) {
+    if (!s.unsafe[cc]) continue;  // uniform: every thread reads the same flag
+    float f[16], g[16], q[16];
+    const bool chan = tid < DK;
+    if (chan) {
+      float lam = s.lamc[cc * DK + tid];
+      for (int e = 0; e < 16; ++e) {
+        const int t = cc * 16 + e;
+        float kk = 0.f, ldv = 0.f, pnv = 0.f, vpv = 0.f, qv = 0.f;
+        if (t < nvalid) {
+          const size_t gx = ((size_t)head * T + t0 + t) * DK + tid;
+          kk = to_f32(static_cast<const In*>(p.k)[gx]);
+          ldv = to_f32(static_cast<const In*>(p.ld)[gx]);
+          pnv = to_f32(static_cast<const In*>(p.pn)[gx]);
+          vpv = to_f32(static_cast<const In*>(p.vp)[gx]);
+          qv = to_f32(static_cast<const In*>(p.q)[gx]);
+        }
+        const float kv = kk * vpv;
+        const float a = __expf(ldv);
+        float lam_pred;
+        const float lam_new = lam_step(lam, a * a, pnv, kk * kv, lam_pred);
+        const float inv = fast_rcp(lam_new);
+        f[e] = a * lam_pred * inv;
+        g[e] = kv * inv;
+        q[e] = qv;
+        lam = lam_new;
+      }
+    }
+    // pair (t, u), u <= t: sum over channels of q_t g_u prod_{w=u+1..t} f_w
+    for (int uu = 0; uu < 16; ++uu) {
+      float d = chan ? g[uu] : 0.f;
+      for (int tt = uu; tt < 16; ++tt) {
+        if (tt > uu) d *= chan ? f[tt] : 0.f;
+        const float part = wave_sum(chan ? q[tt] * d : 0.f);
+        if (lane == 0 && wave < (DK + 63) / 64) s.red[wave * 256 + tt * 16 + uu] = part;
+      }
+    }
+    __syncthreads();
+    {
+      const int tt = tid >> 4, uu = tid & 15;
+      float acc = 0.f;
+      if (uu <= tt)
+        for (int w = 0; w < (DK + 63) / 64; ++w) acc += s.red[w * 256 + tt * 16 + uu];
+      put1<BF16>(A + (cc * 64 + tt + 16 * (uu >> 2)) * 16, uu & 3, acc);
+    }
+    __syncthreads();
+  }
+  for (int cc = wave; cc < NCH; cc += 4) {
+    if (s.unsafe[cc]) continue;
+    Op qo[NRT], ko[NRT];
+#pragma unroll
+    for (int mt = 0; mt < NRT; ++mt) {
+      qo[mt] = M::get(Qs + (cc * 16 + lc) * QROW + (16 * mt + 4 * lg) * 4);
+      ko[mt] = M::get(Ks + (cc * 16 + lc) * QROW + (16 * mt + 4 * lg) * 4);
+    }
+    // D[u][t] = sum_i Ks[u][i] Qs[t][i]: lane l, element e holds S[t = l%16][u = 4*(l/16) + e]
+    v4f st = M::dot(v4f{0.f, 0.f, 0.f, 0.f}, ko, qo);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * lg + e > lc) st[e] = 0.f;  // causal: u <= t
+    M::put(A + (cc * 64 + lane) * 16, st);
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- 4b. chunk loop
   v4f yl[NCH][CPW];
   v4f Macc[NRT][CPW];
 #pragma unroll
@@ -304,92 +406,31 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int mt = 0; mt < NRT; ++mt) Macc[mt][pp] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  if (wave < NCT) {
 #pragma unroll
-  for (int cc = 0; cc < NCH; ++cc) {
-    const bool unsafe = s.unsafe[cc] != 0;
-    if (unsafe) {
-      // Exact intra-chunk scores: re-walk the chunk from its entering precision
-      // (same instructions as the walk above, raw inputs from global memory),
-      // then S[t][u] = sum_i q_ti g_ui prod_{w=u+1..t} f_wi by plain products.
-      if (tid < DK) {
-        float lam = s.lamc[cc * DK + tid];
-        for (int e = 0; e < 16; ++e) {
-          const int t = cc * 16 + e;
-          float kk = 0.f, ldv = 0.f, pnv = 0.f, vpv = 0.f;
-          if (t < nvalid) {
-            const size_t gx = ((size_t)head * T + t0 + t) * DK + tid;
-            kk = to_f32(static_cast<const In*>(p.k)[gx]);
-            ldv = to_f32(static_cast<const In*>(p.ld)[gx]);
-            pnv = to_f32(static_cast<const In*>(p.pn)[gx]);
-            vpv = to_f32(static_cast<const In*>(p.vp)[gx]);
+    for (int cc = 0; cc < NCH; ++cc) {
+      const Op ao = M::get(A + (cc * 64 + lane) * 16);
+      Op qo[NRT];
+#pragma unroll
+      for (int mt = 0; mt < NRT; ++mt) qo[mt] = M::get(Qs + (cc * 16 + lc) * QROW + (16 * mt + 4 * lg) * 4);
+#pragma unroll
+      for (int pp = 0; pp < CPW; ++pp) {
+        const int nt = wave + 4 * pp;
+        if (nt < NCT) {
+          // V block: rows u = cc*16 + 4*lg + e, column 16*nt + lc.
+          const typename M::VOp vo = M::vop(s.v + (cc * 16 + 4 * lg) * DV + 16 * nt + lc, DV);
+          v4f acc = M::dotv(v4f{0.f, 0.f, 0.f, 0.f}, ao, vo);
+          Op mo[NRT];
+#pragma unroll
+          for (int mt = 0; mt < NRT; ++mt) mo[mt] = M::op(Macc[mt][pp]);
+          acc = M::dot(acc, qo, mo);
+          yl[cc][pp] = acc;
+#pragma unroll
+          for (int mt = 0; mt < NRT; ++mt) {
+            const v4f m = Macc[mt][pp] * ld4(s.cpe + cc * DK + 16 * mt + 4 * lg);
+            const Op kdo = M::get(KdT + (16 * mt + lc) * KROW + (cc * 16 + 4 * lg) * 4);
+            Macc[mt][pp] = M::dotv(m, kdo, vo);
           }
-          const float a = __expf(ldv);
-          float lam_pred;
-          const float lam_new = lam_step(lam, a * a, pnv, kk * kk * vpv, lam_pred);
-          const float inv = fast_rcp(lam_new);
-          s.scr_f[e * DK + tid] = a * lam_pred * inv;
-          s.scr_g[e * DK + tid] = kk * vpv * inv;
-          lam = lam_new;
-        }
-      }
-      __syncthreads();
-      {
-        const int tt = tid >> 4, uu = tid & 15;
-        float acc = 0.f;
-        const int t = cc * 16 + tt;
-        if (uu <= tt && t < nvalid) {
-          const In* qrow = static_cast<const In*>(p.q) + ((size_t)head * T + t0 + t) * DK;
-          for (int i = 0; i < DK; ++i) {
-            float d = s.scr_g[uu * DK + i];
-            for (int w = uu + 1; w <= tt; ++w) d *= s.scr_f[w * DK + i];
-            acc = fmaf(to_f32(qrow[i]), d, acc);
-          }
-        }
-        s.S[tt * 16 + uu] = acc;
-      }
-      __syncthreads();
-    }
-
-    // Qs blocks of this chunk: lane -> token cc*16 + lc, channels 16*mt + 4*lg + e.
-    Op qo[NRT];
-#pragma unroll
-    for (int mt = 0; mt < NRT; ++mt) qo[mt] = M::op(ld4(Qs + (cc * 16 + lc) * QLD + 16 * mt + 4 * lg));
-
-    // Intra-chunk scores, transposed: st[e] = S[t = lc][u = 4*lg + e].
-    v4f st = v4f{0.f, 0.f, 0.f, 0.f};
-    if (!unsafe) {
-      Op ko[NRT];
-#pragma unroll
-      for (int mt = 0; mt < NRT; ++mt) ko[mt] = M::op(ld4(Ks + (cc * 16 + lc) * QLD + 16 * mt + 4 * lg));
-      st = M::dot(st, ko, qo);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) st[e] = s.S[lc * 16 + 4 * lg + e];
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (4 * lg + e > lc) st[e] = 0.f;  // causal: u <= t
-    const Op ao = M::op(st);
-
-#pragma unroll
-    for (int pp = 0; pp < CPW; ++pp) {
-      const int nt = wave + 4 * pp;
-      if (nt < NCT) {
-        // V block: rows u = cc*16 + 4*lg + e, column 16*nt + lc.
-        const typename M::VOp vo = M::vop(s.v + (cc * 16 + 4 * lg) * DV + 16 * nt + lc, DV);
-        v4f acc = M::dotv(v4f{0.f, 0.f, 0.f, 0.f}, ao, vo);
-        Op mo[NRT];
-#pragma unroll
-        for (int mt = 0; mt < NRT; ++mt) mo[mt] = M::op(Macc[mt][pp]);
-        acc = M::dot(acc, qo, mo);
-        yl[cc][pp] = acc;
-#pragma unroll
-        for (int mt = 0; mt < NRT; ++mt) {
-          v4f m = Macc[mt][pp];
-          const v4f ce = ld4(s.cpe + cc * DK + 16 * mt + 4 * lg);
-          m = m * ce;
-          const Op kdo = M::op(ld4(KdT + (16 * mt + lc) * KDT_LD + cc * 16 + 4 * lg));
-          Macc[mt][pp] = M::dotv(m, kdo, vo);
         }
       }
     }
@@ -397,11 +438,12 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
 
   // ---------------------------------------------------------------- 5. mean carry
   // Each lane owns, per tile (mt, nt), rows 16*mt + 4*lg + e of column 16*nt + lc.
-  // Workspace payloads are stored in this fragment order, one float4 per lane.
-  const size_t MSZ = (size_t)DK * DV;
-  auto frag_index = [&](int mt, int nt) -> size_t { return ((size_t)(nt * NRT + mt) * 64 + lane) * 4; };
+  // Workspace payloads are stored in this fragment order, 16 bytes per lane.
+  constexpr uint32_t MBYTES = (uint32_t)DK * DV * 4;
+  auto frag_off = [&](int mt, int nt) -> uint32_t { return ((uint32_t)(nt * NRT + mt) * 64 + lane) * 16; };
   v4f Min[NRT][CPW];
-  auto publish_inclusive = [&]() {
+  auto store_inclusive = [&]() {
+    const auto r = coherent_rsrc(p.minc + hs * DK * DV, MBYTES);
 #pragma unroll
     for (int pp = 0; pp < CPW; ++pp) {
       const int nt = wave + 4 * pp;
@@ -412,13 +454,13 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
           v4f o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = fmaf(F[e], Min[mt][pp][e], Macc[mt][pp][e]);
-          *reinterpret_cast<v4f*>(p.minc + hs * MSZ + frag_index(mt, nt)) = o;
+          st_coherent(r, frag_off(mt, nt), o);
         }
       }
     }
-    fence_release();
+    wait_stores();
     __syncthreads();
-    if (tid == 0) st_release(p.mflag + hs, FINC);
+    if (tid == 0) st_relaxed(p.mflag + hs, FINC);
   };
   if (seg == 0) {
 #pragma unroll
@@ -428,34 +470,32 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
       for (int mt = 0; mt < NRT; ++mt) {
         v4f m = v4f{0.f, 0.f, 0.f, 0.f};
         if (nt < NCT && p.M0) {
-          const float* src = p.M0 + (size_t)head * MSZ + (size_t)(16 * mt + 4 * lg) * DV + 16 * nt + lc;
+          const float* src = p.M0 + (size_t)head * DK * DV + (size_t)(16 * mt + 4 * lg) * DV + 16 * nt + lc;
           m = v4f{src[0], src[DV], src[2 * DV], src[3 * DV]};
         }
         Min[mt][pp] = m;
       }
     }
-    if (!last) publish_inclusive();
+    if (!last) store_inclusive();
   } else {
     if (!last) {
-      if (tid < DK) p.mF[hs * DK + tid] = s.fseg[tid];
+      if (tid < DK) st_coherent(p.mF + hs * DK + tid, s.fseg[tid]);
+      const auto r = coherent_rsrc(p.magg + hs * DK * DV, MBYTES);
 #pragma unroll
       for (int pp = 0; pp < CPW; ++pp) {
         const int nt = wave + 4 * pp;
         if (nt < NCT) {
 #pragma unroll
-          for (int mt = 0; mt < NRT; ++mt)
-            *reinterpret_cast<v4f*>(p.magg + hs * MSZ + frag_index(mt, nt)) = Macc[mt][pp];
+          for (int mt = 0; mt < NRT; ++mt) st_coherent(r, frag_off(mt, nt), Macc[mt][pp]);
         }
       }
-      fence_release();
+      wait_stores();
       __syncthreads();
-      if (tid == 0) st_release(p.mflag + hs, FAGG);
+      if (tid == 0) st_relaxed(p.mflag + hs, FAGG);
     }
-    if (tid == 0) s.ctl[3] = lookback_find(p.mflag + (size_t)head * nseg, seg, FAGG, FINC, p.ctrl);
+    if (tid == 0) s.ctl[3] = lookback_find(p.mflag + hb, 1, seg, FAGG, FINC, p.ctrl);
     __syncthreads();
     const int r0 = s.ctl[3];
-    fence_acquire();
-    const size_t hb = (size_t)head * nseg;
 #pragma unroll
     for (int pp = 0; pp < CPW; ++pp) {
       const int nt = wave + 4 * pp;
@@ -463,10 +503,10 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
       for (int mt = 0; mt < NRT; ++mt) {
         v4f m = v4f{0.f, 0.f, 0.f, 0.f};
         if (nt < NCT) {
-          m = *reinterpret_cast<const v4f*>(p.minc + (hb + r0) * MSZ + frag_index(mt, nt));
+          m = ld_coherent(coherent_rsrc(p.minc + (hb + r0) * DK * DV, MBYTES), frag_off(mt, nt));
           for (int u = r0 + 1; u < seg; ++u) {
-            const v4f a = *reinterpret_cast<const v4f*>(p.magg + (hb + u) * MSZ + frag_index(mt, nt));
-            const v4f F = *reinterpret_cast<const v4f*>(p.mF + (hb + u) * DK + 16 * mt + 4 * lg);
+            const v4f a = ld_coherent(coherent_rsrc(p.magg + (hb + u) * DK * DV, MBYTES), frag_off(mt, nt));
+            const v4f F = ld_coherent(coherent_rsrc(p.mF + (hb + u) * DK, DK * 4), (16 * mt + 4 * lg) * 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) m[e] = fmaf(F[e], m[e], a[e]);
           }
@@ -474,8 +514,10 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
         Min[mt][pp] = m;
       }
     }
-    if (!last) publish_inclusive();
+    if (!last) store_inclusive();
   }
+  // Every flag access of this workgroup is done.
+  if (nseg > 1 && tid == 0) epoch_done(p.ctrl, p.hdone + head, (unsigned)nseg, (unsigned)nheads, epoch);
   if (last) {  // final state, row-major
 #pragma unroll
     for (int pp = 0; pp < CPW; ++pp) {
@@ -484,7 +526,7 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int mt = 0; mt < NRT; ++mt) {
           const v4f F = ld4(s.fseg + 16 * mt + 4 * lg);
-          float* dst = p.MT + (size_t)head * MSZ + (size_t)(16 * mt + 4 * lg) * DV + 16 * nt + lc;
+          float* dst = p.MT + (size_t)head * DK * DV + (size_t)(16 * mt + 4 * lg) * DV + 16 * nt + lc;
 #pragma unroll
           for (int e = 0; e < 4; ++e) dst[e * DV] = fmaf(F[e], Min[mt][pp][e], Macc[mt][pp][e]);
         }
@@ -493,16 +535,19 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
   }
 
   // ---------------------------------------------------------------- 6. correction + store
-  {
+  // y_t += Qs_t (diag(prod of earlier chunk decays) M_in), staged in LDS over v
+  // (dead once every wave has left the chunk loop) and written out in 16-byte
+  // units.
+  __syncthreads();
+  if (wave < NCT) {
     v4f decay[NRT];  // prod of chunk decays before chunk cc, per owned row
 #pragma unroll
     for (int mt = 0; mt < NRT; ++mt) decay[mt] = v4f{1.f, 1.f, 1.f, 1.f};
-    In* yout = static_cast<In*>(p.y) + ((size_t)head * T + t0) * DV;
 #pragma unroll
     for (int cc = 0; cc < NCH; ++cc) {
       Op qo[NRT];
 #pragma unroll
-      for (int mt = 0; mt < NRT; ++mt) qo[mt] = M::op(ld4(Qs + (cc * 16 + lc) * QLD + 16 * mt + 4 * lg));
+      for (int mt = 0; mt < NRT; ++mt) qo[mt] = M::get(Qs + (cc * 16 + lc) * QROW + (16 * mt + 4 * lg) * 4);
 #pragma unroll
       for (int pp = 0; pp < CPW; ++pp) {
         const int nt = wave + 4 * pp;
@@ -512,19 +557,15 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
           for (int mt = 0; mt < NRT; ++mt) mo[mt] = M::op(decay[mt] * Min[mt][pp]);
           const v4f acc = M::dot(yl[cc][pp], qo, mo);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = cc * 16 + 4 * lg + e;
-            if (t < nvalid) yout[(size_t)t * DV + 16 * nt + lc] = from_f32<In>(acc[e]);
-          }
+          for (int e = 0; e < 4; ++e) s.v[(cc * 16 + 4 * lg + e) * DV + 16 * nt + lc] = from_f32<In>(acc[e]);
         }
       }
 #pragma unroll
       for (int mt = 0; mt < NRT; ++mt) decay[mt] = decay[mt] * ld4(s.cpe + cc * DK + 16 * mt + 4 * lg);
     }
   }
-
   __syncthreads();
-  if (tid == 0) finish_call(p.ctrl, epoch, nblocks);
+  unstage_tile<In, L, DV>(static_cast<In*>(p.y) + ((size_t)head * T + t0) * DV, s.v, nvalid, tid);
 }
 
 // ------------------------------------------------------------------------------

@@ -7,7 +7,7 @@
 namespace kla {
 
 // Control words at the head of every workspace (32-bit each).
-enum CtrlWord { kEpoch = 0, kTicket = 1, kDone = 2, kError = 3 };
+enum CtrlWord { kError = 3 };
 
 struct FwdParams {
   const void* q;
@@ -24,6 +24,7 @@ struct FwdParams {
   float* lpath;       // nullable
   int nheads, T, nseg;
   unsigned* ctrl;     // workspace control words
+  unsigned* hdone;    // [nheads] segments of the head done with their flags
   unsigned* pflag;    // [nheads*nseg] precision-carry flags
   unsigned* mflag;    // [nheads*nseg] mean-carry flags
   float* pagg;        // [nheads*nseg][dk][4] segment 2x2 aggregates
@@ -43,7 +44,8 @@ struct PscanParams {
   long long nchains;  // B*H*D
   int D, T, nseg, seglen, ncblocks;
   unsigned* ctrl;
-  unsigned* flag;     // [ncblocks*nseg]
+  unsigned* bdone;    // [ncblocks] segments of the block done with their flags
+  unsigned* flag;     // [nseg*ncblocks]
   float* agg;         // [ncblocks*nseg*256][4]
   float* inc;         // [ncblocks*nseg*256]
 };

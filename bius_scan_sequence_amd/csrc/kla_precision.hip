@@ -22,17 +22,10 @@ constexpr int kPB = 8;  // tokens per prefetch block
 __global__ __launch_bounds__(256) void kla_pscan_kernel(PscanParams p) {
   __shared__ int sh[4];
   const int tid = threadIdx.x;
-  const unsigned nblocks = gridDim.x;
-  if (tid == 0) {
-    sh[1] = (int)__hip_atomic_load(p.ctrl + kEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh[0] = (int)(take_ticket(p.ctrl) % nblocks);
-  }
-  __syncthreads();
-  const int ticket = sh[0];
-  const unsigned epoch = (unsigned)sh[1];
-  const unsigned FAGG = 2u * epoch + 2u, FINC = 2u * epoch + 3u;
-  const int seg = ticket / p.ncblocks, cb = ticket % p.ncblocks;
   const int nseg = p.nseg;
+  // Segment-major order: every segment a workgroup waits on has a lower index.
+  const int seg = blockIdx.x / p.ncblocks, cb = blockIdx.x % p.ncblocks;
+  if (tid == 0) sh[1] = nseg > 1 ? (int)ld_relaxed(p.ctrl + kEpoch) : 0;
   const bool last = seg == nseg - 1;
   const long long chain = (long long)cb * 256 + tid;
   const bool valid = chain < p.nchains;
@@ -86,52 +79,42 @@ __global__ __launch_bounds__(256) void kla_pscan_kernel(PscanParams p) {
       }
     }
     // ---- publish and look back
+    __syncthreads();
+    const unsigned epoch = (unsigned)sh[1];
+    const unsigned FAGG = 2u * epoch + 2u, FINC = 2u * epoch + 3u;
     if (seg == 0) {
       if (!last) {
-        p.inc[cslot] = mob_apply(P, lam);
-        fence_release();
+        st_coherent(p.inc + cslot, mob_apply(P, lam));
+        wait_stores();
         __syncthreads();
-        if (tid == 0) st_release(p.flag + slot, FINC);
+        if (tid == 0) st_relaxed(p.flag + slot, FINC);
       }
     } else {
       if (!last) {
-        reinterpret_cast<float4*>(p.agg)[cslot] = make_float4(P.m00, P.m01, P.m10, P.m11);
-        fence_release();
+        st_coherent(coherent_rsrc(p.agg + slot * 256 * 4, 256 * 16), tid * 16, v4f{P.m00, P.m01, P.m10, P.m11});
+        wait_stores();
         __syncthreads();
-        if (tid == 0) st_release(p.flag + slot, FAGG);
+        if (tid == 0) st_relaxed(p.flag + slot, FAGG);
       }
       // flags of this chain block for segments 0..seg-1 sit ncblocks apart
-      if (tid == 0) {
-        int r = seg - 1, spins = 0, found = 0;
-        while (true) {
-          const unsigned f = ld_acquire(p.flag + (size_t)r * p.ncblocks + cb);
-          if (f == FINC) { found = r; break; }
-          if (f == FAGG && r > 0) { --r; continue; }
-          if (++spins > kSpinLimit) {
-            __hip_atomic_store(p.ctrl + kError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            found = r;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        sh[2] = found;
-      }
+      if (tid == 0) sh[2] = lookback_find(p.flag + cb, p.ncblocks, seg, FAGG, FINC, p.ctrl);
       __syncthreads();
       const int r0 = sh[2];
-      fence_acquire();
-      float x = p.inc[((size_t)r0 * p.ncblocks + cb) * 256 + tid];
+      float x = ld_coherent(p.inc + ((size_t)r0 * p.ncblocks + cb) * 256 + tid);
       for (int u = r0 + 1; u < seg; ++u) {
-        const float4 m = reinterpret_cast<const float4*>(p.agg)[((size_t)u * p.ncblocks + cb) * 256 + tid];
-        x = mob_apply(Mob{m.x, m.y, m.z, m.w}, x);
+        const v4f m = ld_coherent(coherent_rsrc(p.agg + ((size_t)u * p.ncblocks + cb) * 256 * 4, 256 * 16), tid * 16);
+        x = mob_apply(Mob{m[0], m[1], m[2], m[3]}, x);
       }
       lam = x;
       if (!last) {
-        p.inc[cslot] = mob_apply(P, lam);
-        fence_release();
+        st_coherent(p.inc + cslot, mob_apply(P, lam));
+        wait_stores();
         __syncthreads();
-        if (tid == 0) st_release(p.flag + slot, FINC);
+        if (tid == 0) st_relaxed(p.flag + slot, FINC);
       }
     }
+    // Every flag access of this workgroup is done.
+    if (tid == 0) epoch_done(p.ctrl, p.bdone + cb, (unsigned)nseg, (unsigned)p.ncblocks, epoch);
   }
 
   // ---- walk, writing the path
@@ -165,9 +148,6 @@ __global__ __launch_bounds__(256) void kla_pscan_kernel(PscanParams p) {
     }
   }
   if (last && valid && p.lamT) p.lamT[chain] = lam;
-
-  __syncthreads();
-  if (tid == 0) finish_call(p.ctrl, epoch, nblocks);
 }
 
 hipError_t launch_pscan(const PscanParams& p, hipStream_t stream) {
