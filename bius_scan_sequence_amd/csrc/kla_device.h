@@ -260,30 +260,39 @@ __device__ __forceinline__ void st_relaxed(unsigned* p, unsigned v) {
 // Wait until this thread's outstanding memory operations have completed.
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 
-// Walk back from segment `s - 1` to the nearest predecessor that has published
-// its inclusive carry (flag == finc); predecessors that have published only
-// their own aggregate (flag == fagg) are stepped over.  Segment 0 always
-// publishes an inclusive carry, so the walk ends.  `stride` is the distance
-// between the flags of consecutive segments.  Called by one thread; on giving
-// up after kSpinLimit polls it records an error and returns.
+// Find the nearest predecessor of segment `s` that has published its
+// inclusive carry (flag == finc) such that every segment between them has
+// published at least its aggregate (flag == fagg).  Segment 0 always
+// publishes an inclusive carry, so the search ends.  One wavefront polls a
+// window of 64 predecessors at once (lane j reads segment s-1-j), so a
+// look-back costs one memory round trip per window instead of one per
+// predecessor.  `stride` is the distance between the flags of consecutive
+// segments.  Called by all 64 lanes of one wavefront (uniform result); on
+// giving up after kSpinLimit polls it records an error and returns.
 __device__ inline int lookback_find(const unsigned* flags, int stride, int s, unsigned fagg, unsigned finc,
                                     unsigned* ctrl) {
-  int r = s - 1;
+  const int lane = threadIdx.x & 63;
+  int top = s - 1;  // newest predecessor of the current window
   int spins = 0;
   while (true) {
-    const unsigned f = ld_relaxed(flags + (size_t)r * stride);
-    if (f == finc) break;
-    if (f == fagg && r > 0) {
-      --r;
+    const int r = top - lane;
+    const unsigned f = r >= 0 ? ld_relaxed(flags + (size_t)r * stride) : 0u;
+    const unsigned long long inc = __ballot(r >= 0 && f == finc);
+    const unsigned long long ready = __ballot(r >= 0 && (f == finc || f == fagg));
+    if (inc) {
+      const int j = __builtin_ctzll(inc);  // nearest inclusive carry in the window
+      const unsigned long long below = j ? ((1ull << j) - 1) : 0ull;
+      if ((ready & below) == below) return top - j;
+    } else if (ready == ~0ull) {
+      top -= 64;  // the whole window holds aggregates only: look further back
       continue;
     }
     if (++spins > kSpinLimit) {
-      st_relaxed(ctrl + kError, 1u);
-      break;
+      if (lane == 0) st_relaxed(ctrl + kError, 1u);
+      return top;
     }
     __builtin_amdgcn_s_sleep(1);
   }
-  return r;
 }
 
 // Call epochs.  Every workgroup reads the workspace epoch e before touching

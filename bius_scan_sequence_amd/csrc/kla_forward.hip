@@ -33,6 +33,8 @@
 // A chunk whose in-chunk decay prod f falls below 2^-64 on some channel would
 // overflow Ks = g / cp; such a chunk takes an exact scalar path for its
 // intra-chunk scores instead.
+#include <type_traits>
+
 #include "kla_device.h"
 #include "kla_internal.h"
 
@@ -60,6 +62,13 @@ struct FwdCfg {
   static constexpr int A_BYTES = NCH * 64 * 16;                         // per chunk: scores, A-operand order
   static constexpr int PAGG_BYTES = NG * DK * 16;
   static constexpr int AP_BYTES = A_BYTES > PAGG_BYTES ? A_BYTES : PAGG_BYTES;
+  // The readout of the chunk states waits for the carried state when the
+  // per-chunk local states fit in registers (NRT*CPW <= 4 tiles per lane);
+  // otherwise it runs in the chunk loop and a correction adds the carry.
+  static constexpr bool DEFER = NRT * CPW <= 4;
+  // The walkers keep a, pbar, c, k*Lambda^v in registers between the two
+  // walks when they own at most 16 tokens.
+  static constexpr bool KEEP = TG <= 16;
   static_assert(TG % 16 == 0, "walker groups must own whole chunks");
 };
 
@@ -103,6 +112,31 @@ __device__ __forceinline__ void stage_tile(In* dst, const In* src, int nvalid, i
     int u = tid + it * 256;
     buf[it] = (u < valid_units) ? s4[u] : make_uint4(0, 0, 0, 0);
   }
+#pragma unroll
+  for (int it = 0; it < (UNITS + 255) / 256; ++it) {
+    int u = tid + it * 256;
+    if (u < UNITS) d4[u] = buf[it];
+  }
+}
+// The two halves of stage_tile, for overlapping a load with other work.
+template <typename In, int ROWS, int WIDTH>
+__device__ __forceinline__ void load_tile(uint4 (&buf)[(ROWS * WIDTH * (int)sizeof(In) / 16 + 255) / 256],
+                                          const In* src, int nvalid, int tid) {
+  constexpr int UNITS = ROWS * WIDTH * (int)sizeof(In) / 16;
+  constexpr int PER_UNIT = 16 / (int)sizeof(In);
+  const int valid_units = nvalid * WIDTH / PER_UNIT;
+  const uint4* s4 = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+  for (int it = 0; it < (UNITS + 255) / 256; ++it) {
+    int u = tid + it * 256;
+    buf[it] = (u < valid_units) ? s4[u] : make_uint4(0, 0, 0, 0);
+  }
+}
+template <typename In, int ROWS, int WIDTH>
+__device__ __forceinline__ void store_tile(In* dst, const uint4 (&buf)[(ROWS * WIDTH * (int)sizeof(In) / 16 + 255) / 256],
+                                           int tid) {
+  constexpr int UNITS = ROWS * WIDTH * (int)sizeof(In) / 16;
+  uint4* d4 = reinterpret_cast<uint4*>(dst);
 #pragma unroll
   for (int it = 0; it < (UNITS + 255) / 256; ++it) {
     int u = tid + it * 256;
@@ -171,15 +205,18 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
   In* const rvp = s.raw(4);
 
   // ---------------------------------------------------------------- stage inputs
-  {
-    const size_t offk = ((size_t)head * T + t0) * DK, offv = ((size_t)head * T + t0) * DV;
-    stage_tile<In, L, DK>(rq, static_cast<const In*>(p.q) + offk, nvalid, tid);
-    stage_tile<In, L, DK>(rk, static_cast<const In*>(p.k) + offk, nvalid, tid);
-    stage_tile<In, L, DK>(rld, static_cast<const In*>(p.ld) + offk, nvalid, tid);
-    stage_tile<In, L, DK>(rpn, static_cast<const In*>(p.pn) + offk, nvalid, tid);
-    stage_tile<In, L, DK>(rvp, static_cast<const In*>(p.vp) + offk, nvalid, tid);
-    stage_tile<In, L, DV>(s.v, static_cast<const In*>(p.v) + offv, nvalid, tid);
-  }
+  // All six tiles are requested at once; the coefficient tiles are written to
+  // LDS first and q, v only after the aggregate walk, so their load latency
+  // overlaps the walk.
+  const size_t offk = ((size_t)head * T + t0) * DK, offv = ((size_t)head * T + t0) * DV;
+  constexpr int UK = (L * DK * (int)sizeof(In) / 16 + 255) / 256, UV = (L * DV * (int)sizeof(In) / 16 + 255) / 256;
+  uint4 bq[UK], bv[UV];
+  load_tile<In, L, DK>(bq, static_cast<const In*>(p.q) + offk, nvalid, tid);
+  load_tile<In, L, DV>(bv, static_cast<const In*>(p.v) + offv, nvalid, tid);
+  stage_tile<In, L, DK>(rk, static_cast<const In*>(p.k) + offk, nvalid, tid);
+  stage_tile<In, L, DK>(rld, static_cast<const In*>(p.ld) + offk, nvalid, tid);
+  stage_tile<In, L, DK>(rpn, static_cast<const In*>(p.pn) + offk, nvalid, tid);
+  stage_tile<In, L, DK>(rvp, static_cast<const In*>(p.vp) + offk, nvalid, tid);
   __syncthreads();
   const unsigned epoch = (unsigned)s.ctl[1];
   const unsigned FAGG = 2u * epoch + 2u, FINC = 2u * epoch + 3u;
@@ -187,18 +224,31 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
   // ---------------------------------------------------------------- 1. group aggregates
   const int wi = tid % DK, wr = tid / DK;
   const bool walker = wr < NG;
+  constexpr int KT = C::KEEP ? TG : 1;
+  float ca[KT], cpn[KT], cc2[KT], ckv[KT];  // a, pbar, c, k*Lambda^v of this thread's tokens
   if (walker) {
     Mob P = mob_identity();
 #pragma unroll
-    for (int e = 0; e < TG; e += 2) {
-      const int x0 = (wr * TG + e) * DK + wi, x1 = x0 + DK;
-      const float k0 = to_f32(rk[x0]), a0 = __expf(to_f32(rld[x0]));
-      const float k1 = to_f32(rk[x1]), a1 = __expf(to_f32(rld[x1]));
-      P = mob_step_raw(P, a0 * a0, to_f32(rpn[x0]), k0 * k0 * to_f32(rvp[x0]));
-      P = mob_normalize(mob_step_raw(P, a1 * a1, to_f32(rpn[x1]), k1 * k1 * to_f32(rvp[x1])));
+    for (int e = 0; e < TG; ++e) {
+      const int x = (wr * TG + e) * DK + wi;
+      const float kk = to_f32(rk[x]);
+      const float kv = kk * to_f32(rvp[x]);
+      const float a = __expf(to_f32(rld[x]));
+      const float pnv = to_f32(rpn[x]);
+      const float c = kk * kv;
+      if constexpr (C::KEEP) {
+        ca[e] = a;
+        cpn[e] = pnv;
+        cc2[e] = c;
+        ckv[e] = kv;
+      }
+      P = mob_step_raw(P, a * a, pnv, c);
+      if (e & 1) P = mob_normalize(P);
     }
     *reinterpret_cast<v4f*>(s.pagg() + (wr * DK + wi) * 4) = v4f{P.m00, P.m01, P.m10, P.m11};
   }
+  store_tile<In, L, DK>(rq, bq, tid);
+  store_tile<In, L, DV>(s.v, bv, tid);
   __syncthreads();
 
   // ---------------------------------------------------------------- 2. precision carry
@@ -231,7 +281,10 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
       __syncthreads();
       if (tid == 0) st_relaxed(p.pflag + hs, FAGG);
     }
-    if (tid == 0) s.ctl[2] = lookback_find(p.pflag + hb, 1, seg, FAGG, FINC, p.ctrl);
+    if (wave == 0) {
+      const int r = lookback_find(p.pflag + hb, 1, seg, FAGG, FINC, p.ctrl);
+      if (tid == 0) s.ctl[2] = r;
+    }
     __syncthreads();
     const int r0 = s.ctl[2];
     if (tid < DK) {
@@ -256,7 +309,8 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
   // Results stay in registers until every walker has finished reading the raw
   // inputs, then overwrite them as stored operands.
   float wq[TG], wk[TG], wd[TG];
-  if (walker) {
+  auto walk = [&](auto with_path) {
+    constexpr bool PATH = decltype(with_path)::value;
     float lam = s.lam_in[wi];
 #pragma unroll
     for (int r = 0; r < NG - 1; ++r) {
@@ -265,6 +319,7 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
         lam = mob_apply(Mob{d[0], d[1], d[2], d[3]}, lam);
       }
     }
+    float* const lp = PATH ? p.lpath + ((size_t)head * T + t0) * DK + wi : nullptr;
 #pragma unroll
     for (int cl = 0; cl < CPG; ++cl) {
       const int cc = wr * CPG + cl;
@@ -273,23 +328,36 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
       float fr[16], gr[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
+        const int te = cl * 16 + e;  // token within this thread's group
         const int t = cc * 16 + e;
         const int x = t * DK + wi;
-        const float kk = to_f32(rk[x]);
-        const float kv = kk * to_f32(rvp[x]);
-        const float a = __expf(to_f32(rld[x]));
+        float a, pnv, c, kv;
+        if constexpr (C::KEEP) {
+          a = ca[te];
+          pnv = cpn[te];
+          c = cc2[te];
+          kv = ckv[te];
+        } else {
+          const float kk = to_f32(rk[x]);
+          kv = kk * to_f32(rvp[x]);
+          a = __expf(to_f32(rld[x]));
+          pnv = to_f32(rpn[x]);
+          c = kk * kv;
+        }
         float lam_pred;
-        const float lam_new = lam_step(lam, a * a, to_f32(rpn[x]), kk * kv, lam_pred);
+        const float lam_new = lam_step(lam, a * a, pnv, c, lam_pred);
         const float inv = fast_rcp(lam_new);
         const float f = a * lam_pred * inv;
         const float g = kv * inv;
         cp *= f;
-        wq[cl * 16 + e] = to_f32(rq[x]) * cp;
-        wk[cl * 16 + e] = g * fast_rcp(cp);
+        wq[te] = to_f32(rq[x]) * cp;
+        wk[te] = g * fast_rcp(cp);
         fr[e] = f;
         gr[e] = g;
         lam = lam_new;
-        if (p.lpath && t < nvalid) p.lpath[((size_t)head * T + t0 + t) * DK + wi] = lam;
+        if constexpr (PATH) {
+          if (t < nvalid) lp[(size_t)t * DK] = lam;
+        }
       }
       s.cpe[cc * DK + wi] = cp;
       if (!(cp >= 0x1p-64f)) s.unsafe[cc] = 1;
@@ -301,6 +369,12 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
       }
     }
     if (last && wr == NG - 1) p.lamT[(size_t)head * DK + wi] = lam;
+  };
+  if (walker) {
+    if (p.lpath)
+      walk(std::true_type{});
+    else
+      walk(std::false_type{});
   }
   __syncthreads();
   unsigned char* const Qs = s.u;
@@ -334,12 +408,14 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
   // from global memory) and the channels are summed with wave reductions, in
   // a fixed order.
   unsigned char* const A = s.ap;
+#pragma unroll 1
   for (int cc = 0; cc < NCH; ++cc) {
     if (!s.unsafe[cc]) continue;  // uniform: every thread reads the same flag
     float f[16], g[16], q[16];
     const bool chan = tid < DK;
     if (chan) {
       float lam = s.lamc[cc * DK + tid];
+#pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int t = cc * 16 + e;
         float kk = 0.f, ldv = 0.f, pnv = 0.f, vpv = 0.f, qv = 0.f;
@@ -363,8 +439,11 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
       }
     }
     // pair (t, u), u <= t: sum over channels of q_t g_u prod_{w=u+1..t} f_w
+    // (rarely taken: kept rolled to keep the kernel's code small)
+#pragma unroll 1
     for (int uu = 0; uu < 16; ++uu) {
       float d = chan ? g[uu] : 0.f;
+#pragma unroll 1
       for (int tt = uu; tt < 16; ++tt) {
         if (tt > uu) d *= chan ? f[tt] : 0.f;
         const float part = wave_sum(chan ? q[tt] * d : 0.f);
@@ -399,8 +478,14 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
   __syncthreads();
 
   // ---------------------------------------------------------------- 4b. chunk loop
+  // Local chunk states from a zero state: M_{c+1} = diag(cp_end_c) M_c + Kd_c^T V_c.
+  // y_c gets the intra-chunk part A_c V_c here; its readout Qs_c M_c either
+  // here (and the carried state is added by a correction later) or, deferred,
+  // once the carried state is known, from the kept states M_c.
   v4f yl[NCH][CPW];
   v4f Macc[NRT][CPW];
+  constexpr int NKEEP = C::DEFER ? NCH : 1;
+  v4f Mkeep[NKEEP][NRT][CPW];  // deferred: local state entering chunk c (c >= 1)
 #pragma unroll
   for (int pp = 0; pp < CPW; ++pp)
 #pragma unroll
@@ -411,8 +496,10 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
     for (int cc = 0; cc < NCH; ++cc) {
       const Op ao = M::get(A + (cc * 64 + lane) * 16);
       Op qo[NRT];
+      if constexpr (!C::DEFER) {
 #pragma unroll
-      for (int mt = 0; mt < NRT; ++mt) qo[mt] = M::get(Qs + (cc * 16 + lc) * QROW + (16 * mt + 4 * lg) * 4);
+        for (int mt = 0; mt < NRT; ++mt) qo[mt] = M::get(Qs + (cc * 16 + lc) * QROW + (16 * mt + 4 * lg) * 4);
+      }
 #pragma unroll
       for (int pp = 0; pp < CPW; ++pp) {
         const int nt = wave + 4 * pp;
@@ -420,16 +507,21 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
           // V block: rows u = cc*16 + 4*lg + e, column 16*nt + lc.
           const typename M::VOp vo = M::vop(s.v + (cc * 16 + 4 * lg) * DV + 16 * nt + lc, DV);
           v4f acc = M::dotv(v4f{0.f, 0.f, 0.f, 0.f}, ao, vo);
-          Op mo[NRT];
+          if constexpr (!C::DEFER) {
+            Op mo[NRT];
 #pragma unroll
-          for (int mt = 0; mt < NRT; ++mt) mo[mt] = M::op(Macc[mt][pp]);
-          acc = M::dot(acc, qo, mo);
+            for (int mt = 0; mt < NRT; ++mt) mo[mt] = M::op(Macc[mt][pp]);
+            acc = M::dot(acc, qo, mo);
+          }
           yl[cc][pp] = acc;
 #pragma unroll
           for (int mt = 0; mt < NRT; ++mt) {
-            const v4f m = Macc[mt][pp] * ld4(s.cpe + cc * DK + 16 * mt + 4 * lg);
+            const v4f m = cc == 0 ? Macc[mt][pp] : Macc[mt][pp] * ld4(s.cpe + cc * DK + 16 * mt + 4 * lg);
             const Op kdo = M::get(KdT + (16 * mt + lc) * KROW + (cc * 16 + 4 * lg) * 4);
             Macc[mt][pp] = M::dotv(m, kdo, vo);
+            if constexpr (C::DEFER) {
+              if (cc + 1 < NCH) Mkeep[cc + 1 < NKEEP ? cc + 1 : 0][mt][pp] = Macc[mt][pp];
+            }
           }
         }
       }
@@ -493,7 +585,10 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
       __syncthreads();
       if (tid == 0) st_relaxed(p.mflag + hs, FAGG);
     }
-    if (tid == 0) s.ctl[3] = lookback_find(p.mflag + hb, 1, seg, FAGG, FINC, p.ctrl);
+    if (wave == 0) {
+      const int r = lookback_find(p.mflag + hb, 1, seg, FAGG, FINC, p.ctrl);
+      if (tid == 0) s.ctl[3] = r;
+    }
     __syncthreads();
     const int r0 = s.ctl[3];
 #pragma unroll
@@ -534,10 +629,13 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
     }
   }
 
-  // ---------------------------------------------------------------- 6. correction + store
-  // y_t += Qs_t (diag(prod of earlier chunk decays) M_in), staged in LDS over v
-  // (dead once every wave has left the chunk loop) and written out in 16-byte
-  // units.
+  // ---------------------------------------------------------------- 6. readout / correction + store
+  // With M_in the state entering the segment, the true state entering chunk c
+  // is M_c + diag(prod of earlier chunk decays) M_in:
+  //   deferred:   y_c = A_c V_c + Qs_c (M_c + diag(decay_c) M_in)
+  //   otherwise:  y_c += Qs_c (diag(decay_c) M_in)
+  // y is staged in LDS over v (dead once every wave has left the chunk loop)
+  // and written out in 16-byte units.
   __syncthreads();
   if (wave < NCT) {
     v4f decay[NRT];  // prod of chunk decays before chunk cc, per owned row
@@ -554,14 +652,23 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
         if (nt < NCT) {
           Op mo[NRT];
 #pragma unroll
-          for (int mt = 0; mt < NRT; ++mt) mo[mt] = M::op(decay[mt] * Min[mt][pp]);
+          for (int mt = 0; mt < NRT; ++mt) {
+            v4f m = cc == 0 ? Min[mt][pp] : decay[mt] * Min[mt][pp];
+            if constexpr (C::DEFER) {
+              if (cc > 0) m = m + Mkeep[cc < NKEEP ? cc : 0][mt][pp];
+            }
+            mo[mt] = M::op(m);
+          }
           const v4f acc = M::dot(yl[cc][pp], qo, mo);
 #pragma unroll
           for (int e = 0; e < 4; ++e) s.v[(cc * 16 + 4 * lg + e) * DV + 16 * nt + lc] = from_f32<In>(acc[e]);
         }
       }
+      if (cc + 1 < NCH) {
 #pragma unroll
-      for (int mt = 0; mt < NRT; ++mt) decay[mt] = decay[mt] * ld4(s.cpe + cc * DK + 16 * mt + 4 * lg);
+        for (int mt = 0; mt < NRT; ++mt)
+          decay[mt] = cc == 0 ? ld4(s.cpe + 16 * mt + 4 * lg) : decay[mt] * ld4(s.cpe + cc * DK + 16 * mt + 4 * lg);
+      }
     }
   }
   __syncthreads();

@@ -97,7 +97,10 @@ __global__ __launch_bounds__(256) void kla_pscan_kernel(PscanParams p) {
         if (tid == 0) st_relaxed(p.flag + slot, FAGG);
       }
       // flags of this chain block for segments 0..seg-1 sit ncblocks apart
-      if (tid == 0) sh[2] = lookback_find(p.flag + cb, p.ncblocks, seg, FAGG, FINC, p.ctrl);
+      if (tid < 64) {
+        const int r = lookback_find(p.flag + cb, p.ncblocks, seg, FAGG, FINC, p.ctrl);
+        if (tid == 0) sh[2] = r;
+      }
       __syncthreads();
       const int r0 = sh[2];
       float x = ld_coherent(p.inc + ((size_t)r0 * p.ncblocks + cb) * 256 + tid);
