@@ -91,6 +91,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--copies", type=int, default=3, help="rotating input/output copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="after timing, run five plain device copies of this many MiB (a reference of known "
+                         "traffic for hardware counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -176,6 +179,14 @@ def main():
                      "kernel_ms_min": float(np.min(kern_ms)), "kernel_ms_max": float(np.max(kern_ms))},
         "cpu_baseline": None,
     }
+    if args.copy_mb:
+        n = args.copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_reference"] = {"mib": args.copy_mb, "launches": 5, "bytes_read": n * 4, "bytes_written": n * 4}
     if not args.no_cpu_baseline:
         y_gpu = copies[0]["y"].float().cpu().numpy()
         cb, margin = cpu_baseline(x, y_gpu)
