@@ -269,14 +269,21 @@ __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F7
 // predecessor.  `stride` is the distance between the flags of consecutive
 // segments.  Called by all 64 lanes of one wavefront (uniform result); on
 // giving up after kSpinLimit polls it records an error and returns.
+//
+// lookback_peek issues the first window's flag loads on their own, so that
+// their round trip can overlap the publication of the caller's own aggregate;
+// its result is handed to lookback_find.
+__device__ __forceinline__ unsigned lookback_peek(const unsigned* flags, int stride, int top) {
+  const int r = top - (int)(threadIdx.x & 63);
+  return r >= 0 ? ld_relaxed(flags + (size_t)r * stride) : 0u;
+}
 __device__ inline int lookback_find(const unsigned* flags, int stride, int s, unsigned fagg, unsigned finc,
-                                    unsigned* ctrl) {
+                                    unsigned* ctrl, unsigned f) {
   const int lane = threadIdx.x & 63;
-  int top = s - 1;  // newest predecessor of the current window
+  int top = s - 1;  // newest predecessor of the current window; f holds its flags
   int spins = 0;
   while (true) {
     const int r = top - lane;
-    const unsigned f = r >= 0 ? ld_relaxed(flags + (size_t)r * stride) : 0u;
     const unsigned long long inc = __ballot(r >= 0 && f == finc);
     const unsigned long long ready = __ballot(r >= 0 && (f == finc || f == fagg));
     if (inc) {
@@ -285,6 +292,7 @@ __device__ inline int lookback_find(const unsigned* flags, int stride, int s, un
       if ((ready & below) == below) return top - j;
     } else if (ready == ~0ull) {
       top -= 64;  // the whole window holds aggregates only: look further back
+      f = lookback_peek(flags, stride, top);
       continue;
     }
     if (++spins > kSpinLimit) {
@@ -292,7 +300,12 @@ __device__ inline int lookback_find(const unsigned* flags, int stride, int s, un
       return top;
     }
     __builtin_amdgcn_s_sleep(1);
+    f = lookback_peek(flags, stride, top);
   }
+}
+__device__ inline int lookback_find(const unsigned* flags, int stride, int s, unsigned fagg, unsigned finc,
+                                    unsigned* ctrl) {
+  return lookback_find(flags, stride, s, fagg, finc, ctrl, lookback_peek(flags, stride, s - 1));
 }
 
 // Call epochs.  Every workgroup reads the workspace epoch e before touching

@@ -252,58 +252,56 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
   __syncthreads();
 
   // ---------------------------------------------------------------- 2. precision carry
-  Mob Pseg = mob_identity();
-  if (tid < DK) {
+  // The carry waves (one lane per channel; a second wave when DK = 128) each
+  // run their own look-back over their channels, with flags of their own, so
+  // no workgroup barrier sits inside the carry.  The first flag poll is issued
+  // before waiting for the aggregate's stores, and the inclusive carry's flag
+  // is raised after the barrier that releases the other waves.
+  constexpr int PW = (DK + 63) / 64;  // carry waves
+  const bool pwave = wave < PW, pch = tid < DK;
+  unsigned* const pfl = p.pflag + hb * 2 + wave;  // flag of segment r: pfl[2 * r]
+  if (pwave) {
+    Mob Pseg = mob_identity();
+    if (pch) {
 #pragma unroll
-    for (int r = 0; r < NG; ++r) {
-      const v4f d = ld4(s.pagg() + (r * DK + tid) * 4);
-      Pseg = mob_mul(Mob{d[0], d[1], d[2], d[3]}, Pseg);
+      for (int r = 0; r < NG; ++r) {
+        const v4f d = ld4(s.pagg() + (r * DK + tid) * 4);
+        Pseg = mob_mul(Mob{d[0], d[1], d[2], d[3]}, Pseg);
+      }
     }
-  }
-  float lam_in = 1.f;
-  if (seg == 0) {
-    if (tid < DK) {
-      lam_in = p.lam0 ? p.lam0[(size_t)head * DK + tid] : 1.f;
-      if (!last) st_coherent(p.pinc + hs * DK + tid, mob_apply(Pseg, lam_in));
-    }
-    if (!last) {
-      wait_stores();
-      __syncthreads();
-      if (tid == 0) st_relaxed(p.pflag + hs, FINC);
-    }
-  } else {
-    if (!last) {  // publish the aggregate first so successors need not wait on us
-      if (tid < DK) {
+    float lam_in = 1.f;
+    if (seg == 0) {
+      if (pch && p.lam0) lam_in = p.lam0[(size_t)head * DK + tid];
+    } else {
+      if (!last && pch) {  // publish the aggregate first so successors need not wait on us
         const auto r = coherent_rsrc(p.pagg + hs * DK * 4, DK * 16);
         st_coherent(r, tid * 16, v4f{Pseg.m00, Pseg.m01, Pseg.m10, Pseg.m11});
       }
+      const unsigned f0 = lookback_peek(pfl, 2, seg - 1);
       wait_stores();
-      __syncthreads();
-      if (tid == 0) st_relaxed(p.pflag + hs, FAGG);
-    }
-    if (wave == 0) {
-      const int r = lookback_find(p.pflag + hb, 1, seg, FAGG, FINC, p.ctrl);
-      if (tid == 0) s.ctl[2] = r;
-    }
-    __syncthreads();
-    const int r0 = s.ctl[2];
-    if (tid < DK) {
-      float lam = ld_coherent(p.pinc + (hb + r0) * DK + tid);
-      for (int u = r0 + 1; u < seg; ++u) {
-        const v4f m = ld_coherent(coherent_rsrc(p.pagg + (hb + u) * DK * 4, DK * 16), tid * 16);
-        lam = mob_apply(Mob{m[0], m[1], m[2], m[3]}, lam);
+      if (!last && lane == 0) st_relaxed(pfl + 2 * seg, FAGG);
+      const int r0 = lookback_find(pfl, 2, seg, FAGG, FINC, p.ctrl, f0);
+      // Fold the carries of segments r0 .. seg-1, loading up to eight at once.
+      float lam = pch ? ld_coherent(p.pinc + (hb + r0) * DK + tid) : 1.f;
+      for (int u0 = r0 + 1; u0 < seg; u0 += 8) {
+        v4f m[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (u0 + j < seg) m[j] = ld_coherent(coherent_rsrc(p.pagg + (hb + u0 + j) * DK * 4, DK * 16), tid * 16);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (u0 + j < seg) lam = mob_apply(Mob{m[j][0], m[j][1], m[j][2], m[j][3]}, lam);
       }
       lam_in = lam;
-      if (!last) st_coherent(p.pinc + hs * DK + tid, mob_apply(Pseg, lam_in));
     }
-    if (!last) {
-      wait_stores();
-      __syncthreads();
-      if (tid == 0) st_relaxed(p.pflag + hs, FINC);
-    }
+    if (!last && pch) st_coherent(p.pinc + hs * DK + tid, mob_apply(Pseg, lam_in));
+    if (pch) s.lam_in[tid] = lam_in;
   }
-  if (tid < DK) s.lam_in[tid] = lam_in;
   __syncthreads();
+  if (pwave && !last) {
+    wait_stores();
+    if (lane == 0) st_relaxed(pfl + 2 * seg, FINC);
+  }
 
   // ---------------------------------------------------------------- 3. gate walk
   // Results stay in registers until every walker has finished reading the raw
@@ -531,87 +529,113 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
   // ---------------------------------------------------------------- 5. mean carry
   // Each lane owns, per tile (mt, nt), rows 16*mt + 4*lg + e of column 16*nt + lc.
   // Workspace payloads are stored in this fragment order, 16 bytes per lane.
+  // The carry of a column tile depends only on the same columns of earlier
+  // segments, so each wave carries its own tiles with flags (and a copy of
+  // prod f) of its own: no workgroup barrier sits inside the carry.
   constexpr uint32_t MBYTES = (uint32_t)DK * DV * 4;
+  constexpr int FB = NRT * CPW <= 8 ? 2 : 1;  // aggregates folded per round trip
   auto frag_off = [&](int mt, int nt) -> uint32_t { return ((uint32_t)(nt * NRT + mt) * 64 + lane) * 16; };
   v4f Min[NRT][CPW];
-  auto store_inclusive = [&]() {
-    const auto r = coherent_rsrc(p.minc + hs * DK * DV, MBYTES);
-#pragma unroll
-    for (int pp = 0; pp < CPW; ++pp) {
-      const int nt = wave + 4 * pp;
-      if (nt < NCT) {
-#pragma unroll
-        for (int mt = 0; mt < NRT; ++mt) {
-          const v4f F = ld4(s.fseg + 16 * mt + 4 * lg);
-          v4f o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = fmaf(F[e], Min[mt][pp][e], Macc[mt][pp][e]);
-          st_coherent(r, frag_off(mt, nt), o);
-        }
-      }
-    }
-    wait_stores();
-    __syncthreads();
-    if (tid == 0) st_relaxed(p.mflag + hs, FINC);
-  };
-  if (seg == 0) {
-#pragma unroll
-    for (int pp = 0; pp < CPW; ++pp) {
-      const int nt = wave + 4 * pp;
-#pragma unroll
-      for (int mt = 0; mt < NRT; ++mt) {
-        v4f m = v4f{0.f, 0.f, 0.f, 0.f};
-        if (nt < NCT && p.M0) {
-          const float* src = p.M0 + (size_t)head * DK * DV + (size_t)(16 * mt + 4 * lg) * DV + 16 * nt + lc;
-          m = v4f{src[0], src[DV], src[2 * DV], src[3 * DV]};
-        }
-        Min[mt][pp] = m;
-      }
-    }
-    if (!last) store_inclusive();
-  } else {
-    if (!last) {
-      if (tid < DK) st_coherent(p.mF + hs * DK + tid, s.fseg[tid]);
-      const auto r = coherent_rsrc(p.magg + hs * DK * DV, MBYTES);
+  if (wave < NCT) {
+    unsigned* const mfl = p.mflag + hb * 4 + wave;  // flag of segment r: mfl[4 * r]
+    auto store_inclusive = [&]() {
+      const auto r = coherent_rsrc(p.minc + hs * DK * DV, MBYTES);
 #pragma unroll
       for (int pp = 0; pp < CPW; ++pp) {
         const int nt = wave + 4 * pp;
         if (nt < NCT) {
 #pragma unroll
-          for (int mt = 0; mt < NRT; ++mt) st_coherent(r, frag_off(mt, nt), Macc[mt][pp]);
+          for (int mt = 0; mt < NRT; ++mt) {
+            const v4f F = ld4(s.fseg + 16 * mt + 4 * lg);
+            v4f o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = fmaf(F[e], Min[mt][pp][e], Macc[mt][pp][e]);
+            st_coherent(r, frag_off(mt, nt), o);
+          }
         }
       }
       wait_stores();
-      __syncthreads();
-      if (tid == 0) st_relaxed(p.mflag + hs, FAGG);
-    }
-    if (wave == 0) {
-      const int r = lookback_find(p.mflag + hb, 1, seg, FAGG, FINC, p.ctrl);
-      if (tid == 0) s.ctl[3] = r;
-    }
-    __syncthreads();
-    const int r0 = s.ctl[3];
+      if (lane == 0) st_relaxed(mfl + 4 * seg, FINC);
+    };
+    if (seg == 0) {
 #pragma unroll
-    for (int pp = 0; pp < CPW; ++pp) {
-      const int nt = wave + 4 * pp;
+      for (int pp = 0; pp < CPW; ++pp) {
+        const int nt = wave + 4 * pp;
 #pragma unroll
-      for (int mt = 0; mt < NRT; ++mt) {
-        v4f m = v4f{0.f, 0.f, 0.f, 0.f};
-        if (nt < NCT) {
-          m = ld_coherent(coherent_rsrc(p.minc + (hb + r0) * DK * DV, MBYTES), frag_off(mt, nt));
-          for (int u = r0 + 1; u < seg; ++u) {
-            const v4f a = ld_coherent(coherent_rsrc(p.magg + (hb + u) * DK * DV, MBYTES), frag_off(mt, nt));
-            const v4f F = ld_coherent(coherent_rsrc(p.mF + (hb + u) * DK, DK * 4), (16 * mt + 4 * lg) * 4);
+        for (int mt = 0; mt < NRT; ++mt) {
+          v4f m = v4f{0.f, 0.f, 0.f, 0.f};
+          if (nt < NCT && p.M0) {
+            const float* src = p.M0 + (size_t)head * DK * DV + (size_t)(16 * mt + 4 * lg) * DV + 16 * nt + lc;
+            m = v4f{src[0], src[DV], src[2 * DV], src[3 * DV]};
+          }
+          Min[mt][pp] = m;
+        }
+      }
+      if (!last) store_inclusive();
+    } else {
+      const size_t fslot = (hs * 4 + wave) * DK;  // this wave's copy of prod f
+      if (!last) {
+        for (int r = lane; r < DK; r += 64) st_coherent(p.mF + fslot + r, s.fseg[r]);
+        const auto r = coherent_rsrc(p.magg + hs * DK * DV, MBYTES);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) m[e] = fmaf(F[e], m[e], a[e]);
+        for (int pp = 0; pp < CPW; ++pp) {
+          const int nt = wave + 4 * pp;
+          if (nt < NCT) {
+#pragma unroll
+            for (int mt = 0; mt < NRT; ++mt) st_coherent(r, frag_off(mt, nt), Macc[mt][pp]);
           }
         }
-        Min[mt][pp] = m;
       }
+      const unsigned f0 = lookback_peek(mfl, 4, seg - 1);
+      wait_stores();
+      if (!last && lane == 0) st_relaxed(mfl + 4 * seg, FAGG);
+      const int r0 = lookback_find(mfl, 4, seg, FAGG, FINC, p.ctrl, f0);
+      // Fold the carries of segments r0 .. seg-1 (M <- diag(prod f) M + local
+      // state), FB aggregates per round trip.
+#pragma unroll
+      for (int pp = 0; pp < CPW; ++pp) {
+        const int nt = wave + 4 * pp;
+#pragma unroll
+        for (int mt = 0; mt < NRT; ++mt)
+          Min[mt][pp] = nt < NCT ? ld_coherent(coherent_rsrc(p.minc + (hb + r0) * DK * DV, MBYTES), frag_off(mt, nt))
+                                 : v4f{0.f, 0.f, 0.f, 0.f};
+      }
+      for (int u0 = r0 + 1; u0 < seg; u0 += FB) {
+        v4f A[FB][NRT][CPW], F[FB][NRT];
+#pragma unroll
+        for (int j = 0; j < FB; ++j) {
+          if (u0 + j < seg) {
+            const size_t us = hb + u0 + j;
+            const auto ra = coherent_rsrc(p.magg + us * DK * DV, MBYTES);
+            const auto rf = coherent_rsrc(p.mF + (us * 4 + wave) * DK, DK * 4);
+#pragma unroll
+            for (int mt = 0; mt < NRT; ++mt) {
+              F[j][mt] = ld_coherent(rf, (16 * mt + 4 * lg) * 4);
+#pragma unroll
+              for (int pp = 0; pp < CPW; ++pp) {
+                const int nt = wave + 4 * pp;
+                A[j][mt][pp] = nt < NCT ? ld_coherent(ra, frag_off(mt, nt)) : v4f{0.f, 0.f, 0.f, 0.f};
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < FB; ++j) {
+          if (u0 + j < seg) {
+#pragma unroll
+            for (int mt = 0; mt < NRT; ++mt)
+#pragma unroll
+              for (int pp = 0; pp < CPW; ++pp)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Min[mt][pp][e] = fmaf(F[j][mt][e], Min[mt][pp][e], A[j][mt][pp][e]);
+          }
+        }
+      }
+      if (!last) store_inclusive();
     }
-    if (!last) store_inclusive();
   }
-  // Every flag access of this workgroup is done.
+  // Every thread read the epoch before the first barrier; count this
+  // workgroup done (other waves may still be polling flags of this call).
   if (nseg > 1 && tid == 0) epoch_done(p.ctrl, p.hdone + head, (unsigned)nseg, (unsigned)nheads, epoch);
   if (last) {  // final state, row-major
 #pragma unroll
@@ -635,8 +659,8 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
   //   deferred:   y_c = A_c V_c + Qs_c (M_c + diag(decay_c) M_in)
   //   otherwise:  y_c += Qs_c (diag(decay_c) M_in)
   // y is staged in LDS over v (dead once every wave has left the chunk loop)
-  // and written out in 16-byte units.
-  __syncthreads();
+  // and written out in 16-byte units.  A wave's y columns are the V columns
+  // only it read in the chunk loop, so no barrier is needed before staging.
   if (wave < NCT) {
     v4f decay[NRT];  // prod of chunk decays before chunk cc, per owned row
 #pragma unroll

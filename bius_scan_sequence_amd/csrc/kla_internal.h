@@ -25,11 +25,11 @@ struct FwdParams {
   int nheads, T, nseg;
   unsigned* ctrl;     // workspace control words
   unsigned* hdone;    // [nheads] segments of the head done with their flags
-  unsigned* pflag;    // [nheads*nseg] precision-carry flags
-  unsigned* mflag;    // [nheads*nseg] mean-carry flags
+  unsigned* pflag;    // [nheads*nseg][2] precision-carry flags, one per carry wave
+  unsigned* mflag;    // [nheads*nseg][4] mean-carry flags, one per wave
   float* pagg;        // [nheads*nseg][dk][4] segment 2x2 aggregates
   float* pinc;        // [nheads*nseg][dk]    precision after the segment
-  float* mF;          // [nheads*nseg][dk]    prod of forget gates over the segment
+  float* mF;          // [nheads*nseg][4][dk] prod of forget gates over the segment (per wave)
   float* magg;        // [nheads*nseg][dk*dv] local mean state (fragment order)
   float* minc;        // [nheads*nseg][dk*dv] mean state after the segment (fragment order)
 };
