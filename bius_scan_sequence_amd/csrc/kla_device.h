@@ -181,8 +181,11 @@ __device__ __forceinline__ Mob mob_normalize(Mob m) {
 }
 
 // step(a2, pb, c) . P as two row operations (predict, then update); not
-// normalised: callers normalise every second step, which keeps every entry
-// far inside the fp32 range for any finite coefficients of realistic size.
+// normalised.  An entry grows per step by at most the step matrix's largest
+// row sum, so normalising every fourth step keeps every entry inside the fp32
+// range while that sum stays below about 10^9 (1 + c*pb + c*a2 for realistic
+// coefficients is many orders smaller).  The (0,0) entry never shrinks below
+// its value before the step, so nothing that matters underflows.
 __device__ __forceinline__ Mob mob_step_raw(Mob P, float a2, float pb, float c) {
   Mob n;
   n.m10 = fmaf(pb, P.m00, a2 * P.m10);  // predict: row1 <- pb*row0 + a2*row1
@@ -310,19 +313,27 @@ __device__ inline int lookback_find(const unsigned* flags, int stride, int s, un
 
 // Call epochs.  Every workgroup reads the workspace epoch e before touching
 // flags, so flags of this call (values 2e+2, 2e+3) never match those left by
-// earlier calls, whatever their shapes.  Workgroups are grouped (the segments
-// of one head, or of one chain block); each counts itself done in its group
-// after its last flag access, the last of a group counts the group done, and
-// the last group resets the counters and advances the epoch for the next call.
+// earlier calls, whatever their shapes.  Each workgroup counts itself done
+// once it no longer needs the epoch; the last of the `ngroups` workgroups
+// resets the counter and advances the epoch for the next call (calls on one
+// workspace are ordered on one stream, so no workgroup of the next call runs
+// before every workgroup of this one has finished).
 enum CtrlEpoch { kEpoch = 0, kGroupsDone = 1 };
-__device__ __forceinline__ void epoch_done(unsigned* ctrl, unsigned* group_done, unsigned group_size,
-                                           unsigned ngroups, unsigned e) {
-  if (__hip_atomic_fetch_add(group_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != group_size - 1) return;
-  st_relaxed(group_done, 0u);
+__device__ __forceinline__ void epoch_done(unsigned* ctrl, unsigned ngroups, unsigned e) {
   if (__hip_atomic_fetch_add(ctrl + kGroupsDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ngroups - 1)
     return;
   st_relaxed(ctrl + kGroupsDone, 0u);
   st_relaxed(ctrl + kEpoch, e + 1u);
+}
+
+// The same with workgroups counted in groups first (one counter per group, then
+// one for the groups), which spreads the counting atomics over many addresses
+// when many workgroups finish together.
+__device__ __forceinline__ void epoch_done_grouped(unsigned* ctrl, unsigned* group_done, unsigned group_size,
+                                                   unsigned ngroups, unsigned e) {
+  if (__hip_atomic_fetch_add(group_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != group_size - 1) return;
+  st_relaxed(group_done, 0u);
+  epoch_done(ctrl, ngroups, e);
 }
 
 }  // namespace kla

@@ -46,9 +46,10 @@ struct FwdCfg {
   static constexpr int L = (BF16 || (DK <= 64 && DV <= 64)) ? 64 : 32;  // tokens per segment
   static constexpr int NT = 256;
   static constexpr int NCH = L / 16;                                    // 16-token chunks
-  static constexpr int NG = (NT / DK < NCH) ? NT / DK : NCH;            // walker token groups
-  static constexpr int TG = L / NG;                                     // tokens per group
-  static constexpr int CPG = TG / 16;                                   // chunks per group
+  // Walkers: one thread per (channel group of CPT channels, half chunk of 8
+  // tokens); wave c walks chunk c, the halves of the chunk in lanes l and l ^ 32.
+  static constexpr int CPT = DK >= 64 ? DK / 32 : 1;                    // channels per walker
+  static_assert(NCH <= 4, "one walker wave per chunk");
   static constexpr int NRT = DK / 16;                                   // state row tiles
   static constexpr int NCT = DV / 16;                                   // state col tiles
   static constexpr int CPW = (NCT + 3) / 4;                             // col tiles per wave
@@ -60,16 +61,15 @@ struct FwdCfg {
   static constexpr int OPS_BYTES = 2 * L * QROW + DK * KROW;            // Qs, Ks, Kd^T
   static constexpr int UNION_BYTES = RAW_BYTES > OPS_BYTES ? RAW_BYTES : OPS_BYTES;
   static constexpr int A_BYTES = NCH * 64 * 16;                         // per chunk: scores, A-operand order
-  static constexpr int PAGG_BYTES = NG * DK * 16;
-  static constexpr int AP_BYTES = A_BYTES > PAGG_BYTES ? A_BYTES : PAGG_BYTES;
+  static constexpr int CAGG_BYTES = NCH * DK * 16;                      // chunk 2x2 aggregates
+  static constexpr int AP_BYTES = A_BYTES > CAGG_BYTES ? A_BYTES : CAGG_BYTES;
   // The readout of the chunk states waits for the carried state when the
   // per-chunk local states fit in registers (NRT*CPW <= 4 tiles per lane);
   // otherwise it runs in the chunk loop and a correction adds the carry.
   static constexpr bool DEFER = NRT * CPW <= 4;
   // The walkers keep a, pbar, c, k*Lambda^v in registers between the two
-  // walks when they own at most 16 tokens.
-  static constexpr bool KEEP = TG <= 16;
-  static_assert(TG % 16 == 0, "walker groups must own whole chunks");
+  // walks when they own at most 16 token-channels.
+  static constexpr bool KEEP = 8 * CPT <= 16;
 };
 
 template <int DK, int DV, bool BF16>
@@ -80,19 +80,18 @@ struct FwdSmem {
   // afterwards the stored operands Qs [L][QROW], Ks [L][QROW], Kd^T [DK][KROW].
   alignas(16) unsigned char u[C::UNION_BYTES];
   alignas(16) In v[C::L * DV];             // raw v; staged y at the end
-  // Walker-group 2x2 aggregates until the gate walk starts; then the causal
+  // Chunk 2x2 aggregates until the precision carry is done; then the causal
   // intra-chunk scores of every chunk in A-operand order.
   alignas(16) unsigned char ap[C::AP_BYTES];
   alignas(16) float cpe[C::NCH * DK];      // per chunk: prod of f over the chunk
   float lamc[C::NCH * DK];                 // per chunk: precision entering the chunk
-  alignas(16) float lam_in[DK];            // precision entering the segment
   alignas(16) float fseg[DK];              // prod of f over the segment
   float red[2 * 256];                      // exact path: per-wave partial sums
   int unsafe[C::NCH];
   int ctl[4];
 
   __device__ In* raw(int which) { return reinterpret_cast<In*>(u) + which * C::L * DK; }
-  __device__ float* pagg() { return reinterpret_cast<float*>(ap); }
+  __device__ float* cagg() { return reinterpret_cast<float*>(ap); }
 };
 
 // Copy one [rows x width] tile between global memory and LDS (16-byte units;
@@ -174,13 +173,61 @@ __device__ __forceinline__ void put1(unsigned char* block, int j, float x) {
   }
 }
 
+// CPT consecutive input values (CPT * sizeof(In)-aligned) as floats.
+template <int CPT>
+__device__ __forceinline__ void load_vals(const uint16_t* p, float (&o)[CPT]) {
+  if constexpr (CPT == 1) {
+    o[0] = to_f32(p[0]);
+  } else if constexpr (CPT == 2) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    o[0] = __uint_as_float(w << 16);
+    o[1] = __uint_as_float(w & 0xffff0000u);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    o[0] = __uint_as_float(w.x << 16);
+    o[1] = __uint_as_float(w.x & 0xffff0000u);
+    o[2] = __uint_as_float(w.y << 16);
+    o[3] = __uint_as_float(w.y & 0xffff0000u);
+  }
+}
+template <int CPT>
+__device__ __forceinline__ void load_vals(const float* p, float (&o)[CPT]) {
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) o[k] = p[k];
+}
+
+// CPT consecutive stored values starting at slot j of a 4-value block (see put1).
+template <bool BF16, int CPT>
+__device__ __forceinline__ void put_vals(unsigned char* block, int j, const float (&x)[CPT]) {
+  if constexpr (CPT == 1) {
+    put1<BF16>(block, j, x[0]);
+  } else if constexpr (BF16 && CPT == 2) {
+    const v2s h = bf16x2(x[0], x[1]);
+    const v2s l = bf16x2(x[0] - to_f32((uint16_t)h[0]), x[1] - to_f32((uint16_t)h[1]));
+    *reinterpret_cast<v2s*>(block + 2 * j) = h;
+    *reinterpret_cast<v2s*>(block + 8 + 2 * j) = l;
+  } else if constexpr (BF16) {
+    Mma<true>::put(block, v4f{x[0], x[1], x[2], x[3]});
+  } else {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) reinterpret_cast<float*>(block)[j + k] = x[k];
+  }
+}
+
+// Waves per SIMD the kernel is compiled for: two workgroups per compute unit
+// (at most 256 registers per lane) when two fit in LDS, else one.
 template <int DK, int DV, bool BF16>
-__global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
+constexpr int fwd_waves_per_eu() {
+  return sizeof(FwdSmem<DK, DV, BF16>) <= 80 * 1024 ? 2 : 1;
+}
+
+template <int DK, int DV, bool BF16>
+__global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_fwd_kernel(FwdParams p) {
   using C = FwdCfg<DK, DV, BF16>;
   using In = typename C::In;
   using M = Mma<BF16>;
   using Op = typename M::Op;
-  constexpr int L = C::L, NCH = C::NCH, NG = C::NG, TG = C::TG, CPG = C::CPG;
+  constexpr int L = C::L, NCH = C::NCH, CPT = C::CPT;
   constexpr int NRT = C::NRT, NCT = C::NCT, CPW = C::CPW, QROW = C::QROW, KROW = C::KROW;
   __shared__ FwdSmem<DK, DV, BF16> s;
 
@@ -221,31 +268,54 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
   const unsigned epoch = (unsigned)s.ctl[1];
   const unsigned FAGG = 2u * epoch + 2u, FINC = 2u * epoch + 3u;
 
-  // ---------------------------------------------------------------- 1. group aggregates
-  const int wi = tid % DK, wr = tid / DK;
-  const bool walker = wr < NG;
-  constexpr int KT = C::KEEP ? TG : 1;
-  float ca[KT], cpn[KT], cc2[KT], ckv[KT];  // a, pbar, c, k*Lambda^v of this thread's tokens
-  if (walker) {
-    Mob P = mob_identity();
+  // ---------------------------------------------------------------- 1. chunk aggregates
+  // Walker (chunk wc = wave, half wh, channel group wg) owns channels
+  // wch .. wch + CPT - 1 and tokens wt0 .. wt0 + 7 and composes their 2x2 step
+  // matrices; the halves of a chunk are joined with a lane exchange.
+  const int wc = wave, wh = lane >> 5;
+  const int wch = (lane & 31) * CPT, wt0 = wc * 16 + wh * 8;
+  const bool walker = wc < NCH && wch < DK;
+  constexpr int KT = C::KEEP ? 8 : 1;
+  float ca[KT][CPT], cpn[KT][CPT], cc2[KT][CPT], ckv[KT][CPT];  // a, pbar, c, k*Lambda^v
+  Mob Pg[CPT];
 #pragma unroll
-    for (int e = 0; e < TG; ++e) {
-      const int x = (wr * TG + e) * DK + wi;
-      const float kk = to_f32(rk[x]);
-      const float kv = kk * to_f32(rvp[x]);
-      const float a = __expf(to_f32(rld[x]));
-      const float pnv = to_f32(rpn[x]);
-      const float c = kk * kv;
-      if constexpr (C::KEEP) {
-        ca[e] = a;
-        cpn[e] = pnv;
-        cc2[e] = c;
-        ckv[e] = kv;
+  for (int k = 0; k < CPT; ++k) Pg[k] = mob_identity();
+  if (walker) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int x = (wt0 + e) * DK + wch;
+      float kk[CPT], vpv[CPT], ldv[CPT], pnv[CPT];
+      load_vals<CPT>(rk + x, kk);
+      load_vals<CPT>(rvp + x, vpv);
+      load_vals<CPT>(rld + x, ldv);
+      load_vals<CPT>(rpn + x, pnv);
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const float kv = kk[k] * vpv[k];
+        const float a = __expf(ldv[k]);
+        const float c = kk[k] * kv;
+        if constexpr (C::KEEP) {
+          ca[e][k] = a;
+          cpn[e][k] = pnv[k];
+          cc2[e][k] = c;
+          ckv[e][k] = kv;
+        }
+        Pg[k] = mob_step_raw(Pg[k], a * a, pnv[k], c);
+        if ((e & 3) == 3) Pg[k] = mob_normalize(Pg[k]);
       }
-      P = mob_step_raw(P, a * a, pnv, c);
-      if (e & 1) P = mob_normalize(P);
     }
-    *reinterpret_cast<v4f*>(s.pagg() + (wr * DK + wi) * 4) = v4f{P.m00, P.m01, P.m10, P.m11};
+  }
+  // Chunk aggregate = (second half) . (first half); both halves form the same
+  // product.  The second half keeps the first half's aggregate to find its
+  // entering precision.
+  Mob Pfirst[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const Mob Pp = Mob{__shfl_xor(Pg[k].m00, 32, 64), __shfl_xor(Pg[k].m01, 32, 64), __shfl_xor(Pg[k].m10, 32, 64),
+                       __shfl_xor(Pg[k].m11, 32, 64)};
+    Pfirst[k] = wh ? Pp : Pg[k];
+    const Mob Pc = wh ? mob_mul(Pg[k], Pp) : mob_mul(Pp, Pg[k]);
+    if (walker && wh == 0) *reinterpret_cast<v4f*>(s.cagg() + (wc * DK + wch + k) * 4) = v4f{Pc.m00, Pc.m01, Pc.m10, Pc.m11};
   }
   store_tile<In, L, DK>(rq, bq, tid);
   store_tile<In, L, DV>(s.v, bv, tid);
@@ -261,13 +331,16 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
   const bool pwave = wave < PW, pch = tid < DK;
   unsigned* const pfl = p.pflag + hb * 2 + wave;  // flag of segment r: pfl[2 * r]
   if (pwave) {
+    Mob cg[NCH];
     Mob Pseg = mob_identity();
-    if (pch) {
 #pragma unroll
-      for (int r = 0; r < NG; ++r) {
-        const v4f d = ld4(s.pagg() + (r * DK + tid) * 4);
-        Pseg = mob_mul(Mob{d[0], d[1], d[2], d[3]}, Pseg);
+    for (int c = 0; c < NCH; ++c) {
+      cg[c] = mob_identity();
+      if (pch) {
+        const v4f d = ld4(s.cagg() + (c * DK + tid) * 4);
+        cg[c] = Mob{d[0], d[1], d[2], d[3]};
       }
+      Pseg = mob_mul(cg[c], Pseg);
     }
     float lam_in = 1.f;
     if (seg == 0) {
@@ -295,7 +368,14 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
       lam_in = lam;
     }
     if (!last && pch) st_coherent(p.pinc + hs * DK + tid, mob_apply(Pseg, lam_in));
-    if (pch) s.lam_in[tid] = lam_in;
+    if (pch) {  // precision entering every chunk
+      float lam = lam_in;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        s.lamc[c * DK + tid] = lam;
+        if (c + 1 < NCH) lam = mob_apply(cg[c], lam);
+      }
+    }
   }
   __syncthreads();
   if (pwave && !last) {
@@ -305,68 +385,81 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
 
   // ---------------------------------------------------------------- 3. gate walk
   // Results stay in registers until every walker has finished reading the raw
-  // inputs, then overwrite them as stored operands.
-  float wq[TG], wk[TG], wd[TG];
+  // inputs, then overwrite them as stored operands.  A second-half walker
+  // starts from the precision after the first half and, once the halves have
+  // exchanged their prod f, rescales its cumulative products to the chunk start.
+  float wq[8][CPT], wk[8][CPT], wd[8][CPT];
+  float Fg[CPT];  // prod f over this walker's tokens
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) Fg[k] = 1.f;
   auto walk = [&](auto with_path) {
     constexpr bool PATH = decltype(with_path)::value;
-    float lam = s.lam_in[wi];
+    float lam[CPT], cp[CPT];
 #pragma unroll
-    for (int r = 0; r < NG - 1; ++r) {
-      if (r < wr) {
-        const v4f d = ld4(s.pagg() + (r * DK + wi) * 4);
-        lam = mob_apply(Mob{d[0], d[1], d[2], d[3]}, lam);
+    for (int k = 0; k < CPT; ++k) {
+      lam[k] = s.lamc[wc * DK + wch + k];
+      if (wh) lam[k] = mob_apply(Pfirst[k], lam[k]);
+      cp[k] = 1.f;
+    }
+    float* const lp = PATH ? p.lpath + ((size_t)head * T + t0) * DK + wch : nullptr;
+    float fr[8][CPT], gr[8][CPT];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = wt0 + e;
+      const int x = t * DK + wch;
+      float qv[CPT];
+      load_vals<CPT>(rq + x, qv);
+      float a[CPT], pnv[CPT], c[CPT], kv[CPT];
+      if constexpr (C::KEEP) {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+          a[k] = ca[e][k];
+          pnv[k] = cpn[e][k];
+          c[k] = cc2[e][k];
+          kv[k] = ckv[e][k];
+        }
+      } else {
+        float kk[CPT], vpv[CPT], ldv[CPT];
+        load_vals<CPT>(rk + x, kk);
+        load_vals<CPT>(rvp + x, vpv);
+        load_vals<CPT>(rld + x, ldv);
+        load_vals<CPT>(rpn + x, pnv);
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+          kv[k] = kk[k] * vpv[k];
+          a[k] = __expf(ldv[k]);
+          c[k] = kk[k] * kv[k];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        float lam_pred;
+        const float lam_new = lam_step(lam[k], a[k] * a[k], pnv[k], c[k], lam_pred);
+        const float inv = fast_rcp(lam_new);
+        const float f = a[k] * lam_pred * inv;
+        const float g = kv[k] * inv;
+        cp[k] *= f;
+        wq[e][k] = qv[k] * cp[k];
+        wk[e][k] = g * fast_rcp(cp[k]);
+        fr[e][k] = f;
+        gr[e][k] = g;
+        lam[k] = lam_new;
+        if constexpr (PATH) {
+          if (t < nvalid) lp[(size_t)t * DK + k] = lam_new;
+        }
       }
     }
-    float* const lp = PATH ? p.lpath + ((size_t)head * T + t0) * DK + wi : nullptr;
 #pragma unroll
-    for (int cl = 0; cl < CPG; ++cl) {
-      const int cc = wr * CPG + cl;
-      s.lamc[cc * DK + wi] = lam;
-      float cp = 1.f;
-      float fr[16], gr[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int te = cl * 16 + e;  // token within this thread's group
-        const int t = cc * 16 + e;
-        const int x = t * DK + wi;
-        float a, pnv, c, kv;
-        if constexpr (C::KEEP) {
-          a = ca[te];
-          pnv = cpn[te];
-          c = cc2[te];
-          kv = ckv[te];
-        } else {
-          const float kk = to_f32(rk[x]);
-          kv = kk * to_f32(rvp[x]);
-          a = __expf(to_f32(rld[x]));
-          pnv = to_f32(rpn[x]);
-          c = kk * kv;
-        }
-        float lam_pred;
-        const float lam_new = lam_step(lam, a * a, pnv, c, lam_pred);
-        const float inv = fast_rcp(lam_new);
-        const float f = a * lam_pred * inv;
-        const float g = kv * inv;
-        cp *= f;
-        wq[te] = to_f32(rq[x]) * cp;
-        wk[te] = g * fast_rcp(cp);
-        fr[e] = f;
-        gr[e] = g;
-        lam = lam_new;
-        if constexpr (PATH) {
-          if (t < nvalid) lp[(size_t)t * DK] = lam;
-        }
-      }
-      s.cpe[cc * DK + wi] = cp;
-      if (!(cp >= 0x1p-64f)) s.unsafe[cc] = 1;
+    for (int k = 0; k < CPT; ++k) {
       float sp = 1.f;
 #pragma unroll
-      for (int e = 15; e >= 0; --e) {
-        wd[cl * 16 + e] = gr[e] * sp;
-        sp *= fr[e];
+      for (int e = 7; e >= 0; --e) {
+        wd[e][k] = gr[e][k] * sp;
+        sp *= fr[e][k];
       }
+      Fg[k] = cp[k];
+      if (last && wc == NCH - 1 && wh) p.lamT[(size_t)head * DK + wch + k] = lam[k];
     }
-    if (last && wr == NG - 1) p.lamT[(size_t)head * DK + wi] = lam;
   };
   if (walker) {
     if (p.lpath)
@@ -374,21 +467,45 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
     else
       walk(std::false_type{});
   }
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const float Fp = __shfl_xor(Fg[k], 32, 64);  // the other half's prod f
+    float cpe;
+    if (wh) {
+      const float r = fast_rcp(Fp);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        wq[e][k] *= Fp;
+        wk[e][k] *= r;
+      }
+      cpe = Fp * Fg[k];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wd[e][k] *= Fp;
+      cpe = Fg[k] * Fp;
+    }
+    if (walker && wh == 0) {
+      s.cpe[wc * DK + wch + k] = cpe;
+      if (!(cpe >= 0x1p-64f)) s.unsafe[wc] = 1;
+    }
+  }
   __syncthreads();
   unsigned char* const Qs = s.u;
   unsigned char* const Ks = s.u + L * QROW;
   unsigned char* const KdT = s.u + 2 * L * QROW;
   if (walker) {
-    const int cb = (wi >> 2) * 16, cj = wi & 3;  // block and slot of channel wi in a row
+    const int cb = (wch >> 2) * 16, cj = wch & 3;  // block and slot of channel wch in a row
 #pragma unroll
-    for (int e = 0; e < TG; ++e) {
-      const int t = wr * TG + e;
-      put1<BF16>(Qs + t * QROW + cb, cj, wq[e]);
-      put1<BF16>(Ks + t * QROW + cb, cj, wk[e]);
+    for (int e = 0; e < 8; ++e) {
+      const int t = wt0 + e;
+      put_vals<BF16, CPT>(Qs + t * QROW + cb, cj, wq[e]);
+      put_vals<BF16, CPT>(Ks + t * QROW + cb, cj, wk[e]);
     }
 #pragma unroll
-    for (int e = 0; e < TG; e += 4)  // Kd^T row wi: four tokens per block
-      M::put(KdT + wi * KROW + (wr * TG + e) * 4, v4f{wd[e], wd[e + 1], wd[e + 2], wd[e + 3]});
+    for (int k = 0; k < CPT; ++k)  // Kd^T row wch + k: four tokens per block
+#pragma unroll
+      for (int e = 0; e < 8; e += 4)
+        M::put(KdT + (wch + k) * KROW + (wt0 + e) * 4, v4f{wd[e][k], wd[e + 1][k], wd[e + 2][k], wd[e + 3][k]});
   }
   if (tid < DK) {
     float F = 1.f;
@@ -636,7 +753,7 @@ __global__ __launch_bounds__(256) void kla_fwd_kernel(FwdParams p) {
   }
   // Every thread read the epoch before the first barrier; count this
   // workgroup done (other waves may still be polling flags of this call).
-  if (nseg > 1 && tid == 0) epoch_done(p.ctrl, p.hdone + head, (unsigned)nseg, (unsigned)nheads, epoch);
+  if (nseg > 1 && tid == 0) epoch_done_grouped(p.ctrl, p.hdone + head, (unsigned)nseg, (unsigned)nheads, epoch);
   if (last) {  // final state, row-major
 #pragma unroll
     for (int pp = 0; pp < CPW; ++pp) {
