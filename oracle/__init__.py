@@ -7,6 +7,8 @@ from the product path.
 """
 from .kla_f64 import (  # noqa: F401
     kla_forward_f64,
+    kla_decode_step_f64,
+    filter_step,
     precision_scan_f64,
     precision_path_from_coeffs,
     predict_precision,

@@ -48,7 +48,8 @@ import numpy as np
 
 __all__ = [
     "predict_precision", "update_precision", "forget_gate", "write_gate", "readout",
-    "kla_forward_f64", "precision_scan_f64", "precision_path_from_coeffs",
+    "filter_step", "kla_forward_f64", "kla_decode_step_f64", "precision_scan_f64",
+    "precision_path_from_coeffs",
 ]
 
 
@@ -103,6 +104,25 @@ def readout(q_t, M):
     return np.einsum("...i,...ij->...j", q_t, M)
 
 
+def filter_step(q_t, k_t, v_t, log_decay_t, proc_noise_t, val_prec_t, lam, M):
+    """One token of every filter: predict, update, gates, mean update, readout.
+
+    Shapes: q_t, k_t, log_decay_t, proc_noise_t, val_prec_t, lam [..., dk];
+    v_t [..., dv]; M [..., dk, dv].  Returns (y_t [..., dv], lam_t [..., dk],
+    M_t [..., dk, dv], f [..., dk], g [..., dk]).
+
+    The mean follows the affine recursion M_t = f M_{t-1} + g v_t ([KLA-nl] §2,
+    the posterior-mean recursion) with the precision-ratio gates of §3.
+    """
+    a = np.exp(log_decay_t)
+    lam_pred = predict_precision(lam, a, proc_noise_t)
+    lam_new = update_precision(lam_pred, k_t * k_t * val_prec_t)
+    f = forget_gate(a, lam_pred, lam_new)
+    g = write_gate(k_t, val_prec_t, lam_new)
+    M_new = f[..., None] * M + g[..., None] * v_t[..., None, :]
+    return readout(q_t, M_new), lam_new, M_new, f, g
+
+
 # --------------------------------------------------------------------------- #
 # Full forward pass.                                                           #
 # --------------------------------------------------------------------------- #
@@ -150,16 +170,8 @@ def kla_forward_f64(q, k, v, log_decay, proc_noise, val_prec, lambda0=None, M0=N
     f_path = np.empty((B, H, T, dk)) if return_gates else None
     g_path = np.empty((B, H, T, dk)) if return_gates else None
     for t in range(T):
-        a = np.exp(ld[:, :, t])
-        kt = k[:, :, t]
-        lt = vp[:, :, t]
-        lam_pred = predict_precision(lam, a, pn[:, :, t])
-        lam_new = update_precision(lam_pred, kt * kt * lt)
-        f = forget_gate(a, lam_pred, lam_new)
-        g = write_gate(kt, lt, lam_new)
-        M = f[..., None] * M + g[..., None] * v[:, :, t, None, :]
-        y[:, :, t] = readout(q[:, :, t], M)
-        lam = lam_new
+        y[:, :, t], lam, M, f, g = filter_step(q[:, :, t], k[:, :, t], v[:, :, t], ld[:, :, t],
+                                               pn[:, :, t], vp[:, :, t], lam, M)
         if return_lambda_path:
             lam_path[:, :, t] = lam
         if return_gates:
@@ -171,6 +183,40 @@ def kla_forward_f64(q, k, v, log_decay, proc_noise, val_prec, lambda0=None, M0=N
     if return_gates:
         out = out + (f_path, g_path)
     return out
+
+
+# --------------------------------------------------------------------------- #
+# Decode: one token per head.                                                  #
+# --------------------------------------------------------------------------- #
+
+def kla_decode_step_f64(q, k, v, log_decay, proc_noise, val_prec, lam, M):
+    """One filter step per head, from the state (lam, M) before the token.
+
+    Shapes: q, k, log_decay, proc_noise, val_prec [B,H,dk]; v [B,H,dv];
+    lam [B,H,dk]; M [B,H,dk,dv].  Returns (y [B,H,dv], lam_new [B,H,dk],
+    M_new [B,H,dk,dv]) in float64: the same step the forward pass takes for
+    every token, so T decode steps from (lambda0, M0) reproduce a forward pass
+    over T tokens.  Raises ValueError on shape mismatches, non-finite inputs or
+    a non-positive lam.
+    """
+    arrs = {n: np.asarray(x, np.float64) for n, x in (("q", q), ("k", k), ("v", v), ("log_decay", log_decay),
+                                                       ("proc_noise", proc_noise), ("val_prec", val_prec),
+                                                       ("lam", lam), ("M", M))}
+    B, H, dk = arrs["k"].shape
+    dv = arrs["v"].shape[-1]
+    want = {"q": (B, H, dk), "log_decay": (B, H, dk), "proc_noise": (B, H, dk), "val_prec": (B, H, dk),
+            "v": (B, H, dv), "lam": (B, H, dk), "M": (B, H, dk, dv)}
+    for n, shp in want.items():
+        if arrs[n].shape != shp:
+            raise ValueError(f"{n} has shape {arrs[n].shape}, expected {shp}")
+    for n, x in arrs.items():
+        if not np.all(np.isfinite(x)):
+            raise ValueError(f"{n} has non-finite entries")
+    if np.any(arrs["lam"] <= 0):
+        raise ValueError("lam must be positive")
+    y, lam_new, M_new, _, _ = filter_step(arrs["q"], arrs["k"], arrs["v"], arrs["log_decay"],
+                                          arrs["proc_noise"], arrs["val_prec"], arrs["lam"], arrs["M"])
+    return y, lam_new, M_new
 
 
 # --------------------------------------------------------------------------- #

@@ -365,9 +365,43 @@ def pin_precision_scan_matches_forward(seed=14):
     np.testing.assert_allclose(l2, lT, rtol=1e-14)
 
 
+# --------------------------------------------------------------------------- #
+# decode step                                                                  #
+# --------------------------------------------------------------------------- #
+
+def pin_decode_covariance_form(seed=15):
+    """One decode step from a random state equals one step of the
+    covariance-form filter started from that state."""
+    rng = np.random.default_rng(seed)
+    q, k, v, ld, pn, vp, lam0, M0 = _rand_inputs(rng, B=3, H=2, T=1, dk=4, dv=5)
+    y, lam, M = O.kla_decode_step_f64(q[:, :, 0], k[:, :, 0], v[:, :, 0], ld[:, :, 0], pn[:, :, 0],
+                                      vp[:, :, 0], lam0, M0)
+    y2, lam2, M2, _ = covariance_form_filter(q, k, v, ld, pn, vp, lam0, M0)
+    np.testing.assert_allclose(lam, lam2, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(M, M2, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(y, y2[:, :, 0], rtol=1e-11, atol=1e-13)
+
+
+def pin_decode_chain_is_dense_posterior(seed=16, T=8):
+    """Decode steps chained from the prior give, at every token, the posterior
+    mean and precision of Gaussian conditioning on the whole history."""
+    rng = np.random.default_rng(seed)
+    q, k, v, ld, pn, vp, lam0, M0 = _rand_inputs(rng, B=1, H=1, T=T, dk=2, dv=2)
+    ref = {(i, j): dense_posterior(np.exp(ld[0, 0, :, i]), pn[0, 0, :, i], k[0, 0, :, i], vp[0, 0, :, i],
+                                   v[0, 0, :, j], lam0[0, 0, i], M0[0, 0, i, j])
+           for i in range(2) for j in range(2)}
+    lam, M = lam0.copy(), M0.copy()
+    for t in range(T):
+        _, lam, M = O.kla_decode_step_f64(q[:, :, t], k[:, :, t], v[:, :, t], ld[:, :, t], pn[:, :, t],
+                                          vp[:, :, t], lam, M)
+        for (i, j), (means, precs) in ref.items():
+            np.testing.assert_allclose(M[0, 0, i, j], means[t], rtol=1e-9, atol=1e-11)
+            np.testing.assert_allclose(lam[0, 0, i], precs[t], rtol=1e-9)
+
+
 ALL_PINS = [
     pin_covariance_form, pin_dense_gaussian, pin_mobius_exact, pin_mobius_mpmath,
     pin_steady_state_dare, pin_no_observation, pin_no_process_noise, pin_least_squares,
     pin_zero_value_precision, pin_invariants, pin_state_carry,
-    pin_precision_scan_matches_forward,
+    pin_precision_scan_matches_forward, pin_decode_covariance_form, pin_decode_chain_is_dense_posterior,
 ]
