@@ -136,7 +136,7 @@ def cpu_baseline(x):
                       f"{wall:.2f} s wall, {cpu:.2f} s CPU"}, y
 
 
-CONFIGS = ("lm45m_bf16", "lm180m_bf16", "long_bf16", "chains_f32")
+CONFIGS = ("lm45m_bf16", "lm180m_bf16", "long_bf16", "chains_f32", "decode_lm45m_bf16", "decode_b256_bf16")
 
 
 def run_configs(only, copies):
@@ -166,6 +166,27 @@ def run_configs(only, copies):
             run = lambda i: K.precision_scan(x["log_decay"], x["proc_noise"], x["obs_prec"], x["lambda0"],
                                              workspace=ws, out=out)
             units, unit, abytes = B * H * T * D, "elements/s", 16 * B * H * T * D
+        elif w.kind == "decode":
+            # One token per head, the state updated in place; enough input and
+            # state copies rotate that the set exceeds the 256 MB last-level cache.
+            B, H, dk, dv = w.B, w.H, w.dk, w.dv
+            abytes = algorithmic_bytes(B, H, 1, dk, dv, 2)
+            ncopy = max(2, min(64, int(1.2e9 // abytes)))
+            xs = []
+            for c in range(ncopy):
+                xc = KI.make_forward_inputs_torch(w, seed=w.seed + c, device=dev)
+                xc = {n: (t.view(B, H, -1) if n in ("q", "k", "v", "log_decay", "proc_noise", "val_prec") else t)
+                      for n, t in xc.items()}
+                xs.append(xc)
+            ys = [torch.empty((B, H, dv), dtype=torch.bfloat16, device=dev) for _ in range(ncopy)]
+            ws = K.Workspace(dev)
+            calls, warm = 100, 10
+
+            def run(i):
+                xc = xs[i % ncopy]
+                return K.decode_step(xc["q"], xc["k"], xc["v"], xc["log_decay"], xc["proc_noise"], xc["val_prec"],
+                                     xc["lambda0"], xc["M0"], out=(ys[i % ncopy], xc["lambda0"], xc["M0"]))
+            units, unit = B * H, "head-steps/s"
         else:
             B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
             esz = 2 if w.dtype == "bf16" else 4

@@ -3,12 +3,12 @@
 Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in include/kla.h.  PyTorch supplies device
 memory and the current stream.  Importing this package loads the library and
-raises if it has not been built (``python -m bius_scan_sequence_amd.build``);
+raises if it has not been built (``python bius_scan_sequence_amd/build.py``);
 there is no fallback implementation.
 
 Low-level functions carry the C names (``kla_forward``, ``kla_precision_scan``,
-``kla_workspace_init``, ...) and take raw pointers; ``forward`` and
-``precision_scan`` are the tensor-level helpers.
+``kla_decode_step``, ``kla_workspace_init``, ...) and take raw pointers;
+``forward``, ``precision_scan`` and ``decode_step`` are the tensor-level helpers.
 """
 from __future__ import annotations
 
@@ -19,15 +19,15 @@ import threading
 __all__ = [
     "LIB_PATH", "lib", "KLA_F32", "KLA_BF16", "KlaError",
     "kla_forward_workspace_bytes", "kla_forward", "kla_precision_scan_workspace_bytes",
-    "kla_precision_scan", "kla_workspace_init", "kla_workspace_error", "kla_status_string",
-    "forward", "precision_scan", "Workspace",
+    "kla_precision_scan", "kla_decode_step", "kla_workspace_init", "kla_workspace_error",
+    "kla_status_string", "forward", "precision_scan", "decode_step", "Workspace",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkla.so")
 KLA_F32, KLA_BF16 = 0, 1
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m bius_scan_sequence_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python bius_scan_sequence_amd/build.py`")
 lib = ctypes.CDLL(LIB_PATH)
 
 _vp, _fp, _sz, _i = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
@@ -39,6 +39,8 @@ lib.kla_precision_scan_workspace_bytes.restype = _sz
 lib.kla_precision_scan_workspace_bytes.argtypes = [_i] * 4
 lib.kla_precision_scan.restype = _i
 lib.kla_precision_scan.argtypes = [_fp] * 6 + [_i] * 4 + [_vp, _sz, _vp]
+lib.kla_decode_step.restype = _i
+lib.kla_decode_step.argtypes = [_vp] * 6 + [_fp] * 4 + [_vp] + [_i] * 5 + [_vp]
 lib.kla_workspace_init.restype = _i
 lib.kla_workspace_init.argtypes = [_vp, _sz, _vp]
 lib.kla_workspace_error.restype = _i
@@ -73,6 +75,12 @@ def kla_precision_scan(log_decay, proc_noise, obs_prec, lambda0, lambda_path, la
                        workspace, workspace_bytes, stream) -> int:
     return int(lib.kla_precision_scan(log_decay, proc_noise, obs_prec, lambda0, lambda_path, lambda_T,
                                       B, H, T, D, workspace, workspace_bytes, stream))
+
+
+def kla_decode_step(q, k, v, log_decay, proc_noise, val_prec, lambda_in, M_in, lambda_out, M_out, y,
+                    B, H, dk, dv, dtype, stream) -> int:
+    return int(lib.kla_decode_step(q, k, v, log_decay, proc_noise, val_prec, lambda_in, M_in, lambda_out,
+                                   M_out, y, B, H, dk, dv, dtype, stream))
 
 
 def kla_workspace_init(workspace, workspace_bytes, stream) -> int:
@@ -229,3 +237,45 @@ def precision_scan(log_decay, proc_noise, obs_prec, lambda0=None, workspace: Wor
     if rc:
         raise KlaError(rc)
     return lpath, lam_T
+
+
+def decode_step(q, k, v, log_decay, proc_noise, val_prec, lam=None, M=None, inplace=True, out=None):
+    """One filter step per head on the current stream (generation, token by token).
+
+    q, k, log_decay, proc_noise, val_prec: [B,H,dk]; v: [B,H,dv]; all bfloat16
+    or all float32.  lam [B,H,dk] and M [B,H,dk,dv] are the float32 state
+    before the token (None: the prior, 1 and 0).  Returns (y [B,H,dv] input
+    dtype, lam_new, M_new).  With ``inplace`` (and a state given) the state
+    tensors are overwritten and returned; otherwise new tensors are returned,
+    or the (y, lam_new, M_new) tensors given in ``out``.
+    """
+    torch = _torch()
+    B, H, dk = k.shape
+    dv = v.shape[-1]
+    dtype, dev = k.dtype, k.device
+    if dtype == torch.bfloat16:
+        code = KLA_BF16
+    elif dtype == torch.float32:
+        code = KLA_F32
+    else:
+        raise ValueError(f"unsupported dtype {dtype}")
+    for name, t, shp in (("q", q, (B, H, dk)), ("k", k, (B, H, dk)), ("v", v, (B, H, dv)),
+                         ("log_decay", log_decay, (B, H, dk)), ("proc_noise", proc_noise, (B, H, dk)),
+                         ("val_prec", val_prec, (B, H, dk))):
+        _check(t, name, shp, dtype, dev)
+    if lam is not None:
+        _check(lam, "lam", (B, H, dk), torch.float32, dev)
+    if M is not None:
+        _check(M, "M", (B, H, dk, dv), torch.float32, dev)
+    if out is not None:
+        y, lam_new, M_new = out
+    else:
+        y = torch.empty((B, H, dv), dtype=dtype, device=dev)
+        lam_new = lam if (inplace and lam is not None) else torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+        M_new = M if (inplace and M is not None) else torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = kla_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(proc_noise), _ptr(val_prec),
+                         _ptr(lam), _ptr(M), _ptr(lam_new), _ptr(M_new), _ptr(y), B, H, dk, dv, code, stream)
+    if rc:
+        raise KlaError(rc)
+    return y, lam_new, M_new

@@ -1,6 +1,6 @@
 """Build libkla.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-    python -m bius_scan_sequence_amd.build        # or: python bius_scan_sequence_amd/build.py
+    python bius_scan_sequence_amd/build.py
 
 Every call recompiles.  Objects go to bius_scan_sequence_amd/_build/, the
 library to bius_scan_sequence_amd/libkla.so.
@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkla.so")
-SOURCES = ["kla_forward.hip", "kla_precision.hip", "kla_util.hip", "kla_api.hip"]
+SOURCES = ["kla_forward.hip", "kla_precision.hip", "kla_decode.hip", "kla_util.hip", "kla_api.hip"]
 ARCH = os.environ.get("KLA_OFFLOAD_ARCH", "gfx950")
 
 

@@ -203,6 +203,31 @@ extern "C" int kla_precision_scan(const float* log_decay, const float* proc_nois
   return e == hipSuccess ? KLA_OK : hip_fail(e, "kla_precision_scan");
 }
 
+extern "C" int kla_decode_step(const void* q, const void* k, const void* v, const void* log_decay,
+                               const void* proc_noise, const void* val_prec, const float* lambda_in,
+                               const float* M_in, float* lambda_out, float* M_out, void* y, int B, int H,
+                               int dk, int dv, int dtype, void* stream) {
+  if (B < 1 || H < 1) return KLA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !log_decay || !proc_noise || !val_prec || !lambda_out || !M_out || !y)
+    return KLA_ERR_INVALID_ARG;
+  if (dtype != KLA_F32 && dtype != KLA_BF16) return KLA_ERR_UNSUPPORTED;
+  if (!supported_width(dk) || !supported_width(dv)) return KLA_ERR_UNSUPPORTED;
+  const long long nheads = (long long)B * H;
+  if (nheads >= (1LL << 31)) return KLA_ERR_INVALID_ARG;
+  const size_t esz = dtype == KLA_BF16 ? 2 : 4;
+  const void* ins[7] = {q, k, v, log_decay, proc_noise, val_prec, y};
+  for (const void* p : ins)
+    if (!aligned(p, esz)) return KLA_ERR_INVALID_ARG;
+  if (!aligned(lambda_out, 4) || !aligned(M_out, 16) || (lambda_in && !aligned(lambda_in, 4)) ||
+      (M_in && !aligned(M_in, 16)))
+    return KLA_ERR_INVALID_ARG;
+  DecodeParams p;
+  p.q = q; p.k = k; p.v = v; p.ld = log_decay; p.pn = proc_noise; p.vp = val_prec;
+  p.lam_in = lambda_in; p.M_in = M_in; p.lam_out = lambda_out; p.M_out = M_out; p.y = y;
+  hipError_t e = launch_decode(p, nheads, dk, dv, dtype == KLA_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KLA_OK : hip_fail(e, "kla_decode_step");
+}
+
 extern "C" int kla_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
   if (!workspace || !aligned(workspace, 256)) return KLA_ERR_WORKSPACE;
   if (workspace_bytes < kHeader || workspace_bytes % 4) return KLA_ERR_INVALID_ARG;

@@ -50,9 +50,24 @@ struct PscanParams {
   float* inc;         // [ncblocks*nseg*256]
 };
 
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* ld;     // log_decay
+  const void* pn;     // proc_noise
+  const void* vp;     // val_prec
+  const float* lam_in;  // nullable (prior precision 1)
+  const float* M_in;    // nullable (prior mean 0)
+  float* lam_out;       // may equal lam_in
+  float* M_out;         // may equal M_in
+  void* y;
+};
+
 int fwd_segment_len(int dk, int dv, bool bf16);
 hipError_t launch_forward(const FwdParams& p, int dk, int dv, bool bf16, hipStream_t stream);
 hipError_t launch_pscan(const PscanParams& p, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, long long nheads, int dk, int dv, bool bf16, hipStream_t stream);
 hipError_t launch_fill_zero(void* ptr, size_t words, hipStream_t stream);
 hipError_t launch_state_copy(const float* lam0, const float* M0, float* lamT, float* MT,
                              long long nl, long long nm, hipStream_t stream);

@@ -24,8 +24,8 @@
  * "Niet-lineaire Gating vanuit Onzekerheid").
  *
  * Conventions for every entry point:
- *   - All tensors are dense, row-major, on the device, not aliased, and owned
- *     by the caller.  The library never allocates or frees device memory and
+ *   - All tensors are dense, row-major, on the device, not aliased (unless an
+ *     entry point allows it), and owned by the caller.  The library never allocates or frees device memory and
  *     never synchronises; work is enqueued on `stream` (a hipStream_t; NULL
  *     means the default stream) and the call returns without waiting.
  *   - Argument validation happens on the host before any HIP call; a
@@ -111,6 +111,38 @@ int kla_precision_scan(const float* log_decay, const float* proc_noise, const fl
                        const float* lambda0, float* lambda_path, float* lambda_T,
                        int B, int H, int T, int D,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode: one filter step per head, for generating token by token.  The same
+ * step the forward pass takes for every token ([KLA-nl] §2: precision
+ * equation and affine mean recursion; §3: precision-ratio gates; §1: readout
+ * of the posterior mean), applied to the state the caller carries.
+ *
+ * Inputs (dtype = KLA_BF16: bfloat16 values; KLA_F32: float32), one token:
+ *   q, k, log_decay, proc_noise, val_prec   [B,H,dk]
+ *   v                                       [B,H,dv]
+ * State before the token (float32, nullable):
+ *   lambda_in [B,H,dk]     posterior precision (NULL: all 1, the prior)
+ *   M_in      [B,H,dk,dv]  posterior mean      (NULL: all 0, the prior)
+ * Outputs:
+ *   lambda_out [B,H,dk]     float32 precision after the token
+ *   M_out      [B,H,dk,dv]  float32 posterior mean after the token
+ *   y          [B,H,dv]     dtype; readout q^T M_out
+ * The state may be updated in place: lambda_out may equal lambda_in and M_out
+ * may equal M_in (the same pointer); any other overlap between arguments is
+ * not allowed.  Starting from (lambda0, M0), T calls reproduce kla_forward
+ * over the same T tokens up to rounding.  No workspace: one kernel, no state
+ * kept between calls.
+ *
+ * Supported: dk, dv in {16, 32, 64, 128}; 1 <= B*H < 2^31.  Alignment:
+ * M_in and M_out 16 bytes, the other arrays their element size.
+ * Arithmetic: float32 throughout.
+ */
+int kla_decode_step(const void* q, const void* k, const void* v,
+                    const void* log_decay, const void* proc_noise, const void* val_prec,
+                    const float* lambda_in, const float* M_in,
+                    float* lambda_out, float* M_out, void* y,
+                    int B, int H, int dk, int dv, int dtype, void* stream);
 
 /* Zero-fills a workspace on `stream` (a fill kernel, no memset node), once
  * before its first use.  bytes must be a multiple of 4. */

@@ -11,6 +11,8 @@ Workloads (names used throughout the repository):
   lm180m_bf16   B=16, H=12, T=2048,  d_k=d_v=64,  bf16, 5% of tokens with val_prec x100
   long_bf16     B=2,  H=16, T=16384, d_k=d_v=128, bf16, long-memory decay
   chains_f32    65536 chains x T=65536 (as B=1, H=1024, D=64), fp32, precision path only
+  decode_lm45m_bf16   one decode step of lm45m_bf16's heads (B=8, H=8, d=64), bf16
+  decode_b256_bf16    one decode step of a batch of 256 sequences (B=256, H=8, d=64), bf16
 
 Distributions (all draws float64, then cast):
   q, k        ~ N(0, 1/d_k)                       (variance 1/d_k)
@@ -42,7 +44,7 @@ __all__ = [
 class Workload:
     index: int
     name: str
-    kind: str            # "forward" or "precision"
+    kind: str            # "forward", "precision" or "decode" (one token per head)
     B: int
     H: int
     T: int
@@ -69,6 +71,8 @@ WORKLOADS = (
              spike_frac=0.05, spike_scale=100.0),
     Workload(3, "long_bf16", "forward", 2, 16, 16384, 128, 128, "bf16", decay_mean=-2.0),
     Workload(4, "chains_f32", "precision", 1, 1024, 65536, 64, 64, "f32"),
+    Workload(5, "decode_lm45m_bf16", "decode", 8, 8, 1, 64, 64, "bf16"),
+    Workload(6, "decode_b256_bf16", "decode", 256, 8, 1, 64, 64, "bf16"),
 )
 
 

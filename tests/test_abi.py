@@ -28,8 +28,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kla_forward", "kla_forward_workspace_bytes", "kla_precision_scan",
-              "kla_precision_scan_workspace_bytes", "kla_workspace_init", "kla_workspace_error",
-              "kla_status_string"):
+              "kla_precision_scan_workspace_bytes", "kla_decode_step", "kla_workspace_init",
+              "kla_workspace_error", "kla_status_string"):
         assert n in names
 
 
@@ -98,6 +98,26 @@ def pscan(K, **over):
 ])
 def test_precision_scan_rejects(K, over, code):
     assert pscan(K, **over) == code
+
+
+def dec(K, **over):
+    args = dict(q=A, k=A, v=A, log_decay=A, proc_noise=A, val_prec=A, lambda_in=None, M_in=None,
+                lambda_out=A, M_out=A, y=A, B=2, H=3, dk=64, dv=64, dtype=1, stream=None)
+    args.update(over)
+    return K.kla_decode_step(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), INVALID), (dict(v=None), INVALID), (dict(y=None), INVALID),
+    (dict(lambda_out=None), INVALID), (dict(M_out=None), INVALID),
+    (dict(B=0), INVALID), (dict(H=-2), INVALID), (dict(B=1 << 16, H=1 << 15), INVALID),
+    (dict(dk=48), UNSUPPORTED), (dict(dv=8), UNSUPPORTED), (dict(dtype=3), UNSUPPORTED),
+    (dict(q=A + 1), INVALID), (dict(k=A + 2, dtype=0), INVALID), (dict(y=A + 1), INVALID),
+    (dict(M_out=A + 4), INVALID), (dict(M_in=A + 8), INVALID), (dict(lambda_in=A + 2), INVALID),
+    (dict(lambda_out=A + 1), INVALID),
+])
+def test_decode_step_rejects(K, over, code):
+    assert dec(K, **over) == code
 
 
 def test_workspace_init_rejects(K):
