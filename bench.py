@@ -143,7 +143,9 @@ def run_configs(only, copies):
     """Kernel time of each workload at its full shape, one JSON line per
     workload: forward workloads as 5 warm-up and 20 timed calls over rotating
     device-side input copies, the precision-only scan as 1 warm-up and 3
-    timed calls; HIP events on the launch stream around every call."""
+    timed calls, with HIP events on the launch stream around every call;
+    decode workloads as 10 warm-up and 100 timed back-to-back calls between
+    one event pair."""
     import numpy as np
     import torch
     import bius_scan_sequence_amd as K
@@ -187,6 +189,26 @@ def run_configs(only, copies):
                 return K.decode_step(xc["q"], xc["k"], xc["v"], xc["log_decay"], xc["proc_noise"], xc["val_prec"],
                                      xc["lambda0"], xc["M0"], out=(ys[i % ncopy], xc["lambda0"], xc["M0"]))
             units, unit = B * H, "head-steps/s"
+            # A decode call lasts a few microseconds, less than an event pair
+            # around each call adds; time back-to-back calls instead (what a
+            # generation loop sees, launch gaps included).
+            for i in range(warm):
+                run(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(calls):
+                run(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            mean_s = e0.elapsed_time(e1) / 1e3 / calls
+            print(json.dumps({"config": name, "calls": calls, "timing": "back-to-back",
+                              "kernel_ms_mean": mean_s * 1e3, "value": units / mean_s, "unit": unit,
+                              "algorithmic_bytes": abytes, "achieved_GBps": abytes / mean_s / 1e9,
+                              "frac_of_8TBps": abytes / mean_s / 8e12}), flush=True)
+            x = xs = ys = run = None
+            torch.cuda.empty_cache()
+            continue
         else:
             B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
             esz = 2 if w.dtype == "bf16" else 4
