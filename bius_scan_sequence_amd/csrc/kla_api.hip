@@ -43,7 +43,7 @@ FwdLayout fwd_layout(int B, int H, int T, int dk, int dv, int nseg) {
   l.pflag = o; o += round256(slots * 2 * 4);  // one flag per carry wave (two when dk = 128)
   l.mflag = o; o += round256(slots * 4 * 4);  // one flag per wave
   l.pagg = o; o += round256(slots * dk * 16);
-  l.pinc = o; o += round256(slots * dk * 4);
+  l.pinc = o; o += round256(slots * dk * 8);  // {value, flag} records
   l.mF = o; o += round256(slots * 4 * dk * 4);  // one copy per wave
   l.magg = o; o += round256(slots * (size_t)dk * dv * 4);
   l.minc = o; o += round256(slots * (size_t)dk * dv * 4);
@@ -157,7 +157,7 @@ extern "C" int kla_forward(const void* q, const void* k, const void* v, const vo
   p.pflag = reinterpret_cast<unsigned*>(ws + l.pflag);
   p.mflag = reinterpret_cast<unsigned*>(ws + l.mflag);
   p.pagg = reinterpret_cast<float*>(ws + l.pagg);
-  p.pinc = reinterpret_cast<float*>(ws + l.pinc);
+  p.pinc = reinterpret_cast<unsigned long long*>(ws + l.pinc);
   p.mF = reinterpret_cast<float*>(ws + l.mF);
   p.magg = reinterpret_cast<float*>(ws + l.magg);
   p.minc = reinterpret_cast<float*>(ws + l.minc);

@@ -208,11 +208,11 @@ __device__ __forceinline__ Mob mob_mul(Mob A, Mob B) {
   return mob_normalize(n);
 }
 
-// The Möbius map of P applied to lam.  Every fold of carries uses this one
-// function, so the carried precision is the same bits whichever predecessor
-// a look-back starts from.
+// The Möbius map of P applied to lam (hardware reciprocal: about 1 ulp).
+// Every fold of carries uses this one function, so the carried precision is
+// the same bits whichever predecessor a look-back starts from.
 __device__ __forceinline__ float mob_apply(Mob P, float lam) {
-  return fmaf(P.m00, lam, P.m01) / fmaf(P.m10, lam, P.m11);
+  return fmaf(P.m00, lam, P.m01) * fast_rcp(fmaf(P.m10, lam, P.m11));
 }
 
 // Scalar predict/update step; returns lam_t and writes lam^-.
@@ -260,6 +260,20 @@ __device__ __forceinline__ unsigned ld_relaxed(const unsigned* p) {
 __device__ __forceinline__ void st_relaxed(unsigned* p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A float published together with its flag in one 64-bit word (value bits
+// low, flag high).  Aligned 64-bit accesses are single-copy atomic, so a
+// reader that sees the flag sees the value stored with it, without waiting
+// for any other store.
+__device__ __forceinline__ void st_record(unsigned long long* p, float v, unsigned flag) {
+  __hip_atomic_store(p, ((unsigned long long)flag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long ld_record(const unsigned long long* p) {
+  return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float record_value(unsigned long long r) { return __uint_as_float((unsigned)r); }
+__device__ __forceinline__ unsigned record_flag(unsigned long long r) { return (unsigned)(r >> 32); }
+
 // Wait until this thread's outstanding memory operations have completed.
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 

@@ -267,6 +267,13 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
   __syncthreads();
   const unsigned epoch = (unsigned)s.ctl[1];
   const unsigned FAGG = 2u * epoch + 2u, FINC = 2u * epoch + 3u;
+  // The precision carry waves ask for the predecessor's inclusive precision
+  // record now; if it has been published by the end of the aggregate walk,
+  // the look-back is skipped (see section 2).
+  constexpr int PW = (DK + 63) / 64;  // precision carry waves
+  const bool pwave = wave < PW, pch = tid < DK;
+  unsigned long long early = 0ull;
+  if (pwave && pch && seg > 0) early = ld_record(p.pinc + (hb + seg - 1) * DK + tid);
 
   // ---------------------------------------------------------------- 1. chunk aggregates
   // Walker (chunk wc = wave, half wh, channel group wg) owns channels
@@ -324,57 +331,67 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
   // ---------------------------------------------------------------- 2. precision carry
   // The carry waves (one lane per channel; a second wave when DK = 128) each
   // run their own look-back over their channels, with flags of their own, so
-  // no workgroup barrier sits inside the carry.  The first flag poll is issued
-  // before waiting for the aggregate's stores, and the inclusive carry's flag
-  // is raised after the barrier that releases the other waves.
-  constexpr int PW = (DK + 63) / 64;  // carry waves
-  const bool pwave = wave < PW, pch = tid < DK;
+  // no workgroup barrier sits inside the carry.  The inclusive precision of a
+  // segment is published as {value, flag} records.  When the predecessor's
+  // records, requested before the aggregate walk, already carry this call's
+  // flag, they are the precision entering the segment: no aggregate is
+  // published and no look-back runs (successors then wait for this segment's
+  // inclusive flag, which follows at once).  Otherwise the aggregate is
+  // published first; the first flag poll is issued before waiting for its
+  // stores.  The inclusive flag is raised after the barrier that releases
+  // the other waves.
   unsigned* const pfl = p.pflag + hb * 2 + wave;  // flag of segment r: pfl[2 * r]
   if (pwave) {
-    Mob cg[NCH];
-    Mob Pseg = mob_identity();
+    // pre[c]: the map from the segment start to the start of chunk c + 1.
+    Mob pre[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      cg[c] = mob_identity();
+      Mob cg = mob_identity();
       if (pch) {
         const v4f d = ld4(s.cagg() + (c * DK + tid) * 4);
-        cg[c] = Mob{d[0], d[1], d[2], d[3]};
+        cg = Mob{d[0], d[1], d[2], d[3]};
       }
-      Pseg = mob_mul(cg[c], Pseg);
+      pre[c] = c == 0 ? cg : mob_mul(cg, pre[c - 1]);
     }
+    const Mob Pseg = pre[NCH - 1];
     float lam_in = 1.f;
+    const bool fast = seg > 0 && __ballot(pch && record_flag(early) != FINC) == 0ull;
     if (seg == 0) {
       if (pch && p.lam0) lam_in = p.lam0[(size_t)head * DK + tid];
+    } else if (fast) {
+      lam_in = pch ? record_value(early) : 1.f;
     } else {
       if (!last && pch) {  // publish the aggregate first so successors need not wait on us
         const auto r = coherent_rsrc(p.pagg + hs * DK * 4, DK * 16);
         st_coherent(r, tid * 16, v4f{Pseg.m00, Pseg.m01, Pseg.m10, Pseg.m11});
       }
       const unsigned f0 = lookback_peek(pfl, 2, seg - 1);
+      // A second look at the predecessor's records, in the same round trip.
+      const unsigned long long again = pch ? ld_record(p.pinc + (hb + seg - 1) * DK + tid) : 0ull;
       wait_stores();
       if (!last && lane == 0) st_relaxed(pfl + 2 * seg, FAGG);
-      const int r0 = lookback_find(pfl, 2, seg, FAGG, FINC, p.ctrl, f0);
-      // Fold the carries of segments r0 .. seg-1, loading up to eight at once.
-      float lam = pch ? ld_coherent(p.pinc + (hb + r0) * DK + tid) : 1.f;
-      for (int u0 = r0 + 1; u0 < seg; u0 += 8) {
-        v4f m[8];
+      if (__ballot(pch && record_flag(again) != FINC) == 0ull) {
+        lam_in = pch ? record_value(again) : 1.f;
+      } else {
+        const int r0 = lookback_find(pfl, 2, seg, FAGG, FINC, p.ctrl, f0);
+        // Fold the carries of segments r0 .. seg-1, loading up to eight at once.
+        float lam = pch ? record_value(ld_record(p.pinc + (hb + r0) * DK + tid)) : 1.f;
+        for (int u0 = r0 + 1; u0 < seg; u0 += 8) {
+          v4f m[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (u0 + j < seg) m[j] = ld_coherent(coherent_rsrc(p.pagg + (hb + u0 + j) * DK * 4, DK * 16), tid * 16);
+          for (int j = 0; j < 8; ++j)
+            if (u0 + j < seg) m[j] = ld_coherent(coherent_rsrc(p.pagg + (hb + u0 + j) * DK * 4, DK * 16), tid * 16);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (u0 + j < seg) lam = mob_apply(Mob{m[j][0], m[j][1], m[j][2], m[j][3]}, lam);
+          for (int j = 0; j < 8; ++j)
+            if (u0 + j < seg) lam = mob_apply(Mob{m[j][0], m[j][1], m[j][2], m[j][3]}, lam);
+        }
+        lam_in = lam;
       }
-      lam_in = lam;
     }
-    if (!last && pch) st_coherent(p.pinc + hs * DK + tid, mob_apply(Pseg, lam_in));
+    if (!last && pch) st_record(p.pinc + hs * DK + tid, mob_apply(Pseg, lam_in), FINC);
     if (pch) {  // precision entering every chunk
-      float lam = lam_in;
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        s.lamc[c * DK + tid] = lam;
-        if (c + 1 < NCH) lam = mob_apply(cg[c], lam);
-      }
+      for (int c = 0; c < NCH; ++c) s.lamc[c * DK + tid] = c == 0 ? lam_in : mob_apply(pre[c - 1], lam_in);
     }
   }
   __syncthreads();

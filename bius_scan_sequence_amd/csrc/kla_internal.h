@@ -28,7 +28,7 @@ struct FwdParams {
   unsigned* pflag;    // [nheads*nseg][2] precision-carry flags, one per carry wave
   unsigned* mflag;    // [nheads*nseg][4] mean-carry flags, one per wave
   float* pagg;        // [nheads*nseg][dk][4] segment 2x2 aggregates
-  float* pinc;        // [nheads*nseg][dk]    precision after the segment
+  unsigned long long* pinc;  // [nheads*nseg][dk] precision after the segment: {value bits, flag}
   float* mF;          // [nheads*nseg][4][dk] prod of forget gates over the segment (per wave)
   float* magg;        // [nheads*nseg][dk*dv] local mean state (fragment order)
   float* minc;        // [nheads*nseg][dk*dv] mean state after the segment (fragment order)
