@@ -97,6 +97,16 @@ __device__ __forceinline__ v4f mma_f32(v4f acc, v4f a, v4f b) {
   return acc;
 }
 
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of
+// 16 lanes, lane i receives element i % 4 of the 8-byte rows read by lanes
+// 4r + i / 4 (as element r, r = 0..3): the 4 x 16 block the group reads as
+// sixteen 4-element pieces comes back transposed.  (Lane layout checked on
+// the device with a probe that filled LDS with each element's own index.)
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+__device__ __forceinline__ v4s lds_read_tr16(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+}
+
 // Operand policy per input dtype.
 //   Op   one K=16 block of a gated fp32 operand.  bf16 inputs: the block's hi
 //        and lo parts as one 8-element vector [hi0..3 | lo0..3] (so an A-side

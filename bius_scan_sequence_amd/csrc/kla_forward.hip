@@ -57,12 +57,23 @@ struct FwdCfg {
   // fp32: the 4 values), rows padded by 16 bytes against bank conflicts.
   static constexpr int QROW = DK * 4 + 16;                              // Qs / Ks row (bytes)
   static constexpr int KROW = L * 4 + 16;                               // Kd^T row (bytes)
+  // bf16: the chunk recursion reads Ks^T straight from the Ks rows with
+  // transposing LDS loads; fp32 keeps a separate Kd^T copy.
+  static constexpr bool KST = BF16;
   static constexpr int RAW_BYTES = 5 * L * DK * (int)sizeof(In);        // q, k, ld, pn, vp
-  static constexpr int OPS_BYTES = 2 * L * QROW + DK * KROW;            // Qs, Ks, Kd^T
+  static constexpr int OPS_BYTES = 2 * L * QROW + (KST ? 0 : DK * KROW);  // Qs, Ks[, Kd^T]
   static constexpr int UNION_BYTES = RAW_BYTES > OPS_BYTES ? RAW_BYTES : OPS_BYTES;
   static constexpr int A_BYTES = NCH * 64 * 16;                         // per chunk: scores, A-operand order
+  static constexpr int RED_BYTES = 2 * 256 * 4;                         // exact path: per-wave partial sums
   static constexpr int CAGG_BYTES = NCH * DK * 16;                      // chunk 2x2 aggregates
-  static constexpr int AP_BYTES = A_BYTES > CAGG_BYTES ? A_BYTES : CAGG_BYTES;
+  // Once the gate walk is done, the raw tiles beyond the stored operands are
+  // free: the scores and the exact path's partial sums go there if they fit.
+  static constexpr bool TAIL = RAW_BYTES - OPS_BYTES >= A_BYTES + RED_BYTES;
+  // The chunk aggregates are needed only until the precision carry is done,
+  // before v is staged: they use v's space when it is large enough.
+  static constexpr bool CAGG_IN_V = CAGG_BYTES <= L * DV * (int)sizeof(In);
+  static constexpr int AP_A = TAIL ? 0 : A_BYTES, AP_C = CAGG_IN_V ? 0 : CAGG_BYTES;
+  static constexpr int AP_BYTES = (AP_A > AP_C ? AP_A : AP_C) > 16 ? (AP_A > AP_C ? AP_A : AP_C) : 16;
   // The readout of the chunk states waits for the carried state when the
   // per-chunk local states fit in registers (NRT*CPW <= 4 tiles per lane);
   // otherwise it runs in the chunk loop and a correction adds the carry.
@@ -77,21 +88,26 @@ struct FwdSmem {
   using C = FwdCfg<DK, DV, BF16>;
   using In = typename C::In;
   // Raw inputs q, k, ld, pn, vp ([L][DK] each) until the gate walk is done;
-  // afterwards the stored operands Qs [L][QROW], Ks [L][QROW], Kd^T [DK][KROW].
+  // afterwards the stored operands Qs [L][QROW], Ks [L][QROW] (Kd in the rows
+  // of an unsafe chunk when KST) and, without KST, Kd^T [DK][KROW].
   alignas(16) unsigned char u[C::UNION_BYTES];
-  alignas(16) In v[C::L * DV];             // raw v; staged y at the end
-  // Chunk 2x2 aggregates until the precision carry is done; then the causal
-  // intra-chunk scores of every chunk in A-operand order.
+  // Chunk 2x2 aggregates until the precision carry is done (when CAGG_IN_V),
+  // then raw v; staged y at the end.
+  alignas(16) In v[C::L * DV];
+  // Chunk aggregates and / or the causal intra-chunk scores of every chunk in
+  // A-operand order, for the parts that have no place elsewhere.
   alignas(16) unsigned char ap[C::AP_BYTES];
   alignas(16) float cpe[C::NCH * DK];      // per chunk: prod of f over the chunk
   float lamc[C::NCH * DK];                 // per chunk: precision entering the chunk
   alignas(16) float fseg[DK];              // prod of f over the segment
-  float red[2 * 256];                      // exact path: per-wave partial sums
+  float red[C::TAIL ? 4 : C::RED_BYTES / 4];
   int unsafe[C::NCH];
   int ctl[4];
 
   __device__ In* raw(int which) { return reinterpret_cast<In*>(u) + which * C::L * DK; }
-  __device__ float* cagg() { return reinterpret_cast<float*>(ap); }
+  __device__ float* cagg() { return C::CAGG_IN_V ? reinterpret_cast<float*>(v) : reinterpret_cast<float*>(ap); }
+  __device__ unsigned char* scores() { return C::TAIL ? u + C::OPS_BYTES : ap; }
+  __device__ float* partial() { return C::TAIL ? reinterpret_cast<float*>(u + C::OPS_BYTES + C::A_BYTES) : red; }
 };
 
 // Copy one [rows x width] tile between global memory and LDS (16-byte units;
@@ -215,7 +231,9 @@ __device__ __forceinline__ void put_vals(unsigned char* block, int j, const floa
 }
 
 // Waves per SIMD the kernel is compiled for: two workgroups per compute unit
-// (at most 256 registers per lane) when two fit in LDS, else one.
+// (at most 256 registers per lane) when two fit in LDS, else one.  (Three
+// fit in LDS at d = 64 but were slower: the 168-register budget spills and
+// twelve segments of a head in flight deepen the look-backs.)
 template <int DK, int DV, bool BF16>
 constexpr int fwd_waves_per_eu() {
   return sizeof(FwdSmem<DK, DV, BF16>) <= 80 * 1024 ? 2 : 1;
@@ -325,7 +343,7 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
     if (walker && wh == 0) *reinterpret_cast<v4f*>(s.cagg() + (wc * DK + wch + k) * 4) = v4f{Pc.m00, Pc.m01, Pc.m10, Pc.m11};
   }
   store_tile<In, L, DK>(rq, bq, tid);
-  store_tile<In, L, DV>(s.v, bv, tid);
+  if constexpr (!C::CAGG_IN_V) store_tile<In, L, DV>(s.v, bv, tid);
   __syncthreads();
 
   // ---------------------------------------------------------------- 2. precision carry
@@ -399,6 +417,7 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
     wait_stores();
     if (lane == 0) st_relaxed(pfl + 2 * seg, FINC);
   }
+  if constexpr (C::CAGG_IN_V) store_tile<In, L, DV>(s.v, bv, tid);  // the aggregates are consumed
 
   // ---------------------------------------------------------------- 3. gate walk
   // Results stay in registers until every walker has finished reading the raw
@@ -484,10 +503,16 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
     else
       walk(std::false_type{});
   }
+  // A chunk is unsafe when some channel's prod f over it falls below 2^-64
+  // (Ks = g / cp could overflow); wave wc walks chunk wc, so the decision is
+  // uniform over the wave.
+  bool unsafe_w = false;
+  float FpA[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
-    const float Fp = __shfl_xor(Fg[k], 32, 64);  // the other half's prod f
-    float cpe;
+    const float Fp = FpA[k] = __shfl_xor(Fg[k], 32, 64);  // the other half's prod f
+    const float cpe = wh ? Fp * Fg[k] : Fg[k] * Fp;
+    unsafe_w |= __ballot(walker && !(cpe >= 0x1p-64f)) != 0ull;
     if (wh) {
       const float r = fast_rcp(Fp);
 #pragma unroll
@@ -495,34 +520,39 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
         wq[e][k] *= Fp;
         wk[e][k] *= r;
       }
-      cpe = Fp * Fg[k];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) wd[e][k] *= Fp;
-      cpe = Fg[k] * Fp;
     }
-    if (walker && wh == 0) {
-      s.cpe[wc * DK + wch + k] = cpe;
-      if (!(cpe >= 0x1p-64f)) s.unsafe[wc] = 1;
+    if (walker && wh == 0) s.cpe[wc * DK + wch + k] = cpe;
+  }
+  if (walker && unsafe_w && lane == 0) s.unsafe[wc] = 1;
+  if (walker && (unsafe_w || !C::KST)) {  // Kd is stored: rescale the first half to the chunk end
+    if (!wh) {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wd[e][k] *= FpA[k];
     }
   }
   __syncthreads();
   unsigned char* const Qs = s.u;
   unsigned char* const Ks = s.u + L * QROW;
-  unsigned char* const KdT = s.u + 2 * L * QROW;
+  unsigned char* const KdT = s.u + 2 * L * QROW;  // without KST only
   if (walker) {
     const int cb = (wch >> 2) * 16, cj = wch & 3;  // block and slot of channel wch in a row
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int t = wt0 + e;
       put_vals<BF16, CPT>(Qs + t * QROW + cb, cj, wq[e]);
-      put_vals<BF16, CPT>(Ks + t * QROW + cb, cj, wk[e]);
+      // With KST the rows of an unsafe chunk hold Kd (its scores take the
+      // exact path and never read Ks).
+      put_vals<BF16, CPT>(Ks + t * QROW + cb, cj, (C::KST && unsafe_w) ? wd[e] : wk[e]);
     }
+    if constexpr (!C::KST) {
 #pragma unroll
-    for (int k = 0; k < CPT; ++k)  // Kd^T row wch + k: four tokens per block
+      for (int k = 0; k < CPT; ++k)  // Kd^T row wch + k: four tokens per block
 #pragma unroll
-      for (int e = 0; e < 8; e += 4)
-        M::put(KdT + (wch + k) * KROW + (wt0 + e) * 4, v4f{wd[e][k], wd[e + 1][k], wd[e + 2][k], wd[e + 3][k]});
+        for (int e = 0; e < 8; e += 4)
+          M::put(KdT + (wch + k) * KROW + (wt0 + e) * 4, v4f{wd[e][k], wd[e + 1][k], wd[e + 2][k], wd[e + 3][k]});
+    }
   }
   if (tid < DK) {
     float F = 1.f;
@@ -539,7 +569,7 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
   // re-derives f, g of its channel (same instructions as the walk, raw inputs
   // from global memory) and the channels are summed with wave reductions, in
   // a fixed order.
-  unsigned char* const A = s.ap;
+  unsigned char* const A = s.scores();
 #pragma unroll 1
   for (int cc = 0; cc < NCH; ++cc) {
     if (!s.unsafe[cc]) continue;  // uniform: every thread reads the same flag
@@ -579,7 +609,7 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
       for (int tt = uu; tt < 16; ++tt) {
         if (tt > uu) d *= chan ? f[tt] : 0.f;
         const float part = wave_sum(chan ? q[tt] * d : 0.f);
-        if (lane == 0 && wave < (DK + 63) / 64) s.red[wave * 256 + tt * 16 + uu] = part;
+        if (lane == 0 && wave < (DK + 63) / 64) s.partial()[wave * 256 + tt * 16 + uu] = part;
       }
     }
     __syncthreads();
@@ -587,7 +617,7 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
       const int tt = tid >> 4, uu = tid & 15;
       float acc = 0.f;
       if (uu <= tt)
-        for (int w = 0; w < (DK + 63) / 64; ++w) acc += s.red[w * 256 + tt * 16 + uu];
+        for (int w = 0; w < (DK + 63) / 64; ++w) acc += s.partial()[w * 256 + tt * 16 + uu];
       put1<BF16>(A + (cc * 64 + tt + 16 * (uu >> 2)) * 16, uu & 3, acc);
     }
     __syncthreads();
@@ -648,9 +678,23 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
           yl[cc][pp] = acc;
 #pragma unroll
           for (int mt = 0; mt < NRT; ++mt) {
-            const v4f m = cc == 0 ? Macc[mt][pp] : Macc[mt][pp] * ld4(s.cpe + cc * DK + 16 * mt + 4 * lg);
-            const Op kdo = M::get(KdT + (16 * mt + lc) * KROW + (cc * 16 + 4 * lg) * 4);
-            Macc[mt][pp] = M::dotv(m, kdo, vo);
+            const v4f ce = ld4(s.cpe + cc * DK + 16 * mt + 4 * lg);
+            if constexpr (C::KST) {
+              // Ks^T block (channels 16mt.., tokens of chunk cc) read transposed
+              // from the Ks rows: input lane j of a 16-lane group reads the hi
+              // (then lo) half of block 4mt + j%4 in token row 4*(l/16) + j/4.
+              const int j = lane & 15;
+              const unsigned char* a = Ks + (cc * 16 + 4 * lg + (j >> 2)) * QROW + (4 * mt + (j & 3)) * 16;
+              const Op kso = cat(lds_read_tr16(a), lds_read_tr16(a + 8));
+              if (s.unsafe[cc])  // rows hold Kd: M' = diag(cp_end) M + Kd^T V
+                Macc[mt][pp] = M::dotv(Macc[mt][pp] * ce, kso, vo);
+              else  // M' = diag(cp_end) (M + Ks^T V), since Kd = Ks cp_end
+                Macc[mt][pp] = M::dotv(Macc[mt][pp], kso, vo) * ce;
+            } else {
+              const v4f m = cc == 0 ? Macc[mt][pp] : Macc[mt][pp] * ce;
+              const Op kdo = M::get(KdT + (16 * mt + lc) * KROW + (cc * 16 + 4 * lg) * 4);
+              Macc[mt][pp] = M::dotv(m, kdo, vo);
+            }
             if constexpr (C::DEFER) {
               if (cc + 1 < NCH) Mkeep[cc + 1 < NKEEP ? cc + 1 : 0][mt][pp] = Macc[mt][pp];
             }
