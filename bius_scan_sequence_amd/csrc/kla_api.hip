@@ -41,10 +41,10 @@ FwdLayout fwd_layout(int B, int H, int T, int dk, int dv, int nseg) {
   size_t o = kHeader;
   l.hdone = o; o += round256((size_t)B * H * 4);
   l.pflag = o; o += round256(slots * 2 * 4);  // one flag per carry wave (two when dk = 128)
-  l.mflag = o; o += round256(slots * 4 * 4);  // one flag per wave
+  l.mflag = o; o += round256(slots * 8 * 4);  // one flag per wave (up to eight)
   l.pagg = o; o += round256(slots * dk * 16);
   l.pinc = o; o += round256(slots * dk * 8);  // {value, flag} records
-  l.mF = o; o += round256(slots * 4 * dk * 4);  // one copy per wave
+  l.mF = o; o += round256(slots * 8 * dk * 4);  // one copy per wave (up to eight)
   l.magg = o; o += round256(slots * (size_t)dk * dv * 4);
   l.minc = o; o += round256(slots * (size_t)dk * dv * 4);
   l.total = o;

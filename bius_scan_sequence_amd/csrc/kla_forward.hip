@@ -9,7 +9,7 @@
 //   §3 "Niet-lineaire Gating vanuit Onzekerheid"   gates are precision ratios
 //   §4 "Architectuur"                       expanded states never go to HBM
 //
-// Decomposition.  One workgroup (256 threads, four wave64s) owns one segment
+// Decomposition.  One workgroup (four wave64s; eight for bf16 at d_k = 128) owns one segment
 // of L tokens of one head (b,h).  The segment's inputs are staged once in LDS.
 //   1. Each walker thread (channel i, token group r) composes the 2x2 step
 //      matrices of its tokens; the segment aggregate is the product of the
@@ -44,15 +44,21 @@ template <int DK, int DV, bool BF16>
 struct FwdCfg {
   using In = typename std::conditional<BF16, uint16_t, float>::type;
   static constexpr int L = (BF16 || (DK <= 64 && DV <= 64)) ? 64 : 32;  // tokens per segment
-  static constexpr int NT = 256;
+  // Waves per workgroup: eight for bf16 at d_k = 128 (two walker waves per
+  // chunk and one state column tile per wave keep the registers of a lane
+  // within 256, so two waves share each SIMD), else four.
+  static constexpr int NW = (BF16 && DK == 128) ? 8 : 4;
+  static constexpr int NT = 64 * NW;                                    // threads
   static constexpr int NCH = L / 16;                                    // 16-token chunks
   // Walkers: one thread per (channel group of CPT channels, half chunk of 8
-  // tokens); wave c walks chunk c, the halves of the chunk in lanes l and l ^ 32.
-  static constexpr int CPT = DK >= 64 ? DK / 32 : 1;                    // channels per walker
-  static_assert(NCH <= 4, "one walker wave per chunk");
+  // tokens); wave w walks chunk w % 4 (channel part w / 4), the halves of the
+  // chunk in lanes l and l ^ 32.
+  static constexpr int WPC = NW / 4;                                    // walker waves per chunk
+  static constexpr int CPT = DK >= 64 ? DK / (32 * WPC) : 1;            // channels per walker
+  static_assert(NCH <= 4, "one walker wave group per chunk");
   static constexpr int NRT = DK / 16;                                   // state row tiles
   static constexpr int NCT = DV / 16;                                   // state col tiles
-  static constexpr int CPW = (NCT + 3) / 4;                             // col tiles per wave
+  static constexpr int CPW = (NCT + NW - 1) / NW;                       // col tiles per wave
   // Stored operands: 16 bytes per 4 consecutive values (bf16: [hi x4 | lo x4];
   // fp32: the 4 values), rows padded by 16 bytes against bank conflicts.
   static constexpr int QROW = DK * 4 + 16;                              // Qs / Ks row (bytes)
@@ -65,6 +71,7 @@ struct FwdCfg {
   static constexpr int UNION_BYTES = RAW_BYTES > OPS_BYTES ? RAW_BYTES : OPS_BYTES;
   static constexpr int A_BYTES = NCH * 64 * 16;                         // per chunk: scores, A-operand order
   static constexpr int RED_BYTES = 2 * 256 * 4;                         // exact path: per-wave partial sums
+  static_assert(DK <= 128, "exact-path partial sums: at most two channel waves");
   static constexpr int CAGG_BYTES = NCH * DK * 16;                      // chunk 2x2 aggregates
   // Once the gate walk is done, the raw tiles beyond the stored operands are
   // free: the scores and the exact path's partial sums go there if they fit.
@@ -114,57 +121,57 @@ struct FwdSmem {
 // width*sizeof(In) is a multiple of 32 bytes for every supported width).
 // Loads zero rows past `nvalid`: zeros are an identity filter step (a = 1,
 // pbar = 0, c = 0) and contribute nothing to y.
-template <typename In, int ROWS, int WIDTH>
+template <typename In, int ROWS, int WIDTH, int NT>
 __device__ __forceinline__ void stage_tile(In* dst, const In* src, int nvalid, int tid) {
   constexpr int UNITS = ROWS * WIDTH * (int)sizeof(In) / 16;
   constexpr int PER_UNIT = 16 / (int)sizeof(In);
   const int valid_units = nvalid * WIDTH / PER_UNIT;
   const uint4* s4 = reinterpret_cast<const uint4*>(src);
   uint4* d4 = reinterpret_cast<uint4*>(dst);
-  uint4 buf[(UNITS + 255) / 256];
+  uint4 buf[(UNITS + NT - 1) / NT];
 #pragma unroll
-  for (int it = 0; it < (UNITS + 255) / 256; ++it) {
-    int u = tid + it * 256;
+  for (int it = 0; it < (UNITS + NT - 1) / NT; ++it) {
+    int u = tid + it * NT;
     buf[it] = (u < valid_units) ? s4[u] : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
-  for (int it = 0; it < (UNITS + 255) / 256; ++it) {
-    int u = tid + it * 256;
+  for (int it = 0; it < (UNITS + NT - 1) / NT; ++it) {
+    int u = tid + it * NT;
     if (u < UNITS) d4[u] = buf[it];
   }
 }
 // The two halves of stage_tile, for overlapping a load with other work.
-template <typename In, int ROWS, int WIDTH>
-__device__ __forceinline__ void load_tile(uint4 (&buf)[(ROWS * WIDTH * (int)sizeof(In) / 16 + 255) / 256],
+template <typename In, int ROWS, int WIDTH, int NT>
+__device__ __forceinline__ void load_tile(uint4 (&buf)[(ROWS * WIDTH * (int)sizeof(In) / 16 + NT - 1) / NT],
                                           const In* src, int nvalid, int tid) {
   constexpr int UNITS = ROWS * WIDTH * (int)sizeof(In) / 16;
   constexpr int PER_UNIT = 16 / (int)sizeof(In);
   const int valid_units = nvalid * WIDTH / PER_UNIT;
   const uint4* s4 = reinterpret_cast<const uint4*>(src);
 #pragma unroll
-  for (int it = 0; it < (UNITS + 255) / 256; ++it) {
-    int u = tid + it * 256;
+  for (int it = 0; it < (UNITS + NT - 1) / NT; ++it) {
+    int u = tid + it * NT;
     buf[it] = (u < valid_units) ? s4[u] : make_uint4(0, 0, 0, 0);
   }
 }
-template <typename In, int ROWS, int WIDTH>
-__device__ __forceinline__ void store_tile(In* dst, const uint4 (&buf)[(ROWS * WIDTH * (int)sizeof(In) / 16 + 255) / 256],
+template <typename In, int ROWS, int WIDTH, int NT>
+__device__ __forceinline__ void store_tile(In* dst, const uint4 (&buf)[(ROWS * WIDTH * (int)sizeof(In) / 16 + NT - 1) / NT],
                                            int tid) {
   constexpr int UNITS = ROWS * WIDTH * (int)sizeof(In) / 16;
   uint4* d4 = reinterpret_cast<uint4*>(dst);
 #pragma unroll
-  for (int it = 0; it < (UNITS + 255) / 256; ++it) {
-    int u = tid + it * 256;
+  for (int it = 0; it < (UNITS + NT - 1) / NT; ++it) {
+    int u = tid + it * NT;
     if (u < UNITS) d4[u] = buf[it];
   }
 }
-template <typename In, int ROWS, int WIDTH>
+template <typename In, int ROWS, int WIDTH, int NT>
 __device__ __forceinline__ void unstage_tile(In* dst, const In* src, int nvalid, int tid) {
   constexpr int PER_UNIT = 16 / (int)sizeof(In);
   const int valid_units = nvalid * WIDTH / PER_UNIT;
   const uint4* s4 = reinterpret_cast<const uint4*>(src);
   uint4* d4 = reinterpret_cast<uint4*>(dst);
-  for (int u = tid; u < valid_units; u += 256) d4[u] = s4[u];
+  for (int u = tid; u < valid_units; u += NT) d4[u] = s4[u];
 }
 
 __device__ __forceinline__ v4f ld4(const float* p) { return *reinterpret_cast<const v4f*>(p); }
@@ -231,21 +238,22 @@ __device__ __forceinline__ void put_vals(unsigned char* block, int j, const floa
 }
 
 // Waves per SIMD the kernel is compiled for: two workgroups per compute unit
-// (at most 256 registers per lane) when two fit in LDS, else one.  (Three
+// when two fit in LDS, else one, times the workgroup's waves per SIMD (two
+// waves per SIMD allow at most 256 registers per lane).  (Three
 // fit in LDS at d = 64 but were slower: the 168-register budget spills and
 // twelve segments of a head in flight deepen the look-backs.)
 template <int DK, int DV, bool BF16>
 constexpr int fwd_waves_per_eu() {
-  return sizeof(FwdSmem<DK, DV, BF16>) <= 80 * 1024 ? 2 : 1;
+  return (sizeof(FwdSmem<DK, DV, BF16>) <= 80 * 1024 ? 2 : 1) * FwdCfg<DK, DV, BF16>::NW / 4;
 }
 
 template <int DK, int DV, bool BF16>
-__global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, DV, BF16>())) void kla_fwd_kernel(FwdParams p) {
   using C = FwdCfg<DK, DV, BF16>;
   using In = typename C::In;
   using M = Mma<BF16>;
   using Op = typename M::Op;
-  constexpr int L = C::L, NCH = C::NCH, CPT = C::CPT;
+  constexpr int L = C::L, NCH = C::NCH, CPT = C::CPT, NW = C::NW, NT = C::NT;
   constexpr int NRT = C::NRT, NCT = C::NCT, CPW = C::CPW, QROW = C::QROW, KROW = C::KROW;
   __shared__ FwdSmem<DK, DV, BF16> s;
 
@@ -274,14 +282,14 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
   // LDS first and q, v only after the aggregate walk, so their load latency
   // overlaps the walk.
   const size_t offk = ((size_t)head * T + t0) * DK, offv = ((size_t)head * T + t0) * DV;
-  constexpr int UK = (L * DK * (int)sizeof(In) / 16 + 255) / 256, UV = (L * DV * (int)sizeof(In) / 16 + 255) / 256;
+  constexpr int UK = (L * DK * (int)sizeof(In) / 16 + NT - 1) / NT, UV = (L * DV * (int)sizeof(In) / 16 + NT - 1) / NT;
   uint4 bq[UK], bv[UV];
-  load_tile<In, L, DK>(bq, static_cast<const In*>(p.q) + offk, nvalid, tid);
-  load_tile<In, L, DV>(bv, static_cast<const In*>(p.v) + offv, nvalid, tid);
-  stage_tile<In, L, DK>(rk, static_cast<const In*>(p.k) + offk, nvalid, tid);
-  stage_tile<In, L, DK>(rld, static_cast<const In*>(p.ld) + offk, nvalid, tid);
-  stage_tile<In, L, DK>(rpn, static_cast<const In*>(p.pn) + offk, nvalid, tid);
-  stage_tile<In, L, DK>(rvp, static_cast<const In*>(p.vp) + offk, nvalid, tid);
+  load_tile<In, L, DK, NT>(bq, static_cast<const In*>(p.q) + offk, nvalid, tid);
+  load_tile<In, L, DV, NT>(bv, static_cast<const In*>(p.v) + offv, nvalid, tid);
+  stage_tile<In, L, DK, NT>(rk, static_cast<const In*>(p.k) + offk, nvalid, tid);
+  stage_tile<In, L, DK, NT>(rld, static_cast<const In*>(p.ld) + offk, nvalid, tid);
+  stage_tile<In, L, DK, NT>(rpn, static_cast<const In*>(p.pn) + offk, nvalid, tid);
+  stage_tile<In, L, DK, NT>(rvp, static_cast<const In*>(p.vp) + offk, nvalid, tid);
   __syncthreads();
   const unsigned epoch = (unsigned)s.ctl[1];
   const unsigned FAGG = 2u * epoch + 2u, FINC = 2u * epoch + 3u;
@@ -294,11 +302,11 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
   if (pwave && pch && seg > 0) early = ld_record(p.pinc + (hb + seg - 1) * DK + tid);
 
   // ---------------------------------------------------------------- 1. chunk aggregates
-  // Walker (chunk wc = wave, half wh, channel group wg) owns channels
-  // wch .. wch + CPT - 1 and tokens wt0 .. wt0 + 7 and composes their 2x2 step
-  // matrices; the halves of a chunk are joined with a lane exchange.
-  const int wc = wave, wh = lane >> 5;
-  const int wch = (lane & 31) * CPT, wt0 = wc * 16 + wh * 8;
+  // Walker (chunk wc, half wh) owns channels wch .. wch + CPT - 1 and tokens
+  // wt0 .. wt0 + 7 and composes their 2x2 step matrices; the halves of a
+  // chunk are joined with a lane exchange.
+  const int wc = wave & 3, wh = lane >> 5;
+  const int wch = (wave >> 2) * 32 * CPT + (lane & 31) * CPT, wt0 = wc * 16 + wh * 8;
   const bool walker = wc < NCH && wch < DK;
   constexpr int KT = C::KEEP ? 8 : 1;
   float ca[KT][CPT], cpn[KT][CPT], cc2[KT][CPT], ckv[KT][CPT];  // a, pbar, c, k*Lambda^v
@@ -342,8 +350,8 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
     const Mob Pc = wh ? mob_mul(Pg[k], Pp) : mob_mul(Pp, Pg[k]);
     if (walker && wh == 0) *reinterpret_cast<v4f*>(s.cagg() + (wc * DK + wch + k) * 4) = v4f{Pc.m00, Pc.m01, Pc.m10, Pc.m11};
   }
-  store_tile<In, L, DK>(rq, bq, tid);
-  if constexpr (!C::CAGG_IN_V) store_tile<In, L, DV>(s.v, bv, tid);
+  store_tile<In, L, DK, NT>(rq, bq, tid);
+  if constexpr (!C::CAGG_IN_V) store_tile<In, L, DV, NT>(s.v, bv, tid);
   __syncthreads();
 
   // ---------------------------------------------------------------- 2. precision carry
@@ -417,7 +425,7 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
     wait_stores();
     if (lane == 0) st_relaxed(pfl + 2 * seg, FINC);
   }
-  if constexpr (C::CAGG_IN_V) store_tile<In, L, DV>(s.v, bv, tid);  // the aggregates are consumed
+  if constexpr (C::CAGG_IN_V) store_tile<In, L, DV, NT>(s.v, bv, tid);  // the aggregates are consumed
 
   // ---------------------------------------------------------------- 3. gate walk
   // Results stay in registers until every walker has finished reading the raw
@@ -504,8 +512,7 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
       walk(std::false_type{});
   }
   // A chunk is unsafe when some channel's prod f over it falls below 2^-64
-  // (Ks = g / cp could overflow); wave wc walks chunk wc, so the decision is
-  // uniform over the wave.
+  // (Ks = g / cp could overflow); the chunk's walker waves flag it in LDS.
   bool unsafe_w = false;
   float FpA[CPT];
 #pragma unroll
@@ -524,15 +531,14 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
     if (walker && wh == 0) s.cpe[wc * DK + wch + k] = cpe;
   }
   if (walker && unsafe_w && lane == 0) s.unsafe[wc] = 1;
-  if (walker && (unsafe_w || !C::KST)) {  // Kd is stored: rescale the first half to the chunk end
-    if (!wh) {
-#pragma unroll
-      for (int k = 0; k < CPT; ++k)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) wd[e][k] *= FpA[k];
-    }
-  }
   __syncthreads();
+  const bool unsafe_c = walker && s.unsafe[wc] != 0;  // uniform over the chunk's walker waves
+  if (walker && (unsafe_c || !C::KST) && !wh) {  // Kd is stored: rescale the first half to the chunk end
+#pragma unroll
+    for (int k = 0; k < CPT; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wd[e][k] *= FpA[k];
+  }
   unsigned char* const Qs = s.u;
   unsigned char* const Ks = s.u + L * QROW;
   unsigned char* const KdT = s.u + 2 * L * QROW;  // without KST only
@@ -544,7 +550,7 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
       put_vals<BF16, CPT>(Qs + t * QROW + cb, cj, wq[e]);
       // With KST the rows of an unsafe chunk hold Kd (its scores take the
       // exact path and never read Ks).
-      put_vals<BF16, CPT>(Ks + t * QROW + cb, cj, (C::KST && unsafe_w) ? wd[e] : wk[e]);
+      put_vals<BF16, CPT>(Ks + t * QROW + cb, cj, (C::KST && unsafe_c) ? wd[e] : wk[e]);
     }
     if constexpr (!C::KST) {
 #pragma unroll
@@ -613,7 +619,7 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
       }
     }
     __syncthreads();
-    {
+    if (tid < 256) {
       const int tt = tid >> 4, uu = tid & 15;
       float acc = 0.f;
       if (uu <= tt)
@@ -622,7 +628,7 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
     }
     __syncthreads();
   }
-  for (int cc = wave; cc < NCH; cc += 4) {
+  for (int cc = wave; cc < NCH; cc += NW) {
     if (s.unsafe[cc]) continue;
     Op qo[NRT], ko[NRT];
 #pragma unroll
@@ -664,7 +670,7 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
       }
 #pragma unroll
       for (int pp = 0; pp < CPW; ++pp) {
-        const int nt = wave + 4 * pp;
+        const int nt = wave + NW * pp;
         if (nt < NCT) {
           // V block: rows u = cc*16 + 4*lg + e, column 16*nt + lc.
           const typename M::VOp vo = M::vop(s.v + (cc * 16 + 4 * lg) * DV + 16 * nt + lc, DV);
@@ -715,12 +721,12 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
   auto frag_off = [&](int mt, int nt) -> uint32_t { return ((uint32_t)(nt * NRT + mt) * 64 + lane) * 16; };
   v4f Min[NRT][CPW];
   if (wave < NCT) {
-    unsigned* const mfl = p.mflag + hb * 4 + wave;  // flag of segment r: mfl[4 * r]
+    unsigned* const mfl = p.mflag + hb * NW + wave;  // flag of segment r: mfl[NW * r]
     auto store_inclusive = [&]() {
       const auto r = coherent_rsrc(p.minc + hs * DK * DV, MBYTES);
 #pragma unroll
       for (int pp = 0; pp < CPW; ++pp) {
-        const int nt = wave + 4 * pp;
+        const int nt = wave + NW * pp;
         if (nt < NCT) {
 #pragma unroll
           for (int mt = 0; mt < NRT; ++mt) {
@@ -733,12 +739,12 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
         }
       }
       wait_stores();
-      if (lane == 0) st_relaxed(mfl + 4 * seg, FINC);
+      if (lane == 0) st_relaxed(mfl + NW * seg, FINC);
     };
     if (seg == 0) {
 #pragma unroll
       for (int pp = 0; pp < CPW; ++pp) {
-        const int nt = wave + 4 * pp;
+        const int nt = wave + NW * pp;
 #pragma unroll
         for (int mt = 0; mt < NRT; ++mt) {
           v4f m = v4f{0.f, 0.f, 0.f, 0.f};
@@ -751,28 +757,28 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
       }
       if (!last) store_inclusive();
     } else {
-      const size_t fslot = (hs * 4 + wave) * DK;  // this wave's copy of prod f
+      const size_t fslot = (hs * NW + wave) * DK;  // this wave's copy of prod f
       if (!last) {
         for (int r = lane; r < DK; r += 64) st_coherent(p.mF + fslot + r, s.fseg[r]);
         const auto r = coherent_rsrc(p.magg + hs * DK * DV, MBYTES);
 #pragma unroll
         for (int pp = 0; pp < CPW; ++pp) {
-          const int nt = wave + 4 * pp;
+          const int nt = wave + NW * pp;
           if (nt < NCT) {
 #pragma unroll
             for (int mt = 0; mt < NRT; ++mt) st_coherent(r, frag_off(mt, nt), Macc[mt][pp]);
           }
         }
       }
-      const unsigned f0 = lookback_peek(mfl, 4, seg - 1);
+      const unsigned f0 = lookback_peek(mfl, NW, seg - 1);
       wait_stores();
-      if (!last && lane == 0) st_relaxed(mfl + 4 * seg, FAGG);
-      const int r0 = lookback_find(mfl, 4, seg, FAGG, FINC, p.ctrl, f0);
+      if (!last && lane == 0) st_relaxed(mfl + NW * seg, FAGG);
+      const int r0 = lookback_find(mfl, NW, seg, FAGG, FINC, p.ctrl, f0);
       // Fold the carries of segments r0 .. seg-1 (M <- diag(prod f) M + local
       // state), FB aggregates per round trip.
 #pragma unroll
       for (int pp = 0; pp < CPW; ++pp) {
-        const int nt = wave + 4 * pp;
+        const int nt = wave + NW * pp;
 #pragma unroll
         for (int mt = 0; mt < NRT; ++mt)
           Min[mt][pp] = nt < NCT ? ld_coherent(coherent_rsrc(p.minc + (hb + r0) * DK * DV, MBYTES), frag_off(mt, nt))
@@ -785,13 +791,13 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
           if (u0 + j < seg) {
             const size_t us = hb + u0 + j;
             const auto ra = coherent_rsrc(p.magg + us * DK * DV, MBYTES);
-            const auto rf = coherent_rsrc(p.mF + (us * 4 + wave) * DK, DK * 4);
+            const auto rf = coherent_rsrc(p.mF + (us * NW + wave) * DK, DK * 4);
 #pragma unroll
             for (int mt = 0; mt < NRT; ++mt) {
               F[j][mt] = ld_coherent(rf, (16 * mt + 4 * lg) * 4);
 #pragma unroll
               for (int pp = 0; pp < CPW; ++pp) {
-                const int nt = wave + 4 * pp;
+                const int nt = wave + NW * pp;
                 A[j][mt][pp] = nt < NCT ? ld_coherent(ra, frag_off(mt, nt)) : v4f{0.f, 0.f, 0.f, 0.f};
               }
             }
@@ -818,7 +824,7 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
   if (last) {  // final state, row-major
 #pragma unroll
     for (int pp = 0; pp < CPW; ++pp) {
-      const int nt = wave + 4 * pp;
+      const int nt = wave + NW * pp;
       if (nt < NCT) {
 #pragma unroll
         for (int mt = 0; mt < NRT; ++mt) {
@@ -850,7 +856,7 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
       for (int mt = 0; mt < NRT; ++mt) qo[mt] = M::get(Qs + (cc * 16 + lc) * QROW + (16 * mt + 4 * lg) * 4);
 #pragma unroll
       for (int pp = 0; pp < CPW; ++pp) {
-        const int nt = wave + 4 * pp;
+        const int nt = wave + NW * pp;
         if (nt < NCT) {
           Op mo[NRT];
 #pragma unroll
@@ -874,7 +880,7 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
     }
   }
   __syncthreads();
-  unstage_tile<In, L, DV>(static_cast<In*>(p.y) + ((size_t)head * T + t0) * DV, s.v, nvalid, tid);
+  unstage_tile<In, L, DV, NT>(static_cast<In*>(p.y) + ((size_t)head * T + t0) * DV, s.v, nvalid, tid);
 }
 
 // ------------------------------------------------------------------------------
@@ -883,7 +889,7 @@ __global__ __launch_bounds__(256, (fwd_waves_per_eu<DK, DV, BF16>())) void kla_f
 template <int DK, int DV, bool BF16>
 static hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   const unsigned nblocks = (unsigned)p.nheads * (unsigned)p.nseg;
-  hipLaunchKernelGGL((kla_fwd_kernel<DK, DV, BF16>), dim3(nblocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((kla_fwd_kernel<DK, DV, BF16>), dim3(nblocks), dim3(FwdCfg<DK, DV, BF16>::NT), 0, stream, p);
   return hipGetLastError();
 }
 

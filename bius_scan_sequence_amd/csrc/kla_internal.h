@@ -26,10 +26,10 @@ struct FwdParams {
   unsigned* ctrl;     // workspace control words
   unsigned* hdone;    // [nheads] segments of the head done with their flags
   unsigned* pflag;    // [nheads*nseg][2] precision-carry flags, one per carry wave
-  unsigned* mflag;    // [nheads*nseg][4] mean-carry flags, one per wave
+  unsigned* mflag;    // [nheads*nseg][waves] mean-carry flags, one per wave
   float* pagg;        // [nheads*nseg][dk][4] segment 2x2 aggregates
   unsigned long long* pinc;  // [nheads*nseg][dk] precision after the segment: {value bits, flag}
-  float* mF;          // [nheads*nseg][4][dk] prod of forget gates over the segment (per wave)
+  float* mF;          // [nheads*nseg][waves][dk] prod of forget gates over the segment (per wave)
   float* magg;        // [nheads*nseg][dk*dv] local mean state (fragment order)
   float* minc;        // [nheads*nseg][dk*dv] mean state after the segment (fragment order)
 };
