@@ -20,13 +20,13 @@
 //   3. The walk is repeated with the true entering precision to produce the
 //      per-token gates f = a lam^-/lam and g = k Lambda^v / lam, folded into the
 //      matrix-core operands of 16-token chunks:
-//        Qs = q * cp,  Ks = g / cp,  Kd = g * prod_{w>u} f_w,  cp = in-chunk
-//        cumulative product of f.
+//        Qs = q * cp,  Ks = g / cp,  Qg = Qs * (prod of f over earlier chunks),
+//        cp = in-chunk cumulative product of f (Kd = g * prod_{w>u} f_w = Ks cp_end).
 //   4. Chunk loop from a zero state: y_c = tril(Qs Ks^T) V + Qs M_c and
-//      M_{c+1} = diag(cp_end) M_c + Kd^T V, on 16x16 matrix-core tiles; the state
-//      stays in accumulator registers, never in HBM.
+//      M_{c+1} = diag(cp_end) (M_c + Ks^T V), on 16x16 matrix-core tiles; the
+//      state stays in accumulator registers, never in HBM.
 //   5. Decoupled look-back of the mean carry (prod f over the segment, local
-//      state), then y += Qs (diag(prod of earlier chunk decays) M_in) and store.
+//      state), then y += Qg M_in and store.
 // Every carry is folded forward in segment order with the same instructions,
 // so results do not depend on which predecessor a look-back stops at.
 //
@@ -67,7 +67,12 @@ struct FwdCfg {
   // transposing LDS loads; fp32 keeps a separate Kd^T copy.
   static constexpr bool KST = BF16;
   static constexpr int RAW_BYTES = 5 * L * DK * (int)sizeof(In);        // q, k, ld, pn, vp
-  static constexpr int OPS_BYTES = 2 * L * QROW + (KST ? 0 : DK * KROW);  // Qs, Ks[, Kd^T]
+  static constexpr int OPS_BYTES = 3 * L * QROW + (KST ? 0 : DK * KROW);  // Qs, Ks, Qg[, Kd^T]
+  // The local readout Qs_c M_c waits until the local state has been published
+  // (it then overlaps that publication and the first flag poll) when the local
+  // chunk states fit in registers (NRT*CPW <= 4 tiles per lane); otherwise it
+  // runs in the chunk loop.
+  static constexpr bool LATE_LOCAL = NRT * CPW <= 4;
   static constexpr int UNION_BYTES = RAW_BYTES > OPS_BYTES ? RAW_BYTES : OPS_BYTES;
   static constexpr int A_BYTES = NCH * 64 * 16;                         // per chunk: scores, A-operand order
   static constexpr int RED_BYTES = 2 * 256 * 4;                         // exact path: per-wave partial sums
@@ -81,10 +86,6 @@ struct FwdCfg {
   static constexpr bool CAGG_IN_V = CAGG_BYTES <= L * DV * (int)sizeof(In);
   static constexpr int AP_A = TAIL ? 0 : A_BYTES, AP_C = CAGG_IN_V ? 0 : CAGG_BYTES;
   static constexpr int AP_BYTES = (AP_A > AP_C ? AP_A : AP_C) > 16 ? (AP_A > AP_C ? AP_A : AP_C) : 16;
-  // The readout of the chunk states waits for the carried state when the
-  // per-chunk local states fit in registers (NRT*CPW <= 4 tiles per lane);
-  // otherwise it runs in the chunk loop and a correction adds the carry.
-  static constexpr bool DEFER = NRT * CPW <= 4;
   // The walkers keep a, pbar, c, k*Lambda^v in registers between the two
   // walks when they own at most 16 token-channels.
   static constexpr bool KEEP = 8 * CPT <= 16;
@@ -96,7 +97,7 @@ struct FwdSmem {
   using In = typename C::In;
   // Raw inputs q, k, ld, pn, vp ([L][DK] each) until the gate walk is done;
   // afterwards the stored operands Qs [L][QROW], Ks [L][QROW] (Kd in the rows
-  // of an unsafe chunk when KST) and, without KST, Kd^T [DK][KROW].
+  // of an unsafe chunk when KST), Qg [L][QROW] and, without KST, Kd^T [DK][KROW].
   alignas(16) unsigned char u[C::UNION_BYTES];
   // Chunk 2x2 aggregates until the precision carry is done (when CAGG_IN_V),
   // then raw v; staged y at the end.
@@ -541,13 +542,28 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   }
   unsigned char* const Qs = s.u;
   unsigned char* const Ks = s.u + L * QROW;
-  unsigned char* const KdT = s.u + 2 * L * QROW;  // without KST only
+  unsigned char* const Qg = s.u + 2 * L * QROW;
+  unsigned char* const KdT = s.u + 3 * L * QROW;  // without KST only
   if (walker) {
     const int cb = (wch >> 2) * 16, cj = wch & 3;  // block and slot of channel wch in a row
+    // Qg = q times the prod of f from the segment start: Qs scaled by the
+    // decays of the earlier chunks.  The carried state enters y only through it.
+    float dec[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      dec[k] = 1.f;
+#pragma unroll
+      for (int c = 0; c < NCH - 1; ++c)
+        if (c < wc) dec[k] *= s.cpe[c * DK + wch + k];
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int t = wt0 + e;
       put_vals<BF16, CPT>(Qs + t * QROW + cb, cj, wq[e]);
+      float qg[CPT];
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) qg[k] = wq[e][k] * dec[k];
+      put_vals<BF16, CPT>(Qg + t * QROW + cb, cj, qg);
       // With KST the rows of an unsafe chunk hold Kd (its scores take the
       // exact path and never read Ks).
       put_vals<BF16, CPT>(Ks + t * QROW + cb, cj, (C::KST && unsafe_c) ? wd[e] : wk[e]);
@@ -647,13 +663,13 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
 
   // ---------------------------------------------------------------- 4b. chunk loop
   // Local chunk states from a zero state: M_{c+1} = diag(cp_end_c) M_c + Kd_c^T V_c.
-  // y_c gets the intra-chunk part A_c V_c here; its readout Qs_c M_c either
-  // here (and the carried state is added by a correction later) or, deferred,
-  // once the carried state is known, from the kept states M_c.
+  // y_c gets its local part A_c V_c + Qs_c M_c, with M_c the local state
+  // entering chunk c, here or (LATE_LOCAL) from the kept states once the local
+  // state is on its way out; the carried state is added once it is known.
   v4f yl[NCH][CPW];
   v4f Macc[NRT][CPW];
-  constexpr int NKEEP = C::DEFER ? NCH : 1;
-  v4f Mkeep[NKEEP][NRT][CPW];  // deferred: local state entering chunk c (c >= 1)
+  constexpr int NKEEP = C::LATE_LOCAL ? NCH : 1;
+  v4f Mkeep[NKEEP][NRT][CPW];  // LATE_LOCAL: local state entering chunk c (c >= 1)
 #pragma unroll
   for (int pp = 0; pp < CPW; ++pp)
 #pragma unroll
@@ -664,7 +680,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
     for (int cc = 0; cc < NCH; ++cc) {
       const Op ao = M::get(A + (cc * 64 + lane) * 16);
       Op qo[NRT];
-      if constexpr (!C::DEFER) {
+      if (!C::LATE_LOCAL && cc > 0) {
 #pragma unroll
         for (int mt = 0; mt < NRT; ++mt) qo[mt] = M::get(Qs + (cc * 16 + lc) * QROW + (16 * mt + 4 * lg) * 4);
       }
@@ -675,7 +691,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
           // V block: rows u = cc*16 + 4*lg + e, column 16*nt + lc.
           const typename M::VOp vo = M::vop(s.v + (cc * 16 + 4 * lg) * DV + 16 * nt + lc, DV);
           v4f acc = M::dotv(v4f{0.f, 0.f, 0.f, 0.f}, ao, vo);
-          if constexpr (!C::DEFER) {
+          if (!C::LATE_LOCAL && cc > 0) {  // the local state entering chunk 0 is zero
             Op mo[NRT];
 #pragma unroll
             for (int mt = 0; mt < NRT; ++mt) mo[mt] = M::op(Macc[mt][pp]);
@@ -701,7 +717,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
               const Op kdo = M::get(KdT + (16 * mt + lc) * KROW + (cc * 16 + 4 * lg) * 4);
               Macc[mt][pp] = M::dotv(m, kdo, vo);
             }
-            if constexpr (C::DEFER) {
+            if constexpr (C::LATE_LOCAL) {
               if (cc + 1 < NCH) Mkeep[cc + 1 < NKEEP ? cc + 1 : 0][mt][pp] = Macc[mt][pp];
             }
           }
@@ -720,6 +736,25 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   constexpr int FB = NRT * CPW <= 8 ? 2 : 1;  // aggregates folded per round trip
   auto frag_off = [&](int mt, int nt) -> uint32_t { return ((uint32_t)(nt * NRT + mt) * 64 + lane) * 16; };
   v4f Min[NRT][CPW];
+  auto local_readout = [&]() {  // LATE_LOCAL: y_c += Qs_c M_c for c >= 1
+    if constexpr (C::LATE_LOCAL) {
+#pragma unroll
+      for (int cc = 1; cc < NCH; ++cc) {
+        Op qo[NRT];
+#pragma unroll
+        for (int mt = 0; mt < NRT; ++mt) qo[mt] = M::get(Qs + (cc * 16 + lc) * QROW + (16 * mt + 4 * lg) * 4);
+#pragma unroll
+        for (int pp = 0; pp < CPW; ++pp) {
+          if (wave + NW * pp < NCT) {
+            Op mo[NRT];
+#pragma unroll
+            for (int mt = 0; mt < NRT; ++mt) mo[mt] = M::op(Mkeep[cc < NKEEP ? cc : 0][mt][pp]);
+            yl[cc][pp] = M::dot(yl[cc][pp], qo, mo);
+          }
+        }
+      }
+    }
+  };
   if (wave < NCT) {
     unsigned* const mfl = p.mflag + hb * NW + wave;  // flag of segment r: mfl[NW * r]
     auto store_inclusive = [&]() {
@@ -755,6 +790,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
           Min[mt][pp] = m;
         }
       }
+      local_readout();
       if (!last) store_inclusive();
     } else {
       const size_t fslot = (hs * NW + wave) * DK;  // this wave's copy of prod f
@@ -771,6 +807,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
         }
       }
       const unsigned f0 = lookback_peek(mfl, NW, seg - 1);
+      local_readout();  // overlaps the stores above and the flag poll
       wait_stores();
       if (!last && lane == 0) st_relaxed(mfl + NW * seg, FAGG);
       const int r0 = lookback_find(mfl, NW, seg, FAGG, FINC, p.ctrl, f0);
@@ -837,45 +874,32 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
     }
   }
 
-  // ---------------------------------------------------------------- 6. readout / correction + store
+  // ---------------------------------------------------------------- 6. carried-state readout + store
   // With M_in the state entering the segment, the true state entering chunk c
-  // is M_c + diag(prod of earlier chunk decays) M_in:
-  //   deferred:   y_c = A_c V_c + Qs_c (M_c + diag(decay_c) M_in)
-  //   otherwise:  y_c += Qs_c (diag(decay_c) M_in)
-  // y is staged in LDS over v (dead once every wave has left the chunk loop)
-  // and written out in 16-byte units.  A wave's y columns are the V columns
-  // only it read in the chunk loop, so no barrier is needed before staging.
+  // is M_c + diag(prod of earlier chunk decays) M_in, so
+  //   y_c = (A_c V_c + Qs_c M_c) + Qg_c M_in,
+  // the bracket from the chunk loop; M_in is split into matrix-core operands
+  // once for all chunks.  y is staged in LDS over v (dead once every wave has
+  // left the chunk loop) and written out in 16-byte units.  A wave's y
+  // columns are the V columns only it read in the chunk loop, so no barrier
+  // is needed before staging.
   if (wave < NCT) {
-    v4f decay[NRT];  // prod of chunk decays before chunk cc, per owned row
 #pragma unroll
-    for (int mt = 0; mt < NRT; ++mt) decay[mt] = v4f{1.f, 1.f, 1.f, 1.f};
+    for (int pp = 0; pp < CPW; ++pp) {
+      const int nt = wave + NW * pp;
+      if (nt < NCT) {
+        Op mo[NRT];
 #pragma unroll
-    for (int cc = 0; cc < NCH; ++cc) {
-      Op qo[NRT];
+        for (int mt = 0; mt < NRT; ++mt) mo[mt] = M::op(Min[mt][pp]);
 #pragma unroll
-      for (int mt = 0; mt < NRT; ++mt) qo[mt] = M::get(Qs + (cc * 16 + lc) * QROW + (16 * mt + 4 * lg) * 4);
+        for (int cc = 0; cc < NCH; ++cc) {
+          Op go[NRT];
 #pragma unroll
-      for (int pp = 0; pp < CPW; ++pp) {
-        const int nt = wave + NW * pp;
-        if (nt < NCT) {
-          Op mo[NRT];
-#pragma unroll
-          for (int mt = 0; mt < NRT; ++mt) {
-            v4f m = cc == 0 ? Min[mt][pp] : decay[mt] * Min[mt][pp];
-            if constexpr (C::DEFER) {
-              if (cc > 0) m = m + Mkeep[cc < NKEEP ? cc : 0][mt][pp];
-            }
-            mo[mt] = M::op(m);
-          }
-          const v4f acc = M::dot(yl[cc][pp], qo, mo);
+          for (int mt = 0; mt < NRT; ++mt) go[mt] = M::get(Qg + (cc * 16 + lc) * QROW + (16 * mt + 4 * lg) * 4);
+          const v4f acc = M::dot(yl[cc][pp], go, mo);
 #pragma unroll
           for (int e = 0; e < 4; ++e) s.v[(cc * 16 + 4 * lg + e) * DV + 16 * nt + lc] = from_f32<In>(acc[e]);
         }
-      }
-      if (cc + 1 < NCH) {
-#pragma unroll
-        for (int mt = 0; mt < NRT; ++mt)
-          decay[mt] = cc == 0 ? ld4(s.cpe + 16 * mt + 4 * lg) : decay[mt] * ld4(s.cpe + cc * DK + 16 * mt + 4 * lg);
       }
     }
   }
