@@ -32,7 +32,11 @@
  *     non-zero return means nothing was enqueued.  KLA_ERR_HIP means a launch
  *     failed; kla_status_string() then returns the HIP error text.
  *   - Device data is not checked: lambda0 must be positive and every input
- *     finite, otherwise outputs are unspecified (typically NaN).
+ *     finite, otherwise outputs are unspecified (typically NaN).  The
+ *     precision is carried in float32 and must stay below FLT_MAX: with
+ *     proc_noise > 0 it is bounded by c + 1/proc_noise, but with proc_noise = 0
+ *     and a < 1 it grows by 1/a^2 per token and overflows after about
+ *     88 / ln(1/a^2) tokens, after which outputs are unspecified.
  *   - A workspace is device memory of at least the size the matching
  *     *_workspace_bytes() function returns, 256-byte aligned, zero-filled once
  *     by kla_workspace_init() before its first use and not touched by the
