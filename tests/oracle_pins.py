@@ -399,9 +399,64 @@ def pin_decode_chain_is_dense_posterior(seed=16, T=8):
             np.testing.assert_allclose(lam[0, 0, i], precs[t], rtol=1e-9)
 
 
+# --------------------------------------------------------------------------- #
+# backward pass                                                                #
+# --------------------------------------------------------------------------- #
+
+def _loss_parts(rng, B, H, T, dk, dv):
+    dy = rng.standard_normal((B, H, T, dv))
+    dlT = rng.standard_normal((B, H, dk))
+    dMT = rng.standard_normal((B, H, dk, dv))
+    return dy, dlT, dMT
+
+
+def pin_backward_finite_differences(seed=17):
+    """Gradients of <dy, y> + <dlam_T, lam_T> + <dM_T, M_T> equal central
+    finite differences of the numpy oracle, for every input element."""
+    import oracle.kla_backward_f64 as OB
+    rng = np.random.default_rng(seed)
+    B, H, T, dk, dv = 1, 2, 5, 3, 2
+    q, k, v, ld, pn, vp, lam0, M0 = _rand_inputs(rng, B, H, T, dk, dv)
+    dy, dlT, dMT = _loss_parts(rng, B, H, T, dk, dv)
+    g = OB.kla_backward_f64(q, k, v, ld, pn, vp, dy, lam0, M0, dlT, dMT)
+
+    def loss(q, k, v, ld, pn, vp, lam0, M0):
+        y, lT, MT = O.kla_forward_f64(q, k, v, ld, pn, vp, lam0, M0)
+        return float(np.sum(y * dy) + np.sum(lT * dlT) + np.sum(MT * dMT))
+
+    args = [q, k, v, ld, pn, vp, lam0, M0]
+    names = ["dq", "dk", "dv", "d_log_decay", "d_proc_noise", "d_val_prec", "d_lambda0", "d_M0"]
+    for ai, name in enumerate(names):
+        x = args[ai]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            h = 1e-6 * (1.0 + abs(x[idx]))
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            a_p = list(args); a_p[ai] = xp
+            a_m = list(args); a_m[ai] = xm
+            fd[idx] = (loss(*a_p) - loss(*a_m)) / (2 * h)
+        np.testing.assert_allclose(g[name], fd, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def pin_backward_forward_is_the_oracle(seed=18):
+    """The differentiable float64 filter of the backward oracle computes the
+    numpy oracle's forward pass."""
+    import torch
+    import oracle.kla_backward_f64 as OB
+    rng = np.random.default_rng(seed)
+    args = _rand_inputs(rng, 2, 2, 30, 4, 3)
+    y, lT, MT = O.kla_forward_f64(*args)
+    yt, lTt, MTt = OB.kla_forward_torch64(*(torch.tensor(x, dtype=torch.float64) for x in args))
+    np.testing.assert_allclose(yt.numpy(), y, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(lTt.numpy(), lT, rtol=1e-13)
+    np.testing.assert_allclose(MTt.numpy(), MT, rtol=1e-13, atol=1e-15)
+
+
 ALL_PINS = [
     pin_covariance_form, pin_dense_gaussian, pin_mobius_exact, pin_mobius_mpmath,
     pin_steady_state_dare, pin_no_observation, pin_no_process_noise, pin_least_squares,
     pin_zero_value_precision, pin_invariants, pin_state_carry,
     pin_precision_scan_matches_forward, pin_decode_covariance_form, pin_decode_chain_is_dense_posterior,
+    pin_backward_finite_differences, pin_backward_forward_is_the_oracle,
 ]
