@@ -7,8 +7,10 @@ raises if it has not been built (``python bius_scan_sequence_amd/build.py``);
 there is no fallback implementation.
 
 Low-level functions carry the C names (``kla_forward``, ``kla_precision_scan``,
-``kla_decode_step``, ``kla_workspace_init``, ...) and take raw pointers;
-``forward``, ``precision_scan`` and ``decode_step`` are the tensor-level helpers.
+``kla_decode_step``, ``kla_backward``, ``kla_workspace_init``, ...) and take raw
+pointers; ``forward``, ``precision_scan``, ``decode_step`` and ``backward`` are
+the tensor-level helpers, and ``scan`` is the forward pass as a differentiable
+torch operation (its backward calls ``backward``).
 """
 from __future__ import annotations
 
@@ -19,8 +21,9 @@ import threading
 __all__ = [
     "LIB_PATH", "lib", "KLA_F32", "KLA_BF16", "KlaError",
     "kla_forward_workspace_bytes", "kla_forward", "kla_precision_scan_workspace_bytes",
-    "kla_precision_scan", "kla_decode_step", "kla_workspace_init", "kla_workspace_error",
-    "kla_status_string", "forward", "precision_scan", "decode_step", "Workspace",
+    "kla_precision_scan", "kla_decode_step", "kla_backward_workspace_bytes", "kla_backward",
+    "kla_workspace_init", "kla_workspace_error", "kla_status_string", "forward", "precision_scan",
+    "decode_step", "backward", "scan", "Workspace",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkla.so")
@@ -41,6 +44,10 @@ lib.kla_precision_scan.restype = _i
 lib.kla_precision_scan.argtypes = [_fp] * 6 + [_i] * 4 + [_vp, _sz, _vp]
 lib.kla_decode_step.restype = _i
 lib.kla_decode_step.argtypes = [_vp] * 6 + [_fp] * 4 + [_vp] + [_i] * 5 + [_vp]
+lib.kla_backward_workspace_bytes.restype = _sz
+lib.kla_backward_workspace_bytes.argtypes = [_i] * 5
+lib.kla_backward.restype = _i
+lib.kla_backward.argtypes = [_vp] * 6 + [_fp] * 3 + [_vp] + [_fp] * 2 + [_vp] * 6 + [_fp] * 2 + [_i] * 6 + [_vp, _sz, _vp]
 lib.kla_workspace_init.restype = _i
 lib.kla_workspace_init.argtypes = [_vp, _sz, _vp]
 lib.kla_workspace_error.restype = _i
@@ -83,6 +90,19 @@ def kla_decode_step(q, k, v, log_decay, proc_noise, val_prec, lambda_in, M_in, l
                                    M_out, y, B, H, dk, dv, dtype, stream))
 
 
+def kla_backward_workspace_bytes(B, H, T, dk, dv) -> int:
+    return int(lib.kla_backward_workspace_bytes(B, H, T, dk, dv))
+
+
+def kla_backward(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0, lambda_path, grad_y, grad_lambda_T,
+                 grad_M_T, grad_q, grad_k, grad_v, grad_log_decay, grad_proc_noise, grad_val_prec, grad_lambda0,
+                 grad_M0, B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream) -> int:
+    return int(lib.kla_backward(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0, lambda_path, grad_y,
+                                grad_lambda_T, grad_M_T, grad_q, grad_k, grad_v, grad_log_decay, grad_proc_noise,
+                                grad_val_prec, grad_lambda0, grad_M0, B, H, T, dk, dv, dtype, workspace,
+                                workspace_bytes, stream))
+
+
 def kla_workspace_init(workspace, workspace_bytes, stream) -> int:
     return int(lib.kla_workspace_init(workspace, workspace_bytes, stream))
 
@@ -108,8 +128,11 @@ def _torch():
 class Workspace:
     """A zero-initialised device workspace that grows on demand.
 
-    One workspace serves calls ordered on one stream.  Growing it allocates a
-    new buffer and initialises it with kla_workspace_init on the given stream.
+    One workspace serves calls of ONE entry point (forward, precision_scan or
+    backward) ordered on one stream: the entry points lay out their flags and
+    counters differently, so they must not share a buffer.  Growing it
+    allocates a new buffer and initialises it with kla_workspace_init on the
+    given stream.
     """
 
     def __init__(self, device=None):
@@ -135,8 +158,8 @@ _ws_lock = threading.Lock()
 _ws_cache: dict = {}
 
 
-def _default_workspace(device, stream_handle) -> Workspace:
-    key = (str(device), int(stream_handle))
+def _default_workspace(device, stream_handle, kind: str) -> Workspace:
+    key = (str(device), int(stream_handle), kind)
     with _ws_lock:
         ws = _ws_cache.get(key)
         if ws is None:
@@ -199,7 +222,7 @@ def forward(q, k, v, log_decay, proc_noise, val_prec, lambda0=None, M0=None,
     need = kla_forward_workspace_bytes(B, H, T, dk, dv)
     if need == 0:
         raise KlaError(2)
-    ws = (workspace or _default_workspace(dev, stream)).get(need, stream)
+    ws = (workspace or _default_workspace(dev, stream, "forward")).get(need, stream)
     rc = kla_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(proc_noise), _ptr(val_prec),
                      _ptr(lambda0), _ptr(M0), _ptr(y), _ptr(lam_T), _ptr(M_T), _ptr(lpath),
                      B, H, T, dk, dv, code, ws.data_ptr(), ws.numel(), stream)
@@ -231,7 +254,7 @@ def precision_scan(log_decay, proc_noise, obs_prec, lambda0=None, workspace: Wor
     need = kla_precision_scan_workspace_bytes(B, H, T, D)
     if need == 0:
         raise KlaError(1)
-    ws = (workspace or _default_workspace(dev, stream)).get(need, stream)
+    ws = (workspace or _default_workspace(dev, stream, "precision_scan")).get(need, stream)
     rc = kla_precision_scan(_ptr(log_decay), _ptr(proc_noise), _ptr(obs_prec), _ptr(lambda0), _ptr(lpath),
                             _ptr(lam_T), B, H, T, D, ws.data_ptr(), ws.numel(), stream)
     if rc:
@@ -279,3 +302,91 @@ def decode_step(q, k, v, log_decay, proc_noise, val_prec, lam=None, M=None, inpl
     if rc:
         raise KlaError(rc)
     return y, lam_new, M_new
+
+
+def _dtype_code(dtype):
+    torch = _torch()
+    if dtype == torch.bfloat16:
+        return KLA_BF16
+    if dtype == torch.float32:
+        return KLA_F32
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+def backward(q, k, v, log_decay, proc_noise, val_prec, grad_y, lambda_path, lambda0=None, M0=None,
+             grad_lambda_T=None, grad_M_T=None, workspace: Workspace | None = None):
+    """Gradients of the KLA forward pass on the current stream.
+
+    Inputs as ``forward`` plus grad_y [B,H,T,dv] (input dtype), the float32
+    precision path the forward call returned (``return_lambda_path=True``), and
+    the optional float32 gradients of the state out, grad_lambda_T [B,H,dk]
+    and grad_M_T [B,H,dk,dv].  Returns (grad_q, grad_k, grad_v,
+    grad_log_decay, grad_proc_noise, grad_val_prec) in the input dtype and
+    (grad_lambda0, grad_M0) in float32.
+    """
+    torch = _torch()
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    dtype, dev = k.dtype, k.device
+    code = _dtype_code(dtype)
+    for name, t, shp in (("q", q, (B, H, T, dk)), ("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)),
+                         ("log_decay", log_decay, (B, H, T, dk)), ("proc_noise", proc_noise, (B, H, T, dk)),
+                         ("val_prec", val_prec, (B, H, T, dk)), ("grad_y", grad_y, (B, H, T, dv))):
+        _check(t, name, shp, dtype, dev)
+    _check(lambda_path, "lambda_path", (B, H, T, dk), torch.float32, dev)
+    for name, t, shp in (("lambda0", lambda0, (B, H, dk)), ("M0", M0, (B, H, dk, dv)),
+                         ("grad_lambda_T", grad_lambda_T, (B, H, dk)), ("grad_M_T", grad_M_T, (B, H, dk, dv))):
+        if t is not None:
+            _check(t, name, shp, torch.float32, dev)
+    grads = [torch.empty_like(x) for x in (q, k, v, log_decay, proc_noise, val_prec)]
+    g_lam0 = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+    g_M0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    need = kla_backward_workspace_bytes(B, H, T, dk, dv)
+    if need == 0:
+        raise KlaError(2)
+    ws = (workspace or _default_workspace(dev, stream, "backward")).get(need, stream)
+    rc = kla_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(proc_noise), _ptr(val_prec),
+                      _ptr(lambda0), _ptr(M0), _ptr(lambda_path), _ptr(grad_y), _ptr(grad_lambda_T),
+                      _ptr(grad_M_T), *(_ptr(g) for g in grads), _ptr(g_lam0), _ptr(g_M0),
+                      B, H, T, dk, dv, code, ws.data_ptr(), ws.numel(), stream)
+    if rc:
+        raise KlaError(rc)
+    return (*grads, g_lam0, g_M0)
+
+
+_scan_fn = None
+
+
+def _scan_function():
+    global _scan_fn
+    if _scan_fn is None:
+        torch = _torch()
+
+        class _Scan(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, log_decay, proc_noise, val_prec, lambda0, M0):
+                y, lam_T, M_T, lpath = forward(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0,
+                                               return_lambda_path=True)
+                ctx.save_for_backward(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0, lpath)
+                ctx.has_state = (lambda0 is not None, M0 is not None)
+                return y, lam_T, M_T
+
+            @staticmethod
+            def backward(ctx, gy, glam, gM):
+                q, k, v, ld, pn, vp, lambda0, M0, lpath = ctx.saved_tensors
+                gy = torch.zeros_like(v) if gy is None else gy.contiguous()
+                glam = None if glam is None else glam.contiguous()
+                gM = None if gM is None else gM.contiguous()
+                g = backward(q, k, v, ld, pn, vp, gy, lpath, lambda0, M0, glam, gM)
+                return (*g[:6], g[6] if ctx.has_state[0] else None, g[7] if ctx.has_state[1] else None)
+
+        _scan_fn = _Scan
+    return _scan_fn
+
+
+def scan(q, k, v, log_decay, proc_noise, val_prec, lambda0=None, M0=None):
+    """The forward pass as a differentiable torch operation: returns
+    (y, lambda_T, M_T) and back-propagates into every input through the
+    library's backward pass."""
+    return _scan_function().apply(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0)

@@ -99,10 +99,102 @@ PscanPlan pscan_plan(int B, int H, int T, int D) {
   return pl;
 }
 
+constexpr int kBwdSeg = 64;  // tokens per segment of the backward pass
+
+struct BwdLayout {
+  size_t F, Mseg, Gseg, rs, dgw, ew, comp, cin, total;
+};
+
+bool bwd_shape_ok(int B, int H, int T, int dk, int dv) {
+  if (B < 1 || H < 1 || T < 0) return false;
+  if (!(dk == 16 || dk == 32 || dk == 64) || !(dv == 16 || dv == 32 || dv == 64)) return false;
+  const long long wide = dk > dv ? dk : dv;
+  return (long long)B * H * (long long)T * wide < (1LL << 31) && (long long)B * H < (1LL << 24);
+}
+
+BwdLayout bwd_layout(int B, int H, int T, int dk, int dv) {
+  const size_t nh = (size_t)B * H;
+  const size_t nseg = T > 0 ? (size_t)(T + kBwdSeg - 1) / kBwdSeg : 1;
+  const size_t chains = nh * dk;
+  BwdLayout l;
+  size_t o = kHeader;
+  l.F = o; o += round256(nh * nseg * dk * 4);
+  l.Mseg = o; o += round256(nh * nseg * dk * dv * 4);
+  l.Gseg = o; o += round256(nh * nseg * dk * dv * 4);
+  l.rs = o; o += round256(chains * 4);
+  l.dgw = o; o += round256(nh * (size_t)T * dk * 4);
+  l.ew = o; o += round256(nh * (size_t)T * dk * 4);
+  l.comp = o; o += round256(nseg * chains * 16);
+  l.cin = o; o += round256(nseg * chains * 8);
+  l.total = o;
+  return l;
+}
+
 }  // namespace
 }  // namespace kla
 
 using namespace kla;
+
+extern "C" size_t kla_backward_workspace_bytes(int B, int H, int T, int dk, int dv) {
+  if (!bwd_shape_ok(B, H, T, dk, dv)) return 0;
+  return bwd_layout(B, H, T, dk, dv).total;
+}
+
+extern "C" int kla_backward(const void* q, const void* k, const void* v, const void* log_decay,
+                            const void* proc_noise, const void* val_prec, const float* lambda0, const float* M0,
+                            const float* lambda_path, const void* grad_y, const float* grad_lambda_T,
+                            const float* grad_M_T, void* grad_q, void* grad_k, void* grad_v,
+                            void* grad_log_decay, void* grad_proc_noise, void* grad_val_prec,
+                            float* grad_lambda0, float* grad_M0, int B, int H, int T, int dk, int dv, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 1 || H < 1 || T < 0) return KLA_ERR_INVALID_ARG;
+  if (!grad_lambda0 || !grad_M0) return KLA_ERR_INVALID_ARG;
+  const void* tok[14] = {q, k, v, log_decay, proc_noise, val_prec, lambda_path, grad_y,
+                         grad_q, grad_k, grad_v, grad_log_decay, grad_proc_noise, grad_val_prec};
+  if (T > 0)
+    for (const void* x : tok)
+      if (!x) return KLA_ERR_INVALID_ARG;
+  if (dtype != KLA_F32 && dtype != KLA_BF16) return KLA_ERR_UNSUPPORTED;
+  if (!supported_width(dk) || !supported_width(dv)) return KLA_ERR_UNSUPPORTED;
+  if (dk > 64 || dv > 64) return KLA_ERR_UNSUPPORTED;
+  if (!bwd_shape_ok(B, H, T, dk, dv)) return KLA_ERR_INVALID_ARG;
+  const size_t esz = dtype == KLA_BF16 ? 2 : 4;
+  for (int x = 0; x < 14; ++x)
+    if (tok[x] && !aligned(tok[x], x == 6 ? 4 : esz)) return KLA_ERR_INVALID_ARG;
+  if ((lambda0 && !aligned(lambda0, 4)) || (grad_lambda_T && !aligned(grad_lambda_T, 4)) ||
+      !aligned(grad_lambda0, 4) || (M0 && !aligned(M0, 16)) || (grad_M_T && !aligned(grad_M_T, 16)) ||
+      !aligned(grad_M0, 16))
+    return KLA_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256)) return KLA_ERR_WORKSPACE;
+  if (workspace_bytes < kla_backward_workspace_bytes(B, H, T, dk, dv)) return KLA_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const long long nheads = (long long)B * H;
+  if (T == 0) {
+    hipError_t e = launch_backward_empty(grad_lambda_T, grad_M_T, grad_lambda0, grad_M0, nheads * dk,
+                                         nheads * dk * dv, st);
+    return e == hipSuccess ? KLA_OK : hip_fail(e, "kla_backward (T = 0)");
+  }
+  const BwdLayout l = bwd_layout(B, H, T, dk, dv);
+  char* ws = static_cast<char*>(workspace);
+  BwdParams p;
+  p.q = q; p.k = k; p.v = v; p.ld = log_decay; p.pn = proc_noise; p.vp = val_prec; p.dy = grad_y;
+  p.lam0 = lambda0; p.M0 = M0; p.lpath = lambda_path; p.dlamT = grad_lambda_T; p.dMT = grad_M_T;
+  p.dq = grad_q; p.dk = grad_k; p.dv = grad_v; p.dld = grad_log_decay; p.dpn = grad_proc_noise;
+  p.dvp = grad_val_prec; p.dlam0 = grad_lambda0; p.dM0 = grad_M0;
+  p.nheads = (int)nheads; p.T = T; p.nseg = (T + kBwdSeg - 1) / kBwdSeg;
+  p.nchains = nheads * dk;
+  p.F = reinterpret_cast<float*>(ws + l.F);
+  p.Mseg = reinterpret_cast<float*>(ws + l.Mseg);
+  p.Gseg = reinterpret_cast<float*>(ws + l.Gseg);
+  p.rs = reinterpret_cast<float*>(ws + l.rs);
+  p.dgw = reinterpret_cast<float*>(ws + l.dgw);
+  p.ew = reinterpret_cast<float*>(ws + l.ew);
+  p.comp = reinterpret_cast<float*>(ws + l.comp);
+  p.cin = reinterpret_cast<float*>(ws + l.cin);
+  hipError_t e = launch_backward(p, dk, dv, dtype == KLA_BF16, st);
+  return e == hipSuccess ? KLA_OK : hip_fail(e, "kla_backward");
+}
 
 extern "C" size_t kla_forward_workspace_bytes(int B, int H, int T, int dk, int dv) {
   if (!fwd_shape_ok(B, H, T, dk, dv)) return 0;

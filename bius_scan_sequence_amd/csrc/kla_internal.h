@@ -64,10 +64,46 @@ struct DecodeParams {
   void* y;
 };
 
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* ld;     // log_decay
+  const void* pn;     // proc_noise
+  const void* vp;     // val_prec
+  const void* dy;     // gradient of y
+  const float* lam0;  // nullable (prior precision 1)
+  const float* M0;    // nullable (prior mean 0)
+  const float* lpath; // precision after every token [nheads][T][dk]
+  const float* dlamT; // nullable
+  const float* dMT;   // nullable
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dld;
+  void* dpn;
+  void* dvp;
+  float* dlam0;
+  float* dM0;
+  int nheads, T, nseg;
+  long long nchains;  // nheads * dk
+  float* F;           // [nheads][nseg][dk] product of forget gates over the segment
+  float* Mseg;        // [nheads][nseg][dk][dv] segment aggregate, then the mean entering the segment
+  float* Gseg;        // [nheads][nseg][dk][dv] segment aggregate, then the adjoint at the segment end
+  float* rs;          // [nheads][dk] sum_j M_T[i][j] dM_T[i][j]
+  float* dgw;         // [nheads][T][dk] gradient of the write gate
+  float* ew;          // [nheads][T][dk] q dq - g dg (per-token share of the log-forget-gate gradient)
+  float* comp;        // [nseg][nchains][4] reverse-chain block composites
+  float* cin;         // [nseg][nchains][2] reverse-chain state entering each block from the right
+};
+
 int fwd_segment_len(int dk, int dv, bool bf16);
 hipError_t launch_forward(const FwdParams& p, int dk, int dv, bool bf16, hipStream_t stream);
 hipError_t launch_pscan(const PscanParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, long long nheads, int dk, int dv, bool bf16, hipStream_t stream);
+hipError_t launch_backward(const BwdParams& p, int dk, int dv, bool bf16, hipStream_t stream);
+hipError_t launch_backward_empty(const float* dlamT, const float* dMT, float* dlam0, float* dM0,
+                                 long long nl, long long nm, hipStream_t stream);
 hipError_t launch_fill_zero(void* ptr, size_t words, hipStream_t stream);
 hipError_t launch_state_copy(const float* lam0, const float* M0, float* lamT, float* MT,
                              long long nl, long long nm, hipStream_t stream);

@@ -41,7 +41,10 @@
  *     *_workspace_bytes() function returns, 256-byte aligned, zero-filled once
  *     by kla_workspace_init() before its first use and not touched by the
  *     caller afterwards.  Calls that share one workspace must be ordered on one
- *     stream; concurrent calls on one workspace race.
+ *     stream; concurrent calls on one workspace race.  A workspace serves one
+ *     entry point only: the entry points keep different flags and counters
+ *     in it, so a buffer used by kla_forward must not be passed to
+ *     kla_precision_scan or kla_backward, and so on.
  */
 #ifndef KLA_H_
 #define KLA_H_
@@ -147,6 +150,53 @@ int kla_decode_step(const void* q, const void* k, const void* v,
                     const float* lambda_in, const float* M_in,
                     float* lambda_out, float* M_out, void* y,
                     int B, int H, int dk, int dv, int dtype, void* stream);
+
+/* Bytes of workspace kla_backward needs for this shape; 0 if the shape is
+ * invalid or unsupported. */
+size_t kla_backward_workspace_bytes(int B, int H, int T, int dk, int dv);
+
+/*
+ * KLA backward pass: the gradients of a scalar loss L with respect to every
+ * input of kla_forward, given dL/dy, dL/dlambda_T and dL/dM_T.  Training KLA
+ * as a sequence mixer needs them ([KLA-nl] "Belangrijkste Bijdragen"); the
+ * step that is differentiated is the filter step of [KLA-nl] §2 (precision
+ * equation, affine mean recursion) with the precision-ratio gates of §3.
+ *
+ * Inputs: the forward call's q, k, v, log_decay, proc_noise, val_prec (dtype,
+ * shapes as kla_forward), lambda0 [B,H,dk] and M0 [B,H,dk,dv] (float32,
+ * nullable: 1 and 0 as in kla_forward), and
+ *   lambda_path   [B,H,T,dk] float32, the precision path kla_forward wrote
+ *                 (its lambda_path output) for these inputs and lambda0;
+ *   grad_y        [B,H,T,dv] dtype, dL/dy;
+ *   grad_lambda_T [B,H,dk]    float32, dL/dlambda_T (nullable: 0);
+ *   grad_M_T      [B,H,dk,dv] float32, dL/dM_T      (nullable: 0).
+ * Outputs (overwritten):
+ *   grad_q, grad_k, grad_log_decay, grad_proc_noise, grad_val_prec
+ *                 [B,H,T,dk] dtype;
+ *   grad_v        [B,H,T,dv] dtype;
+ *   grad_lambda0  [B,H,dk]    float32;
+ *   grad_M0       [B,H,dk,dv] float32.
+ * The mean M is recomputed from (lambda_path, inputs, M0); nothing else is
+ * saved from the forward call.  T = 0 gives grad_lambda0 = grad_lambda_T and
+ * grad_M0 = grad_M_T (zero where those are NULL); the per-token arrays are
+ * then not accessed and may be NULL.
+ *
+ * Supported: dk, dv in {16, 32, 64} (128: KLA_ERR_UNSUPPORTED); B, H >= 1;
+ * T >= 0; B*H*T*max(dk,dv) < 2^31.  Alignment: lambda_path and the float32
+ * vectors 4 bytes, M0, grad_M_T and grad_M0 16 bytes, dtype arrays their
+ * element size.  The workspace holds no flags, so it needs no initialisation.
+ * Arithmetic: float32 throughout; dtype outputs are rounded once at the end
+ * (bf16: nearest even).  Results are deterministic (fixed summation order).
+ */
+int kla_backward(const void* q, const void* k, const void* v,
+                 const void* log_decay, const void* proc_noise, const void* val_prec,
+                 const float* lambda0, const float* M0, const float* lambda_path,
+                 const void* grad_y, const float* grad_lambda_T, const float* grad_M_T,
+                 void* grad_q, void* grad_k, void* grad_v,
+                 void* grad_log_decay, void* grad_proc_noise, void* grad_val_prec,
+                 float* grad_lambda0, float* grad_M0,
+                 int B, int H, int T, int dk, int dv, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Zero-fills a workspace on `stream` (a fill kernel, no memset node), once
  * before its first use.  bytes must be a multiple of 4. */

@@ -44,7 +44,7 @@ __all__ = [
 class Workload:
     index: int
     name: str
-    kind: str            # "forward", "precision" or "decode" (one token per head)
+    kind: str            # "forward", "precision", "decode" (one token per head) or "backward"
     B: int
     H: int
     T: int
@@ -73,6 +73,7 @@ WORKLOADS = (
     Workload(4, "chains_f32", "precision", 1, 1024, 65536, 64, 64, "f32"),
     Workload(5, "decode_lm45m_bf16", "decode", 8, 8, 1, 64, 64, "bf16"),
     Workload(6, "decode_b256_bf16", "decode", 256, 8, 1, 64, 64, "bf16"),
+    Workload(7, "bwd_lm45m_bf16", "backward", 8, 8, 2048, 64, 64, "bf16"),
 )
 
 
@@ -247,3 +248,35 @@ def make_forward_inputs_torch(w: Workload | int | str, *, seed=None, device="cud
     out["dtype"] = dtype
     out["seed"] = seed
     return out
+
+
+def make_backward_grads(*, B: int, H: int, T: int, dk: int, dv: int, seed: int, dtype: str,
+                        state: bool = False) -> dict:
+    """Seeded upstream gradients for the backward pass (host side).
+
+    grad_y ~ N(0, 1) [B,H,T,dv] (bf16-rounded when the dtype is bf16); with
+    ``state``, also grad_lambda_T ~ N(0, 1) [B,H,dk] and grad_M_T ~ N(0, 1)
+    [B,H,dk,dv] in float32, else None for both.  One PCG64 stream per tensor,
+    spawned from SeedSequence([seed, 1]) (disjoint from the forward inputs'
+    streams of the same seed).
+    """
+    ry, rl, rm = (np.random.default_rng(s) for s in np.random.SeedSequence([seed, 1]).spawn(3))
+    gy = ry.standard_normal((B, H, T, dv)).astype(np.float32)
+    out = {"grad_y": round_bf16(gy) if dtype == "bf16" else gy, "grad_lambda_T": None, "grad_M_T": None}
+    if state:
+        out["grad_lambda_T"] = rl.standard_normal((B, H, dk)).astype(np.float32)
+        out["grad_M_T"] = rm.standard_normal((B, H, dk, dv)).astype(np.float32)
+    return out
+
+
+def make_backward_grads_torch(w: Workload | int | str, *, seed=None, device="cuda"):
+    """Device-side grad_y ~ N(0, 1) [B,H,T,dv] of a workload's full shape, in
+    its dtype (torch's generator; values differ from the host version)."""
+    import torch
+    if not isinstance(w, Workload):
+        w = workload(w)
+    seed = w.seed if seed is None else seed
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 16 + 7)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    return torch.randn((w.B, w.H, w.T, w.dv), generator=g, device=device, dtype=torch.float32).to(tdt)

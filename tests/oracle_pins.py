@@ -453,10 +453,27 @@ def pin_backward_forward_is_the_oracle(seed=18):
     np.testing.assert_allclose(MTt.numpy(), MT, rtol=1e-13, atol=1e-15)
 
 
+def pin_backward_prior_precision_identity(seed=19):
+    """lambda0 enters the filter only through the first predict step,
+    lam^- = lambda0 / (a^2 + pbar lambda0), whose partial derivatives are
+    a^2/D^2 in lambda0 and -lambda0^2/D^2 in pbar (D = a^2 + pbar lambda0).
+    Hence dL/dlambda0 = -(a_1^2 / lambda0^2) dL/dpbar_1, whatever the rest of
+    the filter does; the oracle's two gradients must obey it."""
+    import oracle.kla_backward_f64 as OB
+    rng = np.random.default_rng(seed)
+    B, H, T, dk, dv = 2, 2, 12, 4, 3
+    q, k, v, ld, pn, vp, lam0, M0 = _rand_inputs(rng, B, H, T, dk, dv)
+    dy, dlT, dMT = _loss_parts(rng, B, H, T, dk, dv)
+    g = OB.kla_backward_f64(q, k, v, ld, pn, vp, dy, lam0, M0, dlT, dMT)
+    want = -np.exp(2 * ld[:, :, 0]) / lam0 ** 2 * g["d_proc_noise"][:, :, 0]
+    np.testing.assert_allclose(g["d_lambda0"], want, rtol=1e-12, atol=1e-15)
+
+
 ALL_PINS = [
     pin_covariance_form, pin_dense_gaussian, pin_mobius_exact, pin_mobius_mpmath,
     pin_steady_state_dare, pin_no_observation, pin_no_process_noise, pin_least_squares,
     pin_zero_value_precision, pin_invariants, pin_state_carry,
     pin_precision_scan_matches_forward, pin_decode_covariance_form, pin_decode_chain_is_dense_posterior,
     pin_backward_finite_differences, pin_backward_forward_is_the_oracle,
+    pin_backward_prior_precision_identity,
 ]

@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kla_forward", "kla_forward_workspace_bytes", "kla_precision_scan",
-              "kla_precision_scan_workspace_bytes", "kla_decode_step", "kla_workspace_init",
+              "kla_precision_scan_workspace_bytes", "kla_decode_step", "kla_backward",
+              "kla_backward_workspace_bytes", "kla_workspace_init",
               "kla_workspace_error", "kla_status_string"):
         assert n in names
 
@@ -54,6 +55,10 @@ def test_workspace_sizes(K):
     assert K.kla_precision_scan_workspace_bytes(1, 1024, 65536, 64) >= 256
     assert K.kla_precision_scan_workspace_bytes(1, 1, 65536, 64) > 256  # few chains: T split
     assert K.kla_precision_scan_workspace_bytes(1, 1, 10, 0) == 0
+    assert K.kla_backward_workspace_bytes(8, 8, 2048, 64, 64) > 256
+    assert K.kla_backward_workspace_bytes(1, 1, 0, 16, 16) >= 256
+    assert K.kla_backward_workspace_bytes(1, 1, 256, 128, 64) == 0   # d = 128 not supported
+    assert K.kla_backward_workspace_bytes(1, 1, 256, 48, 16) == 0
 
 
 A = 0x10000  # an aligned fake device address; validation never dereferences it
@@ -124,3 +129,29 @@ def test_workspace_init_rejects(K):
     assert K.kla_workspace_init(None, 1024, None) == WORKSPACE
     assert K.kla_workspace_init(A + 4, 1024, None) == WORKSPACE
     assert K.kla_workspace_init(A, 1022, None) == INVALID
+
+
+def bwd(K, **over):
+    args = dict(q=A, k=A, v=A, log_decay=A, proc_noise=A, val_prec=A, lambda0=None, M0=None,
+                lambda_path=A, grad_y=A, grad_lambda_T=None, grad_M_T=None, grad_q=A, grad_k=A, grad_v=A,
+                grad_log_decay=A, grad_proc_noise=A, grad_val_prec=A, grad_lambda0=A, grad_M0=A,
+                B=1, H=2, T=100, dk=64, dv=32, dtype=1, workspace=A, workspace_bytes=1 << 30, stream=None)
+    args.update(over)
+    return K.kla_backward(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), INVALID), (dict(lambda_path=None), INVALID), (dict(grad_y=None), INVALID),
+    (dict(grad_v=None), INVALID), (dict(grad_val_prec=None), INVALID), (dict(grad_lambda0=None), INVALID),
+    (dict(grad_M0=None), INVALID), (dict(B=0), INVALID), (dict(T=-1), INVALID),
+    (dict(dk=128), UNSUPPORTED), (dict(dv=128), UNSUPPORTED), (dict(dk=48), UNSUPPORTED),
+    (dict(dtype=2), UNSUPPORTED),
+    (dict(q=A + 1), INVALID), (dict(lambda_path=A + 2), INVALID), (dict(grad_M0=A + 4), INVALID),
+    (dict(M0=A + 8), INVALID), (dict(grad_M_T=A + 4), INVALID), (dict(grad_lambda_T=A + 2), INVALID),
+    (dict(grad_k=A + 2, dtype=0), INVALID),
+    (dict(workspace=None), WORKSPACE), (dict(workspace=A + 16), WORKSPACE),
+    (dict(workspace_bytes=1024), WORKSPACE),
+    (dict(B=1 << 12, H=1 << 12, T=1 << 10), INVALID),
+])
+def test_backward_rejects(K, over, code):
+    assert bwd(K, **over) == code

@@ -165,7 +165,7 @@ def test_deterministic_bitwise():
         torch.cuda.synchronize()
         for a, b in zip(first, again):
             assert torch.equal(a, b)
-    ws = K._default_workspace(xd["q"].device, torch.cuda.current_stream().cuda_stream)
+    ws = K._default_workspace(xd["q"].device, torch.cuda.current_stream().cuda_stream, "forward")
     assert ws.error() == 0
     say("[ok] determinism")
 
