@@ -34,6 +34,7 @@ PEAK_HBM_GBS = 8000.0
 KERNEL = "kla_fwd_kernel<64, 64, true>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kla_fwd_lm45m_bf16_traffic.json")
 SOURCES = ["kla_forward.hip", "kla_device.h", "kla_internal.h"]
+NAMES = ("q", "k", "v", "log_decay", "proc_noise", "val_prec")
 
 
 def algorithmic_bytes(B, H, T, dk, dv, esz):
@@ -136,7 +137,18 @@ def cpu_baseline(x):
                       f"{wall:.2f} s wall, {cpu:.2f} s CPU"}, y
 
 
-CONFIGS = ("lm45m_bf16", "lm180m_bf16", "long_bf16", "chains_f32", "decode_lm45m_bf16", "decode_b256_bf16")
+CONFIGS = ("lm45m_bf16", "lm180m_bf16", "long_bf16", "chains_f32", "decode_lm45m_bf16", "decode_b256_bf16",
+           "bwd_lm45m_bf16")
+
+
+def backward_algorithmic_bytes(B, H, T, dk, dv, esz):
+    """Bytes the backward pass must move: per token the six inputs and dL/dy
+    read in the input dtype plus the float32 precision path, the six input
+    gradients written in the input dtype; per head the float32 state in
+    (lambda0, M0) read and its gradients written."""
+    per_token = (5 * dk + dv) * esz + dv * esz + 4 * dk + (5 * dk + dv) * esz
+    state = B * H * (dk + dk * dv) * 4 * 2
+    return B * H * T * per_token + state
 
 
 def run_configs(only, copies):
@@ -209,6 +221,31 @@ def run_configs(only, copies):
             x = xs = ys = run = None
             torch.cuda.empty_cache()
             continue
+        elif w.kind == "backward":
+            # One kla_backward call over the whole batch (all six kernels), on
+            # rotating input copies; each copy's precision path comes from one
+            # forward call before timing.
+            B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+            esz = 2 if w.dtype == "bf16" else 4
+            abytes = backward_algorithmic_bytes(B, H, T, dk, dv, esz)
+            ncopy = max(1, min(copies, int(1.2e9 // abytes)))
+            xs = []
+            for c in range(ncopy):
+                xc = KI.make_forward_inputs_torch(w, seed=w.seed + c, device=dev)
+                xc["grad_y"] = KI.make_backward_grads_torch(w, seed=w.seed + c, device=dev)
+                xc["lpath"] = K.forward(*(xc[n] for n in NAMES), xc["lambda0"], xc["M0"],
+                                        return_lambda_path=True)[3]
+                xc["out"] = tuple(torch.empty_like(xc[n]) for n in NAMES) + (
+                    torch.empty_like(xc["lambda0"]), torch.empty_like(xc["M0"]))
+                xs.append(xc)
+            ws = K.Workspace(dev)
+            calls, warm = 20, 5
+
+            def run(i):
+                xc = xs[i % ncopy]
+                return K.backward(*(xc[n] for n in NAMES), xc["grad_y"], xc["lpath"], xc["lambda0"], xc["M0"],
+                                  workspace=ws, out=xc["out"])
+            units, unit = B * H * T, "tokens/s"
         else:
             B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
             esz = 2 if w.dtype == "bf16" else 4

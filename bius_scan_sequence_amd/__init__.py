@@ -314,7 +314,7 @@ def _dtype_code(dtype):
 
 
 def backward(q, k, v, log_decay, proc_noise, val_prec, grad_y, lambda_path, lambda0=None, M0=None,
-             grad_lambda_T=None, grad_M_T=None, workspace: Workspace | None = None):
+             grad_lambda_T=None, grad_M_T=None, workspace: Workspace | None = None, out=None):
     """Gradients of the KLA forward pass on the current stream.
 
     Inputs as ``forward`` plus grad_y [B,H,T,dv] (input dtype), the float32
@@ -322,7 +322,8 @@ def backward(q, k, v, log_decay, proc_noise, val_prec, grad_y, lambda_path, lamb
     the optional float32 gradients of the state out, grad_lambda_T [B,H,dk]
     and grad_M_T [B,H,dk,dv].  Returns (grad_q, grad_k, grad_v,
     grad_log_decay, grad_proc_noise, grad_val_prec) in the input dtype and
-    (grad_lambda0, grad_M0) in float32.
+    (grad_lambda0, grad_M0) in float32.  ``out`` may hold the eight
+    preallocated result tensors in that order.
     """
     torch = _torch()
     B, H, T, dk = k.shape
@@ -338,9 +339,17 @@ def backward(q, k, v, log_decay, proc_noise, val_prec, grad_y, lambda_path, lamb
                          ("grad_lambda_T", grad_lambda_T, (B, H, dk)), ("grad_M_T", grad_M_T, (B, H, dk, dv))):
         if t is not None:
             _check(t, name, shp, torch.float32, dev)
-    grads = [torch.empty_like(x) for x in (q, k, v, log_decay, proc_noise, val_prec)]
-    g_lam0 = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
-    g_M0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if out is None:
+        grads = [torch.empty_like(x) for x in (q, k, v, log_decay, proc_noise, val_prec)]
+        g_lam0 = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+        g_M0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        *grads, g_lam0, g_M0 = out
+        for name, t, ref in zip(("grad_q", "grad_k", "grad_v", "grad_log_decay", "grad_proc_noise",
+                                 "grad_val_prec"), grads, (q, k, v, log_decay, proc_noise, val_prec)):
+            _check(t, name, ref.shape, dtype, dev)
+        _check(g_lam0, "grad_lambda0", (B, H, dk), torch.float32, dev)
+        _check(g_M0, "grad_M0", (B, H, dk, dv), torch.float32, dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     need = kla_backward_workspace_bytes(B, H, T, dk, dv)
     if need == 0:
