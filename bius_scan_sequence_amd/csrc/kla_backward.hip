@@ -59,36 +59,50 @@ __device__ __forceinline__ void stout(void* p, size_t x, float v) {
   static_cast<In*>(p)[x] = from_f32<In>(v);
 }
 
-// Forget and write gates of token t < T, channel i, from the saved precision path.
+// log2 of the forget gate and the write gate of token t < T, channel i, from
+// the saved precision path.  log2 f = log2 a + log2(lam^-/lam) is formed
+// without forming f, so strong decays (f below the fp32 range) stay exact.
 template <bool BF16>
-__device__ __forceinline__ void gates(const BwdParams& p, size_t hd, int t, int i, int K, float& f, float& g) {
+__device__ __forceinline__ void gates(const BwdParams& p, size_t hd, int t, int i, int K, float& lf, float& g) {
   const size_t x = (hd * p.T + t) * K + i;
   const float lam = p.lpath[x];
   const float lprev = t > 0 ? p.lpath[x - K] : (p.lam0 ? p.lam0[hd * K + i] : 1.f);
-  const float a = __expf(ldin<BF16>(p.ld, x));
-  const float lpred = lprev / fmaf(ldin<BF16>(p.pn, x), lprev, a * a);
-  f = a * lpred / lam;
-  g = ldin<BF16>(p.k, x) * ldin<BF16>(p.vp, x) / lam;
+  const float ld = ldin<BF16>(p.ld, x);
+  const float a = __expf(ld);
+  const float inv = fast_rcp(lam);
+  const float lpred = lprev * fast_rcp(fmaf(ldin<BF16>(p.pn, x), lprev, a * a));
+  lf = fmaf(ld, 1.44269504088896341f, __log2f(lpred * inv));
+  g = ldin<BF16>(p.k, x) * ldin<BF16>(p.vp, x) * inv;
 }
 
-// Stages the segment's tokens: f, g, q as [64][K+1] and v, dy as [64][V+1]
-// (rows padded by one word so that column walks hit distinct banks).  Tokens
-// past T are identity steps: f = 1, g = q = v = dy = 0.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Stages the segment's tokens: log2 f, g, q as [64][K+1] and v, dy as
+// [64][V+1] (rows padded by one word so that column walks hit distinct
+// banks), then turns log2 f into the cumulative sum inside each 16-token chunk
+// (lb) and writes each chunk's total to T[4][K].  Tokens past T are identity
+// steps: log2 f = 0, g = q = v = dy = 0.  Every decay the kernels need is then
+// exp2 of a short sum: inside a chunk lb_l - lb_m, across chunks the chunk
+// totals in between (never a difference of two long cumulative sums).
 template <int K, int V, bool BF16, int NT>
-__device__ __forceinline__ void stage_segment(const BwdParams& p, size_t hd, int t0, float* sf, float* sg,
-                                              float* sq, float* sv, float* sd) {
+__device__ __forceinline__ void stage_segment(const BwdParams& p, size_t hd, int t0, float* slb, float* sg,
+                                              float* sq, float* sv, float* sd, float* sT) {
   constexpr int KP = K + 1, VP = V + 1;
+  static_assert((kSL * K) % NT == 0 && (kSL * V) % NT == 0, "whole staging passes");
+  // Unrolled, so that every pass's loads are in flight together.
+#pragma unroll
   for (int x = threadIdx.x; x < kSL * K; x += NT) {
     const int t = x / K, i = x % K;
-    float f = 1.f, g = 0.f, q = 0.f;
+    float lf = 0.f, g = 0.f, q = 0.f;
     if (t0 + t < p.T) {
-      gates<BF16>(p, hd, t0 + t, i, K, f, g);
+      gates<BF16>(p, hd, t0 + t, i, K, lf, g);
       q = ldin<BF16>(p.q, (hd * p.T + t0 + t) * K + i);
     }
-    sf[t * KP + i] = f;
+    slb[t * KP + i] = lf;
     sg[t * KP + i] = g;
     sq[t * KP + i] = q;
   }
+#pragma unroll
   for (int x = threadIdx.x; x < kSL * V; x += NT) {
     const int t = x / V, j = x % V;
     float v = 0.f, d = 0.f;
@@ -100,69 +114,75 @@ __device__ __forceinline__ void stage_segment(const BwdParams& p, size_t hd, int
     sv[t * VP + j] = v;
     sd[t * VP + j] = d;
   }
+  __syncthreads();
+  // One thread per (channel, chunk): cumulative log2 f inside the chunk.
+  for (int x = threadIdx.x; x < 4 * K; x += NT) {
+    const int c = x / K, i = x % K;
+    float acc = 0.f;
+#pragma unroll
+    for (int l = 0; l < kC; ++l) {
+      acc += slb[(c * kC + l) * KP + i];
+      slb[(c * kC + l) * KP + i] = acc;
+    }
+    sT[c * K + i] = acc;
+  }
+  __syncthreads();
 }
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// 1. Segment aggregates.  Grid: nheads * nseg workgroups of 256 threads.
+// 1. Segment aggregates.  Grid: nheads * nseg workgroups of 512 threads.
 // ---------------------------------------------------------------------------
 template <int K, int V, bool BF16>
-__global__ __launch_bounds__(256) void kla_bwd_segagg_kernel(BwdParams p) {
-  constexpr int KP = K + 1, VP = V + 1, NT = 256;
-  __shared__ float sf[kSL * KP], sa[kSL * KP], sb[kSL * KP], sv[kSL * VP], sd[kSL * VP];
+__global__ __launch_bounds__(512) void kla_bwd_segagg_kernel(BwdParams p) {
+  constexpr int KP = K + 1, VP = V + 1, NT = 512;
+  __shared__ float sl[kSL * KP], sa[kSL * KP], sb[kSL * KP], sv[kSL * VP], sd[kSL * VP], sT[4 * K];
   const size_t hd = blockIdx.x / p.nseg;
   const int s = blockIdx.x % p.nseg;
   const int tid = threadIdx.x;
-  stage_segment<K, V, BF16, NT>(p, hd, s * kSL, sf, sa, sb, sv, sd);
-  __syncthreads();
-  if (tid < K) {
-    // alpha_t = g_t prod_{u>t} f_u (in place of g); beta_t = q_t prod_{u<=t} f_u (in place of q).
-    float run = 1.f;
-    for (int t = kSL - 1; t >= 0; --t) {
-      sa[t * KP + tid] *= run;
-      run *= sf[t * KP + tid];
+  stage_segment<K, V, BF16, NT>(p, hd, s * kSL, sl, sa, sb, sv, sd, sT);
+  // alpha_t = g_t prod_{u>t} f_u (in place of g), beta_t = q_t prod_{u<=t} f_u
+  // (in place of q), for t in chunk c: the products are exp2 of the chunk's
+  // partial sums plus the totals of the later / earlier chunks.
+  for (int x = tid; x < kSL * K; x += NT) {
+    const int t = x / K, i = x % K, c = t / kC;
+    float after = 0.f, before = 0.f;
+#pragma unroll
+    for (int c2 = 0; c2 < 4; ++c2) {
+      if (c2 > c) after += sT[c2 * K + i];
+      if (c2 < c) before += sT[c2 * K + i];
     }
-    p.F[(hd * p.nseg + s) * K + tid] = run;
-    float pre = 1.f;
-    for (int t = 0; t < kSL; ++t) {
-      pre *= sf[t * KP + tid];
-      sb[t * KP + tid] *= pre;
-    }
+    const float lb = sl[t * KP + i];
+    sa[t * KP + i] *= ex2((sT[c * K + i] - lb) + after);
+    sb[t * KP + i] *= ex2(lb + before);
   }
+  if (tid < K) p.F[(hd * p.nseg + s) * K + tid] = ex2(sT[tid] + sT[K + tid] + sT[2 * K + tid] + sT[3 * K + tid]);
   __syncthreads();
-  // Mean aggregate alpha^T v and adjoint aggregate beta^T dy, 4x4 tiles per thread.
-  constexpr int NJ = V / 4, NTILE = (K / 4) * NJ;
-  float* UM = p.Mseg + (hd * p.nseg + s) * (size_t)(K * V);
-  float* UH = p.Gseg + (hd * p.nseg + s) * (size_t)(K * V);
-  for (int tile = tid; tile < NTILE; tile += NT) {
-    const int i0 = (tile / NJ) * 4, j0 = (tile % NJ) * 4;
-    float am[4][4], ah[4][4];
+  // Mean aggregate alpha^T v and adjoint aggregate beta^T dy as 16x16 fp32
+  // matrix-core tiles (v_mfma_f32_16x16x4_f32), over the 64 tokens.
+  constexpr int KB = K / 16, VB = V / 16, NTILE = 2 * KB * VB;
+  const int wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+  const size_t base = (hd * p.nseg + s) * (size_t)(K * V);
+  for (int tile = wave; tile < NTILE; tile += NT / 64) {
+    const bool adj = tile >= KB * VB;
+    const int tt = adj ? tile - KB * VB : tile;
+    const int ib = tt / VB, jb = tt % VB;
+    const float* X = adj ? sb : sa;  // coefficient [t][i]
+    const float* Y = adj ? sd : sv;  // [t][j]
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int kb = 0; kb < kSL; kb += 16) {
+      v4f a, b;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) am[r][c] = ah[r][c] = 0.f;
-    for (int t = 0; t < kSL; ++t) {
-      float a[4], b[4], v[4], d[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        a[r] = sa[t * KP + i0 + r];
-        b[r] = sb[t * KP + i0 + r];
-        v[r] = sv[t * VP + j0 + r];
-        d[r] = sd[t * VP + j0 + r];
+      for (int e = 0; e < 4; ++e) {
+        a[e] = X[(kb + 4 * lg + e) * KP + ib * 16 + lr];
+        b[e] = Y[(kb + 4 * lg + e) * VP + jb * 16 + lr];
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          am[r][c] = fmaf(a[r], v[c], am[r][c]);
-          ah[r][c] = fmaf(b[r], d[c], ah[r][c]);
-        }
+      acc = mma_f32(acc, a, b);
     }
+    float* U = (adj ? p.Gseg : p.Mseg) + base;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      *reinterpret_cast<float4*>(UM + (i0 + r) * V + j0) = make_float4(am[r][0], am[r][1], am[r][2], am[r][3]);
-      *reinterpret_cast<float4*>(UH + (i0 + r) * V + j0) = make_float4(ah[r][0], ah[r][1], ah[r][2], ah[r][3]);
-    }
+    for (int e = 0; e < 4; ++e) U[(ib * 16 + 4 * lg + e) * V + jb * 16 + lr] = acc[e];
   }
 }
 
@@ -217,175 +237,287 @@ __global__ __launch_bounds__(256) void kla_bwd_segscan_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. Per-chunk gradients.  Grid: nheads * nseg workgroups of 512 threads.
+// 3. Per-chunk gradients.  Grid: nheads * nseg workgroups of 512 threads
+// (eight waves); the segment's chunks are taken last to first.  The
+// contractions run on the matrix cores in fp32 (v_mfma_f32_16x16x4_f32,
+// 16x16 tiles; lane layout in kla_device.h).  Waves 0-3 are key-side: key
+// wave w keeps, in registers, tiles of M_c^T and of H^T whose columns are key
+// block w; waves 4-7 are value-side: value wave w keeps the tiles of H whose
+// columns are value block w.  Each tile set is in the orientation in which it
+// is the B operand of the product that needs it:
+//   Mt[jb] = tile (jb, w) of M_c^T   (rows j, cols i in key block w):   dY M_c^T
+//   Ht[jb] = tile (jb, w) of H^T                                       V H^T
+//   Hc[ib] = tile (ib, w) of H       (rows i, cols j in value block w): Kd H
+// so the key-side outputs (dq, dg) of key block w and the value-side output
+// (dv) of value block w each come out of one wave with no cross-wave
+// reduction, and two waves share each SIMD.
+//
+// In-chunk decays D(l, m) = prod_{u=m+1..l} f_u = exp2(lb_l - lb_m).  When
+// every channel's log2 decay over each half of the chunk stays above -96
+// ("safe" chunk), D(l, m) = E_l F_m with E_l = exp2(lb_l - lb_7) and
+// F_m = exp2(lb_7 - lb_m) both inside the fp32 range, and the in-chunk terms
+// are matrix-core products of (q E), (g F) and the score matrices.  Other
+// chunks take the exact elementwise path, with every D(l, m) from its own
+// exp2.
 // ---------------------------------------------------------------------------
 template <int K, int V>
 struct BwdChunkSmem {
   static constexpr int KP = K + 1, VP = V + 1;
-  float f[kSL * KP], g[kSL * KP], q[kSL * KP], v[kSL * VP], d[kSL * VP];
-  float M[K * VP], H[K * VP];      // mean entering the chunk; adjoint at its end
-  float al[(kSL - kC) * KP];       // g_t prod_{u=t+1}^{c0-1} f_u for tokens before the chunk
-  float lb[kC * KP];               // cumulative log2 f inside the chunk
-  float cp[kC * KP];               // prod_{u<=l} f_u inside the chunk
-  float sx[kC * KP];               // prod_{u>l} f_u inside the chunk
-  float A[kC * kC], B[kC * kC];    // A[l][m] = q_l . (g_m decayed to l); B[l][m] = dy_l . v_m
-  float P[K];                      // prod of f from the segment start to the chunk start
+  float lb[kSL * KP], g[kSL * KP], q[kSL * KP], v[kSL * VP], d[kSL * VP];
+  float al[(kSL - kC) * KP];  // g_t prod_{u=t+1}^{c0-1} f_u for tokens before the chunk
+  float E[kC * KP];           // exp2(lb_l - lb_7)
+  float F[kC * KP];           // exp2(lb_7 - lb_l)
+  float cp[kC * KP];          // prod_{u<=l} f_u inside the chunk
+  float sx[kC * KP];          // prod_{u>l} f_u inside the chunk
+  float A[kC * kC], B[kC * kC];  // A[l][m] = q_l . (g_m decayed to l); B[l][m] = dy_l . v_m (m <= l; 0 above)
+  float T[4 * K];             // sum of log2 f over each chunk of the segment
 };
 
 template <int K, int V, bool BF16>
 __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams p) {
   constexpr int KP = K + 1, VP = V + 1, NT = kChunkThreads, C = kC;
-  static_assert(NT == 2 * C * C, "one score pair per thread for A and for B");
+  constexpr int KB = K / 16, VB = V / 16;
+  static_assert(NT == 2 * C * C && NT == 512, "eight waves; one score pair per thread of the first four");
   __shared__ BwdChunkSmem<K, V> s;
   const size_t hd = blockIdx.x / p.nseg;
   const int seg = blockIdx.x % p.nseg;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const int t0 = seg * kSL;
   const int nvalid = min(kSL, p.T - t0);
-  stage_segment<K, V, BF16, NT>(p, hd, t0, s.f, s.g, s.q, s.v, s.d);
   const size_t st = (hd * p.nseg + seg) * (size_t)(K * V);
   const float* Mg = p.Mseg + st;
-  for (int x = tid; x < K * V; x += NT) s.H[(x / V) * VP + x % V] = p.Gseg[st + x];
-  __syncthreads();
+  const float* Gg = p.Gseg + st;
+  const int kb_w = wave, vb_w = wave - 4;       // key block of a key wave, value block of a value wave
+  const bool kw = wave < KB, vw = wave >= 4 && vb_w < VB;
+  // Adjoint at the segment end (H for value waves, H^T for key waves) and the
+  // mean entering the segment (M^T, key waves), loaded before staging.
+  v4f Hc[KB], Ht[VB], Mt[VB], Ms[VB];
+#pragma unroll
+  for (int ib = 0; ib < KB; ++ib)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Hc[ib][e] = vw ? Gg[(ib * 16 + 4 * lg + e) * V + vb_w * 16 + lr] : 0.f;
+#pragma unroll
+  for (int jb = 0; jb < VB; ++jb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      Ht[jb][e] = kw ? Gg[(kb_w * 16 + lr) * V + jb * 16 + 4 * lg + e] : 0.f;
+      Ms[jb][e] = kw ? Mg[(kb_w * 16 + lr) * V + jb * 16 + 4 * lg + e] : 0.f;
+    }
+  stage_segment<K, V, BF16, NT>(p, hd, t0, s.lb, s.g, s.q, s.v, s.d, s.T);
 
   for (int w = (nvalid - 1) / C; w >= 0; --w) {
     const int c0 = w * C;
-    // (a) per-channel running products.
-    if (tid < K) {
-      const int i = tid;
-      float run = 1.f;
-      for (int t = c0 - 1; t >= 0; --t) {
-        s.al[t * KP + i] = s.g[t * KP + i] * run;
-        run *= s.f[t * KP + i];
-      }
-      s.P[i] = run;
-      float cp = 1.f, lb = 0.f;
-      for (int l = 0; l < C; ++l) {
-        const float f = s.f[(c0 + l) * KP + i];
-        cp *= f;
-        lb += __log2f(fmaxf(f, 1e-37f));
-        s.cp[l * KP + i] = cp;
-        s.lb[l * KP + i] = lb;
-      }
-      float sx = 1.f;
-      for (int l = C - 1; l >= 0; --l) {
-        s.sx[l * KP + i] = sx;
-        sx *= s.f[(c0 + l) * KP + i];
-      }
-    }
-    __syncthreads();
-    // (b) mean entering the chunk: diag(P) M_seg + sum_{t<c0} al_t v_t^T (4x2 tiles).
-    {
-      constexpr int NJ2 = V / 2, NTILE = (K / 4) * NJ2;
-      for (int tile = tid; tile < NTILE; tile += NT) {
-        const int i0 = (tile / NJ2) * 4, j0 = (tile % NJ2) * 2;
-        float acc[4][2];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float P = s.P[i0 + r];
-          const float2 m = *reinterpret_cast<const float2*>(Mg + (i0 + r) * V + j0);
-          acc[r][0] = P * m.x;
-          acc[r][1] = P * m.y;
-        }
-        for (int t = 0; t < c0; ++t) {
-          const float v0 = s.v[t * VP + j0], v1 = s.v[t * VP + j0 + 1];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float al = s.al[t * KP + i0 + r];
-            acc[r][0] = fmaf(al, v0, acc[r][0]);
-            acc[r][1] = fmaf(al, v1, acc[r][1]);
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          s.M[(i0 + r) * VP + j0] = acc[r][0];
-          s.M[(i0 + r) * VP + j0 + 1] = acc[r][1];
-        }
-      }
-    }
-    // (c) in-chunk scores for m <= l (zero above the diagonal).
-    {
-      const int pr = tid & (C * C - 1), l = pr / C, m = pr % C;
-      float acc = 0.f;
-      if (m <= l) {
-        if (tid < C * C) {
-          for (int i = 0; i < K; ++i)
-            acc = fmaf(s.q[(c0 + l) * KP + i] * s.g[(c0 + m) * KP + i],
-                       exp2f(s.lb[l * KP + i] - s.lb[m * KP + i]), acc);
-        } else {
-          for (int j = 0; j < V; ++j) acc = fmaf(s.d[(c0 + l) * VP + j], s.v[(c0 + m) * VP + j], acc);
-        }
-      }
-      (tid < C * C ? s.A : s.B)[l * C + m] = acc;
-    }
-    __syncthreads();
-    // (d) per (token, key channel): dq, dg, e;  per (token, value channel): dv.
-    const size_t tok0 = hd * (size_t)p.T + t0 + c0;
+    // (a) elementwise decays of this chunk, and of the tokens before it.
+    int unsafe = 0;
     for (int x = tid; x < C * K; x += NT) {
       const int l = x / K, i = x % K;
-      if (c0 + l >= nvalid) continue;
-      float xs = 0.f, ys = 0.f;
-      for (int j = 0; j < V; ++j) {
-        xs = fmaf(s.d[(c0 + l) * VP + j], s.M[i * VP + j], xs);
-        ys = fmaf(s.v[(c0 + l) * VP + j], s.H[i * VP + j], ys);
-      }
-      float dqi = 0.f, D = 1.f;
-      for (int m = l; m >= 0; --m) {
-        dqi = fmaf(s.B[l * C + m] * s.g[(c0 + m) * KP + i], D, dqi);
-        D *= s.f[(c0 + m) * KP + i];
-      }
-      float dgi = 0.f;
-      D = 1.f;
-      for (int l2 = l; l2 < C; ++l2) {
-        dgi = fmaf(s.B[l2 * C + l] * s.q[(c0 + l2) * KP + i], D, dgi);
-        if (l2 + 1 < C) D *= s.f[(c0 + l2 + 1) * KP + i];
-      }
-      const float dq = fmaf(s.cp[l * KP + i], xs, dqi);
-      const float dg = fmaf(s.sx[l * KP + i], ys, dgi);
-      const size_t o = (tok0 + l) * K + i;
-      stout<BF16>(p.dq, o, dq);
-      p.dgw[o] = dg;
-      p.ew[o] = s.q[(c0 + l) * KP + i] * dq - s.g[(c0 + l) * KP + i] * dg;
+      const float lb = s.lb[(c0 + l) * KP + i], lb7 = s.lb[(c0 + 7) * KP + i];
+      const float tot = s.T[w * K + i];
+      s.E[l * KP + i] = ex2(lb - lb7);
+      s.F[l * KP + i] = ex2(lb7 - lb);
+      s.cp[l * KP + i] = ex2(lb);
+      s.sx[l * KP + i] = ex2(tot - lb);
+      if (l == 0) unsafe |= (s.lb[c0 * KP + i] - lb7 > 96.f) | (lb7 - s.lb[(c0 + C - 1) * KP + i] > 96.f);
     }
-    for (int x = tid; x < C * V; x += NT) {
-      const int m = x / V, j = x % V;
-      if (c0 + m >= nvalid) continue;
+    for (int x = tid; x < c0 * K; x += NT) {
+      const int t = x / K, i = x % K, c2 = t / C;
+      float mid = 0.f;
+      for (int c3 = c2 + 1; c3 < w; ++c3) mid += s.T[c3 * K + i];
+      s.al[t * KP + i] = s.g[t * KP + i] * ex2((s.T[c2 * K + i] - s.lb[t * KP + i]) + mid);
+    }
+    const bool safe = __syncthreads_or(unsafe) == 0;
+    // (b) M_c^T tiles: the segment state decayed to the chunk start plus the
+    // tokens before the chunk (v^T al over t < c0); the two score matrices.
+    if (kw) {
+      const int i = kb_w * 16 + lr;
+      float lP = 0.f;
+      for (int c3 = 0; c3 < w; ++c3) lP += s.T[c3 * K + i];
+      const float Pi = ex2(lP);
+#pragma unroll
+      for (int jb = 0; jb < VB; ++jb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Mt[jb][e] = Pi * Ms[jb][e];
+        for (int kb = 0; kb < c0; kb += 16) {
+          v4f a, b;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a[e] = s.v[(kb + 4 * lg + e) * VP + jb * 16 + lr];
+            b[e] = s.al[(kb + 4 * lg + e) * KP + i];
+          }
+          Mt[jb] = mma_f32(Mt[jb], a, b);
+        }
+      }
+    }
+    if (wave == 7) {
+      // B[l][m] = dy_l . v_m (one tile, V/16 blocks).
+      v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jb = 0; jb < VB; ++jb) {
+        v4f a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = s.d[(c0 + lr) * VP + jb * 16 + 4 * lg + e];
+          b[e] = s.v[(c0 + lr) * VP + jb * 16 + 4 * lg + e];
+        }
+        acc = mma_f32(acc, a, b);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s.B[(4 * lg + e) * C + lr] = lr <= 4 * lg + e ? acc[e] : 0.f;
+    }
+    if (safe) {
+      if (wave == 6) {
+        // A = tril((q E)(g F)^T) (one tile, K/16 blocks).
+        v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < K; kb += 16) {
+          v4f a, b;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = kb + 4 * lg + e;
+            a[e] = s.q[(c0 + lr) * KP + i] * s.E[lr * KP + i];
+            b[e] = s.g[(c0 + lr) * KP + i] * s.F[lr * KP + i];
+          }
+          acc = mma_f32(acc, a, b);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s.A[(4 * lg + e) * C + lr] = lr <= 4 * lg + e ? acc[e] : 0.f;
+      }
+    } else {
+      // Exact scores: A[l][m] = sum_i q_l g_m exp2(lb_l - lb_m), m <= l.
+      const int l = (tid / C) % C, m = tid % C;
       float acc = 0.f;
-      for (int l = m; l < C; ++l) acc = fmaf(s.A[l * C + m], s.d[(c0 + l) * VP + j], acc);
-      for (int i = 0; i < K; ++i)
-        acc = fmaf(s.g[(c0 + m) * KP + i] * s.sx[m * KP + i], s.H[i * VP + j], acc);
-      stout<BF16>(p.dv, (tok0 + m) * V + j, acc);
+      if (m <= l && tid < C * C)
+        for (int i = 0; i < K; ++i)
+          acc = fmaf(s.q[(c0 + l) * KP + i] * s.g[(c0 + m) * KP + i],
+                     ex2(s.lb[(c0 + l) * KP + i] - s.lb[(c0 + m) * KP + i]), acc);
+      if (tid < C * C) s.A[l * C + m] = acc;
     }
     __syncthreads();
-    // (e) adjoint at the end of the previous chunk: diag(cp_end) H + sum_l (cp_l q_l) dy_l^T.
-    if (w > 0) {
-      constexpr int NJ2 = V / 2, NTILE = (K / 4) * NJ2;
-      for (int tile = tid; tile < NTILE; tile += NT) {
-        const int i0 = (tile / NJ2) * 4, j0 = (tile % NJ2) * 2;
-        float acc[4][2];
+    // (c) outputs.
+    const size_t tok0 = hd * (size_t)p.T + t0 + c0;
+    if (kw) {
+      // Xs = dY M_c^T, Ys = V H^T; in-chunk parts dqi = E (tril(B) (g F)),
+      // dgi = F (tril(B)^T (q E)) for key block `wave`.
+      const int i = kb_w * 16 + lr;
+      v4f xs = v4f{0.f, 0.f, 0.f, 0.f}, ys = xs, dqi = xs, dgi = xs;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float ce = s.cp[(C - 1) * KP + i0 + r];
-          acc[r][0] = ce * s.H[(i0 + r) * VP + j0];
-          acc[r][1] = ce * s.H[(i0 + r) * VP + j0 + 1];
+      for (int jb = 0; jb < VB; ++jb) {
+        v4f a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = s.d[(c0 + lr) * VP + jb * 16 + 4 * lg + e];
+          b[e] = s.v[(c0 + lr) * VP + jb * 16 + 4 * lg + e];
         }
-        for (int l = 0; l < C; ++l) {
-          const float d0 = s.d[(c0 + l) * VP + j0], d1 = s.d[(c0 + l) * VP + j0 + 1];
+        xs = mma_f32(xs, a, Mt[jb]);
+        ys = mma_f32(ys, b, Ht[jb]);
+      }
+      if (safe) {
+        v4f a, b, c, d;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float b = s.cp[l * KP + i0 + r] * s.q[(c0 + l) * KP + i0 + r];
-            acc[r][0] = fmaf(b, d0, acc[r][0]);
-            acc[r][1] = fmaf(b, d1, acc[r][1]);
+        for (int e = 0; e < 4; ++e) {
+          const int n = 4 * lg + e;
+          a[e] = s.B[lr * C + n];  // tril(B)[l = lr][m = n]
+          b[e] = s.g[(c0 + n) * KP + i] * s.F[n * KP + i];
+          c[e] = s.B[n * C + lr];  // tril(B)^T[l = lr][n]
+          d[e] = s.q[(c0 + n) * KP + i] * s.E[n * KP + i];
+        }
+        dqi = mma_f32(dqi, a, b);
+        dgi = mma_f32(dgi, c, d);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int l = 4 * lg + e;
+          dqi[e] *= s.E[l * KP + i];
+          dgi[e] *= s.F[l * KP + i];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int l = 4 * lg + e;
+          const float lbl = s.lb[(c0 + l) * KP + i];
+          float aq = 0.f, ag = 0.f;
+          for (int m = 0; m < C; ++m) {
+            const float lbm = s.lb[(c0 + m) * KP + i];
+            if (m <= l) aq = fmaf(s.B[l * C + m] * s.g[(c0 + m) * KP + i], ex2(lbl - lbm), aq);
+            if (m >= l) ag = fmaf(s.B[m * C + l] * s.q[(c0 + m) * KP + i], ex2(lbm - lbl), ag);
           }
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          s.H[(i0 + r) * VP + j0] = acc[r][0];
-          s.H[(i0 + r) * VP + j0 + 1] = acc[r][1];
+          dqi[e] = aq;
+          dgi[e] = ag;
         }
       }
-      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int l = 4 * lg + e;
+        if (c0 + l >= nvalid) continue;
+        const float dq = fmaf(s.cp[l * KP + i], xs[e], dqi[e]);
+        const float dg = fmaf(s.sx[l * KP + i], ys[e], dgi[e]);
+        const size_t o = (tok0 + l) * K + i;
+        stout<BF16>(p.dq, o, dq);
+        p.dgw[o] = dg;
+        p.ew[o] = s.q[(c0 + l) * KP + i] * dq - s.g[(c0 + l) * KP + i] * dg;
+      }
     }
+    if (vw) {
+      // dv = Kd H + tril(A)^T dY for value block `wave - 4`, Kd = g sx.
+      const int j = vb_w * 16 + lr;
+      v4f dv = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ib = 0; ib < KB; ++ib) {
+        v4f a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = ib * 16 + 4 * lg + e;
+          a[e] = s.g[(c0 + lr) * KP + i] * s.sx[lr * KP + i];
+        }
+        dv = mma_f32(dv, a, Hc[ib]);
+      }
+      {
+        v4f a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = s.A[(4 * lg + e) * C + lr];  // tril(A)^T[m = lr][l]
+          b[e] = s.d[(c0 + 4 * lg + e) * VP + j];
+        }
+        dv = mma_f32(dv, a, b);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 4 * lg + e;
+        if (c0 + m < nvalid) stout<BF16>(p.dv, (tok0 + m) * V + j, dv[e]);
+      }
+    }
+    // (d) adjoint at the end of the previous chunk: diag(cp_end) H + (cp q)^T dY,
+    // in both orientations (registers of this wave; LDS operands of this chunk).
+    if (w > 0) {
+      if (vw) {
+#pragma unroll
+        for (int ib = 0; ib < KB; ++ib) {
+          v4f a, b;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            Hc[ib][e] *= s.cp[(C - 1) * KP + ib * 16 + 4 * lg + e];
+            a[e] = s.cp[(4 * lg + e) * KP + ib * 16 + lr] * s.q[(c0 + 4 * lg + e) * KP + ib * 16 + lr];
+            b[e] = s.d[(c0 + 4 * lg + e) * VP + vb_w * 16 + lr];
+          }
+          Hc[ib] = mma_f32(Hc[ib], a, b);
+        }
+      }
+      if (kw) {
+        const int i = kb_w * 16 + lr;
+        const float ce = s.cp[(C - 1) * KP + i];
+#pragma unroll
+        for (int jb = 0; jb < VB; ++jb) {
+          v4f a, b;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            Ht[jb][e] *= ce;
+            a[e] = s.d[(c0 + 4 * lg + e) * VP + jb * 16 + lr];
+            b[e] = s.cp[(4 * lg + e) * KP + i] * s.q[(c0 + 4 * lg + e) * KP + i];
+          }
+          Ht[jb] = mma_f32(Ht[jb], a, b);
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -431,7 +563,7 @@ __global__ __launch_bounds__(256) void kla_bwd_chain_comp_kernel(BwdParams p, in
   const int i = (int)(ch % K);
   const int tb = b * kSL, te = min(p.T, tb + kSL);
   float E = 0.f, Pm = 1.f, Qa = 0.f, R = 0.f;
-  for (int t = te - 1; t >= tb; --t) {
+  auto step = [&](int t) {
     const ChainTok c = chain_tok<BF16>(p, hd, ch, t, K, i);
     const float g = c.k * c.vp / c.lam;
     const float m = c.a2 / (c.D * c.D);
@@ -441,6 +573,13 @@ __global__ __launch_bounds__(256) void kla_bwd_chain_comp_kernel(BwdParams p, in
     Pm *= m;
     Qa = m * (Qa + c1);
     R = m * fmaf(c1, E, R + c0);
+  };
+  if (te - tb == kSL) {
+    // Full block: unrolled, so that several tokens' loads are in flight.
+#pragma unroll 8
+    for (int u = kSL - 1; u >= 0; --u) step(tb + u);
+  } else {
+    for (int t = te - 1; t >= tb; --t) step(t);
   }
   reinterpret_cast<float4*>(p.comp)[(size_t)b * p.nchains + ch] = make_float4(E, Pm, Qa, R);
 }
@@ -468,7 +607,7 @@ __global__ __launch_bounds__(256) void kla_bwd_chain_out_kernel(BwdParams p, int
   const int tb = b * kSL, te = min(p.T, tb + kSL);
   const float2 in = reinterpret_cast<const float2*>(p.cin)[(size_t)b * p.nchains + ch];
   float acc = in.x, L = in.y;
-  for (int t = te - 1; t >= tb; --t) {
+  auto step = [&](int t) {
     const ChainTok c = chain_tok<BF16>(p, hd, ch, t, K, i);
     const float g = c.k * c.vp / c.lam;
     const float c0 = -g * c.dg / c.lam;
@@ -482,6 +621,12 @@ __global__ __launch_bounds__(256) void kla_bwd_chain_out_kernel(BwdParams p, int
     stout<BF16>(p.dk, x, c.vp / c.lam * c.dg + 2.f * c.k * c.vp * dc);
     stout<BF16>(p.dvp, x, c.k / c.lam * c.dg + c.k * c.k * dc);
     L = Llp * (c.a2 / (c.D * c.D));
+  };
+  if (te - tb == kSL) {
+#pragma unroll 8
+    for (int u = kSL - 1; u >= 0; --u) step(tb + u);
+  } else {
+    for (int t = te - 1; t >= tb; --t) step(t);
   }
 }
 
@@ -498,7 +643,7 @@ __global__ void kla_bwd_empty_kernel(const float* dlamT, const float* dMT, float
 template <int K, int V, bool BF16>
 static hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   const unsigned nsb = (unsigned)((long long)p.nheads * p.nseg);
-  hipLaunchKernelGGL((kla_bwd_segagg_kernel<K, V, BF16>), dim3(nsb), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((kla_bwd_segagg_kernel<K, V, BF16>), dim3(nsb), dim3(512), 0, stream, p);
   constexpr int NB = (K * V / 4 + 255) / 256;
   hipLaunchKernelGGL((kla_bwd_segscan_kernel<K, V>), dim3((unsigned)(p.nheads * NB)), dim3(256), 0, stream, p);
   hipLaunchKernelGGL((kla_bwd_chunk_kernel<K, V, BF16>), dim3(nsb), dim3(kChunkThreads), 0, stream, p);
