@@ -158,9 +158,9 @@ extern "C" int kla_backward(const void* q, const void* k, const void* v, const v
   if (!supported_width(dk) || !supported_width(dv)) return KLA_ERR_UNSUPPORTED;
   if (dk > 64 || dv > 64) return KLA_ERR_UNSUPPORTED;
   if (!bwd_shape_ok(B, H, T, dk, dv)) return KLA_ERR_INVALID_ARG;
-  const size_t esz = dtype == KLA_BF16 ? 2 : 4;
+  // Per-token arrays are read and written four elements at a time.
   for (int x = 0; x < 14; ++x)
-    if (tok[x] && !aligned(tok[x], x == 6 ? 4 : esz)) return KLA_ERR_INVALID_ARG;
+    if (tok[x] && !aligned(tok[x], 16)) return KLA_ERR_INVALID_ARG;
   if ((lambda0 && !aligned(lambda0, 4)) || (grad_lambda_T && !aligned(grad_lambda_T, 4)) ||
       !aligned(grad_lambda0, 4) || (M0 && !aligned(M0, 16)) || (grad_M_T && !aligned(grad_M_T, 16)) ||
       !aligned(grad_M0, 16))

@@ -59,63 +59,115 @@ __device__ __forceinline__ void stout(void* p, size_t x, float v) {
   static_cast<In*>(p)[x] = from_f32<In>(v);
 }
 
-// log2 of the forget gate and the write gate of token t < T, channel i, from
-// the saved precision path.  log2 f = log2 a + log2(lam^-/lam) is formed
-// without forming f, so strong decays (f below the fp32 range) stay exact.
+// Four consecutive elements x .. x+3 of a per-token input (16-byte aligned
+// rows; x a multiple of 4): one 8-byte load for bf16, one 16-byte load for fp32.
 template <bool BF16>
-__device__ __forceinline__ void gates(const BwdParams& p, size_t hd, int t, int i, int K, float& lf, float& g) {
-  const size_t x = (hd * p.T + t) * K + i;
-  const float lam = p.lpath[x];
-  const float lprev = t > 0 ? p.lpath[x - K] : (p.lam0 ? p.lam0[hd * K + i] : 1.f);
-  const float ld = ldin<BF16>(p.ld, x);
+__device__ __forceinline__ float4 ldin4(const void* p, size_t x) {
+  if constexpr (BF16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + x);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+  } else {
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + x);
+  }
+}
+
+// log2 of the forget gate and the write gate of one element (token t < T),
+// from the saved precision after the token (lam) and before it (lprev).
+// log2 f = log2 a + log2(lam^-/lam) is formed without forming f, so strong
+// decays (f below the fp32 range) stay exact.
+__device__ __forceinline__ void gate1(float lam, float lprev, float ld, float pn, float k, float vp, float& lf,
+                                      float& g) {
   const float a = __expf(ld);
   const float inv = fast_rcp(lam);
-  const float lpred = lprev * fast_rcp(fmaf(ldin<BF16>(p.pn, x), lprev, a * a));
+  const float lpred = lprev * fast_rcp(fmaf(pn, lprev, a * a));
   lf = fmaf(ld, 1.44269504088896341f, __log2f(lpred * inv));
-  g = ldin<BF16>(p.k, x) * ldin<BF16>(p.vp, x) * inv;
+  g = k * vp * inv;
 }
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// v and dy are kept in their input type (bf16 bits are exact); the row
+// stride of those arrays, in elements: bf16 rows padded by 4 elements, so that
+// the four 4-row groups of a matrix-core operand read fall on distinct banks.
+template <int V, bool BF16> struct VRow {
+  using T = typename std::conditional<BF16, uint16_t, float>::type;
+  static constexpr int P = BF16 ? V + 4 : V + 1;
+};
+
 // Stages the segment's tokens: log2 f, g, q as [64][K+1] and v, dy as
-// [64][V+1] (rows padded by one word so that column walks hit distinct
-// banks), then turns log2 f into the cumulative sum inside each 16-token chunk
-// (lb) and writes each chunk's total to T[4][K].  Tokens past T are identity
-// steps: log2 f = 0, g = q = v = dy = 0.  Every decay the kernels need is then
-// exp2 of a short sum: inside a chunk lb_l - lb_m, across chunks the chunk
-// totals in between (never a difference of two long cumulative sums).
+// [64][VRow::P] (rows padded so that column walks hit distinct banks), then
+// turns log2 f into the cumulative sum inside each 16-token chunk (lb) and
+// writes each chunk's total to T[4][K].  Tokens past T are identity steps:
+// log2 f = 0, g = q = v = dy = 0.  Every decay the kernels need is then exp2
+// of a short sum: inside a chunk lb_l - lb_m, across chunks the chunk totals
+// in between (never a difference of two long cumulative sums).  A thread
+// stages four consecutive channels of a token with vector loads.
 template <int K, int V, bool BF16, int NT>
 __device__ __forceinline__ void stage_segment(const BwdParams& p, size_t hd, int t0, float* slb, float* sg,
-                                              float* sq, float* sv, float* sd, float* sT) {
-  constexpr int KP = K + 1, VP = V + 1;
-  static_assert((kSL * K) % NT == 0 && (kSL * V) % NT == 0, "whole staging passes");
+                                              float* sq, typename VRow<V, BF16>::T* sv,
+                                              typename VRow<V, BF16>::T* sd, float* sT) {
+  using In = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr int KP = K + 1, VP = VRow<V, BF16>::P, K4 = K / 4, V4 = V / 4;
+  static_assert((kSL * K4) % NT == 0 || NT % (kSL * K4) == 0, "staging passes");
   // Unrolled, so that every pass's loads are in flight together.
 #pragma unroll
-  for (int x = threadIdx.x; x < kSL * K; x += NT) {
-    const int t = x / K, i = x % K;
-    float lf = 0.f, g = 0.f, q = 0.f;
+  for (int x = threadIdx.x; x < kSL * K4; x += NT) {
+    const int t = x / K4, i = (x % K4) * 4;
+    float lf[4] = {0.f, 0.f, 0.f, 0.f}, g[4] = {0.f, 0.f, 0.f, 0.f}, q[4] = {0.f, 0.f, 0.f, 0.f};
     if (t0 + t < p.T) {
-      gates<BF16>(p, hd, t0 + t, i, K, lf, g);
-      q = ldin<BF16>(p.q, (hd * p.T + t0 + t) * K + i);
+      const size_t e = (hd * p.T + t0 + t) * K + i;
+      const float4 lam = *reinterpret_cast<const float4*>(p.lpath + e);
+      float4 lprev;
+      if (t0 + t > 0) {
+        lprev = *reinterpret_cast<const float4*>(p.lpath + e - K);
+      } else if (p.lam0) {
+        const float* l0 = p.lam0 + hd * K + i;
+        lprev = make_float4(l0[0], l0[1], l0[2], l0[3]);
+      } else {
+        lprev = make_float4(1.f, 1.f, 1.f, 1.f);
+      }
+      const float4 ld = ldin4<BF16>(p.ld, e), pn = ldin4<BF16>(p.pn, e), k = ldin4<BF16>(p.k, e),
+                   vp = ldin4<BF16>(p.vp, e), qq = ldin4<BF16>(p.q, e);
+      gate1(lam.x, lprev.x, ld.x, pn.x, k.x, vp.x, lf[0], g[0]);
+      gate1(lam.y, lprev.y, ld.y, pn.y, k.y, vp.y, lf[1], g[1]);
+      gate1(lam.z, lprev.z, ld.z, pn.z, k.z, vp.z, lf[2], g[2]);
+      gate1(lam.w, lprev.w, ld.w, pn.w, k.w, vp.w, lf[3], g[3]);
+      q[0] = qq.x; q[1] = qq.y; q[2] = qq.z; q[3] = qq.w;
     }
-    slb[t * KP + i] = lf;
-    sg[t * KP + i] = g;
-    sq[t * KP + i] = q;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      slb[t * KP + i + r] = lf[r];
+      sg[t * KP + i + r] = g[r];
+      sq[t * KP + i + r] = q[r];
+    }
   }
 #pragma unroll
-  for (int x = threadIdx.x; x < kSL * V; x += NT) {
-    const int t = x / V, j = x % V;
-    float v = 0.f, d = 0.f;
+  for (int x = threadIdx.x; x < kSL * V4; x += NT) {
+    const int t = x / V4, j = (x % V4) * 4;
+    In v[4] = {0, 0, 0, 0}, d[4] = {0, 0, 0, 0};
     if (t0 + t < p.T) {
       const size_t y = (hd * p.T + t0 + t) * V + j;
-      v = ldin<BF16>(p.v, y);
-      d = ldin<BF16>(p.dy, y);
+      if constexpr (BF16) {
+        const uint2 uv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.v) + y);
+        const uint2 ud = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.dy) + y);
+        v[0] = (In)uv.x; v[1] = (In)(uv.x >> 16); v[2] = (In)uv.y; v[3] = (In)(uv.y >> 16);
+        d[0] = (In)ud.x; d[1] = (In)(ud.x >> 16); d[2] = (In)ud.y; d[3] = (In)(ud.y >> 16);
+      } else {
+        const float4 fv = *reinterpret_cast<const float4*>(static_cast<const float*>(p.v) + y);
+        const float4 fd = *reinterpret_cast<const float4*>(static_cast<const float*>(p.dy) + y);
+        v[0] = fv.x; v[1] = fv.y; v[2] = fv.z; v[3] = fv.w;
+        d[0] = fd.x; d[1] = fd.y; d[2] = fd.z; d[3] = fd.w;
+      }
     }
-    sv[t * VP + j] = v;
-    sd[t * VP + j] = d;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv[t * VP + j + r] = v[r];
+      sd[t * VP + j + r] = d[r];
+    }
   }
   __syncthreads();
-  // One thread per (channel, chunk): cumulative log2 f inside the chunk.
+// One thread per (channel, chunk): cumulative log2 f inside the chunk.
   for (int x = threadIdx.x; x < 4 * K; x += NT) {
     const int c = x / K, i = x % K;
     float acc = 0.f;
@@ -135,8 +187,10 @@ __device__ __forceinline__ void stage_segment(const BwdParams& p, size_t hd, int
 // ---------------------------------------------------------------------------
 template <int K, int V, bool BF16>
 __global__ __launch_bounds__(512) void kla_bwd_segagg_kernel(BwdParams p) {
-  constexpr int KP = K + 1, VP = V + 1, NT = 512;
-  __shared__ float sl[kSL * KP], sa[kSL * KP], sb[kSL * KP], sv[kSL * VP], sd[kSL * VP], sT[4 * K];
+  using SV = typename VRow<V, BF16>::T;
+  constexpr int KP = K + 1, VP = VRow<V, BF16>::P, NT = 512;
+  __shared__ float sl[kSL * KP], sa[kSL * KP], sb[kSL * KP], sT[4 * K];
+  __shared__ SV sv[kSL * VP], sd[kSL * VP];
   const size_t hd = blockIdx.x / p.nseg;
   const int s = blockIdx.x % p.nseg;
   const int tid = threadIdx.x;
@@ -168,7 +222,7 @@ __global__ __launch_bounds__(512) void kla_bwd_segagg_kernel(BwdParams p) {
     const int tt = adj ? tile - KB * VB : tile;
     const int ib = tt / VB, jb = tt % VB;
     const float* X = adj ? sb : sa;  // coefficient [t][i]
-    const float* Y = adj ? sd : sv;  // [t][j]
+    const SV* Y = adj ? sd : sv;     // [t][j]
     v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < kSL; kb += 16) {
@@ -176,7 +230,7 @@ __global__ __launch_bounds__(512) void kla_bwd_segagg_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         a[e] = X[(kb + 4 * lg + e) * KP + ib * 16 + lr];
-        b[e] = Y[(kb + 4 * lg + e) * VP + jb * 16 + lr];
+        b[e] = to_f32(Y[(kb + 4 * lg + e) * VP + jb * 16 + lr]);
       }
       acc = mma_f32(acc, a, b);
     }
@@ -187,52 +241,70 @@ __global__ __launch_bounds__(512) void kla_bwd_segagg_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 2. Scans over segments.  Grid: nheads * ceil(K*V/4 / 256) workgroups of 256
-// threads; a thread owns four consecutive elements of one state row.
+// 2. Scans over segments.  Grid: nheads * ceil(K*V / 256) workgroups of 256
+// threads; one thread per state element, eight segments' loads in flight.
 // ---------------------------------------------------------------------------
 template <int K, int V>
 __global__ __launch_bounds__(256) void kla_bwd_segscan_kernel(BwdParams p) {
-  constexpr int NJ = V / 4, N4 = K * NJ;
-  constexpr int NB = (N4 + 255) / 256;
+  constexpr int N = K * V, NB = (N + 255) / 256, G = 8;
   const size_t hd = blockIdx.x / NB;
-  const int e4 = (blockIdx.x % NB) * 256 + threadIdx.x;
-  const bool live = e4 < N4;
-  const int i = e4 / NJ;
+  const int el = (blockIdx.x % NB) * 256 + threadIdx.x;
+  const bool live = el < N;
+  const int i = el / V;
   const int nseg = p.nseg;
-  float4* Ms = reinterpret_cast<float4*>(p.Mseg + hd * nseg * (size_t)(K * V));
-  float4* Gs = reinterpret_cast<float4*>(p.Gseg + hd * nseg * (size_t)(K * V));
+  float* Ms = p.Mseg + hd * nseg * (size_t)N;
+  float* Gs = p.Gseg + hd * nseg * (size_t)N;
   const float* F = p.F + hd * nseg * (size_t)K + i;
   float part = 0.f;
   if (live) {
-    float4 m = p.M0 ? reinterpret_cast<const float4*>(p.M0 + hd * (size_t)(K * V))[e4] : make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 u = Ms[e4];
-    for (int s = 0; s < nseg; ++s) {
-      const float4 un = s + 1 < nseg ? Ms[(size_t)(s + 1) * N4 + e4] : u;
-      const float f = F[(size_t)s * K];
-      Ms[(size_t)s * N4 + e4] = m;
-      m = make_float4(fmaf(f, m.x, u.x), fmaf(f, m.y, u.y), fmaf(f, m.z, u.z), fmaf(f, m.w, u.w));
-      u = un;
-    }
-    if (p.dMT) {
-      const float4 d = reinterpret_cast<const float4*>(p.dMT + hd * (size_t)(K * V))[e4];
-      part = m.x * d.x + m.y * d.y + m.z * d.z + m.w * d.w;
-    }
-  }
-  // Row sum over the NJ threads of a row (consecutive lanes of one wave).
+    float m = p.M0 ? p.M0[hd * (size_t)N + el] : 0.f;
+    int s = 0;
+    for (; s + G <= nseg; s += G) {
+      float u[G], f[G];
 #pragma unroll
-  for (int o = NJ / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
-  if (live && e4 % NJ == 0) p.rs[hd * K + i] = part;
-  if (live) {
-    float4 h = p.dMT ? reinterpret_cast<const float4*>(p.dMT + hd * (size_t)(K * V))[e4] : make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 u = Gs[(size_t)(nseg - 1) * N4 + e4];
-    for (int s = nseg - 1; s >= 0; --s) {
-      const float4 un = s > 0 ? Gs[(size_t)(s - 1) * N4 + e4] : u;
-      const float f = F[(size_t)s * K];
-      Gs[(size_t)s * N4 + e4] = h;
-      h = make_float4(fmaf(f, h.x, u.x), fmaf(f, h.y, u.y), fmaf(f, h.z, u.z), fmaf(f, h.w, u.w));
-      u = un;
+      for (int r = 0; r < G; ++r) {
+        u[r] = Ms[(size_t)(s + r) * N + el];
+        f[r] = F[(size_t)(s + r) * K];
+      }
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        Ms[(size_t)(s + r) * N + el] = m;
+        m = fmaf(f[r], m, u[r]);
+      }
     }
-    reinterpret_cast<float4*>(p.dM0 + hd * (size_t)(K * V))[e4] = h;
+    for (; s < nseg; ++s) {
+      const float u = Ms[(size_t)s * N + el];
+      Ms[(size_t)s * N + el] = m;
+      m = fmaf(F[(size_t)s * K], m, u);
+    }
+    if (p.dMT) part = m * p.dMT[hd * (size_t)N + el];
+  }
+  // Row sum over the V threads of a row (consecutive lanes of one wave).
+#pragma unroll
+  for (int o = V / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+  if (live && el % V == 0) p.rs[hd * K + i] = part;
+  if (live) {
+    float h = p.dMT ? p.dMT[hd * (size_t)N + el] : 0.f;
+    int s = nseg - 1;
+    for (; s - G + 1 >= 0; s -= G) {
+      float u[G], f[G];
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        u[r] = Gs[(size_t)(s - r) * N + el];
+        f[r] = F[(size_t)(s - r) * K];
+      }
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        Gs[(size_t)(s - r) * N + el] = h;
+        h = fmaf(f[r], h, u[r]);
+      }
+    }
+    for (; s >= 0; --s) {
+      const float u = Gs[(size_t)s * N + el];
+      Gs[(size_t)s * N + el] = h;
+      h = fmaf(F[(size_t)s * K], h, u);
+    }
+    p.dM0[hd * (size_t)N + el] = h;
   }
 }
 
@@ -260,10 +332,12 @@ __global__ __launch_bounds__(256) void kla_bwd_segscan_kernel(BwdParams p) {
 // chunks take the exact elementwise path, with every D(l, m) from its own
 // exp2.
 // ---------------------------------------------------------------------------
-template <int K, int V>
+template <int K, int V, bool BF16>
 struct BwdChunkSmem {
-  static constexpr int KP = K + 1, VP = V + 1;
-  float lb[kSL * KP], g[kSL * KP], q[kSL * KP], v[kSL * VP], d[kSL * VP];
+  using SV = typename VRow<V, BF16>::T;
+  static constexpr int KP = K + 1, VP = VRow<V, BF16>::P;
+  float lb[kSL * KP], g[kSL * KP], q[kSL * KP];
+  SV v[kSL * VP], d[kSL * VP];
   float al[(kSL - kC) * KP];  // g_t prod_{u=t+1}^{c0-1} f_u for tokens before the chunk
   float E[kC * KP];           // exp2(lb_l - lb_7)
   float F[kC * KP];           // exp2(lb_7 - lb_l)
@@ -275,10 +349,10 @@ struct BwdChunkSmem {
 
 template <int K, int V, bool BF16>
 __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams p) {
-  constexpr int KP = K + 1, VP = V + 1, NT = kChunkThreads, C = kC;
+  constexpr int KP = K + 1, VP = VRow<V, BF16>::P, NT = kChunkThreads, C = kC;
   constexpr int KB = K / 16, VB = V / 16;
   static_assert(NT == 2 * C * C && NT == 512, "eight waves; one score pair per thread of the first four");
-  __shared__ BwdChunkSmem<K, V> s;
+  __shared__ BwdChunkSmem<K, V, BF16> s;
   const size_t hd = blockIdx.x / p.nseg;
   const int seg = blockIdx.x % p.nseg;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
@@ -341,7 +415,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
           v4f a, b;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            a[e] = s.v[(kb + 4 * lg + e) * VP + jb * 16 + lr];
+            a[e] = to_f32(s.v[(kb + 4 * lg + e) * VP + jb * 16 + lr]);
             b[e] = s.al[(kb + 4 * lg + e) * KP + i];
           }
           Mt[jb] = mma_f32(Mt[jb], a, b);
@@ -356,8 +430,8 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
         v4f a, b;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a[e] = s.d[(c0 + lr) * VP + jb * 16 + 4 * lg + e];
-          b[e] = s.v[(c0 + lr) * VP + jb * 16 + 4 * lg + e];
+          a[e] = to_f32(s.d[(c0 + lr) * VP + jb * 16 + 4 * lg + e]);
+          b[e] = to_f32(s.v[(c0 + lr) * VP + jb * 16 + 4 * lg + e]);
         }
         acc = mma_f32(acc, a, b);
       }
@@ -405,8 +479,8 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
         v4f a, b;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a[e] = s.d[(c0 + lr) * VP + jb * 16 + 4 * lg + e];
-          b[e] = s.v[(c0 + lr) * VP + jb * 16 + 4 * lg + e];
+          a[e] = to_f32(s.d[(c0 + lr) * VP + jb * 16 + 4 * lg + e]);
+          b[e] = to_f32(s.v[(c0 + lr) * VP + jb * 16 + 4 * lg + e]);
         }
         xs = mma_f32(xs, a, Mt[jb]);
         ys = mma_f32(ys, b, Ht[jb]);
@@ -475,7 +549,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           a[e] = s.A[(4 * lg + e) * C + lr];  // tril(A)^T[m = lr][l]
-          b[e] = s.d[(c0 + 4 * lg + e) * VP + j];
+          b[e] = to_f32(s.d[(c0 + 4 * lg + e) * VP + j]);
         }
         dv = mma_f32(dv, a, b);
       }
@@ -496,7 +570,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
           for (int e = 0; e < 4; ++e) {
             Hc[ib][e] *= s.cp[(C - 1) * KP + ib * 16 + 4 * lg + e];
             a[e] = s.cp[(4 * lg + e) * KP + ib * 16 + lr] * s.q[(c0 + 4 * lg + e) * KP + ib * 16 + lr];
-            b[e] = s.d[(c0 + 4 * lg + e) * VP + vb_w * 16 + lr];
+            b[e] = to_f32(s.d[(c0 + 4 * lg + e) * VP + vb_w * 16 + lr]);
           }
           Hc[ib] = mma_f32(Hc[ib], a, b);
         }
@@ -510,7 +584,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             Ht[jb][e] *= ce;
-            a[e] = s.d[(c0 + 4 * lg + e) * VP + jb * 16 + lr];
+            a[e] = to_f32(s.d[(c0 + 4 * lg + e) * VP + jb * 16 + lr]);
             b[e] = s.cp[(4 * lg + e) * KP + i] * s.q[(c0 + 4 * lg + e) * KP + i];
           }
           Ht[jb] = mma_f32(Ht[jb], a, b);
@@ -532,7 +606,8 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
 // ---------------------------------------------------------------------------
 namespace {
 struct ChainTok {
-  float lam, lprev, a2, D, lpred, k, vp, dg, e;
+  float lam, lprev, a2, D, k, vp, dg, e;
+  float ilam, iD, ilprev;  // hardware reciprocals (about 1 ulp)
 };
 
 template <bool BF16>
@@ -544,7 +619,9 @@ __device__ __forceinline__ ChainTok chain_tok(const BwdParams& p, size_t hd, lon
   const float a = __expf(ldin<BF16>(p.ld, x));
   c.a2 = a * a;
   c.D = fmaf(ldin<BF16>(p.pn, x), c.lprev, c.a2);
-  c.lpred = c.lprev / c.D;
+  c.ilam = fast_rcp(c.lam);
+  c.iD = fast_rcp(c.D);
+  c.ilprev = fast_rcp(c.lprev);
   c.k = ldin<BF16>(p.k, x);
   c.vp = ldin<BF16>(p.vp, x);
   c.dg = p.dgw[x];
@@ -565,10 +642,10 @@ __global__ __launch_bounds__(256) void kla_bwd_chain_comp_kernel(BwdParams p, in
   float E = 0.f, Pm = 1.f, Qa = 0.f, R = 0.f;
   auto step = [&](int t) {
     const ChainTok c = chain_tok<BF16>(p, hd, ch, t, K, i);
-    const float g = c.k * c.vp / c.lam;
-    const float m = c.a2 / (c.D * c.D);
-    const float c1 = c.k * c.k * c.vp / (c.lam * c.lpred);
-    const float c0 = -g * c.dg / c.lam;
+    const float g = c.k * c.vp * c.ilam;
+    const float m = c.a2 * c.iD * c.iD;
+    const float c1 = c.k * c.k * c.vp * c.ilam * c.D * c.ilprev;  // c / (lam lam^-), lam^- = lprev / D
+    const float c0 = -g * c.dg * c.ilam;
     E += c.e;
     Pm *= m;
     Qa = m * (Qa + c1);
@@ -609,18 +686,19 @@ __global__ __launch_bounds__(256) void kla_bwd_chain_out_kernel(BwdParams p, int
   float acc = in.x, L = in.y;
   auto step = [&](int t) {
     const ChainTok c = chain_tok<BF16>(p, hd, ch, t, K, i);
-    const float g = c.k * c.vp / c.lam;
-    const float c0 = -g * c.dg / c.lam;
-    acc += c.e;                                             // d log f_t
-    const float dc = L - acc / c.lam + c0;                  // dL/dlambda_t = dL/dc_t
-    const float Llp = fmaf(c.k * c.k * c.vp / (c.lam * c.lpred), acc, L + c0);  // dL/dlambda^-_t
-    const float w = -Llp * c.lprev / (c.D * c.D);           // dL/d(a^2)
+    const float g = c.k * c.vp * c.ilam;
+    const float c0 = -g * c.dg * c.ilam;
+    acc += c.e;                                                   // d log f_t
+    const float dc = fmaf(-acc, c.ilam, L + c0);                  // dL/dlambda_t = dL/dc_t
+    const float c1 = c.k * c.k * c.vp * c.ilam * c.D * c.ilprev;  // c / (lam lam^-)
+    const float Llp = fmaf(c1, acc, L + c0);                      // dL/dlambda^-_t
+    const float w = -Llp * c.lprev * c.iD * c.iD;                 // dL/d(a^2)
     const size_t x = (hd * p.T + t) * K + i;
-    stout<BF16>(p.dld, x, fmaf(2.f * c.a2, w, acc));        // a dL/da = d log f + 2 a^2 dL/d(a^2)
+    stout<BF16>(p.dld, x, fmaf(2.f * c.a2, w, acc));              // a dL/da = d log f + 2 a^2 dL/d(a^2)
     stout<BF16>(p.dpn, x, w * c.lprev);
-    stout<BF16>(p.dk, x, c.vp / c.lam * c.dg + 2.f * c.k * c.vp * dc);
-    stout<BF16>(p.dvp, x, c.k / c.lam * c.dg + c.k * c.k * dc);
-    L = Llp * (c.a2 / (c.D * c.D));
+    stout<BF16>(p.dk, x, c.vp * c.ilam * c.dg + 2.f * c.k * c.vp * dc);
+    stout<BF16>(p.dvp, x, c.k * c.ilam * c.dg + c.k * c.k * dc);
+    L = Llp * (c.a2 * c.iD * c.iD);
   };
   if (te - tb == kSL) {
 #pragma unroll 8
@@ -644,7 +722,7 @@ template <int K, int V, bool BF16>
 static hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   const unsigned nsb = (unsigned)((long long)p.nheads * p.nseg);
   hipLaunchKernelGGL((kla_bwd_segagg_kernel<K, V, BF16>), dim3(nsb), dim3(512), 0, stream, p);
-  constexpr int NB = (K * V / 4 + 255) / 256;
+  constexpr int NB = (K * V + 255) / 256;
   hipLaunchKernelGGL((kla_bwd_segscan_kernel<K, V>), dim3((unsigned)(p.nheads * NB)), dim3(256), 0, stream, p);
   hipLaunchKernelGGL((kla_bwd_chunk_kernel<K, V, BF16>), dim3(nsb), dim3(kChunkThreads), 0, stream, p);
   const int ncb = (int)((p.nchains + 255) / 256);

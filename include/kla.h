@@ -182,9 +182,10 @@ size_t kla_backward_workspace_bytes(int B, int H, int T, int dk, int dv);
  * then not accessed and may be NULL.
  *
  * Supported: dk, dv in {16, 32, 64} (128: KLA_ERR_UNSUPPORTED); B, H >= 1;
- * T >= 0; B*H*T*max(dk,dv) < 2^31.  Alignment: lambda_path and the float32
- * vectors 4 bytes, M0, grad_M_T and grad_M0 16 bytes, dtype arrays their
- * element size.  The workspace holds no flags, so it needs no initialisation.
+ * T >= 0; B*H*T*max(dk,dv) < 2^31.  Alignment: the per-token arrays (inputs,
+ * lambda_path, grad_y and the per-token gradients) and M0, grad_M_T, grad_M0
+ * 16 bytes; lambda0, grad_lambda_T, grad_lambda0 4 bytes.  The workspace holds
+ * no flags, so it needs no initialisation.
  * Arithmetic: float32 throughout; dtype outputs are rounded once at the end
  * (bf16: nearest even).  Results are deterministic (fixed summation order).
  */

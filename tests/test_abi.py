@@ -146,7 +146,9 @@ def bwd(K, **over):
     (dict(grad_M0=None), INVALID), (dict(B=0), INVALID), (dict(T=-1), INVALID),
     (dict(dk=128), UNSUPPORTED), (dict(dv=128), UNSUPPORTED), (dict(dk=48), UNSUPPORTED),
     (dict(dtype=2), UNSUPPORTED),
-    (dict(q=A + 1), INVALID), (dict(lambda_path=A + 2), INVALID), (dict(grad_M0=A + 4), INVALID),
+    (dict(q=A + 1), INVALID), (dict(q=A + 8), INVALID), (dict(lambda_path=A + 4), INVALID),
+    (dict(grad_y=A + 8), INVALID), (dict(grad_q=A + 8), INVALID),
+    (dict(grad_M0=A + 4), INVALID),
     (dict(M0=A + 8), INVALID), (dict(grad_M_T=A + 4), INVALID), (dict(grad_lambda_T=A + 2), INVALID),
     (dict(grad_k=A + 2, dtype=0), INVALID),
     (dict(workspace=None), WORKSPACE), (dict(workspace=A + 16), WORKSPACE),
