@@ -87,6 +87,15 @@ __device__ __forceinline__ void gate1(float lam, float lprev, float ld, float pn
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Four consecutive staged v / dy values of one row (8-byte aligned for bf16
+// rows, whose stride is a multiple of 4 elements): one 8-byte LDS read for bf16.
+__device__ __forceinline__ v4f row4(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return v4f{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+             __uint_as_float(u.y & 0xffff0000u)};
+}
+__device__ __forceinline__ v4f row4(const float* p) { return v4f{p[0], p[1], p[2], p[3]}; }
+
 // v and dy are kept in their input type (bf16 bits are exact); the row
 // stride of those arrays, in elements: bf16 rows padded by 4 elements, so that
 // the four 4-row groups of a matrix-core operand read fall on distinct banks.
@@ -106,7 +115,7 @@ template <int V, bool BF16> struct VRow {
 template <int K, int V, bool BF16, int NT>
 __device__ __forceinline__ void stage_segment(const BwdParams& p, size_t hd, int t0, float* slb, float* sg,
                                               float* sq, typename VRow<V, BF16>::T* sv,
-                                              typename VRow<V, BF16>::T* sd, float* sT) {
+                                              typename VRow<V, BF16>::T* sd, float* sT, int* unsafe) {
   using In = typename std::conditional<BF16, uint16_t, float>::type;
   constexpr int KP = K + 1, VP = VRow<V, BF16>::P, K4 = K / 4, V4 = V / 4;
   static_assert((kSL * K4) % NT == 0 || NT % (kSL * K4) == 0, "staging passes");
@@ -167,16 +176,21 @@ __device__ __forceinline__ void stage_segment(const BwdParams& p, size_t hd, int
     }
   }
   __syncthreads();
-// One thread per (channel, chunk): cumulative log2 f inside the chunk.
+// One thread per (channel, chunk): cumulative log2 f inside the chunk.  A
+  // chunk is marked in `unsafe` (when given) if a channel's log2 decay over
+  // either half of it falls below -96.
   for (int x = threadIdx.x; x < 4 * K; x += NT) {
     const int c = x / K, i = x % K;
-    float acc = 0.f;
+    float acc = 0.f, mid = 0.f;
 #pragma unroll
     for (int l = 0; l < kC; ++l) {
       acc += slb[(c * kC + l) * KP + i];
       slb[(c * kC + l) * KP + i] = acc;
+      if (l == 7) mid = acc;
     }
     sT[c * K + i] = acc;
+    const float first = slb[c * kC * KP + i];
+    if (unsafe && (first - mid > 96.f || mid - acc > 96.f)) unsafe[c] = 1;  // benign race: all write 1
   }
   __syncthreads();
 }
@@ -194,7 +208,7 @@ __global__ __launch_bounds__(512) void kla_bwd_segagg_kernel(BwdParams p) {
   const size_t hd = blockIdx.x / p.nseg;
   const int s = blockIdx.x % p.nseg;
   const int tid = threadIdx.x;
-  stage_segment<K, V, BF16, NT>(p, hd, s * kSL, sl, sa, sb, sv, sd, sT);
+  stage_segment<K, V, BF16, NT>(p, hd, s * kSL, sl, sa, sb, sv, sd, sT, nullptr);
   // alpha_t = g_t prod_{u>t} f_u (in place of g), beta_t = q_t prod_{u<=t} f_u
   // (in place of q), for t in chunk c: the products are exp2 of the chunk's
   // partial sums plus the totals of the later / earlier chunks.
@@ -338,13 +352,17 @@ struct BwdChunkSmem {
   static constexpr int KP = K + 1, VP = VRow<V, BF16>::P;
   float lb[kSL * KP], g[kSL * KP], q[kSL * KP];
   SV v[kSL * VP], d[kSL * VP];
-  float al[(kSL - kC) * KP];  // g_t prod_{u=t+1}^{c0-1} f_u for tokens before the chunk
   float E[kC * KP];           // exp2(lb_l - lb_7)
   float F[kC * KP];           // exp2(lb_7 - lb_l)
   float cp[kC * KP];          // prod_{u<=l} f_u inside the chunk
   float sx[kC * KP];          // prod_{u>l} f_u inside the chunk
+  float qE[kC * KP];          // q_l E_l
+  float gF[kC * KP];          // g_l F_l
+  float kd[kC * KP];          // g_l sx_l (write gate decayed to the chunk end)
+  float be[kC * KP];          // q_l cp_l (query decayed from the chunk start)
   float A[kC * kC], B[kC * kC];  // A[l][m] = q_l . (g_m decayed to l); B[l][m] = dy_l . v_m (m <= l; 0 above)
   float T[4 * K];             // sum of log2 f over each chunk of the segment
+  int unsafe[4];              // chunk needs the exact in-chunk path
 };
 
 template <int K, int V, bool BF16>
@@ -377,29 +395,29 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
       Ht[jb][e] = kw ? Gg[(kb_w * 16 + lr) * V + jb * 16 + 4 * lg + e] : 0.f;
       Ms[jb][e] = kw ? Mg[(kb_w * 16 + lr) * V + jb * 16 + 4 * lg + e] : 0.f;
     }
-  stage_segment<K, V, BF16, NT>(p, hd, t0, s.lb, s.g, s.q, s.v, s.d, s.T);
+  if (tid < 4) s.unsafe[tid] = 0;
+  stage_segment<K, V, BF16, NT>(p, hd, t0, s.lb, s.g, s.q, s.v, s.d, s.T, s.unsafe);
 
   for (int w = (nvalid - 1) / C; w >= 0; --w) {
     const int c0 = w * C;
-    // (a) elementwise decays of this chunk, and of the tokens before it.
-    int unsafe = 0;
+    // (a) elementwise decays of this chunk.
     for (int x = tid; x < C * K; x += NT) {
       const int l = x / K, i = x % K;
       const float lb = s.lb[(c0 + l) * KP + i], lb7 = s.lb[(c0 + 7) * KP + i];
       const float tot = s.T[w * K + i];
-      s.E[l * KP + i] = ex2(lb - lb7);
-      s.F[l * KP + i] = ex2(lb7 - lb);
-      s.cp[l * KP + i] = ex2(lb);
-      s.sx[l * KP + i] = ex2(tot - lb);
-      if (l == 0) unsafe |= (s.lb[c0 * KP + i] - lb7 > 96.f) | (lb7 - s.lb[(c0 + C - 1) * KP + i] > 96.f);
+      const float E = ex2(lb - lb7), F = ex2(lb7 - lb), cp = ex2(lb), sx = ex2(tot - lb);
+      const float q = s.q[(c0 + l) * KP + i], g = s.g[(c0 + l) * KP + i];
+      s.E[l * KP + i] = E;
+      s.F[l * KP + i] = F;
+      s.cp[l * KP + i] = cp;
+      s.sx[l * KP + i] = sx;
+      s.qE[l * KP + i] = q * E;
+      s.gF[l * KP + i] = g * F;
+      s.kd[l * KP + i] = g * sx;
+      s.be[l * KP + i] = q * cp;
     }
-    for (int x = tid; x < c0 * K; x += NT) {
-      const int t = x / K, i = x % K, c2 = t / C;
-      float mid = 0.f;
-      for (int c3 = c2 + 1; c3 < w; ++c3) mid += s.T[c3 * K + i];
-      s.al[t * KP + i] = s.g[t * KP + i] * ex2((s.T[c2 * K + i] - s.lb[t * KP + i]) + mid);
-    }
-    const bool safe = __syncthreads_or(unsafe) == 0;
+    const bool safe = s.unsafe[w] == 0;
+    __syncthreads();
     // (b) M_c^T tiles: the segment state decayed to the chunk start plus the
     // tokens before the chunk (v^T al over t < c0); the two score matrices.
     if (kw) {
@@ -408,16 +426,26 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
       for (int c3 = 0; c3 < w; ++c3) lP += s.T[c3 * K + i];
       const float Pi = ex2(lP);
 #pragma unroll
-      for (int jb = 0; jb < VB; ++jb) {
+      for (int jb = 0; jb < VB; ++jb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) Mt[jb][e] = Pi * Ms[jb][e];
-        for (int kb = 0; kb < c0; kb += 16) {
-          v4f a, b;
+      // Tokens t of an earlier chunk c2 enter with g_t prod_{u=t+1}^{c0-1} f_u
+      // = g_t exp2((T[c2] - lb_t) + sum of the chunk totals in between).
+      for (int c2 = 0; c2 < w; ++c2) {
+        float off = s.T[c2 * K + i];
+        for (int c3 = c2 + 1; c3 < w; ++c3) off += s.T[c3 * K + i];
+        v4f b;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            a[e] = to_f32(s.v[(kb + 4 * lg + e) * VP + jb * 16 + lr]);
-            b[e] = s.al[(kb + 4 * lg + e) * KP + i];
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int t = c2 * C + 4 * lg + e;
+          b[e] = s.g[t * KP + i] * ex2(off - s.lb[t * KP + i]);
+        }
+        // one 16-token block of this chunk: four k-groups of 4 (e), tiles jb interleaved
+#pragma unroll
+        for (int jb = 0; jb < VB; ++jb) {
+          v4f a;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] = to_f32(s.v[(c2 * C + 4 * lg + e) * VP + jb * 16 + lr]);
           Mt[jb] = mma_f32(Mt[jb], a, b);
         }
       }
@@ -427,12 +455,8 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
       v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int jb = 0; jb < VB; ++jb) {
-        v4f a, b;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = to_f32(s.d[(c0 + lr) * VP + jb * 16 + 4 * lg + e]);
-          b[e] = to_f32(s.v[(c0 + lr) * VP + jb * 16 + 4 * lg + e]);
-        }
+        const v4f a = row4(&s.d[(c0 + lr) * VP + jb * 16 + 4 * lg]);
+        const v4f b = row4(&s.v[(c0 + lr) * VP + jb * 16 + 4 * lg]);
         acc = mma_f32(acc, a, b);
       }
 #pragma unroll
@@ -448,8 +472,8 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = kb + 4 * lg + e;
-            a[e] = s.q[(c0 + lr) * KP + i] * s.E[lr * KP + i];
-            b[e] = s.g[(c0 + lr) * KP + i] * s.F[lr * KP + i];
+            a[e] = s.qE[lr * KP + i];
+            b[e] = s.gF[lr * KP + i];
           }
           acc = mma_f32(acc, a, b);
         }
@@ -476,12 +500,8 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
       v4f xs = v4f{0.f, 0.f, 0.f, 0.f}, ys = xs, dqi = xs, dgi = xs;
 #pragma unroll
       for (int jb = 0; jb < VB; ++jb) {
-        v4f a, b;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = to_f32(s.d[(c0 + lr) * VP + jb * 16 + 4 * lg + e]);
-          b[e] = to_f32(s.v[(c0 + lr) * VP + jb * 16 + 4 * lg + e]);
-        }
+        const v4f a = row4(&s.d[(c0 + lr) * VP + jb * 16 + 4 * lg]);
+        const v4f b = row4(&s.v[(c0 + lr) * VP + jb * 16 + 4 * lg]);
         xs = mma_f32(xs, a, Mt[jb]);
         ys = mma_f32(ys, b, Ht[jb]);
       }
@@ -491,9 +511,9 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
         for (int e = 0; e < 4; ++e) {
           const int n = 4 * lg + e;
           a[e] = s.B[lr * C + n];  // tril(B)[l = lr][m = n]
-          b[e] = s.g[(c0 + n) * KP + i] * s.F[n * KP + i];
+          b[e] = s.gF[n * KP + i];
           c[e] = s.B[n * C + lr];  // tril(B)^T[l = lr][n]
-          d[e] = s.q[(c0 + n) * KP + i] * s.E[n * KP + i];
+          d[e] = s.qE[n * KP + i];
         }
         dqi = mma_f32(dqi, a, b);
         dgi = mma_f32(dgi, c, d);
@@ -540,7 +560,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = ib * 16 + 4 * lg + e;
-          a[e] = s.g[(c0 + lr) * KP + i] * s.sx[lr * KP + i];
+          a[e] = s.kd[lr * KP + i];
         }
         dv = mma_f32(dv, a, Hc[ib]);
       }
@@ -569,7 +589,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             Hc[ib][e] *= s.cp[(C - 1) * KP + ib * 16 + 4 * lg + e];
-            a[e] = s.cp[(4 * lg + e) * KP + ib * 16 + lr] * s.q[(c0 + 4 * lg + e) * KP + ib * 16 + lr];
+            a[e] = s.be[(4 * lg + e) * KP + ib * 16 + lr];
             b[e] = to_f32(s.d[(c0 + 4 * lg + e) * VP + vb_w * 16 + lr]);
           }
           Hc[ib] = mma_f32(Hc[ib], a, b);
@@ -585,7 +605,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
           for (int e = 0; e < 4; ++e) {
             Ht[jb][e] *= ce;
             a[e] = to_f32(s.d[(c0 + 4 * lg + e) * VP + jb * 16 + lr]);
-            b[e] = s.cp[(4 * lg + e) * KP + i] * s.q[(c0 + 4 * lg + e) * KP + i];
+            b[e] = s.be[(4 * lg + e) * KP + i];
           }
           Ht[jb] = mma_f32(Ht[jb], a, b);
         }
