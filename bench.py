@@ -138,7 +138,14 @@ def cpu_baseline(x):
 
 
 CONFIGS = ("lm45m_bf16", "lm180m_bf16", "long_bf16", "chains_f32", "decode_lm45m_bf16", "decode_b256_bf16",
-           "bwd_lm45m_bf16")
+           "bwd_lm45m_bf16", "ou_lm45m_bf16")
+
+
+def ou_algorithmic_bytes(B, H, T, dk, dv, esz):
+    """The forward's bytes with the OU prior in continuous time: per token q,
+    k, dt, val_prec (d_k each) and v read, y written; per (h, i) theta and
+    sigma2; per head the fp32 state in and out."""
+    return B * H * T * ((4 * dk + dv) * esz + dv * esz) + H * dk * 8 + B * H * (dk + dk * dv) * 4 * 2
 
 
 def backward_algorithmic_bytes(B, H, T, dk, dv, esz):
@@ -221,6 +228,23 @@ def run_configs(only, copies):
             x = xs = ys = run = None
             torch.cuda.empty_cache()
             continue
+        elif w.kind == "forward_ou":
+            B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+            esz = 2 if w.dtype == "bf16" else 4
+            abytes = ou_algorithmic_bytes(B, H, T, dk, dv, esz)
+            ncopy = max(1, min(copies, int(1.2e9 // abytes)))
+            xs = [KI.make_ou_inputs_torch(w, seed=w.seed + c, device=dev) for c in range(ncopy)]
+            outs = [(torch.empty((B, H, T, dv), dtype=xs[0]["q"].dtype, device=dev),
+                     torch.empty((B, H, dk), dtype=torch.float32, device=dev),
+                     torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)) for _ in range(ncopy)]
+            ws = K.Workspace(dev)
+            calls, warm = 20, 5
+
+            def run(i):
+                xc = xs[i % ncopy]
+                return K.forward_ou(xc["q"], xc["k"], xc["v"], xc["dt"], xc["theta"], xc["sigma2"], xc["val_prec"],
+                                    xc["lambda0"], xc["M0"], workspace=ws, out=outs[i % ncopy])
+            units, unit = B * H * T, "tokens/s"
         elif w.kind == "backward":
             # One kla_backward call over the whole batch (all six kernels), on
             # rotating input copies; each copy's precision path comes from one

@@ -20,9 +20,9 @@ import threading
 
 __all__ = [
     "LIB_PATH", "lib", "KLA_F32", "KLA_BF16", "KlaError",
-    "kla_forward_workspace_bytes", "kla_forward", "kla_precision_scan_workspace_bytes",
+    "kla_forward_workspace_bytes", "kla_forward", "kla_forward_ou", "kla_precision_scan_workspace_bytes",
     "kla_precision_scan", "kla_decode_step", "kla_backward_workspace_bytes", "kla_backward",
-    "kla_workspace_init", "kla_workspace_error", "kla_status_string", "forward", "precision_scan",
+    "kla_workspace_init", "kla_workspace_error", "kla_status_string", "forward", "forward_ou", "precision_scan",
     "decode_step", "backward", "scan", "Workspace",
 ]
 
@@ -38,6 +38,8 @@ lib.kla_forward_workspace_bytes.restype = _sz
 lib.kla_forward_workspace_bytes.argtypes = [_i] * 5
 lib.kla_forward.restype = _i
 lib.kla_forward.argtypes = [_vp] * 6 + [_fp] * 2 + [_vp] + [_fp] * 3 + [_i] * 6 + [_vp, _sz, _vp]
+lib.kla_forward_ou.restype = _i
+lib.kla_forward_ou.argtypes = [_vp] * 4 + [_fp] * 2 + [_vp] + [_fp] * 2 + [_vp] + [_fp] * 3 + [_i] * 6 + [_vp, _sz, _vp]
 lib.kla_precision_scan_workspace_bytes.restype = _sz
 lib.kla_precision_scan_workspace_bytes.argtypes = [_i] * 4
 lib.kla_precision_scan.restype = _i
@@ -72,6 +74,12 @@ def kla_forward(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0, y, lambda
     return int(lib.kla_forward(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0, y, lambda_T,
                                M_T, lambda_path, B, H, T, dk, dv, dtype, workspace, workspace_bytes,
                                stream))
+
+
+def kla_forward_ou(q, k, v, dt, theta, sigma2, val_prec, lambda0, M0, y, lambda_T, M_T, lambda_path,
+                   B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream) -> int:
+    return int(lib.kla_forward_ou(q, k, v, dt, theta, sigma2, val_prec, lambda0, M0, y, lambda_T, M_T,
+                                  lambda_path, B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream))
 
 
 def kla_precision_scan_workspace_bytes(B, H, T, D) -> int:
@@ -226,6 +234,49 @@ def forward(q, k, v, log_decay, proc_noise, val_prec, lambda0=None, M0=None,
     rc = kla_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(proc_noise), _ptr(val_prec),
                      _ptr(lambda0), _ptr(M0), _ptr(y), _ptr(lam_T), _ptr(M_T), _ptr(lpath),
                      B, H, T, dk, dv, code, ws.data_ptr(), ws.numel(), stream)
+    if rc:
+        raise KlaError(rc)
+    return (y, lam_T, M_T, lpath) if return_lambda_path else (y, lam_T, M_T)
+
+
+def forward_ou(q, k, v, dt, theta, sigma2, val_prec, lambda0=None, M0=None, return_lambda_path=False,
+               workspace: Workspace | None = None, out=None):
+    """KLA forward pass with the OU prior in continuous time, on the current stream.
+
+    q, k, dt, val_prec: [B,H,T,dk]; v: [B,H,T,dv] (all bfloat16 or all
+    float32); theta, sigma2: float32 [H,dk], the OU rate and diffusion; the
+    kernel forms log_decay = -theta dt and proc_noise = sigma2 (1 - e^{-2 theta
+    dt}) / (2 theta).  Everything else as ``forward``.
+    """
+    torch = _torch()
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    dtype, dev = k.dtype, k.device
+    code = _dtype_code(dtype)
+    for name, t, shp in (("q", q, (B, H, T, dk)), ("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)),
+                         ("dt", dt, (B, H, T, dk)), ("val_prec", val_prec, (B, H, T, dk))):
+        _check(t, name, shp, dtype, dev)
+    _check(theta, "theta", (H, dk), torch.float32, dev)
+    _check(sigma2, "sigma2", (H, dk), torch.float32, dev)
+    if lambda0 is not None:
+        _check(lambda0, "lambda0", (B, H, dk), torch.float32, dev)
+    if M0 is not None:
+        _check(M0, "M0", (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        y = torch.empty((B, H, T, dv), dtype=dtype, device=dev)
+        lam_T = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+        M_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        y, lam_T, M_T = out
+    lpath = torch.empty((B, H, T, dk), dtype=torch.float32, device=dev) if return_lambda_path else None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    need = kla_forward_workspace_bytes(B, H, T, dk, dv)
+    if need == 0:
+        raise KlaError(2)
+    ws = (workspace or _default_workspace(dev, stream, "forward")).get(need, stream)
+    rc = kla_forward_ou(_ptr(q), _ptr(k), _ptr(v), _ptr(dt), _ptr(theta), _ptr(sigma2), _ptr(val_prec),
+                        _ptr(lambda0), _ptr(M0), _ptr(y), _ptr(lam_T), _ptr(M_T), _ptr(lpath),
+                        B, H, T, dk, dv, code, ws.data_ptr(), ws.numel(), stream)
     if rc:
         raise KlaError(rc)
     return (y, lam_T, M_T, lpath) if return_lambda_path else (y, lam_T, M_T)

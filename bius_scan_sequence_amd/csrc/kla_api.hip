@@ -205,21 +205,28 @@ extern "C" size_t kla_forward_workspace_bytes(int B, int H, int T, int dk, int d
   return fwd_layout(B, H, T, dk, dv, nseg > nseg_b ? nseg : nseg_b).total;
 }
 
-extern "C" int kla_forward(const void* q, const void* k, const void* v, const void* log_decay,
-                           const void* proc_noise, const void* val_prec, const float* lambda0,
-                           const float* M0, void* y, float* lambda_T, float* M_T, float* lambda_path,
-                           int B, int H, int T, int dk, int dv, int dtype, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+namespace kla {
+namespace {
+// kla_forward and kla_forward_ou: with theta == NULL, log_decay and
+// proc_noise are per-token inputs; otherwise `log_decay` holds the OU step
+// length and theta, sigma2 ([H][dk]) the rate and diffusion.
+int forward_impl(const char* name, const void* q, const void* k, const void* v, const void* log_decay,
+                 const void* proc_noise, const float* theta, const float* sigma2, const void* val_prec,
+                 const float* lambda0, const float* M0, void* y, float* lambda_T, float* M_T, float* lambda_path,
+                 int B, int H, int T, int dk, int dv, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
   if (B < 1 || H < 1 || T < 0) return KLA_ERR_INVALID_ARG;
   if (!lambda_T || !M_T) return KLA_ERR_INVALID_ARG;
+  const bool ou = theta != nullptr;
   // With T = 0 the per-token arrays are empty and never touched (may be null).
-  if (T > 0 && (!q || !k || !v || !log_decay || !proc_noise || !val_prec || !y))
+  if (T > 0 && (!q || !k || !v || !log_decay || (!ou && !proc_noise) || !val_prec || !y))
     return KLA_ERR_INVALID_ARG;
+  if (ou && (!sigma2 || !aligned(theta, 4) || !aligned(sigma2, 4))) return KLA_ERR_INVALID_ARG;
   if (dtype != KLA_F32 && dtype != KLA_BF16) return KLA_ERR_UNSUPPORTED;
   if (!supported_width(dk) || !supported_width(dv)) return KLA_ERR_UNSUPPORTED;
   if (!fwd_shape_ok(B, H, T, dk, dv)) return KLA_ERR_INVALID_ARG;
   const size_t esz = dtype == KLA_BF16 ? 2 : 4;
-  const void* ins[6] = {q, k, v, log_decay, proc_noise, val_prec};
+  const void* ins[6] = {q, k, v, log_decay, ou ? q : proc_noise, val_prec};
   for (const void* p : ins)
     if (!aligned(p, 16)) return KLA_ERR_INVALID_ARG;
   if (!aligned(y, esz) || !aligned(lambda_T, 4) || !aligned(M_T, 4)) return KLA_ERR_INVALID_ARG;
@@ -234,16 +241,17 @@ extern "C" int kla_forward(const void* q, const void* k, const void* v, const vo
   const long long nheads = (long long)B * H;
   if (T == 0) {
     hipError_t e = launch_state_copy(lambda0, M0, lambda_T, M_T, nheads * dk, nheads * dk * dv, st);
-    return e == hipSuccess ? KLA_OK : hip_fail(e, "kla_forward (T = 0 state copy)");
+    return e == hipSuccess ? KLA_OK : hip_fail(e, name);
   }
   const bool bf16 = dtype == KLA_BF16;
   const int nseg = fwd_nseg(T, dk, dv, bf16);
   const FwdLayout l = fwd_layout(B, H, T, dk, dv, nseg);
   char* ws = static_cast<char*>(workspace);
   FwdParams p;
-  p.q = q; p.k = k; p.v = v; p.ld = log_decay; p.pn = proc_noise; p.vp = val_prec;
+  p.q = q; p.k = k; p.v = v; p.ld = log_decay; p.pn = ou ? nullptr : proc_noise; p.vp = val_prec;
   p.lam0 = lambda0; p.M0 = M0; p.y = y; p.lamT = lambda_T; p.MT = M_T; p.lpath = lambda_path;
-  p.nheads = (int)nheads; p.T = T; p.nseg = nseg;
+  p.theta = theta; p.sigma2 = ou ? sigma2 : nullptr;
+  p.nheads = (int)nheads; p.T = T; p.nseg = nseg; p.H = H;
   p.ctrl = reinterpret_cast<unsigned*>(ws);
   p.hdone = reinterpret_cast<unsigned*>(ws + l.hdone);
   p.pflag = reinterpret_cast<unsigned*>(ws + l.pflag);
@@ -254,7 +262,27 @@ extern "C" int kla_forward(const void* q, const void* k, const void* v, const vo
   p.magg = reinterpret_cast<float*>(ws + l.magg);
   p.minc = reinterpret_cast<float*>(ws + l.minc);
   hipError_t e = launch_forward(p, dk, dv, bf16, st);
-  return e == hipSuccess ? KLA_OK : hip_fail(e, "kla_forward");
+  return e == hipSuccess ? KLA_OK : hip_fail(e, name);
+}
+}  // namespace
+}  // namespace kla
+
+extern "C" int kla_forward(const void* q, const void* k, const void* v, const void* log_decay,
+                           const void* proc_noise, const void* val_prec, const float* lambda0,
+                           const float* M0, void* y, float* lambda_T, float* M_T, float* lambda_path,
+                           int B, int H, int T, int dk, int dv, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return forward_impl("kla_forward", q, k, v, log_decay, proc_noise, nullptr, nullptr, val_prec, lambda0, M0, y,
+                      lambda_T, M_T, lambda_path, B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" int kla_forward_ou(const void* q, const void* k, const void* v, const void* dt, const float* theta,
+                              const float* sigma2, const void* val_prec, const float* lambda0, const float* M0,
+                              void* y, float* lambda_T, float* M_T, float* lambda_path, int B, int H, int T,
+                              int dk, int dv, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!theta) return KLA_ERR_INVALID_ARG;
+  return forward_impl("kla_forward_ou", q, k, v, dt, nullptr, theta, sigma2, val_prec, lambda0, M0, y, lambda_T,
+                      M_T, lambda_path, B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream);
 }
 
 extern "C" size_t kla_precision_scan_workspace_bytes(int B, int H, int T, int D) {

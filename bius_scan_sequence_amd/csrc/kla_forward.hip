@@ -220,6 +220,53 @@ __device__ __forceinline__ void load_vals(const float* p, float (&o)[CPT]) {
   for (int k = 0; k < CPT; ++k) o[k] = p[k];
 }
 
+// Exact discretisation of an OU step of length dt with rate theta and
+// diffusion sigma2 ([KLA-nl] §1, "Dynamics Prior": the prior is an exactly
+// discretised OU process): x_t = e^{-theta dt} x_{t-1} + w with
+// Var w = sigma2 (1 - e^{-2 theta dt}) / (2 theta) = sigma2 dt phi(2 theta dt),
+// phi(u) = (1 - e^{-u}) / u (phi -> 1 as theta -> 0, the Brownian step).
+// For |u| > 0.5, phi = (1 - a^2) / u with a = e^{-theta dt}, the decay the
+// walk forms anyway (the cancellation in 1 - a^2 costs well under 1e-6
+// relative there); below, the series sum_{n<=7} (-u)^n / (n+1)! (error
+// below u^8/9!, about 1e-8).
+__device__ __forceinline__ void ou_coef(float th, float s2, float dt, float& ld, float& pn) {
+  const float x = th * dt;
+  ld = -x;
+  const float u = 2.f * x;
+  float phi;
+  if (fabsf(u) > 0.5f) {
+    const float a = __expf(ld);
+    phi = (1.f - a * a) * fast_rcp(u);
+  } else {
+    float s = -1.f / 40320.f;                 // (-1)^7 / 8!
+    s = fmaf(u, s, 1.f / 5040.f);
+    s = fmaf(u, s, -1.f / 720.f);
+    s = fmaf(u, s, 1.f / 120.f);
+    s = fmaf(u, s, -1.f / 24.f);
+    s = fmaf(u, s, 1.f / 6.f);
+    s = fmaf(u, s, -0.5f);
+    phi = fmaf(u, s, 1.f);
+  }
+  pn = s2 * dt * phi;
+}
+
+// log_decay and proc_noise of CPT channels of one token: read from the staged
+// tiles, or (OU inputs) formed from the staged step length and the channels'
+// theta and sigma2.
+template <bool OU, int CPT, typename In>
+__device__ __forceinline__ void coef_vals(const In* rld, const In* rpn, const float (&th)[CPT],
+                                          const float (&s2)[CPT], float (&ldv)[CPT], float (&pnv)[CPT]) {
+  if constexpr (OU) {
+    float dt[CPT];
+    load_vals<CPT>(rld, dt);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) ou_coef(th[k], s2[k], dt[k], ldv[k], pnv[k]);
+  } else {
+    load_vals<CPT>(rld, ldv);
+    load_vals<CPT>(rpn, pnv);
+  }
+}
+
 // CPT consecutive stored values starting at slot j of a 4-value block (see put1).
 template <bool BF16, int CPT>
 __device__ __forceinline__ void put_vals(unsigned char* block, int j, const float (&x)[CPT]) {
@@ -248,7 +295,7 @@ constexpr int fwd_waves_per_eu() {
   return (sizeof(FwdSmem<DK, DV, BF16>) <= 80 * 1024 ? 2 : 1) * FwdCfg<DK, DV, BF16>::NW / 4;
 }
 
-template <int DK, int DV, bool BF16>
+template <int DK, int DV, bool BF16, bool OU>
 __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, DV, BF16>())) void kla_fwd_kernel(FwdParams p) {
   using C = FwdCfg<DK, DV, BF16>;
   using In = typename C::In;
@@ -288,8 +335,8 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   load_tile<In, L, DK, NT>(bq, static_cast<const In*>(p.q) + offk, nvalid, tid);
   load_tile<In, L, DV, NT>(bv, static_cast<const In*>(p.v) + offv, nvalid, tid);
   stage_tile<In, L, DK, NT>(rk, static_cast<const In*>(p.k) + offk, nvalid, tid);
-  stage_tile<In, L, DK, NT>(rld, static_cast<const In*>(p.ld) + offk, nvalid, tid);
-  stage_tile<In, L, DK, NT>(rpn, static_cast<const In*>(p.pn) + offk, nvalid, tid);
+  stage_tile<In, L, DK, NT>(rld, static_cast<const In*>(p.ld) + offk, nvalid, tid);  // OU: the step length
+  if constexpr (!OU) stage_tile<In, L, DK, NT>(rpn, static_cast<const In*>(p.pn) + offk, nvalid, tid);
   stage_tile<In, L, DK, NT>(rvp, static_cast<const In*>(p.vp) + offk, nvalid, tid);
   __syncthreads();
   const unsigned epoch = (unsigned)s.ctl[1];
@@ -309,6 +356,20 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   const int wc = wave & 3, wh = lane >> 5;
   const int wch = (wave >> 2) * 32 * CPT + (lane & 31) * CPT, wt0 = wc * 16 + wh * 8;
   const bool walker = wc < NCH && wch < DK;
+  // OU inputs: the walker's channels' rate and diffusion (unused otherwise).
+  float th[CPT], s2[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    th[k] = 0.f;
+    s2[k] = 0.f;
+    if constexpr (OU) {
+      if (walker) {
+        const size_t hc = (size_t)(head % p.H) * DK + wch + k;
+        th[k] = p.theta[hc];
+        s2[k] = p.sigma2[hc];
+      }
+    }
+  }
   constexpr int KT = C::KEEP ? 8 : 1;
   float ca[KT][CPT], cpn[KT][CPT], cc2[KT][CPT], ckv[KT][CPT];  // a, pbar, c, k*Lambda^v
   Mob Pg[CPT];
@@ -321,8 +382,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
       float kk[CPT], vpv[CPT], ldv[CPT], pnv[CPT];
       load_vals<CPT>(rk + x, kk);
       load_vals<CPT>(rvp + x, vpv);
-      load_vals<CPT>(rld + x, ldv);
-      load_vals<CPT>(rpn + x, pnv);
+      coef_vals<OU, CPT>(rld + x, rpn + x, th, s2, ldv, pnv);
 #pragma unroll
       for (int k = 0; k < CPT; ++k) {
         const float kv = kk[k] * vpv[k];
@@ -467,8 +527,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
         float kk[CPT], vpv[CPT], ldv[CPT];
         load_vals<CPT>(rk + x, kk);
         load_vals<CPT>(rvp + x, vpv);
-        load_vals<CPT>(rld + x, ldv);
-        load_vals<CPT>(rpn + x, pnv);
+        coef_vals<OU, CPT>(rld + x, rpn + x, th, s2, ldv, pnv);
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
           kv[k] = kk[k] * vpv[k];
@@ -598,6 +657,11 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
     float f[16], g[16], q[16];
     const bool chan = tid < DK;
     if (chan) {
+      float th1 = 0.f, s21 = 0.f;
+      if constexpr (OU) {
+        th1 = p.theta[(size_t)(head % p.H) * DK + tid];
+        s21 = p.sigma2[(size_t)(head % p.H) * DK + tid];
+      }
       float lam = s.lamc[cc * DK + tid];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -607,7 +671,11 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
           const size_t gx = ((size_t)head * T + t0 + t) * DK + tid;
           kk = to_f32(static_cast<const In*>(p.k)[gx]);
           ldv = to_f32(static_cast<const In*>(p.ld)[gx]);
-          pnv = to_f32(static_cast<const In*>(p.pn)[gx]);
+          if constexpr (OU) {
+            ou_coef(th1, s21, ldv, ldv, pnv);
+          } else {
+            pnv = to_f32(static_cast<const In*>(p.pn)[gx]);
+          }
           vpv = to_f32(static_cast<const In*>(p.vp)[gx]);
           qv = to_f32(static_cast<const In*>(p.q)[gx]);
         }
@@ -913,7 +981,10 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
 template <int DK, int DV, bool BF16>
 static hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   const unsigned nblocks = (unsigned)p.nheads * (unsigned)p.nseg;
-  hipLaunchKernelGGL((kla_fwd_kernel<DK, DV, BF16>), dim3(nblocks), dim3(FwdCfg<DK, DV, BF16>::NT), 0, stream, p);
+  if (p.theta)
+    hipLaunchKernelGGL((kla_fwd_kernel<DK, DV, BF16, true>), dim3(nblocks), dim3(FwdCfg<DK, DV, BF16>::NT), 0, stream, p);
+  else
+    hipLaunchKernelGGL((kla_fwd_kernel<DK, DV, BF16, false>), dim3(nblocks), dim3(FwdCfg<DK, DV, BF16>::NT), 0, stream, p);
   return hipGetLastError();
 }
 

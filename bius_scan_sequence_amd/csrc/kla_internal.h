@@ -22,7 +22,10 @@ struct FwdParams {
   float* lamT;
   float* MT;
   float* lpath;       // nullable
+  const float* theta;   // OU inputs only ([H][dk] rate; ld then holds the step length), else null
+  const float* sigma2;  // OU inputs only ([H][dk] diffusion)
   int nheads, T, nseg;
+  int H;              // heads per batch row (indexes theta / sigma2)
   unsigned* ctrl;     // workspace control words
   unsigned* hdone;    // [nheads] segments of the head done with their flags
   unsigned* pflag;    // [nheads*nseg][2] precision-carry flags, one per carry wave

@@ -42,9 +42,10 @@
  *     by kla_workspace_init() before its first use and not touched by the
  *     caller afterwards.  Calls that share one workspace must be ordered on one
  *     stream; concurrent calls on one workspace race.  A workspace serves one
- *     entry point only: the entry points keep different flags and counters
- *     in it, so a buffer used by kla_forward must not be passed to
- *     kla_precision_scan or kla_backward, and so on.
+ *     entry point only (kla_forward and kla_forward_ou count as one): the
+ *     entry points keep different flags and counters in it, so a buffer used
+ *     by kla_forward must not be passed to kla_precision_scan or
+ *     kla_backward, and so on.
  */
 #ifndef KLA_H_
 #define KLA_H_
@@ -100,6 +101,31 @@ int kla_forward(const void* q, const void* k, const void* v,
                 void* y, float* lambda_T, float* M_T, float* lambda_path,
                 int B, int H, int T, int dk, int dv, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * KLA forward pass with the OU prior given in continuous time: the same scan
+ * as kla_forward, with log_decay and proc_noise formed inside the kernel by the
+ * exact discretisation of an Ornstein-Uhlenbeck step ([KLA-nl] §1, "Dynamics
+ * Prior": the prior is an exactly discretised OU process):
+ *   a_t   = exp(-theta dt_t)                        (log_decay = -theta dt_t)
+ *   pbar_t = sigma2 (1 - exp(-2 theta dt_t)) / (2 theta)   (-> sigma2 dt_t as theta -> 0)
+ * per (b,h,t,i), with theta and sigma2 per (h,i).  One per-token coefficient
+ * stream (dt) replaces two (log_decay, proc_noise).
+ *
+ * Inputs: q, k, val_prec [B,H,T,dk] and v [B,H,T,dv] as kla_forward;
+ *   dt     [B,H,T,dk] dtype, the step length of each token and channel (>= 0);
+ *   theta  [H,dk]     float32, OU rate (mean reversion), shared over the batch;
+ *   sigma2 [H,dk]     float32, OU diffusion (variance per unit time, >= 0).
+ * State, outputs, workspace (kla_forward_workspace_bytes; the layout is
+ * kla_forward's, so one workspace may serve both), supported shapes and
+ * errors: as kla_forward.  theta and sigma2 need 4-byte alignment.
+ */
+int kla_forward_ou(const void* q, const void* k, const void* v, const void* dt,
+                   const float* theta, const float* sigma2, const void* val_prec,
+                   const float* lambda0, const float* M0,
+                   void* y, float* lambda_T, float* M_T, float* lambda_path,
+                   int B, int H, int T, int dk, int dv, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace kla_precision_scan needs; 0 if the shape is invalid. */
 size_t kla_precision_scan_workspace_bytes(int B, int H, int T, int D);

@@ -44,7 +44,7 @@ __all__ = [
 class Workload:
     index: int
     name: str
-    kind: str            # "forward", "precision", "decode" (one token per head) or "backward"
+    kind: str            # "forward", "forward_ou", "precision", "decode" (one token per head) or "backward"
     B: int
     H: int
     T: int
@@ -74,6 +74,7 @@ WORKLOADS = (
     Workload(5, "decode_lm45m_bf16", "decode", 8, 8, 1, 64, 64, "bf16"),
     Workload(6, "decode_b256_bf16", "decode", 256, 8, 1, 64, 64, "bf16"),
     Workload(7, "bwd_lm45m_bf16", "backward", 8, 8, 2048, 64, 64, "bf16"),
+    Workload(8, "ou_lm45m_bf16", "forward_ou", 8, 8, 2048, 64, 64, "bf16"),
 )
 
 
@@ -280,3 +281,76 @@ def make_backward_grads_torch(w: Workload | int | str, *, seed=None, device="cud
     g.manual_seed(seed * 16 + 7)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     return torch.randn((w.B, w.H, w.T, w.dv), generator=g, device=device, dtype=torch.float32).to(tdt)
+
+
+def make_ou_inputs(w: Workload | int | str, *, B=None, H=None, T=None, dk=None, dv=None, seed=None,
+                   dtype=None) -> dict:
+    """Seeded inputs of the forward pass with the OU prior in continuous time.
+
+    q, k ~ N(0, 1/d_k), v ~ N(0, 1), val_prec = softplus(N(0, 1)) + 1e-3 as in
+    the forward recipe; the step length dt = softplus(N(0, 1)) per (b,h,t,i);
+    the OU rate theta = exp(N(0, 0.25^2)) and diffusion sigma2 =
+    softplus(N(0, 1)) + 1e-3 per (h,i), float32.  With theta near 1 the
+    per-token log decays -theta dt have the scale of the forward recipe's
+    -softplus(N(0, 1)).  Per-token arrays are float32
+    numpy arrays (bf16-rounded for bf16); lambda0 = 1, M0 = 0.  Streams: those
+    of make_forward_inputs, with the log_decay stream drawing dt and the
+    proc_noise stream drawing (theta, sigma2).
+    """
+    if not isinstance(w, Workload):
+        w = workload(w)
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    T = w.T if T is None else T
+    dk = w.dk if dk is None else dk
+    dv = w.dv if dv is None else dv
+    seed = w.seed if seed is None else seed
+    dtype = w.dtype if dtype is None else dtype
+    rq, rk, rv, rd, rp, rl, _ = _streams(seed)
+    sk = (B, H, T, dk)
+    arrs = {"q": rq.standard_normal(sk) / np.sqrt(dk), "k": rk.standard_normal(sk) / np.sqrt(dk),
+            "v": rv.standard_normal((B, H, T, dv)), "dt": softplus(rd.standard_normal(sk)),
+            "val_prec": softplus(rl.standard_normal(sk)) + 1e-3}
+    par = rp.standard_normal((2, H, dk))
+    out = {}
+    for name, arr in arrs.items():
+        a32 = arr.astype(np.float32)
+        out[name] = round_bf16(a32) if dtype == "bf16" else a32
+    out["theta"] = np.exp(0.25 * par[0]).astype(np.float32)
+    out["sigma2"] = (softplus(par[1]) + 1e-3).astype(np.float32)
+    out["lambda0"] = np.ones((B, H, dk), np.float32)
+    out["M0"] = np.zeros((B, H, dk, dv), np.float32)
+    out["dtype"] = dtype
+    out["seed"] = seed
+    return out
+
+
+def make_ou_inputs_torch(w: Workload | int | str, *, seed=None, device="cuda"):
+    """Device-side version of make_ou_inputs at the workload's full shape
+    (torch's generator; values differ from the host version)."""
+    import torch
+    if not isinstance(w, Workload):
+        w = workload(w)
+    seed = w.seed if seed is None else seed
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    gens = []
+    for i in range(6):
+        g = torch.Generator(device=device)
+        g.manual_seed(seed * 16 + i)
+        gens.append(g)
+    sp = torch.nn.functional.softplus
+    rn = lambda shape, g: torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    sk = (B, H, T, dk)
+    return {
+        "q": (rn(sk, gens[0]) / dk ** 0.5).to(tdt),
+        "k": (rn(sk, gens[1]) / dk ** 0.5).to(tdt),
+        "v": rn((B, H, T, dv), gens[2]).to(tdt),
+        "dt": sp(rn(sk, gens[3])).to(tdt),
+        "theta": torch.exp(0.25 * rn((H, dk), gens[4])),
+        "sigma2": sp(rn((H, dk), gens[4])) + 1e-3,
+        "val_prec": (sp(rn(sk, gens[5])) + 1e-3).to(tdt),
+        "lambda0": torch.ones((B, H, dk), dtype=torch.float32, device=device),
+        "M0": torch.zeros((B, H, dk, dv), dtype=torch.float32, device=device),
+        "dtype": w.dtype, "seed": seed,
+    }

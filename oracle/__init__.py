@@ -17,3 +17,4 @@ from .kla_f64 import (  # noqa: F401
     write_gate,
     readout,
 )
+from .kla_ou_f64 import ou_discretize_f64, kla_forward_ou_f64  # noqa: F401,E402

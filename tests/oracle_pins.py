@@ -469,11 +469,58 @@ def pin_backward_prior_precision_identity(seed=19):
     np.testing.assert_allclose(g["d_lambda0"], want, rtol=1e-12, atol=1e-15)
 
 
+def pin_ou_semigroup(seed=21):
+    """OU transitions compose: a step of dt1 followed by one of dt2 is a step
+    of dt1 + dt2, i.e. a(dt1 + dt2) = a(dt1) a(dt2) and
+    pbar(dt1 + dt2) = a(dt2)^2 pbar(dt1) + pbar(dt2) (the first step's noise
+    decays through the second)."""
+    import oracle.kla_ou_f64 as OU
+    rng = np.random.default_rng(seed)
+    th = rng.uniform(0.0, 3.0, 200)
+    s2 = rng.uniform(0.1, 2.0, 200)
+    d1, d2 = rng.uniform(0.0, 2.0, 200), rng.uniform(0.0, 2.0, 200)
+    l1, p1 = OU.ou_discretize_f64(th, s2, d1)
+    l2, p2 = OU.ou_discretize_f64(th, s2, d2)
+    l12, p12 = OU.ou_discretize_f64(th, s2, d1 + d2)
+    np.testing.assert_allclose(l12, l1 + l2, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(p12, np.exp(2 * l2) * p1 + p2, rtol=1e-12)
+
+
+def pin_ou_transition_variance_quadrature(seed=22):
+    """The step noise equals integral_0^dt sigma2 e^{-2 theta s} ds, evaluated
+    by adaptive quadrature (scipy), and the decay equals e^{-theta dt}."""
+    from scipy.integrate import quad
+    import oracle.kla_ou_f64 as OU
+    rng = np.random.default_rng(seed)
+    for _ in range(20):
+        th, s2, dt = rng.uniform(0.0, 4.0), rng.uniform(0.1, 3.0), rng.uniform(0.0, 3.0)
+        want, _ = quad(lambda x: s2 * np.exp(-2.0 * th * x), 0.0, dt, epsabs=1e-14, epsrel=1e-13)
+        ld, pn = OU.ou_discretize_f64(th, s2, dt)
+        np.testing.assert_allclose(pn, want, rtol=1e-11, atol=1e-14)
+        np.testing.assert_allclose(np.exp(ld), np.exp(-th * dt), rtol=1e-15)
+
+
+def pin_ou_limits():
+    """Brownian limit: theta = 0 gives a = 1 and pbar = sigma2 dt (and theta
+    -> 0 approaches it); long steps reach the stationary variance
+    sigma2 / (2 theta) with a -> 0."""
+    import oracle.kla_ou_f64 as OU
+    s2, dt = 1.7, 0.9
+    ld, pn = OU.ou_discretize_f64(0.0, s2, dt)
+    assert ld == 0.0 and abs(pn - s2 * dt) < 1e-15
+    ld, pn = OU.ou_discretize_f64(1e-9, s2, dt)
+    np.testing.assert_allclose(pn, s2 * dt, rtol=1e-8)
+    ld, pn = OU.ou_discretize_f64(0.8, s2, 60.0)
+    np.testing.assert_allclose(pn, s2 / (2 * 0.8), rtol=1e-14)
+    assert np.exp(ld) < 1e-20
+
+
 ALL_PINS = [
     pin_covariance_form, pin_dense_gaussian, pin_mobius_exact, pin_mobius_mpmath,
     pin_steady_state_dare, pin_no_observation, pin_no_process_noise, pin_least_squares,
     pin_zero_value_precision, pin_invariants, pin_state_carry,
     pin_precision_scan_matches_forward, pin_decode_covariance_form, pin_decode_chain_is_dense_posterior,
     pin_backward_finite_differences, pin_backward_forward_is_the_oracle,
-    pin_backward_prior_precision_identity,
+    pin_backward_prior_precision_identity, pin_ou_semigroup, pin_ou_transition_variance_quadrature,
+    pin_ou_limits,
 ]

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("kla_forward", "kla_forward_workspace_bytes", "kla_precision_scan",
+    for n in ("kla_forward", "kla_forward_ou", "kla_forward_workspace_bytes", "kla_precision_scan",
               "kla_precision_scan_workspace_bytes", "kla_decode_step", "kla_backward",
               "kla_backward_workspace_bytes", "kla_workspace_init",
               "kla_workspace_error", "kla_status_string"):
@@ -157,3 +157,21 @@ def bwd(K, **over):
 ])
 def test_backward_rejects(K, over, code):
     assert bwd(K, **over) == code
+
+
+def fwd_ou(K, **over):
+    args = dict(q=A, k=A, v=A, dt=A, theta=A, sigma2=A, val_prec=A, lambda0=None, M0=None,
+                y=A, lambda_T=A, M_T=A, lambda_path=None, B=1, H=1, T=64, dk=16, dv=16, dtype=1,
+                workspace=A, workspace_bytes=1 << 30, stream=None)
+    args.update(over)
+    return K.kla_forward_ou(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(theta=None), INVALID), (dict(sigma2=None), INVALID), (dict(dt=None), INVALID),
+    (dict(q=None), INVALID), (dict(theta=A + 2), INVALID), (dict(sigma2=A + 1), INVALID),
+    (dict(dt=A + 8), INVALID), (dict(dk=48), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED),
+    (dict(workspace_bytes=16), WORKSPACE), (dict(B=0), INVALID),
+])
+def test_forward_ou_rejects(K, over, code):
+    assert fwd_ou(K, **over) == code

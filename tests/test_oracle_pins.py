@@ -35,6 +35,40 @@ MUTANTS = {
 }
 
 
+# Plausible mistakes in the OU discretisation (oracle/kla_ou_f64.py).
+def _ou_no_factor_two(theta, sigma2, dt):
+    th, s2, d = (np.asarray(x, np.float64) for x in (theta, sigma2, dt))
+    return -th * d, s2 * (-np.expm1(-th * d)) / np.where(th == 0, 1.0, th)
+
+
+def _ou_euler(theta, sigma2, dt):
+    th, s2, d = (np.asarray(x, np.float64) for x in (theta, sigma2, dt))
+    return -th * d, s2 * d
+
+
+def _ou_variance_squared_decay(theta, sigma2, dt):
+    th, s2, d = (np.asarray(x, np.float64) for x in (theta, sigma2, dt))
+    return -th * d, s2 * (-np.expm1(-th * d)) / np.where(th == 0, 1.0, 2 * th)
+
+
+OU_MUTANTS = {"ou_drops_factor_two": _ou_no_factor_two, "ou_euler_noise": _ou_euler,
+              "ou_noise_uses_a_not_a2": _ou_variance_squared_decay}
+
+
+@pytest.mark.parametrize("name", sorted(OU_MUTANTS))
+def test_pins_catch_planted_ou_mistake(name, monkeypatch):
+    import oracle.kla_ou_f64 as OU
+    monkeypatch.setattr(OU, "ou_discretize_f64", OU_MUTANTS[name])
+    failed = []
+    for pin in P.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except Exception:
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {name}"
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name, monkeypatch):
     attr, fn = MUTANTS[name]
