@@ -138,7 +138,15 @@ def cpu_baseline(x):
 
 
 CONFIGS = ("lm45m_bf16", "lm180m_bf16", "long_bf16", "chains_f32", "decode_lm45m_bf16", "decode_b256_bf16",
-           "bwd_lm45m_bf16", "ou_lm45m_bf16")
+           "bwd_lm45m_bf16", "ou_lm45m_bf16", "vprec_lm45m_bf16")
+
+
+def vprec_algorithmic_bytes(B, H, T, dk, dv, esz):
+    """Bytes of the variant with the value precision per value channel: per
+    token q, k, log_decay, proc_noise (d_k each), v and val_prec (d_v each)
+    read and y (d_v) written; per head the fp32 d_k x d_v precision and mean
+    out (no state in)."""
+    return B * H * T * ((4 * dk + 3 * dv) * esz) + B * H * dk * dv * 4 * 2
 
 
 def ou_algorithmic_bytes(B, H, T, dk, dv, esz):
@@ -244,6 +252,22 @@ def run_configs(only, copies):
                 xc = xs[i % ncopy]
                 return K.forward_ou(xc["q"], xc["k"], xc["v"], xc["dt"], xc["theta"], xc["sigma2"], xc["val_prec"],
                                     xc["lambda0"], xc["M0"], workspace=ws, out=outs[i % ncopy])
+            units, unit = B * H * T, "tokens/s"
+        elif w.kind == "forward_vprec":
+            B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+            esz = 2 if w.dtype == "bf16" else 4
+            abytes = vprec_algorithmic_bytes(B, H, T, dk, dv, esz)
+            ncopy = max(1, min(copies, int(1.2e9 // abytes)))
+            xs = [KI.make_vprec_inputs_torch(w, seed=w.seed + c, device=dev) for c in range(ncopy)]
+            outs = [(torch.empty((B, H, T, dv), dtype=xs[0]["q"].dtype, device=dev),
+                     torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev),
+                     torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)) for _ in range(ncopy)]
+            ws = K.Workspace(dev)
+            calls, warm = 20, 5
+
+            def run(i):
+                xc = xs[i % ncopy]
+                return K.forward_vprec(*(xc[n] for n in NAMES), out=outs[i % ncopy])
             units, unit = B * H * T, "tokens/s"
         elif w.kind == "backward":
             # One kla_backward call over the whole batch (all six kernels), on

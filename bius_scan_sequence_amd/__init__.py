@@ -20,9 +20,10 @@ import threading
 
 __all__ = [
     "LIB_PATH", "lib", "KLA_F32", "KLA_BF16", "KlaError",
-    "kla_forward_workspace_bytes", "kla_forward", "kla_forward_ou", "kla_precision_scan_workspace_bytes",
+    "kla_forward_workspace_bytes", "kla_forward", "kla_forward_ou", "kla_forward_vprec",
+    "kla_precision_scan_workspace_bytes",
     "kla_precision_scan", "kla_decode_step", "kla_backward_workspace_bytes", "kla_backward",
-    "kla_workspace_init", "kla_workspace_error", "kla_status_string", "forward", "forward_ou", "precision_scan",
+    "kla_workspace_init", "kla_workspace_error", "kla_status_string", "forward", "forward_ou", "forward_vprec", "precision_scan",
     "decode_step", "backward", "scan", "Workspace",
 ]
 
@@ -40,6 +41,8 @@ lib.kla_forward.restype = _i
 lib.kla_forward.argtypes = [_vp] * 6 + [_fp] * 2 + [_vp] + [_fp] * 3 + [_i] * 6 + [_vp, _sz, _vp]
 lib.kla_forward_ou.restype = _i
 lib.kla_forward_ou.argtypes = [_vp] * 4 + [_fp] * 2 + [_vp] + [_fp] * 2 + [_vp] + [_fp] * 3 + [_i] * 6 + [_vp, _sz, _vp]
+lib.kla_forward_vprec.restype = _i
+lib.kla_forward_vprec.argtypes = [_vp] * 6 + [_fp] * 2 + [_vp] + [_fp] * 2 + [_i] * 6 + [_vp]
 lib.kla_precision_scan_workspace_bytes.restype = _sz
 lib.kla_precision_scan_workspace_bytes.argtypes = [_i] * 4
 lib.kla_precision_scan.restype = _i
@@ -80,6 +83,12 @@ def kla_forward_ou(q, k, v, dt, theta, sigma2, val_prec, lambda0, M0, y, lambda_
                    B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream) -> int:
     return int(lib.kla_forward_ou(q, k, v, dt, theta, sigma2, val_prec, lambda0, M0, y, lambda_T, M_T,
                                   lambda_path, B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream))
+
+
+def kla_forward_vprec(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0, y, lambda_T, M_T,
+                      B, H, T, dk, dv, dtype, stream) -> int:
+    return int(lib.kla_forward_vprec(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0, y, lambda_T, M_T,
+                                     B, H, T, dk, dv, dtype, stream))
 
 
 def kla_precision_scan_workspace_bytes(B, H, T, D) -> int:
@@ -280,6 +289,40 @@ def forward_ou(q, k, v, dt, theta, sigma2, val_prec, lambda0=None, M0=None, retu
     if rc:
         raise KlaError(rc)
     return (y, lam_T, M_T, lpath) if return_lambda_path else (y, lam_T, M_T)
+
+
+def forward_vprec(q, k, v, log_decay, proc_noise, val_prec, lambda0=None, M0=None, out=None):
+    """KLA with the value precision per value channel, on the current stream.
+
+    q, k, log_decay, proc_noise: [B,H,T,dk]; v, val_prec: [B,H,T,dv]; all
+    bfloat16 or all float32.  lambda0 and M0 are float32 [B,H,dk,dv] (None: 1
+    and 0).  Returns (y [B,H,T,dv] input dtype, lambda_T [B,H,dk,dv] f32,
+    M_T [B,H,dk,dv] f32); ``out`` may hold preallocated tensors for them.
+    """
+    torch = _torch()
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    dtype, dev = k.dtype, k.device
+    code = _dtype_code(dtype)
+    for name, t, shp in (("q", q, (B, H, T, dk)), ("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)),
+                         ("log_decay", log_decay, (B, H, T, dk)), ("proc_noise", proc_noise, (B, H, T, dk)),
+                         ("val_prec", val_prec, (B, H, T, dv))):
+        _check(t, name, shp, dtype, dev)
+    for name, t in (("lambda0", lambda0), ("M0", M0)):
+        if t is not None:
+            _check(t, name, (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        y = torch.empty((B, H, T, dv), dtype=dtype, device=dev)
+        lam_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        M_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        y, lam_T, M_T = out
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = kla_forward_vprec(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(proc_noise), _ptr(val_prec),
+                           _ptr(lambda0), _ptr(M0), _ptr(y), _ptr(lam_T), _ptr(M_T), B, H, T, dk, dv, code, stream)
+    if rc:
+        raise KlaError(rc)
+    return y, lam_T, M_T
 
 
 def precision_scan(log_decay, proc_noise, obs_prec, lambda0=None, workspace: Workspace | None = None,

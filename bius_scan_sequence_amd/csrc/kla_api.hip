@@ -285,6 +285,36 @@ extern "C" int kla_forward_ou(const void* q, const void* k, const void* v, const
                       M_T, lambda_path, B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream);
 }
 
+extern "C" int kla_forward_vprec(const void* q, const void* k, const void* v, const void* log_decay,
+                                 const void* proc_noise, const void* val_prec, const float* lambda0, const float* M0,
+                                 void* y, float* lambda_T, float* M_T, int B, int H, int T, int dk, int dv, int dtype,
+                                 void* stream) {
+  if (B < 1 || H < 1 || T < 0) return KLA_ERR_INVALID_ARG;
+  if (!lambda_T || !M_T) return KLA_ERR_INVALID_ARG;
+  if (T > 0 && (!q || !k || !v || !log_decay || !proc_noise || !val_prec || !y)) return KLA_ERR_INVALID_ARG;
+  if (dtype != KLA_F32 && dtype != KLA_BF16) return KLA_ERR_UNSUPPORTED;
+  if (!supported_width(dk) || !supported_width(dv)) return KLA_ERR_UNSUPPORTED;
+  if (!fwd_shape_ok(B, H, T, dk, dv)) return KLA_ERR_INVALID_ARG;
+  const size_t esz = dtype == KLA_BF16 ? 2 : 4;
+  const void* ins[7] = {q, k, v, log_decay, proc_noise, val_prec, y};
+  for (const void* x : ins)
+    if (x && !aligned(x, esz)) return KLA_ERR_INVALID_ARG;
+  const void* st4[4] = {lambda0, M0, lambda_T, M_T};
+  for (const void* x : st4)
+    if (x && !aligned(x, 4)) return KLA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const long long nheads = (long long)B * H;
+  if (T == 0) {
+    hipError_t e = launch_state_copy(lambda0, M0, lambda_T, M_T, nheads * dk * dv, nheads * dk * dv, st);
+    return e == hipSuccess ? KLA_OK : hip_fail(e, "kla_forward_vprec (T = 0 state copy)");
+  }
+  VprecParams p;
+  p.q = q; p.k = k; p.v = v; p.ld = log_decay; p.pn = proc_noise; p.vp = val_prec;
+  p.lam0 = lambda0; p.M0 = M0; p.y = y; p.lamT = lambda_T; p.MT = M_T; p.T = T;
+  hipError_t e = launch_vprec(p, nheads, dk, dv, dtype == KLA_BF16, st);
+  return e == hipSuccess ? KLA_OK : hip_fail(e, "kla_forward_vprec");
+}
+
 extern "C" size_t kla_precision_scan_workspace_bytes(int B, int H, int T, int D) {
   if (!pscan_shape_ok(B, H, T, D)) return 0;
   return pscan_plan(B, H, T, D).total;

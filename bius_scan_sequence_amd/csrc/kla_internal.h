@@ -100,6 +100,21 @@ struct BwdParams {
   float* cin;         // [nseg][nchains][2] reverse-chain state entering each block from the right
 };
 
+struct VprecParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* ld;     // log_decay
+  const void* pn;     // proc_noise
+  const void* vp;     // val_prec, [B,H,T,dv]
+  const float* lam0;  // nullable, [B,H,dk,dv]
+  const float* M0;    // nullable
+  void* y;
+  float* lamT;        // [B,H,dk,dv]
+  float* MT;
+  int T;
+};
+
 int fwd_segment_len(int dk, int dv, bool bf16);
 hipError_t launch_forward(const FwdParams& p, int dk, int dv, bool bf16, hipStream_t stream);
 hipError_t launch_pscan(const PscanParams& p, hipStream_t stream);
@@ -107,6 +122,7 @@ hipError_t launch_decode(const DecodeParams& p, long long nheads, int dk, int dv
 hipError_t launch_backward(const BwdParams& p, int dk, int dv, bool bf16, hipStream_t stream);
 hipError_t launch_backward_empty(const float* dlamT, const float* dMT, float* dlam0, float* dM0,
                                  long long nl, long long nm, hipStream_t stream);
+hipError_t launch_vprec(const VprecParams& p, long long nheads, int dk, int dv, bool bf16, hipStream_t stream);
 hipError_t launch_fill_zero(void* ptr, size_t words, hipStream_t stream);
 hipError_t launch_state_copy(const float* lam0, const float* M0, float* lamT, float* MT,
                              long long nl, long long nm, hipStream_t stream);

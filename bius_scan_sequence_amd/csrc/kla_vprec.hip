@@ -1,0 +1,202 @@
+// KLA with the value precision indexed by value channel: one scalar Kalman
+// filter per element (i, j), each with its own precision.
+//
+// Sources: gist.science summaries of arXiv 2602.10743, "Kalman Linear Attention";
+// [KLA-nl] = "Technische Samenvatting: Kalman Linear Attention (KLA)":
+//   §1 "Probabilistische Formulering"  observation model (here Lambda^v per value channel j);
+//                                      readout of the posterior mean
+//   §2 "Parallelisatie via Möbius-transformaties"  precision equation; affine mean recursion
+//   §3 "Niet-lineaire Gating vanuit Onzekerheid"   gates are precision ratios
+// Per element (i, j) of head (b, h), token t (a = exp(log_decay_{t,i}),
+// pbar = proc_noise_{t,i}, c_{t,ij} = k_{t,i}^2 Lambda^v_{t,j}):
+//   lam^- = lam / (a^2 + pbar lam),  lam' = lam^- + c,
+//   f = a lam^- / lam',  g = k_{t,i} Lambda^v_{t,j} / lam',
+//   M' = f M + g v_{t,j},  y_t[j] = sum_i q_{t,i} M'_{ij}.
+// The gates differ per element, so there is no chunked matrix form: the work
+// is elementwise (VALU), O(T d_k d_v).
+//
+// Decomposition.  One workgroup per (head, block of 8 value columns); thread
+// (ig, jj) owns key channels 4 ig .. 4 ig + 3 of column jj and walks the
+// sequence, four independent element chains per thread.  The precision is
+// kept projectively as lam = n / d (the Möbius form of [KLA-nl] §2):
+//   d' = pbar n + a^2 d,  n' = n + c d',
+// for which lam^- / lam' = n / n', so f = a n / n' and g = k Lambda^v d' / n'
+// take one reciprocal per element and token; (n, d) are rescaled by a power
+// of two every fourth token.  Tokens are staged in blocks: the per-(t, i)
+// coefficients (a, a^2, pbar, k, q) once per block in LDS, v and Lambda^v per
+// (t, j).  The readout's sum over key channels is deferred: each thread keeps
+// its four-channel partial per token in LDS, and after the block one thread
+// per (t, j) adds the d_k/4 partials in a fixed order (deterministic).
+#include <type_traits>
+
+#include "kla_device.h"
+#include "kla_internal.h"
+
+namespace kla {
+
+namespace {
+constexpr int kVR = 4;   // key channels per thread
+constexpr int kVJB = 8;  // value columns per workgroup
+
+template <int DK>
+constexpr int vprec_tb() { return DK >= 128 ? 16 : 32; }  // tokens per staged block
+
+template <int DK, int DV, bool BF16>
+struct alignas(16) VprecSmem {
+  static constexpr int TB = vprec_tb<DK>(), NI = DK / kVR;
+  float a[TB][DK], a2[TB][DK], pn[TB][DK], k[TB][DK], q[TB][DK];
+  float v[TB][kVJB], L[TB][kVJB];
+  float part[TB][kVJB][NI + 1];  // padded: the reduction walks NI consecutive words
+};
+}  // namespace
+
+template <int DK, int DV, bool BF16>
+__global__ __launch_bounds__(DK / kVR * kVJB) void kla_vprec_kernel(VprecParams p) {
+  using In = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr int NI = DK / kVR, NT = NI * kVJB, TB = vprec_tb<DK>(), NJB = DV / kVJB;
+  __shared__ VprecSmem<DK, DV, BF16> s;
+  const int tid = threadIdx.x;
+  const int ig = tid % NI, jj = tid / NI;
+  const size_t head = blockIdx.x / NJB;
+  const int j0 = (blockIdx.x % NJB) * kVJB;
+  const int j = j0 + jj;
+  const int T = p.T;
+  const In* q = static_cast<const In*>(p.q);
+  const In* k = static_cast<const In*>(p.k);
+  const In* ld = static_cast<const In*>(p.ld);
+  const In* pn = static_cast<const In*>(p.pn);
+  const In* v = static_cast<const In*>(p.v);
+  const In* vp = static_cast<const In*>(p.vp);
+
+  // Element state: precision n/d and mean, for channels 4 ig + r of column j.
+  float n[kVR], d[kVR], M[kVR];
+#pragma unroll
+  for (int r = 0; r < kVR; ++r) {
+    const size_t e = (head * DK + ig * kVR + r) * DV + j;
+    n[r] = p.lam0 ? p.lam0[e] : 1.f;
+    d[r] = 1.f;
+    M[r] = p.M0 ? p.M0[e] : 0.f;
+  }
+
+  for (int t0 = 0; t0 < T; t0 += TB) {
+    // Stage the block: per-(t, i) coefficients and per-(t, j) values.  Tokens
+    // past T are identity steps (a = 1, pbar = 0, k = 0).
+    for (int x = tid; x < TB * DK; x += NT) {
+      const int t = x / DK, i = x % DK;
+      float av = 1.f, pv = 0.f, kv = 0.f, qv = 0.f;
+      if (t0 + t < T) {
+        const size_t g = (head * T + t0 + t) * DK + i;
+        av = __expf(to_f32(ld[g]));
+        pv = to_f32(pn[g]);
+        kv = to_f32(k[g]);
+        qv = to_f32(q[g]);
+      }
+      s.a[t][i] = av;
+      s.a2[t][i] = av * av;
+      s.pn[t][i] = pv;
+      s.k[t][i] = kv;
+      s.q[t][i] = qv;
+    }
+    for (int x = tid; x < TB * kVJB; x += NT) {
+      const int t = x / kVJB, c = x % kVJB;
+      float vv = 0.f, lv = 0.f;
+      if (t0 + t < T) {
+        const size_t g = (head * T + t0 + t) * DV + j0 + c;
+        vv = to_f32(v[g]);
+        lv = to_f32(vp[g]);
+      }
+      s.v[t][c] = vv;
+      s.L[t][c] = lv;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int t = 0; t < TB; ++t) {
+      const float vj = s.v[t][jj], Lj = s.L[t][jj];
+      const float4 a4 = *reinterpret_cast<const float4*>(&s.a[t][ig * kVR]);
+      const float4 a24 = *reinterpret_cast<const float4*>(&s.a2[t][ig * kVR]);
+      const float4 p4 = *reinterpret_cast<const float4*>(&s.pn[t][ig * kVR]);
+      const float4 k4 = *reinterpret_cast<const float4*>(&s.k[t][ig * kVR]);
+      const float4 q4 = *reinterpret_cast<const float4*>(&s.q[t][ig * kVR]);
+      const float av[4] = {a4.x, a4.y, a4.z, a4.w}, a2v[4] = {a24.x, a24.y, a24.z, a24.w};
+      const float pv[4] = {p4.x, p4.y, p4.z, p4.w}, kv[4] = {k4.x, k4.y, k4.z, k4.w};
+      const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < kVR; ++r) {
+        const float kL = kv[r] * Lj;
+        const float c = kv[r] * kL;
+        const float dd = fmaf(pv[r], n[r], a2v[r] * d[r]);  // d' = pbar n + a^2 d
+        const float nn = fmaf(c, dd, n[r]);                 // n' = n + c d'
+        const float rr = fast_rcp(nn);
+        const float f = av[r] * n[r] * rr;                  // a lam^- / lam'
+        const float g = kL * dd * rr;                       // k Lambda^v / lam'
+        M[r] = fmaf(f, M[r], g * vj);
+        part = fmaf(qv[r], M[r], part);
+        n[r] = nn;
+        d[r] = dd;
+      }
+      if ((t & 3) == 3) {
+#pragma unroll
+        for (int r = 0; r < kVR; ++r) {
+          const int e = __builtin_amdgcn_frexp_expf(fmaxf(n[r], d[r]));
+          n[r] = __builtin_amdgcn_ldexpf(n[r], -e);
+          d[r] = __builtin_amdgcn_ldexpf(d[r], -e);
+        }
+      }
+      s.part[t][jj][ig] = part;
+    }
+    __syncthreads();
+    // y_t[j] = sum over the key-channel groups, in a fixed order.
+    for (int x = tid; x < TB * kVJB; x += NT) {
+      const int t = x / kVJB, c = x % kVJB;
+      if (t0 + t >= T) continue;
+      float y = 0.f;
+#pragma unroll
+      for (int g = 0; g < NI; ++g) y += s.part[t][c][g];
+      static_cast<In*>(p.y)[(head * T + t0 + t) * DV + j0 + c] = from_f32<In>(y);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int r = 0; r < kVR; ++r) {
+    const size_t e = (head * DK + ig * kVR + r) * DV + j;
+    p.lamT[e] = n[r] / d[r];
+    p.MT[e] = M[r];
+  }
+}
+
+template <int DK, int DV, bool BF16>
+static hipError_t launch_vp(const VprecParams& p, long long nheads, hipStream_t stream) {
+  constexpr int NT = DK / kVR * kVJB;
+  hipLaunchKernelGGL((kla_vprec_kernel<DK, DV, BF16>), dim3((unsigned)(nheads * (DV / kVJB))), dim3(NT), 0, stream,
+                     p);
+  return hipGetLastError();
+}
+
+template <int DK, bool BF16>
+static hipError_t vp_dv(const VprecParams& p, long long nheads, int dv, hipStream_t stream) {
+  switch (dv) {
+    case 16: return launch_vp<DK, 16, BF16>(p, nheads, stream);
+    case 32: return launch_vp<DK, 32, BF16>(p, nheads, stream);
+    case 64: return launch_vp<DK, 64, BF16>(p, nheads, stream);
+    case 128: return launch_vp<DK, 128, BF16>(p, nheads, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool BF16>
+static hipError_t vp_dk(const VprecParams& p, long long nheads, int dk, int dv, hipStream_t stream) {
+  switch (dk) {
+    case 16: return vp_dv<16, BF16>(p, nheads, dv, stream);
+    case 32: return vp_dv<32, BF16>(p, nheads, dv, stream);
+    case 64: return vp_dv<64, BF16>(p, nheads, dv, stream);
+    case 128: return vp_dv<128, BF16>(p, nheads, dv, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_vprec(const VprecParams& p, long long nheads, int dk, int dv, bool bf16, hipStream_t stream) {
+  return bf16 ? vp_dk<true>(p, nheads, dk, dv, stream) : vp_dk<false>(p, nheads, dk, dv, stream);
+}
+
+}  // namespace kla

@@ -127,6 +127,28 @@ int kla_forward_ou(const void* q, const void* k, const void* v, const void* dt,
                    int B, int H, int T, int dk, int dv, int dtype,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * KLA with the value precision indexed by value channel: val_prec is
+ * [B,H,T,dv] (Lambda^v_{t,j}) instead of [B,H,T,dk], so every element (i, j)
+ * is its own scalar filter with observation precision c = k_{t,i}^2
+ * Lambda^v_{t,j} ([KLA-nl] §1 "Observatiemodel" read with Lambda^v per value
+ * channel; predict/update of §2 and precision-ratio gates of §3 per element):
+ *   precision lam_{t,ij}, gates f_{t,ij}, g_{t,ij}, mean M_{t,ij},
+ *   y_t[j] = sum_i q_{t,i} M_{t,ij}.
+ * Inputs: q, k, log_decay, proc_noise [B,H,T,dk]; v, val_prec [B,H,T,dv]
+ * (dtype); state in lambda0, M0 [B,H,dk,dv] float32, nullable (1 and 0).
+ * Outputs: y [B,H,T,dv] dtype; lambda_T, M_T [B,H,dk,dv] float32.  T = 0
+ * copies the state in to the state out.  No workspace: one kernel walks the
+ * sequence per element.  Supported: dk, dv in {16, 32, 64, 128};
+ * B*H*T*max(dk,dv) < 2^31.  Alignment: element size (float32 arrays 4 bytes).
+ * Arithmetic: float32; the readout sums over key channels in a fixed order.
+ */
+int kla_forward_vprec(const void* q, const void* k, const void* v,
+                      const void* log_decay, const void* proc_noise, const void* val_prec,
+                      const float* lambda0, const float* M0,
+                      void* y, float* lambda_T, float* M_T,
+                      int B, int H, int T, int dk, int dv, int dtype, void* stream);
+
 /* Bytes of workspace kla_precision_scan needs; 0 if the shape is invalid. */
 size_t kla_precision_scan_workspace_bytes(int B, int H, int T, int D);
 

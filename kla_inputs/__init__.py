@@ -44,7 +44,7 @@ __all__ = [
 class Workload:
     index: int
     name: str
-    kind: str            # "forward", "forward_ou", "precision", "decode" (one token per head) or "backward"
+    kind: str            # "forward", "forward_ou", "forward_vprec", "precision", "decode" or "backward"
     B: int
     H: int
     T: int
@@ -75,6 +75,7 @@ WORKLOADS = (
     Workload(6, "decode_b256_bf16", "decode", 256, 8, 1, 64, 64, "bf16"),
     Workload(7, "bwd_lm45m_bf16", "backward", 8, 8, 2048, 64, 64, "bf16"),
     Workload(8, "ou_lm45m_bf16", "forward_ou", 8, 8, 2048, 64, 64, "bf16"),
+    Workload(9, "vprec_lm45m_bf16", "forward_vprec", 8, 8, 2048, 64, 64, "bf16"),
 )
 
 
@@ -354,3 +355,38 @@ def make_ou_inputs_torch(w: Workload | int | str, *, seed=None, device="cuda"):
         "M0": torch.zeros((B, H, dk, dv), dtype=torch.float32, device=device),
         "dtype": w.dtype, "seed": seed,
     }
+
+
+def make_vprec_inputs(w: Workload | int | str, *, B=None, H=None, T=None, dk=None, dv=None, seed=None,
+                      dtype=None) -> dict:
+    """Seeded inputs of the variant with the value precision per value
+    channel: the forward recipe, except val_prec = softplus(N(0, 1)) + 1e-3
+    drawn with shape [B,H,T,dv] (from the same stream); lambda0 = 1 and M0 = 0
+    as [B,H,dk,dv]."""
+    if not isinstance(w, Workload):
+        w = workload(w)
+    x = make_forward_inputs(w, B=B, H=H, T=T, dk=dk, dv=dv, seed=seed, dtype=dtype)
+    B, H, T, dk = x["k"].shape
+    dv = x["v"].shape[-1]
+    rl = _streams(x["seed"])[5]
+    vp = (softplus(rl.standard_normal((B, H, T, dv))) + 1e-3).astype(np.float32)
+    x["val_prec"] = round_bf16(vp) if x["dtype"] == "bf16" else vp
+    x["lambda0"] = np.ones((B, H, dk, dv), np.float32)
+    x["M0"] = np.zeros((B, H, dk, dv), np.float32)
+    return x
+
+
+def make_vprec_inputs_torch(w: Workload | int | str, *, seed=None, device="cuda"):
+    """Device-side version of make_vprec_inputs at the workload's full shape."""
+    import torch
+    if not isinstance(w, Workload):
+        w = workload(w)
+    x = make_forward_inputs_torch(w, seed=seed, device=device)
+    g = torch.Generator(device=device)
+    g.manual_seed((w.seed if seed is None else seed) * 16 + 8)
+    tdt = x["q"].dtype
+    x["val_prec"] = (torch.nn.functional.softplus(torch.randn((w.B, w.H, w.T, w.dv), generator=g, device=device))
+                     + 1e-3).to(tdt)
+    x["lambda0"] = None
+    x["M0"] = None
+    return x

@@ -18,3 +18,4 @@ from .kla_f64 import (  # noqa: F401
     readout,
 )
 from .kla_ou_f64 import ou_discretize_f64, kla_forward_ou_f64  # noqa: F401,E402
+from .kla_vprec_f64 import kla_forward_vprec_f64  # noqa: F401,E402

@@ -515,6 +515,47 @@ def pin_ou_limits():
     assert np.exp(ld) < 1e-20
 
 
+def pin_vprec_elements_are_dense_posteriors(seed=23):
+    """With the value precision per value channel, every element (i,j) is its
+    own scalar filter: its mean and precision after every token equal dense
+    Gaussian conditioning (numpy.linalg.solve) with coefficients
+    (a_i, pbar_i, k_i, Lambda^v_j, v_j), and y_t[j] = sum_i q_{t,i} mean_ij(t)."""
+    import oracle.kla_vprec_f64 as OV
+    rng = np.random.default_rng(seed)
+    B, H, T, dk, dv = 1, 2, 9, 3, 4
+    q, k, v, ld, pn, _, _, _ = _rand_inputs(rng, B, H, T, dk, dv)
+    vpv = np.logaddexp(0.0, rng.standard_normal((B, H, T, dv))) + 1e-3
+    lam0 = 0.5 + rng.random((B, H, dk, dv))
+    M0 = rng.standard_normal((B, H, dk, dv))
+    y, lT, MT, path = OV.kla_forward_vprec_f64(q, k, v, ld, pn, vpv, lam0, M0, return_lambda_path=True)
+    for h in range(H):
+        means = np.empty((T, dk, dv))
+        for i in range(dk):
+            for j in range(dv):
+                m, prec = dense_posterior(np.exp(ld[0, h, :, i]), pn[0, h, :, i], k[0, h, :, i], vpv[0, h, :, j],
+                                          v[0, h, :, j], lam0[0, h, i, j], M0[0, h, i, j])
+                np.testing.assert_allclose(path[0, h, :, i, j], prec, rtol=1e-9)
+                means[:, i, j] = m
+        np.testing.assert_allclose(MT[0, h], means[-1], rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(y[0, h], np.einsum("ti,tij->tj", q[0, h], means), rtol=1e-9, atol=1e-12)
+
+
+def pin_vprec_shared_precision_is_the_main_path(seed=24):
+    """When Lambda^v is one number per token (the same for every key and value
+    channel), both readings coincide: the variant equals the main oracle."""
+    import oracle.kla_vprec_f64 as OV
+    rng = np.random.default_rng(seed)
+    B, H, T, dk, dv = 2, 1, 20, 3, 5
+    q, k, v, ld, pn, _, lam0, M0 = _rand_inputs(rng, B, H, T, dk, dv)
+    s = np.logaddexp(0.0, rng.standard_normal((B, H, T, 1))) + 1e-3
+    y1, l1, M1 = O.kla_forward_f64(q, k, v, ld, pn, np.broadcast_to(s, (B, H, T, dk)), lam0, M0)
+    y2, l2, M2 = OV.kla_forward_vprec_f64(q, k, v, ld, pn, np.broadcast_to(s, (B, H, T, dv)),
+                                          np.broadcast_to(lam0[..., None], (B, H, dk, dv)), M0)
+    np.testing.assert_allclose(y2, y1, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(M2, M1, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(l2, np.broadcast_to(l1[..., None], l2.shape), rtol=1e-13)
+
+
 ALL_PINS = [
     pin_covariance_form, pin_dense_gaussian, pin_mobius_exact, pin_mobius_mpmath,
     pin_steady_state_dare, pin_no_observation, pin_no_process_noise, pin_least_squares,
@@ -522,5 +563,5 @@ ALL_PINS = [
     pin_precision_scan_matches_forward, pin_decode_covariance_form, pin_decode_chain_is_dense_posterior,
     pin_backward_finite_differences, pin_backward_forward_is_the_oracle,
     pin_backward_prior_precision_identity, pin_ou_semigroup, pin_ou_transition_variance_quadrature,
-    pin_ou_limits,
+    pin_ou_limits, pin_vprec_elements_are_dense_posteriors, pin_vprec_shared_precision_is_the_main_path,
 ]

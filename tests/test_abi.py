@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("kla_forward", "kla_forward_ou", "kla_forward_workspace_bytes", "kla_precision_scan",
+    for n in ("kla_forward", "kla_forward_ou", "kla_forward_vprec", "kla_forward_workspace_bytes", "kla_precision_scan",
               "kla_precision_scan_workspace_bytes", "kla_decode_step", "kla_backward",
               "kla_backward_workspace_bytes", "kla_workspace_init",
               "kla_workspace_error", "kla_status_string"):
@@ -175,3 +175,21 @@ def fwd_ou(K, **over):
 ])
 def test_forward_ou_rejects(K, over, code):
     assert fwd_ou(K, **over) == code
+
+
+def fwd_vp(K, **over):
+    args = dict(q=A, k=A, v=A, log_decay=A, proc_noise=A, val_prec=A, lambda0=None, M0=None,
+                y=A, lambda_T=A, M_T=A, B=1, H=2, T=64, dk=64, dv=32, dtype=1, stream=None)
+    args.update(over)
+    return K.kla_forward_vprec(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), INVALID), (dict(val_prec=None), INVALID), (dict(y=None), INVALID),
+    (dict(lambda_T=None), INVALID), (dict(M_T=None), INVALID), (dict(B=0), INVALID),
+    (dict(dk=48), UNSUPPORTED), (dict(dv=8), UNSUPPORTED), (dict(dtype=9), UNSUPPORTED),
+    (dict(k=A + 1), INVALID), (dict(v=A + 2, dtype=0), INVALID), (dict(M0=A + 2), INVALID),
+    (dict(T=-1), INVALID),
+])
+def test_forward_vprec_rejects(K, over, code):
+    assert fwd_vp(K, **over) == code
