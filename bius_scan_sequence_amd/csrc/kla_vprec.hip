@@ -78,37 +78,61 @@ __global__ __launch_bounds__(DK / kVR * kVJB) void kla_vprec_kernel(VprecParams 
     M[r] = p.M0 ? p.M0[e] : 0.f;
   }
 
-  for (int t0 = 0; t0 < T; t0 += TB) {
-    // Stage the block: per-(t, i) coefficients and per-(t, j) values.  Tokens
-    // past T are identity steps (a = 1, pbar = 0, k = 0).
-    for (int x = tid; x < TB * DK; x += NT) {
-      const int t = x / DK, i = x % DK;
-      float av = 1.f, pv = 0.f, kv = 0.f, qv = 0.f;
-      if (t0 + t < T) {
-        const size_t g = (head * T + t0 + t) * DK + i;
-        av = __expf(to_f32(ld[g]));
-        pv = to_f32(pn[g]);
-        kv = to_f32(k[g]);
-        qv = to_f32(q[g]);
+  // The next block's raw inputs are loaded into registers while the current
+  // block is computed (U1 coefficient and U2 value elements per thread).
+  constexpr int U1 = (TB * DK + NT - 1) / NT, U2 = (TB * kVJB + NT - 1) / NT;
+  In rld[U1], rpn[U1], rk[U1], rq[U1], rv[U2], rvp[U2];
+  auto load_block = [&](int tb) {
+#pragma unroll
+    for (int u = 0; u < U1; ++u) {
+      const int x = tid + u * NT, t = x / DK, i = x % DK;
+      rld[u] = rpn[u] = rk[u] = rq[u] = In(0);
+      if (x < TB * DK && tb + t < T) {
+        const size_t g = (head * T + tb + t) * DK + i;
+        rld[u] = ld[g];
+        rpn[u] = pn[g];
+        rk[u] = k[g];
+        rq[u] = q[g];
       }
-      s.a[t][i] = av;
-      s.a2[t][i] = av * av;
-      s.pn[t][i] = pv;
-      s.k[t][i] = kv;
-      s.q[t][i] = qv;
     }
-    for (int x = tid; x < TB * kVJB; x += NT) {
-      const int t = x / kVJB, c = x % kVJB;
-      float vv = 0.f, lv = 0.f;
-      if (t0 + t < T) {
-        const size_t g = (head * T + t0 + t) * DV + j0 + c;
-        vv = to_f32(v[g]);
-        lv = to_f32(vp[g]);
+#pragma unroll
+    for (int u = 0; u < U2; ++u) {
+      const int x = tid + u * NT, t = x / kVJB, c = x % kVJB;
+      rv[u] = rvp[u] = In(0);
+      if (x < TB * kVJB && tb + t < T) {
+        const size_t g = (head * T + tb + t) * DV + j0 + c;
+        rv[u] = v[g];
+        rvp[u] = vp[g];
       }
-      s.v[t][c] = vv;
-      s.L[t][c] = lv;
+    }
+  };
+  load_block(0);
+  for (int t0 = 0; t0 < T; t0 += TB) {
+    // Stage the block from the registers: per-(t, i) coefficients and
+    // per-(t, j) values.  Tokens past T are identity steps (a = 1, pbar = 0,
+    // k = 0: their zero log_decay gives a = 1).
+#pragma unroll
+    for (int u = 0; u < U1; ++u) {
+      const int x = tid + u * NT, t = x / DK, i = x % DK;
+      if (x < TB * DK) {
+        const float av = __expf(to_f32(rld[u]));
+        s.a[t][i] = av;
+        s.a2[t][i] = av * av;
+        s.pn[t][i] = to_f32(rpn[u]);
+        s.k[t][i] = to_f32(rk[u]);
+        s.q[t][i] = to_f32(rq[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U2; ++u) {
+      const int x = tid + u * NT, t = x / kVJB, c = x % kVJB;
+      if (x < TB * kVJB) {
+        s.v[t][c] = to_f32(rv[u]);
+        s.L[t][c] = to_f32(rvp[u]);
+      }
     }
     __syncthreads();
+    if (t0 + TB < T) load_block(t0 + TB);
 #pragma unroll 4
     for (int t = 0; t < TB; ++t) {
       const float vj = s.v[t][jj], Lj = s.L[t][jj];
@@ -155,7 +179,9 @@ __global__ __launch_bounds__(DK / kVR * kVJB) void kla_vprec_kernel(VprecParams 
       for (int g = 0; g < NI; ++g) y += s.part[t][c][g];
       static_cast<In*>(p.y)[(head * T + t0 + t) * DV + j0 + c] = from_f32<In>(y);
     }
-    __syncthreads();
+    // The next staging writes only the coefficient and value arrays, which
+    // every thread finished reading before the barrier above; the partials
+    // are next written after the staging barrier.
   }
 #pragma unroll
   for (int r = 0; r < kVR; ++r) {
