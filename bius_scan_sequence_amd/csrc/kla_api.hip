@@ -101,13 +101,16 @@ PscanPlan pscan_plan(int B, int H, int T, int D) {
 
 constexpr int kBwdSeg = 64;  // tokens per segment of the backward pass
 
+// Widths of 128 run as 64-wide sub-problems (the kernels take d <= 64).
+int bwd_sub(int d) { return d > 64 ? 64 : d; }
+
 struct BwdLayout {
-  size_t F, Mseg, Gseg, rs, dgw, ew, comp, cin, total;
+  size_t F, Mseg, Gseg, rs, dgw, ew, comp, cin, dqacc, dvacc, total;
 };
 
 bool bwd_shape_ok(int B, int H, int T, int dk, int dv) {
   if (B < 1 || H < 1 || T < 0) return false;
-  if (!(dk == 16 || dk == 32 || dk == 64) || !(dv == 16 || dv == 32 || dv == 64)) return false;
+  if (!supported_width(dk) || !supported_width(dv)) return false;
   const long long wide = dk > dv ? dk : dv;
   return (long long)B * H * (long long)T * wide < (1LL << 31) && (long long)B * H < (1LL << 24);
 }
@@ -115,17 +118,19 @@ bool bwd_shape_ok(int B, int H, int T, int dk, int dv) {
 BwdLayout bwd_layout(int B, int H, int T, int dk, int dv) {
   const size_t nh = (size_t)B * H;
   const size_t nseg = T > 0 ? (size_t)(T + kBwdSeg - 1) / kBwdSeg : 1;
-  const size_t chains = nh * dk;
+  const size_t sk = bwd_sub(dk), sv = bwd_sub(dv);
   BwdLayout l;
   size_t o = kHeader;
-  l.F = o; o += round256(nh * nseg * dk * 4);
-  l.Mseg = o; o += round256(nh * nseg * dk * dv * 4);
-  l.Gseg = o; o += round256(nh * nseg * dk * dv * 4);
-  l.rs = o; o += round256(chains * 4);
+  l.F = o; o += round256(nh * nseg * sk * 4);
+  l.Mseg = o; o += round256(nh * nseg * sk * sv * 4);
+  l.Gseg = o; o += round256(nh * nseg * sk * sv * 4);
+  l.rs = o; o += round256(nh * dk * 4);
   l.dgw = o; o += round256(nh * (size_t)T * dk * 4);
   l.ew = o; o += round256(nh * (size_t)T * dk * 4);
-  l.comp = o; o += round256(nseg * chains * 16);
-  l.cin = o; o += round256(nseg * chains * 8);
+  l.comp = o; o += round256(nseg * nh * sk * 16);
+  l.cin = o; o += round256(nseg * nh * sk * 8);
+  l.dqacc = o; if (dv > 64) o += round256(nh * (size_t)T * dk * 4);
+  l.dvacc = o; if (dk > 64) o += round256(nh * (size_t)T * dv * 4);
   l.total = o;
   return l;
 }
@@ -156,7 +161,6 @@ extern "C" int kla_backward(const void* q, const void* k, const void* v, const v
       if (!x) return KLA_ERR_INVALID_ARG;
   if (dtype != KLA_F32 && dtype != KLA_BF16) return KLA_ERR_UNSUPPORTED;
   if (!supported_width(dk) || !supported_width(dv)) return KLA_ERR_UNSUPPORTED;
-  if (dk > 64 || dv > 64) return KLA_ERR_UNSUPPORTED;
   if (!bwd_shape_ok(B, H, T, dk, dv)) return KLA_ERR_INVALID_ARG;
   // Per-token arrays are read and written four elements at a time.
   for (int x = 0; x < 14; ++x)
@@ -175,24 +179,58 @@ extern "C" int kla_backward(const void* q, const void* k, const void* v, const v
                                          nheads * dk * dv, st);
     return e == hipSuccess ? KLA_OK : hip_fail(e, "kla_backward (T = 0)");
   }
+  const bool bf16 = dtype == KLA_BF16;
+  const size_t esz = bf16 ? 2 : 4;
+  const int sk = bwd_sub(dk), sv = bwd_sub(dv), KH = dk / sk, VH = dv / sv;
   const BwdLayout l = bwd_layout(B, H, T, dk, dv);
   char* ws = static_cast<char*>(workspace);
+  auto kbyte = [&](const void* base, int off) {  // key-side array shifted by `off` channels
+    return base ? static_cast<const char*>(base) + (size_t)off * esz : nullptr;
+  };
   BwdParams p;
-  p.q = q; p.k = k; p.v = v; p.ld = log_decay; p.pn = proc_noise; p.vp = val_prec; p.dy = grad_y;
-  p.lam0 = lambda0; p.M0 = M0; p.lpath = lambda_path; p.dlamT = grad_lambda_T; p.dMT = grad_M_T;
-  p.dq = grad_q; p.dk = grad_k; p.dv = grad_v; p.dld = grad_log_decay; p.dpn = grad_proc_noise;
-  p.dvp = grad_val_prec; p.dlam0 = grad_lambda0; p.dM0 = grad_M0;
   p.nheads = (int)nheads; p.T = T; p.nseg = (T + kBwdSeg - 1) / kBwdSeg;
-  p.nchains = nheads * dk;
+  p.nchains = nheads * sk;
   p.F = reinterpret_cast<float*>(ws + l.F);
   p.Mseg = reinterpret_cast<float*>(ws + l.Mseg);
   p.Gseg = reinterpret_cast<float*>(ws + l.Gseg);
-  p.rs = reinterpret_cast<float*>(ws + l.rs);
-  p.dgw = reinterpret_cast<float*>(ws + l.dgw);
-  p.ew = reinterpret_cast<float*>(ws + l.ew);
   p.comp = reinterpret_cast<float*>(ws + l.comp);
   p.cin = reinterpret_cast<float*>(ws + l.cin);
-  hipError_t e = launch_backward(p, dk, dv, dtype == KLA_BF16, st);
+  p.ks = dk; p.vs = dv; p.kws = dk; p.ksh = dk; p.mrow = dv; p.mhead = dk * dv; p.vacc = dv;
+  float* const rs = reinterpret_cast<float*>(ws + l.rs);
+  float* const dgw = reinterpret_cast<float*>(ws + l.dgw);
+  float* const ew = reinterpret_cast<float*>(ws + l.ew);
+  float* const dqacc = VH > 1 ? reinterpret_cast<float*>(ws + l.dqacc) : nullptr;
+  float* const dvacc = KH > 1 ? reinterpret_cast<float*>(ws + l.dvacc) : nullptr;
+  hipError_t e = hipSuccess;
+  for (int kh = 0; kh < KH && e == hipSuccess; ++kh) {
+    const int ko = kh * sk;
+    p.q = kbyte(q, ko); p.k = kbyte(k, ko); p.ld = kbyte(log_decay, ko); p.pn = kbyte(proc_noise, ko);
+    p.vp = kbyte(val_prec, ko);
+    p.lpath = lambda_path + ko;
+    p.lam0 = lambda0 ? lambda0 + ko : nullptr;
+    p.dlamT = grad_lambda_T ? grad_lambda_T + ko : nullptr;
+    p.dlam0 = grad_lambda0 + ko;
+    p.rs = rs + ko; p.dgw = dgw + ko; p.ew = ew + ko;
+    p.dq = const_cast<char*>(kbyte(grad_q, ko)); p.dk = const_cast<char*>(kbyte(grad_k, ko));
+    p.dld = const_cast<char*>(kbyte(grad_log_decay, ko)); p.dpn = const_cast<char*>(kbyte(grad_proc_noise, ko));
+    p.dvp = const_cast<char*>(kbyte(grad_val_prec, ko));
+    p.dq_acc = dqacc ? dqacc + ko : nullptr;
+    for (int vh = 0; vh < VH && e == hipSuccess; ++vh) {
+      const int vo = vh * sv;
+      p.v = kbyte(v, vo); p.dy = kbyte(grad_y, vo);
+      p.dv = const_cast<char*>(kbyte(grad_v, vo));
+      p.dv_acc = dvacc ? dvacc + vo : nullptr;
+      const size_t mo = (size_t)ko * dv + vo;
+      p.M0 = M0 ? M0 + mo : nullptr;
+      p.dMT = grad_M_T ? grad_M_T + mo : nullptr;
+      p.dM0 = grad_M0 + mo;
+      p.add_e = vh > 0; p.add_dq = vh > 0; p.add_dv = kh > 0;
+      e = launch_backward_front(p, sk, sv, bf16, st);
+    }
+    if (e == hipSuccess) e = launch_backward_chain(p, sk, bf16, st);
+  }
+  if (e == hipSuccess && dqacc) e = launch_backward_convert(dqacc, grad_q, nheads * (long long)T * dk, bf16, st);
+  if (e == hipSuccess && dvacc) e = launch_backward_convert(dvacc, grad_v, nheads * (long long)T * dv, bf16, st);
   return e == hipSuccess ? KLA_OK : hip_fail(e, "kla_backward");
 }
 

@@ -125,13 +125,13 @@ __device__ __forceinline__ void stage_segment(const BwdParams& p, size_t hd, int
     const int t = x / K4, i = (x % K4) * 4;
     float lf[4] = {0.f, 0.f, 0.f, 0.f}, g[4] = {0.f, 0.f, 0.f, 0.f}, q[4] = {0.f, 0.f, 0.f, 0.f};
     if (t0 + t < p.T) {
-      const size_t e = (hd * p.T + t0 + t) * K + i;
+      const size_t e = (hd * p.T + t0 + t) * p.ks + i;
       const float4 lam = *reinterpret_cast<const float4*>(p.lpath + e);
       float4 lprev;
       if (t0 + t > 0) {
-        lprev = *reinterpret_cast<const float4*>(p.lpath + e - K);
+        lprev = *reinterpret_cast<const float4*>(p.lpath + e - p.ks);
       } else if (p.lam0) {
-        const float* l0 = p.lam0 + hd * K + i;
+        const float* l0 = p.lam0 + hd * p.ksh + i;
         lprev = make_float4(l0[0], l0[1], l0[2], l0[3]);
       } else {
         lprev = make_float4(1.f, 1.f, 1.f, 1.f);
@@ -156,7 +156,7 @@ __device__ __forceinline__ void stage_segment(const BwdParams& p, size_t hd, int
     const int t = x / V4, j = (x % V4) * 4;
     In v[4] = {0, 0, 0, 0}, d[4] = {0, 0, 0, 0};
     if (t0 + t < p.T) {
-      const size_t y = (hd * p.T + t0 + t) * V + j;
+      const size_t y = (hd * p.T + t0 + t) * p.vs + j;
       if constexpr (BF16) {
         const uint2 uv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.v) + y);
         const uint2 ud = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.dy) + y);
@@ -265,13 +265,14 @@ __global__ __launch_bounds__(256) void kla_bwd_segscan_kernel(BwdParams p) {
   const int el = (blockIdx.x % NB) * 256 + threadIdx.x;
   const bool live = el < N;
   const int i = el / V;
+  const size_t me = hd * (size_t)p.mhead + (size_t)i * p.mrow + el % V;  // element of M0 / dMT / dM0
   const int nseg = p.nseg;
   float* Ms = p.Mseg + hd * nseg * (size_t)N;
   float* Gs = p.Gseg + hd * nseg * (size_t)N;
   const float* F = p.F + hd * nseg * (size_t)K + i;
   float part = 0.f;
   if (live) {
-    float m = p.M0 ? p.M0[hd * (size_t)N + el] : 0.f;
+    float m = p.M0 ? p.M0[me] : 0.f;
     int s = 0;
     for (; s + G <= nseg; s += G) {
       float u[G], f[G];
@@ -291,14 +292,14 @@ __global__ __launch_bounds__(256) void kla_bwd_segscan_kernel(BwdParams p) {
       Ms[(size_t)s * N + el] = m;
       m = fmaf(F[(size_t)s * K], m, u);
     }
-    if (p.dMT) part = m * p.dMT[hd * (size_t)N + el];
+    if (p.dMT) part = m * p.dMT[me];
   }
   // Row sum over the V threads of a row (consecutive lanes of one wave).
 #pragma unroll
   for (int o = V / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
-  if (live && el % V == 0) p.rs[hd * K + i] = part;
+  if (live && el % V == 0) p.rs[hd * p.ksh + i] = p.add_e ? p.rs[hd * p.ksh + i] + part : part;
   if (live) {
-    float h = p.dMT ? p.dMT[hd * (size_t)N + el] : 0.f;
+    float h = p.dMT ? p.dMT[me] : 0.f;
     int s = nseg - 1;
     for (; s - G + 1 >= 0; s -= G) {
       float u[G], f[G];
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(256) void kla_bwd_segscan_kernel(BwdParams p) {
       Gs[(size_t)s * N + el] = h;
       h = fmaf(F[(size_t)s * K], h, u);
     }
-    p.dM0[hd * (size_t)N + el] = h;
+    p.dM0[me] = h;
   }
 }
 
@@ -544,10 +545,15 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
         if (c0 + l >= nvalid) continue;
         const float dq = fmaf(s.cp[l * KP + i], xs[e], dqi[e]);
         const float dg = fmaf(s.sx[l * KP + i], ys[e], dgi[e]);
-        const size_t o = (tok0 + l) * K + i;
-        stout<BF16>(p.dq, o, dq);
-        p.dgw[o] = dg;
-        p.ew[o] = s.q[(c0 + l) * KP + i] * dq - s.g[(c0 + l) * KP + i] * dg;
+        const size_t ow = (tok0 + l) * p.kws + i;
+        const float ee = s.q[(c0 + l) * KP + i] * dq - s.g[(c0 + l) * KP + i] * dg;
+        if (p.dq_acc) {
+          p.dq_acc[ow] = p.add_dq ? p.dq_acc[ow] + dq : dq;
+        } else {
+          stout<BF16>(p.dq, (tok0 + l) * p.ks + i, dq);
+        }
+        p.dgw[ow] = p.add_e ? p.dgw[ow] + dg : dg;
+        p.ew[ow] = p.add_e ? p.ew[ow] + ee : ee;
       }
     }
     if (vw) {
@@ -576,7 +582,13 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = 4 * lg + e;
-        if (c0 + m < nvalid) stout<BF16>(p.dv, (tok0 + m) * V + j, dv[e]);
+        if (c0 + m >= nvalid) continue;
+        if (p.dv_acc) {
+          const size_t oa = (tok0 + m) * p.vacc + j;
+          p.dv_acc[oa] = p.add_dv ? p.dv_acc[oa] + dv[e] : dv[e];
+        } else {
+          stout<BF16>(p.dv, (tok0 + m) * p.vs + j, dv[e]);
+        }
       }
     }
     // (d) adjoint at the end of the previous chunk: diag(cp_end) H + (cp q)^T dY,
@@ -633,9 +645,9 @@ struct ChainTok {
 template <bool BF16>
 __device__ __forceinline__ ChainTok chain_tok(const BwdParams& p, size_t hd, long long ch, int t, int K, int i) {
   ChainTok c;
-  const size_t x = (hd * p.T + t) * K + i;
+  const size_t x = (hd * p.T + t) * p.ks + i, xw = (hd * p.T + t) * p.kws + i;
   c.lam = p.lpath[x];
-  c.lprev = t > 0 ? p.lpath[x - K] : (p.lam0 ? p.lam0[ch] : 1.f);
+  c.lprev = t > 0 ? p.lpath[x - p.ks] : (p.lam0 ? p.lam0[hd * p.ksh + i] : 1.f);
   const float a = __expf(ldin<BF16>(p.ld, x));
   c.a2 = a * a;
   c.D = fmaf(ldin<BF16>(p.pn, x), c.lprev, c.a2);
@@ -644,8 +656,8 @@ __device__ __forceinline__ ChainTok chain_tok(const BwdParams& p, size_t hd, lon
   c.ilprev = fast_rcp(c.lprev);
   c.k = ldin<BF16>(p.k, x);
   c.vp = ldin<BF16>(p.vp, x);
-  c.dg = p.dgw[x];
-  c.e = p.ew[x];
+  c.dg = p.dgw[xw];
+  c.e = p.ew[xw];
   return c;
 }
 }  // namespace
@@ -681,17 +693,18 @@ __global__ __launch_bounds__(256) void kla_bwd_chain_comp_kernel(BwdParams p, in
   reinterpret_cast<float4*>(p.comp)[(size_t)b * p.nchains + ch] = make_float4(E, Pm, Qa, R);
 }
 
-__global__ __launch_bounds__(256) void kla_bwd_chain_carry_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) void kla_bwd_chain_carry_kernel(BwdParams p, int K) {
   const long long ch = (long long)blockIdx.x * 256 + threadIdx.x;
   if (ch >= p.nchains) return;
-  float acc = p.rs[ch], L = p.dlamT ? p.dlamT[ch] : 0.f;
+  const size_t kv = (size_t)(ch / K) * p.ksh + ch % K;  // this channel in the key vectors
+  float acc = p.rs[kv], L = p.dlamT ? p.dlamT[kv] : 0.f;
   for (int b = p.nseg - 1; b >= 0; --b) {
     reinterpret_cast<float2*>(p.cin)[(size_t)b * p.nchains + ch] = make_float2(acc, L);
     const float4 c = reinterpret_cast<const float4*>(p.comp)[(size_t)b * p.nchains + ch];
     L = fmaf(c.y, L, fmaf(c.z, acc, c.w));
     acc += c.x;
   }
-  p.dlam0[ch] = L;
+  p.dlam0[kv] = L;
 }
 
 template <bool BF16>
@@ -713,7 +726,7 @@ __global__ __launch_bounds__(256) void kla_bwd_chain_out_kernel(BwdParams p, int
     const float c1 = c.k * c.k * c.vp * c.ilam * c.D * c.ilprev;  // c / (lam lam^-)
     const float Llp = fmaf(c1, acc, L + c0);                      // dL/dlambda^-_t
     const float w = -Llp * c.lprev * c.iD * c.iD;                 // dL/d(a^2)
-    const size_t x = (hd * p.T + t) * K + i;
+    const size_t x = (hd * p.T + t) * p.ks + i;
     stout<BF16>(p.dld, x, fmaf(2.f * c.a2, w, acc));              // a dL/da = d log f + 2 a^2 dL/d(a^2)
     stout<BF16>(p.dpn, x, w * c.lprev);
     stout<BF16>(p.dk, x, c.vp * c.ilam * c.dg + 2.f * c.k * c.vp * dc);
@@ -739,42 +752,72 @@ __global__ void kla_bwd_empty_kernel(const float* dlamT, const float* dMT, float
 // Launch sequence.
 // ---------------------------------------------------------------------------
 template <int K, int V, bool BF16>
-static hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
+static hipError_t launch_front(const BwdParams& p, hipStream_t stream) {
   const unsigned nsb = (unsigned)((long long)p.nheads * p.nseg);
   hipLaunchKernelGGL((kla_bwd_segagg_kernel<K, V, BF16>), dim3(nsb), dim3(512), 0, stream, p);
   constexpr int NB = (K * V + 255) / 256;
   hipLaunchKernelGGL((kla_bwd_segscan_kernel<K, V>), dim3((unsigned)(p.nheads * NB)), dim3(256), 0, stream, p);
   hipLaunchKernelGGL((kla_bwd_chunk_kernel<K, V, BF16>), dim3(nsb), dim3(kChunkThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <bool BF16>
+static hipError_t launch_chain(const BwdParams& p, int K, hipStream_t stream) {
   const int ncb = (int)((p.nchains + 255) / 256);
   const unsigned ncomp = (unsigned)((long long)ncb * p.nseg);
   hipLaunchKernelGGL((kla_bwd_chain_comp_kernel<BF16>), dim3(ncomp), dim3(256), 0, stream, p, K, ncb);
-  hipLaunchKernelGGL(kla_bwd_chain_carry_kernel, dim3((unsigned)ncb), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(kla_bwd_chain_carry_kernel, dim3((unsigned)ncb), dim3(256), 0, stream, p, K);
   hipLaunchKernelGGL((kla_bwd_chain_out_kernel<BF16>), dim3(ncomp), dim3(256), 0, stream, p, K, ncb);
   return hipGetLastError();
 }
 
 template <int K, bool BF16>
-static hipError_t bwd_dv(const BwdParams& p, int dv, hipStream_t stream) {
+static hipError_t front_dv(const BwdParams& p, int dv, hipStream_t stream) {
   switch (dv) {
-    case 16: return launch_bwd<K, 16, BF16>(p, stream);
-    case 32: return launch_bwd<K, 32, BF16>(p, stream);
-    case 64: return launch_bwd<K, 64, BF16>(p, stream);
+    case 16: return launch_front<K, 16, BF16>(p, stream);
+    case 32: return launch_front<K, 32, BF16>(p, stream);
+    case 64: return launch_front<K, 64, BF16>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <bool BF16>
-static hipError_t bwd_dk(const BwdParams& p, int dk, int dv, hipStream_t stream) {
+static hipError_t front_dk(const BwdParams& p, int dk, int dv, hipStream_t stream) {
   switch (dk) {
-    case 16: return bwd_dv<16, BF16>(p, dv, stream);
-    case 32: return bwd_dv<32, BF16>(p, dv, stream);
-    case 64: return bwd_dv<64, BF16>(p, dv, stream);
+    case 16: return front_dv<16, BF16>(p, dv, stream);
+    case 32: return front_dv<32, BF16>(p, dv, stream);
+    case 64: return front_dv<64, BF16>(p, dv, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_backward(const BwdParams& p, int dk, int dv, bool bf16, hipStream_t stream) {
-  return bf16 ? bwd_dk<true>(p, dk, dv, stream) : bwd_dk<false>(p, dk, dv, stream);
+// Segment aggregates, segment scans and the chunk kernel of one sub-problem
+// (dk, dv <= 64).
+hipError_t launch_backward_front(const BwdParams& p, int dk, int dv, bool bf16, hipStream_t stream) {
+  return bf16 ? front_dk<true>(p, dk, dv, stream) : front_dk<false>(p, dk, dv, stream);
+}
+
+// The per-channel reverse chain of dk channels (after every value half of
+// them has been through the front).
+hipError_t launch_backward_chain(const BwdParams& p, int dk, bool bf16, hipStream_t stream) {
+  return bf16 ? launch_chain<true>(p, dk, stream) : launch_chain<false>(p, dk, stream);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void kla_bwd_convert_kernel(const float* acc, void* out, long long n) {
+  const long long x = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (x < n) stout<BF16>(out, x, acc[x]);
+}
+
+// fp32 accumulator -> output dtype.
+hipError_t launch_backward_convert(const float* acc, void* out, long long n, bool bf16, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (bf16)
+    hipLaunchKernelGGL(kla_bwd_convert_kernel<true>, grid, dim3(256), 0, stream, acc, out, n);
+  else
+    hipLaunchKernelGGL(kla_bwd_convert_kernel<false>, grid, dim3(256), 0, stream, acc, out, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_backward_empty(const float* dlamT, const float* dMT, float* dlam0, float* dM0, long long nl,

@@ -98,6 +98,19 @@ struct BwdParams {
   float* ew;          // [nheads][T][dk] q dq - g dg (per-token share of the log-forget-gate gradient)
   float* comp;        // [nseg][nchains][4] reverse-chain block composites
   float* cin;         // [nseg][nchains][2] reverse-chain state entering each block from the right
+  // Strides (elements).  A call with d_k or d_v = 128 runs as 64-wide
+  // sub-problems on strided views of the full arrays; otherwise every stride
+  // is the plain one (ks = kws = ksh = dk, vs = dv, mrow = dv, mhead = dk*dv).
+  int ks;             // row of the key-side per-token arrays (inputs, lpath, dq, dk, dld, dpn, dvp)
+  int vs;             // row of the value-side per-token arrays (v, dy, dv)
+  int kws;            // row of dgw, ew and dq_acc
+  int ksh;            // head of the key vectors (lam0, dlamT, dlam0, rs)
+  int mrow, mhead;    // row and head of the state matrices (M0, dMT, dM0)
+  int vacc;           // row of dv_acc
+  float* dq_acc;      // nullable: dq accumulated here in fp32 instead of written
+  float* dv_acc;      // nullable: dv accumulated here in fp32 instead of written
+  int add_e;          // add into dgw, ew and rs (a later value half) instead of writing
+  int add_dq, add_dv; // add into dq_acc / dv_acc instead of writing
 };
 
 struct VprecParams {
@@ -119,7 +132,9 @@ int fwd_segment_len(int dk, int dv, bool bf16);
 hipError_t launch_forward(const FwdParams& p, int dk, int dv, bool bf16, hipStream_t stream);
 hipError_t launch_pscan(const PscanParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, long long nheads, int dk, int dv, bool bf16, hipStream_t stream);
-hipError_t launch_backward(const BwdParams& p, int dk, int dv, bool bf16, hipStream_t stream);
+hipError_t launch_backward_front(const BwdParams& p, int dk, int dv, bool bf16, hipStream_t stream);
+hipError_t launch_backward_chain(const BwdParams& p, int dk, bool bf16, hipStream_t stream);
+hipError_t launch_backward_convert(const float* acc, void* out, long long n, bool bf16, hipStream_t stream);
 hipError_t launch_backward_empty(const float* dlamT, const float* dMT, float* dlam0, float* dM0,
                                  long long nl, long long nm, hipStream_t stream);
 hipError_t launch_vprec(const VprecParams& p, long long nheads, int dk, int dv, bool bf16, hipStream_t stream);

@@ -229,8 +229,8 @@ size_t kla_backward_workspace_bytes(int B, int H, int T, int dk, int dv);
  * grad_M0 = grad_M_T (zero where those are NULL); the per-token arrays are
  * then not accessed and may be NULL.
  *
- * Supported: dk, dv in {16, 32, 64} (128: KLA_ERR_UNSUPPORTED); B, H >= 1;
- * T >= 0; B*H*T*max(dk,dv) < 2^31.  Alignment: the per-token arrays (inputs,
+ * Supported: dk, dv in {16, 32, 64, 128} (a width of 128 runs as two 64-wide
+ * halves); B, H >= 1; T >= 0; B*H*T*max(dk,dv) < 2^31.  Alignment: the per-token arrays (inputs,
  * lambda_path, grad_y and the per-token gradients) and M0, grad_M_T, grad_M0
  * 16 bytes; lambda0, grad_lambda_T, grad_lambda0 4 bytes.  The workspace holds
  * no flags, so it needs no initialisation.

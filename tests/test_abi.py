@@ -57,7 +57,7 @@ def test_workspace_sizes(K):
     assert K.kla_precision_scan_workspace_bytes(1, 1, 10, 0) == 0
     assert K.kla_backward_workspace_bytes(8, 8, 2048, 64, 64) > 256
     assert K.kla_backward_workspace_bytes(1, 1, 0, 16, 16) >= 256
-    assert K.kla_backward_workspace_bytes(1, 1, 256, 128, 64) == 0   # d = 128 not supported
+    assert K.kla_backward_workspace_bytes(1, 1, 256, 128, 64) > K.kla_backward_workspace_bytes(1, 1, 256, 64, 64)
     assert K.kla_backward_workspace_bytes(1, 1, 256, 48, 16) == 0
 
 
@@ -144,7 +144,7 @@ def bwd(K, **over):
     (dict(q=None), INVALID), (dict(lambda_path=None), INVALID), (dict(grad_y=None), INVALID),
     (dict(grad_v=None), INVALID), (dict(grad_val_prec=None), INVALID), (dict(grad_lambda0=None), INVALID),
     (dict(grad_M0=None), INVALID), (dict(B=0), INVALID), (dict(T=-1), INVALID),
-    (dict(dk=128), UNSUPPORTED), (dict(dv=128), UNSUPPORTED), (dict(dk=48), UNSUPPORTED),
+    (dict(dk=256), UNSUPPORTED), (dict(dv=8), UNSUPPORTED), (dict(dk=48), UNSUPPORTED),
     (dict(dtype=2), UNSUPPORTED),
     (dict(q=A + 1), INVALID), (dict(q=A + 8), INVALID), (dict(lambda_path=A + 4), INVALID),
     (dict(grad_y=A + 8), INVALID), (dict(grad_q=A + 8), INVALID),

@@ -131,6 +131,11 @@ SHAPES = [
     (2, 2, 257, 64, 64, "bf16", True),
     (1, 3, 64, 32, 64, "bf16", False),
     (1, 2, 333, 16, 64, "bf16", True),
+    # widths of 128 run as 64-wide halves: key halves, value halves, both
+    (1, 2, 150, 128, 64, "f32", True),
+    (1, 1, 100, 32, 128, "f32", True),
+    (1, 2, 140, 128, 128, "f32", False),
+    (2, 1, 200, 128, 128, "bf16", True),
 ]
 
 
