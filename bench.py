@@ -138,7 +138,7 @@ def cpu_baseline(x):
 
 
 CONFIGS = ("lm45m_bf16", "lm180m_bf16", "long_bf16", "chains_f32", "decode_lm45m_bf16", "decode_b256_bf16",
-           "bwd_lm45m_bf16", "ou_lm45m_bf16", "vprec_lm45m_bf16")
+           "bwd_lm45m_bf16", "bwd_long_bf16", "ou_lm45m_bf16", "vprec_lm45m_bf16")
 
 
 def vprec_algorithmic_bytes(B, H, T, dk, dv, esz):

@@ -643,11 +643,12 @@ struct ChainTok {
 };
 
 template <bool BF16>
-__device__ __forceinline__ ChainTok chain_tok(const BwdParams& p, size_t hd, long long ch, int t, int K, int i) {
+// Token data of one chain at key-side index x and workspace index xw;
+// lam0v is the precision before the first token (used when first).
+__device__ __forceinline__ ChainTok chain_tok(const BwdParams& p, size_t x, size_t xw, bool first, float lam0v) {
   ChainTok c;
-  const size_t x = (hd * p.T + t) * p.ks + i, xw = (hd * p.T + t) * p.kws + i;
   c.lam = p.lpath[x];
-  c.lprev = t > 0 ? p.lpath[x - p.ks] : (p.lam0 ? p.lam0[hd * p.ksh + i] : 1.f);
+  c.lprev = first ? lam0v : p.lpath[x - p.ks];
   const float a = __expf(ldin<BF16>(p.ld, x));
   c.a2 = a * a;
   c.D = fmaf(ldin<BF16>(p.pn, x), c.lprev, c.a2);
@@ -671,9 +672,13 @@ __global__ __launch_bounds__(256) void kla_bwd_chain_comp_kernel(BwdParams p, in
   const size_t hd = ch / K;
   const int i = (int)(ch % K);
   const int tb = b * kSL, te = min(p.T, tb + kSL);
+  // Per-thread bases; each token adds a uniform offset (scalar arithmetic).
+  const size_t bk = (hd * p.T + tb) * p.ks + i, bw = (hd * p.T + tb) * p.kws + i;
+  const float lam0v = (tb == 0 && p.lam0) ? p.lam0[hd * p.ksh + i] : 1.f;
   float E = 0.f, Pm = 1.f, Qa = 0.f, R = 0.f;
   auto step = [&](int t) {
-    const ChainTok c = chain_tok<BF16>(p, hd, ch, t, K, i);
+    const int u = t - tb;
+    const ChainTok c = chain_tok<BF16>(p, bk + (size_t)u * p.ks, bw + (size_t)u * p.kws, t == 0, lam0v);
     const float g = c.k * c.vp * c.ilam;
     const float m = c.a2 * c.iD * c.iD;
     const float c1 = c.k * c.k * c.vp * c.ilam * c.D * c.ilprev;  // c / (lam lam^-), lam^- = lprev / D
@@ -715,10 +720,14 @@ __global__ __launch_bounds__(256) void kla_bwd_chain_out_kernel(BwdParams p, int
   const size_t hd = ch / K;
   const int i = (int)(ch % K);
   const int tb = b * kSL, te = min(p.T, tb + kSL);
+  const size_t bk = (hd * p.T + tb) * p.ks + i, bw = (hd * p.T + tb) * p.kws + i;
+  const float lam0v = (tb == 0 && p.lam0) ? p.lam0[hd * p.ksh + i] : 1.f;
   const float2 in = reinterpret_cast<const float2*>(p.cin)[(size_t)b * p.nchains + ch];
   float acc = in.x, L = in.y;
   auto step = [&](int t) {
-    const ChainTok c = chain_tok<BF16>(p, hd, ch, t, K, i);
+    const int u = t - tb;
+    const size_t x = bk + (size_t)u * p.ks;
+    const ChainTok c = chain_tok<BF16>(p, x, bw + (size_t)u * p.kws, t == 0, lam0v);
     const float g = c.k * c.vp * c.ilam;
     const float c0 = -g * c.dg * c.ilam;
     acc += c.e;                                                   // d log f_t
@@ -726,7 +735,6 @@ __global__ __launch_bounds__(256) void kla_bwd_chain_out_kernel(BwdParams p, int
     const float c1 = c.k * c.k * c.vp * c.ilam * c.D * c.ilprev;  // c / (lam lam^-)
     const float Llp = fmaf(c1, acc, L + c0);                      // dL/dlambda^-_t
     const float w = -Llp * c.lprev * c.iD * c.iD;                 // dL/d(a^2)
-    const size_t x = (hd * p.T + t) * p.ks + i;
     stout<BF16>(p.dld, x, fmaf(2.f * c.a2, w, acc));              // a dL/da = d log f + 2 a^2 dL/d(a^2)
     stout<BF16>(p.dpn, x, w * c.lprev);
     stout<BF16>(p.dk, x, c.vp * c.ilam * c.dg + 2.f * c.k * c.vp * dc);

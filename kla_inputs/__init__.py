@@ -76,6 +76,7 @@ WORKLOADS = (
     Workload(7, "bwd_lm45m_bf16", "backward", 8, 8, 2048, 64, 64, "bf16"),
     Workload(8, "ou_lm45m_bf16", "forward_ou", 8, 8, 2048, 64, 64, "bf16"),
     Workload(9, "vprec_lm45m_bf16", "forward_vprec", 8, 8, 2048, 64, 64, "bf16"),
+    Workload(10, "bwd_long_bf16", "backward", 2, 16, 16384, 128, 128, "bf16", decay_mean=-2.0),
 )
 
 

@@ -270,3 +270,28 @@ def test_backward_full_size_sampled_heads():
         ref = oracle_backward(x, gh)
         got = dict(zip(GRADS, (t[b:b + 1, h:h + 1].float().cpu().numpy() for t in out)))
         compare(f"full size head ({b},{h})", x, got, ref)
+
+
+def test_backward_long_recipe_d128():
+    """The long-memory recipe (log_decay = -softplus(N(-2, 1))) at d = 128 over
+    4096 tokens, generated on the device; one sampled head against the
+    oracle."""
+    import torch
+    import bius_scan_sequence_amd as K
+    w = KI.Workload(91, "long_d128_4k", "backward", 1, 2, 4096, 128, 128, "bf16", decay_mean=-2.0)
+    say(f"[case] backward long recipe B=1 H=2 T=4096 d=128 bf16 seed={w.seed}")
+    xd = KI.make_forward_inputs_torch(w, device="cuda")
+    gy = KI.make_backward_grads_torch(w, device="cuda")
+    _, _, _, lpath = K.forward(*(xd[n] for n in NAMES), return_lambda_path=True)
+    out = K.backward(*(xd[n] for n in NAMES), gy, lpath)
+    torch.cuda.synchronize()
+    say("[step] backward done")
+    h = 1
+    x = {n: xd[n][0:1, h:h + 1].float().cpu().numpy() for n in NAMES}
+    x["dtype"] = "bf16"
+    x["lambda0"] = np.ones((1, 1, 128), np.float32)
+    x["M0"] = np.zeros((1, 1, 128, 128), np.float32)
+    gh = {"grad_y": gy[0:1, h:h + 1].float().cpu().numpy(), "grad_lambda_T": None, "grad_M_T": None}
+    ref = oracle_backward(x, gh)
+    got = dict(zip(GRADS, (t[0:1, h:h + 1].float().cpu().numpy() for t in out)))
+    compare("long recipe d128 head 1", x, got, ref)
