@@ -44,7 +44,8 @@ __all__ = [
 class Workload:
     index: int
     name: str
-    kind: str            # "forward", "forward_ou", "forward_vprec", "precision", "decode" or "backward"
+    kind: str            # "forward", "forward_ou", "forward_prologue", "forward_vprec", "precision",
+                         # "decode" or "backward"
     B: int
     H: int
     T: int
@@ -77,6 +78,7 @@ WORKLOADS = (
     Workload(8, "ou_lm45m_bf16", "forward_ou", 8, 8, 2048, 64, 64, "bf16"),
     Workload(9, "vprec_lm45m_bf16", "forward_vprec", 8, 8, 2048, 64, 64, "bf16"),
     Workload(10, "bwd_long_bf16", "backward", 2, 16, 16384, 128, 128, "bf16", decay_mean=-2.0),
+    Workload(11, "pro_lm45m_bf16", "forward_prologue", 8, 8, 2048, 64, 64, "bf16"),
 )
 
 
@@ -391,3 +393,83 @@ def make_vprec_inputs_torch(w: Workload | int | str, *, seed=None, device="cuda"
     x["lambda0"] = None
     x["M0"] = None
     return x
+
+
+def make_prologue_inputs(w: Workload | int | str, *, B=None, H=None, T=None, dk=None, dv=None, seed=None,
+                         dtype=None, conv_width=4, bias=True) -> dict:
+    """Seeded inputs of the forward pass on raw projections (coefficient
+    prologue: causal conv1d + SiLU on q, k, v; softplus on the step length and
+    the value precision; OU prior).
+
+    Raw projections xq, xk, xv ~ N(0, 1); dt_raw, vp_raw ~ N(0, 1) (so dt and
+    val_prec are softplus(N(0, 1)), the OU recipe's distribution); theta =
+    exp(N(0, 0.25^2)) and sigma2 = softplus(N(0, 1)) + 1e-3 per (h,i) as the
+    OU recipe; convolution taps and biases ~ U(-1/sqrt(W), 1/sqrt(W)) per
+    (h, channel) (the default initialisation of a depthwise torch Conv1d), as
+    float32 [H,d,W] and [H,d].  Per-token arrays are float32 numpy arrays
+    (bf16-rounded for bf16); lambda0 = 1, M0 = 0.  Streams: those of
+    make_forward_inputs (q, k, v, log_decay -> dt_raw, proc_noise -> theta,
+    sigma2, val_prec -> vp_raw, mask -> convolution parameters).
+    """
+    if not isinstance(w, Workload):
+        w = workload(w)
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    T = w.T if T is None else T
+    dk = w.dk if dk is None else dk
+    dv = w.dv if dv is None else dv
+    seed = w.seed if seed is None else seed
+    dtype = w.dtype if dtype is None else dtype
+    rq, rk, rv, rd, rp, rl, rc = _streams(seed)
+    sk = (B, H, T, dk)
+    arrs = {"xq": rq.standard_normal(sk), "xk": rk.standard_normal(sk), "xv": rv.standard_normal((B, H, T, dv)),
+            "dt_raw": rd.standard_normal(sk), "vp_raw": rl.standard_normal(sk)}
+    out = {}
+    for name, arr in arrs.items():
+        a32 = arr.astype(np.float32)
+        out[name] = round_bf16(a32) if dtype == "bf16" else a32
+    par = rp.standard_normal((2, H, dk))
+    out["theta"] = np.exp(0.25 * par[0]).astype(np.float32)
+    out["sigma2"] = (softplus(par[1]) + 1e-3).astype(np.float32)
+    bound = 1.0 / np.sqrt(conv_width)
+    out["conv_w"] = tuple(rc.uniform(-bound, bound, (H, d, conv_width)).astype(np.float32) for d in (dk, dk, dv))
+    cb = tuple(rc.uniform(-bound, bound, (H, d)).astype(np.float32) for d in (dk, dk, dv))
+    out["conv_b"] = cb if bias else (None, None, None)
+    out["lambda0"] = np.ones((B, H, dk), np.float32)
+    out["M0"] = np.zeros((B, H, dk, dv), np.float32)
+    out["dtype"] = dtype
+    out["seed"] = seed
+    return out
+
+
+def make_prologue_inputs_torch(w: Workload | int | str, *, seed=None, device="cuda", conv_width=4):
+    """Device-side version of make_prologue_inputs at the workload's full shape
+    (torch's generator; values differ from the host version)."""
+    import torch
+    if not isinstance(w, Workload):
+        w = workload(w)
+    seed = w.seed if seed is None else seed
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    gens = []
+    for i in range(7):
+        g = torch.Generator(device=device)
+        g.manual_seed(seed * 16 + i)
+        gens.append(g)
+    sp = torch.nn.functional.softplus
+    rn = lambda shape, g: torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    bound = 1.0 / conv_width ** 0.5
+    ru = lambda shape, g: (torch.rand(shape, generator=g, device=device, dtype=torch.float32) * 2 - 1) * bound
+    sk = (B, H, T, dk)
+    return {
+        "xq": rn(sk, gens[0]).to(tdt), "xk": rn(sk, gens[1]).to(tdt), "xv": rn((B, H, T, dv), gens[2]).to(tdt),
+        "dt_raw": rn(sk, gens[3]).to(tdt),
+        "theta": torch.exp(0.25 * rn((H, dk), gens[4])),
+        "sigma2": sp(rn((H, dk), gens[4])) + 1e-3,
+        "vp_raw": rn(sk, gens[5]).to(tdt),
+        "conv_w": tuple(ru((H, d, conv_width), gens[6]) for d in (dk, dk, dv)),
+        "conv_b": tuple(ru((H, d), gens[6]) for d in (dk, dk, dv)),
+        "lambda0": torch.ones((B, H, dk), dtype=torch.float32, device=device),
+        "M0": torch.zeros((B, H, dk, dv), dtype=torch.float32, device=device),
+        "dtype": w.dtype, "seed": seed,
+    }

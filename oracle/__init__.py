@@ -19,3 +19,5 @@ from .kla_f64 import (  # noqa: F401
 )
 from .kla_ou_f64 import ou_discretize_f64, kla_forward_ou_f64  # noqa: F401,E402
 from .kla_vprec_f64 import kla_forward_vprec_f64  # noqa: F401,E402
+from .kla_prologue_f64 import (  # noqa: F401,E402
+    causal_conv_f64, silu_f64, softplus_f64, prologue_f64, kla_forward_prologue_f64)

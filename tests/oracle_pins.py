@@ -556,6 +556,86 @@ def pin_vprec_shared_precision_is_the_main_path(seed=24):
     np.testing.assert_allclose(l2, np.broadcast_to(l1[..., None], l2.shape), rtol=1e-13)
 
 
+def pin_prologue_conv_impulse(seed=25):
+    """A unit impulse at token t0 in channel c comes out of the causal
+    convolution as the channel's taps, newest tap first: u_{t0+m} = w[c, W-1-m]
+    for m < W and nothing before t0 or after t0 + W - 1 (plus the bias
+    everywhere)."""
+    import oracle.kla_prologue_f64 as OP
+    rng = np.random.default_rng(seed)
+    H, T, d, W = 2, 11, 3, 4
+    w = rng.standard_normal((H, d, W))
+    b = rng.standard_normal((H, d))
+    for t0 in (0, 4, 9):
+        x = np.zeros((1, H, T, d))
+        x[0, 1, t0, 2] = 1.0
+        u = OP.causal_conv_f64(x, w, b) - b[None, :, None, :]
+        want = np.zeros_like(u)
+        for m in range(W):
+            if t0 + m < T:
+                want[0, 1, t0 + m, 2] = w[1, 2, W - 1 - m]
+        np.testing.assert_allclose(u, want, rtol=0, atol=1e-14)
+
+
+def pin_prologue_streams_match_library_routines(seed=26):
+    """Each prologue output against library routines: the convolution as
+    numpy.convolve with the taps reversed (its first T outputs are the causal
+    ones), SiLU as u (1 + tanh(u/2)) / 2, softplus as log1p(exp(x)); each
+    stream with weights of its own, so a swapped weight or input fails."""
+    import oracle.kla_prologue_f64 as OP
+    rng = np.random.default_rng(seed)
+    B, H, T, dk, dv, W = 2, 2, 13, 3, 2, 4
+    xs = [rng.standard_normal((B, H, T, d)) for d in (dk, dk, dv)]
+    ws = [rng.uniform(-0.5, 0.5, (H, d, W)) for d in (dk, dk, dv)]
+    bs = [rng.uniform(-0.5, 0.5, (H, d)) for d in (dk, dk, dv)]
+    dtr, vpr = rng.standard_normal((B, H, T, dk)), 3 * rng.standard_normal((B, H, T, dk))
+    out = OP.prologue_f64(*xs, dtr, vpr, ws, bs, dtype="f32")
+    for x, w, b, got in zip(xs, ws, bs, out[:3]):
+        u = np.empty_like(x)
+        for bi in range(B):
+            for h in range(H):
+                for c in range(x.shape[-1]):
+                    u[bi, h, :, c] = np.convolve(x[bi, h, :, c], w[h, c, ::-1])[:T] + b[h, c]
+        want = (u * 0.5 * (1.0 + np.tanh(0.5 * u))).astype(np.float32)
+        np.testing.assert_allclose(got, want, rtol=2e-7, atol=1e-30)
+    np.testing.assert_allclose(out[3], np.log1p(np.exp(dtr)), rtol=1e-14)
+    np.testing.assert_allclose(out[4], np.log1p(np.exp(vpr)), rtol=1e-14)
+
+
+def pin_prologue_closed_forms():
+    """SiLU(0) = 0, SiLU(x) - SiLU(-x) = x, SiLU(x) / x -> 1 for large x;
+    softplus(0) = ln 2, softplus(x) - softplus(-x) = x, and softplus' = sigmoid
+    = SiLU(x) / x (central difference)."""
+    import oracle.kla_prologue_f64 as OP
+    x = np.linspace(-6.0, 6.0, 25)
+    assert OP.silu_f64(0.0) == 0.0
+    np.testing.assert_allclose(OP.silu_f64(x) - OP.silu_f64(-x), x, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(OP.silu_f64(40.0), 40.0, rtol=1e-15)
+    np.testing.assert_allclose(OP.softplus_f64(0.0), np.log(2.0), rtol=1e-15)
+    np.testing.assert_allclose(OP.softplus_f64(x) - OP.softplus_f64(-x), x, rtol=1e-13, atol=1e-15)
+    xn = x[x != 0]
+    h = 1e-5
+    deriv = (OP.softplus_f64(xn + h) - OP.softplus_f64(xn - h)) / (2 * h)
+    np.testing.assert_allclose(deriv, OP.silu_f64(xn) / xn, rtol=1e-8)
+
+
+def pin_prologue_bf16_activations():
+    """For bf16 inputs the activations are the nearest bfloat16 values: every
+    one has a zero low half as float32 and lies within half a bf16 unit in the
+    last place (at most 2^-8 relative) of the exact SiLU(conv)."""
+    import oracle.kla_prologue_f64 as OP
+    rng = np.random.default_rng(27)
+    H, T, d, W = 1, 40, 8, 4
+    x = rng.standard_normal((1, H, T, d))
+    w = rng.uniform(-0.5, 0.5, (H, d, W))
+    out = OP.prologue_f64(x, x, x, x[..., :1], x[..., :1], (w, w, w), dtype="bf16")
+    exact = OP.silu_f64(OP.causal_conv_f64(x, w))
+    for a in out[:3]:
+        bits = np.asarray(a, np.float32).view(np.uint32)
+        assert np.all(bits & 0xFFFF == 0)
+        assert np.all(np.abs(a - exact) <= 2.0 ** -8 * np.abs(exact) + 1e-38)
+
+
 ALL_PINS = [
     pin_covariance_form, pin_dense_gaussian, pin_mobius_exact, pin_mobius_mpmath,
     pin_steady_state_dare, pin_no_observation, pin_no_process_noise, pin_least_squares,
@@ -564,4 +644,6 @@ ALL_PINS = [
     pin_backward_finite_differences, pin_backward_forward_is_the_oracle,
     pin_backward_prior_precision_identity, pin_ou_semigroup, pin_ou_transition_variance_quadrature,
     pin_ou_limits, pin_vprec_elements_are_dense_posteriors, pin_vprec_shared_precision_is_the_main_path,
+    pin_prologue_conv_impulse, pin_prologue_streams_match_library_routines, pin_prologue_closed_forms,
+    pin_prologue_bf16_activations,
 ]

@@ -69,6 +69,52 @@ def test_pins_catch_planted_ou_mistake(name, monkeypatch):
     assert failed, f"no pin catches the planted mistake {name}"
 
 
+# Plausible mistakes in the prologue (oracle/kla_prologue_f64.py): name of the
+# module function and its replacement.
+def _conv_reversed_taps(x, w, b=None):
+    import oracle.kla_prologue_f64 as OP
+    return OP.__dict__["_orig_conv"](x, np.asarray(w)[..., ::-1], b)
+
+
+def _conv_centred(x, w, b=None):
+    import oracle.kla_prologue_f64 as OP
+    u = OP.__dict__["_orig_conv"](x, w, b)
+    sh = (np.asarray(w).shape[-1] - 1) // 2
+    return np.concatenate([u[:, :, sh:], np.zeros_like(u[:, :, :sh])], axis=2)
+
+
+def _conv_no_bias(x, w, b=None):
+    import oracle.kla_prologue_f64 as OP
+    return OP.__dict__["_orig_conv"](x, w, None)
+
+
+PROLOGUE_MUTANTS = {
+    "conv_reversed_taps": ("causal_conv_f64", _conv_reversed_taps),
+    "conv_not_causal": ("causal_conv_f64", _conv_centred),
+    "conv_drops_bias": ("causal_conv_f64", _conv_no_bias),
+    "silu_is_sigmoid": ("silu_f64", lambda u: 1.0 / (1.0 + np.exp(-np.asarray(u, np.float64)))),
+    "silu_wrong_sign": ("silu_f64", lambda u: np.asarray(u, np.float64) / (1.0 + np.exp(np.asarray(u, np.float64)))),
+    "softplus_is_exp": ("softplus_f64", lambda x: np.exp(np.asarray(x, np.float64))),
+    "softplus_is_relu": ("softplus_f64", lambda x: np.maximum(np.asarray(x, np.float64), 0.0)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PROLOGUE_MUTANTS))
+def test_pins_catch_planted_prologue_mistake(name, monkeypatch):
+    import oracle.kla_prologue_f64 as OP
+    attr, fn = PROLOGUE_MUTANTS[name]
+    monkeypatch.setitem(OP.__dict__, "_orig_conv", OP.causal_conv_f64)
+    monkeypatch.setattr(OP, attr, fn)
+    failed = []
+    for pin in P.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except Exception:
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {name}"
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name, monkeypatch):
     attr, fn = MUTANTS[name]
