@@ -138,7 +138,7 @@ def cpu_baseline(x):
 
 
 CONFIGS = ("lm45m_bf16", "lm180m_bf16", "long_bf16", "chains_f32", "decode_lm45m_bf16", "decode_b256_bf16",
-           "bwd_lm45m_bf16", "bwd_long_bf16", "ou_lm45m_bf16", "vprec_lm45m_bf16")
+           "bwd_lm45m_bf16", "bwd_long_bf16", "ou_lm45m_bf16", "pro_lm45m_bf16", "vprec_lm45m_bf16")
 
 
 def vprec_algorithmic_bytes(B, H, T, dk, dv, esz):
@@ -154,6 +154,17 @@ def ou_algorithmic_bytes(B, H, T, dk, dv, esz):
     k, dt, val_prec (d_k each) and v read, y written; per (h, i) theta and
     sigma2; per head the fp32 state in and out."""
     return B * H * T * ((4 * dk + dv) * esz + dv * esz) + H * dk * 8 + B * H * (dk + dk * dv) * 4 * 2
+
+
+def prologue_algorithmic_bytes(B, H, T, dk, dv, esz, width=4):
+    """Bytes of the forward pass on raw projections: per token the raw xq, xk,
+    dt_raw, vp_raw (d_k each) and xv read, y written; per (h, channel) the
+    convolution taps and biases of q, k, v and per (h, i) theta and sigma2;
+    per head the fp32 state in and out.  (The three tokens of history each
+    segment's convolution reads are counted once: they are the previous
+    segment's.)"""
+    return (B * H * T * ((4 * dk + dv) * esz + dv * esz) + H * (2 * dk + dv) * (width + 1) * 4 + H * dk * 8
+            + B * H * (dk + dk * dv) * 4 * 2)
 
 
 def backward_algorithmic_bytes(B, H, T, dk, dv, esz):
@@ -252,6 +263,24 @@ def run_configs(only, copies):
                 xc = xs[i % ncopy]
                 return K.forward_ou(xc["q"], xc["k"], xc["v"], xc["dt"], xc["theta"], xc["sigma2"], xc["val_prec"],
                                     xc["lambda0"], xc["M0"], workspace=ws, out=outs[i % ncopy])
+            units, unit = B * H * T, "tokens/s"
+        elif w.kind == "forward_prologue":
+            B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+            esz = 2 if w.dtype == "bf16" else 4
+            abytes = prologue_algorithmic_bytes(B, H, T, dk, dv, esz)
+            ncopy = max(1, min(copies, int(1.2e9 // abytes)))
+            xs = [KI.make_prologue_inputs_torch(w, seed=w.seed + c, device=dev) for c in range(ncopy)]
+            outs = [(torch.empty((B, H, T, dv), dtype=xs[0]["xq"].dtype, device=dev),
+                     torch.empty((B, H, dk), dtype=torch.float32, device=dev),
+                     torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)) for _ in range(ncopy)]
+            ws = K.Workspace(dev)
+            calls, warm = 20, 5
+
+            def run(i):
+                xc = xs[i % ncopy]
+                return K.forward_prologue(xc["xq"], xc["xk"], xc["xv"], xc["dt_raw"], xc["theta"], xc["sigma2"],
+                                          xc["vp_raw"], xc["conv_w"], xc["conv_b"], xc["lambda0"], xc["M0"],
+                                          workspace=ws, out=outs[i % ncopy])
             units, unit = B * H * T, "tokens/s"
         elif w.kind == "forward_vprec":
             B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv

@@ -20,10 +20,11 @@ import threading
 
 __all__ = [
     "LIB_PATH", "lib", "KLA_F32", "KLA_BF16", "KlaError",
-    "kla_forward_workspace_bytes", "kla_forward", "kla_forward_ou", "kla_forward_vprec",
+    "kla_forward_workspace_bytes", "kla_forward", "kla_forward_ou", "kla_forward_prologue", "kla_forward_vprec",
     "kla_precision_scan_workspace_bytes",
     "kla_precision_scan", "kla_decode_step", "kla_backward_workspace_bytes", "kla_backward",
-    "kla_workspace_init", "kla_workspace_error", "kla_status_string", "forward", "forward_ou", "forward_vprec", "precision_scan",
+    "kla_workspace_init", "kla_workspace_error", "kla_status_string", "forward", "forward_ou", "forward_prologue",
+    "forward_vprec", "precision_scan",
     "decode_step", "backward", "scan", "Workspace",
 ]
 
@@ -41,6 +42,9 @@ lib.kla_forward.restype = _i
 lib.kla_forward.argtypes = [_vp] * 6 + [_fp] * 2 + [_vp] + [_fp] * 3 + [_i] * 6 + [_vp, _sz, _vp]
 lib.kla_forward_ou.restype = _i
 lib.kla_forward_ou.argtypes = [_vp] * 4 + [_fp] * 2 + [_vp] + [_fp] * 2 + [_vp] + [_fp] * 3 + [_i] * 6 + [_vp, _sz, _vp]
+lib.kla_forward_prologue.restype = _i
+lib.kla_forward_prologue.argtypes = ([_vp] * 4 + [_fp] * 2 + [_vp] + [_fp] * 6 + [_i] + [_fp] * 2 + [_vp]
+                                     + [_fp] * 3 + [_i] * 6 + [_vp, _sz, _vp])
 lib.kla_forward_vprec.restype = _i
 lib.kla_forward_vprec.argtypes = [_vp] * 6 + [_fp] * 2 + [_vp] + [_fp] * 2 + [_i] * 6 + [_vp]
 lib.kla_precision_scan_workspace_bytes.restype = _sz
@@ -83,6 +87,14 @@ def kla_forward_ou(q, k, v, dt, theta, sigma2, val_prec, lambda0, M0, y, lambda_
                    B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream) -> int:
     return int(lib.kla_forward_ou(q, k, v, dt, theta, sigma2, val_prec, lambda0, M0, y, lambda_T, M_T,
                                   lambda_path, B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream))
+
+
+def kla_forward_prologue(xq, xk, xv, dt_raw, theta, sigma2, vp_raw, conv_wq, conv_wk, conv_wv, conv_bq, conv_bk,
+                         conv_bv, conv_width, lambda0, M0, y, lambda_T, M_T, lambda_path, B, H, T, dk, dv, dtype,
+                         workspace, workspace_bytes, stream) -> int:
+    return int(lib.kla_forward_prologue(xq, xk, xv, dt_raw, theta, sigma2, vp_raw, conv_wq, conv_wk, conv_wv,
+                                        conv_bq, conv_bk, conv_bv, conv_width, lambda0, M0, y, lambda_T, M_T,
+                                        lambda_path, B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream))
 
 
 def kla_forward_vprec(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0, y, lambda_T, M_T,
@@ -286,6 +298,61 @@ def forward_ou(q, k, v, dt, theta, sigma2, val_prec, lambda0=None, M0=None, retu
     rc = kla_forward_ou(_ptr(q), _ptr(k), _ptr(v), _ptr(dt), _ptr(theta), _ptr(sigma2), _ptr(val_prec),
                         _ptr(lambda0), _ptr(M0), _ptr(y), _ptr(lam_T), _ptr(M_T), _ptr(lpath),
                         B, H, T, dk, dv, code, ws.data_ptr(), ws.numel(), stream)
+    if rc:
+        raise KlaError(rc)
+    return (y, lam_T, M_T, lpath) if return_lambda_path else (y, lam_T, M_T)
+
+
+def forward_prologue(xq, xk, xv, dt_raw, theta, sigma2, vp_raw, conv_w, conv_b=(None, None, None), lambda0=None,
+                     M0=None, return_lambda_path=False, workspace: Workspace | None = None, out=None):
+    """KLA forward pass on raw projections, on the current stream.
+
+    xq, xk, dt_raw, vp_raw: [B,H,T,dk]; xv: [B,H,T,dv] (all bfloat16 or all
+    float32); theta, sigma2: float32 [H,dk] as ``forward_ou``; conv_w: the
+    causal depthwise convolution taps of q, k, v, float32 [H,dk,W], [H,dk,W],
+    [H,dv,W] (W in 1..4, tap W-1 on the current token); conv_b: their biases
+    [H,d] or None.  The kernel forms q, k, v = SiLU(conv(x)) in the input
+    dtype, dt = softplus(dt_raw), val_prec = softplus(vp_raw), then runs the
+    scan of ``forward_ou``.  Returns as ``forward``.
+    """
+    torch = _torch()
+    B, H, T, dk = xk.shape
+    dv = xv.shape[-1]
+    dtype, dev = xk.dtype, xk.device
+    code = _dtype_code(dtype)
+    for name, t, shp in (("xq", xq, (B, H, T, dk)), ("xk", xk, (B, H, T, dk)), ("xv", xv, (B, H, T, dv)),
+                         ("dt_raw", dt_raw, (B, H, T, dk)), ("vp_raw", vp_raw, (B, H, T, dk))):
+        _check(t, name, shp, dtype, dev)
+    _check(theta, "theta", (H, dk), torch.float32, dev)
+    _check(sigma2, "sigma2", (H, dk), torch.float32, dev)
+    if len(conv_w) != 3 or len(conv_b) != 3:
+        raise ValueError("conv_w and conv_b hold the (q, k, v) entries")
+    W = conv_w[0].shape[-1]
+    for name, t, d in (("conv_wq", conv_w[0], dk), ("conv_wk", conv_w[1], dk), ("conv_wv", conv_w[2], dv)):
+        _check(t, name, (H, d, W), torch.float32, dev)
+    for name, t, d in (("conv_bq", conv_b[0], dk), ("conv_bk", conv_b[1], dk), ("conv_bv", conv_b[2], dv)):
+        if t is not None:
+            _check(t, name, (H, d), torch.float32, dev)
+    if lambda0 is not None:
+        _check(lambda0, "lambda0", (B, H, dk), torch.float32, dev)
+    if M0 is not None:
+        _check(M0, "M0", (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        y = torch.empty((B, H, T, dv), dtype=dtype, device=dev)
+        lam_T = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+        M_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        y, lam_T, M_T = out
+    lpath = torch.empty((B, H, T, dk), dtype=torch.float32, device=dev) if return_lambda_path else None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    need = kla_forward_workspace_bytes(B, H, T, dk, dv)
+    if need == 0:
+        raise KlaError(2)
+    ws = (workspace or _default_workspace(dev, stream, "forward")).get(need, stream)
+    rc = kla_forward_prologue(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(dt_raw), _ptr(theta), _ptr(sigma2), _ptr(vp_raw),
+                              *(_ptr(w) for w in conv_w), *(_ptr(b) for b in conv_b), W,
+                              _ptr(lambda0), _ptr(M0), _ptr(y), _ptr(lam_T), _ptr(M_T), _ptr(lpath),
+                              B, H, T, dk, dv, code, ws.data_ptr(), ws.numel(), stream)
     if rc:
         raise KlaError(rc)
     return (y, lam_T, M_T, lpath) if return_lambda_path else (y, lam_T, M_T)

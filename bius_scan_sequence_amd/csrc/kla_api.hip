@@ -252,10 +252,18 @@ int forward_impl(const char* name, const void* q, const void* k, const void* v, 
                  const void* proc_noise, const float* theta, const float* sigma2, const void* val_prec,
                  const float* lambda0, const float* M0, void* y, float* lambda_T, float* M_T, float* lambda_path,
                  int B, int H, int T, int dk, int dv, int dtype, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+                 void* stream, const float* const* conv_w = nullptr, const float* const* conv_b = nullptr,
+                 int conv_width = 0) {
   if (B < 1 || H < 1 || T < 0) return KLA_ERR_INVALID_ARG;
   if (!lambda_T || !M_T) return KLA_ERR_INVALID_ARG;
   const bool ou = theta != nullptr;
+  if (conv_w) {  // coefficient prologue: three weight arrays, taps 1..4, 16-byte aligned
+    if (conv_width < 1 || conv_width > 4) return KLA_ERR_INVALID_ARG;
+    for (int i = 0; i < 3; ++i) {
+      if (!conv_w[i] || !aligned(conv_w[i], 16)) return KLA_ERR_INVALID_ARG;
+      if (conv_b[i] && !aligned(conv_b[i], 4)) return KLA_ERR_INVALID_ARG;
+    }
+  }
   // With T = 0 the per-token arrays are empty and never touched (may be null).
   if (T > 0 && (!q || !k || !v || !log_decay || (!ou && !proc_noise) || !val_prec || !y))
     return KLA_ERR_INVALID_ARG;
@@ -289,6 +297,11 @@ int forward_impl(const char* name, const void* q, const void* k, const void* v, 
   p.q = q; p.k = k; p.v = v; p.ld = log_decay; p.pn = ou ? nullptr : proc_noise; p.vp = val_prec;
   p.lam0 = lambda0; p.M0 = M0; p.y = y; p.lamT = lambda_T; p.MT = M_T; p.lpath = lambda_path;
   p.theta = theta; p.sigma2 = ou ? sigma2 : nullptr;
+  for (int i = 0; i < 3; ++i) {
+    p.cw[i] = conv_w ? conv_w[i] : nullptr;
+    p.cb[i] = conv_w ? conv_b[i] : nullptr;
+  }
+  p.cwidth = conv_w ? conv_width : 0;
   p.nheads = (int)nheads; p.T = T; p.nseg = nseg; p.H = H;
   p.ctrl = reinterpret_cast<unsigned*>(ws);
   p.hdone = reinterpret_cast<unsigned*>(ws + l.hdone);
@@ -321,6 +334,23 @@ extern "C" int kla_forward_ou(const void* q, const void* k, const void* v, const
   if (!theta) return KLA_ERR_INVALID_ARG;
   return forward_impl("kla_forward_ou", q, k, v, dt, nullptr, theta, sigma2, val_prec, lambda0, M0, y, lambda_T,
                       M_T, lambda_path, B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" int kla_forward_prologue(const void* xq, const void* xk, const void* xv, const void* dt_raw,
+                                    const float* theta, const float* sigma2, const void* vp_raw,
+                                    const float* conv_wq, const float* conv_wk, const float* conv_wv,
+                                    const float* conv_bq, const float* conv_bk, const float* conv_bv, int conv_width,
+                                    const float* lambda0, const float* M0, void* y, float* lambda_T, float* M_T,
+                                    float* lambda_path, int B, int H, int T, int dk, int dv, int dtype,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!theta) return KLA_ERR_INVALID_ARG;
+  const float* cw[3] = {conv_wq, conv_wk, conv_wv};
+  const float* cb[3] = {conv_bq, conv_bk, conv_bv};
+  for (const float* w : cw)
+    if (!w) return KLA_ERR_INVALID_ARG;
+  return forward_impl("kla_forward_prologue", xq, xk, xv, dt_raw, nullptr, theta, sigma2, vp_raw, lambda0, M0, y,
+                      lambda_T, M_T, lambda_path, B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream, cw, cb,
+                      conv_width);
 }
 
 extern "C" int kla_forward_vprec(const void* q, const void* k, const void* v, const void* log_decay,

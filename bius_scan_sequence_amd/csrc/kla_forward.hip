@@ -19,20 +19,22 @@
 //      channel crosses workgroups).
 //   3. The walk is repeated with the true entering precision to produce the
 //      per-token gates f = a lam^-/lam and g = k Lambda^v / lam, folded into the
-//      matrix-core operands of 16-token chunks:
-//        Qs = q * cp,  Ks = g / cp,  Qg = Qs * (prod of f over earlier chunks),
-//        cp = in-chunk cumulative product of f (Kd = g * prod_{w>u} f_w = Ks cp_end).
-//   4. Chunk loop from a zero state: y_c = tril(Qs Ks^T) V + Qs M_c and
-//      M_{c+1} = diag(cp_end) (M_c + Ks^T V), on 16x16 matrix-core tiles; the
+//      matrix-core operands of 16-token chunks, referred to the middle of the
+//      chunk:
+//        Qs = q * cp / F1,  Ks = g * F1 / cp,  Qg = q * cp * (prod of f over earlier chunks),
+//        cp = in-chunk cumulative product of f, F1 = its value after the first
+//        half, F2 = cp_end / F1 (Kd = g * prod_{w>u} f_w = Ks F2).
+//   4. Chunk loop from a zero state: y_c = tril(Qs Ks^T) V + Qs (F1 M_c) and
+//      M_{c+1} = diag(F2) (F1 M_c + Ks^T V), on 16x16 matrix-core tiles; the
 //      state stays in accumulator registers, never in HBM.
 //   5. Decoupled look-back of the mean carry (prod f over the segment, local
 //      state), then y += Qg M_in and store.
 // Every carry is folded forward in segment order with the same instructions,
 // so results do not depend on which predecessor a look-back stops at.
 //
-// A chunk whose in-chunk decay prod f falls below 2^-64 on some channel would
-// overflow Ks = g / cp; such a chunk takes an exact scalar path for its
-// intra-chunk scores instead.
+// A chunk whose decay prod f over either half falls below 2^-64 on some
+// channel could overflow Qs or Ks; such a chunk takes an exact scalar path for
+// its intra-chunk scores instead (and chunk-start operands for the rest).
 #include <type_traits>
 
 #include "kla_device.h"
@@ -68,7 +70,7 @@ struct FwdCfg {
   static constexpr bool KST = BF16;
   static constexpr int RAW_BYTES = 5 * L * DK * (int)sizeof(In);        // q, k, ld, pn, vp
   static constexpr int OPS_BYTES = 3 * L * QROW + (KST ? 0 : DK * KROW);  // Qs, Ks, Qg[, Kd^T]
-  // The local readout Qs_c M_c waits until the local state has been published
+  // The local readout Qs_c (F1_c M_c) waits until the local state has been published
   // (it then overlaps that publication and the first flag poll) when the local
   // chunk states fit in registers (NRT*CPW <= 4 tiles per lane); otherwise it
   // runs in the chunk loop.
@@ -106,9 +108,17 @@ struct FwdSmem {
   // A-operand order, for the parts that have no place elsewhere.
   alignas(16) unsigned char ap[C::AP_BYTES];
   alignas(16) float cpe[C::NCH * DK];      // per chunk: prod of f over the chunk
+  // Per chunk: the reference of its scores (prod of f over the first half, or
+  // 1 for an unsafe chunk) and the factor that takes the state, once the
+  // chunk's keys are added, to the chunk end (prod of f over the second half,
+  // or cpe for an unsafe chunk).
+  alignas(16) float cpm[C::NCH * DK];
+  alignas(16) float cp2[C::NCH * DK];
   float lamc[C::NCH * DK];                 // per chunk: precision entering the chunk
   alignas(16) float fseg[DK];              // prod of f over the segment
   float red[C::TAIL ? 4 : C::RED_BYTES / 4];
+  // Coefficient prologue: the three raw rows before the segment of xq, xk, xv.
+  alignas(16) In halo[3 * (2 * DK + DV)];
   int unsafe[C::NCH];
   int ctl[4];
 
@@ -250,17 +260,161 @@ __device__ __forceinline__ void ou_coef(float th, float s2, float dt, float& ld,
   pn = s2 * dt * phi;
 }
 
-// log_decay and proc_noise of CPT channels of one token: read from the staged
-// tiles, or (OU inputs) formed from the staged step length and the channels'
-// theta and sigma2.
-template <bool OU, int CPT, typename In>
-__device__ __forceinline__ void coef_vals(const In* rld, const In* rpn, const float (&th)[CPT],
-                                          const float (&s2)[CPT], float (&ldv)[CPT], float (&pnv)[CPT]) {
-  if constexpr (OU) {
+// Input modes of the kernel: log_decay and proc_noise given per token
+// (kPlain); the OU prior in continuous time, discretised per token (kOU); the
+// OU prior behind the coefficient prologue (kPrologue: raw projections and
+// raw coefficients, see below).
+enum FwdMode { kPlain = 0, kOU = 1, kPrologue = 2 };
+
+// Coefficient prologue of the Mamba-like block ([KLA-nl] §4 "Architectuur":
+// the scan sits between causal 1D convolutions with SiLU activations):
+// q, k, v = SiLU(causal depthwise conv1d of the raw projections), stored in the
+// input dtype; the step length and the value precision are softplus of their
+// raw values, formed in fp32 where they are used.
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))); }
+__device__ __forceinline__ float silu_f(float u) { return u * fast_rcp(1.f + __expf(-u)); }
+
+// Convolution taps of channels c0 .. c0 + N - 1 (weights [d][W] of one head,
+// W <= 4) as four slots, slot j multiplying the token 3 - j steps back; slots
+// before the first tap hold zero.
+template <int N>
+__device__ __forceinline__ void conv_slots(const float* w, const float* b, int W, int c0, float (&ws)[N][4],
+                                           float (&bs)[N]) {
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    if (W == 4) {
+      const float4 v = *reinterpret_cast<const float4*>(w + (size_t)(c0 + c) * 4);
+      ws[c][0] = v.x; ws[c][1] = v.y; ws[c][2] = v.z; ws[c][3] = v.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tap = j - (4 - W);
+        ws[c][j] = tap >= 0 ? w[(size_t)(c0 + c) * W + tap] : 0.f;
+      }
+    }
+    bs[c] = b ? b[c0 + c] : 0.f;
+  }
+}
+
+// Values of one 16-byte unit as floats, and back (bf16: round to nearest even).
+template <typename In>
+__device__ __forceinline__ void unpack_unit(const uint4& u, float (&x)[16 / sizeof(In)]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  if constexpr (sizeof(In) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(w[i]);
+  }
+}
+template <typename In>
+__device__ __forceinline__ uint4 pack_unit(const float (&x)[16 / sizeof(In)]) {
+  uint32_t w[4];
+  if constexpr (sizeof(In) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)bf16_rne(x[2 * i]) | ((uint32_t)bf16_rne(x[2 * i + 1]) << 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(x[i]);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// The three raw rows before a tile (tokens t0 - 3 .. t0 - 1; zero before the
+// sequence start) from global memory into LDS, [3][WIDTH].
+template <typename In, int WIDTH, int NT>
+__device__ __forceinline__ void stage_halo(In* dst, const In* src, int t0, int tid) {
+  constexpr int PER = 16 / (int)sizeof(In), UPR = WIDTH / PER;
+  static_assert(3 * UPR <= NT, "one unit per thread");
+  if (tid < 3 * UPR) {
+    const int r = tid / UPR, c0 = (tid % UPR) * PER;
+    const bool ok = t0 - 3 + r >= 0;
+    reinterpret_cast<uint4*>(dst)[tid] =
+        ok ? *reinterpret_cast<const uint4*>(src + (ptrdiff_t)(r - 3) * WIDTH + c0) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// SiLU of the causal convolution over a staged [ROWS x WIDTH] raw tile (rows
+// r < 0 in `halo`), for rows r < nvalid; rows past nvalid are zero.  The
+// result, in the input dtype, is left in registers in store_tile's unit
+// order.  Each thread's units share one channel group, so it loads its taps
+// once.
+template <typename In, int ROWS, int WIDTH, int NT>
+__device__ __forceinline__ void conv_lds(uint4 (&buf)[(ROWS * WIDTH * (int)sizeof(In) / 16 + NT - 1) / NT],
+                                         const In* tile, const In* halo, int nvalid, const float* w, const float* b,
+                                         int W, int tid) {
+  constexpr int PER = 16 / (int)sizeof(In), UPR = WIDTH / PER, UNITS = ROWS * UPR;
+  constexpr int U = (UNITS + NT - 1) / NT;
+  static_assert(NT % UPR == 0, "a thread's units must share their channels");
+  const int c0 = (tid % UPR) * PER;
+  float ws[PER][4], bs[PER];
+  conv_slots<PER>(w, b, W, c0, ws, bs);
+#pragma unroll
+  for (int it = 0; it < U; ++it) {
+    const int u = tid + it * NT, r = u / UPR;
+    const bool live = u < UNITS && r < nvalid;
+    float acc[PER];
+#pragma unroll
+    for (int c = 0; c < PER; ++c) acc[c] = bs[c];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rr = r - 3 + j;
+      float x[PER];
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (live && j >= 4 - W)
+        raw = *reinterpret_cast<const uint4*>(rr >= 0 ? tile + rr * WIDTH + c0 : halo + (rr + 3) * WIDTH + c0);
+      unpack_unit<In>(raw, x);
+#pragma unroll
+      for (int c = 0; c < PER; ++c) acc[c] = fmaf(ws[c][j], x[c], acc[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < PER; ++c) acc[c] = live ? silu_f(acc[c]) : 0.f;
+    buf[it] = pack_unit<In>(acc);
+  }
+}
+
+// The same activation for one channel at one token (x points at its raw
+// value, rows `stride` apart; tg is the token's index in the sequence), with
+// the instructions of conv_lds, rounded to the input dtype.
+template <typename In>
+__device__ __forceinline__ float conv_at(const In* x, int stride, int tg, int W, const float (&ws)[4], float b) {
+  float acc = b;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float xv = (tg - 3 + j >= 0 && j >= 4 - W) ? to_f32(x[(ptrdiff_t)(j - 3) * stride]) : 0.f;
+    acc = fmaf(ws[j], xv, acc);
+  }
+  return to_f32(from_f32<In>(silu_f(acc)));
+}
+
+// log_decay, proc_noise and val_prec of CPT channels of one token: read from
+// the staged tiles; or (OU) log_decay and proc_noise formed from the staged
+// step length and the channels' theta and sigma2; or (prologue) the same
+// after softplus of the staged raw step length and value precision.  A token
+// past the end (tv false) is an identity step: zero step length and value
+// precision.
+template <int MODE, int CPT, typename In>
+__device__ __forceinline__ void coef_vals(const In* rld, const In* rpn, const In* rvp, const float (&th)[CPT],
+                                          const float (&s2)[CPT], bool tv, float (&ldv)[CPT], float (&pnv)[CPT],
+                                          float (&vpv)[CPT]) {
+  load_vals<CPT>(rvp, vpv);
+  if constexpr (MODE == kPrologue) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) vpv[k] = tv ? softplus_f(vpv[k]) : 0.f;
+  }
+  if constexpr (MODE != kPlain) {
     float dt[CPT];
     load_vals<CPT>(rld, dt);
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) ou_coef(th[k], s2[k], dt[k], ldv[k], pnv[k]);
+    for (int k = 0; k < CPT; ++k) {
+      float d = dt[k];
+      if constexpr (MODE == kPrologue) d = tv ? softplus_f(d) : 0.f;
+      ou_coef(th[k], s2[k], d, ldv[k], pnv[k]);
+    }
   } else {
     load_vals<CPT>(rld, ldv);
     load_vals<CPT>(rpn, pnv);
@@ -295,7 +449,7 @@ constexpr int fwd_waves_per_eu() {
   return (sizeof(FwdSmem<DK, DV, BF16>) <= 80 * 1024 ? 2 : 1) * FwdCfg<DK, DV, BF16>::NW / 4;
 }
 
-template <int DK, int DV, bool BF16, bool OU>
+template <int DK, int DV, bool BF16, int MODE>
 __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, DV, BF16>())) void kla_fwd_kernel(FwdParams p) {
   using C = FwdCfg<DK, DV, BF16>;
   using In = typename C::In;
@@ -303,6 +457,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   using Op = typename M::Op;
   constexpr int L = C::L, NCH = C::NCH, CPT = C::CPT, NW = C::NW, NT = C::NT;
   constexpr int NRT = C::NRT, NCT = C::NCT, CPW = C::CPW, QROW = C::QROW, KROW = C::KROW;
+  constexpr bool OU = MODE != kPlain;
   __shared__ FwdSmem<DK, DV, BF16> s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -332,12 +487,42 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   const size_t offk = ((size_t)head * T + t0) * DK, offv = ((size_t)head * T + t0) * DV;
   constexpr int UK = (L * DK * (int)sizeof(In) / 16 + NT - 1) / NT, UV = (L * DV * (int)sizeof(In) / 16 + NT - 1) / NT;
   uint4 bq[UK], bv[UV];
-  load_tile<In, L, DK, NT>(bq, static_cast<const In*>(p.q) + offk, nvalid, tid);
-  load_tile<In, L, DV, NT>(bv, static_cast<const In*>(p.v) + offv, nvalid, tid);
-  stage_tile<In, L, DK, NT>(rk, static_cast<const In*>(p.k) + offk, nvalid, tid);
-  stage_tile<In, L, DK, NT>(rld, static_cast<const In*>(p.ld) + offk, nvalid, tid);  // OU: the step length
-  if constexpr (!OU) stage_tile<In, L, DK, NT>(rpn, static_cast<const In*>(p.pn) + offk, nvalid, tid);
-  stage_tile<In, L, DK, NT>(rvp, static_cast<const In*>(p.vp) + offk, nvalid, tid);
+  if constexpr (MODE == kPrologue) {
+    // q, k, v are SiLU(conv) of the raw projections.  The raw tiles go to LDS
+    // once (xk in the proc_noise slot, which this mode leaves free; xq and xv
+    // in their own slots, free until the aggregate walk ends), with the three
+    // rows before the segment beside them; after a barrier every thread forms
+    // its units' activations from LDS: k's into their slot, q's and v's into
+    // registers, stored after the walk as in the other modes.
+    In* const hq = s.halo;
+    In* const hk = s.halo + 3 * DK;
+    In* const hv = s.halo + 6 * DK;
+    stage_tile<In, L, DK, NT>(rpn, static_cast<const In*>(p.k) + offk, nvalid, tid);
+    stage_tile<In, L, DK, NT>(rq, static_cast<const In*>(p.q) + offk, nvalid, tid);
+    stage_tile<In, L, DV, NT>(s.v, static_cast<const In*>(p.v) + offv, nvalid, tid);
+    stage_halo<In, DK, NT>(hk, static_cast<const In*>(p.k) + offk, t0, tid);
+    stage_halo<In, DK, NT>(hq, static_cast<const In*>(p.q) + offk, t0, tid);
+    stage_halo<In, DV, NT>(hv, static_cast<const In*>(p.v) + offv, t0, tid);
+    stage_tile<In, L, DK, NT>(rld, static_cast<const In*>(p.ld) + offk, nvalid, tid);  // raw step length
+    stage_tile<In, L, DK, NT>(rvp, static_cast<const In*>(p.vp) + offk, nvalid, tid);  // raw value precision
+    __syncthreads();
+    const int hh = head % p.H, W = p.cwidth;
+    uint4 bk[UK];
+    conv_lds<In, L, DK, NT>(bk, rpn, hk, nvalid, p.cw[1] + (size_t)hh * DK * W,
+                            p.cb[1] ? p.cb[1] + (size_t)hh * DK : nullptr, W, tid);
+    store_tile<In, L, DK, NT>(rk, bk, tid);
+    conv_lds<In, L, DK, NT>(bq, rq, hq, nvalid, p.cw[0] + (size_t)hh * DK * W,
+                            p.cb[0] ? p.cb[0] + (size_t)hh * DK : nullptr, W, tid);
+    conv_lds<In, L, DV, NT>(bv, s.v, hv, nvalid, p.cw[2] + (size_t)hh * DV * W,
+                            p.cb[2] ? p.cb[2] + (size_t)hh * DV : nullptr, W, tid);
+  } else {
+    load_tile<In, L, DK, NT>(bq, static_cast<const In*>(p.q) + offk, nvalid, tid);
+    load_tile<In, L, DV, NT>(bv, static_cast<const In*>(p.v) + offv, nvalid, tid);
+    stage_tile<In, L, DK, NT>(rk, static_cast<const In*>(p.k) + offk, nvalid, tid);
+    stage_tile<In, L, DK, NT>(rld, static_cast<const In*>(p.ld) + offk, nvalid, tid);  // OU: the step length
+    if constexpr (!OU) stage_tile<In, L, DK, NT>(rpn, static_cast<const In*>(p.pn) + offk, nvalid, tid);
+    stage_tile<In, L, DK, NT>(rvp, static_cast<const In*>(p.vp) + offk, nvalid, tid);
+  }
   __syncthreads();
   const unsigned epoch = (unsigned)s.ctl[1];
   const unsigned FAGG = 2u * epoch + 2u, FINC = 2u * epoch + 3u;
@@ -381,8 +566,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
       const int x = (wt0 + e) * DK + wch;
       float kk[CPT], vpv[CPT], ldv[CPT], pnv[CPT];
       load_vals<CPT>(rk + x, kk);
-      load_vals<CPT>(rvp + x, vpv);
-      coef_vals<OU, CPT>(rld + x, rpn + x, th, s2, ldv, pnv);
+      coef_vals<MODE, CPT>(rld + x, rpn + x, rvp + x, th, s2, wt0 + e < nvalid, ldv, pnv, vpv);
 #pragma unroll
       for (int k = 0; k < CPT; ++k) {
         const float kv = kk[k] * vpv[k];
@@ -526,8 +710,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
       } else {
         float kk[CPT], vpv[CPT], ldv[CPT];
         load_vals<CPT>(rk + x, kk);
-        load_vals<CPT>(rvp + x, vpv);
-        coef_vals<OU, CPT>(rld + x, rpn + x, th, s2, ldv, pnv);
+        coef_vals<MODE, CPT>(rld + x, rpn + x, rvp + x, th, s2, t < nvalid, ldv, pnv, vpv);
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
           kv[k] = kk[k] * vpv[k];
@@ -571,28 +754,54 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
     else
       walk(std::false_type{});
   }
-  // A chunk is unsafe when some channel's prod f over it falls below 2^-64
-  // (Ks = g / cp could overflow); the chunk's walker waves flag it in LDS.
+  // The scores of a chunk take the middle of the chunk as reference point:
+  // Qs = q cp / F1 and Ks = g F1 / cp, with cp the prod of f from the chunk
+  // start and F1 its value at the end of the first half, so that every factor
+  // is bounded by the decay over one half (Qs Ks^T still pairs q_t g_u with
+  // the decay from u to t).  A chunk is unsafe when some channel's prod f over
+  // either half falls below 2^-64 (Qs or Ks could overflow); the chunk's
+  // walker waves flag it in LDS, and its rows then hold the chunk-start
+  // versions Qs = q cp and (with KST) Kd for the exact path.
   bool unsafe_w = false;
   float FpA[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
     const float Fp = FpA[k] = __shfl_xor(Fg[k], 32, 64);  // the other half's prod f
     const float cpe = wh ? Fp * Fg[k] : Fg[k] * Fp;
-    unsafe_w |= __ballot(walker && !(cpe >= 0x1p-64f)) != 0ull;
-    if (wh) {
-      const float r = fast_rcp(Fp);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        wq[e][k] *= Fp;
-        wk[e][k] *= r;
-      }
-    }
+    unsafe_w |= __ballot(walker && !(Fg[k] >= 0x1p-64f)) != 0ull;
     if (walker && wh == 0) s.cpe[wc * DK + wch + k] = cpe;
   }
   if (walker && unsafe_w && lane == 0) s.unsafe[wc] = 1;
   __syncthreads();
   const bool unsafe_c = walker && s.unsafe[wc] != 0;  // uniform over the chunk's walker waves
+  float F1[CPT];  // prod of f over the first half of the chunk
+  if (walker) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      F1[k] = wh ? FpA[k] : Fg[k];
+      if (unsafe_c) {  // chunk-start reference: the second half is rescaled
+        if (wh) {
+          const float r = fast_rcp(FpA[k]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            wq[e][k] *= FpA[k];
+            wk[e][k] *= r;
+          }
+        }
+      } else if (!wh) {  // middle reference: the first half is rescaled
+        const float r = fast_rcp(Fg[k]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          wq[e][k] *= r;
+          wk[e][k] *= Fg[k];
+        }
+      }
+      if (wh == 0) {
+        s.cpm[wc * DK + wch + k] = unsafe_c ? 1.f : Fg[k];
+        s.cp2[wc * DK + wch + k] = unsafe_c ? Fg[k] * FpA[k] : FpA[k];
+      }
+    }
+  }
   if (walker && (unsafe_c || !C::KST) && !wh) {  // Kd is stored: rescale the first half to the chunk end
 #pragma unroll
     for (int k = 0; k < CPT; ++k)
@@ -605,12 +814,13 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   unsigned char* const KdT = s.u + 3 * L * QROW;  // without KST only
   if (walker) {
     const int cb = (wch >> 2) * 16, cj = wch & 3;  // block and slot of channel wch in a row
-    // Qg = q times the prod of f from the segment start: Qs scaled by the
-    // decays of the earlier chunks.  The carried state enters y only through it.
+    // Qg = q times the prod of f from the segment start: the chunk-start
+    // version of Qs scaled by the decays of the earlier chunks.  The carried
+    // state enters y only through it.
     float dec[CPT];
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-      dec[k] = 1.f;
+      dec[k] = unsafe_c ? 1.f : F1[k];
 #pragma unroll
       for (int c = 0; c < NCH - 1; ++c)
         if (c < wc) dec[k] *= s.cpe[c * DK + wch + k];
@@ -662,6 +872,12 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
         th1 = p.theta[(size_t)(head % p.H) * DK + tid];
         s21 = p.sigma2[(size_t)(head % p.H) * DK + tid];
       }
+      float wsq[1][4], bsq[1], wsk[1][4], bsk[1];  // prologue: this channel's taps of q and k
+      if constexpr (MODE == kPrologue) {
+        const size_t hh = head % p.H;
+        conv_slots<1>(p.cw[0] + hh * DK * p.cwidth, p.cb[0] ? p.cb[0] + hh * DK : nullptr, p.cwidth, tid, wsq, bsq);
+        conv_slots<1>(p.cw[1] + hh * DK * p.cwidth, p.cb[1] ? p.cb[1] + hh * DK : nullptr, p.cwidth, tid, wsk, bsk);
+      }
       float lam = s.lamc[cc * DK + tid];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -669,15 +885,22 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
         float kk = 0.f, ldv = 0.f, pnv = 0.f, vpv = 0.f, qv = 0.f;
         if (t < nvalid) {
           const size_t gx = ((size_t)head * T + t0 + t) * DK + tid;
-          kk = to_f32(static_cast<const In*>(p.k)[gx]);
           ldv = to_f32(static_cast<const In*>(p.ld)[gx]);
+          vpv = to_f32(static_cast<const In*>(p.vp)[gx]);
+          if constexpr (MODE == kPrologue) {
+            kk = conv_at<In>(static_cast<const In*>(p.k) + gx, DK, t0 + t, p.cwidth, wsk[0], bsk[0]);
+            qv = conv_at<In>(static_cast<const In*>(p.q) + gx, DK, t0 + t, p.cwidth, wsq[0], bsq[0]);
+            ldv = softplus_f(ldv);
+            vpv = softplus_f(vpv);
+          } else {
+            kk = to_f32(static_cast<const In*>(p.k)[gx]);
+            qv = to_f32(static_cast<const In*>(p.q)[gx]);
+          }
           if constexpr (OU) {
             ou_coef(th1, s21, ldv, ldv, pnv);
           } else {
             pnv = to_f32(static_cast<const In*>(p.pn)[gx]);
           }
-          vpv = to_f32(static_cast<const In*>(p.vp)[gx]);
-          qv = to_f32(static_cast<const In*>(p.q)[gx]);
         }
         const float kv = kk * vpv;
         const float a = __expf(ldv);
@@ -731,9 +954,12 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
 
   // ---------------------------------------------------------------- 4b. chunk loop
   // Local chunk states from a zero state: M_{c+1} = diag(cp_end_c) M_c + Kd_c^T V_c.
-  // y_c gets its local part A_c V_c + Qs_c M_c, with M_c the local state
-  // entering chunk c, here or (LATE_LOCAL) from the kept states once the local
-  // state is on its way out; the carried state is added once it is known.
+  // y_c gets its local part A_c V_c + q cp M_c, here or (LATE_LOCAL) from the
+  // kept states once the local state is on its way out; the carried state is
+  // added once it is known.  The accumulators hold the state entering chunk c
+  // times the chunk's score reference (diag(cpm_c) M_c), so the readout is
+  // Qs_c times them; after the chunk's update the state is taken to the next
+  // chunk's reference (1 after the last chunk: the local state).
   v4f yl[NCH][CPW];
   v4f Macc[NRT][CPW];
   constexpr int NKEEP = C::LATE_LOCAL ? NCH : 1;
@@ -768,7 +994,8 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
           yl[cc][pp] = acc;
 #pragma unroll
           for (int mt = 0; mt < NRT; ++mt) {
-            const v4f ce = ld4(s.cpe + cc * DK + 16 * mt + 4 * lg);
+            const v4f ce = ld4(s.cp2 + cc * DK + 16 * mt + 4 * lg);
+            const v4f cn = cc + 1 < NCH ? ld4(s.cpm + (cc + 1) * DK + 16 * mt + 4 * lg) : v4f{1.f, 1.f, 1.f, 1.f};
             if constexpr (C::KST) {
               // Ks^T block (channels 16mt.., tokens of chunk cc) read transposed
               // from the Ks rows: input lane j of a 16-lane group reads the hi
@@ -776,14 +1003,14 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
               const int j = lane & 15;
               const unsigned char* a = Ks + (cc * 16 + 4 * lg + (j >> 2)) * QROW + (4 * mt + (j & 3)) * 16;
               const Op kso = cat(lds_read_tr16(a), lds_read_tr16(a + 8));
-              if (s.unsafe[cc])  // rows hold Kd: M' = diag(cp_end) M + Kd^T V
-                Macc[mt][pp] = M::dotv(Macc[mt][pp] * ce, kso, vo);
-              else  // M' = diag(cp_end) (M + Ks^T V), since Kd = Ks cp_end
-                Macc[mt][pp] = M::dotv(Macc[mt][pp], kso, vo) * ce;
-            } else {
+              if (s.unsafe[cc])  // rows hold Kd: M' = diag(cp_end) M + Kd^T V (reference 1)
+                Macc[mt][pp] = M::dotv(Macc[mt][pp] * ce, kso, vo) * cn;
+              else  // M' = diag(F2) (F1 M + Ks^T V), since Kd = Ks F2
+                Macc[mt][pp] = M::dotv(Macc[mt][pp], kso, vo) * (ce * cn);
+            } else {  // M' = diag(cp_end) M + Kd^T V, with cp_end M = F2 (F1 M)
               const v4f m = cc == 0 ? Macc[mt][pp] : Macc[mt][pp] * ce;
               const Op kdo = M::get(KdT + (16 * mt + lc) * KROW + (cc * 16 + 4 * lg) * 4);
-              Macc[mt][pp] = M::dotv(m, kdo, vo);
+              Macc[mt][pp] = M::dotv(m, kdo, vo) * cn;
             }
             if constexpr (C::LATE_LOCAL) {
               if (cc + 1 < NCH) Mkeep[cc + 1 < NKEEP ? cc + 1 : 0][mt][pp] = Macc[mt][pp];
@@ -804,7 +1031,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   constexpr int FB = NRT * CPW <= 8 ? 2 : 1;  // aggregates folded per round trip
   auto frag_off = [&](int mt, int nt) -> uint32_t { return ((uint32_t)(nt * NRT + mt) * 64 + lane) * 16; };
   v4f Min[NRT][CPW];
-  auto local_readout = [&]() {  // LATE_LOCAL: y_c += Qs_c M_c for c >= 1
+  auto local_readout = [&]() {  // LATE_LOCAL: y_c += Qs_c (F1_c M_c) for c >= 1
     if constexpr (C::LATE_LOCAL) {
 #pragma unroll
       for (int cc = 1; cc < NCH; ++cc) {
@@ -945,7 +1172,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   // ---------------------------------------------------------------- 6. carried-state readout + store
   // With M_in the state entering the segment, the true state entering chunk c
   // is M_c + diag(prod of earlier chunk decays) M_in, so
-  //   y_c = (A_c V_c + Qs_c M_c) + Qg_c M_in,
+  //   y_c = (A_c V_c + Qs_c F1_c M_c) + Qg_c M_in,
   // the bracket from the chunk loop; M_in is split into matrix-core operands
   // once for all chunks.  y is staged in LDS over v (dead once every wave has
   // left the chunk loop) and written out in 16-byte units.  A wave's y
@@ -981,10 +1208,13 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
 template <int DK, int DV, bool BF16>
 static hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   const unsigned nblocks = (unsigned)p.nheads * (unsigned)p.nseg;
-  if (p.theta)
-    hipLaunchKernelGGL((kla_fwd_kernel<DK, DV, BF16, true>), dim3(nblocks), dim3(FwdCfg<DK, DV, BF16>::NT), 0, stream, p);
+  constexpr int NT = FwdCfg<DK, DV, BF16>::NT;
+  if (p.cw[0])
+    hipLaunchKernelGGL((kla_fwd_kernel<DK, DV, BF16, kPrologue>), dim3(nblocks), dim3(NT), 0, stream, p);
+  else if (p.theta)
+    hipLaunchKernelGGL((kla_fwd_kernel<DK, DV, BF16, kOU>), dim3(nblocks), dim3(NT), 0, stream, p);
   else
-    hipLaunchKernelGGL((kla_fwd_kernel<DK, DV, BF16, false>), dim3(nblocks), dim3(FwdCfg<DK, DV, BF16>::NT), 0, stream, p);
+    hipLaunchKernelGGL((kla_fwd_kernel<DK, DV, BF16, kPlain>), dim3(nblocks), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -24,6 +24,13 @@ struct FwdParams {
   float* lpath;       // nullable
   const float* theta;   // OU inputs only ([H][dk] rate; ld then holds the step length), else null
   const float* sigma2;  // OU inputs only ([H][dk] diffusion)
+  // Coefficient prologue (cw[0] non-null): q, k, v hold the raw projections,
+  // ld the raw step length and vp the raw value precision; cw[] are the
+  // causal convolution taps of q, k, v ([H][d][cwidth]), cb[] their biases
+  // ([H][d], nullable).
+  const float* cw[3];
+  const float* cb[3];
+  int cwidth;
   int nheads, T, nseg;
   int H;              // heads per batch row (indexes theta / sigma2)
   unsigned* ctrl;     // workspace control words

@@ -42,10 +42,10 @@
  *     by kla_workspace_init() before its first use and not touched by the
  *     caller afterwards.  Calls that share one workspace must be ordered on one
  *     stream; concurrent calls on one workspace race.  A workspace serves one
- *     entry point only (kla_forward and kla_forward_ou count as one): the
- *     entry points keep different flags and counters in it, so a buffer used
- *     by kla_forward must not be passed to kla_precision_scan or
- *     kla_backward, and so on.
+ *     entry point only (kla_forward, kla_forward_ou and kla_forward_prologue
+ *     count as one): the entry points keep different flags and counters in
+ *     it, so a buffer used by kla_forward must not be passed to
+ *     kla_precision_scan or kla_backward, and so on.
  */
 #ifndef KLA_H_
 #define KLA_H_
@@ -126,6 +126,40 @@ int kla_forward_ou(const void* q, const void* k, const void* v, const void* dt,
                    void* y, float* lambda_T, float* M_T, float* lambda_path,
                    int B, int H, int T, int dk, int dv, int dtype,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * KLA forward pass behind its coefficient prologue: the scan of
+ * kla_forward_ou fed from raw projections, as in a Mamba-like block
+ * ([KLA-nl] §4 "Architectuur": the scan sits between causal 1D convolutions
+ * with SiLU activations; §1 "Dynamics Prior": exactly discretised OU prior).
+ * Per (b,h,t) and channel c, inside the kernel:
+ *   u_t[c]  = b[h,c] + sum_{s<W} w[h,c,s] x_{t-(W-1)+s}[c]   (x_t = 0 for t < 0)
+ *   q, k, v = SiLU(u) = u / (1 + e^{-u}) of xq, xk, xv, each with its own
+ *             taps, held in the input dtype (bf16: rounded to nearest even)
+ *   dt       = softplus(dt_raw),  Lambda^v = softplus(vp_raw)   (float32)
+ *   log_decay, proc_noise from (theta, sigma2, dt) as kla_forward_ou.
+ * The convolution starts from zero history at t = 0: a call covers a whole
+ * sequence (no convolution state is carried between calls; lambda0 / M0 still
+ * continue the filter).
+ *
+ * Inputs: xq, xk, dt_raw, vp_raw [B,H,T,dk] and xv [B,H,T,dv] (dtype, 16-byte
+ *   aligned); theta, sigma2 [H,dk] float32 as kla_forward_ou;
+ *   conv_wq, conv_wk [H,dk,W] and conv_wv [H,dv,W] float32 taps (tap W-1
+ *   multiplies the current token; 16-byte aligned; the layout of a depthwise
+ *   torch Conv1d weight [channels,1,W] per head);
+ *   conv_bq, conv_bk [H,dk], conv_bv [H,dv] float32 biases, nullable (zero);
+ *   conv_width W in 1..4.
+ * State, outputs, workspace (kla_forward_workspace_bytes; the layout is
+ * kla_forward's), supported shapes and errors: as kla_forward.
+ */
+int kla_forward_prologue(const void* xq, const void* xk, const void* xv, const void* dt_raw,
+                         const float* theta, const float* sigma2, const void* vp_raw,
+                         const float* conv_wq, const float* conv_wk, const float* conv_wv,
+                         const float* conv_bq, const float* conv_bk, const float* conv_bv, int conv_width,
+                         const float* lambda0, const float* M0,
+                         void* y, float* lambda_T, float* M_T, float* lambda_path,
+                         int B, int H, int T, int dk, int dv, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * KLA with the value precision indexed by value channel: val_prec is

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("kla_forward", "kla_forward_ou", "kla_forward_vprec", "kla_forward_workspace_bytes", "kla_precision_scan",
+    for n in ("kla_forward", "kla_forward_ou", "kla_forward_prologue", "kla_forward_vprec", "kla_forward_workspace_bytes", "kla_precision_scan",
               "kla_precision_scan_workspace_bytes", "kla_decode_step", "kla_backward",
               "kla_backward_workspace_bytes", "kla_workspace_init",
               "kla_workspace_error", "kla_status_string"):
@@ -175,6 +175,26 @@ def fwd_ou(K, **over):
 ])
 def test_forward_ou_rejects(K, over, code):
     assert fwd_ou(K, **over) == code
+
+
+def fwd_pro(K, **over):
+    args = dict(xq=A, xk=A, xv=A, dt_raw=A, theta=A, sigma2=A, vp_raw=A, conv_wq=A, conv_wk=A, conv_wv=A,
+                conv_bq=None, conv_bk=None, conv_bv=None, conv_width=4, lambda0=None, M0=None,
+                y=A, lambda_T=A, M_T=A, lambda_path=None, B=1, H=1, T=64, dk=16, dv=16, dtype=1,
+                workspace=A, workspace_bytes=1 << 30, stream=None)
+    args.update(over)
+    return K.kla_forward_prologue(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(conv_wq=None), INVALID), (dict(conv_wk=None), INVALID), (dict(conv_wv=None), INVALID),
+    (dict(conv_width=0), INVALID), (dict(conv_width=5), INVALID), (dict(conv_wv=A + 4), INVALID),
+    (dict(conv_bk=A + 2), INVALID), (dict(theta=None), INVALID), (dict(xq=None), INVALID),
+    (dict(dt_raw=A + 8), INVALID), (dict(dk=48), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED),
+    (dict(workspace_bytes=16), WORKSPACE), (dict(B=0), INVALID),
+])
+def test_forward_prologue_rejects(K, over, code):
+    assert fwd_pro(K, **over) == code
 
 
 def fwd_vp(K, **over):

@@ -172,8 +172,8 @@ def test_deterministic_bitwise():
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_extreme_decay_exact_path(dt):
-    """Chunks whose in-chunk decay underflows 2^-64 on some channel take the
-    exact scalar path for their intra-chunk scores."""
+    """Chunks whose decay over a half chunk underflows 2^-64 on some channel
+    take the exact scalar path for their intra-chunk scores."""
     x = KI.make_forward_inputs("tiny_f32", B=1, H=2, T=160, dk=32, dv=16, seed=123, dtype=dt)
     ld = x["log_decay"].copy()
     ld[0, 0, 20:40, 3] = -9.0      # e^-9 per token: far below 2^-64 within a chunk
@@ -181,6 +181,23 @@ def test_extreme_decay_exact_path(dt):
     ld[0, 1, 70, 5] = -60.0        # one token wipes a channel's memory
     x["log_decay"] = KI.round_bf16(ld) if dt == "bf16" else ld.astype(np.float32)
     run_case(f"extreme decay {dt}", x)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_strong_decay_middle_reference(dt):
+    """Chunks whose decay over the whole chunk falls below 2^-64 while each
+    half stays above it: their scores still come from the matrix cores, with
+    the operands referred to the middle of the chunk.  Also a chunk whose
+    first half alone falls below 2^-64 next to one whose second half does
+    (both take the exact path)."""
+    x = KI.make_forward_inputs("tiny_f32", B=1, H=2, T=200, dk=32, dv=16, seed=124, dtype=dt)
+    ld = x["log_decay"].copy()
+    ld[0, 0, 16:80, :] = -3.5      # about 2^-5 per token: 2^-81 per chunk, 2^-40 per half
+    ld[0, 1, 32:48, 0:8] = -3.9
+    ld[0, 1, 96:104, 9] = -7.0     # first half of a chunk only: 2^-81
+    ld[0, 1, 120:128, 9] = -7.0    # second half of the next chunk only
+    x["log_decay"] = KI.round_bf16(ld) if dt == "bf16" else ld.astype(np.float32)
+    run_case(f"strong decay {dt}", x)
 
 
 def test_precision_only_inputs_shared_over_value_channels():
