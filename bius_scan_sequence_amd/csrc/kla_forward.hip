@@ -271,7 +271,22 @@ enum FwdMode { kPlain = 0, kOU = 1, kPrologue = 2 };
 // q, k, v = SiLU(causal depthwise conv1d of the raw projections), stored in the
 // input dtype; the step length and the value precision are softplus of their
 // raw values, formed in fp32 where they are used.
-__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))); }
+// softplus(x) = max(x, 0) + log1p(e) with e = e^{-|x|} in (0, 1], and
+// log1p(e) = 2 atanh(z) = 2 z (1 + z^2/3 + z^4/5 + ...), z = e / (2 + e) <= 1/3:
+// terms to z^12/13 leave a relative error below 2e-8 (branch-free, unlike the
+// library log1pf).
+__device__ __forceinline__ float softplus_f(float x) {
+  const float e = __expf(-fabsf(x));
+  const float z = e * fast_rcp(2.f + e), z2 = z * z;
+  float t = 1.f / 13.f;
+  t = fmaf(t, z2, 1.f / 11.f);
+  t = fmaf(t, z2, 1.f / 9.f);
+  t = fmaf(t, z2, 1.f / 7.f);
+  t = fmaf(t, z2, 1.f / 5.f);
+  t = fmaf(t, z2, 1.f / 3.f);
+  t = fmaf(t, z2, 1.f);
+  return fmaxf(x, 0.f) + 2.f * z * t;
+}
 __device__ __forceinline__ float silu_f(float u) { return u * fast_rcp(1.f + __expf(-u)); }
 
 // Convolution taps of channels c0 .. c0 + N - 1 (weights [d][W] of one head,
@@ -280,19 +295,30 @@ __device__ __forceinline__ float silu_f(float u) { return u * fast_rcp(1.f + __e
 template <int N>
 __device__ __forceinline__ void conv_slots(const float* w, const float* b, int W, int c0, float (&ws)[N][4],
                                            float (&bs)[N]) {
+  // One uniform branch per set (not per channel); the loads of the general
+  // width are clamped into the channel's taps and then selected.
+  if (W == 4) {
 #pragma unroll
-  for (int c = 0; c < N; ++c) {
-    if (W == 4) {
+    for (int c = 0; c < N; ++c) {
       const float4 v = *reinterpret_cast<const float4*>(w + (size_t)(c0 + c) * 4);
       ws[c][0] = v.x; ws[c][1] = v.y; ws[c][2] = v.z; ws[c][3] = v.w;
-    } else {
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < N; ++c)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int tap = j - (4 - W);
-        ws[c][j] = tap >= 0 ? w[(size_t)(c0 + c) * W + tap] : 0.f;
+        const float v = w[(size_t)(c0 + c) * W + (tap > 0 ? tap : 0)];
+        ws[c][j] = tap >= 0 ? v : 0.f;
       }
-    }
-    bs[c] = b ? b[c0 + c] : 0.f;
+  }
+  if (b) {
+#pragma unroll
+    for (int c = 0; c < N; ++c) bs[c] = b[c0 + c];
+  } else {
+#pragma unroll
+    for (int c = 0; c < N; ++c) bs[c] = 0.f;
   }
 }
 
@@ -316,7 +342,7 @@ __device__ __forceinline__ uint4 pack_unit(const float (&x)[16 / sizeof(In)]) {
   uint32_t w[4];
   if constexpr (sizeof(In) == 2) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)bf16_rne(x[2 * i]) | ((uint32_t)bf16_rne(x[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) w[i] = __builtin_bit_cast(uint32_t, bf16x2(x[2 * i], x[2 * i + 1]));
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(x[i]);
@@ -364,9 +390,10 @@ __device__ __forceinline__ void conv_lds(uint4 (&buf)[(ROWS * WIDTH * (int)sizeo
     for (int j = 0; j < 4; ++j) {
       const int rr = r - 3 + j;
       float x[PER];
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (live && j >= 4 - W)
-        raw = *reinterpret_cast<const uint4*>(rr >= 0 ? tile + rr * WIDTH + c0 : halo + (rr + 3) * WIDTH + c0);
+      // Always in bounds (rr >= -3; rows past nvalid and before the sequence
+      // start are staged as zero), so read unconditionally: a slot before the
+      // first tap has weight zero, and a row past nvalid gives no output.
+      const uint4 raw = *reinterpret_cast<const uint4*>(rr >= 0 ? tile + rr * WIDTH + c0 : halo + (rr + 3) * WIDTH + c0);
       unpack_unit<In>(raw, x);
 #pragma unroll
       for (int c = 0; c < PER; ++c) acc[c] = fmaf(ws[c][j], x[c], acc[c]);
@@ -377,18 +404,31 @@ __device__ __forceinline__ void conv_lds(uint4 (&buf)[(ROWS * WIDTH * (int)sizeo
   }
 }
 
-// The same activation for one channel at one token (x points at its raw
-// value, rows `stride` apart; tg is the token's index in the sequence), with
-// the instructions of conv_lds, rounded to the input dtype.
+// The same activations for one channel over one 16-token chunk whose first
+// row is tile row r0 (x points at the channel's raw value in that row, rows
+// `stride` apart; tg0 is that row's token in the sequence), with the
+// instructions of conv_lds: the 19 raw values of the window are loaded once
+// (rows before the sequence start or past nvalid read as zero), and the
+// results are rounded to the input dtype.
 template <typename In>
-__device__ __forceinline__ float conv_at(const In* x, int stride, int tg, int W, const float (&ws)[4], float b) {
-  float acc = b;
+__device__ __forceinline__ void conv_chunk(float (&out)[16], const In* x, int stride, int tg0, int r0, int nvalid,
+                                           const float (&ws)[4], float b) {
+  float win[19];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float xv = (tg - 3 + j >= 0 && j >= 4 - W) ? to_f32(x[(ptrdiff_t)(j - 3) * stride]) : 0.f;
-    acc = fmaf(ws[j], xv, acc);
+  for (int i = 0; i < 19; ++i) {
+    const int r = r0 - 3 + i;  // tile row
+    const bool ok = tg0 - 3 + i >= 0 && r < nvalid;
+    // Rows out of range are read at row r0 (in bounds) and replaced by zero.
+    const float raw = to_f32(x[ok ? (ptrdiff_t)(i - 3) * stride : 0]);
+    win[i] = ok ? raw : 0.f;
   }
-  return to_f32(from_f32<In>(silu_f(acc)));
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    float acc = b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = fmaf(ws[j], win[e + j], acc);
+    out[e] = r0 + e < nvalid ? to_f32(from_f32<In>(silu_f(acc))) : 0.f;
+  }
 }
 
 // log_decay, proc_noise and val_prec of CPT channels of one token: read from
@@ -872,11 +912,15 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
         th1 = p.theta[(size_t)(head % p.H) * DK + tid];
         s21 = p.sigma2[(size_t)(head % p.H) * DK + tid];
       }
-      float wsq[1][4], bsq[1], wsk[1][4], bsk[1];  // prologue: this channel's taps of q and k
+      float qa[16], ka[16];  // prologue: this channel's q and k activations over the chunk
       if constexpr (MODE == kPrologue) {
         const size_t hh = head % p.H;
-        conv_slots<1>(p.cw[0] + hh * DK * p.cwidth, p.cb[0] ? p.cb[0] + hh * DK : nullptr, p.cwidth, tid, wsq, bsq);
-        conv_slots<1>(p.cw[1] + hh * DK * p.cwidth, p.cb[1] ? p.cb[1] + hh * DK : nullptr, p.cwidth, tid, wsk, bsk);
+        float ws[1][4], bs[1];
+        const size_t gx0 = ((size_t)head * T + t0 + cc * 16) * DK + tid;
+        conv_slots<1>(p.cw[0] + hh * DK * p.cwidth, p.cb[0] ? p.cb[0] + hh * DK : nullptr, p.cwidth, tid, ws, bs);
+        conv_chunk<In>(qa, static_cast<const In*>(p.q) + gx0, DK, t0 + cc * 16, cc * 16, nvalid, ws[0], bs[0]);
+        conv_slots<1>(p.cw[1] + hh * DK * p.cwidth, p.cb[1] ? p.cb[1] + hh * DK : nullptr, p.cwidth, tid, ws, bs);
+        conv_chunk<In>(ka, static_cast<const In*>(p.k) + gx0, DK, t0 + cc * 16, cc * 16, nvalid, ws[0], bs[0]);
       }
       float lam = s.lamc[cc * DK + tid];
 #pragma unroll
@@ -888,8 +932,8 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
           ldv = to_f32(static_cast<const In*>(p.ld)[gx]);
           vpv = to_f32(static_cast<const In*>(p.vp)[gx]);
           if constexpr (MODE == kPrologue) {
-            kk = conv_at<In>(static_cast<const In*>(p.k) + gx, DK, t0 + t, p.cwidth, wsk[0], bsk[0]);
-            qv = conv_at<In>(static_cast<const In*>(p.q) + gx, DK, t0 + t, p.cwidth, wsq[0], bsq[0]);
+            kk = ka[e];
+            qv = qa[e];
             ldv = softplus_f(ldv);
             vpv = softplus_f(vpv);
           } else {
