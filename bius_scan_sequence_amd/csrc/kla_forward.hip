@@ -111,7 +111,8 @@ struct FwdSmem {
   // Per chunk: the reference of its scores (prod of f over the first half, or
   // 1 for an unsafe chunk) and the factor that takes the state, once the
   // chunk's keys are added, to the chunk end (prod of f over the second half,
-  // or cpe for an unsafe chunk).
+  // or cpe for an unsafe chunk); with KST, a safe chunk's cp2 then also takes
+  // the next chunk's reference (folded in before the chunk loop).
   alignas(16) float cpm[C::NCH * DK];
   alignas(16) float cp2[C::NCH * DK];
   float lamc[C::NCH * DK];                 // per chunk: precision entering the chunk
@@ -994,6 +995,11 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
       if (4 * lg + e > lc) st[e] = 0.f;  // causal: u <= t
     M::put(A + (cc * 64 + lane) * 16, st);
   }
+  if (C::KST && tid < DK) {  // a safe chunk's update ends with one multiply: F2 times the next reference
+#pragma unroll
+    for (int cc = 0; cc + 1 < NCH; ++cc)
+      if (!s.unsafe[cc]) s.cp2[cc * DK + tid] *= s.cpm[(cc + 1) * DK + tid];
+  }
   __syncthreads();
 
   // ---------------------------------------------------------------- 4b. chunk loop
@@ -1039,7 +1045,9 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
 #pragma unroll
           for (int mt = 0; mt < NRT; ++mt) {
             const v4f ce = ld4(s.cp2 + cc * DK + 16 * mt + 4 * lg);
-            const v4f cn = cc + 1 < NCH ? ld4(s.cpm + (cc + 1) * DK + 16 * mt + 4 * lg) : v4f{1.f, 1.f, 1.f, 1.f};
+            auto next_ref = [&]() {
+              return cc + 1 < NCH ? ld4(s.cpm + (cc + 1) * DK + 16 * mt + 4 * lg) : v4f{1.f, 1.f, 1.f, 1.f};
+            };
             if constexpr (C::KST) {
               // Ks^T block (channels 16mt.., tokens of chunk cc) read transposed
               // from the Ks rows: input lane j of a 16-lane group reads the hi
@@ -1048,13 +1056,13 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
               const unsigned char* a = Ks + (cc * 16 + 4 * lg + (j >> 2)) * QROW + (4 * mt + (j & 3)) * 16;
               const Op kso = cat(lds_read_tr16(a), lds_read_tr16(a + 8));
               if (s.unsafe[cc])  // rows hold Kd: M' = diag(cp_end) M + Kd^T V (reference 1)
-                Macc[mt][pp] = M::dotv(Macc[mt][pp] * ce, kso, vo) * cn;
-              else  // M' = diag(F2) (F1 M + Ks^T V), since Kd = Ks F2
-                Macc[mt][pp] = M::dotv(Macc[mt][pp], kso, vo) * (ce * cn);
+                Macc[mt][pp] = M::dotv(Macc[mt][pp] * ce, kso, vo) * next_ref();
+              else  // M' = diag(F2) (F1 M + Ks^T V), since Kd = Ks F2 (ce includes the next reference)
+                Macc[mt][pp] = M::dotv(Macc[mt][pp], kso, vo) * ce;
             } else {  // M' = diag(cp_end) M + Kd^T V, with cp_end M = F2 (F1 M)
               const v4f m = cc == 0 ? Macc[mt][pp] : Macc[mt][pp] * ce;
               const Op kdo = M::get(KdT + (16 * mt + lc) * KROW + (cc * 16 + 4 * lg) * 4);
-              Macc[mt][pp] = M::dotv(m, kdo, vo) * cn;
+              Macc[mt][pp] = M::dotv(m, kdo, vo) * next_ref();
             }
             if constexpr (C::LATE_LOCAL) {
               if (cc + 1 < NCH) Mkeep[cc + 1 < NKEEP ? cc + 1 : 0][mt][pp] = Macc[mt][pp];
