@@ -389,7 +389,7 @@ __device__ __forceinline__ void conv_lds(uint4 (&buf)[(ROWS * WIDTH * (int)sizeo
     for (int c = 0; c < PER; ++c) acc[c] = bs[c];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int rr = r - 3 + j;
+      const int rr = min(r - 3 + j, ROWS - 1);  // (units past the tile read its last row, unused)
       float x[PER];
       // Always in bounds (rr >= -3; rows past nvalid and before the sequence
       // start are staged as zero), so read unconditionally: a slot before the
@@ -531,19 +531,18 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   if constexpr (MODE == kPrologue) {
     // q, k, v are SiLU(conv) of the raw projections.  The raw tiles go to LDS
     // once (xk in the proc_noise slot, which this mode leaves free; xq and xv
-    // in their own slots, free until the aggregate walk ends), with the three
-    // rows before the segment beside them; after a barrier every thread forms
-    // its units' activations from LDS: k's into their slot, q's and v's into
-    // registers, stored after the walk as in the other modes.
-    In* const hq = s.halo;
+    // in their own slots), with the three rows before the segment beside
+    // them.  After a barrier every thread forms its units of k into k's slot
+    // (the walks need it); q and v are formed during the precision carry by
+    // the waves that do not carry (section 2), and the chunk aggregates go to
+    // the proc_noise slot meanwhile.
     In* const hk = s.halo + 3 * DK;
-    In* const hv = s.halo + 6 * DK;
     stage_tile<In, L, DK, NT>(rpn, static_cast<const In*>(p.k) + offk, nvalid, tid);
     stage_tile<In, L, DK, NT>(rq, static_cast<const In*>(p.q) + offk, nvalid, tid);
     stage_tile<In, L, DV, NT>(s.v, static_cast<const In*>(p.v) + offv, nvalid, tid);
     stage_halo<In, DK, NT>(hk, static_cast<const In*>(p.k) + offk, t0, tid);
-    stage_halo<In, DK, NT>(hq, static_cast<const In*>(p.q) + offk, t0, tid);
-    stage_halo<In, DV, NT>(hv, static_cast<const In*>(p.v) + offv, t0, tid);
+    stage_halo<In, DK, NT>(s.halo, static_cast<const In*>(p.q) + offk, t0, tid);
+    stage_halo<In, DV, NT>(s.halo + 6 * DK, static_cast<const In*>(p.v) + offv, t0, tid);
     stage_tile<In, L, DK, NT>(rld, static_cast<const In*>(p.ld) + offk, nvalid, tid);  // raw step length
     stage_tile<In, L, DK, NT>(rvp, static_cast<const In*>(p.vp) + offk, nvalid, tid);  // raw value precision
     __syncthreads();
@@ -552,10 +551,6 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
     conv_lds<In, L, DK, NT>(bk, rpn, hk, nvalid, p.cw[1] + (size_t)hh * DK * W,
                             p.cb[1] ? p.cb[1] + (size_t)hh * DK : nullptr, W, tid);
     store_tile<In, L, DK, NT>(rk, bk, tid);
-    conv_lds<In, L, DK, NT>(bq, rq, hq, nvalid, p.cw[0] + (size_t)hh * DK * W,
-                            p.cb[0] ? p.cb[0] + (size_t)hh * DK : nullptr, W, tid);
-    conv_lds<In, L, DV, NT>(bv, s.v, hv, nvalid, p.cw[2] + (size_t)hh * DV * W,
-                            p.cb[2] ? p.cb[2] + (size_t)hh * DV : nullptr, W, tid);
   } else {
     load_tile<In, L, DK, NT>(bq, static_cast<const In*>(p.q) + offk, nvalid, tid);
     load_tile<In, L, DV, NT>(bv, static_cast<const In*>(p.v) + offv, nvalid, tid);
@@ -572,6 +567,9 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   // the look-back is skipped (see section 2).
   constexpr int PW = (DK + 63) / 64;  // precision carry waves
   const bool pwave = wave < PW, pch = tid < DK;
+  // Chunk 2x2 aggregates: in v's space (or the spare operand area); with the
+  // prologue in the proc_noise slot, since raw xv waits in v's space.
+  float* const cagg = MODE == kPrologue ? reinterpret_cast<float*>(rpn) : s.cagg();
   unsigned long long early = 0ull;
   if (pwave && pch && seg > 0) early = ld_record(p.pinc + (hb + seg - 1) * DK + tid);
 
@@ -634,10 +632,12 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
                        __shfl_xor(Pg[k].m11, 32, 64)};
     Pfirst[k] = wh ? Pp : Pg[k];
     const Mob Pc = wh ? mob_mul(Pg[k], Pp) : mob_mul(Pp, Pg[k]);
-    if (walker && wh == 0) *reinterpret_cast<v4f*>(s.cagg() + (wc * DK + wch + k) * 4) = v4f{Pc.m00, Pc.m01, Pc.m10, Pc.m11};
+    if (walker && wh == 0) *reinterpret_cast<v4f*>(cagg + (wc * DK + wch + k) * 4) = v4f{Pc.m00, Pc.m01, Pc.m10, Pc.m11};
   }
-  store_tile<In, L, DK, NT>(rq, bq, tid);
-  if constexpr (!C::CAGG_IN_V) store_tile<In, L, DV, NT>(s.v, bv, tid);
+  if constexpr (MODE != kPrologue) {
+    store_tile<In, L, DK, NT>(rq, bq, tid);
+    if constexpr (!C::CAGG_IN_V) store_tile<In, L, DV, NT>(s.v, bv, tid);
+  }
   __syncthreads();
 
   // ---------------------------------------------------------------- 2. precision carry
@@ -660,7 +660,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
     for (int c = 0; c < NCH; ++c) {
       Mob cg = mob_identity();
       if (pch) {
-        const v4f d = ld4(s.cagg() + (c * DK + tid) * 4);
+        const v4f d = ld4(cagg + (c * DK + tid) * 4);
         cg = Mob{d[0], d[1], d[2], d[3]};
       }
       pre[c] = c == 0 ? cg : mob_mul(cg, pre[c - 1]);
@@ -706,12 +706,36 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
       for (int c = 0; c < NCH; ++c) s.lamc[c * DK + tid] = c == 0 ? lam_in : mob_apply(pre[c - 1], lam_in);
     }
   }
+  // Prologue: the waves that do not carry form q and v from the staged raw
+  // tiles meanwhile (into registers; stored in place after the barrier).
+  constexpr int NTC = NT - 64 * PW;
+  constexpr int UKC = (L * DK * (int)sizeof(In) / 16 + NTC - 1) / NTC;
+  constexpr int UVC = (L * DV * (int)sizeof(In) / 16 + NTC - 1) / NTC;
+  uint4 cq[MODE == kPrologue ? UKC : 1], cv[MODE == kPrologue ? UVC : 1];
+  const int tc = tid - 64 * PW;
+  if constexpr (MODE == kPrologue) {
+    if (!pwave) {
+      const int hh = head % p.H, W = p.cwidth;
+      conv_lds<In, L, DK, NTC>(cq, rq, s.halo, nvalid, p.cw[0] + (size_t)hh * DK * W,
+                               p.cb[0] ? p.cb[0] + (size_t)hh * DK : nullptr, W, tc);
+      conv_lds<In, L, DV, NTC>(cv, s.v, s.halo + 6 * DK, nvalid, p.cw[2] + (size_t)hh * DV * W,
+                               p.cb[2] ? p.cb[2] + (size_t)hh * DV : nullptr, W, tc);
+    }
+  }
   __syncthreads();
   if (pwave && !last) {
     wait_stores();
     if (lane == 0) st_relaxed(pfl + 2 * seg, FINC);
   }
-  if constexpr (C::CAGG_IN_V) store_tile<In, L, DV, NT>(s.v, bv, tid);  // the aggregates are consumed
+  if constexpr (MODE == kPrologue) {
+    if (!pwave) {
+      store_tile<In, L, DK, NTC>(rq, cq, tc);
+      store_tile<In, L, DV, NTC>(s.v, cv, tc);
+    }
+    __syncthreads();  // the gate walk reads q
+  } else if constexpr (C::CAGG_IN_V) {
+    store_tile<In, L, DV, NT>(s.v, bv, tid);  // the aggregates are consumed
+  }
 
   // ---------------------------------------------------------------- 3. gate walk
   // Results stay in registers until every walker has finished reading the raw
