@@ -20,9 +20,12 @@
 // sequence, four independent element chains per thread.  The precision is
 // kept projectively as lam = n / d (the Möbius form of [KLA-nl] §2):
 //   d' = pbar n + a^2 d,  n' = n + c d',
-// for which lam^- / lam' = n / n', so f = a n / n' and g = k Lambda^v d' / n'
-// take one reciprocal per element and token; (n, d) are rescaled by a power
-// of two every fourth token.  Tokens are staged in blocks: the per-(t, i)
+// for which lam^- / lam' = n / n', so f = a n / n' and g = k Lambda^v d' / n'.
+// The mean is kept as its numerator m = M n: M' = f M + g v becomes
+//   m' = a m + k Lambda^v d' v,
+// with no reciprocal on the recursion; the one reciprocal per element and
+// token serves the readout M' = m' / n'.  (n, d, m) are rescaled by one
+// power of two every fourth token (n / d and m / n are unchanged).  Tokens are staged in blocks: the per-(t, i)
 // coefficients (a, a^2, pbar, k, q) once per block in LDS, v and Lambda^v per
 // (t, j).  The readout's sum over key channels is deferred: each thread keeps
 // its four-channel partial per token in LDS, and after the block one thread
@@ -68,14 +71,15 @@ __global__ __launch_bounds__(DK / kVR * kVJB) void kla_vprec_kernel(VprecParams 
   const In* v = static_cast<const In*>(p.v);
   const In* vp = static_cast<const In*>(p.vp);
 
-  // Element state: precision n/d and mean, for channels 4 ig + r of column j.
-  float n[kVR], d[kVR], M[kVR];
+  // Element state: precision n/d and mean numerator m = M n, for channels
+  // 4 ig + r of column j.
+  float n[kVR], d[kVR], m[kVR];
 #pragma unroll
   for (int r = 0; r < kVR; ++r) {
     const size_t e = (head * DK + ig * kVR + r) * DV + j;
     n[r] = p.lam0 ? p.lam0[e] : 1.f;
     d[r] = 1.f;
-    M[r] = p.M0 ? p.M0[e] : 0.f;
+    m[r] = p.M0 ? p.M0[e] * n[r] : 0.f;
   }
 
   // The next block's raw inputs are loaded into registers while the current
@@ -151,11 +155,8 @@ __global__ __launch_bounds__(DK / kVR * kVJB) void kla_vprec_kernel(VprecParams 
         const float c = kv[r] * kL;
         const float dd = fmaf(pv[r], n[r], a2v[r] * d[r]);  // d' = pbar n + a^2 d
         const float nn = fmaf(c, dd, n[r]);                 // n' = n + c d'
-        const float rr = fast_rcp(nn);
-        const float f = av[r] * n[r] * rr;                  // a lam^- / lam'
-        const float g = kL * dd * rr;                       // k Lambda^v / lam'
-        M[r] = fmaf(f, M[r], g * vj);
-        part = fmaf(qv[r], M[r], part);
+        m[r] = fmaf(av[r], m[r], kL * (dd * vj));           // m' = a m + k Lambda^v d' v
+        part = fmaf(qv[r] * fast_rcp(nn), m[r], part);      // q M' = q m' / n'
         n[r] = nn;
         d[r] = dd;
       }
@@ -165,6 +166,7 @@ __global__ __launch_bounds__(DK / kVR * kVJB) void kla_vprec_kernel(VprecParams 
           const int e = __builtin_amdgcn_frexp_expf(fmaxf(n[r], d[r]));
           n[r] = __builtin_amdgcn_ldexpf(n[r], -e);
           d[r] = __builtin_amdgcn_ldexpf(d[r], -e);
+          m[r] = __builtin_amdgcn_ldexpf(m[r], -e);
         }
       }
       s.part[t][jj][ig] = part;
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(DK / kVR * kVJB) void kla_vprec_kernel(VprecParams 
   for (int r = 0; r < kVR; ++r) {
     const size_t e = (head * DK + ig * kVR + r) * DV + j;
     p.lamT[e] = n[r] / d[r];
-    p.MT[e] = M[r];
+    p.MT[e] = m[r] / n[r];
   }
 }
 
