@@ -746,13 +746,19 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   float Fg[CPT];  // prod f over this walker's tokens
 #pragma unroll
   for (int k = 0; k < CPT; ++k) Fg[k] = 1.f;
+  // The precision is walked projectively, lam = n / d ([KLA-nl] §2, the
+  // Möbius form): d' = pbar n + a^2 d and n' = n + c d', so lam^- / lam' =
+  // n / n', f = a n / n' and g = k Lambda^v d' / n'.  The recursion carries
+  // two FMAs per token and no reciprocal; one reciprocal per token serves the
+  // gates.  (n, d) are rescaled by a power of two every fourth token.
   auto walk = [&](auto with_path) {
     constexpr bool PATH = decltype(with_path)::value;
-    float lam[CPT], cp[CPT];
+    float pn_[CPT], pd_[CPT], cp[CPT];
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-      lam[k] = s.lamc[wc * DK + wch + k];
-      if (wh) lam[k] = mob_apply(Pfirst[k], lam[k]);
+      pn_[k] = s.lamc[wc * DK + wch + k];
+      if (wh) pn_[k] = mob_apply(Pfirst[k], pn_[k]);
+      pd_[k] = 1.f;
       cp[k] = 1.f;
     }
     float* const lp = PATH ? p.lpath + ((size_t)head * T + t0) * DK + wch : nullptr;
@@ -785,19 +791,28 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
       }
 #pragma unroll
       for (int k = 0; k < CPT; ++k) {
-        float lam_pred;
-        const float lam_new = lam_step(lam[k], a[k] * a[k], pnv[k], c[k], lam_pred);
-        const float inv = fast_rcp(lam_new);
-        const float f = a[k] * lam_pred * inv;
-        const float g = kv[k] * inv;
+        const float d1 = fmaf(pnv[k], pn_[k], a[k] * a[k] * pd_[k]);  // d' = pbar n + a^2 d
+        const float n1 = fmaf(c[k], d1, pn_[k]);                       // n' = n + c d'
+        const float inv = fast_rcp(n1);
+        const float f = a[k] * pn_[k] * inv;
+        const float g = kv[k] * d1 * inv;
         cp[k] *= f;
         wq[e][k] = qv[k] * cp[k];
         wk[e][k] = g * fast_rcp(cp[k]);
         fr[e][k] = f;
         gr[e][k] = g;
-        lam[k] = lam_new;
+        pn_[k] = n1;
+        pd_[k] = d1;
         if constexpr (PATH) {
-          if (t < nvalid) lp[(size_t)t * DK + k] = lam_new;
+          if (t < nvalid) lp[(size_t)t * DK + k] = n1 * fast_rcp(d1);
+        }
+      }
+      if ((e & 3) == 3) {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+          const int ex = __builtin_amdgcn_frexp_expf(fmaxf(pn_[k], pd_[k]));
+          pn_[k] = __builtin_amdgcn_ldexpf(pn_[k], -ex);
+          pd_[k] = __builtin_amdgcn_ldexpf(pd_[k], -ex);
         }
       }
     }
@@ -810,7 +825,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
         sp *= fr[e][k];
       }
       Fg[k] = cp[k];
-      if (last && wc == NCH - 1 && wh) p.lamT[(size_t)head * DK + wch + k] = lam[k];
+      if (last && wc == NCH - 1 && wh) p.lamT[(size_t)head * DK + wch + k] = pn_[k] / pd_[k];
     }
   };
   if (walker) {
