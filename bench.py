@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "KLA fwd tokens/s (B*H*T) at dk=dv=64,T=2048; % of HBM roofline"
 WORKLOAD = "lm45m_bf16"
 PEAK_HBM_GBS = 8000.0
-KERNEL = "kla_fwd_kernel<64, 64, true>"
+KERNEL = "kla_fwd_kernel<64, 64, true, 0>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kla_fwd_lm45m_bf16_traffic.json")
 SOURCES = ["kla_forward.hip", "kla_device.h", "kla_internal.h"]
 NAMES = ("q", "k", "v", "log_decay", "proc_noise", "val_prec")
