@@ -117,6 +117,28 @@ def summarize_traffic(fetch_dir, write_dir, out_path=TRAFFIC_FILE):
                                           "fetch_scale", "write_scale", "launches")}))
 
 
+def device_copy_bandwidth(dev, stream, mb=512, reps=5):
+    """Bandwidth of a plain device-to-device copy of `mb` MB (read + write
+    bytes over time, HIP events on the stream), larger than the 256 MB
+    last-level cache: the second denominator for the roofline fraction."""
+    import torch
+    n = mb * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    secs = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / secs / 1e9
+
+
 def cpu_baseline(x):
     """The float64 oracle, as it stands, on the whole workload (all heads, all
     tokens) on the host, in this process before the GPU is touched (a pool of
@@ -449,6 +471,7 @@ def main():
     abytes = algorithmic_bytes(B, H, T, dk, dv, 2)
     achieved = abytes / kern_mean_s / 1e9
     traffic = measured_traffic()
+    copy_gbs = device_copy_bandwidth(dev, stream)
     out = {
         "metric": METRIC,
         "value": tokens / (ms_per_step / 1e3),
@@ -468,7 +491,8 @@ def main():
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": KERNEL, "algorithmic_bytes": abytes,
                      "kernel_ms_mean": kern_mean_s * 1e3,
-                     "kernel_ms_min": float(np.min(kern_ms)), "kernel_ms_max": float(np.max(kern_ms))},
+                     "kernel_ms_min": float(np.min(kern_ms)), "kernel_ms_max": float(np.max(kern_ms)),
+                     "device_copy_GBps": copy_gbs, "frac_of_device_copy": achieved / copy_gbs},
         "cpu_baseline": None,
     }
     if args.copy_mb:
