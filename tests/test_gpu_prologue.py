@@ -111,16 +111,32 @@ def test_forward_prologue_short_and_boundary_lengths(T):
     say(f"[ok] forward_prologue T={T}: " + ", ".join(f"{k}={v:.2e}" for k, v in stats.items()))
 
 
-def test_forward_prologue_strong_decay_exact_path():
-    """Long steps (dt_raw + 40, so dt ~ 40): chunks whose prod f falls below
-    2^-64 take the kernel's exact path, which forms the activations of its
-    chunk from the raw projections in global memory."""
-    say("[case] forward_prologue strong decay: B=1 H=2 T=200 d=32 f32 seed=9590")
-    x = KI.make_prologue_inputs("pro_lm45m_bf16", B=1, H=2, T=200, dk=32, dv=32, seed=9590, dtype="f32")
-    x["dt_raw"] = (x["dt_raw"] + 40.0).astype(np.float32)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_prologue_strong_decay_exact_path(dtype):
+    """Long steps (dt_raw + 40, so dt ~ 40): chunks whose prod f over half a
+    chunk falls below 2^-64 take the kernel's exact path, which forms the
+    activations of its chunk from the raw projections in global memory (for
+    bf16, rounded as the staged ones are)."""
+    say(f"[case] forward_prologue strong decay: B=1 H=2 T=200 d=32 {dtype} seed=9590")
+    x = KI.make_prologue_inputs("pro_lm45m_bf16", B=1, H=2, T=200, dk=32, dv=32, seed=9590, dtype=dtype)
+    dtr = x["dt_raw"].astype(np.float32) + 40.0
+    x["dt_raw"] = KI.round_bf16(dtr) if dtype == "bf16" else dtr
     got, ref = run(x, state=False)
-    stats = check_forward(x, got, ref, "f32")
+    stats = check_forward(x, got, ref, dtype, exact_coeffs=False)
     say("[ok] forward_prologue strong decay: " + ", ".join(f"{k}={v:.2e}" for k, v in stats.items()))
+
+
+@pytest.mark.parametrize("dims", [(16, 16), (16, 64), (32, 128), (128, 64)], ids=lambda d: f"{d[0]}x{d[1]}")
+def test_forward_prologue_bf16_widths(dims):
+    """bf16 at other widths: the staging units then cover 2 to 16 channels per
+    row and the carry waves are one or two."""
+    dk, dv = dims
+    seed = 9550 + dk + dv
+    say(f"[case] forward_prologue bf16 dk={dk} dv={dv}: B=2 H=2 T=190 seed={seed}")
+    x = KI.make_prologue_inputs("pro_lm45m_bf16", B=2, H=2, T=190, dk=dk, dv=dv, seed=seed, dtype="bf16")
+    got, ref = run(x, state=False)
+    stats = check_forward(x, got, ref, "bf16", exact_coeffs=False)
+    say(f"[ok] forward_prologue bf16 dk={dk} dv={dv}: " + ", ".join(f"{k}={v:.2e}" for k, v in stats.items()))
 
 
 def test_forward_prologue_empty_sequence():
