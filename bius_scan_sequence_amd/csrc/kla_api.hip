@@ -39,7 +39,7 @@ FwdLayout fwd_layout(int B, int H, int T, int dk, int dv, int nseg) {
   const size_t slots = (size_t)B * H * nseg;
   FwdLayout l;
   size_t o = kHeader;
-  l.hdone = o; o += round256((size_t)B * H * 4);
+  l.hdone = o; o += (size_t)kDoneCounters * 4;  // fixed place and size in every layout
   l.pflag = o; o += round256(slots * 2 * 4);  // one flag per carry wave (two when dk = 128)
   l.mflag = o; o += round256(slots * 8 * 4);  // one flag per wave (up to eight)
   l.pagg = o; o += round256(slots * dk * 16);
@@ -87,7 +87,7 @@ PscanPlan pscan_plan(int B, int H, int T, int D) {
   pl.nseg = T > 0 ? (T + seglen - 1) / seglen : 1;
   const size_t slots = (size_t)pl.ncblocks * pl.nseg;
   size_t o = kHeader;
-  pl.bdone = o; o += round256((size_t)pl.ncblocks * 4);
+  pl.bdone = o; o += (size_t)kDoneCounters * 4;  // fixed place and size in every layout
   pl.flag = o; o += round256(slots * 4);
   if (pl.nseg > 1) {
     pl.agg = o; o += round256(slots * 256 * 16);

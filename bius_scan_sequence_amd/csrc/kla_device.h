@@ -360,4 +360,15 @@ __device__ __forceinline__ void epoch_done_grouped(unsigned* ctrl, unsigned* gro
   epoch_done(ctrl, ngroups, e);
 }
 
+// The same for `nunits` units of `per_unit` workgroups each, counted on the
+// fixed array of kDoneCounters words `done` (unit u on word u % kDoneCounters,
+// whose group then holds every unit congruent to it).
+__device__ __forceinline__ void epoch_done_units(unsigned* ctrl, unsigned* done, unsigned unit, unsigned nunits,
+                                                 unsigned per_unit, unsigned e) {
+  constexpr unsigned NC = (unsigned)kDoneCounters;
+  const unsigned g = unit % NC;
+  const unsigned members = nunits / NC + (g < nunits % NC ? 1u : 0u);
+  epoch_done_grouped(ctrl, done + g, per_unit * members, nunits < NC ? nunits : NC, e);
+}
+
 }  // namespace kla

@@ -1243,7 +1243,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   }
   // Every thread read the epoch before the first barrier; count this
   // workgroup done (other waves may still be polling flags of this call).
-  if (nseg > 1 && tid == 0) epoch_done_grouped(p.ctrl, p.hdone + head, (unsigned)nseg, (unsigned)nheads, epoch);
+  if (nseg > 1 && tid == 0) epoch_done_units(p.ctrl, p.hdone, (unsigned)head, (unsigned)nheads, (unsigned)nseg, epoch);
   if (last) {  // final state, row-major
 #pragma unroll
     for (int pp = 0; pp < CPW; ++pp) {

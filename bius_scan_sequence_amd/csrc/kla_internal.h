@@ -9,6 +9,14 @@ namespace kla {
 // Control words at the head of every workspace (32-bit each).
 enum CtrlWord { kError = 3 };
 
+// Done counters: a fixed region of kDoneCounters words right after the
+// 256-byte header, at the same place and of the same size whatever the call's
+// shape, so that no call ever lays flags or payloads over them (a counter
+// that starts from another array's leftover never fires, and the call epoch
+// would then stop advancing).  Unit u (a head, a chain block) counts on word
+// u % kDoneCounters.
+constexpr int kDoneCounters = 4096;
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -34,7 +42,7 @@ struct FwdParams {
   int nheads, T, nseg;
   int H;              // heads per batch row (indexes theta / sigma2)
   unsigned* ctrl;     // workspace control words
-  unsigned* hdone;    // [nheads] segments of the head done with their flags
+  unsigned* hdone;    // [kDoneCounters] segments done with their flags, per head group
   unsigned* pflag;    // [nheads*nseg][2] precision-carry flags, one per carry wave
   unsigned* mflag;    // [nheads*nseg][waves] mean-carry flags, one per wave
   float* pagg;        // [nheads*nseg][dk][4] segment 2x2 aggregates
@@ -54,7 +62,7 @@ struct PscanParams {
   long long nchains;  // B*H*D
   int D, T, nseg, seglen, ncblocks;
   unsigned* ctrl;
-  unsigned* bdone;    // [ncblocks] segments of the block done with their flags
+  unsigned* bdone;    // [kDoneCounters] segments done with their flags, per chain-block group
   unsigned* flag;     // [nseg*ncblocks]
   float* agg;         // [ncblocks*nseg*256][4]
   float* inc;         // [ncblocks*nseg*256]

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void kla_pscan_kernel(PscanParams p) {
       }
     }
     // Every flag access of this workgroup is done.
-    if (tid == 0) epoch_done_grouped(p.ctrl, p.bdone + cb, (unsigned)nseg, (unsigned)p.ncblocks, epoch);
+    if (tid == 0) epoch_done_units(p.ctrl, p.bdone, (unsigned)cb, (unsigned)p.ncblocks, (unsigned)nseg, epoch);
   }
 
   // ---- walk, writing the path
