@@ -303,6 +303,10 @@ int forward_impl(const char* name, const void* q, const void* k, const void* v, 
   }
   p.cwidth = conv_w ? conv_width : 0;
   p.nheads = (int)nheads; p.T = T; p.nseg = nseg; p.H = H;
+  // With 128 or more heads a head's consecutive segments are dispatched at
+  // least 128 workgroups apart (segment-major order), and a segment seldom
+  // has a successor waiting on its aggregate.
+  p.mskip = nheads >= 128;
   p.ctrl = reinterpret_cast<unsigned*>(ws);
   p.hdone = reinterpret_cast<unsigned*>(ws + l.hdone);
   p.pflag = reinterpret_cast<unsigned*>(ws + l.pflag);

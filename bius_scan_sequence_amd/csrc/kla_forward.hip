@@ -1049,6 +1049,10 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   // times the chunk's score reference (diag(cpm_c) M_c), so the readout is
   // Qs_c times them; after the chunk's update the state is taken to the next
   // chunk's reference (1 after the last chunk: the local state).
+  // The mean-carry waves ask for the predecessor's mean flag now (used in
+  // section 5; a lane's flag of segment seg - 1 - lane).
+  const unsigned early_mflag =
+      (p.mskip && wave < NCT && seg > 0) ? lookback_peek(p.mflag + hb * NW + wave, NW, seg - 1) : 0u;
   v4f yl[NCH][CPW];
   v4f Macc[NRT][CPW];
   constexpr int NKEEP = C::LATE_LOCAL ? NCH : 1;
@@ -1179,24 +1183,36 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
       local_readout();
       if (!last) store_inclusive();
     } else {
-      const size_t fslot = (hs * NW + wave) * DK;  // this wave's copy of prod f
-      if (!last) {
-        for (int r = lane; r < DK; r += 64) st_coherent(p.mF + fslot + r, s.fseg[r]);
-        const auto r = coherent_rsrc(p.magg + hs * DK * DV, MBYTES);
+      // If the predecessor's flag read before the chunk loop already showed
+      // its inclusive state, that is the carry: this segment publishes no
+      // aggregate and runs no look-back (successors then wait for its
+      // inclusive flag, which follows at once).  Only with many heads
+      // (p.mskip): consecutive segments of a head are then dispatched far
+      // apart, so no successor is left waiting; with few heads they run side
+      // by side and the aggregate is what lets them proceed.
+      const bool pred_inc = p.mskip && __ballot(lane == 0 && early_mflag == FINC) != 0ull;
+      int r0 = seg - 1;
+      if (pred_inc) local_readout();
+      if (!pred_inc) {
+        const size_t fslot = (hs * NW + wave) * DK;  // this wave's copy of prod f
+        if (!last) {
+          for (int r = lane; r < DK; r += 64) st_coherent(p.mF + fslot + r, s.fseg[r]);
+          const auto r = coherent_rsrc(p.magg + hs * DK * DV, MBYTES);
 #pragma unroll
-        for (int pp = 0; pp < CPW; ++pp) {
-          const int nt = wave + NW * pp;
-          if (nt < NCT) {
+          for (int pp = 0; pp < CPW; ++pp) {
+            const int nt = wave + NW * pp;
+            if (nt < NCT) {
 #pragma unroll
-            for (int mt = 0; mt < NRT; ++mt) st_coherent(r, frag_off(mt, nt), Macc[mt][pp]);
+              for (int mt = 0; mt < NRT; ++mt) st_coherent(r, frag_off(mt, nt), Macc[mt][pp]);
+            }
           }
         }
+        const unsigned f1 = lookback_peek(mfl, NW, seg - 1);
+        local_readout();  // overlaps the stores above and the flag poll
+        wait_stores();
+        if (!last && lane == 0) st_relaxed(mfl + NW * seg, FAGG);
+        r0 = lookback_find(mfl, NW, seg, FAGG, FINC, p.ctrl, f1);
       }
-      const unsigned f0 = lookback_peek(mfl, NW, seg - 1);
-      local_readout();  // overlaps the stores above and the flag poll
-      wait_stores();
-      if (!last && lane == 0) st_relaxed(mfl + NW * seg, FAGG);
-      const int r0 = lookback_find(mfl, NW, seg, FAGG, FINC, p.ctrl, f0);
       // Fold the carries of segments r0 .. seg-1 (M <- diag(prod f) M + local
       // state), FB aggregates per round trip.
 #pragma unroll

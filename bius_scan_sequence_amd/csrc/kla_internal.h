@@ -41,6 +41,7 @@ struct FwdParams {
   int cwidth;
   int nheads, T, nseg;
   int H;              // heads per batch row (indexes theta / sigma2)
+  int mskip;          // a segment whose predecessor's inclusive mean is already out publishes no aggregate
   unsigned* ctrl;     // workspace control words
   unsigned* hdone;    // [kDoneCounters] segments done with their flags, per head group
   unsigned* pflag;    // [nheads*nseg][2] precision-carry flags, one per carry wave

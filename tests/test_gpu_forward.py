@@ -170,6 +170,31 @@ def test_deterministic_bitwise():
     say("[ok] determinism")
 
 
+def test_many_heads_skipped_aggregates_deterministic():
+    """With 128 or more heads a segment whose predecessor's inclusive mean is
+    already out publishes no aggregate.  Results stay bitwise repeatable and
+    match the oracle (two sampled heads)."""
+    import torch
+    import bius_scan_sequence_amd as K
+    say("[case] many heads: B=2 H=80 T=700 d=64 bf16 seed=77")
+    x = KI.make_forward_inputs("lm45m_bf16", B=2, H=80, T=700, seed=77)
+    xd = to_dev(x)
+    names = ("q", "k", "v", "log_decay", "proc_noise", "val_prec")
+    first = K.forward(*(xd[n] for n in names))
+    for _ in range(4):
+        again = K.forward(*(xd[n] for n in names))
+        torch.cuda.synchronize()
+        for a, b in zip(first, again):
+            assert torch.equal(a, b)
+    for b, h in ((0, 3), (1, 77)):
+        xs = {n: x[n][b:b + 1, h:h + 1] for n in names}
+        xs["dtype"] = "bf16"
+        ref = oracle_forward(xs)
+        got = tuple(t[b:b + 1, h:h + 1].float().cpu().numpy() for t in first)
+        check_forward(xs, got, ref, "bf16")
+    say("[ok] many heads")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_extreme_decay_exact_path(dt):
     """Chunks whose decay over a half chunk underflows 2^-64 on some channel
