@@ -193,3 +193,54 @@ def test_decode_batch256_full_size():
     got = gpu_step(xd, lam, M, inplace=True)
     ref = kla_decode_step_f64(*(x[n] for n in NAMES), x["lam"], x["M"])
     check_step("decode batch256", x, got, ref)
+
+
+def test_decode_steps_replayed_from_a_graph():
+    """A generation loop of decode steps captured once in a HIP graph (state
+    updated in place, per-token outputs into fixed buffers) and replayed three
+    times, with eager work between the replays, gives each time exactly the
+    eager loop's outputs and final state."""
+    import torch
+    import bius_scan_sequence_amd as K
+    B, H, T, dk, dv = 4, 8, 12, 64, 64
+    say(f"[case] decode graph replay: B={B} H={H} T={T} d={dk} bf16")
+    w = KI.workload("lm180m_bf16")
+    x = KI.make_forward_inputs(w, B=B, H=H, T=T, dk=dk, dv=dv, seed=8500, dtype="bf16")
+    rng = np.random.default_rng(8500)
+    x["lambda0"] = (0.5 + rng.random((B, H, dk))).astype(np.float32)
+    x["M0"] = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    xd = to_dev(x)
+    toks = [{n: xd[n][:, :, t].contiguous() for n in NAMES} for t in range(T)]
+    # Eager reference.
+    lam, M = xd["lambda0"].clone(), xd["M0"].clone()
+    ref_y = []
+    for t in range(T):
+        y, lam, M = K.decode_step(*(toks[t][n] for n in NAMES), lam, M)
+        ref_y.append(y.clone())
+    torch.cuda.synchronize()
+    ref_lam, ref_M = lam.clone(), M.clone()
+    # Captured loop over fixed buffers.
+    glam, gM = xd["lambda0"].clone(), xd["M0"].clone()
+    ys = [torch.empty((B, H, dv), dtype=torch.bfloat16, device="cuda") for _ in range(T)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the default stream, as graph capture wants
+        K.decode_step(*(toks[0][n] for n in NAMES), glam, gM, out=(ys[0], glam, gM))
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t in range(T):
+            K.decode_step(*(toks[t][n] for n in NAMES), glam, gM, out=(ys[t], glam, gM))
+    for rep in range(3):
+        glam.copy_(xd["lambda0"])
+        gM.copy_(xd["M0"])
+        for y in ys:
+            y.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t in range(T):
+            assert torch.equal(ys[t], ref_y[t]), f"replay {rep}, token {t}"
+        assert torch.equal(glam, ref_lam) and torch.equal(gM, ref_M), f"replay {rep}, state"
+        _ = (xd["q"].float() * 2).sum().item()  # eager work between replays
+    say("[ok] decode graph replay")
