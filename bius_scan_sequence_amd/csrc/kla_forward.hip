@@ -531,15 +531,16 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   if constexpr (MODE == kPrologue) {
     // q, k, v are SiLU(conv) of the raw projections.  The raw tiles go to LDS
     // once (xk in the proc_noise slot, which this mode leaves free; xq and xv
-    // in their own slots), with the three rows before the segment beside
-    // them.  After a barrier every thread forms its units of k into k's slot
-    // (the walks need it); q and v are formed during the precision carry by
-    // the waves that do not carry (section 2), and the chunk aggregates go to
-    // the proc_noise slot meanwhile.
+    // in their own slots, written after the aggregate walk as in the other
+    // modes), with the three rows before the segment beside them.  After a
+    // barrier every thread forms its units of k into k's slot (the walks need
+    // it); q and v are formed during the precision carry by the waves that do
+    // not carry (section 2), and the chunk aggregates go to the proc_noise
+    // slot meanwhile.
     In* const hk = s.halo + 3 * DK;
+    load_tile<In, L, DK, NT>(bq, static_cast<const In*>(p.q) + offk, nvalid, tid);
+    load_tile<In, L, DV, NT>(bv, static_cast<const In*>(p.v) + offv, nvalid, tid);
     stage_tile<In, L, DK, NT>(rpn, static_cast<const In*>(p.k) + offk, nvalid, tid);
-    stage_tile<In, L, DK, NT>(rq, static_cast<const In*>(p.q) + offk, nvalid, tid);
-    stage_tile<In, L, DV, NT>(s.v, static_cast<const In*>(p.v) + offv, nvalid, tid);
     stage_halo<In, DK, NT>(hk, static_cast<const In*>(p.k) + offk, t0, tid);
     stage_halo<In, DK, NT>(s.halo, static_cast<const In*>(p.q) + offk, t0, tid);
     stage_halo<In, DV, NT>(s.halo + 6 * DK, static_cast<const In*>(p.v) + offv, t0, tid);
@@ -634,10 +635,8 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
     const Mob Pc = wh ? mob_mul(Pg[k], Pp) : mob_mul(Pp, Pg[k]);
     if (walker && wh == 0) *reinterpret_cast<v4f*>(cagg + (wc * DK + wch + k) * 4) = v4f{Pc.m00, Pc.m01, Pc.m10, Pc.m11};
   }
-  if constexpr (MODE != kPrologue) {
-    store_tile<In, L, DK, NT>(rq, bq, tid);
-    if constexpr (!C::CAGG_IN_V) store_tile<In, L, DV, NT>(s.v, bv, tid);
-  }
+  store_tile<In, L, DK, NT>(rq, bq, tid);
+  if constexpr (MODE == kPrologue || !C::CAGG_IN_V) store_tile<In, L, DV, NT>(s.v, bv, tid);
   __syncthreads();
 
   // ---------------------------------------------------------------- 2. precision carry
