@@ -2,11 +2,12 @@
 
 The kernels are compile-time instances per (d_k, d_v, dtype): 16 width pairs
 x 2 dtypes for each of the forward modes (plain, OU prior, raw projections),
-the per-channel value precision and the backward.  The other GPU tests cover
-a subset of these instances at several lengths; this sweep runs each instance
-once against the float64 oracle at a length that spans two 64-token segments
-and ends in a ragged chunk (T = 83), with a nondefault state in.  Tolerances
-and comparisons are the entry points' own tests'.
+the per-channel value precision, the decode step and the backward.  The other
+GPU tests cover a subset of these instances at several lengths; this sweep
+runs each instance against the float64 oracle once, at a length that spans two
+64-token segments and ends in a ragged chunk (T = 83), with a nondefault state
+in (the decode step: three steps).  Tolerances and comparisons are the entry
+points' own tests'.
 """
 import numpy as np
 import pytest
@@ -101,3 +102,22 @@ def test_backward_every_width(dk, dv, dt):
     got = TB.gpu_backward(to_dev(x), TB.grads_to_dev(gh, dt), state_in=True)
     ref = TB.oracle_backward(x, gh, state_in=True)
     TB.compare(f"backward widths dk={dk} dv={dv} {dt}", x, got, ref, state_in=True)
+
+
+@pytest.mark.parametrize("dk,dv,dt", CASES, ids=IDS)
+def test_decode_step_every_width(dk, dv, dt):
+    """Three decode steps in a row, each against the oracle's step from the
+    oracle's previous state (so an error does not compound)."""
+    import torch
+    from oracle import kla_decode_step_f64
+    import test_gpu_decode as TD
+    seed = _seed(12500, dk, dv, dt)
+    say(f"[case] decode widths dk={dk} dv={dv} {dt}: B={B} H={H} seed={seed}")
+    x = TD.step_inputs(B, H, dk, dv, dt, seed)
+    lam, M = x["lam"], x["M"]
+    for s in range(3):
+        xs = TD.step_inputs(B, H, dk, dv, dt, seed + 100 * (s + 1)) if s else x
+        got = TD.gpu_step(to_dev(xs), torch.from_numpy(lam).cuda(), torch.from_numpy(M).cuda())
+        ref = kla_decode_step_f64(*(xs[n] for n in TD.NAMES), lam, M)
+        TD.check_step(f"decode widths dk={dk} dv={dv} {dt} step {s}", xs, got, ref)
+        lam, M = ref[1].astype(np.float32), ref[2].astype(np.float32)
