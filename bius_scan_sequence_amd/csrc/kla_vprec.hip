@@ -16,20 +16,23 @@
 // is elementwise (VALU), O(T d_k d_v).
 //
 // Decomposition.  One workgroup per (head, block of 8 value columns); thread
-// (ig, jj) owns key channels 4 ig .. 4 ig + 3 of column jj and walks the
-// sequence, four independent element chains per thread.  The precision is
-// kept projectively as lam = n / d (the Möbius form of [KLA-nl] §2):
+// (ig, jj) owns key channels 2 ig and 2 ig + 1 of column jj and walks the
+// sequence, two independent element chains per thread.  (Four chains per
+// thread left one wave per SIMD at B8 H8 d64 and ran about 25% longer.)  The
+// precision is kept projectively as lam = n / d (the Möbius form of [KLA-nl]
+// §2):
 //   d' = pbar n + a^2 d,  n' = n + c d',
 // for which lam^- / lam' = n / n', so f = a n / n' and g = k Lambda^v d' / n'.
 // The mean is kept as its numerator m = M n: M' = f M + g v becomes
 //   m' = a m + k Lambda^v d' v,
 // with no reciprocal on the recursion; the one reciprocal per element and
 // token serves the readout M' = m' / n'.  (n, d, m) are rescaled by one
-// power of two every fourth token (n / d and m / n are unchanged).  Tokens are staged in blocks: the per-(t, i)
-// coefficients (a, a^2, pbar, k, q) once per block in LDS, v and Lambda^v per
-// (t, j).  The readout's sum over key channels is deferred: each thread keeps
-// its four-channel partial per token in LDS, and after the block one thread
-// per (t, j) adds the d_k/4 partials in a fixed order (deterministic).
+// power of two every fourth token (n / d and m / n are unchanged).  Tokens
+// are staged in blocks: the per-(t, i) coefficients (a, a^2, pbar, k, q) once
+// per block in LDS, v and Lambda^v per (t, j).  The readout's sum over key
+// channels is deferred: each thread keeps its two-channel partial per token
+// in LDS, and after the block one thread per (t, j) adds the d_k/2 partials in
+// a fixed order (deterministic).
 #include <type_traits>
 
 #include "kla_device.h"
@@ -38,11 +41,24 @@
 namespace kla {
 
 namespace {
-constexpr int kVR = 4;   // key channels per thread
+constexpr int kVR = 2;   // key channels per thread
 constexpr int kVJB = 8;  // value columns per workgroup
 
 template <int DK>
 constexpr int vprec_tb() { return DK >= 128 ? 16 : 32; }  // tokens per staged block
+
+// R consecutive fp32 values from LDS in one access.
+template <int R>
+__device__ __forceinline__ void lds_vals(const float* src, float (&x)[R]) {
+  if constexpr (R == 4) {
+    const float4 w = *reinterpret_cast<const float4*>(src);
+    x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
+  } else {
+    static_assert(R == 2, "two or four key channels per thread");
+    const float2 w = *reinterpret_cast<const float2*>(src);
+    x[0] = w.x; x[1] = w.y;
+  }
+}
 
 template <int DK, int DV, bool BF16>
 struct alignas(16) VprecSmem {
@@ -72,7 +88,7 @@ __global__ __launch_bounds__(DK / kVR * kVJB) void kla_vprec_kernel(VprecParams 
   const In* vp = static_cast<const In*>(p.vp);
 
   // Element state: precision n/d and mean numerator m = M n, for channels
-  // 4 ig + r of column j.
+  // kVR ig + r of column j.
   float n[kVR], d[kVR], m[kVR];
 #pragma unroll
   for (int r = 0; r < kVR; ++r) {
@@ -140,14 +156,12 @@ __global__ __launch_bounds__(DK / kVR * kVJB) void kla_vprec_kernel(VprecParams 
 #pragma unroll 4
     for (int t = 0; t < TB; ++t) {
       const float vj = s.v[t][jj], Lj = s.L[t][jj];
-      const float4 a4 = *reinterpret_cast<const float4*>(&s.a[t][ig * kVR]);
-      const float4 a24 = *reinterpret_cast<const float4*>(&s.a2[t][ig * kVR]);
-      const float4 p4 = *reinterpret_cast<const float4*>(&s.pn[t][ig * kVR]);
-      const float4 k4 = *reinterpret_cast<const float4*>(&s.k[t][ig * kVR]);
-      const float4 q4 = *reinterpret_cast<const float4*>(&s.q[t][ig * kVR]);
-      const float av[4] = {a4.x, a4.y, a4.z, a4.w}, a2v[4] = {a24.x, a24.y, a24.z, a24.w};
-      const float pv[4] = {p4.x, p4.y, p4.z, p4.w}, kv[4] = {k4.x, k4.y, k4.z, k4.w};
-      const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
+      float av[kVR], a2v[kVR], pv[kVR], kv[kVR], qv[kVR];
+      lds_vals<kVR>(&s.a[t][ig * kVR], av);
+      lds_vals<kVR>(&s.a2[t][ig * kVR], a2v);
+      lds_vals<kVR>(&s.pn[t][ig * kVR], pv);
+      lds_vals<kVR>(&s.k[t][ig * kVR], kv);
+      lds_vals<kVR>(&s.q[t][ig * kVR], qv);
       float part = 0.f;
 #pragma unroll
       for (int r = 0; r < kVR; ++r) {
