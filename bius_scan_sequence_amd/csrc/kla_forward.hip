@@ -239,26 +239,24 @@ __device__ __forceinline__ void load_vals(const float* p, float (&o)[CPT]) {
 // For |u| > 0.5, phi = (1 - a^2) / u with a = e^{-theta dt}, the decay the
 // walk forms anyway (the cancellation in 1 - a^2 costs well under 1e-6
 // relative there); below, the series sum_{n<=7} (-u)^n / (n+1)! (error
-// below u^8/9!, about 1e-8).
-__device__ __forceinline__ void ou_coef(float th, float s2, float dt, float& ld, float& pn) {
+// below u^8/9!, about 1e-8).  Both forms are evaluated and one is selected,
+// so a wave whose lanes fall on both sides runs no branch; the decay a is
+// returned for the walk.
+__device__ __forceinline__ float ou_coef(float th, float s2, float dt, float& ld, float& pn) {
   const float x = th * dt;
   ld = -x;
+  const float a = __expf(ld);
   const float u = 2.f * x;
-  float phi;
-  if (fabsf(u) > 0.5f) {
-    const float a = __expf(ld);
-    phi = (1.f - a * a) * fast_rcp(u);
-  } else {
-    float s = -1.f / 40320.f;                 // (-1)^7 / 8!
-    s = fmaf(u, s, 1.f / 5040.f);
-    s = fmaf(u, s, -1.f / 720.f);
-    s = fmaf(u, s, 1.f / 120.f);
-    s = fmaf(u, s, -1.f / 24.f);
-    s = fmaf(u, s, 1.f / 6.f);
-    s = fmaf(u, s, -0.5f);
-    phi = fmaf(u, s, 1.f);
-  }
+  float s = -1.f / 40320.f;                   // (-1)^7 / 8!
+  s = fmaf(u, s, 1.f / 5040.f);
+  s = fmaf(u, s, -1.f / 720.f);
+  s = fmaf(u, s, 1.f / 120.f);
+  s = fmaf(u, s, -1.f / 24.f);
+  s = fmaf(u, s, 1.f / 6.f);
+  s = fmaf(u, s, -0.5f);
+  const float phi = fabsf(u) > 0.5f ? (1.f - a * a) * fast_rcp(u) : fmaf(u, s, 1.f);
   pn = s2 * dt * phi;
+  return a;
 }
 
 // Input modes of the kernel: log_decay and proc_noise given per token
@@ -440,8 +438,9 @@ __device__ __forceinline__ void conv_chunk(float (&out)[16], const In* x, int st
 // precision.
 template <int MODE, int CPT, typename In>
 __device__ __forceinline__ void coef_vals(const In* rld, const In* rpn, const In* rvp, const float (&th)[CPT],
-                                          const float (&s2)[CPT], bool tv, float (&ldv)[CPT], float (&pnv)[CPT],
+                                          const float (&s2)[CPT], bool tv, float (&av)[CPT], float (&pnv)[CPT],
                                           float (&vpv)[CPT]) {
+  float ldv[CPT];
   load_vals<CPT>(rvp, vpv);
   if constexpr (MODE == kPrologue) {
 #pragma unroll
@@ -454,11 +453,13 @@ __device__ __forceinline__ void coef_vals(const In* rld, const In* rpn, const In
     for (int k = 0; k < CPT; ++k) {
       float d = dt[k];
       if constexpr (MODE == kPrologue) d = tv ? softplus_f(d) : 0.f;
-      ou_coef(th[k], s2[k], d, ldv[k], pnv[k]);
+      av[k] = ou_coef(th[k], s2[k], d, ldv[k], pnv[k]);
     }
   } else {
     load_vals<CPT>(rld, ldv);
     load_vals<CPT>(rpn, pnv);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) av[k] = __expf(ldv[k]);
   }
 }
 
@@ -604,13 +605,13 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int x = (wt0 + e) * DK + wch;
-      float kk[CPT], vpv[CPT], ldv[CPT], pnv[CPT];
+      float kk[CPT], vpv[CPT], av[CPT], pnv[CPT];
       load_vals<CPT>(rk + x, kk);
-      coef_vals<MODE, CPT>(rld + x, rpn + x, rvp + x, th, s2, wt0 + e < nvalid, ldv, pnv, vpv);
+      coef_vals<MODE, CPT>(rld + x, rpn + x, rvp + x, th, s2, wt0 + e < nvalid, av, pnv, vpv);
 #pragma unroll
       for (int k = 0; k < CPT; ++k) {
         const float kv = kk[k] * vpv[k];
-        const float a = __expf(ldv[k]);
+        const float a = av[k];
         const float c = kk[k] * kv;
         if constexpr (C::KEEP) {
           ca[e][k] = a;
@@ -778,13 +779,12 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
           kv[k] = ckv[e][k];
         }
       } else {
-        float kk[CPT], vpv[CPT], ldv[CPT];
+        float kk[CPT], vpv[CPT];
         load_vals<CPT>(rk + x, kk);
-        coef_vals<MODE, CPT>(rld + x, rpn + x, rvp + x, th, s2, t < nvalid, ldv, pnv, vpv);
+        coef_vals<MODE, CPT>(rld + x, rpn + x, rvp + x, th, s2, t < nvalid, a, pnv, vpv);
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
           kv[k] = kk[k] * vpv[k];
-          a[k] = __expf(ldv[k]);
           c[k] = kk[k] * kv[k];
         }
       }
@@ -965,7 +965,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int t = cc * 16 + e;
-        float kk = 0.f, ldv = 0.f, pnv = 0.f, vpv = 0.f, qv = 0.f;
+        float kk = 0.f, ldv = 0.f, pnv = 0.f, vpv = 0.f, qv = 0.f, a = 1.f;
         if (t < nvalid) {
           const size_t gx = ((size_t)head * T + t0 + t) * DK + tid;
           ldv = to_f32(static_cast<const In*>(p.ld)[gx]);
@@ -980,13 +980,13 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
             qv = to_f32(static_cast<const In*>(p.q)[gx]);
           }
           if constexpr (OU) {
-            ou_coef(th1, s21, ldv, ldv, pnv);
+            a = ou_coef(th1, s21, ldv, ldv, pnv);
           } else {
             pnv = to_f32(static_cast<const In*>(p.pn)[gx]);
+            a = __expf(ldv);
           }
         }
         const float kv = kk * vpv;
-        const float a = __expf(ldv);
         float lam_pred;
         const float lam_new = lam_step(lam, a * a, pnv, kk * kv, lam_pred);
         const float inv = fast_rcp(lam_new);
