@@ -533,11 +533,11 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
     // q, k, v are SiLU(conv) of the raw projections.  The raw tiles go to LDS
     // once (xk in the proc_noise slot, which this mode leaves free; xq and xv
     // in their own slots, written after the aggregate walk as in the other
-    // modes), with the three rows before the segment beside them.  After a
-    // barrier every thread forms its units of k into k's slot (the walks need
-    // it); q and v are formed during the precision carry by the waves that do
-    // not carry (section 2), and the chunk aggregates go to the proc_noise
-    // slot meanwhile.
+    // modes), with the three rows before the segment beside them.  The
+    // walkers form k from the raw rows as they start the aggregate walk
+    // (section 1); q and v are formed during the precision carry by the waves
+    // that do not carry (section 2).  k itself is never stored, so the chunk
+    // aggregates go to k's slot.
     In* const hk = s.halo + 3 * DK;
     load_tile<In, L, DK, NT>(bq, static_cast<const In*>(p.q) + offk, nvalid, tid);
     load_tile<In, L, DV, NT>(bv, static_cast<const In*>(p.v) + offv, nvalid, tid);
@@ -547,12 +547,6 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
     stage_halo<In, DV, NT>(s.halo + 6 * DK, static_cast<const In*>(p.v) + offv, t0, tid);
     stage_tile<In, L, DK, NT>(rld, static_cast<const In*>(p.ld) + offk, nvalid, tid);  // raw step length
     stage_tile<In, L, DK, NT>(rvp, static_cast<const In*>(p.vp) + offk, nvalid, tid);  // raw value precision
-    __syncthreads();
-    const int hh = head % p.H, W = p.cwidth;
-    uint4 bk[UK];
-    conv_lds<In, L, DK, NT>(bk, rpn, hk, nvalid, p.cw[1] + (size_t)hh * DK * W,
-                            p.cb[1] ? p.cb[1] + (size_t)hh * DK : nullptr, W, tid);
-    store_tile<In, L, DK, NT>(rk, bk, tid);
   } else {
     load_tile<In, L, DK, NT>(bq, static_cast<const In*>(p.q) + offk, nvalid, tid);
     load_tile<In, L, DV, NT>(bv, static_cast<const In*>(p.v) + offv, nvalid, tid);
@@ -570,8 +564,8 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   constexpr int PW = (DK + 63) / 64;  // precision carry waves
   const bool pwave = wave < PW, pch = tid < DK;
   // Chunk 2x2 aggregates: in v's space (or the spare operand area); with the
-  // prologue in the proc_noise slot, since raw xv waits in v's space.
-  float* const cagg = MODE == kPrologue ? reinterpret_cast<float*>(rpn) : s.cagg();
+  // prologue in k's slot, since raw xv goes to v's space before the carry.
+  float* const cagg = MODE == kPrologue ? reinterpret_cast<float*>(rk) : s.cagg();
   unsigned long long early = 0ull;
   if (pwave && pch && seg > 0) early = ld_record(p.pinc + (hb + seg - 1) * DK + tid);
 
@@ -598,6 +592,37 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   }
   constexpr int KT = C::KEEP ? 8 : 1;
   float ca[KT][CPT], cpn[KT][CPT], cc2[KT][CPT], ckv[KT][CPT];  // a, pbar, c, k*Lambda^v
+  // Prologue: each walker forms k for its own tokens and channels from the
+  // staged raw xk (rows before the segment in the halo), with conv_lds's
+  // instructions, so the values equal those of the exact path bit for bit.
+  // k is never stored: the gate walk keeps what it needs in registers, or
+  // (more than 16 token-channels per walker) forms k again the same way.
+  float kact[MODE == kPrologue ? 8 : 1][CPT];
+  auto walker_k = [&]() {
+    if constexpr (MODE == kPrologue) {
+      const In* const hk = s.halo + 3 * DK;
+      const int hh = head % p.H;
+      float ws[CPT][4], bs[CPT];
+      conv_slots<CPT>(p.cw[1] + (size_t)hh * DK * p.cwidth, p.cb[1] ? p.cb[1] + (size_t)hh * DK : nullptr, p.cwidth,
+                      wch, ws, bs);
+      float win[11][CPT];  // raw rows wt0 - 3 .. wt0 + 7 (rows past nvalid are staged as zero)
+#pragma unroll
+      for (int i = 0; i < 11; ++i) {
+        const int r = wt0 - 3 + i;
+        load_vals<CPT>(r >= 0 ? rpn + r * DK + wch : hk + (r + 3) * DK + wch, win[i]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+          float acc = bs[k];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc = fmaf(ws[k][j], win[e + j][k], acc);
+          kact[e][k] = wt0 + e < nvalid ? to_f32(from_f32<In>(silu_f(acc))) : 0.f;
+        }
+    }
+  };
+  if (walker) walker_k();
   Mob Pg[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) Pg[k] = mob_identity();
@@ -606,7 +631,12 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
     for (int e = 0; e < 8; ++e) {
       const int x = (wt0 + e) * DK + wch;
       float kk[CPT], vpv[CPT], av[CPT], pnv[CPT];
-      load_vals<CPT>(rk + x, kk);
+      if constexpr (MODE == kPrologue) {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) kk[k] = kact[e][k];
+      } else {
+        load_vals<CPT>(rk + x, kk);
+      }
       coef_vals<MODE, CPT>(rld + x, rpn + x, rvp + x, th, s2, wt0 + e < nvalid, av, pnv, vpv);
 #pragma unroll
       for (int k = 0; k < CPT; ++k) {
@@ -751,6 +781,9 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   // n / n', f = a n / n' and g = k Lambda^v d' / n'.  The recursion carries
   // two FMAs per token and no reciprocal; one reciprocal per token serves the
   // gates.  (n, d) are rescaled by a power of two every fourth token.
+  if constexpr (MODE == kPrologue && !C::KEEP) {
+    if (walker) walker_k();  // raw xk is still staged
+  }
   auto walk = [&](auto with_path) {
     constexpr bool PATH = decltype(with_path)::value;
     float pn_[CPT], pd_[CPT], cp[CPT];
@@ -780,7 +813,12 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
         }
       } else {
         float kk[CPT], vpv[CPT];
-        load_vals<CPT>(rk + x, kk);
+        if constexpr (MODE == kPrologue) {
+#pragma unroll
+          for (int k = 0; k < CPT; ++k) kk[k] = kact[e][k];
+        } else {
+          load_vals<CPT>(rk + x, kk);
+        }
         coef_vals<MODE, CPT>(rld + x, rpn + x, rvp + x, th, s2, t < nvalid, a, pnv, vpv);
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
