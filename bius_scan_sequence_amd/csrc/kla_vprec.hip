@@ -15,7 +15,7 @@
 // The gates differ per element, so there is no chunked matrix form: the work
 // is elementwise (VALU), O(T d_k d_v).
 //
-// Decomposition.  One workgroup per (head, block of 8 value columns); thread
+// Decomposition.  One workgroup per (head, block of 16 value columns); thread
 // (ig, jj) owns key channels 2 ig and 2 ig + 1 of column jj and walks the
 // sequence, two independent element chains per thread.  (Four chains per
 // thread left one wave per SIMD at B8 H8 d64 and ran about 25% longer.)  The
@@ -28,7 +28,7 @@
 // with no reciprocal on the recursion; the one reciprocal per element and
 // token serves the readout M' = m' / n'.  (n, d, m) are rescaled by one
 // power of two every fourth token (n / d and m / n are unchanged).  Tokens
-// are staged in blocks: the per-(t, i) coefficients (a, a^2, pbar, k, q) once
+// are staged in blocks: the per-(t, i) coefficients (a, pbar, k, q) once
 // per block in LDS, v and Lambda^v per (t, j).  The readout's sum over key
 // channels is deferred: each thread keeps its two-channel partial per token
 // in LDS, and after the block one thread per (t, j) adds the d_k/2 partials in
@@ -42,7 +42,7 @@ namespace kla {
 
 namespace {
 constexpr int kVR = 2;   // key channels per thread
-constexpr int kVJB = 8;  // value columns per workgroup
+constexpr int kVJB = 16;  // value columns per workgroup
 
 template <int DK>
 constexpr int vprec_tb() { return DK >= 128 ? 16 : 32; }  // tokens per staged block
@@ -63,7 +63,7 @@ __device__ __forceinline__ void lds_vals(const float* src, float (&x)[R]) {
 template <int DK, int DV, bool BF16>
 struct alignas(16) VprecSmem {
   static constexpr int TB = vprec_tb<DK>(), NI = DK / kVR;
-  float a[TB][DK], a2[TB][DK], pn[TB][DK], k[TB][DK], q[TB][DK];
+  float a[TB][DK], pn[TB][DK], k[TB][DK], q[TB][DK];
   float v[TB][kVJB], L[TB][kVJB];
   float part[TB][kVJB][NI + 1];  // padded: the reduction walks NI consecutive words
 };
@@ -137,7 +137,6 @@ __global__ __launch_bounds__(DK / kVR * kVJB) void kla_vprec_kernel(VprecParams 
       if (x < TB * DK) {
         const float av = __expf(to_f32(rld[u]));
         s.a[t][i] = av;
-        s.a2[t][i] = av * av;
         s.pn[t][i] = to_f32(rpn[u]);
         s.k[t][i] = to_f32(rk[u]);
         s.q[t][i] = to_f32(rq[u]);
@@ -158,7 +157,8 @@ __global__ __launch_bounds__(DK / kVR * kVJB) void kla_vprec_kernel(VprecParams 
       const float vj = s.v[t][jj], Lj = s.L[t][jj];
       float av[kVR], a2v[kVR], pv[kVR], kv[kVR], qv[kVR];
       lds_vals<kVR>(&s.a[t][ig * kVR], av);
-      lds_vals<kVR>(&s.a2[t][ig * kVR], a2v);
+#pragma unroll
+      for (int r = 0; r < kVR; ++r) a2v[r] = av[r] * av[r];
       lds_vals<kVR>(&s.pn[t][ig * kVR], pv);
       lds_vals<kVR>(&s.k[t][ig * kVR], kv);
       lds_vals<kVR>(&s.q[t][ig * kVR], qv);
