@@ -23,13 +23,16 @@ __all__ = [
     "kla_forward_workspace_bytes", "kla_forward", "kla_forward_ou", "kla_forward_prologue", "kla_forward_vprec",
     "kla_precision_scan_workspace_bytes",
     "kla_precision_scan", "kla_decode_step", "kla_backward_workspace_bytes", "kla_backward",
-    "kla_workspace_init", "kla_workspace_error", "kla_status_string", "forward", "forward_ou", "forward_prologue",
+    "kla_workspace_init", "kla_workspace_error", "kla_status_string", "KLA_ERR_DEVICE_WAIT", "forward", "forward_ou", "forward_prologue",
     "forward_vprec", "precision_scan",
     "decode_step", "backward", "scan", "Workspace",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkla.so")
 KLA_F32, KLA_BF16 = 0, 1
+# Not a C status: raised (as KlaError) when a call asked to be checked and the
+# workspace's device-side error word is set (a look-back gave up waiting).
+KLA_ERR_DEVICE_WAIT = 100
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python bius_scan_sequence_amd/build.py`")
@@ -60,14 +63,18 @@ lib.kla_backward.argtypes = [_vp] * 6 + [_fp] * 3 + [_vp] + [_fp] * 2 + [_vp] * 
 lib.kla_workspace_init.restype = _i
 lib.kla_workspace_init.argtypes = [_vp, _sz, _vp]
 lib.kla_workspace_error.restype = _i
-lib.kla_workspace_error.argtypes = [_vp, ctypes.POINTER(ctypes.c_int)]
+lib.kla_workspace_error.argtypes = [_vp, ctypes.POINTER(ctypes.c_int), _vp]
 lib.kla_status_string.restype = ctypes.c_char_p
 lib.kla_status_string.argtypes = [_i]
 
 
 class KlaError(RuntimeError):
     def __init__(self, code: int):
-        super().__init__(f"KLA status {code}: {kla_status_string(code)}")
+        if code == KLA_ERR_DEVICE_WAIT:
+            text = "a workgroup gave up waiting for a predecessor's carry; the call's outputs are unspecified"
+        else:
+            text = kla_status_string(code)
+        super().__init__(f"KLA status {code}: {text}")
         self.code = code
 
 
@@ -136,9 +143,9 @@ def kla_workspace_init(workspace, workspace_bytes, stream) -> int:
     return int(lib.kla_workspace_init(workspace, workspace_bytes, stream))
 
 
-def kla_workspace_error(workspace) -> int:
+def kla_workspace_error(workspace, stream=None) -> int:
     out = ctypes.c_int(0)
-    rc = int(lib.kla_workspace_error(workspace, ctypes.byref(out)))
+    rc = int(lib.kla_workspace_error(workspace, ctypes.byref(out), stream))
     if rc:
         raise KlaError(rc)
     return out.value
@@ -179,8 +186,18 @@ class Workspace:
                 raise KlaError(rc)
         return self.buf
 
-    def error(self) -> int:
-        return 0 if self.buf is None else kla_workspace_error(self.buf.data_ptr())
+    def error(self, stream_handle=None) -> int:
+        """The device-side error word (see kla_workspace_error), read after the
+        work queued on `stream_handle` (default: the current stream)."""
+        if self.buf is None:
+            return 0
+        if stream_handle is None:
+            stream_handle = _torch().cuda.current_stream(self.device).cuda_stream
+        return kla_workspace_error(self.buf.data_ptr(), stream_handle)
+
+    def raise_on_error(self, stream_handle=None) -> None:
+        if self.error(stream_handle):
+            raise KlaError(KLA_ERR_DEVICE_WAIT)
 
 
 _ws_lock = threading.Lock()
@@ -211,8 +228,27 @@ def _check(t, name, shape, dtype, device):
         raise ValueError(f"{name}: must be contiguous")
 
 
+def _outputs(out, specs, dev):
+    """Preallocated outputs checked against what the call would allocate
+    (shape, dtype, device, contiguity), or new tensors."""
+    torch = _torch()
+    if out is None:
+        return tuple(torch.empty(shape, dtype=dt, device=dev) for _, shape, dt in specs)
+    out = tuple(out)
+    if len(out) != len(specs):
+        raise ValueError(f"out holds {len(out)} tensors, expected {len(specs)}")
+    for t, (name, shape, dt) in zip(out, specs):
+        _check(t, f"out[{name}]", shape, dt, dev)
+    return out
+
+
+def _checked(ws, stream, check):
+    if check:
+        ws.raise_on_error(stream)
+
+
 def forward(q, k, v, log_decay, proc_noise, val_prec, lambda0=None, M0=None,
-            return_lambda_path=False, workspace: Workspace | None = None, out=None):
+            return_lambda_path=False, workspace: Workspace | None = None, out=None, check=False):
     """KLA forward pass on the current stream.
 
     q, k, log_decay, proc_noise, val_prec: [B,H,T,dk]; v: [B,H,T,dv]; all
@@ -220,7 +256,11 @@ def forward(q, k, v, log_decay, proc_noise, val_prec, lambda0=None, M0=None,
     M0 [B,H,dk,dv] are float32 (None: 1 and 0).  Returns
     (y [B,H,T,dv] input dtype, lambda_T [B,H,dk] f32, M_T [B,H,dk,dv] f32) and
     the f32 precision path [B,H,T,dk] when return_lambda_path.  ``out`` may
-    hold preallocated (y, lambda_T, M_T) tensors.
+    hold preallocated (y, lambda_T, M_T) tensors (the shapes and dtypes it
+    would allocate, contiguous, on the inputs' device).  With ``check`` the
+    call waits for the stream and raises KlaError if a look-back gave up
+    waiting (outputs unspecified); otherwise the device-side error word is
+    readable through ``Workspace.error``.
     """
     torch = _torch()
     B, H, T, dk = k.shape
@@ -240,28 +280,26 @@ def forward(q, k, v, log_decay, proc_noise, val_prec, lambda0=None, M0=None,
         _check(lambda0, "lambda0", (B, H, dk), torch.float32, dev)
     if M0 is not None:
         _check(M0, "M0", (B, H, dk, dv), torch.float32, dev)
-    if out is None:
-        y = torch.empty((B, H, T, dv), dtype=dtype, device=dev)
-        lam_T = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
-        M_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    else:
-        y, lam_T, M_T = out
+    y, lam_T, M_T = _outputs(out, (("y", (B, H, T, dv), dtype), ("lambda_T", (B, H, dk), torch.float32),
+                                   ("M_T", (B, H, dk, dv), torch.float32)), dev)
     lpath = torch.empty((B, H, T, dk), dtype=torch.float32, device=dev) if return_lambda_path else None
     stream = torch.cuda.current_stream(dev).cuda_stream
     need = kla_forward_workspace_bytes(B, H, T, dk, dv)
     if need == 0:
         raise KlaError(2)
-    ws = (workspace or _default_workspace(dev, stream, "forward")).get(need, stream)
+    ws_obj = workspace or _default_workspace(dev, stream, "forward")
+    ws = ws_obj.get(need, stream)
     rc = kla_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(proc_noise), _ptr(val_prec),
                      _ptr(lambda0), _ptr(M0), _ptr(y), _ptr(lam_T), _ptr(M_T), _ptr(lpath),
                      B, H, T, dk, dv, code, ws.data_ptr(), ws.numel(), stream)
     if rc:
         raise KlaError(rc)
+    _checked(ws_obj, stream, check)
     return (y, lam_T, M_T, lpath) if return_lambda_path else (y, lam_T, M_T)
 
 
 def forward_ou(q, k, v, dt, theta, sigma2, val_prec, lambda0=None, M0=None, return_lambda_path=False,
-               workspace: Workspace | None = None, out=None):
+               workspace: Workspace | None = None, out=None, check=False):
     """KLA forward pass with the OU prior in continuous time, on the current stream.
 
     q, k, dt, val_prec: [B,H,T,dk]; v: [B,H,T,dv] (all bfloat16 or all
@@ -283,28 +321,26 @@ def forward_ou(q, k, v, dt, theta, sigma2, val_prec, lambda0=None, M0=None, retu
         _check(lambda0, "lambda0", (B, H, dk), torch.float32, dev)
     if M0 is not None:
         _check(M0, "M0", (B, H, dk, dv), torch.float32, dev)
-    if out is None:
-        y = torch.empty((B, H, T, dv), dtype=dtype, device=dev)
-        lam_T = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
-        M_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    else:
-        y, lam_T, M_T = out
+    y, lam_T, M_T = _outputs(out, (("y", (B, H, T, dv), dtype), ("lambda_T", (B, H, dk), torch.float32),
+                                   ("M_T", (B, H, dk, dv), torch.float32)), dev)
     lpath = torch.empty((B, H, T, dk), dtype=torch.float32, device=dev) if return_lambda_path else None
     stream = torch.cuda.current_stream(dev).cuda_stream
     need = kla_forward_workspace_bytes(B, H, T, dk, dv)
     if need == 0:
         raise KlaError(2)
-    ws = (workspace or _default_workspace(dev, stream, "forward")).get(need, stream)
+    ws_obj = workspace or _default_workspace(dev, stream, "forward")
+    ws = ws_obj.get(need, stream)
     rc = kla_forward_ou(_ptr(q), _ptr(k), _ptr(v), _ptr(dt), _ptr(theta), _ptr(sigma2), _ptr(val_prec),
                         _ptr(lambda0), _ptr(M0), _ptr(y), _ptr(lam_T), _ptr(M_T), _ptr(lpath),
                         B, H, T, dk, dv, code, ws.data_ptr(), ws.numel(), stream)
     if rc:
         raise KlaError(rc)
+    _checked(ws_obj, stream, check)
     return (y, lam_T, M_T, lpath) if return_lambda_path else (y, lam_T, M_T)
 
 
 def forward_prologue(xq, xk, xv, dt_raw, theta, sigma2, vp_raw, conv_w, conv_b=(None, None, None), lambda0=None,
-                     M0=None, return_lambda_path=False, workspace: Workspace | None = None, out=None):
+                     M0=None, return_lambda_path=False, workspace: Workspace | None = None, out=None, check=False):
     """KLA forward pass on raw projections, on the current stream.
 
     xq, xk, dt_raw, vp_raw: [B,H,T,dk]; xv: [B,H,T,dv] (all bfloat16 or all
@@ -337,24 +373,22 @@ def forward_prologue(xq, xk, xv, dt_raw, theta, sigma2, vp_raw, conv_w, conv_b=(
         _check(lambda0, "lambda0", (B, H, dk), torch.float32, dev)
     if M0 is not None:
         _check(M0, "M0", (B, H, dk, dv), torch.float32, dev)
-    if out is None:
-        y = torch.empty((B, H, T, dv), dtype=dtype, device=dev)
-        lam_T = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
-        M_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    else:
-        y, lam_T, M_T = out
+    y, lam_T, M_T = _outputs(out, (("y", (B, H, T, dv), dtype), ("lambda_T", (B, H, dk), torch.float32),
+                                   ("M_T", (B, H, dk, dv), torch.float32)), dev)
     lpath = torch.empty((B, H, T, dk), dtype=torch.float32, device=dev) if return_lambda_path else None
     stream = torch.cuda.current_stream(dev).cuda_stream
     need = kla_forward_workspace_bytes(B, H, T, dk, dv)
     if need == 0:
         raise KlaError(2)
-    ws = (workspace or _default_workspace(dev, stream, "forward")).get(need, stream)
+    ws_obj = workspace or _default_workspace(dev, stream, "forward")
+    ws = ws_obj.get(need, stream)
     rc = kla_forward_prologue(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(dt_raw), _ptr(theta), _ptr(sigma2), _ptr(vp_raw),
                               *(_ptr(w) for w in conv_w), *(_ptr(b) for b in conv_b), W,
                               _ptr(lambda0), _ptr(M0), _ptr(y), _ptr(lam_T), _ptr(M_T), _ptr(lpath),
                               B, H, T, dk, dv, code, ws.data_ptr(), ws.numel(), stream)
     if rc:
         raise KlaError(rc)
+    _checked(ws_obj, stream, check)
     return (y, lam_T, M_T, lpath) if return_lambda_path else (y, lam_T, M_T)
 
 
@@ -378,12 +412,8 @@ def forward_vprec(q, k, v, log_decay, proc_noise, val_prec, lambda0=None, M0=Non
     for name, t in (("lambda0", lambda0), ("M0", M0)):
         if t is not None:
             _check(t, name, (B, H, dk, dv), torch.float32, dev)
-    if out is None:
-        y = torch.empty((B, H, T, dv), dtype=dtype, device=dev)
-        lam_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-        M_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    else:
-        y, lam_T, M_T = out
+    y, lam_T, M_T = _outputs(out, (("y", (B, H, T, dv), dtype), ("lambda_T", (B, H, dk, dv), torch.float32),
+                                   ("M_T", (B, H, dk, dv), torch.float32)), dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     rc = kla_forward_vprec(_ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(proc_noise), _ptr(val_prec),
                            _ptr(lambda0), _ptr(M0), _ptr(y), _ptr(lam_T), _ptr(M_T), B, H, T, dk, dv, code, stream)
@@ -393,11 +423,12 @@ def forward_vprec(q, k, v, log_decay, proc_noise, val_prec, lambda0=None, M0=Non
 
 
 def precision_scan(log_decay, proc_noise, obs_prec, lambda0=None, workspace: Workspace | None = None,
-                   out=None):
+                   out=None, check=False):
     """Precision path of B*H*D independent chains (float32 [B,H,T,D] inputs).
 
     Returns (lambda_path [B,H,T,D], lambda_T [B,H,D]); ``out`` may hold
-    preallocated tensors for both.
+    preallocated tensors for both (checked as ``forward`` checks its).
+    ``check`` as ``forward``.
     """
     torch = _torch()
     B, H, T, D = log_decay.shape
@@ -406,20 +437,19 @@ def precision_scan(log_decay, proc_noise, obs_prec, lambda0=None, workspace: Wor
         _check(t, name, (B, H, T, D), torch.float32, dev)
     if lambda0 is not None:
         _check(lambda0, "lambda0", (B, H, D), torch.float32, dev)
-    if out is None:
-        lpath = torch.empty((B, H, T, D), dtype=torch.float32, device=dev)
-        lam_T = torch.empty((B, H, D), dtype=torch.float32, device=dev)
-    else:
-        lpath, lam_T = out
+    lpath, lam_T = _outputs(out, (("lambda_path", (B, H, T, D), torch.float32),
+                                  ("lambda_T", (B, H, D), torch.float32)), dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     need = kla_precision_scan_workspace_bytes(B, H, T, D)
     if need == 0:
         raise KlaError(1)
-    ws = (workspace or _default_workspace(dev, stream, "precision_scan")).get(need, stream)
+    ws_obj = workspace or _default_workspace(dev, stream, "precision_scan")
+    ws = ws_obj.get(need, stream)
     rc = kla_precision_scan(_ptr(log_decay), _ptr(proc_noise), _ptr(obs_prec), _ptr(lambda0), _ptr(lpath),
                             _ptr(lam_T), B, H, T, D, ws.data_ptr(), ws.numel(), stream)
     if rc:
         raise KlaError(rc)
+    _checked(ws_obj, stream, check)
     return lpath, lam_T
 
 
@@ -452,7 +482,8 @@ def decode_step(q, k, v, log_decay, proc_noise, val_prec, lam=None, M=None, inpl
     if M is not None:
         _check(M, "M", (B, H, dk, dv), torch.float32, dev)
     if out is not None:
-        y, lam_new, M_new = out
+        y, lam_new, M_new = _outputs(out, (("y", (B, H, dv), dtype), ("lam_new", (B, H, dk), torch.float32),
+                                           ("M_new", (B, H, dk, dv), torch.float32)), dev)
     else:
         y = torch.empty((B, H, dv), dtype=dtype, device=dev)
         lam_new = lam if (inplace and lam is not None) else torch.empty((B, H, dk), dtype=torch.float32, device=dev)
@@ -538,6 +569,7 @@ def _scan_function():
             def forward(ctx, q, k, v, log_decay, proc_noise, val_prec, lambda0, M0):
                 y, lam_T, M_T, lpath = forward(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0,
                                                return_lambda_path=True)
+                ctx.ws = _default_workspace(k.device, torch.cuda.current_stream(k.device).cuda_stream, "forward")
                 ctx.save_for_backward(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0, lpath)
                 ctx.has_state = (lambda0 is not None, M0 is not None)
                 return y, lam_T, M_T
@@ -548,6 +580,9 @@ def _scan_function():
                 gy = torch.zeros_like(v) if gy is None else gy.contiguous()
                 glam = None if glam is None else glam.contiguous()
                 gM = None if gM is None else gM.contiguous()
+                # The precision path feeds the gradients: refuse to differentiate
+                # a forward pass whose look-back gave up waiting.
+                ctx.ws.raise_on_error()
                 g = backward(q, k, v, ld, pn, vp, gy, lpath, lambda0, M0, glam, gM)
                 return (*g[:6], g[6] if ctx.has_state[0] else None, g[7] if ctx.has_state[1] else None)
 

@@ -275,7 +275,8 @@ int forward_impl(const char* name, const void* q, const void* k, const void* v, 
   const void* ins[6] = {q, k, v, log_decay, ou ? q : proc_noise, val_prec};
   for (const void* p : ins)
     if (!aligned(p, 16)) return KLA_ERR_INVALID_ARG;
-  if (!aligned(y, esz) || !aligned(lambda_T, 4) || !aligned(M_T, 4)) return KLA_ERR_INVALID_ARG;
+  // y is written in 16-byte units.
+  if (!aligned(y, 16) || !aligned(lambda_T, 4) || !aligned(M_T, 4)) return KLA_ERR_INVALID_ARG;
   if ((lambda0 && !aligned(lambda0, 4)) || (M0 && !aligned(M0, 4)) ||
       (lambda_path && !aligned(lambda_path, 4)))
     return KLA_ERR_INVALID_ARG;
@@ -457,10 +458,14 @@ extern "C" int kla_workspace_init(void* workspace, size_t workspace_bytes, void*
   return e == hipSuccess ? KLA_OK : hip_fail(e, "kla_workspace_init");
 }
 
-extern "C" int kla_workspace_error(const void* workspace, int* error_out) {
+extern "C" int kla_workspace_error(const void* workspace, int* error_out, void* stream) {
   if (!workspace || !error_out || !aligned(workspace, 256)) return KLA_ERR_INVALID_ARG;
+  // Ordered after the work already queued on `stream` (which may be a
+  // non-blocking stream that the null stream does not wait for).
+  hipStream_t st = static_cast<hipStream_t>(stream);
   unsigned w = 0;
-  hipError_t e = hipMemcpy(&w, static_cast<const char*>(workspace) + 4 * kError, 4, hipMemcpyDeviceToHost);
+  hipError_t e = hipMemcpyAsync(&w, static_cast<const char*>(workspace) + 4 * kError, 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return hip_fail(e, "kla_workspace_error");
   *error_out = (int)w;
   return KLA_OK;

@@ -285,10 +285,15 @@ int kla_backward(const void* q, const void* k, const void* v,
  * before its first use.  bytes must be a multiple of 4. */
 int kla_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
-/* Reads (synchronously, with hipMemcpy) the device-side error word of a
- * workspace: 0 = no error; 1 = a workgroup gave up waiting for a predecessor
- * (the outputs of that call are then unspecified).  For tests and debugging. */
-int kla_workspace_error(const void* workspace, int* error_out);
+/* Reads the device-side error word of a workspace, ordered after the work
+ * queued on `stream` (an asynchronous copy on that stream, then a stream
+ * synchronisation): 0 = no error; 1 = a workgroup gave up waiting for a
+ * predecessor's carry after about 2^25 polls (1-2 s): it then went on with
+ * whatever carry it had found, so the y, lambda_T, M_T and lambda_path of
+ * that call are unspecified.  The word is sticky: it stays set for later
+ * calls on the same workspace until kla_workspace_init clears it.  The
+ * Python binding reads it when a call asks for `check=True`. */
+int kla_workspace_error(const void* workspace, int* error_out, void* stream);
 
 /* Static text for a status code; for KLA_ERR_HIP, the last HIP error text
  * recorded on the calling thread. */

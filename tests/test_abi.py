@@ -80,6 +80,7 @@ def fwd(K, **over):
     (dict(dtype=7), UNSUPPORTED),
     (dict(q=A + 2), INVALID), (dict(log_decay=A + 8), INVALID),
     (dict(lambda0=A + 2), INVALID),
+    (dict(y=A + 2), INVALID), (dict(y=A + 8), INVALID),  # y is written in 16-byte units
     (dict(workspace=None), WORKSPACE), (dict(workspace=A + 64), WORKSPACE),
     (dict(workspace_bytes=16), WORKSPACE),
     (dict(B=1 << 16, H=1 << 16, T=1024), INVALID),
@@ -213,3 +214,11 @@ def fwd_vp(K, **over):
 ])
 def test_forward_vprec_rejects(K, over, code):
     assert fwd_vp(K, **over) == code
+
+
+def test_workspace_error_rejects(K):
+    import ctypes
+    out = ctypes.c_int(0)
+    assert K.lib.kla_workspace_error(None, ctypes.byref(out), None) == INVALID
+    assert K.lib.kla_workspace_error(A + 4, ctypes.byref(out), None) == INVALID
+    assert K.lib.kla_workspace_error(A, None, None) == INVALID
