@@ -38,9 +38,10 @@ sys.path.insert(0, ROOT)
 METRIC = "KLA fwd tokens/s (B*H*T) at dk=dv=64,T=2048; % of HBM roofline"
 WORKLOAD = "lm45m_bf16"
 PEAK_HBM_GBS = 8000.0
-KERNEL = "kla_fwd_kernel<64, 64, true, 0>"
+KERNEL = "kla_fwd_run_kernel"  # the run-streaming forward (bf16, d_k = d_v = 64)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kla_fwd_lm45m_bf16_traffic.json")
-SOURCES = ["kla_forward.hip", "kla_device.h", "kla_internal.h"]
+SOURCES = ["kla_forward_run.hip", "kla_device.h", "kla_internal.h"]
+PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense bf16 matrix-core peak of the MI355X (no sparsity)
 NAMES = ("q", "k", "v", "log_decay", "proc_noise", "val_prec")
 
 
@@ -51,6 +52,47 @@ def algorithmic_bytes(B, H, T, dk, dv, esz):
     per_token = (5 * dk + dv) * esz + dv * esz
     state = B * H * (dk + dk * dv) * 4 * 2
     return B * H * T * per_token + state
+
+
+def run_plan(nheads, T, ncu):
+    """Tiles per run and runs per head the library picks for the run-streaming
+    kernel (kla_forward_run.hip, fwd_run_plan): the run count that minimises
+    rounds of workgroups x tiles per workgroup, fewest runs on ties."""
+    ntiles = (T + 63) // 64
+    best, bestn = None, 1
+    for n in range(1, ntiles + 1):
+        r = (ntiles + n - 1) // n
+        if (ntiles + r - 1) // r != n:
+            continue
+        cost = ((nheads * n + ncu - 1) // ncu) * r
+        if best is None or cost < best:
+            best, bestn = cost, n
+    return (ntiles + bestn - 1) // bestn, bestn
+
+
+def mfma_flops(B, H, T, ncu):
+    """Matrix-core flops the run-streaming kernel executes per launch, from its
+    instruction shape: every v_mfma_f32_16x16x32_bf16 is 2*16*16*32 = 16384
+    flops.  Per 16-token chunk, each of the four matrix waves issues 6 for the
+    readout (split state x split Qt), 1 for scores x V and 4 for the state
+    update (split Kt^T x V): 11; one walker wave forms the chunk's causal
+    scores (split Kt x split Qt) with 6.  A run with a predecessor corrects its
+    two held tiles (8 chunks) with 6 more per chunk and matrix wave."""
+    nheads = B * H
+    ntiles = (T + 63) // 64
+    R, nrun = run_plan(nheads, T, ncu)
+    chunks = nheads * ntiles * 4
+    held_runs = nheads * (nrun - 1)
+    held_chunks_per_run = 4 * min(2, R)
+    instrs = chunks * (4 * 11 + 6) + held_runs * held_chunks_per_run * 4 * 6
+    return instrs * 16384, instrs
+
+
+def algorithmic_flops(B, H, T, dk, dv):
+    """Flops of the recurrent form per token: 5 dk dv for the mean update
+    (decay, gated outer product) and readout, plus about 12 dk for the
+    precision recursion and the gates."""
+    return B * H * T * (5 * dk * dv + 12 * dk)
 
 
 def kernel_source_hash():
@@ -89,7 +131,7 @@ def summarize_traffic(fetch_dir, write_dir, out_path=TRAFFIC_FILE):
         for r in rows:
             key = (r["Kernel_Name"], r["Dispatch_Id"])
             tot[key] = tot.get(key, 0.0) + float(r["Counter_Value"])
-        fwd = [v for (k, _), v in tot.items() if "kla_fwd_kernel" in k]
+        fwd = [v for (k, _), v in tot.items() if KERNEL in k]
         ref = [v for (k, _), v in tot.items() if "bfloat16_copy_kernel" in k]
         if not fwd or not ref:
             raise SystemExit(f"no {counter} rows for the forward kernel or the reference cast in {d}")
@@ -562,6 +604,9 @@ def main():
     achieved = abytes / kern_mean_s / 1e9
     traffic = measured_traffic()
     copy_gbs = device_copy_bandwidth(dev, stream)
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    mflops, minstr = mfma_flops(B, H, T, ncu)
+    aflops = algorithmic_flops(B, H, T, dk, dv)
     out = {
         "metric": METRIC,
         "value": tokens / (ms_per_step / 1e3),
@@ -584,7 +629,15 @@ def main():
                      "kernel_ms_mean_eager_events": eager_kern_mean_ms,
                      "kernel_ms_min_eager_events": float(np.min(kern_ms)),
                      "kernel_ms_max_eager_events": float(np.max(kern_ms)),
-                     "device_copy_GBps": copy_gbs, "frac_of_device_copy": achieved / copy_gbs},
+                     "device_copy_GBps": copy_gbs, "frac_of_device_copy": achieved / copy_gbs,
+                     "traffic_ratio": (traffic / abytes) if traffic else None,
+                     "mfma_frac": mflops / kern_mean_s / 1e12 / PEAK_MFMA_BF16_TFLOPS,
+                     "mfma": {"peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                              "executed_flops": mflops, "instructions": minstr,
+                              "achieved": mflops / kern_mean_s / 1e12,
+                              "frac": mflops / kern_mean_s / 1e12 / PEAK_MFMA_BF16_TFLOPS,
+                              "algorithmic_flops": aflops,
+                              "algorithmic_frac": aflops / kern_mean_s / 1e12 / PEAK_MFMA_BF16_TFLOPS}},
         "cpu_baseline": None,
         "launch": {"timed": "eager calls" if args.copy_mb else "one captured HIP graph of the K steps",
                    "eager_ms_per_step": eager_ms_per_step, "eager_value": tokens / (eager_ms_per_step / 1e3)},

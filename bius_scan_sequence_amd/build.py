@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkla.so")
-SOURCES = ["kla_forward.hip", "kla_precision.hip", "kla_decode.hip", "kla_backward.hip", "kla_vprec.hip", "kla_util.hip", "kla_api.hip"]
+SOURCES = ["kla_forward.hip", "kla_forward_run.hip", "kla_precision.hip", "kla_decode.hip", "kla_backward.hip", "kla_vprec.hip", "kla_util.hip", "kla_api.hip"]
 ARCH = os.environ.get("KLA_OFFLOAD_ARCH", "gfx950")
 
 

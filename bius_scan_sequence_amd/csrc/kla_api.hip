@@ -56,6 +56,40 @@ int fwd_nseg(int T, int dk, int dv, bool bf16) {
   return (T + L - 1) / L;
 }
 
+// The run-streaming kernel (kla_forward_run.hip) serves bf16 inputs at
+// d_k = d_v = 64 with log_decay and proc_noise given per token.
+bool fwd_uses_run(int dk, int dv, bool bf16, bool plain) { return bf16 && plain && dk == 64 && dv == 64; }
+
+struct RunLayout {
+  size_t flag, dv, magg, minc, total;
+};
+
+RunLayout run_layout(long long nheads, int nrun) {
+  const size_t slots = (size_t)nheads * nrun;
+  RunLayout l;
+  size_t o = kHeader;
+  o += (size_t)kDoneCounters * 4;  // the fixed done-counter region of every layout (unused here)
+  l.flag = o; o += round256(slots * 4 * 4);
+  l.dv = o; o += round256(slots * 4 * 64 * 4);
+  l.magg = o; o += round256(slots * 4096 * 4);
+  l.minc = o; o += round256(slots * 4096 * 4);
+  l.total = o;
+  return l;
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 struct PscanPlan {
   int ncblocks, nseg, seglen;
   size_t bdone, flag, agg, inc, total;
@@ -237,10 +271,16 @@ extern "C" int kla_backward(const void* q, const void* k, const void* v, const v
 extern "C" size_t kla_forward_workspace_bytes(int B, int H, int T, int dk, int dv) {
   if (!fwd_shape_ok(B, H, T, dk, dv)) return 0;
   // The layout does not depend on the dtype except through the segment
-  // length; size for the shorter segment (more segments) to cover both.
+  // length; size for the shorter segment (more segments) to cover both, and
+  // for the run-streaming kernel at its most runs (one tile each).
   const int nseg = T > 0 ? fwd_nseg(T, dk, dv, false) : 1;
   const int nseg_b = T > 0 ? fwd_nseg(T, dk, dv, true) : 1;
-  return fwd_layout(B, H, T, dk, dv, nseg > nseg_b ? nseg : nseg_b).total;
+  size_t need = fwd_layout(B, H, T, dk, dv, nseg > nseg_b ? nseg : nseg_b).total;
+  if (fwd_uses_run(dk, dv, true, true) && T > 0) {
+    const size_t r = run_layout((long long)B * H, (T + 63) / 64).total;
+    if (r > need) need = r;
+  }
+  return need;
 }
 
 namespace kla {
@@ -291,9 +331,28 @@ int forward_impl(const char* name, const void* q, const void* k, const void* v, 
     return e == hipSuccess ? KLA_OK : hip_fail(e, name);
   }
   const bool bf16 = dtype == KLA_BF16;
+  char* ws = static_cast<char*>(workspace);
+  if (fwd_uses_run(dk, dv, bf16, !ou && !conv_w)) {
+    FwdRunParams r;
+    r.q = static_cast<const uint16_t*>(q); r.k = static_cast<const uint16_t*>(k);
+    r.v = static_cast<const uint16_t*>(v); r.ld = static_cast<const uint16_t*>(log_decay);
+    r.pn = static_cast<const uint16_t*>(proc_noise); r.vp = static_cast<const uint16_t*>(val_prec);
+    r.lam0 = lambda0; r.M0 = M0; r.y = static_cast<uint16_t*>(y); r.lamT = lambda_T; r.MT = M_T;
+    r.lpath = lambda_path;
+    r.nheads = (int)nheads; r.T = T; r.ntiles = (T + 63) / 64;
+    fwd_run_plan(r.nheads, T, device_cus(), r.R, r.nrun);
+    const RunLayout rl = run_layout(nheads, r.nrun);
+    if (workspace_bytes < rl.total) return KLA_ERR_WORKSPACE;
+    r.ctrl = reinterpret_cast<unsigned*>(ws);
+    r.flag = reinterpret_cast<unsigned*>(ws + rl.flag);
+    r.dv = reinterpret_cast<float*>(ws + rl.dv);
+    r.magg = reinterpret_cast<float*>(ws + rl.magg);
+    r.minc = reinterpret_cast<float*>(ws + rl.minc);
+    hipError_t e = launch_forward_run(r, st);
+    return e == hipSuccess ? KLA_OK : hip_fail(e, name);
+  }
   const int nseg = fwd_nseg(T, dk, dv, bf16);
   const FwdLayout l = fwd_layout(B, H, T, dk, dv, nseg);
-  char* ws = static_cast<char*>(workspace);
   FwdParams p;
   p.q = q; p.k = k; p.v = v; p.ld = log_decay; p.pn = ou ? nullptr : proc_noise; p.vp = val_prec;
   p.lam0 = lambda0; p.M0 = M0; p.y = y; p.lamT = lambda_T; p.MT = M_T; p.lpath = lambda_path;

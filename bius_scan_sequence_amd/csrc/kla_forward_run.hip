@@ -1,0 +1,842 @@
+// KLA forward scan for bf16 inputs at d_k = d_v = 64: one workgroup streams a
+// run of consecutive 64-token tiles of one head.
+//
+// Sources: gist.science summaries of arXiv 2602.10743, "Kalman Linear Attention";
+// [KLA-nl] = "Technische Samenvatting: Kalman Linear Attention (KLA)":
+//   §1 "Probabilistische Formulering"      model: OU prior, observation, readout
+//   §2 "Parallelisatie via Möbius-transformaties"  precision equation; associative
+//                                          composition; affine mean recursion
+//   §3 "Niet-lineaire Gating vanuit Onzekerheid"   gates are precision ratios
+//   §4 "Architectuur"                       expanded states never go to HBM
+//
+// Work decomposition.  A head's T tokens are cut into runs of R tiles of 64
+// tokens; one workgroup (512 threads) owns one run and walks its tiles in
+// order, the next tile's inputs in flight in registers while the current one
+// is computed.  Its eight waves have two roles, one tile apart:
+//   walkers (waves 0-3): the precision recursion and the gates of tile j.
+//     Thread (channel, 16-token chunk) composes the 2x2 step matrices of its
+//     chunk; the four chunks of a channel are joined by a scan across lanes;
+//     a second walk from the chunk's entering precision forms the gates,
+//     folded into matrix-core operands referred to the chunk end:
+//       Qt = q cp / cp16,   Kt = g cp16 / cp
+//     (cp = in-chunk cumulative product of the forget gate f, cp16 its value
+//     over the chunk, g the write gate).  The walk is projective (lam = n / d),
+//     so g / cp = k Lambda^v d / (a-product * lam_in) needs no reciprocal of n.
+//     Walker wave w then forms the causal scores of chunk w, S = tril(Qt Kt^T),
+//     once for all four matrix waves, and keeps the decay from the run start.
+//   matrix waves (4-7): wave 4 + c owns value columns 16c..16c+15 of the
+//     state M (a 64 x 16 strip, in registers across the whole run).  Per chunk
+//       W = diag(cp16) M,   y = Qt W + S V,   M <- W + Kt^T V,
+//     on v_mfma_f32_16x16x32_bf16 with split (hi + lo bf16) operands.
+// Carries between runs:
+//   precision: none.  The precision entering a run is a Möbius image of the
+//     one W tokens earlier; the composed map of those W tokens sends every
+//     positive precision into an interval that shrinks geometrically with W
+//     ([KLA-nl] §2: the maps compose associatively; with process noise they
+//     contract).  The run composes the step matrices of the tile before it
+//     (then earlier tiles, until the interval is below fp32 resolution or the
+//     sequence start is reached, where lambda0 is applied exactly).
+//   mean: one decoupled look-back per run (not per tile) over (prod f over
+//     the run, local state), in ticket order.  Until the state entering the
+//     run is known, the outputs of its first two tiles are held in registers
+//     and corrected at the end (y += Qt diag(cp16 * decay from the run start)
+//     M_in); a later tile whose decay from the run start is below 2^-100 on
+//     every channel gets no correction (the entering state is checked to stay
+//     below 2^40, else the error word is set); any other tile first waits for
+//     the entering state.
+// A chunk whose decay falls below 2^-120 on some channel could overflow Qt;
+// it takes an exact per-token path instead (the walkers hand over f and g in
+// fp32).
+#include "kla_device.h"
+#include "kla_internal.h"
+
+namespace kla {
+namespace {
+
+constexpr int RD = 64;     // d_k = d_v
+constexpr int RTL = 64;    // tokens per tile
+constexpr int RNT = 512;   // threads
+constexpr int RHOLD = 2;   // leading tiles of a run held for the entering-mean correction
+constexpr float kTiny = 0x1p-100f;
+constexpr float kMinBig = 0x1p40f;
+
+// Control words in LDS.
+enum RunCtl {
+  cTicket = 0, cEpoch = 1, cWSync = 2, cXSync = 3,
+  cUnsafe = 4,    // [2 tile parities][4 walker waves]: chunks that take the exact path
+  cNotFree = 12,  // [2][4]: some channel's decay from the run start to the tile start above 2^-100
+  cVote = 20      // [4]: window walk not converged
+};
+
+struct alignas(16) RunSmem {
+  unsigned char raw[5][RTL * RD * 2];     // q, k, log_decay, proc_noise, val_prec: [token][channel] bf16
+  unsigned char vb[RTL * RD * 2];         // v: [token][column] bf16
+  unsigned char qop[4][2][RD * RTL * 2];  // Qt hi / lo: [channel][token] bf16 (slots 0, 1: held tiles)
+  unsigned char kop[2][2][RD * RTL * 2];  // Kt hi / lo: [channel][token] bf16
+  unsigned char sop[2][4][64 * 16];       // per chunk: the causal scores as split B operands, 16 bytes per lane
+  float fac[2][4][RD];                    // per chunk: cp16, the decay over the chunk
+  float dtile[2][RD];                     // decay from the run start to the tile start
+  float hfac[RHOLD][4][RD];               // held chunks: cp16 * decay from the run start to the chunk start
+  float dend[RD];                         // decay over the whole run
+  unsigned ctl[32];
+};
+
+// Byte offset of element x (bf16) of row `row` in a [rows][64] bf16 array:
+// each 128-byte row is four 32-byte blocks, permuted by the row's low two
+// bits, so that four consecutive rows read at one column hit different banks.
+__device__ __forceinline__ int swz(int row, int x) {
+  return row * 128 + ((((x >> 4) ^ row) & 3) << 5) + ((x & 15) << 1);
+}
+
+__device__ __forceinline__ float bfv(short x) { return __uint_as_float((uint32_t)(uint16_t)x << 16); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) { return __builtin_bit_cast(uint32_t, bf16x2(a, b)); }
+
+// 16 consecutive fp32 values of one row, as bf16 hi and lo parts (hi =
+// bf16(x), lo = bf16(x - hi)), stored as two 32-byte blocks.
+__device__ __forceinline__ void put_split16(unsigned char* hi, unsigned char* lo, const float (&x)[16]) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const v2s hh = bf16x2(x[2 * k], x[2 * k + 1]);
+    h[k] = __builtin_bit_cast(uint32_t, hh);
+    l[k] = pack_bf16(x[2 * k] - to_f32((uint16_t)hh[0]), x[2 * k + 1] - to_f32((uint16_t)hh[1]));
+  }
+  *reinterpret_cast<uint4*>(hi) = make_uint4(h[0], h[1], h[2], h[3]);
+  *reinterpret_cast<uint4*>(hi + 16) = make_uint4(h[4], h[5], h[6], h[7]);
+  *reinterpret_cast<uint4*>(lo) = make_uint4(l[0], l[1], l[2], l[3]);
+  *reinterpret_cast<uint4*>(lo + 16) = make_uint4(l[4], l[5], l[6], l[7]);
+}
+
+// A barrier among the four waves of one role (walkers or matrix waves),
+// counted in an LDS word: one lane per wave adds one after its earlier LDS
+// accesses completed, and every wave waits for 4 * k arrivals.
+__device__ __forceinline__ void role_sync(unsigned* cnt, unsigned target) {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS accesses are done
+  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  while (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target) __builtin_amdgcn_s_sleep(1);
+}
+
+__device__ __forceinline__ Mob shfl_up_mob(const Mob& m, int d) {
+  return Mob{__shfl_up(m.m00, d, 64), __shfl_up(m.m01, d, 64), __shfl_up(m.m10, d, 64), __shfl_up(m.m11, d, 64)};
+}
+__device__ __forceinline__ Mob shfl_mob(const Mob& m, int src) {
+  return Mob{__shfl(m.m00, src, 64), __shfl(m.m01, src, 64), __shfl(m.m10, src, 64), __shfl(m.m11, src, 64)};
+}
+
+// Lane geometry.  Walkers: wave w (0-3), lane l: chunk g = l / 16 (tokens
+// 16g..16g+15 of the tile), channel ch = 16w + l % 16.  For the matrix-core
+// operands of every wave: G = l / 16, li = l % 16, and the transposing reads
+// take their 8-byte row from (row 4G + li / 4 of a 16-row block, column
+// piece li % 4).
+struct WLane {
+  int g, i, ch, rr, mm;
+};
+
+// The raw values of one array for the walker's 16 tokens, four per
+// transposing read: element r of part sb is token 16g + 4sb + r.
+__device__ __forceinline__ void read_raw16(const unsigned char* arr, const WLane& L, int w, v4s (&o)[4]) {
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) o[sb] = lds_read_tr16(arr + swz(16 * L.g + 4 * sb + L.rr, 16 * w + 4 * L.mm));
+}
+
+// Composes the step matrices of the walker's 16 tokens (predict then update:
+// [[1 + c pb, c a^2], [pb, a^2]], [KLA-nl] §2), keeping (a, pb, c, k Lambda^v)
+// per token for the gate walk when asked.
+template <bool KEEP>
+__device__ __forceinline__ Mob agg_walk16(const RunSmem& s, const WLane& L, int w, float (&ka)[16], float (&kp)[16],
+                                          float (&kc)[16], float (&kv)[16]) {
+  v4s rk[4], rl[4], rp[4], rv[4];
+  read_raw16(s.raw[1], L, w, rk);
+  read_raw16(s.raw[2], L, w, rl);
+  read_raw16(s.raw[3], L, w, rp);
+  read_raw16(s.raw[4], L, w, rv);
+  Mob P = mob_identity();
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int sb = t >> 2, e = t & 3;
+    const float k = bfv(rk[sb][e]), ld = bfv(rl[sb][e]), pb = bfv(rp[sb][e]), vp = bfv(rv[sb][e]);
+    const float a = __expf(ld);
+    const float kvv = k * vp, c = k * kvv;
+    P = mob_step_raw(P, a * a, pb, c);
+    if (e == 3) P = mob_normalize(P);
+    if constexpr (KEEP) {
+      ka[t] = a;
+      kp[t] = pb;
+      kc[t] = c;
+      kv[t] = kvv;
+    }
+  }
+  return P;
+}
+
+// Inclusive scan of the chunk products over the tile's four chunks (lanes
+// 16 apart hold the same channel); returns the product of chunks 0..g and
+// sets `excl` to that of chunks 0..g-1.
+__device__ __forceinline__ Mob scan_chunks(Mob P, int g, Mob& excl) {
+  Mob Q = shfl_up_mob(P, 16);
+  if (g >= 1) P = mob_mul(P, Q);
+  Q = shfl_up_mob(P, 32);
+  if (g >= 2) P = mob_mul(P, Q);
+  excl = shfl_up_mob(P, 16);
+  if (g == 0) excl = mob_identity();
+  return P;
+}
+
+// acc + A B over 64 channels with split operands, A = (Ah, Al) and B = (Bh,
+// Bl) per 16-channel block: hi*hi + lo*hi + hi*lo, blocks paired into one
+// 16x16x32 instruction each (6 instructions).
+__device__ __forceinline__ v4f mma_split64(v4f acc, const v4s (&Ah)[4], const v4s (&Al)[4], const v4s (&Bh)[4],
+                                           const v4s (&Bl)[4]) {
+#pragma unroll
+  for (int kb = 0; kb < 4; kb += 2) {
+    const v8s bh = cat(Bh[kb], Bh[kb + 1]);
+    acc = mma_x32(acc, cat(Ah[kb], Ah[kb + 1]), bh);
+    acc = mma_x32(acc, cat(Al[kb], Al[kb + 1]), bh);
+    acc = mma_x32(acc, cat(Ah[kb], Ah[kb + 1]), cat(Bl[kb], Bl[kb + 1]));
+  }
+  return acc;
+}
+
+// What both roles of a workgroup know about its run.
+struct RunCtx {
+  int tid, lane, wave;
+  int head, run, tb, ntl, T, nrun;
+  size_t hoff;  // element offset of the head in [B,H,T,64] arrays
+  bool last_run;
+  unsigned FAGG, FINC;
+};
+
+// ---------------------------------------------------------------------------
+// Walker waves (0-3): precision scan, gates and causal scores of tile j during
+// step j.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, const RunCtx& x) {
+  const int tid = x.tid, lane = x.lane, w = x.wave, T = x.T, tb = x.tb, ntl = x.ntl;
+  const size_t hoff = x.hoff;
+  WLane L;
+  L.g = lane >> 4;
+  L.i = lane & 15;
+  L.ch = 16 * w + L.i;
+  L.rr = L.i >> 2;
+  L.mm = L.i & 3;
+  // 16-byte units of q, k, ld, pn, vp of one tile: unit tid + 256 (it & 1) of
+  // array it / 2.
+  auto load = [&](int tile, uint4 (&buf)[10], int first) {
+    const int t0 = tile * RTL;
+#pragma unroll
+    for (int it = 0; it < 10; ++it) {
+      if (it < first) continue;
+      const int a = it >> 1, u = tid + 256 * (it & 1), row = u >> 3, xx = (u & 7) << 3;
+      const uint16_t* src = a == 0 ? p.q : a == 1 ? p.k : a == 2 ? p.ld : a == 3 ? p.pn : p.vp;
+      buf[it] = t0 + row < T ? *reinterpret_cast<const uint4*>(src + hoff + (size_t)(t0 + row) * RD + xx)
+                             : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store = [&](const uint4 (&buf)[10], int first) {
+#pragma unroll
+    for (int it = 0; it < 10; ++it) {
+      if (it < first) continue;
+      const int a = it >> 1, u = tid + 256 * (it & 1), row = u >> 3, xx = (u & 7) << 3;
+      *reinterpret_cast<uint4*>(s.raw[a] + swz(row, xx)) = buf[it];
+    }
+  };
+  uint4 pf[10];  // the next tile's units, in flight
+  load(tb, pf, 0);
+  float lam_start = 1.f;
+  const float lam0 = p.lam0 ? p.lam0[(size_t)x.head * RD + L.ch] : 1.f;
+  if (x.run == 0) {
+    lam_start = lam0;
+  } else {
+    // Precision entering the run: compose the step matrices of the tiles
+    // before it, newest first, until the image of (0, inf) under the composed
+    // map is below fp32 resolution on every channel, or down to the sequence
+    // start, where lambda0 is applied.
+    Mob Ptot = mob_identity();
+    int wt = tb - 1;
+    while (true) {
+      {
+        uint4 tmp[10];
+        load(wt, tmp, 2);
+        store(tmp, 2);
+      }
+      __syncthreads();
+      float ka[16], kp[16], kc[16], kv[16];
+      Mob excl;
+      const Mob Pc = scan_chunks(agg_walk16<false>(s, L, w, ka, kp, kc, kv), L.g, excl);
+      const Mob Pw = shfl_mob(Pc, 48 + L.i);  // product over the whole tile
+      Ptot = mob_mul(Ptot, Pw);               // the older tile acts first
+      const float lo = Ptot.m01 * fast_rcp(Ptot.m11), hi = Ptot.m00 * fast_rcp(Ptot.m10);
+      const bool conv = hi - lo <= 0x1p-21f * lo;
+      const unsigned long long bad = __ballot(!conv);
+      if (lane == 0) s.ctl[cVote + w] = bad ? 1u : 0u;
+      __syncthreads();
+      const bool all = (s.ctl[cVote] | s.ctl[cVote + 1] | s.ctl[cVote + 2] | s.ctl[cVote + 3]) == 0u;
+      if (all || wt == 0) {
+        lam_start = mob_apply(Ptot, wt == 0 ? lam0 : 1.f);
+        break;
+      }
+      --wt;
+    }
+  }
+  store(pf, 0);
+  if (ntl > 1) load(tb + 1, pf, 0);
+  __syncthreads();
+
+  unsigned wsync = 0;
+  float dtile = 1.f;  // decay of this channel from the run start to the tile start
+  float* const lp = p.lpath;
+  const int G = L.g, li = L.i, xe = L.rr, xj = L.mm;
+  for (int j = 0; j <= ntl; ++j) {
+    if (j < ntl) {
+      const int tile = tb + j;
+      const int qs = j < RHOLD ? j : RHOLD + (j & 1), ks = j & 1;
+      float ka[16], kp[16], kc[16], kv[16];
+      Mob excl;
+      (void)scan_chunks(agg_walk16<true>(s, L, w, ka, kp, kc, kv), L.g, excl);
+      const float lam_g = mob_apply(excl, lam_start);
+      v4s rq[4];
+      read_raw16(s.raw[0], L, w, rq);
+      // Gate walk, projective: (n, d) starts as (lam_g, 1) and is rescaled by
+      // a power of two every fourth token (sE = 2^-E, sEi = 2^E undo the
+      // scale).  With Ab the product of a over the chunk so far:
+      //   cpg = Ab lam_g / n            (prod of f, since f = a n_prev / n)
+      //   g / cpg = k Lambda^v d / (Ab lam_g)
+      // and the operands, referred to the chunk end, are
+      //   Qt = q cpg / cp16,   Kt = (g / cpg) cp16 = k Lambda^v d / Ab * (cp16 / lam_g),
+      // with cp16 / lam_g = Ab_16 / n_16 formed without lam_g (products stay
+      // inside the fp32 range on every chunk the matrix path takes).
+      float n = lam_g, d = 1.f, Ab = 1.f, sE = 1.f, lsE = lam_g, sEi = 1.f;
+      float qt[16], kt[16];
+      float cp16 = 1.f, kfac = 1.f;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const float a = ka[t];
+        const float d1 = fmaf(kp[t], n, a * a * d);  // d' = pb n + a^2 d (predict)
+        const float n1 = fmaf(kc[t], d1, n);         // n' = n + c d'      (update)
+        const float rn = fast_rcp(n1);
+        Ab *= a;
+        const float abrn = Ab * rn;
+        const float cpg = abrn * lsE;                // prod of f over the chunk so far
+        qt[t] = bfv(rq[t >> 2][t & 3]) * cpg;
+        kt[t] = (kv[t] * d1) * (sEi * fast_rcp(Ab));
+        if (t == 15) {
+          cp16 = cpg;
+          kfac = abrn * sE;
+        }
+        if (lp) {
+          const int tok = tile * RTL + 16 * L.g + t;
+          if (tok < T) lp[hoff + (size_t)tok * RD + L.ch] = n1 * fast_rcp(d1);
+        }
+        n = n1;
+        d = d1;
+        if ((t & 3) == 3) {
+          const int ex = __builtin_amdgcn_frexp_expf(fmaxf(n, d));
+          n = __builtin_amdgcn_ldexpf(n, -ex);
+          d = __builtin_amdgcn_ldexpf(d, -ex);
+          sE = __builtin_amdgcn_ldexpf(sE, -ex);
+          lsE = __builtin_amdgcn_ldexpf(lsE, -ex);
+          sEi = __builtin_amdgcn_ldexpf(sEi, ex);
+        }
+      }
+      // Precision after the tile, for the next tile (from chunk 3's walk).
+      const float lam_end = __shfl(n * fast_rcp(d), 48 + L.i, 64);
+      // The matrix path needs every operand and score of the chunk inside the
+      // fp32 range: the chunk's decay at least 2^-120 on every channel, and
+      // every operand finite.
+      const float r16 = fast_rcp(cp16);
+      float mag = 0.f;  // inf or NaN if an operand left the fp32 range
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        qt[t] *= r16;
+        kt[t] *= kfac;
+        mag += fabsf(qt[t]) + fabsf(kt[t]);
+      }
+      const bool unsafe = !(cp16 >= 0x1p-120f) || !(kfac < 0x1p120f) || !(mag < 0x1p126f);
+      put_split16(s.qop[qs][0] + swz(L.ch, 16 * L.g), s.qop[qs][1] + swz(L.ch, 16 * L.g), qt);
+      put_split16(s.kop[ks][0] + swz(L.ch, 16 * L.g), s.kop[ks][1] + swz(L.ch, 16 * L.g), kt);
+      s.fac[ks][L.g][L.ch] = cp16;
+      // Decay from the run start to each chunk start: an exclusive product
+      // over the tile's chunks, on top of the decay to the tile start.
+      float ip = cp16;
+      {
+        float o = __shfl_up(ip, 16, 64);
+        if (L.g >= 1) ip *= o;
+        o = __shfl_up(ip, 32, 64);
+        if (L.g >= 2) ip *= o;
+      }
+      float ep = __shfl_up(ip, 16, 64);
+      if (L.g == 0) ep = 1.f;
+      if (j < RHOLD) s.hfac[j][L.g][L.ch] = cp16 * (dtile * ep);
+      if (L.g == 0) s.dtile[ks][L.ch] = dtile;
+      const unsigned long long bad = __ballot(unsafe);
+      const unsigned long long notfree = __ballot(!(dtile <= kTiny));
+      if (lane == 0) {
+        unsigned m = 0;
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) m |= ((bad >> (16 * gg)) & 0xffffull) ? (1u << gg) : 0u;
+        s.ctl[cUnsafe + 4 * ks + w] = m;
+        s.ctl[cNotFree + 4 * ks + w] = notfree ? 1u : 0u;
+      }
+      dtile *= __shfl(ip, 48 + L.i, 64);
+      wsync += 4;
+      role_sync(&s.ctl[cWSync], wsync);
+      // Causal scores of chunk w for every matrix wave: S^T[u][t] = Kt_u . Qt_t
+      // (u, t tokens of the chunk; zero where u > t), as split B operands.
+      {
+        const int r = w;
+        v4s Ah[4], Al[4], Bh[4], Bl[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const int off = swz(16 * kb + 4 * G + xe, 16 * r + 4 * xj);
+          Ah[kb] = lds_read_tr16(s.kop[ks][0] + off);
+          Al[kb] = lds_read_tr16(s.kop[ks][1] + off);
+          Bh[kb] = lds_read_tr16(s.qop[qs][0] + off);
+          Bl[kb] = lds_read_tr16(s.qop[qs][1] + off);
+        }
+        v4f S = mma_split64(v4f{0.f, 0.f, 0.f, 0.f}, Ah, Al, Bh, Bl);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * G + e > li) S[e] = 0.f;
+        v4s Sh, Sl;
+        split4(S, Sh, Sl);
+        *reinterpret_cast<v8s*>(s.sop[ks][r] + 16 * lane) = cat(Sh, Sl);
+      }
+      const unsigned um = s.ctl[cUnsafe + 4 * ks] | s.ctl[cUnsafe + 4 * ks + 1] | s.ctl[cUnsafe + 4 * ks + 2] |
+                          s.ctl[cUnsafe + 4 * ks + 3];
+      if ((um >> L.g) & 1u) {
+        // Exact path for this chunk: f and g per token in fp32, in the
+        // chunk's operand bytes (tokens 0-7 in the hi block, 8-15 in lo).
+        float nn = lam_g, dd = 1.f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const float a = ka[t];
+          const float d1 = fmaf(kp[t], nn, a * a * dd);
+          const float n1 = fmaf(kc[t], d1, nn);
+          const float rn = fast_rcp(n1);
+          const int off = swz(L.ch, 16 * L.g) + 4 * (t & 7);
+          *reinterpret_cast<float*>(s.qop[qs][t >> 3] + off) = a * nn * rn;
+          *reinterpret_cast<float*>(s.kop[ks][t >> 3] + off) = kv[t] * d1 * rn;
+          nn = n1;
+          dd = d1;
+          if ((t & 3) == 3) {
+            const int ex = __builtin_amdgcn_frexp_expf(fmaxf(nn, dd));
+            nn = __builtin_amdgcn_ldexpf(nn, -ex);
+            dd = __builtin_amdgcn_ldexpf(dd, -ex);
+          }
+        }
+      }
+      lam_start = lam_end;
+      if (j + 1 < ntl) {
+        store(pf, 0);
+        if (j + 2 < ntl) load(tile + 2, pf, 0);
+      } else {
+        if (L.g == 0) s.dend[L.ch] = dtile;
+        if (x.last_run && L.g == 0) p.lamT[(size_t)x.head * RD + L.ch] = lam_start;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix waves (4-7): wave 4 + c owns value columns 16c..16c+15; tile j-1
+// during step j; the mean carry at the end of the run.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, const RunCtx& x) {
+  const int lane = x.lane, c = x.wave - 4, T = x.T, tb = x.tb, ntl = x.ntl, run = x.run, head = x.head;
+  const int nrun = x.nrun;
+  const size_t hoff = x.hoff;
+  const int G = lane >> 4, li = lane & 15;
+  const int xe = li >> 2, xj = li & 3;  // transposing-read supply row / column piece
+  const int tv = x.tid - 256;
+  uint4 vpf[2];
+  auto v_load = [&](int tile) {
+    const int t0 = tile * RTL;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int u = tv + 256 * it, row = u >> 3, xx = (u & 7) << 3;
+      vpf[it] = t0 + row < T ? *reinterpret_cast<const uint4*>(p.v + hoff + (size_t)(t0 + row) * RD + xx)
+                             : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto v_store = [&]() {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int u = tv + 256 * it, row = u >> 3, xx = (u & 7) << 3;
+      *reinterpret_cast<uint4*>(s.vb + swz(row, xx)) = vpf[it];
+    }
+  };
+  v4f Mst[4];
+  v4f Yh[4 * RHOLD];  // held chunks' y, chunk-major (tile j, chunk r at 4 j + r)
+#pragma unroll
+  for (int k = 0; k < 4 * RHOLD; ++k) Yh[k] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      Mst[rt][e] = (run == 0 && p.M0) ? p.M0[(size_t)head * 4096 + (16 * rt + 4 * G + e) * RD + 16 * c + li] : 0.f;
+  // The state's loads complete here, before the next tile's values are in
+  // flight: no wait inside the chunk loop then stands for them.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  v_load(tb);
+  bool mres = run == 0;  // state entering the run known (and folded into Mst)
+  bool dropped = false;  // some chunk skipped the entering-mean correction
+  const size_t hs = (size_t)head * nrun + run;  // (head, run) slot
+  unsigned* const hflag = p.flag + (size_t)head * nrun * 4 + c;  // flag of run r: hflag[4 r]
+
+  // y of 16 tokens (this wave's 16 columns) as bf16, 8 bytes per lane.
+  auto store_y = [&](int tile, int r, const v4f& Y) {
+    const int tok = tile * RTL + 16 * r + li;
+    if (tok < T) {
+      const uint2 wv = make_uint2(pack_bf16(Y[0], Y[1]), pack_bf16(Y[2], Y[3]));
+      *reinterpret_cast<uint2*>(p.y + hoff + (size_t)tok * RD + 16 * c + 4 * G) = wv;
+    }
+  };
+  // Four consecutive per-channel values of an LDS vector, for rows 16 rt + 4 G
+  // .. + 3 of the state strip.
+  auto lds4 = [&](const float* vec, int rt) { return *reinterpret_cast<const v4f*>(vec + 16 * rt + 4 * G); };
+  // Y + Qt W for the 16 tokens of chunk r of an operand slot (W in the state's
+  // register layout: rows = channels, columns = this wave's value columns).
+  auto readout = [&](v4f Y, const v4f (&W)[4], int qs, int r) {
+    v4s Ah[4], Al[4], Bh[4], Bl[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      split4(W[kb], Ah[kb], Al[kb]);
+      const int off = swz(16 * kb + 4 * G + xe, 16 * r + 4 * xj);
+      Bh[kb] = lds_read_tr16(s.qop[qs][0] + off);
+      Bl[kb] = lds_read_tr16(s.qop[qs][1] + off);
+    }
+    return mma_split64(Y, Ah, Al, Bh, Bl);
+  };
+  // One chunk on the matrix cores: W = diag(cp16) M, y = Qt W + S V,
+  // M <- W + Kt^T V.  Returns y (this wave's columns).
+  auto chunk = [&](int qs, int ks, int r) {
+    v4f W[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) W[rt] = Mst[rt] * lds4(s.fac[ks][r], rt);
+    const v4s Vf = lds_read_tr16(s.vb + swz(16 * r + 4 * G + xe, 16 * c + 4 * xj));
+    const v8s Vb = cat(Vf, Vf);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int off = swz(16 * rt + li, 16 * r + 4 * G);
+      const v4s th = *reinterpret_cast<const v4s*>(s.kop[ks][0] + off);
+      const v4s tl = *reinterpret_cast<const v4s*>(s.kop[ks][1] + off);
+      Mst[rt] = mma_x32(W[rt], cat(th, tl), Vb);
+    }
+    const v8s Sv = *reinterpret_cast<const v8s*>(s.sop[ks][r] + 16 * lane);
+    return readout(mma_x32(v4f{0.f, 0.f, 0.f, 0.f}, Vb, Sv), W, qs, r);
+  };
+  // Entering mean for this wave's strip: look back over the head's earlier
+  // runs and fold their carries forward, M_end(u) = diag(D_u) M_end(u-1) +
+  // Magg_u, with the same instructions whatever run the look-back stops at.
+  auto lookback_mean = [&](v4f (&Min)[4]) {
+    const int r0 = __builtin_amdgcn_readfirstlane(lookback_find(hflag, 4, run, x.FAGG, x.FINC, p.ctrl));
+    const auto rinc = coherent_rsrc(p.minc + ((size_t)head * nrun + r0) * 4096 + c * 1024, 4096);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) Min[rt] = ld_coherent(rinc, (rt * 64 + lane) * 16);
+    for (int u = r0 + 1; u < run; ++u) {
+      const size_t us = (size_t)head * nrun + u;
+      const auto ragg = coherent_rsrc(p.magg + us * 4096 + c * 1024, 4096);
+      const auto rdv = coherent_rsrc(p.dv + (us * 4 + c) * 64, 256);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const v4f a = ld_coherent(ragg, (rt * 64 + lane) * 16);
+        const v4f d = ld_coherent(rdv, (16 * rt + 4 * G) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Min[rt][e] = fmaf(d[e], Min[rt][e], a[e]);
+      }
+    }
+    if (dropped) {
+      // Outputs after the run's held tiles skipped the entering mean where
+      // its decay was below 2^-100: fine while the mean stays below 2^40.
+      float mx = 0.f;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(Min[rt][e]));
+      if (__ballot(!(mx < kMinBig)) && lane == 0) st_relaxed(p.ctrl + kError, 1u);
+    }
+  };
+  // Held chunk k (tile k / 4, chunk k % 4): y += Qt diag(cp16 * decay from
+  // the run start to the chunk start) M_in, stored.
+  auto correct = [&](int k, const v4f& y0, const v4f (&Min)[4]) {
+    const int j = k >> 2, r = k & 3;
+    v4f W[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) W[rt] = Min[rt] * lds4(s.hfac[j][r], rt);
+    store_y(tb + j, r, readout(y0, W, j, r));
+  };
+  // Resolve the entering mean mid-run: fold the predecessors' carries
+  // (M_in), correct the first `nheld` held chunks, and add diag(D) M_in to
+  // the state (D: the decay from the run start to this point).
+  auto resolve_mid = [&](int nheld, const v4f (&D)[4]) {
+    v4f Min[4];
+    lookback_mean(Min);
+#pragma unroll 1
+    for (int k = 0; k < nheld; ++k) {
+      v4f y0;
+      switch (__builtin_amdgcn_readfirstlane(k)) {  // static register indices
+        case 0: y0 = Yh[0]; break;
+        case 1: y0 = Yh[1]; break;
+        case 2: y0 = Yh[2]; break;
+        case 3: y0 = Yh[3]; break;
+        case 4: y0 = Yh[4]; break;
+        case 5: y0 = Yh[5]; break;
+        case 6: y0 = Yh[6]; break;
+        default: y0 = Yh[7]; break;
+      }
+      correct(k, y0, Min);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Mst[rt][e] = fmaf(D[rt][e], Min[rt][e], Mst[rt][e]);
+    mres = true;
+  };
+
+  // The walkers' window walk: the same barriers, and the same exit.
+  if (run > 0) {
+    int wt = tb - 1;
+    while (true) {
+      __syncthreads();
+      __syncthreads();
+      const bool all = (s.ctl[cVote] | s.ctl[cVote + 1] | s.ctl[cVote + 2] | s.ctl[cVote + 3]) == 0u;
+      if (all || wt == 0) break;
+      --wt;
+    }
+  }
+  __syncthreads();
+
+  unsigned xsync = 0;
+  for (int j = 0; j <= ntl; ++j) {
+    if (j >= 1) {
+      const int jt = j - 1, tile = tb + jt;
+      const int qs = jt < RHOLD ? jt : RHOLD + (jt & 1), ks = jt & 1;
+      const unsigned um = s.ctl[cUnsafe + 4 * ks] | s.ctl[cUnsafe + 4 * ks + 1] | s.ctl[cUnsafe + 4 * ks + 2] |
+                          s.ctl[cUnsafe + 4 * ks + 3];
+      const unsigned nf = s.ctl[cNotFree + 4 * ks] | s.ctl[cNotFree + 4 * ks + 1] | s.ctl[cNotFree + 4 * ks + 2] |
+                          s.ctl[cNotFree + 4 * ks + 3];
+      // One decision for the whole tile about the entering mean: hold (the
+      // run's first tiles), drop (the decay from the run start is below
+      // 2^-100 on every channel at the tile start, hence at every chunk
+      // start), or wait for it here.  A tile with a chunk on the exact path
+      // holds only the chunks before it.
+      const bool fast = um == 0u;
+      bool hold_tile = false;
+      if (!mres) {
+        if (jt < RHOLD) {
+          hold_tile = fast;
+        } else if (fast && nf == 0u) {
+          dropped = true;
+        } else {
+          v4f D[4];
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) D[rt] = lds4(s.dtile[ks], rt);
+          resolve_mid(4 * RHOLD, D);
+        }
+      }
+      if (fast) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const v4f Y = chunk(qs, ks, r);
+          if (!hold_tile) {
+            store_y(tile, r, Y);
+          } else if (jt == 0) {
+            Yh[r] = Y;
+          } else {
+            Yh[4 + r] = Y;
+          }
+        }
+      }
+      for (int r = 0; r < 4 && !fast; ++r) {
+        const bool unsafe = (um >> r) & 1u;
+        bool hold = false;
+        if (!mres) {  // a held tile (jt < RHOLD)
+          if (!unsafe) {
+            hold = true;
+          } else {
+            v4f D[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+              D[rt] = lds4(s.dtile[ks], rt);
+              for (int q = 0; q < r; ++q) D[rt] = D[rt] * lds4(s.fac[ks][q], rt);
+            }
+            resolve_mid(4 * jt + r, D);
+          }
+        }
+        if (!unsafe) {
+          const v4f Y = chunk(qs, ks, r);
+          if (hold) {
+            const int idx = 4 * jt + r;
+#pragma unroll
+            for (int k = 0; k < 4 * RHOLD; ++k)
+              if (k == idx) Yh[k] = Y;
+          } else {
+            store_y(tile, r, Y);
+          }
+        } else {
+          // Exact per-token path (the state here is the true state).
+          for (int t = 0; t < 16; ++t) {
+            const int tok = tile * RTL + 16 * r + t;
+            float qv[16];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+              uint2 qw = make_uint2(0, 0);
+              if (tok < T) qw = *reinterpret_cast<const uint2*>(p.q + hoff + (size_t)tok * RD + 16 * rt + 4 * G);
+              qv[4 * rt + 0] = __uint_as_float(qw.x << 16);
+              qv[4 * rt + 1] = __uint_as_float(qw.x & 0xffff0000u);
+              qv[4 * rt + 2] = __uint_as_float(qw.y << 16);
+              qv[4 * rt + 3] = __uint_as_float(qw.y & 0xffff0000u);
+            }
+            const float vv = bfv(*reinterpret_cast<const short*>(s.vb + swz(16 * r + t, 16 * c + li)));
+            float part = 0.f;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int off = swz(16 * rt + 4 * G + e, 16 * r) + 4 * (t & 7);
+                const float f = *reinterpret_cast<const float*>(s.qop[qs][t >> 3] + off);
+                const float gg = *reinterpret_cast<const float*>(s.kop[ks][t >> 3] + off);
+                Mst[rt][e] = fmaf(f, Mst[rt][e], gg * vv);
+                part = fmaf(qv[4 * rt + e], Mst[rt][e], part);
+              }
+            part += __shfl_xor(part, 16, 64);
+            part += __shfl_xor(part, 32, 64);
+            if (G == 0 && tok < T) p.y[hoff + (size_t)tok * RD + 16 * c + li] = bf16_rne(part);
+          }
+        }
+      }
+    }
+    if (j < ntl) {
+      xsync += 4;
+      role_sync(&s.ctl[cXSync], xsync);
+      v_store();
+      if (j + 1 < ntl) v_load(tb + j + 1);
+    }
+    __syncthreads();
+  }
+
+  // End of the run: the mean carry.
+  if (!mres) {
+    v4f D[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) D[rt] = lds4(s.dend, rt);
+    // Publish the run's aggregate (prod f over the run, local state) unless
+    // the predecessor's inclusive carry is already out or nothing follows.
+    const unsigned fprev = ld_relaxed(hflag + 4 * (run - 1));
+    if (fprev != x.FINC && !x.last_run) {
+      const auto ragg = coherent_rsrc(p.magg + hs * 4096 + c * 1024, 4096);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) st_coherent(ragg, (rt * 64 + lane) * 16, Mst[rt]);
+      if (li == 0) {
+        const auto rdv = coherent_rsrc(p.dv + (hs * 4 + c) * 64, 256);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) st_coherent(rdv, (16 * rt + 4 * G) * 4, D[rt]);
+      }
+      wait_stores();
+      if (lane == 0) st_relaxed(hflag + 4 * run, x.FAGG);
+    }
+    v4f Min[4];
+    lookback_mean(Min);
+    if (ntl >= RHOLD) {
+#pragma unroll
+      for (int k = 0; k < 4 * RHOLD; ++k) correct(k, Yh[k], Min);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) correct(k, Yh[k], Min);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Mst[rt][e] = fmaf(D[rt][e], Min[rt][e], Mst[rt][e]);
+  }
+  if (!x.last_run) {
+    const auto rinc = coherent_rsrc(p.minc + hs * 4096 + c * 1024, 4096);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) st_coherent(rinc, (rt * 64 + lane) * 16, Mst[rt]);
+    wait_stores();
+    if (lane == 0) st_relaxed(hflag + 4 * run, x.FINC);
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p.MT[(size_t)head * 4096 + (16 * rt + 4 * G + e) * RD + 16 * c + li] = Mst[rt][e];
+  }
+}
+
+}  // namespace
+
+// Eight waves share four SIMDs: two waves per SIMD, 256 registers per lane.
+__global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
+  __shared__ RunSmem s;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    s.ctl[cTicket] = __hip_atomic_fetch_add(p.ctrl + kTicket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s.ctl[cEpoch] = p.nrun > 1 ? ld_relaxed(p.ctrl + kEpoch) : 0u;
+    s.ctl[cWSync] = 0u;
+    s.ctl[cXSync] = 0u;
+  }
+  __syncthreads();
+  // Ticket order is run-major, so every run a workgroup waits on holds a
+  // smaller ticket and started earlier.
+  RunCtx x;
+  const unsigned ticket = s.ctl[cTicket];
+  const unsigned epoch = s.ctl[cEpoch];
+  x.tid = tid;
+  x.lane = tid & 63;
+  x.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  x.FAGG = 2u * epoch + 2u;
+  x.FINC = 2u * epoch + 3u;
+  x.nrun = p.nrun;
+  x.run = (int)(ticket / (unsigned)p.nheads);
+  x.head = (int)(ticket % (unsigned)p.nheads);
+  x.T = p.T;
+  x.tb = x.run * p.R;
+  x.ntl = min(x.tb + p.R, p.ntiles) - x.tb;
+  x.hoff = (size_t)x.head * p.T * RD;
+  x.last_run = x.run == p.nrun - 1;
+  if (x.wave < 4)
+    walker_role(p, s, x);
+  else
+    matrix_role(p, s, x);
+  __syncthreads();
+  // Count the workgroup done; the last one resets the ticket and the counter
+  // and advances the call epoch (the flags of the next call differ).
+  if (tid == 0) {
+    const unsigned ng = (unsigned)p.nheads * (unsigned)p.nrun;
+    if (__hip_atomic_fetch_add(p.ctrl + kGroupsDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ng - 1) {
+      st_relaxed(p.ctrl + kTicket, 0u);
+      st_relaxed(p.ctrl + kGroupsDone, 0u);
+      if (p.nrun > 1) st_relaxed(p.ctrl + kEpoch, epoch + 1u);
+    }
+  }
+}
+
+// Runs per head: the count that minimises (rounds of workgroups) x (tiles
+// per workgroup) on `ncu` compute units, fewest runs on ties.
+void fwd_run_plan(int nheads, int T, int ncu, int& R, int& nrun) {
+  const int ntiles = (T + RTL - 1) / RTL;
+  long long best = -1;
+  int bestn = 1;
+  for (int n = 1; n <= ntiles; ++n) {
+    const int r = (ntiles + n - 1) / n;
+    const int nr = (ntiles + r - 1) / r;  // runs actually needed at r tiles each
+    if (nr != n) continue;
+    const long long rounds = ((long long)nheads * n + ncu - 1) / ncu;
+    const long long cost = rounds * r;
+    if (best < 0 || cost < best) {
+      best = cost;
+      bestn = n;
+    }
+  }
+  nrun = bestn;
+  R = (ntiles + bestn - 1) / bestn;
+}
+
+hipError_t launch_forward_run(const FwdRunParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(kla_fwd_run_kernel, dim3((unsigned)p.nheads * (unsigned)p.nrun), dim3(RNT), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace kla

@@ -6,8 +6,9 @@
 
 namespace kla {
 
-// Control words at the head of every workspace (32-bit each).
-enum CtrlWord { kError = 3 };
+// Control words at the head of every workspace (32-bit each).  Words 0 and 1
+// hold the call epoch and the groups-done counter (kla_device.h).
+enum CtrlWord { kError = 3, kTicket = 4 };
 
 // Done counters: a fixed region of kDoneCounters words right after the
 // 256-byte header, at the same place and of the same size whatever the call's
@@ -143,6 +144,32 @@ struct VprecParams {
   float* MT;
   int T;
 };
+
+// The run-streaming forward kernel (bf16, d_k = d_v = 64, log_decay and
+// proc_noise given per token): one workgroup per (head, run of R tiles of 64
+// tokens), taken in ticket order.
+struct FwdRunParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* ld;  // log_decay
+  const uint16_t* pn;  // proc_noise
+  const uint16_t* vp;  // val_prec
+  const float* lam0;   // nullable
+  const float* M0;     // nullable
+  uint16_t* y;
+  float* lamT;
+  float* MT;
+  float* lpath;        // nullable
+  int nheads, T, ntiles, R, nrun;
+  unsigned* ctrl;      // workspace control words (epoch, groups done, error, ticket)
+  unsigned* flag;      // [nheads*nrun][4] mean-carry flags, one per matrix wave
+  float* dv;           // [nheads*nrun][4][64] prod of forget gates over the run (a copy per wave)
+  float* magg;         // [nheads*nrun][4096] local mean state of the run (fragment order)
+  float* minc;         // [nheads*nrun][4096] mean state after the run (fragment order)
+};
+void fwd_run_plan(int nheads, int T, int ncu, int& R, int& nrun);
+hipError_t launch_forward_run(const FwdRunParams& p, hipStream_t stream);
 
 int fwd_segment_len(int dk, int dv, bool bf16);
 hipError_t launch_forward(const FwdParams& p, int dk, int dv, bool bf16, hipStream_t stream);
