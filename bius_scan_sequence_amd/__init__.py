@@ -20,7 +20,8 @@ import threading
 
 __all__ = [
     "LIB_PATH", "lib", "KLA_F32", "KLA_BF16", "KlaError",
-    "kla_forward_workspace_bytes", "kla_forward", "kla_forward_ou", "kla_forward_prologue", "kla_forward_vprec",
+    "kla_forward_workspace_bytes", "kla_forward", "kla_forward_noalloc", "KLA_NOALLOC_SCRATCH_BYTES",
+    "kla_forward_ou", "kla_forward_prologue", "kla_forward_vprec",
     "kla_precision_scan_workspace_bytes",
     "kla_precision_scan", "kla_decode_step", "kla_backward_workspace_bytes", "kla_backward",
     "kla_workspace_init", "kla_workspace_error", "kla_status_string", "KLA_ERR_DEVICE_WAIT", "forward", "forward_ou", "forward_prologue",
@@ -30,6 +31,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkla.so")
 KLA_F32, KLA_BF16 = 0, 1
+KLA_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/kla.h
 # Not a C status: raised (as KlaError) when a call asked to be checked and the
 # workspace's device-side error word is set (a look-back gave up waiting).
 KLA_ERR_DEVICE_WAIT = 100
@@ -43,6 +45,8 @@ lib.kla_forward_workspace_bytes.restype = _sz
 lib.kla_forward_workspace_bytes.argtypes = [_i] * 5
 lib.kla_forward.restype = _i
 lib.kla_forward.argtypes = [_vp] * 6 + [_fp] * 2 + [_vp] + [_fp] * 3 + [_i] * 6 + [_vp, _sz, _vp]
+lib.kla_forward_noalloc.restype = _i
+lib.kla_forward_noalloc.argtypes = [_vp] * 6 + [_fp] * 2 + [_vp] + [_fp] * 3 + [_i] * 6 + [_vp, _vp]
 lib.kla_forward_ou.restype = _i
 lib.kla_forward_ou.argtypes = [_vp] * 4 + [_fp] * 2 + [_vp] + [_fp] * 2 + [_vp] + [_fp] * 3 + [_i] * 6 + [_vp, _sz, _vp]
 lib.kla_forward_prologue.restype = _i
@@ -88,6 +92,12 @@ def kla_forward(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0, y, lambda
     return int(lib.kla_forward(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0, y, lambda_T,
                                M_T, lambda_path, B, H, T, dk, dv, dtype, workspace, workspace_bytes,
                                stream))
+
+
+def kla_forward_noalloc(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0, y, lambda_T, M_T,
+                        lambda_path, B, H, T, dk, dv, dtype, error_flag, stream) -> int:
+    return int(lib.kla_forward_noalloc(q, k, v, log_decay, proc_noise, val_prec, lambda0, M0, y, lambda_T,
+                                       M_T, lambda_path, B, H, T, dk, dv, dtype, error_flag, stream))
 
 
 def kla_forward_ou(q, k, v, dt, theta, sigma2, val_prec, lambda0, M0, y, lambda_T, M_T, lambda_path,

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/kla.h"
 #include "kla_internal.h"
 
@@ -285,6 +287,38 @@ extern "C" size_t kla_forward_workspace_bytes(int B, int H, int T, int dk, int d
 
 namespace kla {
 namespace {
+// The scratch array of kla_forward_noalloc.  In host code `scratch` names a
+// host-side stand-in, not the device array: only the address looked up with
+// hipGetSymbolAddress (per device, with that device current) is ever passed
+// to a kernel or a fill.
+constexpr size_t kScratchBytes = KLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "kla_forward_noalloc (hipGetDevice)");
+  if (dev < 0 || dev >= kMaxDevices) return KLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "kla_forward_noalloc (hipGetSymbolAddress)");
+    if (!ptr || !aligned(ptr, 256)) return hip_fail(hipErrorInvalidSymbol, "kla_forward_noalloc (scratch address)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KLA_OK;
+}
+}  // namespace
+}  // namespace kla
+
+namespace kla {
+namespace {
 // kla_forward and kla_forward_ou: with theta == NULL, log_decay and
 // proc_noise are per-token inputs; otherwise `log_decay` holds the OU step
 // length and theta, sigma2 ([H][dk]) the rate and diffusion.
@@ -293,7 +327,7 @@ int forward_impl(const char* name, const void* q, const void* k, const void* v, 
                  const float* lambda0, const float* M0, void* y, float* lambda_T, float* M_T, float* lambda_path,
                  int B, int H, int T, int dk, int dv, int dtype, void* workspace, size_t workspace_bytes,
                  void* stream, const float* const* conv_w = nullptr, const float* const* conv_b = nullptr,
-                 int conv_width = 0) {
+                 int conv_width = 0, bool lib_scratch = false) {
   if (B < 1 || H < 1 || T < 0) return KLA_ERR_INVALID_ARG;
   if (!lambda_T || !M_T) return KLA_ERR_INVALID_ARG;
   const bool ou = theta != nullptr;
@@ -320,9 +354,13 @@ int forward_impl(const char* name, const void* q, const void* k, const void* v, 
   if ((lambda0 && !aligned(lambda0, 4)) || (M0 && !aligned(M0, 4)) ||
       (lambda_path && !aligned(lambda_path, 4)))
     return KLA_ERR_INVALID_ARG;
-  if (!workspace || !aligned(workspace, 256)) return KLA_ERR_WORKSPACE;
-  const size_t need = kla_forward_workspace_bytes(B, H, T, dk, dv);
-  if (workspace_bytes < need) return KLA_ERR_WORKSPACE;
+  // A caller's workspace covers every layout of the shape; the library's
+  // scratch array (kla_forward_noalloc) is checked against the layout this
+  // call takes, below.
+  if (!lib_scratch) {
+    if (!workspace || !aligned(workspace, 256)) return KLA_ERR_WORKSPACE;
+    if (workspace_bytes < kla_forward_workspace_bytes(B, H, T, dk, dv)) return KLA_ERR_WORKSPACE;
+  }
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const long long nheads = (long long)B * H;
@@ -332,6 +370,20 @@ int forward_impl(const char* name, const void* q, const void* k, const void* v, 
   }
   const bool bf16 = dtype == KLA_BF16;
   char* ws = static_cast<char*>(workspace);
+  // The workspace of the layout this call takes: the caller's (checked above
+  // against every layout), or the library's scratch array, checked here before
+  // its address is looked up, its first `clear` bytes (control words,
+  // counters, flags) then zero-filled on the stream.
+  auto take = [&](size_t need, size_t clear) -> int {
+    if (!lib_scratch) return workspace_bytes < need ? KLA_ERR_WORKSPACE : KLA_OK;
+    if (need > kScratchBytes) return KLA_ERR_TOO_LARGE;
+    void* base = nullptr;
+    const int rc = scratch_address(&base);
+    if (rc != KLA_OK) return rc;
+    ws = static_cast<char*>(base);
+    hipError_t e = launch_fill_zero(ws, clear / 4, st);
+    return e == hipSuccess ? KLA_OK : hip_fail(e, name);
+  };
   if (fwd_uses_run(dk, dv, bf16, !ou && !conv_w)) {
     FwdRunParams r;
     r.q = static_cast<const uint16_t*>(q); r.k = static_cast<const uint16_t*>(k);
@@ -342,7 +394,8 @@ int forward_impl(const char* name, const void* q, const void* k, const void* v, 
     r.nheads = (int)nheads; r.T = T; r.ntiles = (T + 63) / 64;
     fwd_run_plan(r.nheads, T, device_cus(), r.R, r.nrun);
     const RunLayout rl = run_layout(nheads, r.nrun);
-    if (workspace_bytes < rl.total) return KLA_ERR_WORKSPACE;
+    const int rc = take(rl.total, rl.dv);
+    if (rc != KLA_OK) return rc;
     r.ctrl = reinterpret_cast<unsigned*>(ws);
     r.flag = reinterpret_cast<unsigned*>(ws + rl.flag);
     r.dv = reinterpret_cast<float*>(ws + rl.dv);
@@ -353,6 +406,8 @@ int forward_impl(const char* name, const void* q, const void* k, const void* v, 
   }
   const int nseg = fwd_nseg(T, dk, dv, bf16);
   const FwdLayout l = fwd_layout(B, H, T, dk, dv, nseg);
+  const int rc = take(l.total, l.mF);  // the flagged precision records (pinc) lie before mF
+  if (rc != KLA_OK) return rc;
   FwdParams p;
   p.q = q; p.k = k; p.v = v; p.ld = log_decay; p.pn = ou ? nullptr : proc_noise; p.vp = val_prec;
   p.lam0 = lambda0; p.M0 = M0; p.y = y; p.lamT = lambda_T; p.MT = M_T; p.lpath = lambda_path;
@@ -389,6 +444,24 @@ extern "C" int kla_forward(const void* q, const void* k, const void* v, const vo
                            size_t workspace_bytes, void* stream) {
   return forward_impl("kla_forward", q, k, v, log_decay, proc_noise, nullptr, nullptr, val_prec, lambda0, M0, y,
                       lambda_T, M_T, lambda_path, B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream);
+}
+
+
+extern "C" int kla_forward_noalloc(const void* q, const void* k, const void* v, const void* log_decay,
+                                   const void* proc_noise, const void* val_prec, const float* lambda0,
+                                   const float* M0, void* y, float* lambda_T, float* M_T, float* lambda_path,
+                                   int B, int H, int T, int dk, int dv, int dtype, int* error_flag, void* stream) {
+  if (error_flag && !aligned(error_flag, 4)) return KLA_ERR_INVALID_ARG;
+  int rc = forward_impl("kla_forward_noalloc", q, k, v, log_decay, proc_noise, nullptr, nullptr, val_prec, lambda0, M0,
+                        y, lambda_T, M_T, lambda_path, B, H, T, dk, dv, dtype, nullptr, 0, stream, nullptr, nullptr, 0,
+                        true);
+  if (rc != KLA_OK || !error_flag) return rc;
+  // T = 0 launches no scan and leaves the scratch alone: its error word is 0.
+  void* ws = nullptr;
+  if (T > 0 && (rc = scratch_address(&ws)) != KLA_OK) return rc;
+  const unsigned* word = T > 0 ? static_cast<const unsigned*>(ws) + kError : nullptr;
+  hipError_t e = launch_word_copy(word, error_flag, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KLA_OK : hip_fail(e, "kla_forward_noalloc (error word)");
 }
 
 extern "C" int kla_forward_ou(const void* q, const void* k, const void* v, const void* dt, const float* theta,
@@ -537,6 +610,8 @@ extern "C" const char* kla_status_string(int status) {
     case KLA_ERR_UNSUPPORTED: return "unsupported d_k/d_v or dtype (widths 16, 32, 64, 128; dtype f32 or bf16)";
     case KLA_ERR_WORKSPACE: return "workspace missing, not 256-byte aligned, or smaller than required";
     case KLA_ERR_HIP: return g_hip_error[0] ? g_hip_error : "HIP error";
+    case KLA_ERR_TOO_LARGE:
+      return "kla_forward_noalloc: the shape needs more than KLA_NOALLOC_SCRATCH_BYTES of scratch (use kla_forward)";
     default: return "unknown status";
   }
 }

@@ -182,6 +182,8 @@ hipError_t launch_backward_empty(const float* dlamT, const float* dMT, float* dl
                                  long long nl, long long nm, hipStream_t stream);
 hipError_t launch_vprec(const VprecParams& p, long long nheads, int dk, int dv, bool bf16, hipStream_t stream);
 hipError_t launch_fill_zero(void* ptr, size_t words, hipStream_t stream);
+// *dst = *src (0 when src is null), one thread.
+hipError_t launch_word_copy(const unsigned* src, int* dst, hipStream_t stream);
 hipError_t launch_state_copy(const float* lam0, const float* M0, float* lamT, float* MT,
                              long long nl, long long nm, hipStream_t stream);
 

@@ -9,6 +9,10 @@ __global__ void kla_fill_zero_kernel(unsigned* p, size_t words) {
     p[i] = 0u;
 }
 
+__global__ void kla_word_copy_kernel(const unsigned* src, int* dst) {
+  if (threadIdx.x == 0) *dst = src ? (int)*src : 0;
+}
+
 // T = 0: the scan is the identity, so the state out equals the state in
 // (lambda0 = 1 and M0 = 0 when not given).
 __global__ void kla_state_copy_kernel(const float* lam0, const float* M0, float* lamT, float* MT,
@@ -32,6 +36,11 @@ static unsigned grid_for(long long n) {
 hipError_t launch_fill_zero(void* ptr, size_t words, hipStream_t stream) {
   hipLaunchKernelGGL(kla_fill_zero_kernel, dim3(grid_for((long long)words)), dim3(256), 0, stream,
                      static_cast<unsigned*>(ptr), words);
+  return hipGetLastError();
+}
+
+hipError_t launch_word_copy(const unsigned* src, int* dst, hipStream_t stream) {
+  hipLaunchKernelGGL(kla_word_copy_kernel, dim3(1), dim3(64), 0, stream, src, dst);
   return hipGetLastError();
 }
 

@@ -25,8 +25,11 @@
  *
  * Conventions for every entry point:
  *   - All tensors are dense, row-major, on the device, not aliased (unless an
- *     entry point allows it), and owned by the caller.  The library never allocates or frees device memory and
- *     never synchronises; work is enqueued on `stream` (a hipStream_t; NULL
+ *     entry point allows it), and owned by the caller.  The library never
+ *     allocates or frees device memory (the scratch array of
+ *     kla_forward_noalloc is part of its code object, placed by the HIP
+ *     loader) and never synchronises (kla_workspace_error excepted); work is
+ *     enqueued on `stream` (a hipStream_t; NULL
  *     means the default stream) and the call returns without waiting.
  *   - Argument validation happens on the host before any HIP call; a
  *     non-zero return means nothing was enqueued.  KLA_ERR_HIP means a launch
@@ -63,7 +66,9 @@ typedef enum {
   KLA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, bad alignment        */
   KLA_ERR_UNSUPPORTED = 2,  /* d_k / d_v / dtype outside the supported set  */
   KLA_ERR_WORKSPACE = 3,    /* workspace missing, misaligned or too small   */
-  KLA_ERR_HIP = 4           /* a HIP call failed (text via status string)   */
+  KLA_ERR_HIP = 4,          /* a HIP call failed (text via status string)   */
+  KLA_ERR_TOO_LARGE = 5     /* kla_forward_noalloc: the shape needs more
+                               than KLA_NOALLOC_SCRATCH_BYTES of scratch    */
 } kla_status;
 
 /* Bytes of workspace kla_forward needs for this shape; 0 if the shape is
@@ -101,6 +106,46 @@ int kla_forward(const void* q, const void* k, const void* v,
                 void* y, float* lambda_T, float* M_T, float* lambda_path,
                 int B, int H, int T, int dk, int dv, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the device scratch array inside the library that
+ * kla_forward_noalloc works in (one array per GPU). */
+#define KLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * kla_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Inputs, outputs, shapes, dtypes, alignment rules and results are those of
+ * kla_forward (same kernels); the workspace is replaced by a file-scope device
+ * array of KLA_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU,
+ * which that GPU holds until the process ends.  The call allocates nothing
+ * (no hipMalloc / hipFree, no allocating library routine).
+ *
+ * Per call, on `stream`: a fill kernel clears the scratch's control words and
+ * carry flags (every call starts as on a freshly initialised workspace), then
+ * kla_forward's kernels run.  The first call on a device looks up the array's
+ * device address there (that device current) and keeps it for later calls.
+ *
+ * error_flag: nullable device pointer to one int (4-byte aligned).  When
+ *   given, a one-thread kernel on `stream` writes this call's device error
+ *   word there after the call's kernels: 0 = none, 1 = as kla_workspace_error
+ *   reports it (a look-back gave up waiting; outputs unspecified).
+ * Errors: KLA_ERR_TOO_LARGE when this shape needs more scratch than
+ *   KLA_NOALLOC_SCRATCH_BYTES (nothing is launched; kla_forward with a
+ *   workspace serves every shape); otherwise as kla_forward.  The run kernel
+ *   (bf16, dk = dv = 64) fits up to about 1900 (head, run) pairs, e.g.
+ *   B*H = 64 at T = 2048 or B*H = 192 at T = 2048; the segment kernels fit
+ *   B*H*ceil(T/64) up to about 2000 at dk = dv = 64.
+ * Concurrency: every call on one GPU shares that GPU's array and leaves its
+ *   contents behind: calls that overlap on one GPU (two streams, two threads,
+ *   two graph replays in flight) race and give unspecified results.  Order
+ *   them on one stream.
+ */
+int kla_forward_noalloc(const void* q, const void* k, const void* v,
+                        const void* log_decay, const void* proc_noise, const void* val_prec,
+                        const float* lambda0, const float* M0,
+                        void* y, float* lambda_T, float* M_T, float* lambda_path,
+                        int B, int H, int T, int dk, int dv, int dtype,
+                        int* error_flag, void* stream);
 
 /*
  * KLA forward pass with the OU prior given in continuous time: the same scan

@@ -222,3 +222,34 @@ def test_workspace_error_rejects(K):
     assert K.lib.kla_workspace_error(None, ctypes.byref(out), None) == INVALID
     assert K.lib.kla_workspace_error(A + 4, ctypes.byref(out), None) == INVALID
     assert K.lib.kla_workspace_error(A, None, None) == INVALID
+
+
+def fwd_na(K, **over):
+    args = dict(q=A, k=A, v=A, log_decay=A, proc_noise=A, val_prec=A, lambda0=None, M0=None,
+                y=A, lambda_T=A, M_T=A, lambda_path=None, B=1, H=1, T=64, dk=16, dv=16, dtype=1,
+                error_flag=None, stream=None)
+    args.update(over)
+    return K.kla_forward_noalloc(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), INVALID), (dict(y=None), INVALID), (dict(M_T=None), INVALID),
+    (dict(B=0), INVALID), (dict(T=-1), INVALID), (dict(dk=48), UNSUPPORTED), (dict(dtype=7), UNSUPPORTED),
+    (dict(q=A + 2), INVALID), (dict(y=A + 8), INVALID), (dict(lambda0=A + 2), INVALID),
+    (dict(error_flag=A + 2), INVALID), (dict(B=1 << 16, H=1 << 16, T=1024), INVALID),
+])
+def test_forward_noalloc_rejects(K, over, code):
+    assert fwd_na(K, **over) == code
+
+
+def test_forward_noalloc_rejects_beyond_scratch(K):
+    """2048 heads at T = 2048 (bf16, d64) need about 69 MB, more than the
+    64 MiB scratch array: KLA_ERR_TOO_LARGE before any launch."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("fake device addresses: run where no GPU is visible (the GPU test uses real tensors)")
+    m = re.search(r"#define KLA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and K.KLA_NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+    rc = fwd_na(K, B=32, H=64, T=2048, dk=64, dv=64)
+    assert rc == 5
+    assert "KLA_NOALLOC_SCRATCH_BYTES" in K.kla_status_string(rc)
