@@ -393,6 +393,7 @@ int forward_impl(const char* name, const void* q, const void* k, const void* v, 
     r.lpath = lambda_path;
     r.nheads = (int)nheads; r.T = T; r.ntiles = (T + 63) / 64;
     fwd_run_plan(r.nheads, T, device_cus(), r.R, r.nrun);
+    r.tgroups = r.nheads % 8 == 0 ? 8 : r.nheads % 4 == 0 ? 4 : r.nheads % 2 == 0 ? 2 : 1;
     const RunLayout rl = run_layout(nheads, r.nrun);
     const int rc = take(rl.total, rl.dv);
     if (rc != KLA_OK) return rc;

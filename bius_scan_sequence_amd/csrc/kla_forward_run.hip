@@ -47,6 +47,8 @@
 // A chunk whose decay falls below 2^-120 on some channel could overflow Qt;
 // it takes an exact per-token path instead (the walkers hand over f and g in
 // fp32).
+#include <type_traits>
+
 #include "kla_device.h"
 #include "kla_internal.h"
 
@@ -71,8 +73,8 @@ enum RunCtl {
 struct alignas(16) RunSmem {
   unsigned char raw[5][RTL * RD * 2];     // q, k, log_decay, proc_noise, val_prec: [token][channel] bf16
   unsigned char vb[RTL * RD * 2];         // v: [token][column] bf16
-  unsigned char qop[4][2][RD * RTL * 2];  // Qt hi / lo: [channel][token] bf16 (slots 0, 1: held tiles)
-  unsigned char kop[2][2][RD * RTL * 2];  // Kt hi / lo: [channel][token] bf16
+  unsigned char qop[4][2][4][RD * 32];    // Qt hi / lo per chunk: [channel][16 tokens] bf16 (slots 0, 1: held tiles)
+  unsigned char kop[2][2][4][RD * 32];    // Kt hi / lo per chunk: [channel][16 tokens] bf16
   unsigned char sop[2][4][64 * 16];       // per chunk: the causal scores as split B operands, 16 bytes per lane
   float fac[2][4][RD];                    // per chunk: cp16, the decay over the chunk
   float dtile[2][RD];                     // decay from the run start to the tile start
@@ -81,20 +83,42 @@ struct alignas(16) RunSmem {
   unsigned ctl[32];
 };
 
-// Byte offset of element x (bf16) of row `row` in a [rows][64] bf16 array:
-// each 128-byte row is four 32-byte blocks, permuted by the row's low two
-// bits, so that four consecutive rows read at one column hit different banks.
-__device__ __forceinline__ int swz(int row, int x) {
-  return row * 128 + ((((x >> 4) ^ row) & 3) << 5) + ((x & 15) << 1);
+// LDS layouts.  Every array is addressed in 8-byte pieces (4 bf16); a piece
+// index is permuted by XOR with a few bits of its row so that the accesses
+// of a half-wave (32 lanes, 256 bytes, 64 banks) hit distinct banks; the
+// permutations are even, so 16-byte units stay whole and in order.
+//
+// Raw inputs [64 tokens][64 channels]: the walkers' transposing reads take
+// rows 4b..4b+3 and 16 + 4b..16 + 4b + 3 (two chunks) in one half-wave, so
+// piece p of row r sits at p ^ (4 r1 + 8 r4) (r_i: bit i of the row).
+__device__ __forceinline__ int raw_off(int row, int x) {
+  const int f = (((row >> 1) & 1) << 2) | (((row >> 4) & 1) << 3);
+  return row * 128 + ((((x >> 2) ^ f) & 15) << 3) + ((x & 3) << 1);
 }
+// V [64 tokens][64 columns]: the matrix waves' transposing reads take rows
+// 16r..16r+7 in one half-wave: piece p of row r at p ^ (4 r1 + 8 r2).
+__device__ __forceinline__ int v_off(int row, int x) {
+  const int f = (((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 3);
+  return row * 128 + ((((x >> 2) ^ f) & 15) << 3) + ((x & 3) << 1);
+}
+// Operand chunk arrays [64 channels][16 tokens] (32-byte rows): piece p of
+// channel ch at p ^ 2 ch3.  Transposing reads (eight consecutive channels,
+// four pieces) and plain reads of one piece for 16 consecutive channels are
+// both conflict-free; a chunk's index and a channel block's enter as
+// constant offsets.
+__device__ __forceinline__ int op_off(int ch, int t) {
+  return ch * 32 + ((((t >> 2) ^ (((ch >> 3) & 1) << 1)) & 3) << 3) + ((t & 3) << 1);
+}
+
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bfv(short x) { return __uint_as_float((uint32_t)(uint16_t)x << 16); }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) { return __builtin_bit_cast(uint32_t, bf16x2(a, b)); }
 
-// 16 consecutive fp32 values of one row, as bf16 hi and lo parts (hi =
-// bf16(x), lo = bf16(x - hi)), stored as two 32-byte blocks.
-__device__ __forceinline__ void put_split16(unsigned char* hi, unsigned char* lo, const float (&x)[16]) {
+// The 16 tokens of channel ch in a chunk's operand arrays `hi` and `lo`, as
+// bf16 hi and lo parts (hi = bf16(x), lo = bf16(x - hi)), in 16-byte units.
+__device__ __forceinline__ void put_split16(unsigned char* hi, unsigned char* lo, int ch, const float (&x)[16]) {
   uint32_t h[8], l[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -102,10 +126,11 @@ __device__ __forceinline__ void put_split16(unsigned char* hi, unsigned char* lo
     h[k] = __builtin_bit_cast(uint32_t, hh);
     l[k] = pack_bf16(x[2 * k] - to_f32((uint16_t)hh[0]), x[2 * k + 1] - to_f32((uint16_t)hh[1]));
   }
-  *reinterpret_cast<uint4*>(hi) = make_uint4(h[0], h[1], h[2], h[3]);
-  *reinterpret_cast<uint4*>(hi + 16) = make_uint4(h[4], h[5], h[6], h[7]);
-  *reinterpret_cast<uint4*>(lo) = make_uint4(l[0], l[1], l[2], l[3]);
-  *reinterpret_cast<uint4*>(lo + 16) = make_uint4(l[4], l[5], l[6], l[7]);
+  const int o0 = op_off(ch, 0), o1 = op_off(ch, 8);
+  *reinterpret_cast<uint4*>(hi + o0) = make_uint4(h[0], h[1], h[2], h[3]);
+  *reinterpret_cast<uint4*>(hi + o1) = make_uint4(h[4], h[5], h[6], h[7]);
+  *reinterpret_cast<uint4*>(lo + o0) = make_uint4(l[0], l[1], l[2], l[3]);
+  *reinterpret_cast<uint4*>(lo + o1) = make_uint4(l[4], l[5], l[6], l[7]);
 }
 
 // A barrier among the four waves of one role (walkers or matrix waves),
@@ -137,15 +162,15 @@ struct WLane {
 // transposing read: element r of part sb is token 16g + 4sb + r.
 __device__ __forceinline__ void read_raw16(const unsigned char* arr, const WLane& L, int w, v4s (&o)[4]) {
 #pragma unroll
-  for (int sb = 0; sb < 4; ++sb) o[sb] = lds_read_tr16(arr + swz(16 * L.g + 4 * sb + L.rr, 16 * w + 4 * L.mm));
+  for (int sb = 0; sb < 4; ++sb) o[sb] = lds_read_tr16(arr + raw_off(16 * L.g + 4 * sb + L.rr, 16 * w + 4 * L.mm));
 }
 
 // Composes the step matrices of the walker's 16 tokens (predict then update:
-// [[1 + c pb, c a^2], [pb, a^2]], [KLA-nl] §2), keeping (a, pb, c, k Lambda^v)
-// per token for the gate walk when asked.
+// [[1 + c pb, c a^2], [pb, a^2]], [KLA-nl] §2), keeping (a, a^2, pb, c,
+// k Lambda^v) per token for the gate walk when asked.
 template <bool KEEP>
-__device__ __forceinline__ Mob agg_walk16(const RunSmem& s, const WLane& L, int w, float (&ka)[16], float (&kp)[16],
-                                          float (&kc)[16], float (&kv)[16]) {
+__device__ __forceinline__ Mob agg_walk16(const RunSmem& s, const WLane& L, int w, float (&ka)[16], float (&ka2)[16],
+                                          float (&kp)[16], float (&kc)[16], float (&kv)[16]) {
   v4s rk[4], rl[4], rp[4], rv[4];
   read_raw16(s.raw[1], L, w, rk);
   read_raw16(s.raw[2], L, w, rl);
@@ -157,11 +182,12 @@ __device__ __forceinline__ Mob agg_walk16(const RunSmem& s, const WLane& L, int 
     const int sb = t >> 2, e = t & 3;
     const float k = bfv(rk[sb][e]), ld = bfv(rl[sb][e]), pb = bfv(rp[sb][e]), vp = bfv(rv[sb][e]);
     const float a = __expf(ld);
-    const float kvv = k * vp, c = k * kvv;
-    P = mob_step_raw(P, a * a, pb, c);
+    const float kvv = k * vp, c = k * kvv, a2 = a * a;
+    P = mob_step_raw(P, a2, pb, c);
     if (e == 3) P = mob_normalize(P);
     if constexpr (KEEP) {
       ka[t] = a;
+      ka2[t] = a2;
       kp[t] = pb;
       kc[t] = c;
       kv[t] = kvv;
@@ -238,7 +264,7 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
     for (int it = 0; it < 10; ++it) {
       if (it < first) continue;
       const int a = it >> 1, u = tid + 256 * (it & 1), row = u >> 3, xx = (u & 7) << 3;
-      *reinterpret_cast<uint4*>(s.raw[a] + swz(row, xx)) = buf[it];
+      *reinterpret_cast<uint4*>(s.raw[a] + raw_off(row, xx)) = buf[it];
     }
   };
   uint4 pf[10];  // the next tile's units, in flight
@@ -261,9 +287,9 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
         store(tmp, 2);
       }
       __syncthreads();
-      float ka[16], kp[16], kc[16], kv[16];
+      float ka[16], ka2[16], kp[16], kc[16], kv[16];
       Mob excl;
-      const Mob Pc = scan_chunks(agg_walk16<false>(s, L, w, ka, kp, kc, kv), L.g, excl);
+      const Mob Pc = scan_chunks(agg_walk16<false>(s, L, w, ka, ka2, kp, kc, kv), L.g, excl);
       const Mob Pw = shfl_mob(Pc, 48 + L.i);  // product over the whole tile
       Ptot = mob_mul(Ptot, Pw);               // the older tile acts first
       const float lo = Ptot.m01 * fast_rcp(Ptot.m11), hi = Ptot.m00 * fast_rcp(Ptot.m10);
@@ -291,38 +317,36 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
     if (j < ntl) {
       const int tile = tb + j;
       const int qs = j < RHOLD ? j : RHOLD + (j & 1), ks = j & 1;
-      float ka[16], kp[16], kc[16], kv[16];
+      float ka[16], ka2[16], kp[16], kc[16], kv[16];
       Mob excl;
-      (void)scan_chunks(agg_walk16<true>(s, L, w, ka, kp, kc, kv), L.g, excl);
+      (void)scan_chunks(agg_walk16<true>(s, L, w, ka, ka2, kp, kc, kv), L.g, excl);
       const float lam_g = mob_apply(excl, lam_start);
       v4s rq[4];
       read_raw16(s.raw[0], L, w, rq);
       // Gate walk, projective: (n, d) starts as (lam_g, 1) and is rescaled by
-      // a power of two every fourth token (sE = 2^-E, sEi = 2^E undo the
-      // scale).  With Ab the product of a over the chunk so far:
-      //   cpg = Ab lam_g / n            (prod of f, since f = a n_prev / n)
-      //   g / cpg = k Lambda^v d / (Ab lam_g)
-      // and the operands, referred to the chunk end, are
-      //   Qt = q cpg / cp16,   Kt = (g / cpg) cp16 = k Lambda^v d / Ab * (cp16 / lam_g),
-      // with cp16 / lam_g = Ab_16 / n_16 formed without lam_g (products stay
-      // inside the fp32 range on every chunk the matrix path takes).
-      float n = lam_g, d = 1.f, Ab = 1.f, sE = 1.f, lsE = lam_g, sEi = 1.f;
+      // 2^-ex_g after token group g (tokens 4g..4g+3), so within group g both
+      // carry the scale 2^-E_g, E_g = ex_0 + .. + ex_(g-1).  With Ab the
+      // product of a over the chunk so far (f = a n_prev / n, g = k Lambda^v
+      // d' / n), cp_t = Ab_t lam_g / n_t, and the operands referred to the
+      // chunk end are
+      //   Qt_t = q_t cp_t / cp16 = q_t (Ab_t / n_t) (n_16 / Ab_16),
+      //   Kt_t = g_t cp16 / cp_t = k Lambda^v d'_t (Ab_16 / Ab_t) / n_16:
+      // Qt from this forward pass and one factor per group, Kt from this pass
+      // and a backward (suffix) product of a, both carrying 2^(+-(E_3 - E_g)).
+      float n = lam_g, d = 1.f, Ab = 1.f, n16 = 1.f, rn16 = 1.f;
       float qt[16], kt[16];
-      float cp16 = 1.f, kfac = 1.f;
+      int exg[4];
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        const float a = ka[t];
-        const float d1 = fmaf(kp[t], n, a * a * d);  // d' = pb n + a^2 d (predict)
-        const float n1 = fmaf(kc[t], d1, n);         // n' = n + c d'      (update)
+        const float d1 = fmaf(kp[t], n, ka2[t] * d);  // d' = pb n + a^2 d (predict)
+        const float n1 = fmaf(kc[t], d1, n);          // n' = n + c d'      (update)
         const float rn = fast_rcp(n1);
-        Ab *= a;
-        const float abrn = Ab * rn;
-        const float cpg = abrn * lsE;                // prod of f over the chunk so far
-        qt[t] = bfv(rq[t >> 2][t & 3]) * cpg;
-        kt[t] = (kv[t] * d1) * (sEi * fast_rcp(Ab));
+        Ab *= ka[t];
+        qt[t] = bfv(rq[t >> 2][t & 3]) * (Ab * rn);
+        kt[t] = kv[t] * d1;
         if (t == 15) {
-          cp16 = cpg;
-          kfac = abrn * sE;
+          n16 = n1;
+          rn16 = rn;
         }
         if (lp) {
           const int tok = tile * RTL + 16 * L.g + t;
@@ -334,27 +358,36 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
           const int ex = __builtin_amdgcn_frexp_expf(fmaxf(n, d));
           n = __builtin_amdgcn_ldexpf(n, -ex);
           d = __builtin_amdgcn_ldexpf(d, -ex);
-          sE = __builtin_amdgcn_ldexpf(sE, -ex);
-          lsE = __builtin_amdgcn_ldexpf(lsE, -ex);
-          sEi = __builtin_amdgcn_ldexpf(sEi, ex);
+          exg[t >> 2] = ex;
         }
       }
       // Precision after the tile, for the next tile (from chunk 3's walk).
       const float lam_end = __shfl(n * fast_rcp(d), 48 + L.i, 64);
-      // The matrix path needs every operand and score of the chunk inside the
-      // fp32 range: the chunk's decay at least 2^-120 on every channel, and
-      // every operand finite.
-      const float r16 = fast_rcp(cp16);
-      float mag = 0.f;  // inf or NaN if an operand left the fp32 range
+      const int E3 = exg[0] + exg[1] + exg[2];
+      const float cp16 = __builtin_amdgcn_ldexpf(Ab * rn16 * lam_g, -E3);
+      {
+        float fq = n16 * fast_rcp(Ab);  // group 3
+        float sk = rn16;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        qt[t] *= r16;
-        kt[t] *= kfac;
-        mag += fabsf(qt[t]) + fabsf(kt[t]);
+        for (int t = 15; t >= 0; --t) {
+          qt[t] *= fq;
+          kt[t] *= sk;
+          sk *= ka[t];
+          if ((t & 3) == 0 && t > 0) {
+            fq = __builtin_amdgcn_ldexpf(fq, exg[(t >> 2) - 1]);
+            sk = __builtin_amdgcn_ldexpf(sk, -exg[(t >> 2) - 1]);
+          }
+        }
       }
-      const bool unsafe = !(cp16 >= 0x1p-120f) || !(kfac < 0x1p120f) || !(mag < 0x1p126f);
-      put_split16(s.qop[qs][0] + swz(L.ch, 16 * L.g), s.qop[qs][1] + swz(L.ch, 16 * L.g), qt);
-      put_split16(s.kop[ks][0] + swz(L.ch, 16 * L.g), s.kop[ks][1] + swz(L.ch, 16 * L.g), kt);
+      // The matrix path needs every operand and score of the chunk inside the
+      // fp32 range: the chunk's decay at least 2^-120 on every channel and Qt
+      // finite (Kt is bounded by the write gate).
+      float qmag = 0.f;
+#pragma unroll
+      for (int t = 0; t < 16; t += 2) qmag = fmaxf(qmag, fmaxf(fabsf(qt[t]), fabsf(qt[t + 1])));
+      const bool unsafe = !(cp16 >= 0x1p-120f) || !(qmag < 0x1p126f);
+      put_split16(s.qop[qs][0][L.g], s.qop[qs][1][L.g], L.ch, qt);
+      put_split16(s.kop[ks][0][L.g], s.kop[ks][1][L.g], L.ch, kt);
       s.fac[ks][L.g][L.ch] = cp16;
       // Decay from the run start to each chunk start: an exclusive product
       // over the tile's chunks, on top of the decay to the tile start.
@@ -388,11 +421,11 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
         v4s Ah[4], Al[4], Bh[4], Bl[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          const int off = swz(16 * kb + 4 * G + xe, 16 * r + 4 * xj);
-          Ah[kb] = lds_read_tr16(s.kop[ks][0] + off);
-          Al[kb] = lds_read_tr16(s.kop[ks][1] + off);
-          Bh[kb] = lds_read_tr16(s.qop[qs][0] + off);
-          Bl[kb] = lds_read_tr16(s.qop[qs][1] + off);
+          const int off = op_off(16 * kb + 4 * G + xe, 4 * xj);
+          Ah[kb] = lds_read_tr16(s.kop[ks][0][r] + off);
+          Al[kb] = lds_read_tr16(s.kop[ks][1][r] + off);
+          Bh[kb] = lds_read_tr16(s.qop[qs][0][r] + off);
+          Bl[kb] = lds_read_tr16(s.qop[qs][1][r] + off);
         }
         v4f S = mma_split64(v4f{0.f, 0.f, 0.f, 0.f}, Ah, Al, Bh, Bl);
 #pragma unroll
@@ -414,9 +447,9 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
           const float d1 = fmaf(kp[t], nn, a * a * dd);
           const float n1 = fmaf(kc[t], d1, nn);
           const float rn = fast_rcp(n1);
-          const int off = swz(L.ch, 16 * L.g) + 4 * (t & 7);
-          *reinterpret_cast<float*>(s.qop[qs][t >> 3] + off) = a * nn * rn;
-          *reinterpret_cast<float*>(s.kop[ks][t >> 3] + off) = kv[t] * d1 * rn;
+          const int off = op_off(L.ch, 8 * ((t & 7) >> 2)) + 4 * (t & 3);
+          *reinterpret_cast<float*>(s.qop[qs][t >> 3][L.g] + off) = a * nn * rn;
+          *reinterpret_cast<float*>(s.kop[ks][t >> 3][L.g] + off) = kv[t] * d1 * rn;
           nn = n1;
           dd = d1;
           if ((t & 3) == 3) {
@@ -464,7 +497,7 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int u = tv + 256 * it, row = u >> 3, xx = (u & 7) << 3;
-      *reinterpret_cast<uint4*>(s.vb + swz(row, xx)) = vpf[it];
+      *reinterpret_cast<uint4*>(s.vb + v_off(row, xx)) = vpf[it];
     }
   };
   v4f Mst[4];
@@ -486,12 +519,13 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
   unsigned* const hflag = p.flag + (size_t)head * nrun * 4 + c;  // flag of run r: hflag[4 r]
 
   // y of 16 tokens (this wave's 16 columns) as bf16, 8 bytes per lane.
+  // A buffer store: the hardware drops the tokens at or past T (the head's
+  // record ends there), so no branch splits the chunk loop.
+  const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(p.y + hoff, (short)0, T * RD * 2, 0x00020000);
   auto store_y = [&](int tile, int r, const v4f& Y) {
     const int tok = tile * RTL + 16 * r + li;
-    if (tok < T) {
-      const uint2 wv = make_uint2(pack_bf16(Y[0], Y[1]), pack_bf16(Y[2], Y[3]));
-      *reinterpret_cast<uint2*>(p.y + hoff + (size_t)tok * RD + 16 * c + 4 * G) = wv;
-    }
+    const v2u wv = v2u{pack_bf16(Y[0], Y[1]), pack_bf16(Y[2], Y[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(wv, yrs, tok * (RD * 2) + (16 * c + 4 * G) * 2, 0, 0);
   };
   // Four consecutive per-channel values of an LDS vector, for rows 16 rt + 4 G
   // .. + 3 of the state strip.
@@ -503,9 +537,9 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       split4(W[kb], Ah[kb], Al[kb]);
-      const int off = swz(16 * kb + 4 * G + xe, 16 * r + 4 * xj);
-      Bh[kb] = lds_read_tr16(s.qop[qs][0] + off);
-      Bl[kb] = lds_read_tr16(s.qop[qs][1] + off);
+      const int off = op_off(16 * kb + 4 * G + xe, 4 * xj);
+      Bh[kb] = lds_read_tr16(s.qop[qs][0][r] + off);
+      Bl[kb] = lds_read_tr16(s.qop[qs][1][r] + off);
     }
     return mma_split64(Y, Ah, Al, Bh, Bl);
   };
@@ -515,13 +549,13 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
     v4f W[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) W[rt] = Mst[rt] * lds4(s.fac[ks][r], rt);
-    const v4s Vf = lds_read_tr16(s.vb + swz(16 * r + 4 * G + xe, 16 * c + 4 * xj));
+    const v4s Vf = lds_read_tr16(s.vb + v_off(16 * r + 4 * G + xe, 16 * c + 4 * xj));
     const v8s Vb = cat(Vf, Vf);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      const int off = swz(16 * rt + li, 16 * r + 4 * G);
-      const v4s th = *reinterpret_cast<const v4s*>(s.kop[ks][0] + off);
-      const v4s tl = *reinterpret_cast<const v4s*>(s.kop[ks][1] + off);
+      const int off = op_off(16 * rt + li, 4 * G);
+      const v4s th = *reinterpret_cast<const v4s*>(s.kop[ks][0][r] + off);
+      const v4s tl = *reinterpret_cast<const v4s*>(s.kop[ks][1][r] + off);
       Mst[rt] = mma_x32(W[rt], cat(th, tl), Vb);
     }
     const v8s Sv = *reinterpret_cast<const v8s*>(s.sop[ks][r] + 16 * lane);
@@ -530,21 +564,50 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
   // Entering mean for this wave's strip: look back over the head's earlier
   // runs and fold their carries forward, M_end(u) = diag(D_u) M_end(u-1) +
   // Magg_u, with the same instructions whatever run the look-back stops at.
-  auto lookback_mean = [&](v4f (&Min)[4]) {
+  // With up to three aggregates to fold (PREFETCH), every load is issued
+  // before the first fold.
+  auto lookback_mean = [&](v4f (&Min)[4], auto prefetch) {
     const int r0 = __builtin_amdgcn_readfirstlane(lookback_find(hflag, 4, run, x.FAGG, x.FINC, p.ctrl));
     const auto rinc = coherent_rsrc(p.minc + ((size_t)head * nrun + r0) * 4096 + c * 1024, 4096);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) Min[rt] = ld_coherent(rinc, (rt * 64 + lane) * 16);
-    for (int u = r0 + 1; u < run; ++u) {
-      const size_t us = (size_t)head * nrun + u;
-      const auto ragg = coherent_rsrc(p.magg + us * 4096 + c * 1024, 4096);
-      const auto rdv = coherent_rsrc(p.dv + (us * 4 + c) * 64, 256);
+    auto agg_rsrc = [&](int u) { return coherent_rsrc(p.magg + ((size_t)head * nrun + u) * 4096 + c * 1024, 4096); };
+    auto dv_rsrc = [&](int u) { return coherent_rsrc(p.dv + (((size_t)head * nrun + u) * 4 + c) * 64, 256); };
+    const int nfold = run - r0 - 1;
+    if (decltype(prefetch)::value && nfold <= 3) {
+      v4f A[3][4], Dd[3][4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const v4f a = ld_coherent(ragg, (rt * 64 + lane) * 16);
-        const v4f d = ld_coherent(rdv, (16 * rt + 4 * G) * 4);
+      for (int k = 0; k < 3; ++k) {
+        if (k < nfold) {
+          const auto ragg = agg_rsrc(r0 + 1 + k);
+          const auto rdv = dv_rsrc(r0 + 1 + k);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Min[rt][e] = fmaf(d[e], Min[rt][e], a[e]);
+          for (int rt = 0; rt < 4; ++rt) {
+            A[k][rt] = ld_coherent(ragg, (rt * 64 + lane) * 16);
+            Dd[k][rt] = ld_coherent(rdv, (16 * rt + 4 * G) * 4);
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        if (k < nfold) {
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Min[rt][e] = fmaf(Dd[k][rt][e], Min[rt][e], A[k][rt][e]);
+        }
+      }
+    } else {
+      for (int u = r0 + 1; u < run; ++u) {
+        const auto ragg = agg_rsrc(u);
+        const auto rdv = dv_rsrc(u);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const v4f a = ld_coherent(ragg, (rt * 64 + lane) * 16);
+          const v4f d = ld_coherent(rdv, (16 * rt + 4 * G) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Min[rt][e] = fmaf(d[e], Min[rt][e], a[e]);
+        }
       }
     }
     if (dropped) {
@@ -572,7 +635,7 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
   // the state (D: the decay from the run start to this point).
   auto resolve_mid = [&](int nheld, const v4f (&D)[4]) {
     v4f Min[4];
-    lookback_mean(Min);
+    lookback_mean(Min, std::false_type{});
 #pragma unroll 1
     for (int k = 0; k < nheld; ++k) {
       v4f y0;
@@ -637,16 +700,19 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
         }
       }
       if (fast) {
+        // The four chunks as one branch-free block, outputs placed after it.
+        v4f Yc[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const v4f Y = chunk(qs, ks, r);
-          if (!hold_tile) {
-            store_y(tile, r, Y);
-          } else if (jt == 0) {
-            Yh[r] = Y;
-          } else {
-            Yh[4 + r] = Y;
-          }
+        for (int r = 0; r < 4; ++r) Yc[r] = chunk(qs, ks, r);
+        if (!hold_tile) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) store_y(tile, r, Yc[r]);
+        } else if (jt == 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Yh[r] = Yc[r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Yh[4 + r] = Yc[r];
         }
       }
       for (int r = 0; r < 4 && !fast; ++r) {
@@ -689,15 +755,15 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
               qv[4 * rt + 2] = __uint_as_float(qw.y << 16);
               qv[4 * rt + 3] = __uint_as_float(qw.y & 0xffff0000u);
             }
-            const float vv = bfv(*reinterpret_cast<const short*>(s.vb + swz(16 * r + t, 16 * c + li)));
+            const float vv = bfv(*reinterpret_cast<const short*>(s.vb + v_off(16 * r + t, 16 * c + li)));
             float part = 0.f;
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const int off = swz(16 * rt + 4 * G + e, 16 * r) + 4 * (t & 7);
-                const float f = *reinterpret_cast<const float*>(s.qop[qs][t >> 3] + off);
-                const float gg = *reinterpret_cast<const float*>(s.kop[ks][t >> 3] + off);
+                const int off = op_off(16 * rt + 4 * G + e, 8 * ((t & 7) >> 2)) + 4 * (t & 3);
+                const float f = *reinterpret_cast<const float*>(s.qop[qs][t >> 3][r] + off);
+                const float gg = *reinterpret_cast<const float*>(s.kop[ks][t >> 3][r] + off);
                 Mst[rt][e] = fmaf(f, Mst[rt][e], gg * vv);
                 part = fmaf(qv[4 * rt + e], Mst[rt][e], part);
               }
@@ -738,7 +804,7 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
       if (lane == 0) st_relaxed(hflag + 4 * run, x.FAGG);
     }
     v4f Min[4];
-    lookback_mean(Min);
+    lookback_mean(Min, std::true_type{});
     if (ntl >= RHOLD) {
 #pragma unroll
       for (int k = 0; k < 4 * RHOLD; ++k) correct(k, Yh[k], Min);
@@ -772,14 +838,16 @@ __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
   __shared__ RunSmem s;
   const int tid = threadIdx.x;
   if (tid == 0) {
-    s.ctl[cTicket] = __hip_atomic_fetch_add(p.ctrl + kTicket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s.ctl[cTicket] = __hip_atomic_fetch_add(p.ctrl + kTicket + blockIdx.x % (unsigned)p.tgroups, 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
     s.ctl[cEpoch] = p.nrun > 1 ? ld_relaxed(p.ctrl + kEpoch) : 0u;
     s.ctl[cWSync] = 0u;
     s.ctl[cXSync] = 0u;
   }
   __syncthreads();
-  // Ticket order is run-major, so every run a workgroup waits on holds a
-  // smaller ticket and started earlier.
+  // Ticket order is run-major within a group, and all runs of a head fall in
+  // one group, so every run a workgroup waits on holds a smaller ticket of
+  // its own counter and started earlier.
   RunCtx x;
   const unsigned ticket = s.ctl[cTicket];
   const unsigned epoch = s.ctl[cEpoch];
@@ -789,8 +857,11 @@ __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
   x.FAGG = 2u * epoch + 2u;
   x.FINC = 2u * epoch + 3u;
   x.nrun = p.nrun;
-  x.run = (int)(ticket / (unsigned)p.nheads);
-  x.head = (int)(ticket % (unsigned)p.nheads);
+  // Group x = blockIdx % tgroups serves heads x, x + tgroups, ...: its
+  // tickets run over those heads, run-major.
+  const unsigned hpg = (unsigned)p.nheads / (unsigned)p.tgroups;
+  x.run = (int)(ticket / hpg);
+  x.head = (int)((ticket % hpg) * (unsigned)p.tgroups + blockIdx.x % (unsigned)p.tgroups);
   x.T = p.T;
   x.tb = x.run * p.R;
   x.ntl = min(x.tb + p.R, p.ntiles) - x.tb;
@@ -806,7 +877,7 @@ __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
   if (tid == 0) {
     const unsigned ng = (unsigned)p.nheads * (unsigned)p.nrun;
     if (__hip_atomic_fetch_add(p.ctrl + kGroupsDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ng - 1) {
-      st_relaxed(p.ctrl + kTicket, 0u);
+      for (int g = 0; g < p.tgroups; ++g) st_relaxed(p.ctrl + kTicket + g, 0u);
       st_relaxed(p.ctrl + kGroupsDone, 0u);
       if (p.nrun > 1) st_relaxed(p.ctrl + kEpoch, epoch + 1u);
     }

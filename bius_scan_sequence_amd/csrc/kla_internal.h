@@ -8,7 +8,9 @@ namespace kla {
 
 // Control words at the head of every workspace (32-bit each).  Words 0 and 1
 // hold the call epoch and the groups-done counter (kla_device.h).
-enum CtrlWord { kError = 3, kTicket = 4 };
+// kTicket: eight words (8..15) of ticket counters, one per group of
+// workgroups of the run-streaming forward (blockIdx % groups).
+enum CtrlWord { kError = 3, kTicket = 8 };
 
 // Done counters: a fixed region of kDoneCounters words right after the
 // 256-byte header, at the same place and of the same size whatever the call's
@@ -162,7 +164,8 @@ struct FwdRunParams {
   float* MT;
   float* lpath;        // nullable
   int nheads, T, ntiles, R, nrun;
-  unsigned* ctrl;      // workspace control words (epoch, groups done, error, ticket)
+  int tgroups;         // ticket groups (1, 2, 4 or 8; divides nheads): group x takes the heads h = x mod tgroups
+  unsigned* ctrl;      // workspace control words (epoch, groups done, error, tickets)
   unsigned* flag;      // [nheads*nrun][4] mean-carry flags, one per matrix wave
   float* dv;           // [nheads*nrun][4][64] prod of forget gates over the run (a copy per wave)
   float* magg;         // [nheads*nrun][4096] local mean state of the run (fragment order)
