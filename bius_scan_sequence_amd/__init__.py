@@ -29,7 +29,9 @@ __all__ = [
     "decode_step", "backward", "scan", "Workspace",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkla.so")
+# BIUS_KLA_LIB selects another build of the same library (the host-sanitizer
+# build that tests/test_abi_sanitized.py runs the ABI tests against).
+LIB_PATH = os.environ.get("BIUS_KLA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkla.so")
 KLA_F32, KLA_BF16 = 0, 1
 KLA_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/kla.h
 # Not a C status: raised (as KlaError) when a call asked to be checked and the

@@ -64,6 +64,48 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-sanitizer build: the C ABI's host code (argument validation, workspace
+# layout, launch set-up in kla_api.hip) compiled with AddressSanitizer and
+# UBSan for the host side only; every kernel object is the ordinary one.  The
+# library expects the ASan runtime preloaded (see asan_runtime()).
+SAN_DIR = os.path.join(BUILD, "hostsan")
+SAN_LIB = os.path.join(SAN_DIR, "libkla_hostsan.so")
+
+
+def asan_runtime() -> str:
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    return subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                          text=True, check=True).stdout.strip()
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Builds SAN_LIB, reusing the ordinary kernel objects when they exist."""
+    if not all(os.path.exists(os.path.join(BUILD, os.path.splitext(s)[0] + ".o")) for s in SOURCES):
+        build()
+    os.makedirs(SAN_DIR, exist_ok=True)
+    obj = os.path.join(SAN_DIR, "kla_api_san.o")
+    cmd = [hipcc(), *common_flags(), "-g", "-fno-omit-frame-pointer",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-c", os.path.join(CSRC, "kla_api.hip"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    objs = [obj] + [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "kla_api.hip"]
+    cmd = ["g++", "-shared", "-fPIC", "-o", SAN_LIB, *objs, "-L/opt/rocm/lib", "-lamdhip64",
+           "-Wl,-rpath,/opt/rocm/lib", "-Wl,--allow-shlib-undefined"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print("built", SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--host-sanitized" in sys.argv:
+        build_host_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

@@ -419,6 +419,7 @@ int forward_impl(const char* name, const void* q, const void* k, const void* v, 
   }
   p.cwidth = conv_w ? conv_width : 0;
   p.nheads = (int)nheads; p.T = T; p.nseg = nseg; p.H = H;
+  p.tgroups = nheads % 8 == 0 ? 8 : nheads % 4 == 0 ? 4 : nheads % 2 == 0 ? 2 : 1;
   // With 128 or more heads a head's consecutive segments are dispatched at
   // least 128 workgroups apart (segment-major order), and a segment seldom
   // has a successor waiting on its aggregate.
@@ -550,6 +551,7 @@ extern "C" int kla_precision_scan(const float* log_decay, const float* proc_nois
   p.lpath = lambda_path; p.lamT = lambda_T;
   p.nchains = chains; p.D = D; p.T = T;
   p.nseg = pl.nseg; p.seglen = pl.seglen; p.ncblocks = pl.ncblocks;
+  p.tgroups = pl.ncblocks % 8 == 0 ? 8 : pl.ncblocks % 4 == 0 ? 4 : pl.ncblocks % 2 == 0 ? 2 : 1;
   p.ctrl = reinterpret_cast<unsigned*>(ws);
   p.bdone = reinterpret_cast<unsigned*>(ws + pl.bdone);
   p.flag = reinterpret_cast<unsigned*>(ws + pl.flag);

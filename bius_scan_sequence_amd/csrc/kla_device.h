@@ -347,6 +347,7 @@ __device__ __forceinline__ void epoch_done(unsigned* ctrl, unsigned ngroups, uns
   if (__hip_atomic_fetch_add(ctrl + kGroupsDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ngroups - 1)
     return;
   st_relaxed(ctrl + kGroupsDone, 0u);
+  for (int g = 0; g < 8; ++g) st_relaxed(ctrl + kTicket + g, 0u);  // ticket counters for the next call
   st_relaxed(ctrl + kEpoch, e + 1u);
 }
 

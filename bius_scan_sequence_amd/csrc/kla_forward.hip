@@ -505,15 +505,24 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lc = lane & 15;  // lane group (k block) / lane column
   const int nheads = p.nheads, T = p.T, nseg = p.nseg;
-  // Segment-major order: every segment a workgroup waits on has a lower index.
-  const int seg = blockIdx.x / nheads, head = blockIdx.x % nheads;
+  // (head, segment) from a ticket when segments wait on predecessors: group
+  // x = blockIdx % tgroups serves heads x, x + tgroups, ..., segment-major, so
+  // every segment a workgroup waits on holds a smaller ticket of its own
+  // counter and started earlier.
+  if (nseg > 1 && tid == 0)
+    s.ctl[2] = (int)__hip_atomic_fetch_add(p.ctrl + kTicket + blockIdx.x % (unsigned)p.tgroups, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) s.ctl[1] = nseg > 1 ? (int)ld_relaxed(p.ctrl + kEpoch) : 0;
+  if (nseg > 1) __syncthreads();
+  const unsigned ticket = nseg > 1 ? (unsigned)s.ctl[2] : blockIdx.x;
+  const unsigned tg = nseg > 1 ? (unsigned)p.tgroups : 1u, hpg = (unsigned)nheads / tg;
+  const int seg = (int)(ticket / hpg), head = (int)((ticket % hpg) * tg + blockIdx.x % tg);
   const int t0 = seg * L;
   const int nvalid = min(L, T - t0);
   const bool last = (seg == nseg - 1);
   const size_t hs = (size_t)head * nseg + seg;  // (head, segment) slot
   const size_t hb = (size_t)head * nseg;
 
-  if (tid == 0) s.ctl[1] = nseg > 1 ? (int)ld_relaxed(p.ctrl + kEpoch) : 0;
   if (tid < NCH) s.unsafe[tid] = 0;
 
   In* const rq = s.raw(0);

@@ -166,34 +166,58 @@ __device__ __forceinline__ void read_raw16(const unsigned char* arr, const WLane
 }
 
 // Composes the step matrices of the walker's 16 tokens (predict then update:
-// [[1 + c pb, c a^2], [pb, a^2]], [KLA-nl] §2), keeping (a, a^2, pb, c,
-// k Lambda^v) per token for the gate walk when asked.
+// [[1 + c pb, c a^2], [pb, a^2]], [KLA-nl] §2) as two independent 8-token
+// products walked side by side (twice the independent work per step of the
+// dependent chain), keeping (a, a^2, pb, c, k Lambda^v) per token for the
+// gate walk when asked.  Returns the chunk's product and sets `first` to that
+// of its first eight tokens.
 template <bool KEEP>
-__device__ __forceinline__ Mob agg_walk16(const RunSmem& s, const WLane& L, int w, float (&ka)[16], float (&ka2)[16],
-                                          float (&kp)[16], float (&kc)[16], float (&kv)[16]) {
+__device__ __forceinline__ Mob agg_walk16(const RunSmem& s, const WLane& L, int w, Mob& first, float (&ka)[16],
+                                          float (&ka2)[16], float (&kp)[16], float (&kc)[16], float (&kv)[16]) {
   v4s rk[4], rl[4], rp[4], rv[4];
   read_raw16(s.raw[1], L, w, rk);
   read_raw16(s.raw[2], L, w, rl);
   read_raw16(s.raw[3], L, w, rp);
   read_raw16(s.raw[4], L, w, rv);
-  Mob P = mob_identity();
+  // Software-pipelined: the coefficients of tokens u + 1 and u + 9 are formed
+  // beside the chain steps of tokens u and u + 8, and each step is its own
+  // scheduling region, so the dependent chain steps of both halves sit
+  // between independent work.
+  float A2[2][2], PB[2][2], C[2][2];  // [buffer][half]
+  auto coef = [&](int u, int buf) {
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int sb = t >> 2, e = t & 3;
-    const float k = bfv(rk[sb][e]), ld = bfv(rl[sb][e]), pb = bfv(rp[sb][e]), vp = bfv(rv[sb][e]);
-    const float a = __expf(ld);
-    const float kvv = k * vp, c = k * kvv, a2 = a * a;
-    P = mob_step_raw(P, a2, pb, c);
-    if (e == 3) P = mob_normalize(P);
-    if constexpr (KEEP) {
-      ka[t] = a;
-      ka2[t] = a2;
-      kp[t] = pb;
-      kc[t] = c;
-      kv[t] = kvv;
+    for (int h = 0; h < 2; ++h) {
+      const int t = u + 8 * h, sb = t >> 2, e = t & 3;
+      const float k = bfv(rk[sb][e]), ld = bfv(rl[sb][e]), pb = bfv(rp[sb][e]), vp = bfv(rv[sb][e]);
+      const float a = __expf(ld);
+      const float kvv = k * vp, c = k * kvv, a2 = a * a;
+      A2[buf][h] = a2;
+      PB[buf][h] = pb;
+      C[buf][h] = c;
+      if constexpr (KEEP) {
+        ka[t] = a;
+        ka2[t] = a2;
+        kp[t] = pb;
+        kc[t] = c;
+        kv[t] = kvv;
+      }
     }
+  };
+  Mob P[2] = {mob_identity(), mob_identity()};
+  coef(0, 0);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    if (u + 1 < 8) coef(u + 1, (u + 1) & 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) P[h] = mob_step_raw(P[h], A2[u & 1][h], PB[u & 1][h], C[u & 1][h]);
+    if ((u & 3) == 3) {
+      P[0] = mob_normalize(P[0]);
+      P[1] = mob_normalize(P[1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  return P;
+  first = P[0];
+  return mob_mul(P[1], P[0]);
 }
 
 // Inclusive scan of the chunk products over the tile's four chunks (lanes
@@ -288,8 +312,8 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
       }
       __syncthreads();
       float ka[16], ka2[16], kp[16], kc[16], kv[16];
-      Mob excl;
-      const Mob Pc = scan_chunks(agg_walk16<false>(s, L, w, ka, ka2, kp, kc, kv), L.g, excl);
+      Mob excl, first;
+      const Mob Pc = scan_chunks(agg_walk16<false>(s, L, w, first, ka, ka2, kp, kc, kv), L.g, excl);
       const Mob Pw = shfl_mob(Pc, 48 + L.i);  // product over the whole tile
       Ptot = mob_mul(Ptot, Pw);               // the older tile acts first
       const float lo = Ptot.m01 * fast_rcp(Ptot.m11), hi = Ptot.m00 * fast_rcp(Ptot.m10);
@@ -318,64 +342,104 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
       const int tile = tb + j;
       const int qs = j < RHOLD ? j : RHOLD + (j & 1), ks = j & 1;
       float ka[16], ka2[16], kp[16], kc[16], kv[16];
-      Mob excl;
-      (void)scan_chunks(agg_walk16<true>(s, L, w, ka, ka2, kp, kc, kv), L.g, excl);
+      Mob excl, first;
+      (void)scan_chunks(agg_walk16<true>(s, L, w, first, ka, ka2, kp, kc, kv), L.g, excl);
       const float lam_g = mob_apply(excl, lam_start);
+      const float lam_g8 = mob_apply(first, lam_g);  // precision after the chunk's first 8 tokens
       v4s rq[4];
       read_raw16(s.raw[0], L, w, rq);
-      // Gate walk, projective: (n, d) starts as (lam_g, 1) and is rescaled by
-      // 2^-ex_g after token group g (tokens 4g..4g+3), so within group g both
-      // carry the scale 2^-E_g, E_g = ex_0 + .. + ex_(g-1).  With Ab the
-      // product of a over the chunk so far (f = a n_prev / n, g = k Lambda^v
-      // d' / n), cp_t = Ab_t lam_g / n_t, and the operands referred to the
-      // chunk end are
-      //   Qt_t = q_t cp_t / cp16 = q_t (Ab_t / n_t) (n_16 / Ab_16),
-      //   Kt_t = g_t cp16 / cp_t = k Lambda^v d'_t (Ab_16 / Ab_t) / n_16:
+      // Gate walk, projective, as two 8-token halves walked side by side: half
+      // h starts from (lam_h, 1) (lam_0 = lam_g, lam_1 = lam_g8) and is
+      // rescaled by 2^-ex[h][g] after its token group g (4 tokens), so within
+      // group g both n and d' carry 2^-E_g (E_0 = 0, E_1 = ex[h][0]).  With
+      // Ab the product of a over the half so far (f = a n_prev / n, g =
+      // k Lambda^v d' / n), cp_t = Ab_t lam_h / n_t within the half, and
+      // referred to the half's end
+      //   Qt_t = q_t (Ab_t / n_t) (n_8 / Ab_8),   Kt_t = k Lambda^v d'_t (Ab_8 / Ab_t) / n_8:
       // Qt from this forward pass and one factor per group, Kt from this pass
-      // and a backward (suffix) product of a, both carrying 2^(+-(E_3 - E_g)).
-      float n = lam_g, d = 1.f, Ab = 1.f, n16 = 1.f, rn16 = 1.f;
+      // and a backward (suffix) product of a.  Referred to the chunk end,
+      // the first half's Qt takes a further 1 / cp8b and its Kt a further
+      // cp8b (cp8b: the second half's decay), and cp16 = cp8a cp8b.
+      float n[2] = {lam_g, lam_g8}, d[2] = {1.f, 1.f}, Ab[2] = {1.f, 1.f}, n8[2], rn8[2];
       float qt[16], kt[16];
-      int exg[4];
+      int exg[2][2];
+      // Software-pipelined like the composition walk: step u advances both
+      // chains (token u of each half) and finishes the per-token work of the
+      // step before it.
+      float pn1[2] = {1.f, 1.f}, pd1[2] = {1.f, 1.f};
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const float d1 = fmaf(kp[t], n, ka2[t] * d);  // d' = pb n + a^2 d (predict)
-        const float n1 = fmaf(kc[t], d1, n);          // n' = n + c d'      (update)
-        const float rn = fast_rcp(n1);
-        Ab *= ka[t];
-        qt[t] = bfv(rq[t >> 2][t & 3]) * (Ab * rn);
-        kt[t] = kv[t] * d1;
-        if (t == 15) {
-          n16 = n1;
-          rn16 = rn;
+      for (int u = 0; u <= 8; ++u) {
+        float cn1[2], cd1[2];
+        if (u < 8) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int t = u + 8 * h;
+            const float d1 = fmaf(kp[t], n[h], ka2[t] * d[h]);  // d' = pb n + a^2 d (predict)
+            const float n1 = fmaf(kc[t], d1, n[h]);              // n' = n + c d'      (update)
+            cn1[h] = n1;
+            cd1[h] = d1;
+            n[h] = n1;
+            d[h] = d1;
+          }
         }
-        if (lp) {
-          const int tok = tile * RTL + 16 * L.g + t;
-          if (tok < T) lp[hoff + (size_t)tok * RD + L.ch] = n1 * fast_rcp(d1);
+        if (u > 0) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int t = u - 1 + 8 * h;
+            const float rn = fast_rcp(pn1[h]);
+            Ab[h] *= ka[t];
+            qt[t] = bfv(rq[t >> 2][t & 3]) * (Ab[h] * rn);
+            kt[t] = kv[t] * pd1[h];
+            if (u - 1 == 7) {
+              n8[h] = pn1[h];
+              rn8[h] = rn;
+            }
+            if (lp) {
+              const int tok = tile * RTL + 16 * L.g + t;
+              if (tok < T) lp[hoff + (size_t)tok * RD + L.ch] = pn1[h] * fast_rcp(pd1[h]);
+            }
+          }
         }
-        n = n1;
-        d = d1;
-        if ((t & 3) == 3) {
-          const int ex = __builtin_amdgcn_frexp_expf(fmaxf(n, d));
-          n = __builtin_amdgcn_ldexpf(n, -ex);
-          d = __builtin_amdgcn_ldexpf(d, -ex);
-          exg[t >> 2] = ex;
+        if (u < 8) {
+          if ((u & 3) == 3) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int ex = __builtin_amdgcn_frexp_expf(fmaxf(n[h], d[h]));
+              n[h] = __builtin_amdgcn_ldexpf(n[h], -ex);
+              d[h] = __builtin_amdgcn_ldexpf(d[h], -ex);
+              exg[h][u >> 2] = ex;
+            }
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            pn1[h] = cn1[h];
+            pd1[h] = cd1[h];
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       // Precision after the tile, for the next tile (from chunk 3's walk).
-      const float lam_end = __shfl(n * fast_rcp(d), 48 + L.i, 64);
-      const int E3 = exg[0] + exg[1] + exg[2];
-      const float cp16 = __builtin_amdgcn_ldexpf(Ab * rn16 * lam_g, -E3);
-      {
-        float fq = n16 * fast_rcp(Ab);  // group 3
-        float sk = rn16;
+      const float lam_end = __shfl(n[1] * fast_rcp(d[1]), 48 + L.i, 64);
+      const float cp8a = __builtin_amdgcn_ldexpf(Ab[0] * rn8[0] * lam_g, -exg[0][0]);
+      const float cp8b = __builtin_amdgcn_ldexpf(Ab[1] * rn8[1] * lam_g8, -exg[1][0]);
+      const float cp16 = cp8a * cp8b;
 #pragma unroll
-        for (int t = 15; t >= 0; --t) {
+      for (int h = 0; h < 2; ++h) {
+        float fq = n8[h] * fast_rcp(Ab[h]);  // group 1 of the half
+        float sk = rn8[h];
+        if (h == 0) {
+          fq *= fast_rcp(cp8b);
+          sk *= cp8b;
+        }
+#pragma unroll
+        for (int u = 7; u >= 0; --u) {
+          const int t = u + 8 * h;
           qt[t] *= fq;
           kt[t] *= sk;
           sk *= ka[t];
-          if ((t & 3) == 0 && t > 0) {
-            fq = __builtin_amdgcn_ldexpf(fq, exg[(t >> 2) - 1]);
-            sk = __builtin_amdgcn_ldexpf(sk, -exg[(t >> 2) - 1]);
+          if (u == 4) {
+            fq = __builtin_amdgcn_ldexpf(fq, exg[h][0]);
+            sk = __builtin_amdgcn_ldexpf(sk, -exg[h][0]);
           }
         }
       }

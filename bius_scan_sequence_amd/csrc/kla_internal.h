@@ -43,6 +43,7 @@ struct FwdParams {
   const float* cb[3];
   int cwidth;
   int nheads, T, nseg;
+  int tgroups;        // ticket groups (1, 2, 4 or 8; divides nheads): group x takes the heads h = x mod tgroups
   int H;              // heads per batch row (indexes theta / sigma2)
   int mskip;          // a segment whose predecessor's inclusive mean is already out publishes no aggregate
   unsigned* ctrl;     // workspace control words
@@ -65,6 +66,7 @@ struct PscanParams {
   float* lamT;        // nullable
   long long nchains;  // B*H*D
   int D, T, nseg, seglen, ncblocks;
+  int tgroups;        // ticket groups (1, 2, 4 or 8; divides ncblocks): group x takes the chain blocks cb = x mod tgroups
   unsigned* ctrl;
   unsigned* bdone;    // [kDoneCounters] segments done with their flags, per chain-block group
   unsigned* flag;     // [nseg*ncblocks]

@@ -23,9 +23,18 @@ __global__ __launch_bounds__(256) void kla_pscan_kernel(PscanParams p) {
   __shared__ int sh[4];
   const int tid = threadIdx.x;
   const int nseg = p.nseg;
-  // Segment-major order: every segment a workgroup waits on has a lower index.
-  const int seg = blockIdx.x / p.ncblocks, cb = blockIdx.x % p.ncblocks;
+  // (chain block, segment) from a ticket when segments wait on predecessors:
+  // group x = blockIdx % tgroups serves chain blocks x, x + tgroups, ...,
+  // segment-major, so every segment a workgroup waits on holds a smaller
+  // ticket of its own counter and started earlier.
+  if (nseg > 1 && tid == 0)
+    sh[3] = (int)__hip_atomic_fetch_add(p.ctrl + kTicket + blockIdx.x % (unsigned)p.tgroups, 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
   if (tid == 0) sh[1] = nseg > 1 ? (int)ld_relaxed(p.ctrl + kEpoch) : 0;
+  if (nseg > 1) __syncthreads();
+  const unsigned ticket = nseg > 1 ? (unsigned)sh[3] : blockIdx.x;
+  const unsigned tg = nseg > 1 ? (unsigned)p.tgroups : 1u, cpg = (unsigned)p.ncblocks / tg;
+  const int seg = (int)(ticket / cpg), cb = (int)((ticket % cpg) * tg + blockIdx.x % tg);
   const bool last = seg == nseg - 1;
   const long long chain = (long long)cb * 256 + tid;
   const bool valid = chain < p.nchains;

@@ -49,7 +49,7 @@ def test_lm180m_bf16_full():
 
 def test_long_bf16_full_size_sampled_heads():
     """long_bf16 at its full shape (B=2, H=16, T=16384, d=128), generated on the
-    device; the oracle checks two sampled heads over all 16384 tokens."""
+    device; the oracle checks four sampled heads over all 16384 tokens."""
     import torch
     import bius_scan_sequence_amd as K
     w = KI.workload("long_bf16")
@@ -58,7 +58,7 @@ def test_long_bf16_full_size_sampled_heads():
     y, lT, MT = K.forward(xd["q"], xd["k"], xd["v"], xd["log_decay"], xd["proc_noise"], xd["val_prec"])
     torch.cuda.synchronize()
     rng = np.random.default_rng(w.seed)
-    for flat in rng.choice(w.B * w.H, size=2, replace=False):
+    for flat in rng.choice(w.B * w.H, size=4, replace=False):
         b, h = divmod(int(flat), w.H)
         x = {n: xd[n][b:b + 1, h:h + 1].float().cpu().numpy() for n in
              ("q", "k", "v", "log_decay", "proc_noise", "val_prec")}
@@ -168,6 +168,33 @@ def test_deterministic_bitwise():
     ws = K._default_workspace(xd["q"].device, torch.cuda.current_stream().cuda_stream, "forward")
     assert ws.error() == 0
     say("[ok] determinism")
+
+
+@pytest.mark.parametrize("case", ["lm180m_bf16", "deep_runs"])
+def test_deterministic_bitwise_ten_repeats(case):
+    """Ten repeated calls give the first call's bits, stopping at the first
+    mismatch: lm180m_bf16 at full size (192 heads), and 8 heads x 8192 tokens
+    (128 tiles per head, so the run kernel cuts each head into many runs and
+    folds their carries through look-backs)."""
+    import torch
+    import bius_scan_sequence_amd as K
+    if case == "lm180m_bf16":
+        x = KI.make_forward_inputs("lm180m_bf16")
+    else:
+        x = KI.make_forward_inputs("lm45m_bf16", B=1, H=8, T=8192, seed=311)
+    say(f"[case] determinism x10 {case}: q={x['q'].shape}")
+    xd = to_dev(x)
+    names = ("q", "k", "v", "log_decay", "proc_noise", "val_prec")
+    ws = K.Workspace()
+    first = K.forward(*(xd[n] for n in names), workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(10):
+        again = K.forward(*(xd[n] for n in names), workspace=ws)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("y", "lambda_T", "M_T"), first, again):
+            assert torch.equal(a, b), f"repeat {rep}: {name} differs"
+    assert ws.error() == 0
+    say(f"[ok] determinism x10 {case}")
 
 
 def test_many_heads_skipped_aggregates_deterministic():
