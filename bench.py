@@ -55,9 +55,11 @@ def algorithmic_bytes(B, H, T, dk, dv, esz):
 
 
 def run_plan(nheads, T, ncu):
-    """Tiles per run and runs per head the library picks for the run-streaming
-    kernel (kla_forward_run.hip, fwd_run_plan): the run count that minimises
-    rounds of workgroups x tiles per workgroup, fewest runs on ties."""
+    """Runs per head and their tile counts as the library plans them for the
+    run-streaming kernel (kla_forward_run.hip, fwd_run_plan): the run count
+    that minimises rounds of workgroups x tiles per workgroup (fewest runs on
+    ties); run 0 takes one tile more than an even share, the other runs split
+    the rest evenly.  Returns the list of tile counts, one per run."""
     ntiles = (T + 63) // 64
     best, bestn = None, 1
     for n in range(1, ntiles + 1):
@@ -67,7 +69,12 @@ def run_plan(nheads, T, ncu):
         cost = ((nheads * n + ncu - 1) // ncu) * r
         if best is None or cost < best:
             best, bestn = cost, n
-    return (ntiles + bestn - 1) // bestn, bestn
+    if bestn == 1:
+        return [ntiles]
+    r0 = min((ntiles + bestn - 1) // bestn + 1, ntiles - (bestn - 1))
+    rest = ntiles - r0
+    rb, rx = divmod(rest, bestn - 1)
+    return [r0] + [rb + (1 if k < rx else 0) for k in range(bestn - 1)]
 
 
 def mfma_flops(B, H, T, ncu):
@@ -80,11 +87,10 @@ def mfma_flops(B, H, T, ncu):
     two held tiles (8 chunks) with 6 more per chunk and matrix wave."""
     nheads = B * H
     ntiles = (T + 63) // 64
-    R, nrun = run_plan(nheads, T, ncu)
+    runs = run_plan(nheads, T, ncu)
     chunks = nheads * ntiles * 4
-    held_runs = nheads * (nrun - 1)
-    held_chunks_per_run = 4 * min(2, R)
-    instrs = chunks * (4 * 11 + 6) + held_runs * held_chunks_per_run * 4 * 6
+    held_chunks = nheads * sum(4 * min(2, r) for r in runs[1:])
+    instrs = chunks * (4 * 11 + 6) + held_chunks * 4 * 6
     return instrs * 16384, instrs
 
 

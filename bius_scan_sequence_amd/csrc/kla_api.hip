@@ -392,7 +392,7 @@ int forward_impl(const char* name, const void* q, const void* k, const void* v, 
     r.lam0 = lambda0; r.M0 = M0; r.y = static_cast<uint16_t*>(y); r.lamT = lambda_T; r.MT = M_T;
     r.lpath = lambda_path;
     r.nheads = (int)nheads; r.T = T; r.ntiles = (T + 63) / 64;
-    fwd_run_plan(r.nheads, T, device_cus(), r.R, r.nrun);
+    fwd_run_plan(r.nheads, T, device_cus(), r.R0, r.Rb, r.Rx, r.nrun);
     r.tgroups = r.nheads % 8 == 0 ? 8 : r.nheads % 4 == 0 ? 4 : r.nheads % 2 == 0 ? 2 : 1;
     const RunLayout rl = run_layout(nheads, r.nrun);
     const int rc = take(rl.total, rl.dv);

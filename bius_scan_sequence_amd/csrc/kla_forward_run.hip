@@ -927,8 +927,15 @@ __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
   x.run = (int)(ticket / hpg);
   x.head = (int)((ticket % hpg) * (unsigned)p.tgroups + blockIdx.x % (unsigned)p.tgroups);
   x.T = p.T;
-  x.tb = x.run * p.R;
-  x.ntl = min(x.tb + p.R, p.ntiles) - x.tb;
+  // Run 0 takes R0 tiles, the others Rb or Rb + 1 (the first Rx of them).
+  if (x.run == 0) {
+    x.tb = 0;
+    x.ntl = p.R0;
+  } else {
+    const int k = x.run - 1;
+    x.tb = p.R0 + k * p.Rb + min(k, p.Rx);
+    x.ntl = p.Rb + (k < p.Rx ? 1 : 0);
+  }
   x.hoff = (size_t)x.head * p.T * RD;
   x.last_run = x.run == p.nrun - 1;
   if (x.wave < 4)
@@ -949,8 +956,13 @@ __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
 }
 
 // Runs per head: the count that minimises (rounds of workgroups) x (tiles
-// per workgroup) on `ncu` compute units, fewest runs on ties.
-void fwd_run_plan(int nheads, int T, int ncu, int& R, int& nrun) {
+// per workgroup) on `ncu` compute units, fewest runs on ties.  Every run but
+// the first starts with a window walk (about one tile's time), and every run
+// resolves its entering mean only once all earlier runs have published, so
+// the first run takes kFirstExtra tiles more than an even share to end its
+// loop with the others; the other runs split the rest as evenly as they can.
+constexpr int kFirstExtra = 1;
+void fwd_run_plan(int nheads, int T, int ncu, int& R0, int& Rb, int& Rx, int& nrun) {
   const int ntiles = (T + RTL - 1) / RTL;
   long long best = -1;
   int bestn = 1;
@@ -966,7 +978,15 @@ void fwd_run_plan(int nheads, int T, int ncu, int& R, int& nrun) {
     }
   }
   nrun = bestn;
-  R = (ntiles + bestn - 1) / bestn;
+  if (nrun == 1) {
+    R0 = ntiles;
+    Rb = Rx = 0;
+    return;
+  }
+  R0 = min((ntiles + nrun - 1) / nrun + kFirstExtra, ntiles - (nrun - 1));
+  const int rest = ntiles - R0;
+  Rb = rest / (nrun - 1);
+  Rx = rest % (nrun - 1);
 }
 
 hipError_t launch_forward_run(const FwdRunParams& p, hipStream_t stream) {

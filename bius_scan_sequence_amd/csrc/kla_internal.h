@@ -165,7 +165,8 @@ struct FwdRunParams {
   float* lamT;
   float* MT;
   float* lpath;        // nullable
-  int nheads, T, ntiles, R, nrun;
+  int nheads, T, ntiles, nrun;
+  int R0, Rb, Rx;      // run 0 takes R0 tiles; run r >= 1 takes Rb, plus one if r - 1 < Rx
   int tgroups;         // ticket groups (1, 2, 4 or 8; divides nheads): group x takes the heads h = x mod tgroups
   unsigned* ctrl;      // workspace control words (epoch, groups done, error, tickets)
   unsigned* flag;      // [nheads*nrun][4] mean-carry flags, one per matrix wave
@@ -173,7 +174,7 @@ struct FwdRunParams {
   float* magg;         // [nheads*nrun][4096] local mean state of the run (fragment order)
   float* minc;         // [nheads*nrun][4096] mean state after the run (fragment order)
 };
-void fwd_run_plan(int nheads, int T, int ncu, int& R, int& nrun);
+void fwd_run_plan(int nheads, int T, int ncu, int& R0, int& Rb, int& Rx, int& nrun);
 hipError_t launch_forward_run(const FwdRunParams& p, hipStream_t stream);
 
 int fwd_segment_len(int dk, int dv, bool bf16);
