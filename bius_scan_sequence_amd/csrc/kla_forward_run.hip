@@ -67,7 +67,8 @@ enum RunCtl {
   cTicket = 0, cEpoch = 1, cWSync = 2, cXSync = 3,
   cUnsafe = 4,    // [2 tile parities][4 walker waves]: chunks that take the exact path
   cNotFree = 12,  // [2][4]: some channel's decay from the run start to the tile start above 2^-100
-  cVote = 20      // [4]: window walk not converged
+  cVote = 20,     // [4]: window walk not converged
+  cLamReady = 24  // the window walk's precision is in lamst
 };
 
 struct alignas(16) RunSmem {
@@ -80,6 +81,7 @@ struct alignas(16) RunSmem {
   float dtile[2][RD];                     // decay from the run start to the tile start
   float hfac[RHOLD][4][RD];               // held chunks: cp16 * decay from the run start to the chunk start
   float dend[RD];                         // decay over the whole run
+  float lamst[RD];                        // precision entering the run (from the window walk)
   unsigned ctl[32];
 };
 
@@ -171,14 +173,17 @@ __device__ __forceinline__ void read_raw16(const unsigned char* arr, const WLane
 // dependent chain), keeping (a, a^2, pb, c, k Lambda^v) per token for the
 // gate walk when asked.  Returns the chunk's product and sets `first` to that
 // of its first eight tokens.
+// `arr` holds the tile's k, log_decay, proc_noise and val_prec arrays, 8 KB
+// apart, in the raw-input layout.
 template <bool KEEP>
-__device__ __forceinline__ Mob agg_walk16(const RunSmem& s, const WLane& L, int w, Mob& first, float (&ka)[16],
-                                          float (&ka2)[16], float (&kp)[16], float (&kc)[16], float (&kv)[16]) {
+__device__ __forceinline__ Mob agg_walk16(const unsigned char* arr, const WLane& L, int w, Mob& first,
+                                          float (&ka)[16], float (&ka2)[16], float (&kp)[16], float (&kc)[16],
+                                          float (&kv)[16]) {
   v4s rk[4], rl[4], rp[4], rv[4];
-  read_raw16(s.raw[1], L, w, rk);
-  read_raw16(s.raw[2], L, w, rl);
-  read_raw16(s.raw[3], L, w, rp);
-  read_raw16(s.raw[4], L, w, rv);
+  read_raw16(arr, L, w, rk);
+  read_raw16(arr + RTL * RD * 2, L, w, rl);
+  read_raw16(arr + 2 * RTL * RD * 2, L, w, rp);
+  read_raw16(arr + 3 * RTL * RD * 2, L, w, rv);
   // Software-pipelined: the coefficients of tokens u + 1 and u + 9 are formed
   // beside the chain steps of tokens u and u + 8, and each step is its own
   // scheduling region, so the dependent chain steps of both halves sit
@@ -293,42 +298,9 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
   };
   uint4 pf[10];  // the next tile's units, in flight
   load(tb, pf, 0);
-  float lam_start = 1.f;
-  const float lam0 = p.lam0 ? p.lam0[(size_t)x.head * RD + L.ch] : 1.f;
-  if (x.run == 0) {
-    lam_start = lam0;
-  } else {
-    // Precision entering the run: compose the step matrices of the tiles
-    // before it, newest first, until the image of (0, inf) under the composed
-    // map is below fp32 resolution on every channel, or down to the sequence
-    // start, where lambda0 is applied.
-    Mob Ptot = mob_identity();
-    int wt = tb - 1;
-    while (true) {
-      {
-        uint4 tmp[10];
-        load(wt, tmp, 2);
-        store(tmp, 2);
-      }
-      __syncthreads();
-      float ka[16], ka2[16], kp[16], kc[16], kv[16];
-      Mob excl, first;
-      const Mob Pc = scan_chunks(agg_walk16<false>(s, L, w, first, ka, ka2, kp, kc, kv), L.g, excl);
-      const Mob Pw = shfl_mob(Pc, 48 + L.i);  // product over the whole tile
-      Ptot = mob_mul(Ptot, Pw);               // the older tile acts first
-      const float lo = Ptot.m01 * fast_rcp(Ptot.m11), hi = Ptot.m00 * fast_rcp(Ptot.m10);
-      const bool conv = hi - lo <= 0x1p-21f * lo;
-      const unsigned long long bad = __ballot(!conv);
-      if (lane == 0) s.ctl[cVote + w] = bad ? 1u : 0u;
-      __syncthreads();
-      const bool all = (s.ctl[cVote] | s.ctl[cVote + 1] | s.ctl[cVote + 2] | s.ctl[cVote + 3]) == 0u;
-      if (all || wt == 0) {
-        lam_start = mob_apply(Ptot, wt == 0 ? lam0 : 1.f);
-        break;
-      }
-      --wt;
-    }
-  }
+  // The precision entering the run: lambda0 for the first run, else the
+  // matrix waves' window walk (read in step 0, once they have published it).
+  float lam_start = p.lam0 ? p.lam0[(size_t)x.head * RD + L.ch] : 1.f;
   store(pf, 0);
   if (ntl > 1) load(tb + 1, pf, 0);
   __syncthreads();
@@ -343,7 +315,12 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
       const int qs = j < RHOLD ? j : RHOLD + (j & 1), ks = j & 1;
       float ka[16], ka2[16], kp[16], kc[16], kv[16];
       Mob excl, first;
-      (void)scan_chunks(agg_walk16<true>(s, L, w, first, ka, ka2, kp, kc, kv), L.g, excl);
+      (void)scan_chunks(agg_walk16<true>(s.raw[1], L, w, first, ka, ka2, kp, kc, kv), L.g, excl);
+      if (j == 0 && x.run > 0) {
+        while (__hip_atomic_load(&s.ctl[cLamReady], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u)
+          __builtin_amdgcn_s_sleep(1);
+        lam_start = s.lamst[L.ch];
+      }
       const float lam_g = mob_apply(excl, lam_start);
       const float lam_g8 = mob_apply(first, lam_g);  // precision after the chunk's first 8 tokens
       v4s rq[4];
@@ -722,20 +699,74 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
     mres = true;
   };
 
-  // The walkers' window walk: the same barriers, and the same exit.
-  if (run > 0) {
-    int wt = tb - 1;
-    while (true) {
-      __syncthreads();
-      __syncthreads();
-      const bool all = (s.ctl[cVote] | s.ctl[cVote + 1] | s.ctl[cVote + 2] | s.ctl[cVote + 3]) == 0u;
-      if (all || wt == 0) break;
-      --wt;
+  // Precision entering the run (not the first): compose the step matrices of
+  // the tiles before it, newest first, until the image of (0, inf) under the
+  // composed map is below fp32 resolution on every channel, or down to the
+  // sequence start, where lambda0 is applied.  The matrix waves do this while
+  // the walkers stage and compose tile 0; the window tiles go to the first
+  // two Q slots, which the walkers first write after reading the result.
+  unsigned char* const stage = &s.qop[0][0][0][0];
+  auto stage_tile = [&](int wt) {
+    const int t0 = wt * RTL;
+    uint4 buf[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int a = it >> 1, u = tv + 256 * (it & 1), row = u >> 3, xx = (u & 7) << 3;
+      const uint16_t* src = a == 0 ? p.k : a == 1 ? p.ld : a == 2 ? p.pn : p.vp;
+      buf[it] = *reinterpret_cast<const uint4*>(src + hoff + (size_t)(t0 + row) * RD + xx);
     }
-  }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int a = it >> 1, u = tv + 256 * (it & 1), row = u >> 3, xx = (u & 7) << 3;
+      *reinterpret_cast<uint4*>(stage + a * RTL * RD * 2 + raw_off(row, xx)) = buf[it];
+    }
+  };
+  unsigned msync = 0;
+  if (run > 0) stage_tile(tb - 1);  // a full tile: it precedes the run
   __syncthreads();
+  if (run > 0) {
+    WLane L;
+    L.g = G;
+    L.i = li;
+    L.ch = 16 * c + li;
+    L.rr = xe;
+    L.mm = xj;
+    const float lam0 = p.lam0 ? p.lam0[(size_t)head * RD + L.ch] : 1.f;
+    Mob Ptot = mob_identity();
+    int wt = tb - 1;
+    float lam_in;
+    while (true) {
+      float ka[16], ka2[16], kp[16], kc[16], kv[16];
+      Mob excl, first;
+      const Mob Pc = scan_chunks(agg_walk16<false>(stage, L, c, first, ka, ka2, kp, kc, kv), L.g, excl);
+      const Mob Pw = shfl_mob(Pc, 48 + L.i);  // product over the whole tile
+      Ptot = mob_mul(Ptot, Pw);               // the older tile acts first
+      const float lo = Ptot.m01 * fast_rcp(Ptot.m11), hi = Ptot.m00 * fast_rcp(Ptot.m10);
+      const bool conv = hi - lo <= 0x1p-21f * lo;
+      const unsigned long long bad = __ballot(!conv);
+      if (lane == 0) s.ctl[cVote + c] = bad ? 1u : 0u;
+      msync += 4;
+      role_sync(&s.ctl[cXSync], msync);
+      const bool all = (s.ctl[cVote] | s.ctl[cVote + 1] | s.ctl[cVote + 2] | s.ctl[cVote + 3]) == 0u;
+      if (all || wt == 0) {
+        lam_in = mob_apply(Ptot, wt == 0 ? lam0 : 1.f);
+        break;
+      }
+      --wt;
+      msync += 4;
+      role_sync(&s.ctl[cXSync], msync);  // every matrix wave has read the votes and the staged tile
+      stage_tile(wt);
+      msync += 4;
+      role_sync(&s.ctl[cXSync], msync);
+    }
+    if (L.g == 0) s.lamst[L.ch] = lam_in;
+    msync += 4;
+    role_sync(&s.ctl[cXSync], msync);  // all 64 channels written
+    if (x.wave == 4 && lane == 0)
+      __hip_atomic_store(&s.ctl[cLamReady], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
 
-  unsigned xsync = 0;
+  unsigned xsync = msync;
   for (int j = 0; j <= ntl; ++j) {
     if (j >= 1) {
       const int jt = j - 1, tile = tb + jt;
@@ -907,6 +938,7 @@ __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
     s.ctl[cEpoch] = p.nrun > 1 ? ld_relaxed(p.ctrl + kEpoch) : 0u;
     s.ctl[cWSync] = 0u;
     s.ctl[cXSync] = 0u;
+    s.ctl[cLamReady] = 0u;
   }
   __syncthreads();
   // Ticket order is run-major within a group, and all runs of a head fall in
