@@ -63,14 +63,18 @@ int fwd_nseg(int T, int dk, int dv, bool bf16) {
 bool fwd_uses_run(int dk, int dv, bool bf16, bool plain) { return bf16 && plain && dk == 64 && dv == 64; }
 
 struct RunLayout {
-  size_t flag, dv, magg, minc, total;
+  size_t tick, flag, dv, magg, minc, total;
 };
 
 RunLayout run_layout(long long nheads, int nrun) {
   const size_t slots = (size_t)nheads * nrun;
   RunLayout l;
   size_t o = kHeader;
-  o += (size_t)kDoneCounters * 4;  // the fixed done-counter region of every layout (unused here)
+  // The fixed done-counter region of every layout holds the ticket counters
+  // here: like the done counters, each is zero again when a call ends.
+  static_assert(kRunTicketStride * kRunTicketGroups <= kDoneCounters, "ticket counters outside the region");
+  l.tick = o;
+  o += (size_t)kDoneCounters * 4;
   l.flag = o; o += round256(slots * 4 * 4);
   l.dv = o; o += round256(slots * 4 * 64 * 4);
   l.magg = o; o += round256(slots * 4096 * 4);
@@ -393,11 +397,17 @@ int forward_impl(const char* name, const void* q, const void* k, const void* v, 
     r.lpath = lambda_path;
     r.nheads = (int)nheads; r.T = T; r.ntiles = (T + 63) / 64;
     fwd_run_plan(r.nheads, T, device_cus(), r.R0, r.Rb, r.Rx, r.nrun);
-    r.tgroups = r.nheads % 8 == 0 ? 8 : r.nheads % 4 == 0 ? 4 : r.nheads % 2 == 0 ? 2 : 1;
+    r.tgroups = 1;  // the largest divisor of nheads that has a counter
+    for (int g = kRunTicketGroups; g >= 1; --g)
+      if (r.nheads % g == 0) {
+        r.tgroups = g;
+        break;
+      }
     const RunLayout rl = run_layout(nheads, r.nrun);
     const int rc = take(rl.total, rl.dv);
     if (rc != KLA_OK) return rc;
     r.ctrl = reinterpret_cast<unsigned*>(ws);
+    r.tick = reinterpret_cast<unsigned*>(ws + rl.tick);
     r.flag = reinterpret_cast<unsigned*>(ws + rl.flag);
     r.dv = reinterpret_cast<float*>(ws + rl.dv);
     r.magg = reinterpret_cast<float*>(ws + rl.magg);

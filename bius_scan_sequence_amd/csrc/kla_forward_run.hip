@@ -933,8 +933,12 @@ __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
   __shared__ RunSmem s;
   const int tid = threadIdx.x;
   if (tid == 0) {
-    s.ctl[cTicket] = __hip_atomic_fetch_add(p.ctrl + kTicket + blockIdx.x % (unsigned)p.tgroups, 1u, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
+    // The group's counter takes nheads / tgroups * nrun tickets per call; the
+    // workgroup that draws the last one sets it back to zero for the next call.
+    unsigned* const tk = p.tick + kRunTicketStride * (blockIdx.x % (unsigned)p.tgroups);
+    const unsigned t = __hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == (unsigned)p.nheads / (unsigned)p.tgroups * (unsigned)p.nrun - 1u) st_relaxed(tk, 0u);
+    s.ctl[cTicket] = t;
     s.ctl[cEpoch] = p.nrun > 1 ? ld_relaxed(p.ctrl + kEpoch) : 0u;
     s.ctl[cWSync] = 0u;
     s.ctl[cXSync] = 0u;
@@ -975,12 +979,11 @@ __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
   else
     matrix_role(p, s, x);
   __syncthreads();
-  // Count the workgroup done; the last one resets the ticket and the counter
-  // and advances the call epoch (the flags of the next call differ).
+  // Count the workgroup done; the last one resets the counter and advances
+  // the call epoch (the flags of the next call differ).
   if (tid == 0) {
     const unsigned ng = (unsigned)p.nheads * (unsigned)p.nrun;
     if (__hip_atomic_fetch_add(p.ctrl + kGroupsDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ng - 1) {
-      for (int g = 0; g < p.tgroups; ++g) st_relaxed(p.ctrl + kTicket + g, 0u);
       st_relaxed(p.ctrl + kGroupsDone, 0u);
       if (p.nrun > 1) st_relaxed(p.ctrl + kEpoch, epoch + 1u);
     }

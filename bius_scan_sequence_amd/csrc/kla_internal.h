@@ -9,7 +9,8 @@ namespace kla {
 // Control words at the head of every workspace (32-bit each).  Words 0 and 1
 // hold the call epoch and the groups-done counter (kla_device.h).
 // kTicket: eight words (8..15) of ticket counters, one per group of
-// workgroups of the run-streaming forward (blockIdx % groups).
+// workgroups (blockIdx % groups) of the segmented forward and the precision
+// scan (the run-streaming forward keeps its own, one per line).
 enum CtrlWord { kError = 3, kTicket = 8 };
 
 // Done counters: a fixed region of kDoneCounters words right after the
@@ -167,13 +168,18 @@ struct FwdRunParams {
   float* lpath;        // nullable
   int nheads, T, ntiles, nrun;
   int R0, Rb, Rx;      // run 0 takes R0 tiles; run r >= 1 takes Rb, plus one if r - 1 < Rx
-  int tgroups;         // ticket groups (1, 2, 4 or 8; divides nheads): group x takes the heads h = x mod tgroups
-  unsigned* ctrl;      // workspace control words (epoch, groups done, error, tickets)
+  int tgroups;         // ticket groups (divides nheads, at most kRunTicketGroups): group x takes the heads h = x mod tgroups
+  unsigned* ctrl;      // workspace control words (epoch, groups done, error)
+  unsigned* tick;      // ticket counters, group x at word kRunTicketStride * x (zero between calls)
   unsigned* flag;      // [nheads*nrun][4] mean-carry flags, one per matrix wave
   float* dv;           // [nheads*nrun][4][64] prod of forget gates over the run (a copy per wave)
   float* magg;         // [nheads*nrun][4096] local mean state of the run (fragment order)
   float* minc;         // [nheads*nrun][4096] mean state after the run (fragment order)
 };
+// Ticket counters of the run-streaming forward: one per 64-byte line, so
+// that the workgroups starting together spread their atomics over many lines.
+constexpr int kRunTicketStride = 16;
+constexpr int kRunTicketGroups = 256;
 void fwd_run_plan(int nheads, int T, int ncu, int& R0, int& Rb, int& Rx, int& nrun);
 hipError_t launch_forward_run(const FwdRunParams& p, hipStream_t stream);
 
