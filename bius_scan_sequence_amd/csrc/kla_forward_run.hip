@@ -991,15 +991,17 @@ __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
 }
 
 // Runs per head: the count that minimises (rounds of workgroups) x (tiles
-// per workgroup) on `ncu` compute units, fewest runs on ties.  Every run but
-// the first starts with a window walk (about one tile's time), and every run
-// resolves its entering mean only once all earlier runs have published, so
-// the first run takes kFirstExtra tiles more than an even share to end its
-// loop with the others; the other runs split the rest as evenly as they can.
-constexpr int kFirstExtra = 1;
+// per workgroup) on `ncu` compute units, fewest runs on ties.  Every run
+// resolves its entering mean only once all earlier runs have published.  When
+// all runs of a head run in one round, they end their loops together, and the
+// first run, whose mean is known from the start, takes one tile more than an
+// even share (the others begin with a window walk, about a tile's time, and
+// correct their held tiles at the end); with several rounds a run's
+// predecessors have mostly finished before it starts, and the runs split the
+// tiles evenly.
 void fwd_run_plan(int nheads, int T, int ncu, int& R0, int& Rb, int& Rx, int& nrun) {
   const int ntiles = (T + RTL - 1) / RTL;
-  long long best = -1;
+  long long best = -1, best_rounds = 1;
   int bestn = 1;
   for (int n = 1; n <= ntiles; ++n) {
     const int r = (ntiles + n - 1) / n;
@@ -1009,16 +1011,18 @@ void fwd_run_plan(int nheads, int T, int ncu, int& R0, int& Rb, int& Rx, int& nr
     const long long cost = rounds * r;
     if (best < 0 || cost < best) {
       best = cost;
+      best_rounds = rounds;
       bestn = n;
     }
   }
   nrun = bestn;
+  const int first_extra = best_rounds == 1 ? 1 : 0;
   if (nrun == 1) {
     R0 = ntiles;
     Rb = Rx = 0;
     return;
   }
-  R0 = min((ntiles + nrun - 1) / nrun + kFirstExtra, ntiles - (nrun - 1));
+  R0 = min((ntiles + nrun - 1) / nrun + first_extra, ntiles - (nrun - 1));
   const int rest = ntiles - R0;
   Rb = rest / (nrun - 1);
   Rx = rest % (nrun - 1);
