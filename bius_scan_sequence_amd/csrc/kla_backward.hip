@@ -104,7 +104,8 @@ template <int V, bool BF16> struct VRow {
   static constexpr int P = BF16 ? V + 4 : V + 1;
 };
 
-// Stages the segment's tokens: log2 f, g, q as [64][K+1] and v, dy as
+// Stages the segment's tokens: log2 f, g, q as [64][K+1] (q in fp32 or, for
+// bf16 inputs, in its own bf16 bits) and v, dy as
 // [64][VRow::P] (rows padded so that column walks hit distinct banks), then
 // turns log2 f into the cumulative sum inside each 16-token chunk (lb) and
 // writes each chunk's total to T[4][K].  Tokens past T are identity steps:
@@ -112,9 +113,9 @@ template <int V, bool BF16> struct VRow {
 // of a short sum: inside a chunk lb_l - lb_m, across chunks the chunk totals
 // in between (never a difference of two long cumulative sums).  A thread
 // stages four consecutive channels of a token with vector loads.
-template <int K, int V, bool BF16, int NT>
+template <int K, int V, bool BF16, int NT, typename QT>
 __device__ __forceinline__ void stage_segment(const BwdParams& p, size_t hd, int t0, float* slb, float* sg,
-                                              float* sq, typename VRow<V, BF16>::T* sv,
+                                              QT* sq, typename VRow<V, BF16>::T* sv,
                                               typename VRow<V, BF16>::T* sd, float* sT, int* unsafe) {
   using In = typename std::conditional<BF16, uint16_t, float>::type;
   constexpr int KP = K + 1, VP = VRow<V, BF16>::P, K4 = K / 4, V4 = V / 4;
@@ -148,7 +149,7 @@ __device__ __forceinline__ void stage_segment(const BwdParams& p, size_t hd, int
     for (int r = 0; r < 4; ++r) {
       slb[t * KP + i + r] = lf[r];
       sg[t * KP + i + r] = g[r];
-      sq[t * KP + i + r] = q[r];
+      sq[t * KP + i + r] = from_f32<QT>(q[r]);  // exact: q is a value of the input type
     }
   }
 #pragma unroll
@@ -347,16 +348,16 @@ __global__ __launch_bounds__(256) void kla_bwd_segscan_kernel(BwdParams p) {
 // chunks take the exact elementwise path, with every D(l, m) from its own
 // exp2.
 // ---------------------------------------------------------------------------
+// The in-chunk decays E_l = exp2(lb_l - lb_7), F_l = exp2(lb_7 - lb_l),
+// cp_l = exp2(lb_l) (prod_{u<=l} f_u) and sx_l = exp2(T_c - lb_l)
+// (prod_{u>l} f_u) are formed where they are used, from the staged lb.
 template <int K, int V, bool BF16>
 struct BwdChunkSmem {
   using SV = typename VRow<V, BF16>::T;
   static constexpr int KP = K + 1, VP = VRow<V, BF16>::P;
-  float lb[kSL * KP], g[kSL * KP], q[kSL * KP];
+  float lb[kSL * KP], g[kSL * KP];
+  SV q[kSL * KP];
   SV v[kSL * VP], d[kSL * VP];
-  float E[kC * KP];           // exp2(lb_l - lb_7)
-  float F[kC * KP];           // exp2(lb_7 - lb_l)
-  float cp[kC * KP];          // prod_{u<=l} f_u inside the chunk
-  float sx[kC * KP];          // prod_{u>l} f_u inside the chunk
   float qE[kC * KP];          // q_l E_l
   float gF[kC * KP];          // g_l F_l
   float kd[kC * KP];          // g_l sx_l (write gate decayed to the chunk end)
@@ -382,22 +383,35 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
   const float* Gg = p.Gseg + st;
   const int kb_w = wave, vb_w = wave - 4;       // key block of a key wave, value block of a value wave
   const bool kw = wave < KB, vw = wave >= 4 && vb_w < VB;
-  // Adjoint at the segment end (H for value waves, H^T for key waves) and the
-  // mean entering the segment (M^T, key waves), loaded before staging.
-  v4f Hc[KB], Ht[VB], Mt[VB], Ms[VB];
-#pragma unroll
-  for (int ib = 0; ib < KB; ++ib)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Hc[ib][e] = vw ? Gg[(ib * 16 + 4 * lg + e) * V + vb_w * 16 + lr] : 0.f;
-#pragma unroll
-  for (int jb = 0; jb < VB; ++jb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      Ht[jb][e] = kw ? Gg[(kb_w * 16 + lr) * V + jb * 16 + 4 * lg + e] : 0.f;
-      Ms[jb][e] = kw ? Mg[(kb_w * 16 + lr) * V + jb * 16 + 4 * lg + e] : 0.f;
-    }
   if (tid < 4) s.unsafe[tid] = 0;
   stage_segment<K, V, BF16, NT>(p, hd, t0, s.lb, s.g, s.q, s.v, s.d, s.T, s.unsafe);
+  // Adjoint at the segment end and the mean entering the segment, loaded
+  // after staging (fewer registers live at once).  A value wave keeps H
+  // tiles (Hc[ib], ib < KB), a key wave H^T tiles (Ht[jb], jb < VB) in the
+  // same registers, and M^T (Ms).
+  constexpr int HB = KB > VB ? KB : VB;
+  v4f Hx[HB], Mt[VB], Ms[VB];
+  v4f(&Hc)[HB] = Hx;
+  v4f(&Ht)[HB] = Hx;
+#pragma unroll
+  for (int b = 0; b < HB; ++b) {
+    Hx[b] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (b < VB) Ms[b] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  if (vw) {  // wave-uniform branches: every load of a wave issued together
+#pragma unroll
+    for (int ib = 0; ib < KB; ++ib)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Hc[ib][e] = Gg[(ib * 16 + 4 * lg + e) * V + vb_w * 16 + lr];
+  } else if (kw) {
+#pragma unroll
+    for (int jb = 0; jb < VB; ++jb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Ht[jb][e] = Gg[(kb_w * 16 + lr) * V + jb * 16 + 4 * lg + e];
+        Ms[jb][e] = Mg[(kb_w * 16 + lr) * V + jb * 16 + 4 * lg + e];
+      }
+  }
 
   for (int w = (nvalid - 1) / C; w >= 0; --w) {
     const int c0 = w * C;
@@ -407,11 +421,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
       const float lb = s.lb[(c0 + l) * KP + i], lb7 = s.lb[(c0 + 7) * KP + i];
       const float tot = s.T[w * K + i];
       const float E = ex2(lb - lb7), F = ex2(lb7 - lb), cp = ex2(lb), sx = ex2(tot - lb);
-      const float q = s.q[(c0 + l) * KP + i], g = s.g[(c0 + l) * KP + i];
-      s.E[l * KP + i] = E;
-      s.F[l * KP + i] = F;
-      s.cp[l * KP + i] = cp;
-      s.sx[l * KP + i] = sx;
+      const float q = to_f32(s.q[(c0 + l) * KP + i]), g = s.g[(c0 + l) * KP + i];
       s.qE[l * KP + i] = q * E;
       s.gF[l * KP + i] = g * F;
       s.kd[l * KP + i] = g * sx;
@@ -487,7 +497,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
       float acc = 0.f;
       if (m <= l && tid < C * C)
         for (int i = 0; i < K; ++i)
-          acc = fmaf(s.q[(c0 + l) * KP + i] * s.g[(c0 + m) * KP + i],
+          acc = fmaf(to_f32(s.q[(c0 + l) * KP + i]) * s.g[(c0 + m) * KP + i],
                      ex2(s.lb[(c0 + l) * KP + i] - s.lb[(c0 + m) * KP + i]), acc);
       if (tid < C * C) s.A[l * C + m] = acc;
     }
@@ -518,11 +528,12 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
         }
         dqi = mma_f32(dqi, a, b);
         dgi = mma_f32(dgi, c, d);
+        const float lb7 = s.lb[(c0 + 7) * KP + i];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int l = 4 * lg + e;
-          dqi[e] *= s.E[l * KP + i];
-          dgi[e] *= s.F[l * KP + i];
+          const float lb = s.lb[(c0 + 4 * lg + e) * KP + i];
+          dqi[e] *= ex2(lb - lb7);
+          dgi[e] *= ex2(lb7 - lb);
         }
       } else {
 #pragma unroll
@@ -533,7 +544,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
           for (int m = 0; m < C; ++m) {
             const float lbm = s.lb[(c0 + m) * KP + i];
             if (m <= l) aq = fmaf(s.B[l * C + m] * s.g[(c0 + m) * KP + i], ex2(lbl - lbm), aq);
-            if (m >= l) ag = fmaf(s.B[m * C + l] * s.q[(c0 + m) * KP + i], ex2(lbm - lbl), ag);
+            if (m >= l) ag = fmaf(s.B[m * C + l] * to_f32(s.q[(c0 + m) * KP + i]), ex2(lbm - lbl), ag);
           }
           dqi[e] = aq;
           dgi[e] = ag;
@@ -543,10 +554,11 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
       for (int e = 0; e < 4; ++e) {
         const int l = 4 * lg + e;
         if (c0 + l >= nvalid) continue;
-        const float dq = fmaf(s.cp[l * KP + i], xs[e], dqi[e]);
-        const float dg = fmaf(s.sx[l * KP + i], ys[e], dgi[e]);
+        const float lb = s.lb[(c0 + l) * KP + i];
+        const float dq = fmaf(ex2(lb), xs[e], dqi[e]);
+        const float dg = fmaf(ex2(s.T[w * K + i] - lb), ys[e], dgi[e]);
         const size_t ow = (tok0 + l) * p.kws + i;
-        const float ee = s.q[(c0 + l) * KP + i] * dq - s.g[(c0 + l) * KP + i] * dg;
+        const float ee = to_f32(s.q[(c0 + l) * KP + i]) * dq - s.g[(c0 + l) * KP + i] * dg;
         if (p.dq_acc) {
           p.dq_acc[ow] = p.add_dq ? p.dq_acc[ow] + dq : dq;
         } else {
@@ -600,7 +612,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
           v4f a, b;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            Hc[ib][e] *= s.cp[(C - 1) * KP + ib * 16 + 4 * lg + e];
+            Hc[ib][e] *= ex2(s.lb[(c0 + C - 1) * KP + ib * 16 + 4 * lg + e]);
             a[e] = s.be[(4 * lg + e) * KP + ib * 16 + lr];
             b[e] = to_f32(s.d[(c0 + 4 * lg + e) * VP + vb_w * 16 + lr]);
           }
@@ -609,7 +621,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
       }
       if (kw) {
         const int i = kb_w * 16 + lr;
-        const float ce = s.cp[(C - 1) * KP + i];
+        const float ce = ex2(s.lb[(c0 + C - 1) * KP + i]);
 #pragma unroll
         for (int jb = 0; jb < VB; ++jb) {
           v4f a, b;

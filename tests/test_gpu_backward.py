@@ -272,6 +272,33 @@ def test_backward_full_size_sampled_heads():
         compare(f"full size head ({b},{h})", x, got, ref)
 
 
+def test_backward_long_full_size_sampled_head():
+    """The long-context backward shape at full size (B=2, H=16, T=16384,
+    d=128, bf16, long-memory decays), generated on the device and run in the
+    launch configuration the benchmark times; every gradient of one sampled
+    head against the oracle (about a minute and a half of float64 work)."""
+    import torch
+    import bius_scan_sequence_amd as K
+    w = KI.workload("bwd_long_bf16")
+    say(f"[case] backward full size {w.B}x{w.H}x{w.T} d={w.dk} bf16 seed={w.seed}")
+    xd = KI.make_forward_inputs_torch(w, device="cuda")
+    gy = KI.make_backward_grads_torch(w, device="cuda")
+    _, _, _, lpath = K.forward(*(xd[n] for n in NAMES), return_lambda_path=True)
+    out = K.backward(*(xd[n] for n in NAMES), gy, lpath)
+    torch.cuda.synchronize()
+    say("[step] full-size long backward done; oracle on one head")
+    b, h = 1, 11
+    x = {n: xd[n][b:b + 1, h:h + 1].float().cpu().numpy() for n in NAMES}
+    x["dtype"] = "bf16"
+    x["lambda0"] = np.ones((1, 1, w.dk), np.float32)
+    x["M0"] = np.zeros((1, 1, w.dk, w.dv), np.float32)
+    gh = {"grad_y": gy[b:b + 1, h:h + 1].float().cpu().numpy(), "grad_lambda_T": None, "grad_M_T": None}
+    got = dict(zip(GRADS, (t[b:b + 1, h:h + 1].float().cpu().numpy() for t in out)))
+    del out, xd, gy, lpath
+    ref = oracle_backward(x, gh)
+    compare(f"full size long head ({b},{h})", x, got, ref)
+
+
 def test_backward_long_recipe_d128():
     """The long-memory recipe (log_decay = -softplus(N(-2, 1))) at d = 128 over
     4096 tokens, generated on the device; one sampled head against the
