@@ -58,23 +58,20 @@ def run_plan(nheads, T, ncu):
     """Runs per head and their tile counts as the library plans them for the
     run-streaming kernel (kla_forward_run.hip, fwd_run_plan): the run count
     that minimises rounds of workgroups x tiles per workgroup (fewest runs on
-    ties); when every workgroup fits in one round, run 0 takes one tile more
-    than an even share, and the other runs split the rest evenly.  Returns
-    the list of tile counts, one per run."""
+    ties), the tiles split as evenly as they go.  Returns the list of tile
+    counts, one per run."""
     ntiles = (T + 63) // 64
-    best, bestn, best_rounds = None, 1, 1
+    best, bestn = None, 1
     for n in range(1, ntiles + 1):
         r = (ntiles + n - 1) // n
         if (ntiles + r - 1) // r != n:
             continue
-        rounds = (nheads * n + ncu - 1) // ncu
-        cost = rounds * r
+        cost = ((nheads * n + ncu - 1) // ncu) * r
         if best is None or cost < best:
-            best, bestn, best_rounds = cost, n, rounds
+            best, bestn = cost, n
     if bestn == 1:
         return [ntiles]
-    extra = 1 if best_rounds == 1 else 0
-    r0 = min((ntiles + bestn - 1) // bestn + extra, ntiles - (bestn - 1))
+    r0 = min((ntiles + bestn - 1) // bestn, ntiles - (bestn - 1))
     rest = ntiles - r0
     rb, rx = divmod(rest, bestn - 1)
     return [r0] + [rb + (1 if k < rx else 0) for k in range(bestn - 1)]

@@ -103,9 +103,38 @@ def build_host_sanitized(verbose: bool = False) -> str:
     return SAN_LIB
 
 
+# Timeline build: the run-streaming forward compiled with -DKLA_TIMELINE (per
+# workgroup real-time stamps, read by bius_scan_sequence_amd/timeline.py);
+# every other object is the ordinary one.
+TL_DIR = os.path.join(BUILD, "timeline")
+TL_LIB = os.path.join(PKG, "libkla_timeline.so")
+
+
+def build_timeline(verbose: bool = False) -> str:
+    """Builds TL_LIB next to libkla.so, reusing the ordinary objects when they exist."""
+    if not all(os.path.exists(os.path.join(BUILD, os.path.splitext(s)[0] + ".o")) for s in SOURCES):
+        build()
+    os.makedirs(TL_DIR, exist_ok=True)
+    obj = os.path.join(TL_DIR, "kla_forward_run_tl.o")
+    cmd = [hipcc(), *common_flags(), "-DKLA_TIMELINE", "-c", os.path.join(CSRC, "kla_forward_run.hip"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    objs = [obj] + [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "kla_forward_run.hip"]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", TL_LIB, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print("built", TL_LIB)
+    return TL_LIB
+
+
 if __name__ == "__main__":
     if "--host-sanitized" in sys.argv:
         build_host_sanitized(verbose=True)
+    elif "--timeline" in sys.argv:
+        build_timeline(verbose=True)
     else:
         build(verbose=True)
     sys.exit(0)

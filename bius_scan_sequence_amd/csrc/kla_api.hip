@@ -396,7 +396,9 @@ int forward_impl(const char* name, const void* q, const void* k, const void* v, 
     r.lam0 = lambda0; r.M0 = M0; r.y = static_cast<uint16_t*>(y); r.lamT = lambda_T; r.MT = M_T;
     r.lpath = lambda_path;
     r.nheads = (int)nheads; r.T = T; r.ntiles = (T + 63) / 64;
-    fwd_run_plan(r.nheads, T, device_cus(), r.R0, r.Rb, r.Rx, r.nrun);
+    bool one_round = false;
+    fwd_run_plan(r.nheads, T, device_cus(), r.R0, r.Rb, r.Rx, r.nrun, one_round);
+    r.agg_always = one_round ? 1 : 0;
     r.tgroups = 1;  // the largest divisor of nheads that has a counter
     for (int g = kRunTicketGroups; g >= 1; --g)
       if (r.nheads % g == 0) {

@@ -53,12 +53,35 @@
 #include "kla_internal.h"
 
 namespace kla {
+
+#ifdef KLA_TIMELINE
+// Timeline tracing, built only with -DKLA_TIMELINE (build.py --timeline; the
+// library then also exports kla_timeline_read and kla_timeline_clear).  The
+// first lane of wave 0 (a walker) and of wave 4 (a matrix wave) of every
+// workgroup records the 100 MHz real-time counter at fixed points of its
+// role, into kla_timeline_buf[workgroup][role][slot].
+constexpr int kTlSlots = 64, kTlGroups = 4096;
+__device__ unsigned long long kla_timeline_buf[kTlGroups * 2 * kTlSlots];
+#define KLA_STAMP(role, k)                                                                              \
+  do {                                                                                                  \
+    const int kla_slot_ = (k);                                                                          \
+    if ((threadIdx.x & 255) == 0 && blockIdx.x < (unsigned)kTlGroups && kla_slot_ < kTlSlots)           \
+      kla_timeline_buf[((size_t)blockIdx.x * 2 + (role)) * kTlSlots + kla_slot_] =                      \
+          __builtin_amdgcn_s_memrealtime();                                                             \
+  } while (0)
+#else
+#define KLA_STAMP(role, k) \
+  do {                     \
+  } while (0)
+#endif
+
 namespace {
 
 constexpr int RD = 64;     // d_k = d_v
 constexpr int RTL = 64;    // tokens per tile
 constexpr int RNT = 512;   // threads
 constexpr int RHOLD = 2;   // leading tiles of a run held for the entering-mean correction
+constexpr int kNoSlot = 1 << 20;  // a timeline slot past the end: not recorded
 constexpr float kTiny = 0x1p-100f;
 constexpr float kMinBig = 0x1p40f;
 
@@ -304,6 +327,7 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
   store(pf, 0);
   if (ntl > 1) load(tb + 1, pf, 0);
   __syncthreads();
+  KLA_STAMP(0, 2);
 
   unsigned wsync = 0;
   float dtile = 1.f;  // decay of this channel from the run start to the tile start
@@ -315,7 +339,10 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
       const int qs = j < RHOLD ? j : RHOLD + (j & 1), ks = j & 1;
       float ka[16], ka2[16], kp[16], kc[16], kv[16];
       Mob excl, first;
+      [[maybe_unused]] const int ts = j < 8 ? 3 + 7 * j : kNoSlot;  // timeline slots of this step
+      KLA_STAMP(0, ts);
       (void)scan_chunks(agg_walk16<true>(s.raw[1], L, w, first, ka, ka2, kp, kc, kv), L.g, excl);
+      KLA_STAMP(0, ts + 1);
       if (j == 0 && x.run > 0) {
         while (__hip_atomic_load(&s.ctl[cLamReady], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u)
           __builtin_amdgcn_s_sleep(1);
@@ -395,6 +422,7 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      KLA_STAMP(0, ts + 2);
       // Precision after the tile, for the next tile (from chunk 3's walk).
       const float lam_end = __shfl(n[1] * fast_rcp(d[1]), 48 + L.i, 64);
       const float cp8a = __builtin_amdgcn_ldexpf(Ab[0] * rn8[0] * lam_g, -exg[0][0]);
@@ -453,8 +481,10 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
         s.ctl[cNotFree + 4 * ks + w] = notfree ? 1u : 0u;
       }
       dtile *= __shfl(ip, 48 + L.i, 64);
+      KLA_STAMP(0, ts + 3);
       wsync += 4;
       role_sync(&s.ctl[cWSync], wsync);
+      KLA_STAMP(0, ts + 4);
       // Causal scores of chunk w for every matrix wave: S^T[u][t] = Kt_u . Qt_t
       // (u, t tokens of the chunk; zero where u > t), as split B operands.
       {
@@ -476,6 +506,7 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
         split4(S, Sh, Sl);
         *reinterpret_cast<v8s*>(s.sop[ks][r] + 16 * lane) = cat(Sh, Sl);
       }
+      KLA_STAMP(0, ts + 5);
       const unsigned um = s.ctl[cUnsafe + 4 * ks] | s.ctl[cUnsafe + 4 * ks + 1] | s.ctl[cUnsafe + 4 * ks + 2] |
                           s.ctl[cUnsafe + 4 * ks + 3];
       if ((um >> L.g) & 1u) {
@@ -508,6 +539,7 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
         if (L.g == 0) s.dend[L.ch] = dtile;
         if (x.last_run && L.g == 0) p.lamT[(size_t)x.head * RD + L.ch] = lam_start;
       }
+      KLA_STAMP(0, ts + 6);
     }
     __syncthreads();
   }
@@ -766,6 +798,7 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
       __hip_atomic_store(&s.ctl[cLamReady], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 
+  KLA_STAMP(1, 2);
   unsigned xsync = msync;
   for (int j = 0; j <= ntl; ++j) {
     if (j >= 1) {
@@ -869,24 +902,32 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
         }
       }
     }
+    KLA_STAMP(1, j < 10 ? 3 + 2 * j : kNoSlot);
     if (j < ntl) {
       xsync += 4;
       role_sync(&s.ctl[cXSync], xsync);
       v_store();
       if (j + 1 < ntl) v_load(tb + j + 1);
     }
+    KLA_STAMP(1, j < 10 ? 4 + 2 * j : kNoSlot);
     __syncthreads();
   }
 
   // End of the run: the mean carry.
+  KLA_STAMP(1, 40);
+  v4f D[4];
   if (!mres) {
-    v4f D[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) D[rt] = lds4(s.dend, rt);
     // Publish the run's aggregate (prod f over the run, local state) unless
-    // the predecessor's inclusive carry is already out or nothing follows.
-    const unsigned fprev = ld_relaxed(hflag + 4 * (run - 1));
-    if (fprev != x.FINC && !x.last_run) {
+    // nothing follows.  When all runs of a head are resident together, this
+    // is done even if the predecessor's inclusive carry is already out: the
+    // later runs, which end their loops at the same time, then fold it at
+    // once instead of waiting for this run's own look-back.  With several
+    // rounds of workgroups the predecessors have mostly finished, and the
+    // aggregate is skipped when the inclusive carry is there.
+    const bool skip = !p.agg_always && ld_relaxed(hflag + 4 * (run - 1)) == x.FINC;
+    if (!x.last_run && !skip) {
       const auto ragg = coherent_rsrc(p.magg + hs * 4096 + c * 1024, 4096);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) st_coherent(ragg, (rt * 64 + lane) * 16, Mst[rt]);
@@ -898,8 +939,37 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
       wait_stores();
       if (lane == 0) st_relaxed(hflag + 4 * run, x.FAGG);
     }
+  }
+  // The state after the run (inclusive mean): published for the runs after
+  // it, or written as M_T by the last run.
+  auto publish = [&]() {
+    if (!x.last_run) {
+      const auto rinc = coherent_rsrc(p.minc + hs * 4096 + c * 1024, 4096);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) st_coherent(rinc, (rt * 64 + lane) * 16, Mst[rt]);
+      wait_stores();
+      if (lane == 0) st_relaxed(hflag + 4 * run, x.FINC);
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p.MT[(size_t)head * 4096 + (16 * rt + 4 * G + e) * RD + 16 * c + li] = Mst[rt][e];
+    }
+  };
+  if (!mres) {
+    KLA_STAMP(1, 41);
     v4f Min[4];
     lookback_mean(Min, std::true_type{});
+    KLA_STAMP(1, 42);
+    // The inclusive mean goes out before the held tiles are corrected (the
+    // correction changes outputs only): a successor waiting on it does not
+    // wait for the correction too.
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Mst[rt][e] = fmaf(D[rt][e], Min[rt][e], Mst[rt][e]);
+    publish();
+    KLA_STAMP(1, 43);
     if (ntl >= RHOLD) {
 #pragma unroll
       for (int k = 0; k < 4 * RHOLD; ++k) correct(k, Yh[k], Min);
@@ -907,23 +977,11 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
 #pragma unroll
       for (int k = 0; k < 4; ++k) correct(k, Yh[k], Min);
     }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Mst[rt][e] = fmaf(D[rt][e], Min[rt][e], Mst[rt][e]);
-  }
-  if (!x.last_run) {
-    const auto rinc = coherent_rsrc(p.minc + hs * 4096 + c * 1024, 4096);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) st_coherent(rinc, (rt * 64 + lane) * 16, Mst[rt]);
-    wait_stores();
-    if (lane == 0) st_relaxed(hflag + 4 * run, x.FINC);
   } else {
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p.MT[(size_t)head * 4096 + (16 * rt + 4 * G + e) * RD + 16 * c + li] = Mst[rt][e];
+    publish();
+    KLA_STAMP(1, 43);
   }
+  KLA_STAMP(1, 44);
 }
 
 }  // namespace
@@ -932,6 +990,7 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
 __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
   __shared__ RunSmem s;
   const int tid = threadIdx.x;
+  KLA_STAMP(tid >> 8, 0);
   if (tid == 0) {
     // The group's counter takes nheads / tgroups * nrun tickets per call; the
     // workgroup that draws the last one sets it back to zero for the next call.
@@ -974,6 +1033,13 @@ __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
   }
   x.hoff = (size_t)x.head * p.T * RD;
   x.last_run = x.run == p.nrun - 1;
+  KLA_STAMP(tid >> 8, 1);
+#ifdef KLA_TIMELINE
+  if (tid == 0 && blockIdx.x < (unsigned)kTlGroups) {
+    kla_timeline_buf[(size_t)blockIdx.x * 2 * kTlSlots + 62] = (unsigned long long)x.run;
+    kla_timeline_buf[(size_t)blockIdx.x * 2 * kTlSlots + 63] = (unsigned long long)x.ntl;
+  }
+#endif
   if (x.wave < 4)
     walker_role(p, s, x);
   else
@@ -991,15 +1057,10 @@ __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
 }
 
 // Runs per head: the count that minimises (rounds of workgroups) x (tiles
-// per workgroup) on `ncu` compute units, fewest runs on ties.  Every run
-// resolves its entering mean only once all earlier runs have published.  When
-// all runs of a head run in one round, they end their loops together, and the
-// first run, whose mean is known from the start, takes one tile more than an
-// even share (the others begin with a window walk, about a tile's time, and
-// correct their held tiles at the end); with several rounds a run's
-// predecessors have mostly finished before it starts, and the runs split the
-// tiles evenly.
-void fwd_run_plan(int nheads, int T, int ncu, int& R0, int& Rb, int& Rx, int& nrun) {
+// per workgroup) on `ncu` compute units, fewest runs on ties; the tiles are
+// split as evenly as they go (the first Rx runs after run 0 take one more).
+// one_round: every run of every head is resident at once.
+void fwd_run_plan(int nheads, int T, int ncu, int& R0, int& Rb, int& Rx, int& nrun, bool& one_round) {
   const int ntiles = (T + RTL - 1) / RTL;
   long long best = -1, best_rounds = 1;
   int bestn = 1;
@@ -1016,13 +1077,13 @@ void fwd_run_plan(int nheads, int T, int ncu, int& R0, int& Rb, int& Rx, int& nr
     }
   }
   nrun = bestn;
-  const int first_extra = best_rounds == 1 ? 1 : 0;
+  one_round = best_rounds == 1;
   if (nrun == 1) {
     R0 = ntiles;
     Rb = Rx = 0;
     return;
   }
-  R0 = min((ntiles + nrun - 1) / nrun + first_extra, ntiles - (nrun - 1));
+  R0 = min((ntiles + nrun - 1) / nrun, ntiles - (nrun - 1));
   const int rest = ntiles - R0;
   Rb = rest / (nrun - 1);
   Rx = rest % (nrun - 1);
@@ -1034,3 +1095,15 @@ hipError_t launch_forward_run(const FwdRunParams& p, hipStream_t stream) {
 }
 
 }  // namespace kla
+
+#ifdef KLA_TIMELINE
+extern "C" int kla_timeline_read(void* host, size_t bytes) {
+  const size_t n = sizeof(kla::kla_timeline_buf);
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(kla::kla_timeline_buf), bytes < n ? bytes : n, 0,
+                                  hipMemcpyDeviceToHost);
+}
+extern "C" int kla_timeline_clear() {
+  static unsigned long long zeros[kla::kTlGroups * 2 * kla::kTlSlots];
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(kla::kla_timeline_buf), zeros, sizeof(zeros), 0, hipMemcpyHostToDevice);
+}
+#endif

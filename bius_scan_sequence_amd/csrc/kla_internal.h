@@ -168,6 +168,7 @@ struct FwdRunParams {
   float* lpath;        // nullable
   int nheads, T, ntiles, nrun;
   int R0, Rb, Rx;      // run 0 takes R0 tiles; run r >= 1 takes Rb, plus one if r - 1 < Rx
+  int agg_always;      // every run but the last publishes its aggregate (all runs resident at once)
   int tgroups;         // ticket groups (divides nheads, at most kRunTicketGroups): group x takes the heads h = x mod tgroups
   unsigned* ctrl;      // workspace control words (epoch, groups done, error)
   unsigned* tick;      // ticket counters, group x at word kRunTicketStride * x (zero between calls)
@@ -180,7 +181,7 @@ struct FwdRunParams {
 // that the workgroups starting together spread their atomics over many lines.
 constexpr int kRunTicketStride = 16;
 constexpr int kRunTicketGroups = 256;
-void fwd_run_plan(int nheads, int T, int ncu, int& R0, int& Rb, int& Rx, int& nrun);
+void fwd_run_plan(int nheads, int T, int ncu, int& R0, int& Rb, int& Rx, int& nrun, bool& one_round);
 hipError_t launch_forward_run(const FwdRunParams& p, hipStream_t stream);
 
 int fwd_segment_len(int dk, int dv, bool bf16);
