@@ -69,9 +69,18 @@ __device__ unsigned long long kla_timeline_buf[kTlGroups * 2 * kTlSlots];
       kla_timeline_buf[((size_t)blockIdx.x * 2 + (role)) * kTlSlots + kla_slot_] =                      \
           __builtin_amdgcn_s_memrealtime();                                                             \
   } while (0)
+// A value (a path counter) in place of a time.
+#define KLA_VALUE(role, k, v)                                                                           \
+  do {                                                                                                  \
+    if ((threadIdx.x & 255) == 0 && blockIdx.x < (unsigned)kTlGroups)                                   \
+      kla_timeline_buf[((size_t)blockIdx.x * 2 + (role)) * kTlSlots + (k)] = (unsigned long long)(v);   \
+  } while (0)
 #else
 #define KLA_STAMP(role, k) \
   do {                     \
+  } while (0)
+#define KLA_VALUE(role, k, v) \
+  do {                        \
   } while (0)
 #endif
 
@@ -706,7 +715,9 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
   // Resolve the entering mean mid-run: fold the predecessors' carries
   // (M_in), correct the first `nheld` held chunks, and add diag(D) M_in to
   // the state (D: the decay from the run start to this point).
+  [[maybe_unused]] int tl_resolves = 0, tl_exact = 0, tl_window = 0;  // path counters of the timeline build
   auto resolve_mid = [&](int nheld, const v4f (&D)[4]) {
+    ++tl_resolves;
     v4f Min[4];
     lookback_mean(Min, std::false_type{});
 #pragma unroll 1
@@ -768,6 +779,7 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
     int wt = tb - 1;
     float lam_in;
     while (true) {
+      ++tl_window;
       float ka[16], ka2[16], kp[16], kc[16], kv[16];
       Mob excl, first;
       const Mob Pc = scan_chunks(agg_walk16<false>(stage, L, c, first, ka, ka2, kp, kc, kv), L.g, excl);
@@ -871,6 +883,7 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
           }
         } else {
           // Exact per-token path (the state here is the true state).
+          ++tl_exact;
           for (int t = 0; t < 16; ++t) {
             const int tok = tile * RTL + 16 * r + t;
             float qv[16];
@@ -982,6 +995,9 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
     KLA_STAMP(1, 43);
   }
   KLA_STAMP(1, 44);
+  KLA_VALUE(1, 50, tl_window);
+  KLA_VALUE(1, 51, tl_resolves);
+  KLA_VALUE(1, 52, tl_exact);
 }
 
 }  // namespace

@@ -21,7 +21,9 @@ Slots (per workgroup): role 0 = walkers, role 1 = matrix waves.
   matrix       2 window walk done (precision entering the run), 3 + 2 j after
                the work of tile j - 1, 4 + 2 j before the step's barrier;
                40 loop done, 41 look-back start, 42 look-back done,
-               43 inclusive mean published, 44 end (held tiles corrected)
+               43 inclusive mean published, 44 end (held tiles corrected);
+               path counters (values): 50 window tiles composed, 51 mid-run
+               resolves of the entering mean, 52 chunks on the exact path
 """
 from __future__ import annotations
 
@@ -153,6 +155,9 @@ def run(config: str = "lm45m_bf16", calls: int = 5, lib_path: str = TL_LIB) -> s
         m = runs == r
         p(f"| {r} | {int(m.sum())} | {_us(_med(X[m, 40] - t0)):.2f} | {_us(_med(X[m, 44] - t0)):.2f} |")
     p("")
+    p(f"paths: window tiles composed per later run (median / max) {_med(X[sel, 50]):.0f} / {int(X[sel, 50].max()) if sel.any() else 0}; "
+      f"mid-run resolves {int(X[:, 51].sum())}; chunks on the exact path {int(X[:, 52].sum())} "
+      f"(matrix wave 4 of each workgroup)")
     p(f"kernel span (first entry to last end): {_us(max(X[:, 44].max(), W[:, 0].max()) - t0):.2f} us")
     return "\n".join(out)
 

@@ -252,6 +252,52 @@ def test_strong_decay_middle_reference(dt):
     run_case(f"strong decay {dt}", x)
 
 
+# ----------------------------------------------------------------------------- run-streaming kernel paths
+# bf16 at d = 64 runs the run-streaming kernel.  At B8 H8 T2048 a head is cut
+# into 4 runs of 8 tiles.  The lm45m recipe forgets fast (every tile after a
+# run's two held tiles is free, and one window tile always converges), so the
+# paths below need recipes of their own; every head is checked.
+def _scaled(ld_s, pn_s, vp_s, seed):
+    x = KI.make_forward_inputs("lm45m_bf16", seed=seed)
+    x["log_decay"] = KI.round_bf16(ld_s * x["log_decay"].astype(np.float32))
+    x["proc_noise"] = KI.round_bf16(pn_s * x["proc_noise"].astype(np.float32))
+    x["val_prec"] = KI.round_bf16(vp_s * x["val_prec"].astype(np.float32))
+    return x
+
+
+@pytest.mark.parametrize("case", ["long_memory", "window_4_tiles", "window_to_start"])
+def test_run_kernel_slow_forgetting(case):
+    """Decays near 1: the entering mean still matters after the held tiles, so
+    every later run resolves it mid-run (look-back, held tiles corrected,
+    state folded) instead of dropping it.  The precision maps contract slowly:
+    the window walk composes about 4 tiles (window_4_tiles), or 12 tiles and
+    for the second run the whole prefix down to lambda0 (window_to_start)."""
+    if case == "long_memory":
+        x = KI.make_forward_inputs("long_bf16", B=8, H=8, T=2048, dk=64, dv=64, seed=8100)
+    elif case == "window_4_tiles":
+        x = _scaled(0.05, 0.05, 0.2, 8101)
+    else:
+        x = _scaled(0.02, 0.01, 0.01, 8102)
+    run_case(f"run kernel {case}", x)
+
+
+def test_run_kernel_extreme_decays():
+    """Chunks whose decay underflows 2^-120 on some channel take the run
+    kernel's exact per-token path: in a free tile, across the boundary of two
+    runs, and inside a held tile of a later run (which then resolves the
+    entering mean mid-run at that chunk)."""
+    x = KI.make_forward_inputs("lm45m_bf16", seed=8103)
+    ld = x["log_decay"].astype(np.float32).copy()
+    ld[0, 0, 600:620, 3] = -9.0       # e^-9 per token: a chunk far below 2^-120 on one channel
+    ld[0, 1, 1000, 5] = -60.0         # one token wipes a channel's memory
+    ld[1, 2, 1500:1512, :] = -12.0    # every channel
+    ld[2, 3, 504:520, 7] = -12.0      # across the boundary of runs 0 and 1 (token 512)
+    ld[3, 4, 530:546, 0:4] = -9.0     # inside the first held tile of run 1
+    ld[5, 6, 1540:1556, 60] = -12.0   # inside the first held tile of run 3
+    x["log_decay"] = KI.round_bf16(ld)
+    run_case("run kernel extreme decays", x)
+
+
 def test_precision_only_inputs_shared_over_value_channels():
     """The precision path of kla_forward does not depend on q, v or M0."""
     import torch
