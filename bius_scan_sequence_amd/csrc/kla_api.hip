@@ -27,8 +27,15 @@ size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 constexpr size_t kHeader = 256;
 
 struct FwdLayout {
-  size_t hdone, pflag, mflag, pagg, pinc, mF, magg, minc, total;
+  size_t hdone, tick, pflag, mflag, pagg, pinc, mF, magg, minc, total;
 };
+
+// The largest divisor of `units` that has a ticket counter.
+int ticket_groups(long long units) {
+  for (int g = kTicketGroups; g > 1; --g)
+    if (units % g == 0) return g;
+  return 1;
+}
 
 bool fwd_shape_ok(int B, int H, int T, int dk, int dv) {
   if (B < 1 || H < 1 || T < 0) return false;
@@ -42,6 +49,7 @@ FwdLayout fwd_layout(int B, int H, int T, int dk, int dv, int nseg) {
   FwdLayout l;
   size_t o = kHeader;
   l.hdone = o; o += (size_t)kDoneCounters * 4;  // fixed place and size in every layout
+  l.tick = o; o += (size_t)kTicketWords * 4;     // likewise
   l.pflag = o; o += round256(slots * 2 * 4);  // one flag per carry wave (two when dk = 128)
   l.mflag = o; o += round256(slots * 8 * 4);  // one flag per wave (up to eight)
   l.pagg = o; o += round256(slots * dk * 16);
@@ -70,11 +78,8 @@ RunLayout run_layout(long long nheads, int nrun) {
   const size_t slots = (size_t)nheads * nrun;
   RunLayout l;
   size_t o = kHeader;
-  // The fixed done-counter region of every layout holds the ticket counters
-  // here: like the done counters, each is zero again when a call ends.
-  static_assert(kRunTicketStride * kRunTicketGroups <= kDoneCounters, "ticket counters outside the region");
-  l.tick = o;
-  o += (size_t)kDoneCounters * 4;
+  o += (size_t)kDoneCounters * 4;  // the fixed done-counter region of every layout (unused here)
+  l.tick = o; o += (size_t)kTicketWords * 4;  // the fixed ticket region
   l.flag = o; o += round256(slots * 4 * 4);
   l.dv = o; o += round256(slots * 4 * 64 * 4);
   l.magg = o; o += round256(slots * 4096 * 4);
@@ -98,7 +103,7 @@ int device_cus() {
 
 struct PscanPlan {
   int ncblocks, nseg, seglen;
-  size_t bdone, flag, agg, inc, total;
+  size_t bdone, tick, flag, agg, inc, total;
 };
 
 bool pscan_shape_ok(int B, int H, int T, int D) {
@@ -128,6 +133,7 @@ PscanPlan pscan_plan(int B, int H, int T, int D) {
   const size_t slots = (size_t)pl.ncblocks * pl.nseg;
   size_t o = kHeader;
   pl.bdone = o; o += (size_t)kDoneCounters * 4;  // fixed place and size in every layout
+  pl.tick = o; o += (size_t)kTicketWords * 4;     // likewise
   pl.flag = o; o += round256(slots * 4);
   if (pl.nseg > 1) {
     pl.agg = o; o += round256(slots * 256 * 16);
@@ -399,12 +405,7 @@ int forward_impl(const char* name, const void* q, const void* k, const void* v, 
     bool one_round = false;
     fwd_run_plan(r.nheads, T, device_cus(), r.R0, r.Rb, r.Rx, r.nrun, one_round);
     r.agg_always = one_round ? 1 : 0;
-    r.tgroups = 1;  // the largest divisor of nheads that has a counter
-    for (int g = kRunTicketGroups; g >= 1; --g)
-      if (r.nheads % g == 0) {
-        r.tgroups = g;
-        break;
-      }
+    r.tgroups = ticket_groups(r.nheads);
     const RunLayout rl = run_layout(nheads, r.nrun);
     const int rc = take(rl.total, rl.dv);
     if (rc != KLA_OK) return rc;
@@ -431,12 +432,13 @@ int forward_impl(const char* name, const void* q, const void* k, const void* v, 
   }
   p.cwidth = conv_w ? conv_width : 0;
   p.nheads = (int)nheads; p.T = T; p.nseg = nseg; p.H = H;
-  p.tgroups = nheads % 8 == 0 ? 8 : nheads % 4 == 0 ? 4 : nheads % 2 == 0 ? 2 : 1;
+  p.tgroups = ticket_groups(nheads);
   // With 128 or more heads a head's consecutive segments are dispatched at
   // least 128 workgroups apart (segment-major order), and a segment seldom
   // has a successor waiting on its aggregate.
   p.mskip = nheads >= 128;
   p.ctrl = reinterpret_cast<unsigned*>(ws);
+  p.tick = reinterpret_cast<unsigned*>(ws + l.tick);
   p.hdone = reinterpret_cast<unsigned*>(ws + l.hdone);
   p.pflag = reinterpret_cast<unsigned*>(ws + l.pflag);
   p.mflag = reinterpret_cast<unsigned*>(ws + l.mflag);
@@ -563,8 +565,9 @@ extern "C" int kla_precision_scan(const float* log_decay, const float* proc_nois
   p.lpath = lambda_path; p.lamT = lambda_T;
   p.nchains = chains; p.D = D; p.T = T;
   p.nseg = pl.nseg; p.seglen = pl.seglen; p.ncblocks = pl.ncblocks;
-  p.tgroups = pl.ncblocks % 8 == 0 ? 8 : pl.ncblocks % 4 == 0 ? 4 : pl.ncblocks % 2 == 0 ? 2 : 1;
+  p.tgroups = ticket_groups(pl.ncblocks);
   p.ctrl = reinterpret_cast<unsigned*>(ws);
+  p.tick = reinterpret_cast<unsigned*>(ws + pl.tick);
   p.bdone = reinterpret_cast<unsigned*>(ws + pl.bdone);
   p.flag = reinterpret_cast<unsigned*>(ws + pl.flag);
   p.agg = reinterpret_cast<float*>(ws + pl.agg);

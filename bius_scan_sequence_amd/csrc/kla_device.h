@@ -335,6 +335,16 @@ __device__ inline int lookback_find(const unsigned* flags, int stride, int s, un
   return lookback_find(flags, stride, s, fagg, finc, ctrl, lookback_peek(flags, stride, s - 1));
 }
 
+// Draws this workgroup's ticket from the counter of its group (blockIdx %
+// groups), which takes `per_group` tickets per call; the workgroup that draws
+// the last one sets the counter back to zero for the next call.
+__device__ __forceinline__ unsigned draw_ticket(unsigned* tick, unsigned groups, unsigned per_group) {
+  unsigned* const tk = tick + kTicketStride * (blockIdx.x % groups);
+  const unsigned t = __hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (t == per_group - 1u) st_relaxed(tk, 0u);
+  return t;
+}
+
 // Call epochs.  Every workgroup reads the workspace epoch e before touching
 // flags, so flags of this call (values 2e+2, 2e+3) never match those left by
 // earlier calls, whatever their shapes.  Each workgroup counts itself done
@@ -347,7 +357,6 @@ __device__ __forceinline__ void epoch_done(unsigned* ctrl, unsigned ngroups, uns
   if (__hip_atomic_fetch_add(ctrl + kGroupsDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ngroups - 1)
     return;
   st_relaxed(ctrl + kGroupsDone, 0u);
-  for (int g = 0; g < 8; ++g) st_relaxed(ctrl + kTicket + g, 0u);  // ticket counters for the next call
   st_relaxed(ctrl + kEpoch, e + 1u);
 }
 

@@ -510,8 +510,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   // every segment a workgroup waits on holds a smaller ticket of its own
   // counter and started earlier.
   if (nseg > 1 && tid == 0)
-    s.ctl[2] = (int)__hip_atomic_fetch_add(p.ctrl + kTicket + blockIdx.x % (unsigned)p.tgroups, 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+    s.ctl[2] = (int)draw_ticket(p.tick, (unsigned)p.tgroups, (unsigned)nheads / (unsigned)p.tgroups * (unsigned)nseg);
   if (tid == 0) s.ctl[1] = nseg > 1 ? (int)ld_relaxed(p.ctrl + kEpoch) : 0;
   if (nseg > 1) __syncthreads();
   const unsigned ticket = nseg > 1 ? (unsigned)s.ctl[2] : blockIdx.x;

@@ -1008,12 +1008,7 @@ __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
   const int tid = threadIdx.x;
   KLA_STAMP(tid >> 8, 0);
   if (tid == 0) {
-    // The group's counter takes nheads / tgroups * nrun tickets per call; the
-    // workgroup that draws the last one sets it back to zero for the next call.
-    unsigned* const tk = p.tick + kRunTicketStride * (blockIdx.x % (unsigned)p.tgroups);
-    const unsigned t = __hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (t == (unsigned)p.nheads / (unsigned)p.tgroups * (unsigned)p.nrun - 1u) st_relaxed(tk, 0u);
-    s.ctl[cTicket] = t;
+    s.ctl[cTicket] = draw_ticket(p.tick, (unsigned)p.tgroups, (unsigned)p.nheads / (unsigned)p.tgroups * (unsigned)p.nrun);
     s.ctl[cEpoch] = p.nrun > 1 ? ld_relaxed(p.ctrl + kEpoch) : 0u;
     s.ctl[cWSync] = 0u;
     s.ctl[cXSync] = 0u;

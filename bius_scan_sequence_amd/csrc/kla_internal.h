@@ -8,10 +8,7 @@ namespace kla {
 
 // Control words at the head of every workspace (32-bit each).  Words 0 and 1
 // hold the call epoch and the groups-done counter (kla_device.h).
-// kTicket: eight words (8..15) of ticket counters, one per group of
-// workgroups (blockIdx % groups) of the segmented forward and the precision
-// scan (the run-streaming forward keeps its own, one per line).
-enum CtrlWord { kError = 3, kTicket = 8 };
+enum CtrlWord { kError = 3 };
 
 // Done counters: a fixed region of kDoneCounters words right after the
 // 256-byte header, at the same place and of the same size whatever the call's
@@ -20,6 +17,17 @@ enum CtrlWord { kError = 3, kTicket = 8 };
 // would then stop advancing).  Unit u (a head, a chain block) counts on word
 // u % kDoneCounters.
 constexpr int kDoneCounters = 4096;
+
+// Ticket counters: a fixed region right after the done counters, one counter
+// per 64-byte line (so that the atomics of many workgroups starting together
+// spread over many lines), zero whenever no call runs.  A kernel whose
+// workgroups wait on each other numbers them with tickets: group x =
+// blockIdx % tgroups (tgroups divides the unit count, at most kTicketGroups)
+// draws from counter x, and the workgroup that draws a counter's last ticket
+// sets it back to zero.
+constexpr int kTicketStride = 16;
+constexpr int kTicketGroups = 256;
+constexpr int kTicketWords = kTicketStride * kTicketGroups;
 
 struct FwdParams {
   const void* q;
@@ -44,7 +52,8 @@ struct FwdParams {
   const float* cb[3];
   int cwidth;
   int nheads, T, nseg;
-  int tgroups;        // ticket groups (1, 2, 4 or 8; divides nheads): group x takes the heads h = x mod tgroups
+  int tgroups;        // ticket groups (divides nheads, at most kTicketGroups): group x takes the heads h = x mod tgroups
+  unsigned* tick;     // ticket counters, group x at word kTicketStride * x
   int H;              // heads per batch row (indexes theta / sigma2)
   int mskip;          // a segment whose predecessor's inclusive mean is already out publishes no aggregate
   unsigned* ctrl;     // workspace control words
@@ -67,7 +76,8 @@ struct PscanParams {
   float* lamT;        // nullable
   long long nchains;  // B*H*D
   int D, T, nseg, seglen, ncblocks;
-  int tgroups;        // ticket groups (1, 2, 4 or 8; divides ncblocks): group x takes the chain blocks cb = x mod tgroups
+  int tgroups;        // ticket groups (divides ncblocks, at most kTicketGroups): group x takes the chain blocks cb = x mod tgroups
+  unsigned* tick;     // ticket counters, group x at word kTicketStride * x
   unsigned* ctrl;
   unsigned* bdone;    // [kDoneCounters] segments done with their flags, per chain-block group
   unsigned* flag;     // [nseg*ncblocks]
@@ -169,18 +179,14 @@ struct FwdRunParams {
   int nheads, T, ntiles, nrun;
   int R0, Rb, Rx;      // run 0 takes R0 tiles; run r >= 1 takes Rb, plus one if r - 1 < Rx
   int agg_always;      // every run but the last publishes its aggregate (all runs resident at once)
-  int tgroups;         // ticket groups (divides nheads, at most kRunTicketGroups): group x takes the heads h = x mod tgroups
+  int tgroups;         // ticket groups (divides nheads, at most kTicketGroups): group x takes the heads h = x mod tgroups
   unsigned* ctrl;      // workspace control words (epoch, groups done, error)
-  unsigned* tick;      // ticket counters, group x at word kRunTicketStride * x (zero between calls)
+  unsigned* tick;      // ticket counters, group x at word kTicketStride * x
   unsigned* flag;      // [nheads*nrun][4] mean-carry flags, one per matrix wave
   float* dv;           // [nheads*nrun][4][64] prod of forget gates over the run (a copy per wave)
   float* magg;         // [nheads*nrun][4096] local mean state of the run (fragment order)
   float* minc;         // [nheads*nrun][4096] mean state after the run (fragment order)
 };
-// Ticket counters of the run-streaming forward: one per 64-byte line, so
-// that the workgroups starting together spread their atomics over many lines.
-constexpr int kRunTicketStride = 16;
-constexpr int kRunTicketGroups = 256;
 void fwd_run_plan(int nheads, int T, int ncu, int& R0, int& Rb, int& Rx, int& nrun, bool& one_round);
 hipError_t launch_forward_run(const FwdRunParams& p, hipStream_t stream);
 

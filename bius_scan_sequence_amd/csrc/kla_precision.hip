@@ -28,8 +28,7 @@ __global__ __launch_bounds__(256) void kla_pscan_kernel(PscanParams p) {
   // segment-major, so every segment a workgroup waits on holds a smaller
   // ticket of its own counter and started earlier.
   if (nseg > 1 && tid == 0)
-    sh[3] = (int)__hip_atomic_fetch_add(p.ctrl + kTicket + blockIdx.x % (unsigned)p.tgroups, 1u, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
+    sh[3] = (int)draw_ticket(p.tick, (unsigned)p.tgroups, (unsigned)p.ncblocks / (unsigned)p.tgroups * (unsigned)nseg);
   if (tid == 0) sh[1] = nseg > 1 ? (int)ld_relaxed(p.ctrl + kEpoch) : 0;
   if (nseg > 1) __syncthreads();
   const unsigned ticket = nseg > 1 ? (unsigned)sh[3] : blockIdx.x;
