@@ -332,12 +332,17 @@ int kla_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Reads the device-side error word of a workspace, ordered after the work
  * queued on `stream` (an asynchronous copy on that stream, then a stream
- * synchronisation): 0 = no error; 1 = a workgroup gave up waiting for a
- * predecessor's carry after about 2^25 polls (1-2 s): it then went on with
- * whatever carry it had found, so the y, lambda_T, M_T and lambda_path of
- * that call are unspecified.  The word is sticky: it stays set for later
- * calls on the same workspace until kla_workspace_init clears it.  The
- * Python binding reads it when a call asks for `check=True`. */
+ * synchronisation): 0 = no error; 1 = the outputs of some call are
+ * unspecified, because
+ *   - a workgroup gave up waiting for a predecessor's carry after about 2^25
+ *     polls (1-2 s) and went on with whatever carry it had found, or
+ *   - (kla_forward with bf16 inputs at dk = dv = 64) a stretch of tokens
+ *     dropped the posterior mean entering it where its decay since the
+ *     stretch's start had fallen below 2^-100, and that mean then turned
+ *     out to be 2^40 or more in magnitude, so the dropped term may matter.
+ * The word is sticky: it stays set for later calls on the same workspace
+ * until kla_workspace_init clears it.  The Python binding reads it when a
+ * call asks for `check=True`. */
 int kla_workspace_error(const void* workspace, int* error_out, void* stream);
 
 /* Static text for a status code; for KLA_ERR_HIP, the last HIP error text
