@@ -100,7 +100,8 @@ enum RunCtl {
   cUnsafe = 4,    // [2 tile parities][4 walker waves]: chunks that take the exact path
   cNotFree = 12,  // [2][4]: some channel's decay from the run start to the tile start above 2^-100
   cVote = 20,     // [4]: window walk not converged
-  cLamReady = 24  // the window walk's precision is in lamst
+  cLamReady = 24,  // the window walk's precision is in lamst
+  cCorr = 25       // [4]: walker wave w's share of the held-tile correction (1: tile 1 to correct, 2: nothing)
 };
 
 struct alignas(16) RunSmem {
@@ -298,6 +299,28 @@ struct RunCtx {
 // Walker waves (0-3): precision scan, gates and causal scores of tile j during
 // step j.
 // ---------------------------------------------------------------------------
+// Held chunk r of Qt slot `slot` (tile `tile`), value columns 16c..16c+15:
+// y = y0 + Qt diag(h) M_in (h: the chunk's per-channel factor), stored as
+// bf16.  Lane layout of the matrix waves; any wave runs it for any column
+// block c (the walkers take the second held tile at the end of a run).
+__device__ __forceinline__ void correct_held(RunSmem& s, int lane, int c, int tile, int slot, int r, const float* h,
+                                             const v4f& y0, const v4f (&Min)[4], __amdgpu_buffer_rsrc_t yrs) {
+  const int G = lane >> 4, li = lane & 15, xe = li >> 2, xj = li & 3;
+  v4s Ah[4], Al[4], Bh[4], Bl[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const v4f W = Min[kb] * *reinterpret_cast<const v4f*>(h + 16 * kb + 4 * G);
+    split4(W, Ah[kb], Al[kb]);
+    const int off = op_off(16 * kb + 4 * G + xe, 4 * xj);
+    Bh[kb] = lds_read_tr16(s.qop[slot][0][r] + off);
+    Bl[kb] = lds_read_tr16(s.qop[slot][1][r] + off);
+  }
+  const v4f Y = mma_split64(y0, Ah, Al, Bh, Bl);
+  const int tok = tile * RTL + 16 * r + li;
+  const v2u wv = v2u{pack_bf16(Y[0], Y[1]), pack_bf16(Y[2], Y[3])};
+  __builtin_amdgcn_raw_buffer_store_b64(wv, yrs, tok * (RD * 2) + (16 * c + 4 * G) * 2, 0, 0);
+}
+
 __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, const RunCtx& x) {
   const int tid = x.tid, lane = x.lane, w = x.wave, T = x.T, tb = x.tb, ntl = x.ntl;
   const size_t hoff = x.hoff;
@@ -552,6 +575,25 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
     }
     __syncthreads();
   }
+  // End of a later run: the second held tile's correction for column block
+  // w, once the matrix waves have the entering mean (they correct the first).
+  if (x.run > 0) {
+    unsigned f;
+    while ((f = __hip_atomic_load(&s.ctl[cCorr + w], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) == 0u)
+      __builtin_amdgcn_s_sleep(1);
+    if (f == 1u) {
+      const unsigned char* hb = s.raw[w];
+      v4f Min[4], y0[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) Min[rt] = *reinterpret_cast<const v4f*>(hb + (rt * 64 + lane) * 16);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y0[r] = *reinterpret_cast<const v4f*>(hb + 4096 + (r * 64 + lane) * 16);
+      const __amdgpu_buffer_rsrc_t yrs =
+          __builtin_amdgcn_make_buffer_rsrc(p.y + hoff, (short)0, T * RD * 2, 0x00020000);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) correct_held(s, lane, w, tb + 1, 1, r, s.hfac[1][r], y0[r], Min, yrs);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -707,10 +749,13 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
   // the run start to the chunk start) M_in, stored.
   auto correct = [&](int k, const v4f& y0, const v4f (&Min)[4]) {
     const int j = k >> 2, r = k & 3;
-    v4f W[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) W[rt] = Min[rt] * lds4(s.hfac[j][r], rt);
-    store_y(tb + j, r, readout(y0, W, j, r));
+    correct_held(s, lane, c, tb + j, j, r, s.hfac[j][r], y0, Min, yrs);
+  };
+  // Tells walker wave c (this wave's partner) what it corrects at the end of
+  // the run: 1 = the second held tile (its inputs are in raw[c]), 2 = nothing.
+  auto tell_walker = [&](unsigned what) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+    if (lane == 0) __hip_atomic_store(&s.ctl[cCorr + c], what, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   };
   // Resolve the entering mean mid-run: fold the predecessors' carries
   // (M_in), correct the first `nheld` held chunks, and add diag(D) M_in to
@@ -929,6 +974,7 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
   // End of the run: the mean carry.
   KLA_STAMP(1, 40);
   v4f D[4];
+  bool agg_out = false;  // this run's aggregate is published
   if (!mres) {
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) D[rt] = lds4(s.dend, rt);
@@ -941,6 +987,7 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
     // aggregate is skipped when the inclusive carry is there.
     const bool skip = !p.agg_always && ld_relaxed(hflag + 4 * (run - 1)) == x.FINC;
     if (!x.last_run && !skip) {
+      agg_out = true;
       const auto ragg = coherent_rsrc(p.magg + hs * 4096 + c * 1024, 4096);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) st_coherent(ragg, (rt * 64 + lane) * 16, Mst[rt]);
@@ -953,20 +1000,23 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
       if (lane == 0) st_relaxed(hflag + 4 * run, x.FAGG);
     }
   }
-  // The state after the run (inclusive mean): published for the runs after
-  // it, or written as M_T by the last run.
+  // The state after the run (inclusive mean): written as M_T by the last run,
+  // else published for the runs after it.  When all runs of a head are
+  // resident together and this run published its aggregate, the runs after
+  // it fold that aggregate down to the first run's inclusive state, and this
+  // run's inclusive state would never be read: it is skipped.
   auto publish = [&]() {
-    if (!x.last_run) {
+    if (x.last_run) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p.MT[(size_t)head * 4096 + (16 * rt + 4 * G + e) * RD + 16 * c + li] = Mst[rt][e];
+    } else if (!(p.agg_always && agg_out)) {
       const auto rinc = coherent_rsrc(p.minc + hs * 4096 + c * 1024, 4096);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) st_coherent(rinc, (rt * 64 + lane) * 16, Mst[rt]);
       wait_stores();
       if (lane == 0) st_relaxed(hflag + 4 * run, x.FINC);
-    } else {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p.MT[(size_t)head * 4096 + (16 * rt + 4 * G + e) * RD + 16 * c + li] = Mst[rt][e];
     }
   };
   if (!mres) {
@@ -983,16 +1033,26 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
       for (int e = 0; e < 4; ++e) Mst[rt][e] = fmaf(D[rt][e], Min[rt][e], Mst[rt][e]);
     publish();
     KLA_STAMP(1, 43);
+    static_assert(RHOLD == 2, "the walkers take the second of two held tiles");
     if (ntl >= RHOLD) {
+      // The second held tile goes to the walker wave of the same column
+      // block: the entering mean and the held outputs through LDS (the raw
+      // input tiles are no longer read).
+      unsigned char* const hb = s.raw[c];
 #pragma unroll
-      for (int k = 0; k < 4 * RHOLD; ++k) correct(k, Yh[k], Min);
+      for (int rt = 0; rt < 4; ++rt) *reinterpret_cast<v4f*>(hb + (rt * 64 + lane) * 16) = Min[rt];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) *reinterpret_cast<v4f*>(hb + 4096 + (r * 64 + lane) * 16) = Yh[4 + r];
+      tell_walker(1u);
     } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) correct(k, Yh[k], Min);
+      tell_walker(2u);
     }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) correct(k, Yh[k], Min);
   } else {
     publish();
     KLA_STAMP(1, 43);
+    if (run > 0) tell_walker(2u);
   }
   KLA_STAMP(1, 44);
   KLA_VALUE(1, 50, tl_window);
@@ -1013,6 +1073,8 @@ __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
     s.ctl[cWSync] = 0u;
     s.ctl[cXSync] = 0u;
     s.ctl[cLamReady] = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s.ctl[cCorr + i] = 0u;
   }
   __syncthreads();
   // Ticket order is run-major within a group, and all runs of a head fall in
