@@ -171,12 +171,15 @@ BwdLayout bwd_layout(int B, int H, int T, int dk, int dv) {
   l.Mseg = o; o += round256(nh * nseg * sk * sv * 4);
   l.Gseg = o; o += round256(nh * nseg * sk * sv * 4);
   l.rs = o; o += round256(nh * dk * 4);
-  l.dgw = o; o += round256(nh * (size_t)T * dk * 4);
-  l.ew = o; o += round256(nh * (size_t)T * dk * 4);
+  // dgw, ew: one [nh][T][dk] partial per value half; dq and dv partials one
+  // per value half and key half when there are two.
+  const size_t vh = (size_t)(dv / sv), kh = (size_t)(dk / sk);
+  l.dgw = o; o += round256(vh * nh * (size_t)T * dk * 4);
+  l.ew = o; o += round256(vh * nh * (size_t)T * dk * 4);
   l.comp = o; o += round256(nseg * nh * sk * 16);
   l.cin = o; o += round256(nseg * nh * sk * 8);
-  l.dqacc = o; if (dv > 64) o += round256(nh * (size_t)T * dk * 4);
-  l.dvacc = o; if (dk > 64) o += round256(nh * (size_t)T * dv * 4);
+  l.dqacc = o; if (vh > 1) o += round256(vh * nh * (size_t)T * dk * 4);
+  l.dvacc = o; if (kh > 1) o += round256(kh * nh * (size_t)T * dv * 4);
   l.total = o;
   return l;
 }
@@ -233,8 +236,9 @@ extern "C" int kla_backward(const void* q, const void* k, const void* v, const v
   auto kbyte = [&](const void* base, int off) {  // key-side array shifted by `off` channels
     return base ? static_cast<const char*>(base) + (size_t)off * esz : nullptr;
   };
-  BwdParams p;
+  BwdParams p{};
   p.nheads = (int)nheads; p.T = T; p.nseg = (T + kBwdSeg - 1) / kBwdSeg;
+  p.ncu = device_cus();
   p.nchains = nheads * sk;
   p.F = reinterpret_cast<float*>(ws + l.F);
   p.Mseg = reinterpret_cast<float*>(ws + l.Mseg);
@@ -256,23 +260,29 @@ extern "C" int kla_backward(const void* q, const void* k, const void* v, const v
     p.lam0 = lambda0 ? lambda0 + ko : nullptr;
     p.dlamT = grad_lambda_T ? grad_lambda_T + ko : nullptr;
     p.dlam0 = grad_lambda0 + ko;
-    p.rs = rs + ko; p.dgw = dgw + ko; p.ew = ew + ko;
+    p.rs = rs + ko;
     p.dq = const_cast<char*>(kbyte(grad_q, ko)); p.dk = const_cast<char*>(kbyte(grad_k, ko));
     p.dld = const_cast<char*>(kbyte(grad_log_decay, ko)); p.dpn = const_cast<char*>(kbyte(grad_proc_noise, ko));
     p.dvp = const_cast<char*>(kbyte(grad_val_prec, ko));
-    p.dq_acc = dqacc ? dqacc + ko : nullptr;
+    // Each value half writes its own partials of dg, e and dq (and each key
+    // half its own of dv); the chain and the conversion add them.
+    const size_t half_k = (size_t)nheads * T * dk, half_v = (size_t)nheads * T * dv;
     for (int vh = 0; vh < VH && e == hipSuccess; ++vh) {
       const int vo = vh * sv;
+      p.dgw = dgw + vh * half_k + ko; p.ew = ew + vh * half_k + ko;
+      p.dq_acc = dqacc ? dqacc + vh * half_k + ko : nullptr;
       p.v = kbyte(v, vo); p.dy = kbyte(grad_y, vo);
       p.dv = const_cast<char*>(kbyte(grad_v, vo));
-      p.dv_acc = dvacc ? dvacc + vo : nullptr;
+      p.dv_acc = dvacc ? dvacc + kh * half_v + vo : nullptr;
       const size_t mo = (size_t)ko * dv + vo;
       p.M0 = M0 ? M0 + mo : nullptr;
       p.dMT = grad_M_T ? grad_M_T + mo : nullptr;
       p.dM0 = grad_M0 + mo;
-      p.add_e = vh > 0; p.add_dq = vh > 0; p.add_dv = kh > 0;
+      p.add_rs = vh > 0;
       e = launch_backward_front(p, sk, sv, bf16, st);
     }
+    p.dgw = dgw + ko; p.ew = ew + ko;
+    p.ehalf = VH > 1 ? half_k : 0;
     if (e == hipSuccess) e = launch_backward_chain(p, sk, bf16, st);
   }
   if (e == hipSuccess && dqacc) e = launch_backward_convert(dqacc, grad_q, nheads * (long long)T * dk, bf16, st);

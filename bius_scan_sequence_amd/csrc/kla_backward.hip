@@ -46,6 +46,9 @@ namespace {
 constexpr int kSL = 64;  // tokens per segment
 constexpr int kC = 16;   // tokens per chunk
 constexpr int kChunkThreads = 512;
+// s_waitcnt operand that waits for every vector memory operation (vmcnt 0)
+// and leaves the export and LDS/scalar counters at their maxima.
+constexpr int kVmcntZero = 0x0F70;
 
 template <bool BF16>
 __device__ __forceinline__ float ldin(const void* p, size_t x) {
@@ -104,30 +107,89 @@ template <int V, bool BF16> struct VRow {
   static constexpr int P = BF16 ? V + 4 : V + 1;
 };
 
-// Stages the segment's tokens: log2 f, g, q as [64][K+1] (q in fp32 or, for
-// bf16 inputs, in its own bf16 bits) and v, dy as
-// [64][VRow::P] (rows padded so that column walks hit distinct banks), then
-// turns log2 f into the cumulative sum inside each 16-token chunk (lb) and
-// writes each chunk's total to T[4][K].  Tokens past T are identity steps:
-// log2 f = 0, g = q = v = dy = 0.  Every decay the kernels need is then exp2
-// of a short sum: inside a chunk lb_l - lb_m, across chunks the chunk totals
-// in between (never a difference of two long cumulative sums).  A thread
-// stages four consecutive channels of a token with vector loads.
-template <int K, int V, bool BF16, int NT, typename QT>
-__device__ __forceinline__ void stage_segment(const BwdParams& p, size_t hd, int t0, float* slb, float* sg,
-                                              QT* sq, typename VRow<V, BF16>::T* sv,
-                                              typename VRow<V, BF16>::T* sd, float* sT, int* unsafe) {
-  using In = typename std::conditional<BF16, uint16_t, float>::type;
-  constexpr int KP = K + 1, VP = VRow<V, BF16>::P, K4 = K / 4, V4 = V / 4;
-  static_assert((kSL * K4) % NT == 0 || NT % (kSL * K4) == 0, "staging passes");
-  // Unrolled, so that every pass's loads are in flight together.
+// A segment's raw inputs in registers: the first half of staging, issued a
+// segment ahead by the chunk kernel so that their loads overlap the chunks of
+// the segment before.  Four consecutive elements per load: 8 bytes for bf16,
+// 16 for fp32; pass x of the key side covers (token x / K4, channels
+// 4 (x % K4) ..), pass x of the value side likewise.
+template <bool BF16> using Raw4 = typename std::conditional<BF16, uint2, float4>::type;
+template <int K, int V, bool BF16, int NT>
+struct SegLoads {
+  static constexpr int PK = (kSL * (K / 4) + NT - 1) / NT, PV = (kSL * (V / 4) + NT - 1) / NT;
+  float4 lam[PK];
+  Raw4<BF16> ld[PK], pn[PK], k[PK], vp[PK], q[PK];
+  Raw4<BF16> v[PV], d[PV];
+};
+
+template <bool BF16>
+__device__ __forceinline__ Raw4<BF16> ldraw4(const void* p, size_t x) {
+  if constexpr (BF16)
+    return *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + x);
+  else
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + x);
+}
+__device__ __forceinline__ float4 raw_f4(uint2 u) {
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+__device__ __forceinline__ float4 raw_f4(float4 f) { return f; }
+
+template <int K, int V, bool BF16, int NT>
+__device__ __forceinline__ void seg_load(const BwdParams& p, size_t hd, int t0, SegLoads<K, V, BF16, NT>& r) {
+  constexpr int K4 = K / 4, V4 = V / 4;
+  using L = SegLoads<K, V, BF16, NT>;
+  const Raw4<BF16> z{};
 #pragma unroll
-  for (int x = threadIdx.x; x < kSL * K4; x += NT) {
-    const int t = x / K4, i = (x % K4) * 4;
+  for (int pk = 0; pk < L::PK; ++pk) {
+    const int x = threadIdx.x + pk * NT, t = x / K4, i = (x % K4) * 4;
+    r.lam[pk] = make_float4(0.f, 0.f, 0.f, 0.f);
+    r.ld[pk] = r.pn[pk] = r.k[pk] = r.vp[pk] = r.q[pk] = z;
+    if (x < kSL * K4 && t0 + t < p.T) {
+      const size_t e = (hd * p.T + t0 + t) * p.ks + i;
+      r.lam[pk] = *reinterpret_cast<const float4*>(p.lpath + e);
+      r.ld[pk] = ldraw4<BF16>(p.ld, e);
+      r.pn[pk] = ldraw4<BF16>(p.pn, e);
+      r.k[pk] = ldraw4<BF16>(p.k, e);
+      r.vp[pk] = ldraw4<BF16>(p.vp, e);
+      r.q[pk] = ldraw4<BF16>(p.q, e);
+    }
+  }
+#pragma unroll
+  for (int pv = 0; pv < L::PV; ++pv) {
+    const int x = threadIdx.x + pv * NT, t = x / V4, j = (x % V4) * 4;
+    r.v[pv] = r.d[pv] = z;
+    if (x < kSL * V4 && t0 + t < p.T) {
+      const size_t y = (hd * p.T + t0 + t) * p.vs + j;
+      r.v[pv] = ldraw4<BF16>(p.v, y);
+      r.d[pv] = ldraw4<BF16>(p.dy, y);
+    }
+  }
+}
+
+// The second half of staging: log2 f, g, q as [64][K+1] (q in fp32 or, for
+// bf16 inputs, in its own bf16 bits) and v, dy as [64][VRow::P] (rows padded
+// so that column walks hit distinct banks), then log2 f turned into the
+// cumulative sum inside each 16-token chunk (lb) with each chunk's total in
+// T[4][K].  Tokens past T are identity steps: log2 f = 0, g = q = v = dy = 0.
+// Every decay the kernels need is then exp2 of a short sum: inside a chunk
+// lb_l - lb_m, across chunks the chunk totals in between (never a difference
+// of two long cumulative sums).
+template <int K, int V, bool BF16, int NT, typename QT>
+__device__ __forceinline__ void seg_store(const BwdParams& p, size_t hd, int t0, const SegLoads<K, V, BF16, NT>& r, float* slb,
+                                          float* sg, QT* sq, typename VRow<V, BF16>::T* sv,
+                                          typename VRow<V, BF16>::T* sd, float* sT, int* unsafe) {
+  using In = typename std::conditional<BF16, uint16_t, float>::type;
+  using L = SegLoads<K, V, BF16, NT>;
+  constexpr int KP = K + 1, VP = VRow<V, BF16>::P, K4 = K / 4, V4 = V / 4;
+#pragma unroll
+  for (int pk = 0; pk < L::PK; ++pk) {
+    const int x = threadIdx.x + pk * NT, t = x / K4, i = (x % K4) * 4;
+    if (x >= kSL * K4) continue;
     float lf[4] = {0.f, 0.f, 0.f, 0.f}, g[4] = {0.f, 0.f, 0.f, 0.f}, q[4] = {0.f, 0.f, 0.f, 0.f};
     if (t0 + t < p.T) {
+      // The precision before the token: the path one token earlier (read
+      // here, mostly from cache: the rows were just loaded), or the prior.
       const size_t e = (hd * p.T + t0 + t) * p.ks + i;
-      const float4 lam = *reinterpret_cast<const float4*>(p.lpath + e);
       float4 lprev;
       if (t0 + t > 0) {
         lprev = *reinterpret_cast<const float4*>(p.lpath + e - p.ks);
@@ -137,8 +199,9 @@ __device__ __forceinline__ void stage_segment(const BwdParams& p, size_t hd, int
       } else {
         lprev = make_float4(1.f, 1.f, 1.f, 1.f);
       }
-      const float4 ld = ldin4<BF16>(p.ld, e), pn = ldin4<BF16>(p.pn, e), k = ldin4<BF16>(p.k, e),
-                   vp = ldin4<BF16>(p.vp, e), qq = ldin4<BF16>(p.q, e);
+      const float4 lam = r.lam[pk];
+      const float4 ld = raw_f4(r.ld[pk]), pn = raw_f4(r.pn[pk]), k = raw_f4(r.k[pk]), vp = raw_f4(r.vp[pk]),
+                   qq = raw_f4(r.q[pk]);
       gate1(lam.x, lprev.x, ld.x, pn.x, k.x, vp.x, lf[0], g[0]);
       gate1(lam.y, lprev.y, ld.y, pn.y, k.y, vp.y, lf[1], g[1]);
       gate1(lam.z, lprev.z, ld.z, pn.z, k.z, vp.z, lf[2], g[2]);
@@ -146,38 +209,34 @@ __device__ __forceinline__ void stage_segment(const BwdParams& p, size_t hd, int
       q[0] = qq.x; q[1] = qq.y; q[2] = qq.z; q[3] = qq.w;
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      slb[t * KP + i + r] = lf[r];
-      sg[t * KP + i + r] = g[r];
-      sq[t * KP + i + r] = from_f32<QT>(q[r]);  // exact: q is a value of the input type
+    for (int e = 0; e < 4; ++e) {
+      slb[t * KP + i + e] = lf[e];
+      sg[t * KP + i + e] = g[e];
+      sq[t * KP + i + e] = from_f32<QT>(q[e]);  // exact: q is a value of the input type
     }
   }
 #pragma unroll
-  for (int x = threadIdx.x; x < kSL * V4; x += NT) {
-    const int t = x / V4, j = (x % V4) * 4;
-    In v[4] = {0, 0, 0, 0}, d[4] = {0, 0, 0, 0};
-    if (t0 + t < p.T) {
-      const size_t y = (hd * p.T + t0 + t) * p.vs + j;
-      if constexpr (BF16) {
-        const uint2 uv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.v) + y);
-        const uint2 ud = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.dy) + y);
-        v[0] = (In)uv.x; v[1] = (In)(uv.x >> 16); v[2] = (In)uv.y; v[3] = (In)(uv.y >> 16);
-        d[0] = (In)ud.x; d[1] = (In)(ud.x >> 16); d[2] = (In)ud.y; d[3] = (In)(ud.y >> 16);
-      } else {
-        const float4 fv = *reinterpret_cast<const float4*>(static_cast<const float*>(p.v) + y);
-        const float4 fd = *reinterpret_cast<const float4*>(static_cast<const float*>(p.dy) + y);
-        v[0] = fv.x; v[1] = fv.y; v[2] = fv.z; v[3] = fv.w;
-        d[0] = fd.x; d[1] = fd.y; d[2] = fd.z; d[3] = fd.w;
-      }
+  for (int pv = 0; pv < L::PV; ++pv) {
+    const int x = threadIdx.x + pv * NT, t = x / V4, j = (x % V4) * 4;
+    if (x >= kSL * V4) continue;
+    In vv[4], dd[4];
+    if constexpr (BF16) {  // the inputs' own bits
+      const uint2 uv = r.v[pv], ud = r.d[pv];
+      vv[0] = (In)uv.x; vv[1] = (In)(uv.x >> 16); vv[2] = (In)uv.y; vv[3] = (In)(uv.y >> 16);
+      dd[0] = (In)ud.x; dd[1] = (In)(ud.x >> 16); dd[2] = (In)ud.y; dd[3] = (In)(ud.y >> 16);
+    } else {
+      const float4 fv = r.v[pv], fd = r.d[pv];
+      vv[0] = fv.x; vv[1] = fv.y; vv[2] = fv.z; vv[3] = fv.w;
+      dd[0] = fd.x; dd[1] = fd.y; dd[2] = fd.z; dd[3] = fd.w;
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sv[t * VP + j + r] = v[r];
-      sd[t * VP + j + r] = d[r];
+    for (int e = 0; e < 4; ++e) {
+      sv[t * VP + j + e] = vv[e];
+      sd[t * VP + j + e] = dd[e];
     }
   }
   __syncthreads();
-// One thread per (channel, chunk): cumulative log2 f inside the chunk.  A
+  // One thread per (channel, chunk): cumulative log2 f inside the chunk.  A
   // chunk is marked in `unsafe` (when given) if a channel's log2 decay over
   // either half of it falls below -96.
   for (int x = threadIdx.x; x < 4 * K; x += NT) {
@@ -194,6 +253,15 @@ __device__ __forceinline__ void stage_segment(const BwdParams& p, size_t hd, int
     if (unsafe && (first - mid > 96.f || mid - acc > 96.f)) unsafe[c] = 1;  // benign race: all write 1
   }
   __syncthreads();
+}
+
+template <int K, int V, bool BF16, int NT, typename QT>
+__device__ __forceinline__ void stage_segment(const BwdParams& p, size_t hd, int t0, float* slb, float* sg,
+                                              QT* sq, typename VRow<V, BF16>::T* sv,
+                                              typename VRow<V, BF16>::T* sd, float* sT, int* unsafe) {
+  SegLoads<K, V, BF16, NT> r;
+  seg_load<K, V, BF16, NT>(p, hd, t0, r);
+  seg_store<K, V, BF16, NT>(p, hd, t0, r, slb, sg, sq, sv, sd, sT, unsafe);
 }
 }  // namespace
 
@@ -298,7 +366,7 @@ __global__ __launch_bounds__(256) void kla_bwd_segscan_kernel(BwdParams p) {
   // Row sum over the V threads of a row (consecutive lanes of one wave).
 #pragma unroll
   for (int o = V / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
-  if (live && el % V == 0) p.rs[hd * p.ksh + i] = p.add_e ? p.rs[hd * p.ksh + i] + part : part;
+  if (live && el % V == 0) p.rs[hd * p.ksh + i] = p.add_rs ? p.rs[hd * p.ksh + i] + part : part;
   if (live) {
     float h = p.dMT ? p.dMT[me] : 0.f;
     int s = nseg - 1;
@@ -351,6 +419,35 @@ __global__ __launch_bounds__(256) void kla_bwd_segscan_kernel(BwdParams p) {
 // The in-chunk decays E_l = exp2(lb_l - lb_7), F_l = exp2(lb_7 - lb_l),
 // cp_l = exp2(lb_l) (prod_{u<=l} f_u) and sx_l = exp2(T_c - lb_l)
 // (prod_{u>l} f_u) are formed where they are used, from the staged lb.
+// The chunk kernel's per-segment state tiles from global memory: a value wave
+// takes H tiles (Hx[ib] = H[16 ib + 4 lg + e][16 vb + lr], ib < K/16), a key
+// wave H^T tiles (Hx[jb] = H[16 kb + lr][16 jb + 4 lg + e], jb < V/16) and the
+// same tiles of the mean M (Ms); the rest stay zero.
+template <int K, int V, int HB>
+__device__ __forceinline__ void load_state(const float* Gg, const float* Mg, bool vw, bool kw, int kb, int vb, int lg,
+                                           int lr, v4f (&Hx)[HB], v4f (&Ms)[V / 16]) {
+  constexpr int KB = K / 16, VB = V / 16;
+#pragma unroll
+  for (int b = 0; b < HB; ++b) {
+    Hx[b] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (b < VB) Ms[b] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  if (vw) {  // wave-uniform branches: every load of a wave issued together
+#pragma unroll
+    for (int ib = 0; ib < KB; ++ib)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Hx[ib][e] = Gg[(ib * 16 + 4 * lg + e) * V + vb * 16 + lr];
+  } else if (kw) {
+#pragma unroll
+    for (int jb = 0; jb < VB; ++jb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Hx[jb][e] = Gg[(kb * 16 + lr) * V + jb * 16 + 4 * lg + e];
+        Ms[jb][e] = Mg[(kb * 16 + lr) * V + jb * 16 + 4 * lg + e];
+      }
+  }
+}
+
 template <int K, int V, bool BF16>
 struct BwdChunkSmem {
   using SV = typename VRow<V, BF16>::T;
@@ -373,44 +470,51 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
   constexpr int KB = K / 16, VB = V / 16;
   static_assert(NT == 2 * C * C && NT == 512, "eight waves; one score pair per thread of the first four");
   __shared__ BwdChunkSmem<K, V, BF16> s;
-  const size_t hd = blockIdx.x / p.nseg;
-  const int seg = blockIdx.x % p.nseg;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+  const int kb_w = wave, vb_w = wave - 4;       // key block of a key wave, value block of a value wave
+  const bool kw = wave < KB, vw = wave >= 4 && vb_w < VB;
+  // Each workgroup takes segments blockIdx, blockIdx + gridDim, ...; for bf16
+  // inputs the next segment's inputs are loaded into registers while this
+  // one's chunks run, so their latency is hidden (one workgroup per CU leaves
+  // nothing else to hide it behind).  fp32 inputs (twice the registers) load
+  // each segment when it starts.
+  constexpr bool PREFETCH = BF16;
+  const unsigned nsb = (unsigned)p.nheads * (unsigned)p.nseg;
+  SegLoads<K, V, BF16, NT> nxt;
+  if constexpr (PREFETCH)
+    if (blockIdx.x < nsb)
+    seg_load<K, V, BF16, NT>(p, blockIdx.x / p.nseg, (int)(blockIdx.x % p.nseg) * kSL, nxt);
+  for (unsigned sb = blockIdx.x; sb < nsb; sb += gridDim.x) {
+  const size_t hd = sb / p.nseg;
+  const int seg = (int)(sb % p.nseg);
   const int t0 = seg * kSL;
   const int nvalid = min(kSL, p.T - t0);
   const size_t st = (hd * p.nseg + seg) * (size_t)(K * V);
   const float* Mg = p.Mseg + st;
   const float* Gg = p.Gseg + st;
-  const int kb_w = wave, vb_w = wave - 4;       // key block of a key wave, value block of a value wave
-  const bool kw = wave < KB, vw = wave >= 4 && vb_w < VB;
-  if (tid < 4) s.unsafe[tid] = 0;
-  stage_segment<K, V, BF16, NT>(p, hd, t0, s.lb, s.g, s.q, s.v, s.d, s.T, s.unsafe);
-  // Adjoint at the segment end and the mean entering the segment, loaded
-  // after staging (fewer registers live at once).  A value wave keeps H
-  // tiles (Hc[ib], ib < KB), a key wave H^T tiles (Ht[jb], jb < VB) in the
-  // same registers, and M^T (Ms).
+  // Adjoint at the segment end and the mean entering the segment.  A value
+  // wave keeps H tiles (Hc[ib], ib < KB), a key wave H^T tiles (Ht[jb],
+  // jb < VB) in the same registers, and M^T (Ms).  With the prefetch their
+  // loads go out first and land during staging; without it (fp32 inputs,
+  // more registers held by the staging) they follow the staging.
   constexpr int HB = KB > VB ? KB : VB;
   v4f Hx[HB], Mt[VB], Ms[VB];
   v4f(&Hc)[HB] = Hx;
   v4f(&Ht)[HB] = Hx;
-#pragma unroll
-  for (int b = 0; b < HB; ++b) {
-    Hx[b] = v4f{0.f, 0.f, 0.f, 0.f};
-    if (b < VB) Ms[b] = v4f{0.f, 0.f, 0.f, 0.f};
-  }
-  if (vw) {  // wave-uniform branches: every load of a wave issued together
-#pragma unroll
-    for (int ib = 0; ib < KB; ++ib)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Hc[ib][e] = Gg[(ib * 16 + 4 * lg + e) * V + vb_w * 16 + lr];
-  } else if (kw) {
-#pragma unroll
-    for (int jb = 0; jb < VB; ++jb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Ht[jb][e] = Gg[(kb_w * 16 + lr) * V + jb * 16 + 4 * lg + e];
-        Ms[jb][e] = Mg[(kb_w * 16 + lr) * V + jb * 16 + 4 * lg + e];
-      }
+  if constexpr (PREFETCH) load_state<K, V>(Gg, Mg, vw, kw, kb_w, vb_w, lg, lr, Hx, Ms);
+  if (tid < 4) s.unsafe[tid] = 0;
+  if constexpr (!PREFETCH) seg_load<K, V, BF16, NT>(p, hd, t0, nxt);
+  seg_store<K, V, BF16, NT>(p, hd, t0, nxt, s.lb, s.g, s.q, s.v, s.d, s.T, s.unsafe);
+  if constexpr (!PREFETCH) load_state<K, V>(Gg, Mg, vw, kw, kb_w, vb_w, lg, lr, Hx, Ms);
+  // Every load of this segment has landed before the chunk loop starts.
+  // Global stores share the load counter and it drains in order: a load
+  // still pending inside the loop would make each chunk wait for the stores
+  // of the chunk before it.
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  // The next segment's loads go out now; only the next staging waits for them.
+  if constexpr (PREFETCH) {
+    const unsigned nb = sb + gridDim.x;
+    if (nb < nsb) seg_load<K, V, BF16, NT>(p, nb / p.nseg, (int)(nb % p.nseg) * kSL, nxt);
   }
 
   for (int w = (nvalid - 1) / C; w >= 0; --w) {
@@ -560,12 +664,12 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
         const size_t ow = (tok0 + l) * p.kws + i;
         const float ee = to_f32(s.q[(c0 + l) * KP + i]) * dq - s.g[(c0 + l) * KP + i] * dg;
         if (p.dq_acc) {
-          p.dq_acc[ow] = p.add_dq ? p.dq_acc[ow] + dq : dq;
+          p.dq_acc[ow] = dq;
         } else {
           stout<BF16>(p.dq, (tok0 + l) * p.ks + i, dq);
         }
-        p.dgw[ow] = p.add_e ? p.dgw[ow] + dg : dg;
-        p.ew[ow] = p.add_e ? p.ew[ow] + ee : ee;
+        p.dgw[ow] = dg;
+        p.ew[ow] = ee;
       }
     }
     if (vw) {
@@ -597,7 +701,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
         if (c0 + m >= nvalid) continue;
         if (p.dv_acc) {
           const size_t oa = (tok0 + m) * p.vacc + j;
-          p.dv_acc[oa] = p.add_dv ? p.dv_acc[oa] + dv[e] : dv[e];
+          p.dv_acc[oa] = dv[e];
         } else {
           stout<BF16>(p.dv, (tok0 + m) * p.vs + j, dv[e]);
         }
@@ -637,6 +741,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
     }
     __syncthreads();
   }
+  }  // segments
 }
 
 // ---------------------------------------------------------------------------
@@ -671,6 +776,10 @@ __device__ __forceinline__ ChainTok chain_tok(const BwdParams& p, size_t x, size
   c.vp = ldin<BF16>(p.vp, x);
   c.dg = p.dgw[xw];
   c.e = p.ew[xw];
+  if (p.ehalf) {  // the second value half's partials, added to the first's
+    c.dg += p.dgw[xw + p.ehalf];
+    c.e += p.ew[xw + p.ehalf];
+  }
   return c;
 }
 }  // namespace
@@ -777,7 +886,10 @@ static hipError_t launch_front(const BwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((kla_bwd_segagg_kernel<K, V, BF16>), dim3(nsb), dim3(512), 0, stream, p);
   constexpr int NB = (K * V + 255) / 256;
   hipLaunchKernelGGL((kla_bwd_segscan_kernel<K, V>), dim3((unsigned)(p.nheads * NB)), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((kla_bwd_chunk_kernel<K, V, BF16>), dim3(nsb), dim3(kChunkThreads), 0, stream, p);
+  // One workgroup per compute unit (its registers allow no more), each
+  // walking several segments.
+  const unsigned nchunk = nsb < (unsigned)p.ncu ? nsb : (unsigned)p.ncu;
+  hipLaunchKernelGGL((kla_bwd_chunk_kernel<K, V, BF16>), dim3(nchunk), dim3(kChunkThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -826,10 +938,11 @@ hipError_t launch_backward_chain(const BwdParams& p, int dk, bool bf16, hipStrea
 template <bool BF16>
 __global__ __launch_bounds__(256) void kla_bwd_convert_kernel(const float* acc, void* out, long long n) {
   const long long x = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (x < n) stout<BF16>(out, x, acc[x]);
+  if (x < n) stout<BF16>(out, x, acc[x] + acc[x + n]);
 }
 
-// fp32 accumulator -> output dtype.
+// Two fp32 partials (acc[0 .. n) and acc[n .. 2n), the two halves of a
+// 128-wide sum) -> their sum in the output dtype.
 hipError_t launch_backward_convert(const float* acc, void* out, long long n, bool bf16, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256));

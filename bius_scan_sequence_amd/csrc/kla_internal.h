@@ -121,6 +121,7 @@ struct BwdParams {
   float* dlam0;
   float* dM0;
   int nheads, T, nseg;
+  int ncu;            // compute units of the device (the chunk kernel's grid)
   long long nchains;  // nheads * dk
   float* F;           // [nheads][nseg][dk] product of forget gates over the segment
   float* Mseg;        // [nheads][nseg][dk][dv] segment aggregate, then the mean entering the segment
@@ -128,6 +129,8 @@ struct BwdParams {
   float* rs;          // [nheads][dk] sum_j M_T[i][j] dM_T[i][j]
   float* dgw;         // [nheads][T][dk] gradient of the write gate
   float* ew;          // [nheads][T][dk] q dq - g dg (per-token share of the log-forget-gate gradient)
+  size_t ehalf;       // nonzero: dgw and ew hold a second value half's partials ehalf elements on,
+                      // which the chain adds to the first's
   float* comp;        // [nseg][nchains][4] reverse-chain block composites
   float* cin;         // [nseg][nchains][2] reverse-chain state entering each block from the right
   // Strides (elements).  A call with d_k or d_v = 128 runs as 64-wide
@@ -139,10 +142,9 @@ struct BwdParams {
   int ksh;            // head of the key vectors (lam0, dlamT, dlam0, rs)
   int mrow, mhead;    // row and head of the state matrices (M0, dMT, dM0)
   int vacc;           // row of dv_acc
-  float* dq_acc;      // nullable: dq accumulated here in fp32 instead of written
-  float* dv_acc;      // nullable: dv accumulated here in fp32 instead of written
-  int add_e;          // add into dgw, ew and rs (a later value half) instead of writing
-  int add_dq, add_dv; // add into dq_acc / dv_acc instead of writing
+  float* dq_acc;      // nullable: this value half's fp32 partial of dq, written instead of dq
+  float* dv_acc;      // nullable: this key half's fp32 partial of dv, written instead of dv
+  int add_rs;         // add into rs (a later value half) instead of writing
 };
 
 struct VprecParams {
