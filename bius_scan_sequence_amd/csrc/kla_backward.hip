@@ -46,6 +46,15 @@ namespace {
 constexpr int kSL = 64;  // tokens per segment
 constexpr int kC = 16;   // tokens per chunk
 constexpr int kChunkThreads = 512;
+// LDS row strides, in elements.  Rows of the 64-token [t][channel] arrays are
+// K + 4 long (a multiple of 4 that is 4 modulo 32): a matrix-core operand read
+// (rows 4 lg + e, columns lr of a 16-lane group) then hits distinct banks, and
+// staging writes four channels at once.  The 16-row per-chunk arrays are read
+// both by rows lr and by rows 4 lg + e: K + 3 keeps both at two-way at most.
+// The 16 x 16 score tiles use rows of 17 for the same reason.
+template <int K> constexpr int kRowP = K + 4;
+template <int K> constexpr int kRow16P = K + 3;
+constexpr int kCP = 17;
 // s_waitcnt operand that waits for every vector memory operation (vmcnt 0)
 // and leaves the export and LDS/scalar counters at their maxima.
 constexpr int kVmcntZero = 0x0F70;
@@ -108,8 +117,8 @@ template <int V, bool BF16> struct VRow {
 };
 
 // A segment's raw inputs in registers: the first half of staging, issued a
-// segment ahead by the chunk kernel so that their loads overlap the chunks of
-// the segment before.  Four consecutive elements per load: 8 bytes for bf16,
+// segment ahead by the segment-aggregate and chunk kernels so that their
+// loads overlap the work on the segment before.  Four consecutive elements per load: 8 bytes for bf16,
 // 16 for fp32; pass x of the key side covers (token x / K4, channels
 // 4 (x % K4) ..), pass x of the value side likewise.
 template <bool BF16> using Raw4 = typename std::conditional<BF16, uint2, float4>::type;
@@ -180,7 +189,7 @@ __device__ __forceinline__ void seg_store(const BwdParams& p, size_t hd, int t0,
                                           typename VRow<V, BF16>::T* sd, float* sT, int* unsafe) {
   using In = typename std::conditional<BF16, uint16_t, float>::type;
   using L = SegLoads<K, V, BF16, NT>;
-  constexpr int KP = K + 1, VP = VRow<V, BF16>::P, K4 = K / 4, V4 = V / 4;
+  constexpr int KP = kRowP<K>, VP = VRow<V, BF16>::P, K4 = K / 4, V4 = V / 4;
 #pragma unroll
   for (int pk = 0; pk < L::PK; ++pk) {
     const int x = threadIdx.x + pk * NT, t = x / K4, i = (x % K4) * 4;
@@ -208,11 +217,14 @@ __device__ __forceinline__ void seg_store(const BwdParams& p, size_t hd, int t0,
       gate1(lam.w, lprev.w, ld.w, pn.w, k.w, vp.w, lf[3], g[3]);
       q[0] = qq.x; q[1] = qq.y; q[2] = qq.z; q[3] = qq.w;
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      slb[t * KP + i + e] = lf[e];
-      sg[t * KP + i + e] = g[e];
-      sq[t * KP + i + e] = from_f32<QT>(q[e]);  // exact: q is a value of the input type
+    *reinterpret_cast<float4*>(slb + t * KP + i) = make_float4(lf[0], lf[1], lf[2], lf[3]);
+    *reinterpret_cast<float4*>(sg + t * KP + i) = make_float4(g[0], g[1], g[2], g[3]);
+    if constexpr (std::is_same<QT, float>::value) {
+      *reinterpret_cast<float4*>(sq + t * KP + i) = make_float4(q[0], q[1], q[2], q[3]);
+    } else {  // bf16 bits of q (exact: q is a bf16 value)
+      *reinterpret_cast<uint2*>(sq + t * KP + i) =
+          make_uint2((__float_as_uint(q[0]) >> 16) | (__float_as_uint(q[1]) & 0xffff0000u),
+                     (__float_as_uint(q[2]) >> 16) | (__float_as_uint(q[3]) & 0xffff0000u));
     }
   }
 #pragma unroll
@@ -255,29 +267,38 @@ __device__ __forceinline__ void seg_store(const BwdParams& p, size_t hd, int t0,
   __syncthreads();
 }
 
-template <int K, int V, bool BF16, int NT, typename QT>
-__device__ __forceinline__ void stage_segment(const BwdParams& p, size_t hd, int t0, float* slb, float* sg,
-                                              QT* sq, typename VRow<V, BF16>::T* sv,
-                                              typename VRow<V, BF16>::T* sd, float* sT, int* unsafe) {
-  SegLoads<K, V, BF16, NT> r;
-  seg_load<K, V, BF16, NT>(p, hd, t0, r);
-  seg_store<K, V, BF16, NT>(p, hd, t0, r, slb, sg, sq, sv, sd, sT, unsafe);
-}
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// 1. Segment aggregates.  Grid: nheads * nseg workgroups of 512 threads.
+// 1. Segment aggregates.  Workgroups of 512 threads, each taking segments
+// blockIdx, blockIdx + gridDim, ...; for bf16 inputs the next segment's inputs
+// are loaded into registers while the current one is reduced.
 // ---------------------------------------------------------------------------
 template <int K, int V, bool BF16>
 __global__ __launch_bounds__(512) void kla_bwd_segagg_kernel(BwdParams p) {
   using SV = typename VRow<V, BF16>::T;
-  constexpr int KP = K + 1, VP = VRow<V, BF16>::P, NT = 512;
-  __shared__ float sl[kSL * KP], sa[kSL * KP], sb[kSL * KP], sT[4 * K];
+  constexpr int KP = kRowP<K>, VP = VRow<V, BF16>::P, NT = 512;
+  __shared__ __align__(16) float sl[kSL * KP];
+  __shared__ __align__(16) float sa[kSL * KP];
+  __shared__ __align__(16) float sb[kSL * KP];
+  __shared__ float sT[4 * K];
   __shared__ SV sv[kSL * VP], sd[kSL * VP];
-  const size_t hd = blockIdx.x / p.nseg;
-  const int s = blockIdx.x % p.nseg;
   const int tid = threadIdx.x;
-  stage_segment<K, V, BF16, NT>(p, hd, s * kSL, sl, sa, sb, sv, sd, sT, nullptr);
+  constexpr bool PREFETCH = BF16;
+  const unsigned nsb = (unsigned)p.nheads * (unsigned)p.nseg;
+  SegLoads<K, V, BF16, NT> nxt;
+  if constexpr (PREFETCH)
+    if (blockIdx.x < nsb) seg_load<K, V, BF16, NT>(p, blockIdx.x / p.nseg, (int)(blockIdx.x % p.nseg) * kSL, nxt);
+  for (unsigned sg = blockIdx.x; sg < nsb; sg += gridDim.x) {
+  const size_t hd = sg / p.nseg;
+  const int s = (int)(sg % p.nseg);
+  if (sg != blockIdx.x) __syncthreads();  // the previous segment's tiles are read
+  if constexpr (!PREFETCH) seg_load<K, V, BF16, NT>(p, hd, s * kSL, nxt);
+  seg_store<K, V, BF16, NT>(p, hd, s * kSL, nxt, sl, sa, sb, sv, sd, sT, static_cast<int*>(nullptr));
+  if constexpr (PREFETCH) {
+    const unsigned nb = sg + gridDim.x;
+    if (nb < nsb) seg_load<K, V, BF16, NT>(p, nb / p.nseg, (int)(nb % p.nseg) * kSL, nxt);
+  }
   // alpha_t = g_t prod_{u>t} f_u (in place of g), beta_t = q_t prod_{u<=t} f_u
   // (in place of q), for t in chunk c: the products are exp2 of the chunk's
   // partial sums plus the totals of the later / earlier chunks.
@@ -321,6 +342,7 @@ __global__ __launch_bounds__(512) void kla_bwd_segagg_kernel(BwdParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) U[(ib * 16 + 4 * lg + e) * V + jb * 16 + lr] = acc[e];
   }
+  }  // segments
 }
 
 // ---------------------------------------------------------------------------
@@ -449,24 +471,91 @@ __device__ __forceinline__ void load_state(const float* Gg, const float* Mg, boo
 }
 
 template <int K, int V, bool BF16>
-struct BwdChunkSmem {
+struct alignas(16) BwdChunkSmem {
   using SV = typename VRow<V, BF16>::T;
-  static constexpr int KP = K + 1, VP = VRow<V, BF16>::P;
+  static constexpr int KP = kRowP<K>, K16 = kRow16P<K>, VP = VRow<V, BF16>::P;
   float lb[kSL * KP], g[kSL * KP];
   SV q[kSL * KP];
   SV v[kSL * VP], d[kSL * VP];
-  float qE[kC * KP];          // q_l E_l
-  float gF[kC * KP];          // g_l F_l
-  float kd[kC * KP];          // g_l sx_l (write gate decayed to the chunk end)
-  float be[kC * KP];          // q_l cp_l (query decayed from the chunk start)
-  float A[kC * kC], B[kC * kC];  // A[l][m] = q_l . (g_m decayed to l); B[l][m] = dy_l . v_m (m <= l; 0 above)
+  // Per-chunk operands, two buffers: chunk w's in buffer w & 1 while chunk
+  // w - 1's are being formed.
+  float qE[2][kC * K16];      // q_l E_l
+  float gF[2][kC * K16];      // g_l F_l
+  float kd[2][kC * K16];      // g_l sx_l (write gate decayed to the chunk end)
+  float be[2][kC * K16];      // q_l cp_l (query decayed from the chunk start)
+  float A[2][kC * kCP], B[2][kC * kCP];  // A[l][m] = q_l . (g_m decayed to l); B[l][m] = dy_l . v_m (m <= l; 0 above)
   float T[4 * K];             // sum of log2 f over each chunk of the segment
   int unsafe[4];              // chunk needs the exact in-chunk path
 };
 
+// Operands of chunk w (tokens 16 w ..) into buffer `buf`: the decayed rows
+// qE, gF, kd, be by threads grp, grp + gsize, ... of a group of gsize threads
+// (E = prod f from the chunk's token 7 to l, F its inverse, cp = prod f from
+// the chunk start, sx = prod f to the chunk end, all exp2 of short sums), and
+// the two 16 x 16 score tiles: B by wave 7, A by wave 6 from the same products
+// (or, on the exact path, one (l, m) pair per group thread).
+template <int K, int V, bool BF16>
+__device__ __forceinline__ void chunk_operands(BwdChunkSmem<K, V, BF16>& s, int w, int buf, int grp, int gsize, int wave,
+                                               int lg, int lr) {
+  constexpr int KP = kRowP<K>, K16 = kRow16P<K>, VP = VRow<V, BF16>::P, C = kC, CP = kCP, VB = V / 16;
+  const int c0 = w * C;
+  for (int x = grp; x < C * K; x += gsize) {
+    const int l = x / K, i = x % K;
+    const float lb = s.lb[(c0 + l) * KP + i], lb7 = s.lb[(c0 + 7) * KP + i];
+    const float tot = s.T[w * K + i];
+    const float E = ex2(lb - lb7), F = ex2(lb7 - lb), cp = ex2(lb), sx = ex2(tot - lb);
+    const float q = to_f32(s.q[(c0 + l) * KP + i]), g = s.g[(c0 + l) * KP + i];
+    s.qE[buf][l * K16 + i] = q * E;
+    s.gF[buf][l * K16 + i] = g * F;
+    s.kd[buf][l * K16 + i] = g * sx;
+    s.be[buf][l * K16 + i] = q * cp;
+  }
+  if (wave == 7) {
+    // B[l][m] = dy_l . v_m (one tile, V/16 blocks).
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jb = 0; jb < VB; ++jb) {
+      const v4f a = row4(&s.d[(c0 + lr) * VP + jb * 16 + 4 * lg]);
+      const v4f b = row4(&s.v[(c0 + lr) * VP + jb * 16 + 4 * lg]);
+      acc = mma_f32(acc, a, b);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s.B[buf][(4 * lg + e) * CP + lr] = lr <= 4 * lg + e ? acc[e] : 0.f;
+  }
+  if (s.unsafe[w] == 0) {
+    if (wave == 6) {
+      // A = tril((q E)(g F)^T) (one tile, K/16 blocks).
+      v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < K; kb += 16) {
+        v4f a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = kb + 4 * lg + e;
+          const float lb = s.lb[(c0 + lr) * KP + i], lb7 = s.lb[(c0 + 7) * KP + i];
+          a[e] = to_f32(s.q[(c0 + lr) * KP + i]) * ex2(lb - lb7);
+          b[e] = s.g[(c0 + lr) * KP + i] * ex2(lb7 - lb);
+        }
+        acc = mma_f32(acc, a, b);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s.A[buf][(4 * lg + e) * CP + lr] = lr <= 4 * lg + e ? acc[e] : 0.f;
+    }
+  } else if (grp < C * C) {
+    // Exact scores: A[l][m] = sum_i q_l g_m exp2(lb_l - lb_m), m <= l.
+    const int l = grp / C, m = grp % C;
+    float acc = 0.f;
+    if (m <= l)
+      for (int i = 0; i < K; ++i)
+        acc = fmaf(to_f32(s.q[(c0 + l) * KP + i]) * s.g[(c0 + m) * KP + i],
+                   ex2(s.lb[(c0 + l) * KP + i] - s.lb[(c0 + m) * KP + i]), acc);
+    s.A[buf][l * CP + m] = acc;
+  }
+}
+
 template <int K, int V, bool BF16>
 __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams p) {
-  constexpr int KP = K + 1, VP = VRow<V, BF16>::P, NT = kChunkThreads, C = kC;
+  constexpr int KP = kRowP<K>, K16 = kRow16P<K>, VP = VRow<V, BF16>::P, NT = kChunkThreads, C = kC, CP = kCP;
   constexpr int KB = K / 16, VB = V / 16;
   static_assert(NT == 2 * C * C && NT == 512, "eight waves; one score pair per thread of the first four");
   __shared__ BwdChunkSmem<K, V, BF16> s;
@@ -517,24 +606,17 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
     if (nb < nsb) seg_load<K, V, BF16, NT>(p, nb / p.nseg, (int)(nb % p.nseg) * kSL, nxt);
   }
 
-  for (int w = (nvalid - 1) / C; w >= 0; --w) {
-    const int c0 = w * C;
-    // (a) elementwise decays of this chunk.
-    for (int x = tid; x < C * K; x += NT) {
-      const int l = x / K, i = x % K;
-      const float lb = s.lb[(c0 + l) * KP + i], lb7 = s.lb[(c0 + 7) * KP + i];
-      const float tot = s.T[w * K + i];
-      const float E = ex2(lb - lb7), F = ex2(lb7 - lb), cp = ex2(lb), sx = ex2(tot - lb);
-      const float q = to_f32(s.q[(c0 + l) * KP + i]), g = s.g[(c0 + l) * KP + i];
-      s.qE[l * KP + i] = q * E;
-      s.gF[l * KP + i] = g * F;
-      s.kd[l * KP + i] = g * sx;
-      s.be[l * KP + i] = q * cp;
-    }
+  // The last chunk's operands by the whole workgroup; inside the loop the
+  // key waves work on chunk w while waves 4..7, after their own share of it,
+  // form chunk w - 1's operands in the other buffer: one barrier per chunk.
+  const int wl = (nvalid - 1) / C;
+  chunk_operands<K, V, BF16>(s, wl, wl & 1, tid, NT, wave, lg, lr);
+  __syncthreads();
+  for (int w = wl; w >= 0; --w) {
+    const int c0 = w * C, cur = w & 1;
     const bool safe = s.unsafe[w] == 0;
-    __syncthreads();
     // (b) M_c^T tiles: the segment state decayed to the chunk start plus the
-    // tokens before the chunk (v^T al over t < c0); the two score matrices.
+    // tokens before the chunk (v^T al over t < c0).
     if (kw) {
       const int i = kb_w * 16 + lr;
       float lP = 0.f;
@@ -565,47 +647,6 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
         }
       }
     }
-    if (wave == 7) {
-      // B[l][m] = dy_l . v_m (one tile, V/16 blocks).
-      v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int jb = 0; jb < VB; ++jb) {
-        const v4f a = row4(&s.d[(c0 + lr) * VP + jb * 16 + 4 * lg]);
-        const v4f b = row4(&s.v[(c0 + lr) * VP + jb * 16 + 4 * lg]);
-        acc = mma_f32(acc, a, b);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s.B[(4 * lg + e) * C + lr] = lr <= 4 * lg + e ? acc[e] : 0.f;
-    }
-    if (safe) {
-      if (wave == 6) {
-        // A = tril((q E)(g F)^T) (one tile, K/16 blocks).
-        v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < K; kb += 16) {
-          v4f a, b;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = kb + 4 * lg + e;
-            a[e] = s.qE[lr * KP + i];
-            b[e] = s.gF[lr * KP + i];
-          }
-          acc = mma_f32(acc, a, b);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s.A[(4 * lg + e) * C + lr] = lr <= 4 * lg + e ? acc[e] : 0.f;
-      }
-    } else {
-      // Exact scores: A[l][m] = sum_i q_l g_m exp2(lb_l - lb_m), m <= l.
-      const int l = (tid / C) % C, m = tid % C;
-      float acc = 0.f;
-      if (m <= l && tid < C * C)
-        for (int i = 0; i < K; ++i)
-          acc = fmaf(to_f32(s.q[(c0 + l) * KP + i]) * s.g[(c0 + m) * KP + i],
-                     ex2(s.lb[(c0 + l) * KP + i] - s.lb[(c0 + m) * KP + i]), acc);
-      if (tid < C * C) s.A[l * C + m] = acc;
-    }
-    __syncthreads();
     // (c) outputs.
     const size_t tok0 = hd * (size_t)p.T + t0 + c0;
     if (kw) {
@@ -625,10 +666,10 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int n = 4 * lg + e;
-          a[e] = s.B[lr * C + n];  // tril(B)[l = lr][m = n]
-          b[e] = s.gF[n * KP + i];
-          c[e] = s.B[n * C + lr];  // tril(B)^T[l = lr][n]
-          d[e] = s.qE[n * KP + i];
+          a[e] = s.B[cur][lr * CP + n];  // tril(B)[l = lr][m = n]
+          b[e] = s.gF[cur][n * K16 + i];
+          c[e] = s.B[cur][n * CP + lr];  // tril(B)^T[l = lr][n]
+          d[e] = s.qE[cur][n * K16 + i];
         }
         dqi = mma_f32(dqi, a, b);
         dgi = mma_f32(dgi, c, d);
@@ -647,8 +688,8 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
           float aq = 0.f, ag = 0.f;
           for (int m = 0; m < C; ++m) {
             const float lbm = s.lb[(c0 + m) * KP + i];
-            if (m <= l) aq = fmaf(s.B[l * C + m] * s.g[(c0 + m) * KP + i], ex2(lbl - lbm), aq);
-            if (m >= l) ag = fmaf(s.B[m * C + l] * to_f32(s.q[(c0 + m) * KP + i]), ex2(lbm - lbl), ag);
+            if (m <= l) aq = fmaf(s.B[cur][l * CP + m] * s.g[(c0 + m) * KP + i], ex2(lbl - lbm), aq);
+            if (m >= l) ag = fmaf(s.B[cur][m * CP + l] * to_f32(s.q[(c0 + m) * KP + i]), ex2(lbm - lbl), ag);
           }
           dqi[e] = aq;
           dgi[e] = ag;
@@ -682,7 +723,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = ib * 16 + 4 * lg + e;
-          a[e] = s.kd[lr * KP + i];
+          a[e] = s.kd[cur][lr * K16 + i];
         }
         dv = mma_f32(dv, a, Hc[ib]);
       }
@@ -690,7 +731,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
         v4f a, b;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a[e] = s.A[(4 * lg + e) * C + lr];  // tril(A)^T[m = lr][l]
+          a[e] = s.A[cur][(4 * lg + e) * CP + lr];  // tril(A)^T[m = lr][l]
           b[e] = to_f32(s.d[(c0 + 4 * lg + e) * VP + j]);
         }
         dv = mma_f32(dv, a, b);
@@ -717,7 +758,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             Hc[ib][e] *= ex2(s.lb[(c0 + C - 1) * KP + ib * 16 + 4 * lg + e]);
-            a[e] = s.be[(4 * lg + e) * KP + ib * 16 + lr];
+            a[e] = s.be[cur][(4 * lg + e) * K16 + ib * 16 + lr];
             b[e] = to_f32(s.d[(c0 + 4 * lg + e) * VP + vb_w * 16 + lr]);
           }
           Hc[ib] = mma_f32(Hc[ib], a, b);
@@ -733,12 +774,13 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
           for (int e = 0; e < 4; ++e) {
             Ht[jb][e] *= ce;
             a[e] = to_f32(s.d[(c0 + 4 * lg + e) * VP + jb * 16 + lr]);
-            b[e] = s.be[(4 * lg + e) * KP + i];
+            b[e] = s.be[cur][(4 * lg + e) * K16 + i];
           }
           Ht[jb] = mma_f32(Ht[jb], a, b);
         }
       }
     }
+    if (wave >= 4 && w > 0) chunk_operands<K, V, BF16>(s, w - 1, (w - 1) & 1, tid - 256, NT - 256, wave, lg, lr);
     __syncthreads();
   }
   }  // segments
@@ -824,9 +866,25 @@ __global__ __launch_bounds__(256) void kla_bwd_chain_carry_kernel(BwdParams p, i
   if (ch >= p.nchains) return;
   const size_t kv = (size_t)(ch / K) * p.ksh + ch % K;  // this channel in the key vectors
   float acc = p.rs[kv], L = p.dlamT ? p.dlamT[kv] : 0.f;
-  for (int b = p.nseg - 1; b >= 0; --b) {
-    reinterpret_cast<float2*>(p.cin)[(size_t)b * p.nchains + ch] = make_float2(acc, L);
-    const float4 c = reinterpret_cast<const float4*>(p.comp)[(size_t)b * p.nchains + ch];
+  const float4* comp = reinterpret_cast<const float4*>(p.comp);
+  float2* cin = reinterpret_cast<float2*>(p.cin);
+  int b = p.nseg - 1;
+  // Blocks in batches of eight, the batch's loads issued together (the
+  // recursion itself is a few multiply-adds per block).
+  for (; b >= 7; b -= 8) {
+    float4 c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c[u] = comp[(size_t)(b - u) * p.nchains + ch];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      cin[(size_t)(b - u) * p.nchains + ch] = make_float2(acc, L);
+      L = fmaf(c[u].y, L, fmaf(c[u].z, acc, c[u].w));
+      acc += c[u].x;
+    }
+  }
+  for (; b >= 0; --b) {
+    cin[(size_t)b * p.nchains + ch] = make_float2(acc, L);
+    const float4 c = comp[(size_t)b * p.nchains + ch];
     L = fmaf(c.y, L, fmaf(c.z, acc, c.w));
     acc += c.x;
   }
@@ -883,7 +941,9 @@ __global__ void kla_bwd_empty_kernel(const float* dlamT, const float* dMT, float
 template <int K, int V, bool BF16>
 static hipError_t launch_front(const BwdParams& p, hipStream_t stream) {
   const unsigned nsb = (unsigned)((long long)p.nheads * p.nseg);
-  hipLaunchKernelGGL((kla_bwd_segagg_kernel<K, V, BF16>), dim3(nsb), dim3(512), 0, stream, p);
+  // Two workgroups per compute unit fit its LDS; each walks several segments.
+  const unsigned nagg = nsb < 2u * (unsigned)p.ncu ? nsb : 2u * (unsigned)p.ncu;
+  hipLaunchKernelGGL((kla_bwd_segagg_kernel<K, V, BF16>), dim3(nagg), dim3(512), 0, stream, p);
   constexpr int NB = (K * V + 255) / 256;
   hipLaunchKernelGGL((kla_bwd_segscan_kernel<K, V>), dim3((unsigned)(p.nheads * NB)), dim3(256), 0, stream, p);
   // One workgroup per compute unit (its registers allow no more), each
