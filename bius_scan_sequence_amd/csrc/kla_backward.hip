@@ -108,6 +108,42 @@ __device__ __forceinline__ v4f row4(const uint16_t* p) {
 }
 __device__ __forceinline__ v4f row4(const float* p) { return v4f{p[0], p[1], p[2], p[3]}; }
 
+// bf16 inputs: a product whose one operand is exact in bf16 (the inputs v and
+// dy, held as their bit patterns) runs on v_mfma_f32_16x16x32_bf16.  The fp32
+// operand y is split into three bf16 terms, hi = bf16(y), mid = bf16(y - hi),
+// lo = bf16(y - hi - mid), about 24 bits of y together (two terms, 17 bits,
+// are too few: d log_decay sums the per-token products over the whole
+// sequence and their errors with it).  One instruction forms x.hi + x.mid,
+// a second x.lo: two instructions per K = 16 block against four of
+// v_mfma_f32_16x16x4_f32, at half the cycles each.  Products of two fp32
+// operands keep the fp32 path.
+struct Split3 {
+  v8s hm;  // [hi | mid]
+  v8s l0;  // [lo | 0]
+};
+__device__ __forceinline__ Split3 split3(v4f y) {
+  v4s h, m, l, r2;
+  split4(y, h, m);
+  v4f r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = (y[e] - to_f32((uint16_t)h[e])) - to_f32((uint16_t)m[e]);
+  split4(r, l, r2);
+  return Split3{cat(h, m), cat(l, v4s{0, 0, 0, 0})};
+}
+__device__ __forceinline__ v4f mma_ex(v4f acc, v4s x, const Split3& y) {  // x on the A side
+  acc = mma_x32(acc, cat(x, x), y.hm);
+  return mma_x32(acc, cat(x, v4s{0, 0, 0, 0}), y.l0);
+}
+__device__ __forceinline__ v4f mma_xe(v4f acc, const Split3& y, v4s x) {  // x on the B side
+  acc = mma_x32(acc, y.hm, cat(x, x));
+  return mma_x32(acc, y.l0, cat(x, v4s{0, 0, 0, 0}));
+}
+// Bit patterns of four bf16 values: consecutive (8-byte aligned) or strided.
+__device__ __forceinline__ v4s bits4(const uint16_t* p) { return *reinterpret_cast<const v4s*>(p); }
+__device__ __forceinline__ v4s bits4(const uint16_t* p, int stride) {
+  return v4s{(short)p[0], (short)p[stride], (short)p[2 * stride], (short)p[3 * stride]};
+}
+
 // v and dy are kept in their input type (bf16 bits are exact); the row
 // stride of those arrays, in elements: bf16 rows padded by 4 elements, so that
 // the four 4-row groups of a matrix-core operand read fall on distinct banks.
@@ -125,7 +161,7 @@ template <bool BF16> using Raw4 = typename std::conditional<BF16, uint2, float4>
 template <int K, int V, bool BF16, int NT>
 struct SegLoads {
   static constexpr int PK = (kSL * (K / 4) + NT - 1) / NT, PV = (kSL * (V / 4) + NT - 1) / NT;
-  float4 lam[PK];
+  float4 lam[PK], lprev[PK];  // the precision path at the token and one token earlier
   Raw4<BF16> ld[PK], pn[PK], k[PK], vp[PK], q[PK];
   Raw4<BF16> v[PV], d[PV];
 };
@@ -152,10 +188,18 @@ __device__ __forceinline__ void seg_load(const BwdParams& p, size_t hd, int t0, 
   for (int pk = 0; pk < L::PK; ++pk) {
     const int x = threadIdx.x + pk * NT, t = x / K4, i = (x % K4) * 4;
     r.lam[pk] = make_float4(0.f, 0.f, 0.f, 0.f);
+    r.lprev[pk] = make_float4(1.f, 1.f, 1.f, 1.f);
     r.ld[pk] = r.pn[pk] = r.k[pk] = r.vp[pk] = r.q[pk] = z;
     if (x < kSL * K4 && t0 + t < p.T) {
       const size_t e = (hd * p.T + t0 + t) * p.ks + i;
       r.lam[pk] = *reinterpret_cast<const float4*>(p.lpath + e);
+      // The precision before the token: the path one token earlier, or the prior.
+      if (t0 + t > 0) {
+        r.lprev[pk] = *reinterpret_cast<const float4*>(p.lpath + e - p.ks);
+      } else if (p.lam0) {
+        const float* l0 = p.lam0 + hd * p.ksh + i;
+        r.lprev[pk] = make_float4(l0[0], l0[1], l0[2], l0[3]);
+      }
       r.ld[pk] = ldraw4<BF16>(p.ld, e);
       r.pn[pk] = ldraw4<BF16>(p.pn, e);
       r.k[pk] = ldraw4<BF16>(p.k, e);
@@ -196,19 +240,7 @@ __device__ __forceinline__ void seg_store(const BwdParams& p, size_t hd, int t0,
     if (x >= kSL * K4) continue;
     float lf[4] = {0.f, 0.f, 0.f, 0.f}, g[4] = {0.f, 0.f, 0.f, 0.f}, q[4] = {0.f, 0.f, 0.f, 0.f};
     if (t0 + t < p.T) {
-      // The precision before the token: the path one token earlier (read
-      // here, mostly from cache: the rows were just loaded), or the prior.
-      const size_t e = (hd * p.T + t0 + t) * p.ks + i;
-      float4 lprev;
-      if (t0 + t > 0) {
-        lprev = *reinterpret_cast<const float4*>(p.lpath + e - p.ks);
-      } else if (p.lam0) {
-        const float* l0 = p.lam0 + hd * p.ksh + i;
-        lprev = make_float4(l0[0], l0[1], l0[2], l0[3]);
-      } else {
-        lprev = make_float4(1.f, 1.f, 1.f, 1.f);
-      }
-      const float4 lam = r.lam[pk];
+      const float4 lam = r.lam[pk], lprev = r.lprev[pk];
       const float4 ld = raw_f4(r.ld[pk]), pn = raw_f4(r.pn[pk]), k = raw_f4(r.k[pk]), vp = raw_f4(r.vp[pk]),
                    qq = raw_f4(r.q[pk]);
       gate1(lam.x, lprev.x, ld.x, pn.x, k.x, vp.x, lf[0], g[0]);
@@ -301,46 +333,80 @@ __global__ __launch_bounds__(512) void kla_bwd_segagg_kernel(BwdParams p) {
   }
   // alpha_t = g_t prod_{u>t} f_u (in place of g), beta_t = q_t prod_{u<=t} f_u
   // (in place of q), for t in chunk c: the products are exp2 of the chunk's
-  // partial sums plus the totals of the later / earlier chunks.
-  for (int x = tid; x < kSL * K; x += NT) {
-    const int t = x / K, i = x % K, c = t / kC;
-    float after = 0.f, before = 0.f;
+  // partial sums plus the totals of the later / earlier chunks.  A thread
+  // keeps one channel (NT is a multiple of K), so its four chunks' offsets
+  // are formed once.
+  {
+    static_assert(NT % K == 0, "one channel per thread");
+    const int i = tid % K;
+    float tot[4], aft[4], bef[4];
 #pragma unroll
-    for (int c2 = 0; c2 < 4; ++c2) {
-      if (c2 > c) after += sT[c2 * K + i];
-      if (c2 < c) before += sT[c2 * K + i];
+    for (int c = 0; c < 4; ++c) tot[c] = sT[c * K + i];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      aft[c] = 0.f;
+      bef[c] = 0.f;
+#pragma unroll
+      for (int c2 = 0; c2 < 4; ++c2) {
+        if (c2 > c) aft[c] += tot[c2];
+        if (c2 < c) bef[c] += tot[c2];
+      }
     }
-    const float lb = sl[t * KP + i];
-    sa[t * KP + i] *= ex2((sT[c * K + i] - lb) + after);
-    sb[t * KP + i] *= ex2(lb + before);
+#pragma unroll
+    for (int u = 0; u < kSL * K / NT; ++u) {
+      const int t = tid / K + u * (NT / K), c = t / kC;
+      // c is a compile-time function of u when a pass covers whole chunks;
+      // otherwise pick among the four without indexing the register arrays.
+      const float Tc = c == 0 ? tot[0] : c == 1 ? tot[1] : c == 2 ? tot[2] : tot[3];
+      const float A = c == 0 ? aft[0] : c == 1 ? aft[1] : c == 2 ? aft[2] : aft[3];
+      const float Bf = c == 0 ? bef[0] : c == 1 ? bef[1] : c == 2 ? bef[2] : bef[3];
+      const float lb = sl[t * KP + i];
+      sa[t * KP + i] *= ex2((Tc - lb) + A);
+      sb[t * KP + i] *= ex2(lb + Bf);
+    }
   }
   if (tid < K) p.F[(hd * p.nseg + s) * K + tid] = ex2(sT[tid] + sT[K + tid] + sT[2 * K + tid] + sT[3 * K + tid]);
   __syncthreads();
-  // Mean aggregate alpha^T v and adjoint aggregate beta^T dy as 16x16 fp32
-  // matrix-core tiles (v_mfma_f32_16x16x4_f32), over the 64 tokens.
-  constexpr int KB = K / 16, VB = V / 16, NTILE = 2 * KB * VB;
+  // Mean aggregate alpha^T v and adjoint aggregate beta^T dy as 16x16
+  // matrix-core tiles over the 64 tokens.  A wave takes one (aggregate, key
+  // block) pair and every value block, so each coefficient block is read
+  // (and, for bf16 inputs, split) once.
+  constexpr int KB = K / 16, VB = V / 16;
   const int wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
   const size_t base = (hd * p.nseg + s) * (size_t)(K * V);
-  for (int tile = wave; tile < NTILE; tile += NT / 64) {
-    const bool adj = tile >= KB * VB;
-    const int tt = adj ? tile - KB * VB : tile;
-    const int ib = tt / VB, jb = tt % VB;
+  for (int pr = wave; pr < 2 * KB; pr += NT / 64) {
+    const bool adj = pr >= KB;
+    const int ib = adj ? pr - KB : pr;
     const float* X = adj ? sb : sa;  // coefficient [t][i]
     const SV* Y = adj ? sd : sv;     // [t][j]
-    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    v4f acc[VB];
+#pragma unroll
+    for (int jb = 0; jb < VB; ++jb) acc[jb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < kSL; kb += 16) {
-      v4f a, b;
+      v4f a;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a[e] = X[(kb + 4 * lg + e) * KP + ib * 16 + lr];
-        b[e] = to_f32(Y[(kb + 4 * lg + e) * VP + jb * 16 + lr]);
+      for (int e = 0; e < 4; ++e) a[e] = X[(kb + 4 * lg + e) * KP + ib * 16 + lr];
+      if constexpr (BF16) {  // v and dy exact in bf16: the three-term split
+        const Split3 as = split3(a);
+#pragma unroll
+        for (int jb = 0; jb < VB; ++jb)
+          acc[jb] = mma_xe(acc[jb], as, bits4(&Y[(kb + 4 * lg) * VP + jb * 16 + lr], VP));
+      } else {
+#pragma unroll
+        for (int jb = 0; jb < VB; ++jb) {
+          v4f b;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b[e] = to_f32(Y[(kb + 4 * lg + e) * VP + jb * 16 + lr]);
+          acc[jb] = mma_f32(acc[jb], a, b);
+        }
       }
-      acc = mma_f32(acc, a, b);
     }
     float* U = (adj ? p.Gseg : p.Mseg) + base;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) U[(ib * 16 + 4 * lg + e) * V + jb * 16 + lr] = acc[e];
+    for (int jb = 0; jb < VB; ++jb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) U[(ib * 16 + 4 * lg + e) * V + jb * 16 + lr] = acc[jb][e];
   }
   }  // segments
 }
@@ -511,13 +577,25 @@ __device__ __forceinline__ void chunk_operands(BwdChunkSmem<K, V, BF16>& s, int 
     s.be[buf][l * K16 + i] = q * cp;
   }
   if (wave == 7) {
-    // B[l][m] = dy_l . v_m (one tile, V/16 blocks).
+    // B[l][m] = dy_l . v_m (one tile, V/16 blocks; bf16 inputs: exact
+    // products, two blocks per instruction).
     v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    if constexpr (BF16) {
 #pragma unroll
-    for (int jb = 0; jb < VB; ++jb) {
-      const v4f a = row4(&s.d[(c0 + lr) * VP + jb * 16 + 4 * lg]);
-      const v4f b = row4(&s.v[(c0 + lr) * VP + jb * 16 + 4 * lg]);
-      acc = mma_f32(acc, a, b);
+      for (int jb = 0; jb < VB; jb += 2) {
+        const v4s a0 = bits4(&s.d[(c0 + lr) * VP + jb * 16 + 4 * lg]);
+        const v4s b0 = bits4(&s.v[(c0 + lr) * VP + jb * 16 + 4 * lg]);
+        const v4s a1 = jb + 1 < VB ? bits4(&s.d[(c0 + lr) * VP + (jb + 1) * 16 + 4 * lg]) : v4s{0, 0, 0, 0};
+        const v4s b1 = jb + 1 < VB ? bits4(&s.v[(c0 + lr) * VP + (jb + 1) * 16 + 4 * lg]) : v4s{0, 0, 0, 0};
+        acc = mma_x32(acc, cat(a0, a1), cat(b0, b1));
+      }
+    } else {
+#pragma unroll
+      for (int jb = 0; jb < VB; ++jb) {
+        const v4f a = row4(&s.d[(c0 + lr) * VP + jb * 16 + 4 * lg]);
+        const v4f b = row4(&s.v[(c0 + lr) * VP + jb * 16 + 4 * lg]);
+        acc = mma_f32(acc, a, b);
+      }
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) s.B[buf][(4 * lg + e) * CP + lr] = lr <= 4 * lg + e ? acc[e] : 0.f;
@@ -638,12 +716,19 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
           b[e] = s.g[t * KP + i] * ex2(off - s.lb[t * KP + i]);
         }
         // one 16-token block of this chunk: four k-groups of 4 (e), tiles jb interleaved
+        if constexpr (BF16) {
+          const Split3 bs = split3(b);
 #pragma unroll
-        for (int jb = 0; jb < VB; ++jb) {
-          v4f a;
+          for (int jb = 0; jb < VB; ++jb)
+            Mt[jb] = mma_ex(Mt[jb], bits4(&s.v[(c2 * C + 4 * lg) * VP + jb * 16 + lr], VP), bs);
+        } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) a[e] = to_f32(s.v[(c2 * C + 4 * lg + e) * VP + jb * 16 + lr]);
-          Mt[jb] = mma_f32(Mt[jb], a, b);
+          for (int jb = 0; jb < VB; ++jb) {
+            v4f a;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] = to_f32(s.v[(c2 * C + 4 * lg + e) * VP + jb * 16 + lr]);
+            Mt[jb] = mma_f32(Mt[jb], a, b);
+          }
         }
       }
     }
@@ -654,12 +739,20 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
       // dgi = F (tril(B)^T (q E)) for key block `wave`.
       const int i = kb_w * 16 + lr;
       v4f xs = v4f{0.f, 0.f, 0.f, 0.f}, ys = xs, dqi = xs, dgi = xs;
+      if constexpr (BF16) {
 #pragma unroll
-      for (int jb = 0; jb < VB; ++jb) {
-        const v4f a = row4(&s.d[(c0 + lr) * VP + jb * 16 + 4 * lg]);
-        const v4f b = row4(&s.v[(c0 + lr) * VP + jb * 16 + 4 * lg]);
-        xs = mma_f32(xs, a, Mt[jb]);
-        ys = mma_f32(ys, b, Ht[jb]);
+        for (int jb = 0; jb < VB; ++jb) {
+          xs = mma_ex(xs, bits4(&s.d[(c0 + lr) * VP + jb * 16 + 4 * lg]), split3(Mt[jb]));
+          ys = mma_ex(ys, bits4(&s.v[(c0 + lr) * VP + jb * 16 + 4 * lg]), split3(Ht[jb]));
+        }
+      } else {
+#pragma unroll
+        for (int jb = 0; jb < VB; ++jb) {
+          const v4f a = row4(&s.d[(c0 + lr) * VP + jb * 16 + 4 * lg]);
+          const v4f b = row4(&s.v[(c0 + lr) * VP + jb * 16 + 4 * lg]);
+          xs = mma_f32(xs, a, Mt[jb]);
+          ys = mma_f32(ys, b, Ht[jb]);
+        }
       }
       if (safe) {
         v4f a, b, c, d;
@@ -732,9 +825,15 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           a[e] = s.A[cur][(4 * lg + e) * CP + lr];  // tril(A)^T[m = lr][l]
-          b[e] = to_f32(s.d[(c0 + 4 * lg + e) * VP + j]);
+          if constexpr (!BF16) b[e] = to_f32(s.d[(c0 + 4 * lg + e) * VP + j]);
         }
-        dv = mma_f32(dv, a, b);
+        if constexpr (BF16) {
+          // its own accumulator: no matrix-core instruction of one shape reads
+          // an accumulator that one of the other shape has just written
+          dv += mma_xe(v4f{0.f, 0.f, 0.f, 0.f}, split3(a), bits4(&s.d[(c0 + 4 * lg) * VP + j], VP));
+        } else {
+          dv = mma_f32(dv, a, b);
+        }
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -752,6 +851,8 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
     // in both orientations (registers of this wave; LDS operands of this chunk).
     if (w > 0) {
       if (vw) {
+        v4s bx = v4s{0, 0, 0, 0};
+        if constexpr (BF16) bx = bits4(&s.d[(c0 + 4 * lg) * VP + vb_w * 16 + lr], VP);
 #pragma unroll
         for (int ib = 0; ib < KB; ++ib) {
           v4f a, b;
@@ -759,24 +860,40 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
           for (int e = 0; e < 4; ++e) {
             Hc[ib][e] *= ex2(s.lb[(c0 + C - 1) * KP + ib * 16 + 4 * lg + e]);
             a[e] = s.be[cur][(4 * lg + e) * K16 + ib * 16 + lr];
-            b[e] = to_f32(s.d[(c0 + 4 * lg + e) * VP + vb_w * 16 + lr]);
+            if constexpr (!BF16) b[e] = to_f32(s.d[(c0 + 4 * lg + e) * VP + vb_w * 16 + lr]);
           }
-          Hc[ib] = mma_f32(Hc[ib], a, b);
+          if constexpr (BF16)
+            Hc[ib] = mma_xe(Hc[ib], split3(a), bx);
+          else
+            Hc[ib] = mma_f32(Hc[ib], a, b);
         }
       }
       if (kw) {
         const int i = kb_w * 16 + lr;
         const float ce = ex2(s.lb[(c0 + C - 1) * KP + i]);
+        if constexpr (BF16) {
+          v4f b;
 #pragma unroll
-        for (int jb = 0; jb < VB; ++jb) {
-          v4f a, b;
+          for (int e = 0; e < 4; ++e) b[e] = s.be[cur][(4 * lg + e) * K16 + i];
+          const Split3 bs = split3(b);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            Ht[jb][e] *= ce;
-            a[e] = to_f32(s.d[(c0 + 4 * lg + e) * VP + jb * 16 + lr]);
-            b[e] = s.be[cur][(4 * lg + e) * K16 + i];
+          for (int jb = 0; jb < VB; ++jb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ht[jb][e] *= ce;
+            Ht[jb] = mma_ex(Ht[jb], bits4(&s.d[(c0 + 4 * lg) * VP + jb * 16 + lr], VP), bs);
           }
-          Ht[jb] = mma_f32(Ht[jb], a, b);
+        } else {
+#pragma unroll
+          for (int jb = 0; jb < VB; ++jb) {
+            v4f a, b;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              Ht[jb][e] *= ce;
+              a[e] = to_f32(s.d[(c0 + 4 * lg + e) * VP + jb * 16 + lr]);
+              b[e] = s.be[cur][(4 * lg + e) * K16 + i];
+            }
+            Ht[jb] = mma_f32(Ht[jb], a, b);
+          }
         }
       }
     }
