@@ -57,16 +57,16 @@ def algorithmic_bytes(B, H, T, dk, dv, esz):
 def run_plan(nheads, T, ncu):
     """Runs per head and their tile counts as the library plans them for the
     run-streaming kernel (kla_forward_run.hip, fwd_run_plan): the run count
-    that minimises rounds of workgroups x tiles per workgroup (fewest runs on
-    ties), the tiles split as evenly as they go.  Returns the list of tile
-    counts, one per run."""
+    that minimises rounds of workgroups x (tiles per workgroup + 4, a run's
+    start and end), fewest runs on ties, the tiles split as evenly as they
+    go.  Returns the list of tile counts, one per run."""
     ntiles = (T + 63) // 64
     best, bestn = None, 1
     for n in range(1, ntiles + 1):
         r = (ntiles + n - 1) // n
         if (ntiles + r - 1) // r != n:
             continue
-        cost = ((nheads * n + ncu - 1) // ncu) * r
+        cost = ((nheads * n + ncu - 1) // ncu) * (r + 4)
         if best is None or cost < best:
             best, bestn = cost, n
     if bestn == 1:

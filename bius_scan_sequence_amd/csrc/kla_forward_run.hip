@@ -1133,6 +1133,12 @@ __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
 // per workgroup) on `ncu` compute units, fewest runs on ties; the tiles are
 // split as evenly as they go (the first Rx runs after run 0 take one more).
 // one_round: every run of every head is resident at once.
+// A run's start (workgroup launch, ticket, first tile's loads) and end (the
+// look-back, the held tiles' correction) cost about four tile steps; a round of
+// runs is priced at its tiles plus that.  (lm180m_bf16, 192 heads x 32 tiles:
+// three rounds of 8-tile runs took 152 us, one round of 32-tile runs 139 us.)
+constexpr int kRunOverheadTiles = 4;
+
 void fwd_run_plan(int nheads, int T, int ncu, int& R0, int& Rb, int& Rx, int& nrun, bool& one_round) {
   const int ntiles = (T + RTL - 1) / RTL;
   long long best = -1, best_rounds = 1;
@@ -1142,7 +1148,7 @@ void fwd_run_plan(int nheads, int T, int ncu, int& R0, int& Rb, int& Rx, int& nr
     const int nr = (ntiles + r - 1) / r;  // runs actually needed at r tiles each
     if (nr != n) continue;
     const long long rounds = ((long long)nheads * n + ncu - 1) / ncu;
-    const long long cost = rounds * r;
+    const long long cost = rounds * (r + kRunOverheadTiles);
     if (best < 0 || cost < best) {
       best = cost;
       best_rounds = rounds;

@@ -281,6 +281,34 @@ def test_run_kernel_slow_forgetting(case):
     run_case(f"run kernel {case}", x)
 
 
+def test_run_kernel_several_rounds():
+    """More runs than compute units: B24 H16 T1024 plans two 8-tile runs per
+    head, 768 workgroups in three rounds, so tickets are drawn across rounds
+    and a later run's look-back may meet predecessors that finished long ago
+    (their inclusive means out, some aggregates never published).  Bitwise
+    repeatable over three calls, and six heads against the oracle: from the
+    first and the last tickets of each run index."""
+    import torch
+    import bius_scan_sequence_amd as K
+    say("[case] run kernel several rounds: B=24 H=16 T=1024 d=64 bf16 seed=8104")
+    x = KI.make_forward_inputs("lm45m_bf16", B=24, H=16, T=1024, seed=8104)
+    xd = to_dev(x)
+    names = ("q", "k", "v", "log_decay", "proc_noise", "val_prec")
+    first = K.forward(*(xd[n] for n in names), return_lambda_path=True)
+    for _ in range(2):
+        again = K.forward(*(xd[n] for n in names), return_lambda_path=True)
+        torch.cuda.synchronize()
+        for a, b in zip(first, again):
+            assert torch.equal(a, b)
+    for b, h in ((0, 0), (0, 1), (11, 7), (12, 8), (23, 14), (23, 15)):
+        xs = {n: x[n][b:b + 1, h:h + 1] for n in names}
+        xs["dtype"] = "bf16"
+        ref = oracle_forward(xs, return_lambda_path=True)
+        got = tuple(t[b:b + 1, h:h + 1].float().cpu().numpy() for t in first)
+        check_forward(xs, got, ref, "bf16")
+    say("[ok] run kernel several rounds")
+
+
 def test_run_kernel_extreme_decays():
     """Chunks whose decay underflows 2^-120 on some channel take the run
     kernel's exact per-token path: in a free tile, across the boundary of two
