@@ -550,22 +550,24 @@ struct alignas(16) BwdChunkSmem {
   float kd[2][kC * K16];      // g_l sx_l (write gate decayed to the chunk end)
   float be[2][kC * K16];      // q_l cp_l (query decayed from the chunk start)
   float A[2][kC * kCP], B[2][kC * kCP];  // A[l][m] = q_l . (g_m decayed to l); B[l][m] = dy_l . v_m (m <= l; 0 above)
+  float cdec[2][K];           // prod f over the chunk, per channel (exp2 of its total)
   float T[4 * K];             // sum of log2 f over each chunk of the segment
   int unsafe[4];              // chunk needs the exact in-chunk path
 };
 
 // Operands of chunk w (tokens 16 w ..) into buffer `buf`: the decayed rows
-// qE, gF, kd, be by threads grp, grp + gsize, ... of a group of gsize threads
-// (E = prod f from the chunk's token 7 to l, F its inverse, cp = prod f from
-// the chunk start, sx = prod f to the chunk end, all exp2 of short sums), and
-// the two 16 x 16 score tiles: B by wave 7, A by wave 6 from the same products
-// (or, on the exact path, one (l, m) pair per group thread).
+// qE, gF, kd, be and the chunk's decay per channel by threads grp, grp + gsize,
+// ... of a group of gsize threads (none if grp < 0) (E = prod f from the
+// chunk's token 7 to l, F its inverse, cp = prod f from the chunk start,
+// sx = prod f to the chunk end, all exp2 of short sums), and the two 16 x 16
+// score tiles: B by wave 7, A by wave 6 from the same products (or, on the
+// exact path, one (l, m) pair per thread xp < 256 of the workgroup).
 template <int K, int V, bool BF16>
-__device__ __forceinline__ void chunk_operands(BwdChunkSmem<K, V, BF16>& s, int w, int buf, int grp, int gsize, int wave,
-                                               int lg, int lr) {
+__device__ __forceinline__ void chunk_operands(BwdChunkSmem<K, V, BF16>& s, int w, int buf, int grp, int gsize, int xp,
+                                               int wave, int lg, int lr) {
   constexpr int KP = kRowP<K>, K16 = kRow16P<K>, VP = VRow<V, BF16>::P, C = kC, CP = kCP, VB = V / 16;
   const int c0 = w * C;
-  for (int x = grp; x < C * K; x += gsize) {
+  for (int x = grp; grp >= 0 && x < C * K; x += gsize) {
     const int l = x / K, i = x % K;
     const float lb = s.lb[(c0 + l) * KP + i], lb7 = s.lb[(c0 + 7) * KP + i];
     const float tot = s.T[w * K + i];
@@ -575,6 +577,7 @@ __device__ __forceinline__ void chunk_operands(BwdChunkSmem<K, V, BF16>& s, int 
     s.gF[buf][l * K16 + i] = g * F;
     s.kd[buf][l * K16 + i] = g * sx;
     s.be[buf][l * K16 + i] = q * cp;
+    if (l == C - 1) s.cdec[buf][i] = cp;  // exp2 of the chunk's last cumulative value: its total
   }
   if (wave == 7) {
     // B[l][m] = dy_l . v_m (one tile, V/16 blocks; bf16 inputs: exact
@@ -619,9 +622,9 @@ __device__ __forceinline__ void chunk_operands(BwdChunkSmem<K, V, BF16>& s, int 
 #pragma unroll
       for (int e = 0; e < 4; ++e) s.A[buf][(4 * lg + e) * CP + lr] = lr <= 4 * lg + e ? acc[e] : 0.f;
     }
-  } else if (grp < C * C) {
+  } else if (xp >= 0 && xp < C * C) {
     // Exact scores: A[l][m] = sum_i q_l g_m exp2(lb_l - lb_m), m <= l.
-    const int l = grp / C, m = grp % C;
+    const int l = xp / C, m = xp % C;
     float acc = 0.f;
     if (m <= l)
       for (int i = 0; i < K; ++i)
@@ -688,7 +691,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
   // key waves work on chunk w while waves 4..7, after their own share of it,
   // form chunk w - 1's operands in the other buffer: one barrier per chunk.
   const int wl = (nvalid - 1) / C;
-  chunk_operands<K, V, BF16>(s, wl, wl & 1, tid, NT, wave, lg, lr);
+  chunk_operands<K, V, BF16>(s, wl, wl & 1, tid, NT, tid, wave, lg, lr);
   __syncthreads();
   for (int w = wl; w >= 0; --w) {
     const int c0 = w * C, cur = w & 1;
@@ -858,7 +861,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
           v4f a, b;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            Hc[ib][e] *= ex2(s.lb[(c0 + C - 1) * KP + ib * 16 + 4 * lg + e]);
+            Hc[ib][e] *= s.cdec[cur][ib * 16 + 4 * lg + e];
             a[e] = s.be[cur][(4 * lg + e) * K16 + ib * 16 + lr];
             if constexpr (!BF16) b[e] = to_f32(s.d[(c0 + 4 * lg + e) * VP + vb_w * 16 + lr]);
           }
@@ -870,7 +873,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
       }
       if (kw) {
         const int i = kb_w * 16 + lr;
-        const float ce = ex2(s.lb[(c0 + C - 1) * KP + i]);
+        const float ce = s.cdec[cur][i];
         if constexpr (BF16) {
           v4f b;
 #pragma unroll
@@ -897,7 +900,11 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
         }
       }
     }
-    if (wave >= 4 && w > 0) chunk_operands<K, V, BF16>(s, w - 1, (w - 1) & 1, tid - 256, NT - 256, wave, lg, lr);
+    // Wave 6 forms the score tile A and takes no share of the rows.
+    if (wave >= 4 && w > 0) {
+      const int grp = wave == 6 ? -1 : wave == 7 ? tid - 320 : tid - 256;
+      chunk_operands<K, V, BF16>(s, w - 1, (w - 1) & 1, grp, NT - 320, tid - 256, wave, lg, lr);
+    }
     __syncthreads();
   }
   }  // segments
