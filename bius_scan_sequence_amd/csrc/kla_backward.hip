@@ -24,10 +24,10 @@
 //               entering the chunk (from the segment's, plus the tokens before
 //               the chunk), the adjoint at its end (carried backwards), then
 //               dq and dv (final) and, per channel, the write-gate gradient dg
-//               and e = q dq - g dg.  In-chunk decays prod_{u=m+1..l} f_u are
-//               formed as running products (never as ratios of cumulative
-//               products, which can underflow), and inside the score matrix
-//               as exp2 of differences of cumulative log2 f.
+//               and e = q dq - g dg.  Decays prod_{u=m+1..l} f_u are exp2 of
+//               short sums of log2 f: differences of cumulative sums inside
+//               one 16-token chunk plus whole chunks' totals (never ratios of
+//               products over the segment, which can underflow).
 //   4. chain    per channel, backwards over tokens: d log f_t is the suffix
 //               sum of e (plus the M_T * dM_T row sum), and the adjoint of the
 //               precision obeys an affine recursion; both run as a two-level
