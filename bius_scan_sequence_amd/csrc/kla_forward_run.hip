@@ -321,7 +321,8 @@ __device__ __forceinline__ void correct_held(RunSmem& s, int lane, int c, int ti
   __builtin_amdgcn_raw_buffer_store_b64(wv, yrs, tok * (RD * 2) + (16 * c + 4 * G) * 2, 0, 0);
 }
 
-__device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, const RunCtx& x) {
+__device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, const RunCtx& x, uint4 (&pf)[10],
+                                            bool have_first) {
   const int tid = x.tid, lane = x.lane, w = x.wave, T = x.T, tb = x.tb, ntl = x.ntl;
   const size_t hoff = x.hoff;
   WLane L;
@@ -351,8 +352,9 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
       *reinterpret_cast<uint4*>(s.raw[a] + raw_off(row, xx)) = buf[it];
     }
   };
-  uint4 pf[10];  // the next tile's units, in flight
-  load(tb, pf, 0);
+  // pf: the next tile's units, in flight.  The first tile's are in flight
+  // already when the workgroup guessed its run right (have_first).
+  if (!have_first) load(tb, pf, 0);
   // The precision entering the run: lambda0 for the first run, else the
   // matrix waves' window walk (read in step 0, once they have published it).
   float lam_start = p.lam0 ? p.lam0[(size_t)x.head * RD + L.ch] : 1.f;
@@ -1067,56 +1069,79 @@ __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
   __shared__ RunSmem s;
   const int tid = threadIdx.x;
   KLA_STAMP(tid >> 8, 0);
-  if (tid == 0) {
-    s.ctl[cTicket] = draw_ticket(p.tick, (unsigned)p.tgroups, (unsigned)p.nheads / (unsigned)p.tgroups * (unsigned)p.nrun);
-    s.ctl[cEpoch] = p.nrun > 1 ? ld_relaxed(p.ctrl + kEpoch) : 0u;
-    s.ctl[cWSync] = 0u;
-    s.ctl[cXSync] = 0u;
-    s.ctl[cLamReady] = 0u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s.ctl[cCorr + i] = 0u;
-  }
-  __syncthreads();
-  // Ticket order is run-major within a group, and all runs of a head fall in
-  // one group, so every run a workgroup waits on holds a smaller ticket of
-  // its own counter and started earlier.
-  RunCtx x;
-  const unsigned ticket = s.ctl[cTicket];
-  const unsigned epoch = s.ctl[cEpoch];
-  x.tid = tid;
-  x.lane = tid & 63;
-  x.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  x.FAGG = 2u * epoch + 2u;
-  x.FINC = 2u * epoch + 3u;
-  x.nrun = p.nrun;
   // Group x = blockIdx % tgroups serves heads x, x + tgroups, ...: its
-  // tickets run over those heads, run-major.
+  // tickets run over those heads, run-major.  Ticket order is run-major within
+  // a group, and all runs of a head fall in one group, so every run a
+  // workgroup waits on holds a smaller ticket of its own counter and started
+  // earlier.
   const unsigned hpg = (unsigned)p.nheads / (unsigned)p.tgroups;
-  x.run = (int)(ticket / hpg);
-  x.head = (int)((ticket % hpg) * (unsigned)p.tgroups + blockIdx.x % (unsigned)p.tgroups);
-  x.T = p.T;
+  auto run_head = [&](unsigned t, int& run, int& head) {
+    run = (int)(t / hpg);
+    head = (int)((t % hpg) * (unsigned)p.tgroups + blockIdx.x % (unsigned)p.tgroups);
+  };
   // Run 0 takes R0 tiles, the others Rb or Rb + 1 (the first Rx of them).
-  if (x.run == 0) {
-    x.tb = 0;
-    x.ntl = p.R0;
-  } else {
-    const int k = x.run - 1;
-    x.tb = p.R0 + k * p.Rb + min(k, p.Rx);
-    x.ntl = p.Rb + (k < p.Rx ? 1 : 0);
-  }
-  x.hoff = (size_t)x.head * p.T * RD;
-  x.last_run = x.run == p.nrun - 1;
-  KLA_STAMP(tid >> 8, 1);
+  auto run_start = [&](int run) { return run == 0 ? 0 : p.R0 + (run - 1) * p.Rb + min(run - 1, p.Rx); };
+  // The run context, once the ticket is out (after the barrier each role takes).
+  auto context = [&]() {
+    RunCtx x;
+    const unsigned ticket = s.ctl[cTicket];
+    const unsigned epoch = s.ctl[cEpoch];
+    x.tid = tid;
+    x.lane = tid & 63;
+    x.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    x.FAGG = 2u * epoch + 2u;
+    x.FINC = 2u * epoch + 3u;
+    x.nrun = p.nrun;
+    run_head(ticket, x.run, x.head);
+    x.T = p.T;
+    x.tb = run_start(x.run);
+    x.ntl = x.run == 0 ? p.R0 : p.Rb + (x.run - 1 < p.Rx ? 1 : 0);
+    x.hoff = (size_t)x.head * p.T * RD;
+    x.last_run = x.run == p.nrun - 1;
+    KLA_STAMP(tid >> 8, 1);
 #ifdef KLA_TIMELINE
-  if (tid == 0 && blockIdx.x < (unsigned)kTlGroups) {
-    kla_timeline_buf[(size_t)blockIdx.x * 2 * kTlSlots + 62] = (unsigned long long)x.run;
-    kla_timeline_buf[(size_t)blockIdx.x * 2 * kTlSlots + 63] = (unsigned long long)x.ntl;
-  }
+    if (tid == 0 && blockIdx.x < (unsigned)kTlGroups) {
+      kla_timeline_buf[(size_t)blockIdx.x * 2 * kTlSlots + 62] = (unsigned long long)x.run;
+      kla_timeline_buf[(size_t)blockIdx.x * 2 * kTlSlots + 63] = (unsigned long long)x.ntl;
+    }
 #endif
-  if (x.wave < 4)
-    walker_role(p, s, x);
-  else
-    matrix_role(p, s, x);
+    return x;
+  };
+  if (tid < 256) {
+    // The workgroups of a group mostly draw their tickets in index order, so
+    // the walkers start the first tile's loads for the run of ticket
+    // blockIdx / tgroups before their own ticket is known; a wrong guess
+    // costs only those loads (the tile is loaded again).
+    int g_run, g_head;
+    run_head(blockIdx.x / (unsigned)p.tgroups, g_run, g_head);
+    const size_t ghoff = (size_t)g_head * p.T * RD;
+    const int t0 = run_start(g_run) * RTL;
+    uint4 pf[10];
+#pragma unroll
+    for (int it = 0; it < 10; ++it) {
+      const int a = it >> 1, u = tid + 256 * (it & 1), row = u >> 3, xx = (u & 7) << 3;
+      const uint16_t* src = a == 0 ? p.q : a == 1 ? p.k : a == 2 ? p.ld : a == 3 ? p.pn : p.vp;
+      pf[it] = t0 + row < p.T ? *reinterpret_cast<const uint4*>(src + ghoff + (size_t)(t0 + row) * RD + xx)
+                              : make_uint4(0, 0, 0, 0);
+    }
+    // The ticket, drawn once those loads are on their way.
+    if (tid == 0) {
+      s.ctl[cTicket] =
+          draw_ticket(p.tick, (unsigned)p.tgroups, (unsigned)p.nheads / (unsigned)p.tgroups * (unsigned)p.nrun);
+      s.ctl[cEpoch] = p.nrun > 1 ? ld_relaxed(p.ctrl + kEpoch) : 0u;
+      s.ctl[cWSync] = 0u;
+      s.ctl[cXSync] = 0u;
+      s.ctl[cLamReady] = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s.ctl[cCorr + i] = 0u;
+    }
+    __syncthreads();  // the ticket is out
+    const RunCtx x = context();
+    walker_role(p, s, x, pf, x.head == g_head && x.run == g_run);
+  } else {
+    __syncthreads();  // the ticket is out
+    matrix_role(p, s, context());
+  }
   __syncthreads();
   // Count the workgroup done; the last one resets the counter and advances
   // the call epoch (the flags of the next call differ).
@@ -1124,7 +1149,7 @@ __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
     const unsigned ng = (unsigned)p.nheads * (unsigned)p.nrun;
     if (__hip_atomic_fetch_add(p.ctrl + kGroupsDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ng - 1) {
       st_relaxed(p.ctrl + kGroupsDone, 0u);
-      if (p.nrun > 1) st_relaxed(p.ctrl + kEpoch, epoch + 1u);
+      if (p.nrun > 1) st_relaxed(p.ctrl + kEpoch, s.ctl[cEpoch] + 1u);
     }
   }
 }
