@@ -598,11 +598,25 @@ __device__ __forceinline__ void walker_role(const FwdRunParams& p, RunSmem& s, c
   }
 }
 
+// The 16-byte units of tile wt's k, log_decay, proc_noise and val_prec that
+// matrix-wave thread tv (0..255) stages for the window walk: unit tv + 256
+// (it & 1) of array it / 2.  A full tile (it precedes a run), so no row check.
+__device__ __forceinline__ void window_tile_load(const FwdRunParams& p, size_t hoff, int wt, int tv, uint4 (&buf)[8]) {
+  const int t0 = wt * RTL;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int a = it >> 1, u = tv + 256 * (it & 1), row = u >> 3, xx = (u & 7) << 3;
+    const uint16_t* src = a == 0 ? p.k : a == 1 ? p.ld : a == 2 ? p.pn : p.vp;
+    buf[it] = *reinterpret_cast<const uint4*>(src + hoff + (size_t)(t0 + row) * RD + xx);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Matrix waves (4-7): wave 4 + c owns value columns 16c..16c+15; tile j-1
 // during step j; the mean carry at the end of the run.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, const RunCtx& x) {
+__device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, const RunCtx& x, uint4 (&wbuf)[8],
+                                            bool have_window) {
   const int lane = x.lane, c = x.wave - 4, T = x.T, tb = x.tb, ntl = x.ntl, run = x.run, head = x.head;
   const int nrun = x.nrun;
   const size_t hoff = x.hoff;
@@ -796,23 +810,25 @@ __device__ __forceinline__ void matrix_role(const FwdRunParams& p, RunSmem& s, c
   // the walkers stage and compose tile 0; the window tiles go to the first
   // two Q slots, which the walkers first write after reading the result.
   unsigned char* const stage = &s.qop[0][0][0][0];
-  auto stage_tile = [&](int wt) {
-    const int t0 = wt * RTL;
-    uint4 buf[8];
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int a = it >> 1, u = tv + 256 * (it & 1), row = u >> 3, xx = (u & 7) << 3;
-      const uint16_t* src = a == 0 ? p.k : a == 1 ? p.ld : a == 2 ? p.pn : p.vp;
-      buf[it] = *reinterpret_cast<const uint4*>(src + hoff + (size_t)(t0 + row) * RD + xx);
-    }
+  auto put_tile = [&](const uint4 (&buf)[8]) {
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int a = it >> 1, u = tv + 256 * (it & 1), row = u >> 3, xx = (u & 7) << 3;
       *reinterpret_cast<uint4*>(stage + a * RTL * RD * 2 + raw_off(row, xx)) = buf[it];
     }
   };
+  auto stage_tile = [&](int wt) {
+    uint4 buf[8];
+    window_tile_load(p, hoff, wt, tv, buf);
+    put_tile(buf);
+  };
   unsigned msync = 0;
-  if (run > 0) stage_tile(tb - 1);  // a full tile: it precedes the run
+  if (run > 0) {  // a full tile: it precedes the run
+    if (have_window)
+      put_tile(wbuf);  // loaded before the ticket, for the run guessed right
+    else
+      stage_tile(tb - 1);
+  }
   __syncthreads();
   if (run > 0) {
     WLane L;
@@ -1139,8 +1155,20 @@ __global__ __launch_bounds__(RNT, 2) void kla_fwd_run_kernel(FwdRunParams p) {
     const RunCtx x = context();
     walker_role(p, s, x, pf, x.head == g_head && x.run == g_run);
   } else {
+    // Likewise the matrix waves load the guessed run's window tile (the tile
+    // before the run) for the walk to the run's entering precision.
+    int g_run, g_head;
+    run_head(blockIdx.x / (unsigned)p.tgroups, g_run, g_head);
+    uint4 wbuf[8];
+    if (g_run > 0) {
+      window_tile_load(p, (size_t)g_head * p.T * RD, run_start(g_run) - 1, tid - 256, wbuf);
+    } else {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) wbuf[it] = make_uint4(0, 0, 0, 0);
+    }
     __syncthreads();  // the ticket is out
-    matrix_role(p, s, context());
+    const RunCtx x = context();
+    matrix_role(p, s, x, wbuf, g_run > 0 && x.head == g_head && x.run == g_run);
   }
   __syncthreads();
   // Count the workgroup done; the last one resets the counter and advances
