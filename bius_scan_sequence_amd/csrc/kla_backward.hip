@@ -634,6 +634,50 @@ __device__ __forceinline__ void chunk_operands(BwdChunkSmem<K, V, BF16>& s, int 
   }
 }
 
+// M_c^T tiles of key wave kb (block kb of the key channels) for chunk w: the
+// segment state decayed to the chunk start plus the tokens before the chunk
+// (v^T al over t < 16 w).  Reads only the staged rows.
+template <int K, int V, bool BF16>
+__device__ __forceinline__ void mean_tiles(const BwdChunkSmem<K, V, BF16>& s, int w, int kb_w, int lg, int lr,
+                                           const v4f (&Ms)[V / 16], v4f (&Mt)[V / 16]) {
+  constexpr int KP = kRowP<K>, VP = VRow<V, BF16>::P, C = kC, VB = V / 16;
+  const int i = kb_w * 16 + lr;
+  float lP = 0.f;
+  for (int c3 = 0; c3 < w; ++c3) lP += s.T[c3 * K + i];
+  const float Pi = ex2(lP);
+#pragma unroll
+  for (int jb = 0; jb < VB; ++jb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Mt[jb][e] = Pi * Ms[jb][e];
+  // Tokens t of an earlier chunk c2 enter with g_t prod_{u=t+1}^{c0-1} f_u
+  // = g_t exp2((T[c2] - lb_t) + sum of the chunk totals in between).
+  for (int c2 = 0; c2 < w; ++c2) {
+    float off = s.T[c2 * K + i];
+    for (int c3 = c2 + 1; c3 < w; ++c3) off += s.T[c3 * K + i];
+    v4f b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = c2 * C + 4 * lg + e;
+      b[e] = s.g[t * KP + i] * ex2(off - s.lb[t * KP + i]);
+    }
+    // one 16-token block of this chunk: four k-groups of 4 (e), tiles jb interleaved
+    if constexpr (BF16) {
+      const Split3 bs = split3(b);
+#pragma unroll
+      for (int jb = 0; jb < VB; ++jb)
+        Mt[jb] = mma_ex(Mt[jb], bits4(&s.v[(c2 * C + 4 * lg) * VP + jb * 16 + lr], VP), bs);
+    } else {
+#pragma unroll
+      for (int jb = 0; jb < VB; ++jb) {
+        v4f a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = to_f32(s.v[(c2 * C + 4 * lg + e) * VP + jb * 16 + lr]);
+        Mt[jb] = mma_f32(Mt[jb], a, b);
+      }
+    }
+  }
+}
+
 template <int K, int V, bool BF16>
 __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams p) {
   constexpr int KP = kRowP<K>, K16 = kRow16P<K>, VP = VRow<V, BF16>::P, NT = kChunkThreads, C = kC, CP = kCP;
@@ -687,54 +731,23 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
     if (nb < nsb) seg_load<K, V, BF16, NT>(p, nb / p.nseg, (int)(nb % p.nseg) * kSL, nxt);
   }
 
-  // The last chunk's operands by the whole workgroup; inside the loop the
-  // key waves work on chunk w while waves 4..7, after their own share of it,
-  // form chunk w - 1's operands in the other buffer: one barrier per chunk.
+  // Inside the loop the key waves work on chunk w while waves 4..7, after
+  // their own share of it, form chunk w - 1's operands in the other buffer:
+  // one barrier per chunk.  Before it waves 4..7 form the last chunk's
+  // operands the same way while the key waves rebuild that chunk's mean tiles.
   const int wl = (nvalid - 1) / C;
-  chunk_operands<K, V, BF16>(s, wl, wl & 1, tid, NT, tid, wave, lg, lr);
+  if (wave >= 4) {
+    const int grp = wave == 6 ? -1 : wave == 7 ? tid - 320 : tid - 256;
+    chunk_operands<K, V, BF16>(s, wl, wl & 1, grp, NT - 320, tid - 256, wave, lg, lr);
+  } else if (kw) {
+    mean_tiles<K, V, BF16>(s, wl, kb_w, lg, lr, Ms, Mt);
+  }
   __syncthreads();
   for (int w = wl; w >= 0; --w) {
     const int c0 = w * C, cur = w & 1;
     const bool safe = s.unsafe[w] == 0;
-    // (b) M_c^T tiles: the segment state decayed to the chunk start plus the
-    // tokens before the chunk (v^T al over t < c0).
-    if (kw) {
-      const int i = kb_w * 16 + lr;
-      float lP = 0.f;
-      for (int c3 = 0; c3 < w; ++c3) lP += s.T[c3 * K + i];
-      const float Pi = ex2(lP);
-#pragma unroll
-      for (int jb = 0; jb < VB; ++jb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Mt[jb][e] = Pi * Ms[jb][e];
-      // Tokens t of an earlier chunk c2 enter with g_t prod_{u=t+1}^{c0-1} f_u
-      // = g_t exp2((T[c2] - lb_t) + sum of the chunk totals in between).
-      for (int c2 = 0; c2 < w; ++c2) {
-        float off = s.T[c2 * K + i];
-        for (int c3 = c2 + 1; c3 < w; ++c3) off += s.T[c3 * K + i];
-        v4f b;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = c2 * C + 4 * lg + e;
-          b[e] = s.g[t * KP + i] * ex2(off - s.lb[t * KP + i]);
-        }
-        // one 16-token block of this chunk: four k-groups of 4 (e), tiles jb interleaved
-        if constexpr (BF16) {
-          const Split3 bs = split3(b);
-#pragma unroll
-          for (int jb = 0; jb < VB; ++jb)
-            Mt[jb] = mma_ex(Mt[jb], bits4(&s.v[(c2 * C + 4 * lg) * VP + jb * 16 + lr], VP), bs);
-        } else {
-#pragma unroll
-          for (int jb = 0; jb < VB; ++jb) {
-            v4f a;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) a[e] = to_f32(s.v[(c2 * C + 4 * lg + e) * VP + jb * 16 + lr]);
-            Mt[jb] = mma_f32(Mt[jb], a, b);
-          }
-        }
-      }
-    }
+    // (b) M_c^T tiles (for the last chunk, formed before the loop).
+    if (kw && w != wl) mean_tiles<K, V, BF16>(s, w, kb_w, lg, lr, Ms, Mt);
     // (c) outputs.
     const size_t tok0 = hd * (size_t)p.T + t0 + c0;
     if (kw) {
