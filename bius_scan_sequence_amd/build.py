@@ -103,9 +103,10 @@ def build_host_sanitized(verbose: bool = False) -> str:
     return SAN_LIB
 
 
-# Timeline build: the run-streaming forward compiled with -DKLA_TIMELINE (per
-# workgroup real-time stamps, read by bius_scan_sequence_amd/timeline.py);
-# every other object is the ordinary one.
+# Timeline build: the run-streaming forward and the backward compiled with
+# -DKLA_TIMELINE (per workgroup real-time stamps and per wave phase sums of the
+# backward chunk kernel, read by bius_scan_sequence_amd/timeline.py); every
+# other object is the ordinary one.
 TL_DIR = os.path.join(BUILD, "timeline")
 TL_LIB = os.path.join(PKG, "libkla_timeline.so")
 
@@ -115,12 +116,16 @@ def build_timeline(verbose: bool = False) -> str:
     if not all(os.path.exists(os.path.join(BUILD, os.path.splitext(s)[0] + ".o")) for s in SOURCES):
         build()
     os.makedirs(TL_DIR, exist_ok=True)
-    obj = os.path.join(TL_DIR, "kla_forward_run_tl.o")
-    cmd = [hipcc(), *common_flags(), "-DKLA_TIMELINE", "-c", os.path.join(CSRC, "kla_forward_run.hip"), "-o", obj]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    objs = [obj] + [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "kla_forward_run.hip"]
+    traced = ("kla_forward_run.hip", "kla_backward.hip")
+    objs = []
+    for src in traced:
+        obj = os.path.join(TL_DIR, os.path.splitext(src)[0] + "_tl.o")
+        cmd = [hipcc(), *common_flags(), "-DKLA_TIMELINE", "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        objs.append(obj)
+    objs += [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s not in traced]
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", TL_LIB, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -42,6 +42,49 @@
 
 namespace kla {
 
+#ifdef KLA_TIMELINE
+// Timeline build only (-DKLA_TIMELINE): every wave of the chunk kernel sums
+// the shader clock (s_memtime) spent in each phase of its work over all its
+// segments, and lane 0 writes the sums to kla_bwd_timeline_buf[workgroup]
+// [wave][phase] at the end.  Phases: 0 staging of a segment, 1 work before the
+// chunk loop, 2 barrier before the loop, 3 mean tiles, 4 outputs, 5 adjoint
+// update, 6 operands of the next chunk, 7 barrier after a chunk, 10 the
+// staging proper (seg_store), 11 the wait for the segment's loads (and the
+// stores before them), 12 the next segment's loads issued, 13 and 14 the key
+// waves' outputs split (Xs and Ys; the in-chunk parts); slot 8 counts
+// segments, slot 9 the wave's whole life in cycles.
+constexpr int kBtlPhases = 16, kBtlGroups = 4096;
+__device__ unsigned long long kla_bwd_timeline_buf[kBtlGroups * 8 * kBtlPhases];
+#define KLA_BTL_DECL                                 \
+  unsigned long long btl_acc[kBtlPhases] = {};       \
+  const unsigned long long btl_t0 = __builtin_amdgcn_s_memtime(); \
+  unsigned long long btl_t = btl_t0
+#define KLA_BTL(k)                                                \
+  do {                                                            \
+    const unsigned long long btl_n = __builtin_amdgcn_s_memtime(); \
+    btl_acc[k] += btl_n - btl_t;                                  \
+    btl_t = btl_n;                                                \
+  } while (0)
+#define KLA_BTL_END()                                                                          \
+  do {                                                                                         \
+    btl_acc[9] = __builtin_amdgcn_s_memtime() - btl_t0;                                        \
+    if ((threadIdx.x & 63) == 0 && blockIdx.x < (unsigned)kBtlGroups) _Pragma("unroll")         \
+      for (int btl_k = 0; btl_k < kBtlPhases; ++btl_k)                                         \
+        kla_bwd_timeline_buf[((size_t)blockIdx.x * 8 + (threadIdx.x >> 6)) * kBtlPhases + btl_k] = \
+            btl_acc[btl_k];                                                                    \
+  } while (0)
+#else
+#define KLA_BTL_DECL \
+  do {               \
+  } while (0)
+#define KLA_BTL(k) \
+  do {             \
+  } while (0)
+#define KLA_BTL_END() \
+  do {                \
+  } while (0)
+#endif
+
 namespace {
 constexpr int kSL = 64;  // tokens per segment
 constexpr int kC = 16;   // tokens per chunk
@@ -69,6 +112,19 @@ template <bool BF16>
 __device__ __forceinline__ void stout(void* p, size_t x, float v) {
   using In = typename std::conditional<BF16, uint16_t, float>::type;
   static_cast<In*>(p)[x] = from_f32<In>(v);
+}
+
+// Four consecutive elements x .. x+3 of a per-token output (x a multiple of
+// 4): one 8-byte store for bf16, one 16-byte store for fp32.
+template <bool BF16>
+__device__ __forceinline__ void stout4(void* p, size_t x, v4f v) {
+  if constexpr (BF16) {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + x) =
+        make_uint2((uint32_t)bf16_rne(v[0]) | ((uint32_t)bf16_rne(v[1]) << 16),
+                   (uint32_t)bf16_rne(v[2]) | ((uint32_t)bf16_rne(v[3]) << 16));
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(p) + x) = make_float4(v[0], v[1], v[2], v[3]);
+  }
 }
 
 // Four consecutive elements x .. x+3 of a per-token input (16-byte aligned
@@ -161,6 +217,9 @@ template <bool BF16> using Raw4 = typename std::conditional<BF16, uint2, float4>
 template <int K, int V, bool BF16, int NT>
 struct SegLoads {
   static constexpr int PK = (kSL * (K / 4) + NT - 1) / NT, PV = (kSL * (V / 4) + NT - 1) / NT;
+  // Load parts that can be issued separately: each pass of the key side, then
+  // the whole value side.
+  static constexpr int NPART = PK + 1;
   float4 lam[PK], lprev[PK];  // the precision path at the token and one token earlier
   Raw4<BF16> ld[PK], pn[PK], k[PK], vp[PK], q[PK];
   Raw4<BF16> v[PV], d[PV];
@@ -179,14 +238,21 @@ __device__ __forceinline__ float4 raw_f4(uint2 u) {
 }
 __device__ __forceinline__ float4 raw_f4(float4 f) { return f; }
 
-template <int K, int V, bool BF16, int NT>
-__device__ __forceinline__ void seg_load(const BwdParams& p, size_t hd, int t0, SegLoads<K, V, BF16, NT>& r) {
+// Part PART of a segment's loads (SegLoads::NPART parts: pass PART of the key
+// side, or for the last part the value side).
+template <int PART, int K, int V, bool BF16, int NT>
+__device__ __forceinline__ void seg_load_part(const BwdParams& p, size_t hd, int t0, SegLoads<K, V, BF16, NT>& r) {
   constexpr int K4 = K / 4, V4 = V / 4;
   using L = SegLoads<K, V, BF16, NT>;
   const Raw4<BF16> z{};
-#pragma unroll
-  for (int pk = 0; pk < L::PK; ++pk) {
-    const int x = threadIdx.x + pk * NT, t = x / K4, i = (x % K4) * 4;
+  // The thread index through an empty asm: the addresses are formed here,
+  // where the loads go out, not hoisted out of a loop that issues them and
+  // held in registers across it.
+  int tix = (int)threadIdx.x;
+  asm volatile("" : "+v"(tix));
+  if constexpr (PART < L::PK) {
+    constexpr int pk = PART;
+    const int x = tix + pk * NT, t = x / K4, i = (x % K4) * 4;
     r.lam[pk] = make_float4(0.f, 0.f, 0.f, 0.f);
     r.lprev[pk] = make_float4(1.f, 1.f, 1.f, 1.f);
     r.ld[pk] = r.pn[pk] = r.k[pk] = r.vp[pk] = r.q[pk] = z;
@@ -206,16 +272,28 @@ __device__ __forceinline__ void seg_load(const BwdParams& p, size_t hd, int t0, 
       r.vp[pk] = ldraw4<BF16>(p.vp, e);
       r.q[pk] = ldraw4<BF16>(p.q, e);
     }
-  }
+  } else {
 #pragma unroll
-  for (int pv = 0; pv < L::PV; ++pv) {
-    const int x = threadIdx.x + pv * NT, t = x / V4, j = (x % V4) * 4;
-    r.v[pv] = r.d[pv] = z;
-    if (x < kSL * V4 && t0 + t < p.T) {
-      const size_t y = (hd * p.T + t0 + t) * p.vs + j;
-      r.v[pv] = ldraw4<BF16>(p.v, y);
-      r.d[pv] = ldraw4<BF16>(p.dy, y);
+    for (int pv = 0; pv < L::PV; ++pv) {
+      const int x = tix + pv * NT, t = x / V4, j = (x % V4) * 4;
+      r.v[pv] = r.d[pv] = z;
+      if (x < kSL * V4 && t0 + t < p.T) {
+        const size_t y = (hd * p.T + t0 + t) * p.vs + j;
+        r.v[pv] = ldraw4<BF16>(p.v, y);
+        r.d[pv] = ldraw4<BF16>(p.dy, y);
+      }
     }
+  }
+}
+
+// Parts PART, PART + 1, ... of a segment's loads; with `only` >= 0 just part
+// `only` (a wave-uniform index; none if it is past the last part).
+template <int PART = 0, int K, int V, bool BF16, int NT>
+__device__ __forceinline__ void seg_load(const BwdParams& p, size_t hd, int t0, SegLoads<K, V, BF16, NT>& r,
+                                         int only = -1) {
+  if constexpr (PART < SegLoads<K, V, BF16, NT>::NPART) {
+    if (only < 0 || only == PART) seg_load_part<PART>(p, hd, t0, r);
+    seg_load<PART + 1>(p, hd, t0, r, only);
   }
 }
 
@@ -283,17 +361,24 @@ __device__ __forceinline__ void seg_store(const BwdParams& p, size_t hd, int t0,
   // One thread per (channel, chunk): cumulative log2 f inside the chunk.  A
   // chunk is marked in `unsafe` (when given) if a channel's log2 decay over
   // either half of it falls below -96.
+  // The chunk's 16 values are read before any is written back, so that the
+  // reads are in flight together.
   for (int x = threadIdx.x; x < 4 * K; x += NT) {
     const int c = x / K, i = x % K;
+    float r[kC];
+#pragma unroll
+    for (int l = 0; l < kC; ++l) r[l] = slb[(c * kC + l) * KP + i];
     float acc = 0.f, mid = 0.f;
 #pragma unroll
     for (int l = 0; l < kC; ++l) {
-      acc += slb[(c * kC + l) * KP + i];
-      slb[(c * kC + l) * KP + i] = acc;
+      acc += r[l];
+      r[l] = acc;
       if (l == 7) mid = acc;
     }
+#pragma unroll
+    for (int l = 0; l < kC; ++l) slb[(c * kC + l) * KP + i] = r[l];
     sT[c * K + i] = acc;
-    const float first = slb[c * kC * KP + i];
+    const float first = r[0];
     if (unsafe && (first - mid > 96.f || mid - acc > 96.f)) unsafe[c] = 1;  // benign race: all write 1
   }
   __syncthreads();
@@ -320,16 +405,16 @@ __global__ __launch_bounds__(512) void kla_bwd_segagg_kernel(BwdParams p) {
   const unsigned nsb = (unsigned)p.nheads * (unsigned)p.nseg;
   SegLoads<K, V, BF16, NT> nxt;
   if constexpr (PREFETCH)
-    if (blockIdx.x < nsb) seg_load<K, V, BF16, NT>(p, blockIdx.x / p.nseg, (int)(blockIdx.x % p.nseg) * kSL, nxt);
+    if (blockIdx.x < nsb) seg_load(p, blockIdx.x / p.nseg, (int)(blockIdx.x % p.nseg) * kSL, nxt);
   for (unsigned sg = blockIdx.x; sg < nsb; sg += gridDim.x) {
   const size_t hd = sg / p.nseg;
   const int s = (int)(sg % p.nseg);
   if (sg != blockIdx.x) __syncthreads();  // the previous segment's tiles are read
-  if constexpr (!PREFETCH) seg_load<K, V, BF16, NT>(p, hd, s * kSL, nxt);
+  if constexpr (!PREFETCH) seg_load(p, hd, s * kSL, nxt);
   seg_store<K, V, BF16, NT>(p, hd, s * kSL, nxt, sl, sa, sb, sv, sd, sT, static_cast<int*>(nullptr));
   if constexpr (PREFETCH) {
     const unsigned nb = sg + gridDim.x;
-    if (nb < nsb) seg_load<K, V, BF16, NT>(p, nb / p.nseg, (int)(nb % p.nseg) * kSL, nxt);
+    if (nb < nsb) seg_load(p, nb / p.nseg, (int)(nb % p.nseg) * kSL, nxt);
   }
   // alpha_t = g_t prod_{u>t} f_u (in place of g), beta_t = q_t prod_{u<=t} f_u
   // (in place of q), for t in chunk c: the products are exp2 of the chunk's
@@ -694,11 +779,16 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
   // each segment when it starts.
   constexpr bool PREFETCH = BF16;
   const unsigned nsb = (unsigned)p.nheads * (unsigned)p.nseg;
+  KLA_BTL_DECL;
   SegLoads<K, V, BF16, NT> nxt;
   if constexpr (PREFETCH)
     if (blockIdx.x < nsb)
-    seg_load<K, V, BF16, NT>(p, blockIdx.x / p.nseg, (int)(blockIdx.x % p.nseg) * kSL, nxt);
+    seg_load(p, blockIdx.x / p.nseg, (int)(blockIdx.x % p.nseg) * kSL, nxt);
   for (unsigned sb = blockIdx.x; sb < nsb; sb += gridDim.x) {
+  KLA_BTL(7);
+#ifdef KLA_TIMELINE
+  ++btl_acc[8];
+#endif
   const size_t hd = sb / p.nseg;
   const int seg = (int)(sb % p.nseg);
   const int t0 = seg * kSL;
@@ -717,19 +807,25 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
   v4f(&Ht)[HB] = Hx;
   if constexpr (PREFETCH) load_state<K, V>(Gg, Mg, vw, kw, kb_w, vb_w, lg, lr, Hx, Ms);
   if (tid < 4) s.unsafe[tid] = 0;
-  if constexpr (!PREFETCH) seg_load<K, V, BF16, NT>(p, hd, t0, nxt);
+  if constexpr (!PREFETCH) seg_load(p, hd, t0, nxt);
+  KLA_BTL(0);
   seg_store<K, V, BF16, NT>(p, hd, t0, nxt, s.lb, s.g, s.q, s.v, s.d, s.T, s.unsafe);
   if constexpr (!PREFETCH) load_state<K, V>(Gg, Mg, vw, kw, kb_w, vb_w, lg, lr, Hx, Ms);
+  KLA_BTL(10);
   // Every load of this segment has landed before the chunk loop starts.
   // Global stores share the load counter and it drains in order: a load
   // still pending inside the loop would make each chunk wait for the stores
   // of the chunk before it.
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
-  // The next segment's loads go out now; only the next staging waits for them.
-  if constexpr (PREFETCH) {
-    const unsigned nb = sb + gridDim.x;
-    if (nb < nsb) seg_load<K, V, BF16, NT>(p, nb / p.nseg, (int)(nb % p.nseg) * kSL, nxt);
-  }
+  KLA_BTL(11);
+  // The next segment's loads go out in parts, one at the start of each chunk
+  // (the rest after the last chunk), so that they queue behind the chunks'
+  // work rather than stall the waves all at once; only the next staging
+  // waits for them.
+  const unsigned nb = sb + gridDim.x;
+  const bool more = PREFETCH && nb < nsb;
+  const size_t nhd = nb / p.nseg;
+  const int nt0 = (int)(nb % p.nseg) * kSL;
 
   // Inside the loop the key waves work on chunk w while waves 4..7, after
   // their own share of it, form chunk w - 1's operands in the other buffer:
@@ -742,34 +838,44 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
   } else if (kw) {
     mean_tiles<K, V, BF16>(s, wl, kb_w, lg, lr, Ms, Mt);
   }
+  KLA_BTL(1);
   __syncthreads();
+  KLA_BTL(2);
   for (int w = wl; w >= 0; --w) {
     const int c0 = w * C, cur = w & 1;
     const bool safe = s.unsafe[w] == 0;
+    if (more) seg_load(p, nhd, nt0, nxt, wl - w);
+    KLA_BTL(12);
     // (b) M_c^T tiles (for the last chunk, formed before the loop).
     if (kw && w != wl) mean_tiles<K, V, BF16>(s, w, kb_w, lg, lr, Ms, Mt);
+    KLA_BTL(3);
     // (c) outputs.
     const size_t tok0 = hd * (size_t)p.T + t0 + c0;
     if (kw) {
       // Xs = dY M_c^T, Ys = V H^T; in-chunk parts dqi = E (tril(B) (g F)),
-      // dgi = F (tril(B)^T (q E)) for key block `wave`.
-      const int i = kb_w * 16 + lr;
+      // dgi = F (tril(B)^T (q E)) for key block `wave`, each formed transposed
+      // (the operands of every product swapped): lane (lg, lr) holds token lr
+      // of the chunk and channels i0 .. i0 + 3, so that its outputs go out as
+      // one vector store per array.
+      const int i = kb_w * 16 + lr, i0 = kb_w * 16 + 4 * lg;
       v4f xs = v4f{0.f, 0.f, 0.f, 0.f}, ys = xs, dqi = xs, dgi = xs;
       if constexpr (BF16) {
 #pragma unroll
         for (int jb = 0; jb < VB; ++jb) {
-          xs = mma_ex(xs, bits4(&s.d[(c0 + lr) * VP + jb * 16 + 4 * lg]), split3(Mt[jb]));
-          ys = mma_ex(ys, bits4(&s.v[(c0 + lr) * VP + jb * 16 + 4 * lg]), split3(Ht[jb]));
+          xs = mma_xe(xs, split3(Mt[jb]), bits4(&s.d[(c0 + lr) * VP + jb * 16 + 4 * lg]));
+          ys = mma_xe(ys, split3(Ht[jb]), bits4(&s.v[(c0 + lr) * VP + jb * 16 + 4 * lg]));
         }
       } else {
 #pragma unroll
         for (int jb = 0; jb < VB; ++jb) {
           const v4f a = row4(&s.d[(c0 + lr) * VP + jb * 16 + 4 * lg]);
           const v4f b = row4(&s.v[(c0 + lr) * VP + jb * 16 + 4 * lg]);
-          xs = mma_f32(xs, a, Mt[jb]);
-          ys = mma_f32(ys, b, Ht[jb]);
+          xs = mma_f32(xs, Mt[jb], a);
+          ys = mma_f32(ys, Ht[jb], b);
         }
       }
+      KLA_BTL(13);
+      const v4f lb = *reinterpret_cast<const v4f*>(&s.lb[(c0 + lr) * KP + i0]);
       if (safe) {
         v4f a, b, c, d;
 #pragma unroll
@@ -780,51 +886,59 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
           c[e] = s.B[cur][n * CP + lr];  // tril(B)^T[l = lr][n]
           d[e] = s.qE[cur][n * K16 + i];
         }
-        dqi = mma_f32(dqi, a, b);
-        dgi = mma_f32(dgi, c, d);
-        const float lb7 = s.lb[(c0 + 7) * KP + i];
+        dqi = mma_f32(dqi, b, a);
+        dgi = mma_f32(dgi, d, c);
+        const v4f lb7 = *reinterpret_cast<const v4f*>(&s.lb[(c0 + 7) * KP + i0]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float lb = s.lb[(c0 + 4 * lg + e) * KP + i];
-          dqi[e] *= ex2(lb - lb7);
-          dgi[e] *= ex2(lb7 - lb);
+          dqi[e] *= ex2(lb[e] - lb7[e]);
+          dgi[e] *= ex2(lb7[e] - lb[e]);
         }
       } else {
+        const int l = lr;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int l = 4 * lg + e;
-          const float lbl = s.lb[(c0 + l) * KP + i];
+          const int ic = i0 + e;
           float aq = 0.f, ag = 0.f;
           for (int m = 0; m < C; ++m) {
-            const float lbm = s.lb[(c0 + m) * KP + i];
-            if (m <= l) aq = fmaf(s.B[cur][l * CP + m] * s.g[(c0 + m) * KP + i], ex2(lbl - lbm), aq);
-            if (m >= l) ag = fmaf(s.B[cur][m * CP + l] * to_f32(s.q[(c0 + m) * KP + i]), ex2(lbm - lbl), ag);
+            const float lbm = s.lb[(c0 + m) * KP + ic];
+            if (m <= l) aq = fmaf(s.B[cur][l * CP + m] * s.g[(c0 + m) * KP + ic], ex2(lb[e] - lbm), aq);
+            if (m >= l) ag = fmaf(s.B[cur][m * CP + l] * to_f32(s.q[(c0 + m) * KP + ic]), ex2(lbm - lb[e]), ag);
           }
           dqi[e] = aq;
           dgi[e] = ag;
         }
       }
+      KLA_BTL(14);
+      if (c0 + lr < nvalid) {
+        const v4f tot = *reinterpret_cast<const v4f*>(&s.T[w * K + i0]);
+        const v4f gl = *reinterpret_cast<const v4f*>(&s.g[(c0 + lr) * KP + i0]);
+        v4f ql;
+        if constexpr (BF16)
+          ql = row4(&s.q[(c0 + lr) * KP + i0]);
+        else
+          ql = *reinterpret_cast<const v4f*>(&s.q[(c0 + lr) * KP + i0]);
+        v4f dq, dg, ee;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int l = 4 * lg + e;
-        if (c0 + l >= nvalid) continue;
-        const float lb = s.lb[(c0 + l) * KP + i];
-        const float dq = fmaf(ex2(lb), xs[e], dqi[e]);
-        const float dg = fmaf(ex2(s.T[w * K + i] - lb), ys[e], dgi[e]);
-        const size_t ow = (tok0 + l) * p.kws + i;
-        const float ee = to_f32(s.q[(c0 + l) * KP + i]) * dq - s.g[(c0 + l) * KP + i] * dg;
-        if (p.dq_acc) {
-          p.dq_acc[ow] = dq;
-        } else {
-          stout<BF16>(p.dq, (tok0 + l) * p.ks + i, dq);
+        for (int e = 0; e < 4; ++e) {
+          dq[e] = fmaf(ex2(lb[e]), xs[e], dqi[e]);
+          dg[e] = fmaf(ex2(tot[e] - lb[e]), ys[e], dgi[e]);
+          ee[e] = ql[e] * dq[e] - gl[e] * dg[e];
         }
-        p.dgw[ow] = dg;
-        p.ew[ow] = ee;
+        const size_t ow = (tok0 + lr) * p.kws + i0;
+        if (p.dq_acc)
+          *reinterpret_cast<float4*>(p.dq_acc + ow) = make_float4(dq[0], dq[1], dq[2], dq[3]);
+        else
+          stout4<BF16>(p.dq, (tok0 + lr) * p.ks + i0, dq);
+        *reinterpret_cast<float4*>(p.dgw + ow) = make_float4(dg[0], dg[1], dg[2], dg[3]);
+        *reinterpret_cast<float4*>(p.ew + ow) = make_float4(ee[0], ee[1], ee[2], ee[3]);
       }
     }
     if (vw) {
-      // dv = Kd H + tril(A)^T dY for value block `wave - 4`, Kd = g sx.
-      const int j = vb_w * 16 + lr;
+      // dv = Kd H + tril(A)^T dY for value block `wave - 4`, Kd = g sx, formed
+      // transposed like the key side: lane (lg, lr) holds token lr and value
+      // columns j0 .. j0 + 3.
+      const int j = vb_w * 16 + lr, j0 = vb_w * 16 + 4 * lg;
       v4f dv = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ib = 0; ib < KB; ++ib) {
@@ -834,35 +948,31 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
           const int i = ib * 16 + 4 * lg + e;
           a[e] = s.kd[cur][lr * K16 + i];
         }
-        dv = mma_f32(dv, a, Hc[ib]);
+        dv = mma_f32(dv, Hc[ib], a);
       }
       {
         v4f a, b;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a[e] = s.A[cur][(4 * lg + e) * CP + lr];  // tril(A)^T[m = lr][l]
+          a[e] = s.A[cur][(4 * lg + e) * CP + lr];  // tril(A)[l][m = lr]
           if constexpr (!BF16) b[e] = to_f32(s.d[(c0 + 4 * lg + e) * VP + j]);
         }
         if constexpr (BF16) {
           // its own accumulator: no matrix-core instruction of one shape reads
           // an accumulator that one of the other shape has just written
-          dv += mma_xe(v4f{0.f, 0.f, 0.f, 0.f}, split3(a), bits4(&s.d[(c0 + 4 * lg) * VP + j], VP));
+          dv += mma_ex(v4f{0.f, 0.f, 0.f, 0.f}, bits4(&s.d[(c0 + 4 * lg) * VP + j], VP), split3(a));
         } else {
-          dv = mma_f32(dv, a, b);
+          dv = mma_f32(dv, b, a);
         }
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = 4 * lg + e;
-        if (c0 + m >= nvalid) continue;
-        if (p.dv_acc) {
-          const size_t oa = (tok0 + m) * p.vacc + j;
-          p.dv_acc[oa] = dv[e];
-        } else {
-          stout<BF16>(p.dv, (tok0 + m) * p.vs + j, dv[e]);
-        }
+      if (c0 + lr < nvalid) {
+        if (p.dv_acc)
+          *reinterpret_cast<float4*>(p.dv_acc + (tok0 + lr) * p.vacc + j0) = make_float4(dv[0], dv[1], dv[2], dv[3]);
+        else
+          stout4<BF16>(p.dv, (tok0 + lr) * p.vs + j0, dv);
       }
     }
+    KLA_BTL(4);
     // (d) adjoint at the end of the previous chunk: diag(cp_end) H + (cp q)^T dY,
     // in both orientations (registers of this wave; LDS operands of this chunk).
     if (w > 0) {
@@ -913,14 +1023,20 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
         }
       }
     }
+    KLA_BTL(5);
     // Wave 6 forms the score tile A and takes no share of the rows.
     if (wave >= 4 && w > 0) {
       const int grp = wave == 6 ? -1 : wave == 7 ? tid - 320 : tid - 256;
       chunk_operands<K, V, BF16>(s, w - 1, (w - 1) & 1, grp, NT - 320, tid - 256, wave, lg, lr);
     }
+    KLA_BTL(6);
     __syncthreads();
   }
+  if (more)
+    for (int pt = wl + 1; pt < SegLoads<K, V, BF16, NT>::NPART; ++pt) seg_load(p, nhd, nt0, nxt, pt);
   }  // segments
+  KLA_BTL(7);
+  KLA_BTL_END();
 }
 
 // ---------------------------------------------------------------------------
@@ -1160,3 +1276,11 @@ hipError_t launch_backward_empty(const float* dlamT, const float* dMT, float* dl
 }
 
 }  // namespace kla
+
+#ifdef KLA_TIMELINE
+extern "C" int kla_bwd_timeline_read(void* host, size_t bytes) {
+  const size_t n = sizeof(kla::kla_bwd_timeline_buf);
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(kla::kla_bwd_timeline_buf), bytes < n ? bytes : n, 0,
+                                  hipMemcpyDeviceToHost);
+}
+#endif

@@ -1,7 +1,9 @@
-"""Per-phase timeline of the run-streaming forward (kla_fwd_run_kernel).
+"""Per-phase timeline of the run-streaming forward (kla_fwd_run_kernel) and of
+the backward chunk kernel (kla_bwd_chunk_kernel).
 
     python3 bius_scan_sequence_amd/build.py --timeline
     python3 bius_scan_sequence_amd/timeline.py [--config lm45m_bf16] [--calls 5]
+    python3 bius_scan_sequence_amd/timeline.py --backward [--config bwd_lm45m_bf16]
 
 The timeline build (libkla_timeline.so) compiles the run kernel with
 -DKLA_TIMELINE: the first lane of wave 0 (a walker) and of wave 4 (a matrix
@@ -162,13 +164,87 @@ def run(config: str = "lm45m_bf16", calls: int = 5, lib_path: str = TL_LIB) -> s
     return "\n".join(out)
 
 
+BWD_PHASES = ("segment start: state loads issued", "work before the chunk loop",
+              "barrier before the chunk loop", "mean tiles M_c^T", "outputs (dq, dg, e / dv)",
+              "adjoint update", "operands of the next chunk", "barrier after a chunk")
+
+
+def run_backward(config: str = "bwd_lm45m_bf16", calls: int = 3, lib_path: str = TL_LIB) -> str:
+    """Per-wave phase sums of kla_bwd_chunk_kernel (the timeline build's s_memtime
+    accumulators), averaged over the workgroups of the recorded call's last
+    chunk-kernel launch, in us at the measured shader clock."""
+    import time
+
+    if not os.path.exists(lib_path):
+        raise RuntimeError(f"{lib_path} missing: build it with bius_scan_sequence_amd/build.py --timeline")
+    os.environ["BIUS_KLA_LIB"] = lib_path
+    import torch
+    sys.path.insert(0, os.path.dirname(PKG))
+    import bius_scan_sequence_amd as K
+    import kla_inputs as KI
+
+    lib = K.lib
+    lib.kla_bwd_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.kla_bwd_timeline_read.restype = ctypes.c_int
+    w = KI.workload(config)
+    dev = torch.device("cuda", 0)
+    x = KI.make_forward_inputs_torch(w, device=dev)
+    gy = KI.make_backward_grads_torch(w, device=dev)
+    lpath = K.forward(*(x[n] for n in NAMES), x["lambda0"], x["M0"], return_lambda_path=True)[3]
+    ws = K.Workspace(dev)
+
+    def call():
+        return K.backward(*(x[n] for n in NAMES), gy, lpath, x["lambda0"], x["M0"], workspace=ws)
+
+    for _ in range(calls):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    P, G = 16, 4096
+    buf = np.zeros(G * 8 * P, dtype=np.uint64)
+    assert lib.kla_bwd_timeline_read(buf.ctypes.data, buf.nbytes) == 0
+    S = buf.reshape(G, 8, P).astype(np.float64)
+    used = S[:, 0, 8] > 0
+    S = S[used]
+    life = S[:, :, 9]
+    # The shader clock: s_memtime counts it; 2.4 GHz is the nominal rate.
+    ghz = 2.4
+    out = []
+    p = out.append
+    p(f"kla_bwd_chunk_kernel phases: {config} (B{w.B} H{w.H} T{w.T} d_k {w.dk} d_v {w.dv} {w.dtype}), "
+      f"{int(used.sum())} workgroups, {S[:, 0, 8].mean():.1f} segments each (last launch of the call)")
+    p(f"per-wave sums averaged over workgroups, us at {ghz} GHz; the stamps add a little time "
+      f"(whole call {wall * 1e3:.2f} ms wall)")
+    p("")
+    p("| phase | " + " | ".join(f"wave {v}" for v in range(8)) + " |")
+    p("|---|" + "---|" * 8)
+    rows = [(0, BWD_PHASES[0]), (10, "staging: gates, cumulative decays, LDS writes (two barriers)"),
+            (11, "staging: wait for the state loads and earlier stores"),
+            (12, "next segment's input loads issued")] + \
+        [(k, BWD_PHASES[k]) for k in range(1, 4)] + \
+        [(13, "outputs, key waves: Xs = dY M_c^T, Ys = V H^T"), (14, "outputs, key waves: in-chunk dq, dg parts"),
+         (4, BWD_PHASES[4] + " (key waves: the stores)")] + \
+        [(k, BWD_PHASES[k]) for k in range(5, len(BWD_PHASES))]
+    for k, n in rows:
+        p(f"| {n} | " + " | ".join(f"{S[:, v, k].mean() / ghz / 1e3:.2f}" for v in range(8)) + " |")
+    p("| **life of the wave** | " + " | ".join(f"**{life[:, v].mean() / ghz / 1e3:.2f}**" for v in range(8)) + " |")
+    return "\n".join(out)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--config", default="lm45m_bf16")
+    ap.add_argument("--config", default=None)
     ap.add_argument("--calls", type=int, default=5, help="calls before the recorded one")
     ap.add_argument("--lib", default=TL_LIB, help="another timeline build of the library")
+    ap.add_argument("--backward", action="store_true", help="the backward chunk kernel's phases")
     a = ap.parse_args()
-    print(run(a.config, a.calls, a.lib), flush=True)
+    if a.backward:
+        print(run_backward(a.config or "bwd_lm45m_bf16", a.calls, a.lib), flush=True)
+    else:
+        print(run(a.config or "lm45m_bf16", a.calls, a.lib), flush=True)
     return 0
 
 
