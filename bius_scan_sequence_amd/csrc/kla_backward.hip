@@ -46,13 +46,15 @@ namespace kla {
 // Timeline build only (-DKLA_TIMELINE): every wave of the chunk kernel sums
 // the shader clock (s_memtime) spent in each phase of its work over all its
 // segments, and lane 0 writes the sums to kla_bwd_timeline_buf[workgroup]
-// [wave][phase] at the end.  Phases: 0 staging of a segment, 1 work before the
-// chunk loop, 2 barrier before the loop, 3 mean tiles, 4 outputs, 5 adjoint
-// update, 6 operands of the next chunk, 7 barrier after a chunk, 10 the
-// staging proper (seg_store), 11 the wait for the segment's loads (and the
-// stores before them), 12 the next segment's loads issued, 13 and 14 the key
-// waves' outputs split (Xs and Ys; the in-chunk parts); slot 8 counts
-// segments, slot 9 the wave's whole life in cycles.
+// [wave][phase] at the end.  Phases: 0 state loads issued at a segment's
+// start, 10 the staging proper (seg_store), 11 the wait for the segment's loads
+// (and the stores before them), 12 the next segment's loads issued (a share
+// per chunk), 1 work before the chunk loop, 2 barrier before the loop; per
+// chunk: 15 the barrier after the chunk before (and a flag read), 3 mean
+// tiles, 13 and 14 the key waves' Xs / Ys and in-chunk parts of the outputs,
+// 4 the rest of the outputs, 5 adjoint update, 6 operands of the next chunk;
+// 7 the barrier after a segment's last chunk.  Slot 8 counts segments, slot 9
+// holds the wave's whole life in cycles.
 constexpr int kBtlPhases = 16, kBtlGroups = 4096;
 __device__ unsigned long long kla_bwd_timeline_buf[kBtlGroups * 8 * kBtlPhases];
 #define KLA_BTL_DECL                                 \
@@ -844,6 +846,7 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
   for (int w = wl; w >= 0; --w) {
     const int c0 = w * C, cur = w & 1;
     const bool safe = s.unsafe[w] == 0;
+    KLA_BTL(15);
     if (more) seg_load(p, nhd, nt0, nxt, wl - w);
     KLA_BTL(12);
     // (b) M_c^T tiles (for the last chunk, formed before the loop).

@@ -166,7 +166,7 @@ def run(config: str = "lm45m_bf16", calls: int = 5, lib_path: str = TL_LIB) -> s
 
 BWD_PHASES = ("segment start: state loads issued", "work before the chunk loop",
               "barrier before the chunk loop", "mean tiles M_c^T", "outputs (dq, dg, e / dv)",
-              "adjoint update", "operands of the next chunk", "barrier after a chunk")
+              "adjoint update", "operands of the next chunk", "barrier after the last chunk of a segment")
 
 
 def run_backward(config: str = "bwd_lm45m_bf16", calls: int = 3, lib_path: str = TL_LIB) -> str:
@@ -223,8 +223,9 @@ def run_backward(config: str = "bwd_lm45m_bf16", calls: int = 3, lib_path: str =
     p("|---|" + "---|" * 8)
     rows = [(0, BWD_PHASES[0]), (10, "staging: gates, cumulative decays, LDS writes (two barriers)"),
             (11, "staging: wait for the state loads and earlier stores"),
-            (12, "next segment's input loads issued")] + \
-        [(k, BWD_PHASES[k]) for k in range(1, 4)] + \
+            (12, "next segment's input loads issued (a share per chunk)")] + \
+        [(k, BWD_PHASES[k]) for k in range(1, 3)] + [(15, "barrier after the chunk before (and a flag read)")] + \
+        [(3, BWD_PHASES[3])] + \
         [(13, "outputs, key waves: Xs = dY M_c^T, Ys = V H^T"), (14, "outputs, key waves: in-chunk dq, dg parts"),
          (4, BWD_PHASES[4] + " (key waves: the stores)")] + \
         [(k, BWD_PHASES[k]) for k in range(5, len(BWD_PHASES))]
