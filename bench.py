@@ -119,9 +119,18 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def summarize_traffic(fetch_dir, write_dir, out_path=TRAFFIC_FILE):
+# Measured traffic of another workload's forward kernel (`--traffic-config`):
+# the kernel's name, the summary file and the workload's algorithmic bytes.
+TRAFFIC_CONFIGS = {
+    "long_bf16": ("kla_fwd_kernel<128, 128, true", os.path.join(ROOT, "profiles", "kla_fwd_long_bf16_traffic.json"),
+                  "long_bf16 (B2 H16 T16384 d128, bf16)", (2, 16, 16384, 128, 128, 2)),
+}
+
+
+def summarize_traffic(fetch_dir, write_dir, config=None):
     """Write the measured-traffic summary from two rocprofv3 counter runs of
-    `bench.py --copy-mb 256` (one with FETCH_SIZE, one with WRITE_SIZE).
+    `bench.py --copy-mb 256` (one with FETCH_SIZE, one with WRITE_SIZE), or, for
+    `config`, of `bench.py --configs <config> --copy-mb 256`.
 
     The counters are read per dispatch in KiB.  Each is scaled by what it reads
     for a kernel of known traffic in the same run: the float32 -> bfloat16 cast
@@ -137,12 +146,20 @@ def summarize_traffic(fetch_dir, write_dir, out_path=TRAFFIC_FILE):
         for r in rows:
             key = (r["Kernel_Name"], r["Dispatch_Id"])
             tot[key] = tot.get(key, 0.0) + float(r["Counter_Value"])
-        fwd = [v for (k, _), v in tot.items() if KERNEL in k]
-        ref = [v for (k, _), v in tot.items() if "bfloat16_copy_kernel" in k]
+        fwd = [v for (k, _), v in tot.items() if kernel in k]
+        ref = [v for (k, _), v in sorted(tot.items(), key=lambda kv: int(kv[0][1])) if "bfloat16_copy_kernel" in k]
+        if config is not None:  # the run's last five casts: the reference (the inputs' own casts come first)
+            ref = ref[-5:]
         if not fwd or not ref:
             raise SystemExit(f"no {counter} rows for the forward kernel or the reference cast in {d}")
         return sum(fwd) / len(fwd), len(fwd), sum(ref) / len(ref)
 
+    if config is None:
+        kernel, out_path, label, shape = KERNEL, TRAFFIC_FILE, "lm45m_bf16 (B8 H8 T2048 d64, bf16)", (8, 8, 2048, 64, 64, 2)
+        runs = ("python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline --copy-mb 256", "")
+    else:
+        kernel, out_path, label, shape = TRAFFIC_CONFIGS[config]
+        runs = (f"python3 bench.py --configs {config} --no-cpu-baseline --copy-mb 256", f" --traffic-config {config}")
     fetch, n, ref_fetch = per_kernel(fetch_dir, "FETCH_SIZE")
     write, _, ref_write = per_kernel(write_dir, "WRITE_SIZE")
     fetch_scale = 33554432 / 1024 / ref_fetch
@@ -150,22 +167,23 @@ def summarize_traffic(fetch_dir, write_dir, out_path=TRAFFIC_FILE):
     rd = fetch * 1024 * fetch_scale
     wr = write * 1024 * write_scale
     out = {
-        "kernel": KERNEL, "workload": "lm45m_bf16 (B8 H8 T2048 d64, bf16)", "source_sha256": kernel_source_hash(),
+        "kernel": kernel, "workload": label,
         "fetch_size_kib_per_launch": fetch, "write_size_kib_per_launch": write, "launches": n,
         "reference_kernel": "torch float32->bfloat16 cast of one [8,8,2048,64] tensor "
                             "(33554432 B read, 16777216 B written per launch)",
         "reference_fetch_kib": ref_fetch, "reference_write_kib": ref_write,
         "fetch_scale": fetch_scale, "write_scale": write_scale,
         "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr, "hbm_bytes_per_launch": rd + wr,
-        "algorithmic_bytes_per_launch": algorithmic_bytes(8, 8, 2048, 64, 64, 2),
+        "algorithmic_bytes_per_launch": algorithmic_bytes(*shape),
         "commands": [
-            "rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/fetch -o bench -- python3 bench.py --steps 10 --warmup 2 "
-            "--no-cpu-baseline --copy-mb 256",
-            "rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/write -o bench -- python3 bench.py --steps 10 --warmup 2 "
-            "--no-cpu-baseline --copy-mb 256",
-            "python3 bench.py --traffic-from <out>/fetch <out>/write",
+            f"rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/fetch -o bench -- {runs[0]}",
+            f"rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/write -o bench -- {runs[0]}",
+            f"python3 bench.py --traffic-from <out>/fetch <out>/write{runs[1]}",
         ],
     }
+    if config is None:  # the bench line uses it only while the kernel's sources are unchanged
+        out["source_sha256"] = kernel_source_hash()
+    out["traffic_ratio"] = out["hbm_bytes_per_launch"] / out["algorithmic_bytes_per_launch"]
     with open(out_path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps({k: out[k] for k in ("hbm_read_bytes_per_launch", "hbm_write_bytes_per_launch",
@@ -286,7 +304,7 @@ def backward_algorithmic_bytes(B, H, T, dk, dv, esz):
     return B * H * T * per_token + state
 
 
-def run_configs(only, copies):
+def run_configs(only, copies, copy_mb=0):
     """Kernel time of each workload at its full shape, one JSON line per
     workload: forward workloads as 5 warm-up and 20 timed calls over rotating
     device-side input copies, the precision-only scan as 1 warm-up and 3
@@ -487,6 +505,13 @@ def run_configs(only, copies):
                           "frac_of_8TBps": abytes / mean_s / 8e12}), flush=True)
         x = xs = outs = out = run = None
         torch.cuda.empty_cache()
+    if copy_mb:
+        # The reference of known traffic for hardware-counter runs: five
+        # float32 -> bfloat16 casts of one [8,8,2048,64] tensor.
+        src = torch.ones((8, 8, 2048, 64), dtype=torch.float32, device=dev)
+        for _ in range(5):
+            src.to(torch.bfloat16)
+        torch.cuda.synchronize()
 
 
 def main():
@@ -501,12 +526,14 @@ def main():
                          "traffic for hardware counter runs)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the measured-traffic summary from two rocprofv3 counter runs and exit")
+    ap.add_argument("--traffic-config", choices=sorted(TRAFFIC_CONFIGS),
+                    help="with --traffic-from: the counter runs were of `--configs NAME --copy-mb 256`")
     ap.add_argument("--configs", nargs="*", metavar="NAME",
                     help=f"instead of the headline line, time every workload at its full shape (or the named "
                          f"ones of {', '.join(CONFIGS)}), one JSON line each")
     args = ap.parse_args()
     if args.traffic_from:
-        summarize_traffic(*args.traffic_from)
+        summarize_traffic(*args.traffic_from, config=args.traffic_config)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -514,7 +541,7 @@ def main():
         sys.exit(2)
 
     if args.configs is not None:
-        run_configs(set(args.configs), args.copies)
+        run_configs(set(args.configs), args.copies, args.copy_mb)
         return
 
     import numpy as np
