@@ -14,7 +14,7 @@ graph and replayed (wall clock and one event pair around the replay).
 Prints one JSON line:
   value      tokens/s (B*H*T per step / wall time per step of the graph-launched
              K steps; `launch` reports the eager loop's figure beside it)
-  roofline   dominant kernel (kla_fwd_kernel<64,64,bf16>): algorithmic bytes
+  roofline   dominant kernel (kla_fwd_run_kernel, the run-streaming forward): algorithmic bytes
              per launch / mean launch duration (HIP events on the launch
              stream around the replayed K launches), against the 8 TB/s HBM
              peak, with a measured device-copy bandwidth as second
