@@ -643,18 +643,18 @@ struct alignas(16) BwdChunkSmem {
 };
 
 // Operands of chunk w (tokens 16 w ..) into buffer `buf`: the decayed rows
-// qE, gF, kd, be and the chunk's decay per channel by threads grp, grp + gsize,
-// ... of a group of gsize threads (none if grp < 0) (E = prod f from the
-// chunk's token 7 to l, F its inverse, cp = prod f from the chunk start,
-// sx = prod f to the chunk end, all exp2 of short sums), and the two 16 x 16
-// score tiles: B by wave 7, A by wave 6 from the same products (or, on the
-// exact path, one (l, m) pair per thread xp < 256 of the workgroup).
+// qE, gF, kd, be and the chunk's decay per channel, elements x = grp, grp +
+// gsize, ... below xend (none if grp < 0) (E = prod f from the chunk's token 7
+// to l, F its inverse, cp = prod f from the chunk start, sx = prod f to the
+// chunk end, all exp2 of short sums); the score tile B when do_b; the score
+// tile A by wave 6 from the same products (or, on the exact path, one (l, m)
+// pair per thread xp < 256 of the workgroup).
 template <int K, int V, bool BF16>
-__device__ __forceinline__ void chunk_operands(BwdChunkSmem<K, V, BF16>& s, int w, int buf, int grp, int gsize, int xp,
-                                               int wave, int lg, int lr) {
+__device__ __forceinline__ void chunk_operands(BwdChunkSmem<K, V, BF16>& s, int w, int buf, int grp, int xend,
+                                               int gsize, bool do_b, int xp, int wave, int lg, int lr) {
   constexpr int KP = kRowP<K>, K16 = kRow16P<K>, VP = VRow<V, BF16>::P, C = kC, CP = kCP, VB = V / 16;
   const int c0 = w * C;
-  for (int x = grp; grp >= 0 && x < C * K; x += gsize) {
+  for (int x = grp; grp >= 0 && x < xend; x += gsize) {
     const int l = x / K, i = x % K;
     const float lb = s.lb[(c0 + l) * KP + i], lb7 = s.lb[(c0 + 7) * KP + i];
     const float tot = s.T[w * K + i];
@@ -666,7 +666,7 @@ __device__ __forceinline__ void chunk_operands(BwdChunkSmem<K, V, BF16>& s, int 
     s.be[buf][l * K16 + i] = q * cp;
     if (l == C - 1) s.cdec[buf][i] = cp;  // exp2 of the chunk's last cumulative value: its total
   }
-  if (wave == 7) {
+  if (do_b) {
     // B[l][m] = dy_l . v_m (one tile, V/16 blocks; bf16 inputs: exact
     // products, two blocks per instruction).
     v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
@@ -829,16 +829,20 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
   const size_t nhd = nb / p.nseg;
   const int nt0 = (int)(nb % p.nseg) * kSL;
 
-  // Inside the loop the key waves work on chunk w while waves 4..7, after
-  // their own share of it, form chunk w - 1's operands in the other buffer:
-  // one barrier per chunk.  Before it waves 4..7 form the last chunk's
-  // operands the same way while the key waves rebuild that chunk's mean tiles.
+  // Inside the loop every wave works on chunk w and then forms its share of
+  // chunk w - 1's operands in the other buffer: one barrier per chunk.  The
+  // rows go to waves 4, 5 and 7 in whole passes of 192 elements, the rest
+  // (and the score tile B) to waves 0..3, which wait at the barriers longer;
+  // wave 6 forms the score tile A.  Before the loop the waves form the last
+  // chunk's operands the same way while the key waves rebuild its mean tiles.
+  constexpr int kRowsV = (C * K / 192) * 192;  // row elements of waves 4, 5, 7
   const int wl = (nvalid - 1) / C;
+  const int grp_v = wave == 6 ? -1 : wave == 7 ? tid - 320 : tid - 256;
   if (wave >= 4) {
-    const int grp = wave == 6 ? -1 : wave == 7 ? tid - 320 : tid - 256;
-    chunk_operands<K, V, BF16>(s, wl, wl & 1, grp, NT - 320, tid - 256, wave, lg, lr);
-  } else if (kw) {
-    mean_tiles<K, V, BF16>(s, wl, kb_w, lg, lr, Ms, Mt);
+    chunk_operands<K, V, BF16>(s, wl, wl & 1, grp_v, kRowsV, 192, false, tid - 256, wave, lg, lr);
+  } else {
+    if (kw) mean_tiles<K, V, BF16>(s, wl, kb_w, lg, lr, Ms, Mt);
+    chunk_operands<K, V, BF16>(s, wl, wl & 1, kRowsV + tid, C * K, 256, wave == 3, -1, wave, lg, lr);
   }
   KLA_BTL(1);
   __syncthreads();
@@ -1027,10 +1031,11 @@ __global__ __launch_bounds__(kChunkThreads) void kla_bwd_chunk_kernel(BwdParams 
       }
     }
     KLA_BTL(5);
-    // Wave 6 forms the score tile A and takes no share of the rows.
-    if (wave >= 4 && w > 0) {
-      const int grp = wave == 6 ? -1 : wave == 7 ? tid - 320 : tid - 256;
-      chunk_operands<K, V, BF16>(s, w - 1, (w - 1) & 1, grp, NT - 320, tid - 256, wave, lg, lr);
+    if (w > 0) {
+      if (wave >= 4)
+        chunk_operands<K, V, BF16>(s, w - 1, (w - 1) & 1, grp_v, kRowsV, 192, false, tid - 256, wave, lg, lr);
+      else
+        chunk_operands<K, V, BF16>(s, w - 1, (w - 1) & 1, kRowsV + tid, C * K, 256, wave == 3, -1, wave, lg, lr);
     }
     KLA_BTL(6);
     __syncthreads();
