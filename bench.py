@@ -231,8 +231,8 @@ def cpu_baseline(x):
     tokens) on the host, in this process before the GPU is touched: once on
     one core (the whole batch in one vectorised call), then split into n
     contiguous blocks of (b, h) pairs over a pool of n forked processes,
-    n = the cores this process may run on (at most 16, a one-GPU machine's
-    share).  `value` is the n-core rate; the 1-core rate is reported beside
+    n = the cores this process may run on (at most 16, the host share of one
+    GPU on an eight-GPU node).  `value` is the n-core rate; the 1-core rate is reported beside
     it.  Returns the JSON object and the oracle's y for the parity margin."""
     import multiprocessing as mp
     import numpy as np
