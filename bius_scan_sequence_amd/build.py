@@ -103,10 +103,10 @@ def build_host_sanitized(verbose: bool = False) -> str:
     return SAN_LIB
 
 
-# Timeline build: the run-streaming forward and the backward compiled with
-# -DKLA_TIMELINE (per workgroup real-time stamps and per wave phase sums of the
-# backward chunk kernel, read by bius_scan_sequence_amd/timeline.py); every
-# other object is the ordinary one.
+# Timeline build: the forward kernels and the backward compiled with
+# -DKLA_TIMELINE (per workgroup real-time stamps of the run-streaming and the
+# segmented forward, per wave phase sums of the backward chunk kernel, read by
+# bius_scan_sequence_amd/timeline.py); every other object is the ordinary one.
 TL_DIR = os.path.join(BUILD, "timeline")
 TL_LIB = os.path.join(PKG, "libkla_timeline.so")
 
@@ -116,7 +116,7 @@ def build_timeline(verbose: bool = False) -> str:
     if not all(os.path.exists(os.path.join(BUILD, os.path.splitext(s)[0] + ".o")) for s in SOURCES):
         build()
     os.makedirs(TL_DIR, exist_ok=True)
-    traced = ("kla_forward_run.hip", "kla_backward.hip")
+    traced = ("kla_forward_run.hip", "kla_forward.hip", "kla_backward.hip")
     objs = []
     for src in traced:
         obj = os.path.join(TL_DIR, os.path.splitext(src)[0] + "_tl.o")

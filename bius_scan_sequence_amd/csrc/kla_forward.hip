@@ -42,6 +42,34 @@
 
 namespace kla {
 
+#ifdef KLA_TIMELINE
+// Timeline build only (-DKLA_TIMELINE): the first thread of every workgroup
+// of the segmented kernel records the 100 MHz real-time counter at the start
+// of each section, into kla_seg_timeline_buf[workgroup][slot]: 0 entry, 1
+// ticket read, 2 inputs staged, 3 chunk aggregates done, 4 precision carry
+// done, 5 gate walk done, 6 scores done, 7 chunk loop done, 8 mean carry done,
+// 9 end; values: 10 segment, 11 segments the mean look-back folded (0: none).
+constexpr int kStlSlots = 16, kStlGroups = 16384;
+__device__ unsigned long long kla_seg_timeline_buf[kStlGroups * kStlSlots];
+#define KLA_SSTAMP(k)                                                                               \
+  do {                                                                                              \
+    if (threadIdx.x == 0 && blockIdx.x < (unsigned)kStlGroups)                                      \
+      kla_seg_timeline_buf[(size_t)blockIdx.x * kStlSlots + (k)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define KLA_SVALUE(k, v)                                                                             \
+  do {                                                                                               \
+    if (threadIdx.x == 0 && blockIdx.x < (unsigned)kStlGroups)                                       \
+      kla_seg_timeline_buf[(size_t)blockIdx.x * kStlSlots + (k)] = (unsigned long long)(v);          \
+  } while (0)
+#else
+#define KLA_SSTAMP(k) \
+  do {                \
+  } while (0)
+#define KLA_SVALUE(k, v) \
+  do {                   \
+  } while (0)
+#endif
+
 template <int DK, int DV, bool BF16>
 struct FwdCfg {
   using In = typename std::conditional<BF16, uint16_t, float>::type;
@@ -505,6 +533,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lc = lane & 15;  // lane group (k block) / lane column
   const int nheads = p.nheads, T = p.T, nseg = p.nseg;
+  KLA_SSTAMP(0);
   // (head, segment) from a ticket when segments wait on predecessors: group
   // x = blockIdx % tgroups serves heads x, x + tgroups, ..., segment-major, so
   // every segment a workgroup waits on holds a smaller ticket of its own
@@ -520,6 +549,8 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   const int nvalid = min(L, T - t0);
   const bool last = (seg == nseg - 1);
   const size_t hs = (size_t)head * nseg + seg;  // (head, segment) slot
+  KLA_SSTAMP(1);
+  KLA_SVALUE(10, seg);
   const size_t hb = (size_t)head * nseg;
 
   if (tid < NCH) s.unsafe[tid] = 0;
@@ -577,6 +608,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   unsigned long long early = 0ull;
   if (pwave && pch && seg > 0) early = ld_record(p.pinc + (hb + seg - 1) * DK + tid);
 
+  KLA_SSTAMP(2);
   // ---------------------------------------------------------------- 1. chunk aggregates
   // Walker (chunk wc, half wh) owns channels wch .. wch + CPT - 1 and tokens
   // wt0 .. wt0 + 7 and composes their 2x2 step matrices; the halves of a
@@ -678,6 +710,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   if constexpr (MODE == kPrologue || !C::CAGG_IN_V) store_tile<In, L, DV, NT>(s.v, bv, tid);
   __syncthreads();
 
+  KLA_SSTAMP(3);
   // ---------------------------------------------------------------- 2. precision carry
   // The carry waves (one lane per channel; a second wave when DK = 128) each
   // run their own look-back over their channels, with flags of their own, so
@@ -775,6 +808,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
     store_tile<In, L, DV, NT>(s.v, bv, tid);  // the aggregates are consumed
   }
 
+  KLA_SSTAMP(4);
   // ---------------------------------------------------------------- 3. gate walk
   // Results stay in registers until every walker has finished reading the raw
   // inputs, then overwrite them as stored operands.  A second-half walker
@@ -978,6 +1012,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   }
   __syncthreads();
 
+  KLA_SSTAMP(5);
   // ---------------------------------------------------------------- 4a. intra-chunk scores
   // A[t][u] = sum_i Qs[t][i] Ks[u][i] for u <= t (0 above the diagonal),
   // stored in A-operand order: lane l, element e -> A[t = l%16][u = 4*(l/16) + e].
@@ -1086,6 +1121,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   }
   __syncthreads();
 
+  KLA_SSTAMP(6);
   // ---------------------------------------------------------------- 4b. chunk loop
   // Local chunk states from a zero state: M_{c+1} = diag(cp_end_c) M_c + Kd_c^T V_c.
   // y_c gets its local part A_c V_c + q cp M_c, here or (LATE_LOCAL) from the
@@ -1161,6 +1197,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
     }
   }
 
+  KLA_SSTAMP(7);
   // ---------------------------------------------------------------- 5. mean carry
   // Each lane owns, per tile (mt, nt), rows 16*mt + 4*lg + e of column 16*nt + lc.
   // Workspace payloads are stored in this fragment order, 16 bytes per lane.
@@ -1257,6 +1294,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
         wait_stores();
         if (!last && lane == 0) st_relaxed(mfl + NW * seg, FAGG);
         r0 = lookback_find(mfl, NW, seg, FAGG, FINC, p.ctrl, f1);
+        KLA_SVALUE(11, seg - r0);
       }
       // Fold the carries of segments r0 .. seg-1 (M <- diag(prod f) M + local
       // state), FB aggregates per round trip.
@@ -1321,6 +1359,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
     }
   }
 
+  KLA_SSTAMP(8);
   // ---------------------------------------------------------------- 6. carried-state readout + store
   // With M_in the state entering the segment, the true state entering chunk c
   // is M_c + diag(prod of earlier chunk decays) M_in, so
@@ -1352,6 +1391,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   }
   __syncthreads();
   unstage_tile<In, L, DV, NT>(static_cast<In*>(p.y) + ((size_t)head * T + t0) * DV, s.v, nvalid, tid);
+  KLA_SSTAMP(9);
 }
 
 // ------------------------------------------------------------------------------
@@ -1389,3 +1429,16 @@ hipError_t launch_forward(const FwdParams& p, int dk, int dv, bool bf16, hipStre
 }
 
 }  // namespace kla
+
+#ifdef KLA_TIMELINE
+extern "C" int kla_seg_timeline_read(void* host, size_t bytes) {
+  const size_t n = sizeof(kla::kla_seg_timeline_buf);
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(kla::kla_seg_timeline_buf), bytes < n ? bytes : n, 0,
+                                  hipMemcpyDeviceToHost);
+}
+extern "C" int kla_seg_timeline_clear() {
+  static unsigned long long zeros[kla::kStlGroups * kla::kStlSlots];
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(kla::kla_seg_timeline_buf), zeros, sizeof(zeros), 0, hipMemcpyHostToDevice);
+}
+#endif
+

@@ -4,6 +4,7 @@ the backward chunk kernel (kla_bwd_chunk_kernel).
     python3 bius_scan_sequence_amd/build.py --timeline
     python3 bius_scan_sequence_amd/timeline.py [--config lm45m_bf16] [--calls 5]
     python3 bius_scan_sequence_amd/timeline.py --backward [--config bwd_lm45m_bf16]
+    python3 bius_scan_sequence_amd/timeline.py --segmented [--config long_bf16]
 
 The timeline build (libkla_timeline.so) compiles the run kernel with
 -DKLA_TIMELINE: the first lane of wave 0 (a walker) and of wave 4 (a matrix
@@ -235,14 +236,84 @@ def run_backward(config: str = "bwd_lm45m_bf16", calls: int = 3, lib_path: str =
     return "\n".join(out)
 
 
+SEG_PHASES = ("ticket read", "inputs staged", "chunk aggregates (precision maps)", "precision carry",
+              "gate walk", "intra-chunk scores", "chunk loop (local states)", "mean carry (publish, look-back, fold)",
+              "carried-state readout and store")
+
+
+def run_segmented(config: str = "long_bf16", calls: int = 3, lib_path: str = TL_LIB) -> str:
+    """Per-section durations of the segmented forward (kla_fwd_kernel), one
+    workgroup per segment: medians over the workgroups of the recorded call,
+    the spread of the mean carry, and how many segments its look-back folded."""
+    if not os.path.exists(lib_path):
+        raise RuntimeError(f"{lib_path} missing: build it with bius_scan_sequence_amd/build.py --timeline")
+    os.environ["BIUS_KLA_LIB"] = lib_path
+    import torch
+    sys.path.insert(0, os.path.dirname(PKG))
+    import bius_scan_sequence_amd as K
+    import kla_inputs as KI
+
+    lib = K.lib
+    lib.kla_seg_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.kla_seg_timeline_read.restype = ctypes.c_int
+    lib.kla_seg_timeline_clear.restype = ctypes.c_int
+    w = KI.workload(config)
+    dev = torch.device("cuda", 0)
+    x = KI.make_forward_inputs_torch(w, device=dev)
+    ws = K.Workspace(dev)
+
+    def call():
+        return K.forward(*(x[n] for n in NAMES), x["lambda0"], x["M0"], workspace=ws)
+
+    for _ in range(calls):
+        call()
+    torch.cuda.synchronize()
+    assert lib.kla_seg_timeline_clear() == 0
+    call()
+    torch.cuda.synchronize()
+    S_, G = 16, 16384
+    buf = np.zeros(G * S_, dtype=np.uint64)
+    assert lib.kla_seg_timeline_read(buf.ctypes.data, buf.nbytes) == 0
+    S = buf.reshape(G, S_).astype(np.int64)
+    S = S[S[:, 9] > 0]
+    if len(S) == 0:
+        raise SystemExit(f"{config}: kla_forward ran no segmented kernel (bf16 at d_k = d_v = 64 takes the "
+                         f"run-streaming kernel; use the plain timeline)")
+    t0 = S[:, 0].min()
+    out = []
+    p = out.append
+    p(f"kla_fwd_kernel (segmented) timeline: {config} (B{w.B} H{w.H} T{w.T} d_k {w.dk} d_v {w.dv} {w.dtype}), "
+      f"{len(S)} workgroups (one segment each)")
+    p("medians over workgroups, in us (100 MHz real-time counter; the stamps add a little time)")
+    p("")
+    p("| section | median us | 90th percentile us |")
+    p("|---|---|---|")
+    for k, n in enumerate(SEG_PHASES):
+        d = (S[:, k + 1] - S[:, k]) / 100.0
+        p(f"| {n} | {np.median(d):.2f} | {np.percentile(d, 90):.2f} |")
+    life = (S[:, 9] - S[:, 0]) / 100.0
+    p(f"| **workgroup life** | **{np.median(life):.2f}** | {np.percentile(life, 90):.2f} |")
+    folded = S[:, 11]
+    p("")
+    vals, cnt = np.unique(folded, return_counts=True)
+    p("mean look-back: segments folded (1 = the predecessor's inclusive state only) -> workgroups: " +
+      ", ".join(f"{int(v)}: {int(c)}" for v, c in zip(vals, cnt)))
+    p(f"kernel span (first entry to last end): {(S[:, 9].max() - t0) / 100.0:.1f} us; "
+      f"workgroup entries spread over {(S[:, 0].max() - t0) / 100.0:.1f} us")
+    return "\n".join(out)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--config", default=None)
     ap.add_argument("--calls", type=int, default=5, help="calls before the recorded one")
     ap.add_argument("--lib", default=TL_LIB, help="another timeline build of the library")
     ap.add_argument("--backward", action="store_true", help="the backward chunk kernel's phases")
+    ap.add_argument("--segmented", action="store_true", help="the segmented forward's sections")
     a = ap.parse_args()
-    if a.backward:
+    if a.segmented:
+        print(run_segmented(a.config or "long_bf16", a.calls, a.lib), flush=True)
+    elif a.backward:
         print(run_backward(a.config or "bwd_lm45m_bf16", a.calls, a.lib), flush=True)
     else:
         print(run(a.config or "lm45m_bf16", a.calls, a.lib), flush=True)
