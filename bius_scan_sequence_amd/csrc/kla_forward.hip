@@ -534,6 +534,26 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   const int lg = lane >> 4, lc = lane & 15;  // lane group (k block) / lane column
   const int nheads = p.nheads, T = p.T, nseg = p.nseg;
   KLA_SSTAMP(0);
+  // The inputs of the (head, segment) the workgroup index predicts are
+  // requested before the ticket is drawn (workgroups of a group mostly draw
+  // their tickets in index order); a wrong guess costs only these loads.
+  constexpr int UK = (L * DK * (int)sizeof(In) / 16 + NT - 1) / NT, UV = (L * DV * (int)sizeof(In) / 16 + NT - 1) / NT;
+  uint4 gq[UK], gv[UV], gk[UK], gld[UK], gpn[UK], gvp[UK];
+  int g_seg = -1, g_head = -1;
+  if constexpr (MODE != kPrologue) {
+    const unsigned tgg = nseg > 1 ? (unsigned)p.tgroups : 1u, hpgg = (unsigned)nheads / tgg;
+    const unsigned gt = nseg > 1 ? blockIdx.x / tgg : blockIdx.x;
+    g_seg = (int)(gt / hpgg);
+    g_head = (int)((gt % hpgg) * tgg + blockIdx.x % tgg);
+    const int gnv = min(L, T - g_seg * L);
+    const size_t gko = ((size_t)g_head * T + (size_t)g_seg * L) * DK, gvo = ((size_t)g_head * T + (size_t)g_seg * L) * DV;
+    load_tile<In, L, DK, NT>(gq, static_cast<const In*>(p.q) + gko, gnv, tid);
+    load_tile<In, L, DV, NT>(gv, static_cast<const In*>(p.v) + gvo, gnv, tid);
+    load_tile<In, L, DK, NT>(gk, static_cast<const In*>(p.k) + gko, gnv, tid);
+    load_tile<In, L, DK, NT>(gld, static_cast<const In*>(p.ld) + gko, gnv, tid);
+    if constexpr (!OU) load_tile<In, L, DK, NT>(gpn, static_cast<const In*>(p.pn) + gko, gnv, tid);
+    load_tile<In, L, DK, NT>(gvp, static_cast<const In*>(p.vp) + gko, gnv, tid);
+  }
   // (head, segment) from a ticket when segments wait on predecessors: group
   // x = blockIdx % tgroups serves heads x, x + tgroups, ..., segment-major, so
   // every segment a workgroup waits on holds a smaller ticket of its own
@@ -566,7 +586,6 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   // LDS first and q, v only after the aggregate walk, so their load latency
   // overlaps the walk.
   const size_t offk = ((size_t)head * T + t0) * DK, offv = ((size_t)head * T + t0) * DV;
-  constexpr int UK = (L * DK * (int)sizeof(In) / 16 + NT - 1) / NT, UV = (L * DV * (int)sizeof(In) / 16 + NT - 1) / NT;
   uint4 bq[UK], bv[UV];
   if constexpr (MODE == kPrologue) {
     // q, k, v are SiLU(conv) of the raw projections.  The raw tiles go to LDS
@@ -586,6 +605,15 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
     stage_halo<In, DV, NT>(s.halo + 6 * DK, static_cast<const In*>(p.v) + offv, t0, tid);
     stage_tile<In, L, DK, NT>(rld, static_cast<const In*>(p.ld) + offk, nvalid, tid);  // raw step length
     stage_tile<In, L, DK, NT>(rvp, static_cast<const In*>(p.vp) + offk, nvalid, tid);  // raw value precision
+  } else if (seg == g_seg && head == g_head) {  // the guess was right: the tiles are in flight
+#pragma unroll
+    for (int u = 0; u < UK; ++u) bq[u] = gq[u];
+#pragma unroll
+    for (int u = 0; u < UV; ++u) bv[u] = gv[u];
+    store_tile<In, L, DK, NT>(rk, gk, tid);
+    store_tile<In, L, DK, NT>(rld, gld, tid);
+    if constexpr (!OU) store_tile<In, L, DK, NT>(rpn, gpn, tid);
+    store_tile<In, L, DK, NT>(rvp, gvp, tid);
   } else {
     load_tile<In, L, DK, NT>(bq, static_cast<const In*>(p.q) + offk, nvalid, tid);
     load_tile<In, L, DV, NT>(bv, static_cast<const In*>(p.v) + offv, nvalid, tid);
