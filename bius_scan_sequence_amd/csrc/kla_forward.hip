@@ -540,7 +540,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
   constexpr int UK = (L * DK * (int)sizeof(In) / 16 + NT - 1) / NT, UV = (L * DV * (int)sizeof(In) / 16 + NT - 1) / NT;
   uint4 gq[UK], gv[UV], gk[UK], gld[UK], gpn[UK], gvp[UK];
   int g_seg = -1, g_head = -1;
-  if constexpr (MODE != kPrologue) {
+  {
     const unsigned tgg = nseg > 1 ? (unsigned)p.tgroups : 1u, hpgg = (unsigned)nheads / tgg;
     const unsigned gt = nseg > 1 ? blockIdx.x / tgg : blockIdx.x;
     g_seg = (int)(gt / hpgg);
@@ -551,7 +551,7 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
     load_tile<In, L, DV, NT>(gv, static_cast<const In*>(p.v) + gvo, gnv, tid);
     load_tile<In, L, DK, NT>(gk, static_cast<const In*>(p.k) + gko, gnv, tid);
     load_tile<In, L, DK, NT>(gld, static_cast<const In*>(p.ld) + gko, gnv, tid);
-    if constexpr (!OU) load_tile<In, L, DK, NT>(gpn, static_cast<const In*>(p.pn) + gko, gnv, tid);
+    if constexpr (MODE == kPlain) load_tile<In, L, DK, NT>(gpn, static_cast<const In*>(p.pn) + gko, gnv, tid);
     load_tile<In, L, DK, NT>(gvp, static_cast<const In*>(p.vp) + gko, gnv, tid);
   }
   // (head, segment) from a ticket when segments wait on predecessors: group
@@ -597,14 +597,27 @@ __global__ __launch_bounds__((FwdCfg<DK, DV, BF16>::NT), (fwd_waves_per_eu<DK, D
     // that do not carry (section 2).  k itself is never stored, so the chunk
     // aggregates go to k's slot.
     In* const hk = s.halo + 3 * DK;
-    load_tile<In, L, DK, NT>(bq, static_cast<const In*>(p.q) + offk, nvalid, tid);
-    load_tile<In, L, DV, NT>(bv, static_cast<const In*>(p.v) + offv, nvalid, tid);
-    stage_tile<In, L, DK, NT>(rpn, static_cast<const In*>(p.k) + offk, nvalid, tid);
+    if (seg == g_seg && head == g_head) {  // the guess was right: the tiles are in flight
+#pragma unroll
+      for (int u = 0; u < UK; ++u) bq[u] = gq[u];
+#pragma unroll
+      for (int u = 0; u < UV; ++u) bv[u] = gv[u];
+      store_tile<In, L, DK, NT>(rpn, gk, tid);
+    } else {
+      load_tile<In, L, DK, NT>(bq, static_cast<const In*>(p.q) + offk, nvalid, tid);
+      load_tile<In, L, DV, NT>(bv, static_cast<const In*>(p.v) + offv, nvalid, tid);
+      stage_tile<In, L, DK, NT>(rpn, static_cast<const In*>(p.k) + offk, nvalid, tid);
+    }
     stage_halo<In, DK, NT>(hk, static_cast<const In*>(p.k) + offk, t0, tid);
     stage_halo<In, DK, NT>(s.halo, static_cast<const In*>(p.q) + offk, t0, tid);
     stage_halo<In, DV, NT>(s.halo + 6 * DK, static_cast<const In*>(p.v) + offv, t0, tid);
-    stage_tile<In, L, DK, NT>(rld, static_cast<const In*>(p.ld) + offk, nvalid, tid);  // raw step length
-    stage_tile<In, L, DK, NT>(rvp, static_cast<const In*>(p.vp) + offk, nvalid, tid);  // raw value precision
+    if (seg == g_seg && head == g_head) {
+      store_tile<In, L, DK, NT>(rld, gld, tid);  // raw step length
+      store_tile<In, L, DK, NT>(rvp, gvp, tid);  // raw value precision
+    } else {
+      stage_tile<In, L, DK, NT>(rld, static_cast<const In*>(p.ld) + offk, nvalid, tid);  // raw step length
+      stage_tile<In, L, DK, NT>(rvp, static_cast<const In*>(p.vp) + offk, nvalid, tid);  // raw value precision
+    }
   } else if (seg == g_seg && head == g_head) {  // the guess was right: the tiles are in flight
 #pragma unroll
     for (int u = 0; u < UK; ++u) bq[u] = gq[u];
